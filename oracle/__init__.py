@@ -1,0 +1,319 @@
+"""CPU oracle for the block-quantized GEMV (TEST INFRASTRUCTURE ONLY).
+
+Only the tests, the smoke check and the benchmark's CPU-baseline leg may import
+this package. The GPU library never imports it and shares no code with it.
+
+Thin ctypes binding over `qgemv_oracle.c` (plain C, float64 results, exact
+integer partials). The arithmetic lives in the C file; this module only moves
+numpy arrays in and out. `build()` compiles the C file with gcc into
+`oracle/_build/liboracle.so`; loading builds it when it is missing.
+
+Byte layouts (restated in the C file):
+  Q4_K tensor  = rows x (cols/256) blocks of 144 bytes, row-major.
+  Q6_K tensor  = rows x (cols/256) bodies of 208 bytes, then the same number of
+                 fp16 super-scales d (two planes, 210 bytes per 256 weights).
+  activations  = int8 codes [nvec][cols] and float32 scales [nvec][cols/32].
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "qgemv_oracle.c")
+_LIB = os.path.join(_HERE, "_build", "liboracle.so")
+
+Q4K_BYTES = 144
+Q6K_BODY = 208
+Q6K_BYTES = 210
+QK = 256
+
+CFLAGS = ["-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off", "-fno-fast-math",
+          "-Wall", "-Wextra"]
+
+_lock = threading.Lock()
+_lib = None
+
+
+def build(out: str = _LIB, extra_flags=(), src: str = _SRC) -> str:
+    """Compile the oracle with gcc (always rebuilds). Returns the library path."""
+    os.makedirs(os.path.dirname(out), exist_ok=True)
+    tmp = out + ".tmp%d" % os.getpid()
+    cmd = ["gcc", *CFLAGS, *extra_flags, src, "-o", tmp, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, out)
+    return out
+
+
+def _p(a, ctype):
+    return a.ctypes.data_as(ctypes.POINTER(ctype)) if a is not None else None
+
+
+def load(path: str | None = None):
+    """Load the compiled oracle (building it first if it is missing)."""
+    global _lib
+    with _lock:
+        if path is None and _lib is not None:
+            return _lib
+        lib_path = path or _LIB
+        if not os.path.exists(lib_path):
+            build(lib_path)
+        lib = ctypes.CDLL(lib_path)
+        u8p, i8p, u16p = (ctypes.POINTER(ctypes.c_uint8), ctypes.POINTER(ctypes.c_int8),
+                          ctypes.POINTER(ctypes.c_uint16))
+        f32p, f64p, i32p = (ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_double),
+                            ctypes.POINTER(ctypes.c_int32))
+        i64, i32 = ctypes.c_int64, ctypes.c_int32
+        sig = {
+            "orc_f32_to_f16": (ctypes.c_uint16, [ctypes.c_float]),
+            "orc_f16_to_f32": (ctypes.c_float, [ctypes.c_uint16]),
+            "orc_f32_to_f16_array": (None, [f32p, u16p, i64]),
+            "orc_f16_to_f32_array": (None, [u16p, f32p, i64]),
+            "orc_quantize_act": (None, [f32p, i64, i32, i8p, f32p]),
+            "orc_q4k_pack_block": (None, [ctypes.c_uint16, ctypes.c_uint16, u8p, u8p, u8p, u8p]),
+            "orc_q4k_unpack_block": (None, [u8p, u16p, u16p, u8p, u8p, u8p]),
+            "orc_q6k_pack_block": (None, [i8p, u8p, u8p]),
+            "orc_q6k_unpack_block": (None, [u8p, i8p, u8p]),
+            "orc_quantize_q4k": (None, [f32p, i64, i64, u8p]),
+            "orc_quantize_q6k": (None, [f32p, i64, i64, u8p, u16p, ctypes.c_int]),
+            "orc_dequant_q4k": (None, [u8p, i64, i64, f64p]),
+            "orc_dequant_q6k": (None, [u8p, u16p, i64, i64, f64p]),
+            "orc_gemv_q4k": (None, [u8p, i64, i64, i32, i8p, f32p, i32p, i32p, f64p, f64p]),
+            "orc_gemv_q6k": (None, [u8p, u16p, i64, i64, i32, i8p, f32p, i32p, f64p, f64p]),
+            "orc_bruteforce": (None, [f64p, i64, i64, i32, i8p, f32p, f64p]),
+        }
+        for name, (res, args) in sig.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        if path is None:
+            _lib = lib
+        return lib
+
+
+# ------------------------------------------------------------------ fp16 --
+def f32_to_f16(x, lib=None) -> np.ndarray:
+    lib = lib or load()
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.empty(x.shape, dtype=np.uint16)
+    lib.orc_f32_to_f16_array(_p(x, ctypes.c_float), _p(out, ctypes.c_uint16), x.size)
+    return out
+
+
+def f16_to_f32(h, lib=None) -> np.ndarray:
+    lib = lib or load()
+    h = np.ascontiguousarray(h, dtype=np.uint16)
+    out = np.empty(h.shape, dtype=np.float32)
+    lib.orc_f16_to_f32_array(_p(h, ctypes.c_uint16), _p(out, ctypes.c_float), h.size)
+    return out
+
+
+# ----------------------------------------------------------- activations --
+def quantize_act(x, lib=None):
+    """x float32 [nvec][cols] -> (xq int8 [nvec][cols], xd float32 [nvec][cols/32])."""
+    lib = lib or load()
+    x = np.ascontiguousarray(np.atleast_2d(x), dtype=np.float32)
+    nvec, cols = x.shape
+    xq = np.empty((nvec, cols), dtype=np.int8)
+    xd = np.empty((nvec, cols // 32), dtype=np.float32)
+    lib.orc_quantize_act(_p(x, ctypes.c_float), cols, nvec, _p(xq, ctypes.c_int8),
+                         _p(xd, ctypes.c_float))
+    return xq, xd
+
+
+# ---------------------------------------------------------- block layout --
+def q4k_pack_block(d16: int, dmin16: int, sc, m, q, lib=None) -> np.ndarray:
+    lib = lib or load()
+    sc = np.ascontiguousarray(sc, dtype=np.uint8)
+    m = np.ascontiguousarray(m, dtype=np.uint8)
+    q = np.ascontiguousarray(q, dtype=np.uint8)
+    out = np.empty(Q4K_BYTES, dtype=np.uint8)
+    lib.orc_q4k_pack_block(d16, dmin16, _p(sc, ctypes.c_uint8), _p(m, ctypes.c_uint8),
+                           _p(q, ctypes.c_uint8), _p(out, ctypes.c_uint8))
+    return out
+
+
+def q4k_unpack_block(blk, lib=None):
+    """-> (d fp16 bits, dmin fp16 bits, sc[8], m[8], q[256])"""
+    lib = lib or load()
+    blk = np.ascontiguousarray(blk, dtype=np.uint8)
+    d = np.zeros(1, np.uint16)
+    dm = np.zeros(1, np.uint16)
+    sc = np.zeros(8, np.uint8)
+    m = np.zeros(8, np.uint8)
+    q = np.zeros(QK, np.uint8)
+    lib.orc_q4k_unpack_block(_p(blk, ctypes.c_uint8), _p(d, ctypes.c_uint16),
+                             _p(dm, ctypes.c_uint16), _p(sc, ctypes.c_uint8),
+                             _p(m, ctypes.c_uint8), _p(q, ctypes.c_uint8))
+    return int(d[0]), int(dm[0]), sc, m, q
+
+
+def q6k_pack_block(sc, q, lib=None) -> np.ndarray:
+    lib = lib or load()
+    sc = np.ascontiguousarray(sc, dtype=np.int8)
+    q = np.ascontiguousarray(q, dtype=np.uint8)
+    out = np.empty(Q6K_BODY, dtype=np.uint8)
+    lib.orc_q6k_pack_block(_p(sc, ctypes.c_int8), _p(q, ctypes.c_uint8), _p(out, ctypes.c_uint8))
+    return out
+
+
+def q6k_unpack_block(body, lib=None):
+    """-> (sc int8[16], q uint8[256])"""
+    lib = lib or load()
+    body = np.ascontiguousarray(body, dtype=np.uint8)
+    sc = np.zeros(16, np.int8)
+    q = np.zeros(QK, np.uint8)
+    lib.orc_q6k_unpack_block(_p(body, ctypes.c_uint8), _p(sc, ctypes.c_int8),
+                             _p(q, ctypes.c_uint8))
+    return sc, q
+
+
+def q6k_planes(buf, rows: int, cols: int):
+    """Split a Q6_K tensor (uint8, 210 bytes per 256 weights) into (bodies, d plane)."""
+    nb = cols // QK
+    buf = np.ascontiguousarray(buf, dtype=np.uint8).reshape(-1)
+    if buf.size != rows * nb * Q6K_BYTES:
+        raise ValueError("Q6_K tensor has %d bytes, expected %d" % (buf.size, rows * nb * Q6K_BYTES))
+    bodies = buf[:rows * nb * Q6K_BODY]
+    dplane = buf[rows * nb * Q6K_BODY:].view(np.uint16)
+    return bodies, dplane
+
+
+def q6k_join(bodies, dplane) -> np.ndarray:
+    return np.concatenate([np.ascontiguousarray(bodies, np.uint8).reshape(-1),
+                           np.ascontiguousarray(dplane, np.uint16).reshape(-1).view(np.uint8)])
+
+
+# ------------------------------------------------------ weight quantizers --
+def quantize_q4k(w, lib=None) -> np.ndarray:
+    """w float32 [rows][cols] -> Q4_K tensor, uint8 [rows * cols/256 * 144]."""
+    lib = lib or load()
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    rows, cols = w.shape
+    out = np.empty(rows * (cols // QK) * Q4K_BYTES, dtype=np.uint8)
+    lib.orc_quantize_q4k(_p(w, ctypes.c_float), rows, cols, _p(out, ctypes.c_uint8))
+    return out
+
+
+def quantize_q6k(w, negate_scales: bool = False, lib=None) -> np.ndarray:
+    """w float32 [rows][cols] -> Q6_K tensor, uint8 [rows * cols/256 * 210] (two planes)."""
+    lib = lib or load()
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    rows, cols = w.shape
+    nb = cols // QK
+    bodies = np.empty(rows * nb * Q6K_BODY, dtype=np.uint8)
+    dplane = np.empty(rows * nb, dtype=np.uint16)
+    lib.orc_quantize_q6k(_p(w, ctypes.c_float), rows, cols, _p(bodies, ctypes.c_uint8),
+                         _p(dplane, ctypes.c_uint16), int(bool(negate_scales)))
+    return q6k_join(bodies, dplane)
+
+
+def dequantize(wtype: str, wbuf, rows: int, cols: int, lib=None) -> np.ndarray:
+    """Dequantized weights, float64 [rows][cols]."""
+    lib = lib or load()
+    out = np.empty((rows, cols), dtype=np.float64)
+    if wtype == "q4k":
+        wbuf = np.ascontiguousarray(wbuf, dtype=np.uint8)
+        lib.orc_dequant_q4k(_p(wbuf, ctypes.c_uint8), rows, cols, _p(out, ctypes.c_double))
+    else:
+        bodies, dplane = q6k_planes(wbuf, rows, cols)
+        lib.orc_dequant_q6k(_p(bodies, ctypes.c_uint8), _p(dplane, ctypes.c_uint16), rows, cols,
+                            _p(out, ctypes.c_double))
+    return out
+
+
+# ---------------------------------------------------------- integer GEMV --
+def gemv(wtype: str, wbuf, rows: int, cols: int, xq, xd, partials: bool = False,
+         bound: bool = True, lib=None) -> dict:
+    """Integer-formulated GEMV. Returns y [nvec][rows] (float64), bound, and optionally
+    the exact partials P (Q4_K [nvec][rows][cols/32], Q6_K [nvec][rows][cols/16]) and
+    S [nvec][cols/32] (Q4_K only)."""
+    lib = lib or load()
+    xq = np.ascontiguousarray(np.atleast_2d(xq), dtype=np.int8)
+    xd = np.ascontiguousarray(np.atleast_2d(xd), dtype=np.float32)
+    nvec = xq.shape[0]
+    if xq.shape != (nvec, cols) or xd.shape != (nvec, cols // 32):
+        raise ValueError("activation shapes do not match cols")
+    y = np.empty((nvec, rows), dtype=np.float64)
+    bnd = np.empty((nvec, rows), dtype=np.float64) if bound else None
+    out = {"y": y}
+    if wtype == "q4k":
+        P = np.empty((nvec, rows, cols // 32), dtype=np.int32) if partials else None
+        S = np.empty((nvec, cols // 32), dtype=np.int32) if partials else None
+        wbuf = np.ascontiguousarray(wbuf, dtype=np.uint8)
+        lib.orc_gemv_q4k(_p(wbuf, ctypes.c_uint8), rows, cols, nvec, _p(xq, ctypes.c_int8),
+                         _p(xd, ctypes.c_float), _p(P, ctypes.c_int32), _p(S, ctypes.c_int32),
+                         _p(y, ctypes.c_double), _p(bnd, ctypes.c_double))
+        if partials:
+            out["P"], out["S"] = P, S
+    elif wtype == "q6k":
+        P = np.empty((nvec, rows, cols // 16), dtype=np.int32) if partials else None
+        bodies, dplane = q6k_planes(wbuf, rows, cols)
+        lib.orc_gemv_q6k(_p(bodies, ctypes.c_uint8), _p(dplane, ctypes.c_uint16), rows, cols,
+                         nvec, _p(xq, ctypes.c_int8), _p(xd, ctypes.c_float),
+                         _p(P, ctypes.c_int32), _p(y, ctypes.c_double), _p(bnd, ctypes.c_double))
+        if partials:
+            out["P"] = P
+    else:
+        raise ValueError("unknown weight type %r" % wtype)
+    if bound:
+        out["bound"] = bnd
+    return out
+
+
+def block_sums(xq) -> np.ndarray:
+    """S [nvec][cols/32]: exact sums of the activation codes per block of 32 (Q4_K's S)."""
+    xq = np.atleast_2d(np.asarray(xq, dtype=np.int64))
+    nvec, cols = xq.shape
+    return xq.reshape(nvec, cols // 32, 32).sum(axis=2).astype(np.int32)
+
+
+def bruteforce(what, xq, xd, lib=None) -> np.ndarray:
+    """y [nvec][rows] = what @ (xd * xq) in float64, from a dequantized matrix."""
+    lib = lib or load()
+    what = np.ascontiguousarray(what, dtype=np.float64)
+    xq = np.ascontiguousarray(np.atleast_2d(xq), dtype=np.int8)
+    xd = np.ascontiguousarray(np.atleast_2d(xd), dtype=np.float32)
+    rows, cols = what.shape
+    nvec = xq.shape[0]
+    y = np.empty((nvec, rows), dtype=np.float64)
+    lib.orc_bruteforce(_p(what, ctypes.c_double), rows, cols, nvec, _p(xq, ctypes.c_int8),
+                       _p(xd, ctypes.c_float), _p(y, ctypes.c_double))
+    return y
+
+
+def row_slice(wtype: str, wbuf, rows: int, cols: int, r0: int, r1: int) -> np.ndarray:
+    """The tensor of rows r0 .. r1 - 1 of a quantized tensor, in the same format."""
+    nb = cols // QK
+    if wtype == "q4k":
+        return np.ascontiguousarray(wbuf, np.uint8).reshape(rows, nb * Q4K_BYTES)[r0:r1].reshape(-1)
+    bodies, dplane = q6k_planes(wbuf, rows, cols)
+    return q6k_join(bodies.reshape(rows, nb * Q6K_BODY)[r0:r1], dplane.reshape(rows, nb)[r0:r1])
+
+
+def gemv_threaded(wtype: str, wbuf, rows: int, cols: int, xq, xd, threads: int) -> np.ndarray:
+    """The same integer GEMV over equal contiguous row ranges on `threads` host threads
+    (ctypes releases the GIL during each call). Returns y only."""
+    if threads <= 1:
+        return gemv(wtype, wbuf, rows, cols, xq, xd, bound=False)["y"]
+    nvec = np.atleast_2d(xq).shape[0]
+    y = np.empty((nvec, rows), dtype=np.float64)
+    cuts = [rows * i // threads for i in range(threads + 1)]
+    parts = [row_slice(wtype, wbuf, rows, cols, cuts[i], cuts[i + 1]) for i in range(threads)]
+
+    def work(i):
+        r0, r1 = cuts[i], cuts[i + 1]
+        if r1 > r0:
+            y[:, r0:r1] = gemv(wtype, parts[i], r1 - r0, cols, xq, xd, bound=False)["y"]
+
+    ts = [threading.Thread(target=work, args=(i,)) for i in range(threads)]
+    for t in ts:
+        t.start()
+    for t in ts:
+        t.join()
+    return y

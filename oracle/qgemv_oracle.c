@@ -1,0 +1,473 @@
+/*
+ * CPU oracle for the block-quantized weight x int8-activation GEMV y = W x.
+ *
+ * TEST INFRASTRUCTURE ONLY. Only the tests, the smoke check and the benchmark's
+ * CPU-baseline leg may load this file's library. The GPU library shares no code
+ * with it: no headers, no helpers, no tables.
+ *
+ * It is written to be read against the sources, not to be fast: plain loops,
+ * one element at a time, every weight code located by an index formula over the
+ * byte layout (never by word masks), every integer partial in 64-bit with an
+ * int32 range check, and the result y and its error bound in float64.
+ *
+ * Sources of the method (cited by page title and section):
+ *  - genie-ai-runtime v1.1 -> v1.3.1 (jared-hpc.com), "The decode arc": the
+ *    quantized matrix-vector product for Q4_K and Q6_K weights is done in int8
+ *    with 4-way byte dot products instead of dequantizing to floating point;
+ *    "v1.2.0": one int8 activation (q8_1) is shared by several such products.
+ *  - oxinfer README (docs.rs), "How it works" (quant.rs): per-matmul activation
+ *    quantization to int8; decode kernels take int8 dot products block by block.
+ *    "Build and run" (--quant q8): activation blocks of 32 with one f32 scale.
+ *  - The workload definitions: Q4_K = 256-weight super-blocks of 8 x 32, 6-bit
+ *    sub-scales and sub-mins, fp16 d and dmin, 4-bit codes; Q6_K = 16 x 16,
+ *    int8 sub-scales, fp16 d, 6-bit codes with offset -32; activations to int8
+ *    blocks of 32 with an fp32 scale; exact int32 sub-block dot products, then
+ *    scaling and reduction in floating point.
+ *
+ * The pages fix neither byte layouts nor rounding rules. The readings taken
+ * here (byte layouts, quantizer steps, round-to-nearest-even everywhere) are
+ * listed with their reasons in the design notes; the layouts are restated in
+ * the comments of the pack/unpack functions below.
+ *
+ * Pins (all in the CPU test suite): fp16 codec against numpy's IEEE binary16;
+ * hand-derived layout fixtures; closed-form activation cases; quantizer
+ * round-trip bounds and nearest-code optimality; integer GEMV against a
+ * float64 brute force over dequantized weights; one-hot / constant / zero
+ * inputs; extreme codes at the int32 bounds. Every function below is pinned.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define QK 256            /* weights per super-block */
+#define Q4K_BYTES 144     /* bytes per Q4_K super-block */
+#define Q6K_BODY 208      /* bytes per Q6_K super-block body (the fp16 d lives in a separate plane) */
+#define ACT_BLOCK 32      /* activation elements per int8 block */
+
+static void die(const char *what) {
+    fprintf(stderr, "qgemv oracle: %s\n", what);
+    abort();
+}
+
+/* ---------------------------------------------------------------- fp16 ---- */
+/* IEEE 754 binary16: 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits.
+ * float -> half rounds to nearest, ties to even, keeping subnormals; overflow
+ * gives infinity; NaN stays NaN. half -> float is exact. */
+
+static uint32_t f32_bits(float f) { uint32_t u; memcpy(&u, &f, 4); return u; }
+
+uint16_t orc_f32_to_f16(float f) {
+    uint32_t u = f32_bits(f);
+    uint16_t sign = (uint16_t)((u >> 16) & 0x8000u);
+    uint32_t a = u & 0x7FFFFFFFu;
+    if (a >= 0x7F800000u)                       /* inf or NaN */
+        return (uint16_t)(sign | (a > 0x7F800000u ? 0x7E00u : 0x7C00u));
+    if (a < 0x00800000u)                        /* float32 subnormal or zero: below half's range */
+        return sign;
+    int e = (int)(a >> 23) - 127;               /* value = mant * 2^(e - 23), mant has 24 bits */
+    uint32_t mant = (a & 0x007FFFFFu) | 0x00800000u;
+    if (e > 15)
+        return (uint16_t)(sign | 0x7C00u);
+    int shift = 13;                             /* keep 11 significant bits for a normal half */
+    if (e < -14) shift += -14 - e;              /* fewer for a subnormal half */
+    if (shift > 25)
+        return sign;                            /* below half the smallest subnormal */
+    uint32_t kept = mant >> shift;
+    uint32_t rest = mant & ((1u << shift) - 1u);
+    uint32_t half = 1u << (shift - 1);
+    if (rest > half || (rest == half && (kept & 1u)))
+        kept += 1;                              /* may carry into the exponent: still correct */
+    uint32_t h = (e < -14) ? kept : ((uint32_t)(e + 14) << 10) + kept;
+    return (uint16_t)(sign | h);                /* e = 15 with carry lands on 0x7C00 = inf */
+}
+
+float orc_f16_to_f32(uint16_t h) {
+    int sign = (h >> 15) & 1;
+    int e = (h >> 10) & 0x1F;
+    int m = h & 0x3FF;
+    float v;
+    if (e == 0)
+        v = ldexpf((float)m, -24);
+    else if (e == 31)
+        v = m ? NAN : INFINITY;
+    else
+        v = ldexpf((float)(m + 1024), e - 25);
+    return sign ? -v : v;
+}
+
+void orc_f32_to_f16_array(const float *x, uint16_t *h, int64_t n) {
+    for (int64_t i = 0; i < n; i++) h[i] = orc_f32_to_f16(x[i]);
+}
+
+void orc_f16_to_f32_array(const uint16_t *h, float *x, int64_t n) {
+    for (int64_t i = 0; i < n; i++) x[i] = orc_f16_to_f32(h[i]);
+}
+
+static uint16_t rd16(const uint8_t *p) { return (uint16_t)(p[0] | (p[1] << 8)); }
+static void wr16(uint8_t *p, uint16_t v) { p[0] = (uint8_t)v; p[1] = (uint8_t)(v >> 8); }
+
+static float clampf(float v, float lo, float hi) { return v < lo ? lo : (v > hi ? hi : v); }
+
+/* ------------------------------------------------------- activations ---- */
+/* Per block of 32 elements: amax = max |x|; scale xd = amax / 127 (float32
+ * division); inverse id = 127 / amax, or 0 when amax = 0; code
+ * qx = clamp(rint(x * id), -127, 127) with one float32 multiply and
+ * round-to-nearest-even. The codes never take -128. */
+void orc_quantize_act(const float *x, int64_t cols, int32_t nvec, int8_t *xq, float *xd) {
+    if (cols % ACT_BLOCK) die("cols must be a multiple of 32");
+    for (int32_t v = 0; v < nvec; v++) {
+        for (int64_t b = 0; b < cols / ACT_BLOCK; b++) {
+            const float *xb = x + (int64_t)v * cols + b * ACT_BLOCK;
+            float amax = 0.0f;
+            for (int i = 0; i < ACT_BLOCK; i++) {
+                if (!isfinite(xb[i])) die("non-finite activation");
+                float a = fabsf(xb[i]);
+                if (a > amax) amax = a;
+            }
+            float scale = amax / 127.0f;
+            float inv = amax > 0.0f ? 127.0f / amax : 0.0f;
+            for (int i = 0; i < ACT_BLOCK; i++) {
+                float prod = xb[i] * inv;
+                float code = clampf(rintf(prod), -127.0f, 127.0f);
+                xq[(int64_t)v * cols + b * ACT_BLOCK + i] = (int8_t)code;
+            }
+            xd[(int64_t)v * (cols / ACT_BLOCK) + b] = scale;
+        }
+    }
+}
+
+/* ---------------------------------------------------------- Q4_K layout --- */
+/* One 144-byte super-block of 256 weights (sub-block j = weights 32j..32j+31):
+ *   bytes [0,2)    d    (fp16, little-endian)  super-scale of the sub-scales
+ *   bytes [2,4)    dmin (fp16)                 super-scale of the sub-mins
+ *   bytes [4,8)    low 4 bits of sc_j: byte 4 + j/2, bits 4*(j%2) .. +3
+ *   bytes [8,12)   low 4 bits of m_j : byte 8 + j/2, bits 4*(j%2) .. +3
+ *   bytes [12,14)  high 2 bits of sc_j: byte 12 + j/4, bits 2*(j%4) .. +1
+ *   bytes [14,16)  high 2 bits of m_j : byte 14 + j/4, bits 2*(j%4) .. +1
+ *   bytes [16,144) codes: weight i = 32j + 16h + t (h in {0,1}, t < 16) is
+ *                  nibble h (h=0 low, h=1 high) of byte 16 + 16j + t.
+ * Dequantized weight: d * sc_j * q_i - dmin * m_j.                          */
+
+static int q4k_sc(const uint8_t *blk, int j) {
+    int lo = (blk[4 + j / 2] >> (4 * (j % 2))) & 15;
+    int hi = (blk[12 + j / 4] >> (2 * (j % 4))) & 3;
+    return lo | (hi << 4);
+}
+
+static int q4k_m(const uint8_t *blk, int j) {
+    int lo = (blk[8 + j / 2] >> (4 * (j % 2))) & 15;
+    int hi = (blk[14 + j / 4] >> (2 * (j % 4))) & 3;
+    return lo | (hi << 4);
+}
+
+static int q4k_q(const uint8_t *blk, int i) {
+    int j = i / 32, h = (i % 32) / 16, t = i % 16;
+    return (blk[16 + 16 * j + t] >> (4 * h)) & 15;
+}
+
+void orc_q4k_pack_block(uint16_t d, uint16_t dmin, const uint8_t *sc, const uint8_t *m,
+                        const uint8_t *q, uint8_t *blk) {
+    memset(blk, 0, Q4K_BYTES);
+    wr16(blk + 0, d);
+    wr16(blk + 2, dmin);
+    for (int j = 0; j < 8; j++) {
+        if (sc[j] > 63 || m[j] > 63) die("6-bit scale out of range");
+        blk[4 + j / 2] |= (uint8_t)((sc[j] & 15) << (4 * (j % 2)));
+        blk[8 + j / 2] |= (uint8_t)((m[j] & 15) << (4 * (j % 2)));
+        blk[12 + j / 4] |= (uint8_t)((sc[j] >> 4) << (2 * (j % 4)));
+        blk[14 + j / 4] |= (uint8_t)((m[j] >> 4) << (2 * (j % 4)));
+    }
+    for (int i = 0; i < QK; i++) {
+        if (q[i] > 15) die("4-bit code out of range");
+        int j = i / 32, h = (i % 32) / 16, t = i % 16;
+        blk[16 + 16 * j + t] |= (uint8_t)(q[i] << (4 * h));
+    }
+}
+
+void orc_q4k_unpack_block(const uint8_t *blk, uint16_t *d, uint16_t *dmin, uint8_t *sc,
+                          uint8_t *m, uint8_t *q) {
+    *d = rd16(blk + 0);
+    *dmin = rd16(blk + 2);
+    for (int j = 0; j < 8; j++) { sc[j] = (uint8_t)q4k_sc(blk, j); m[j] = (uint8_t)q4k_m(blk, j); }
+    for (int i = 0; i < QK; i++) q[i] = (uint8_t)q4k_q(blk, i);
+}
+
+/* ---------------------------------------------------------- Q6_K layout --- */
+/* A Q6_K tensor of R rows x nb super-blocks is two planes: R*nb bodies of 208
+ * bytes (block (r, b) at offset 208 * (r*nb + b)), then R*nb fp16 super-scales
+ * d. One body (sub-block j = weights 16j..16j+15, signed scale sc_j):
+ *   bytes [0,128)   low 4 bits: weight i = 32k + 16g + t (k < 8, g in {0,1},
+ *                   t < 16) is nibble g of byte 16k + t
+ *   bytes [128,192) high 2 bits: weight i = 32k + 16g + 4s + c (s, c < 4) is
+ *                   bits 2s .. 2s+1 of byte 128 + 8k + 4g + c
+ *   bytes [192,208) sc_j as int8 at byte 192 + j
+ * Code q_i in [0, 63]; dequantized weight: d * sc_j * (q_i - 32).            */
+
+static int q6k_q(const uint8_t *body, int i) {
+    int k = i / 32, g = (i % 32) / 16, t = i % 16, s = t / 4, c = t % 4;
+    int lo = (body[16 * k + t] >> (4 * g)) & 15;
+    int hi = (body[128 + 8 * k + 4 * g + c] >> (2 * s)) & 3;
+    return lo | (hi << 4);
+}
+
+static int q6k_sc(const uint8_t *body, int j) { return (int)(int8_t)body[192 + j]; }
+
+void orc_q6k_pack_block(const int8_t *sc, const uint8_t *q, uint8_t *body) {
+    memset(body, 0, Q6K_BODY);
+    for (int i = 0; i < QK; i++) {
+        if (q[i] > 63) die("6-bit code out of range");
+        int k = i / 32, g = (i % 32) / 16, t = i % 16, s = t / 4, c = t % 4;
+        body[16 * k + t] |= (uint8_t)((q[i] & 15) << (4 * g));
+        body[128 + 8 * k + 4 * g + c] |= (uint8_t)((q[i] >> 4) << (2 * s));
+    }
+    for (int j = 0; j < 16; j++) body[192 + j] = (uint8_t)sc[j];
+}
+
+void orc_q6k_unpack_block(const uint8_t *body, int8_t *sc, uint8_t *q) {
+    for (int j = 0; j < 16; j++) sc[j] = (int8_t)q6k_sc(body, j);
+    for (int i = 0; i < QK; i++) q[i] = (uint8_t)q6k_q(body, i);
+}
+
+/* ------------------------------------------------------ weight quantizers - */
+/* Used to make test data; the GEMV never quantizes weights. Every decision
+ * that yields an integer is taken in float32 with round-to-nearest-even.
+ *
+ * Q4_K, per super-block, per sub-block j of 32 weights:
+ *   lo_j = min(0, min w), hi_j = max w, s_j = (hi_j - lo_j) / 15, o_j = -lo_j
+ *   d = fp16(max_j s_j / 63), dmin = fp16(max_j o_j / 63)
+ *   sc_j = clamp(rint(s_j / d), 0, 63), m_j = clamp(rint(o_j / dmin), 0, 63)
+ *          (0 when the divisor is 0)
+ *   q_i = clamp(rint((w_i + dmin*m_j) / (d*sc_j)), 0, 15)  (0 when d*sc_j = 0)
+ * so that the codes 0..15 span [lo_j, hi_j] on a grid of step d*sc_j.        */
+void orc_quantize_q4k(const float *w, int64_t rows, int64_t cols, uint8_t *out) {
+    if (cols % QK) die("cols must be a multiple of 256");
+    int64_t nb = cols / QK;
+    uint8_t sc[8], m[8], q[QK];
+    for (int64_t r = 0; r < rows; r++) {
+        for (int64_t b = 0; b < nb; b++) {
+            const float *wb = w + r * cols + b * QK;
+            float s[8], o[8], smax = 0.0f, omax = 0.0f;
+            for (int j = 0; j < 8; j++) {
+                float lo = 0.0f, hi = wb[32 * j];
+                for (int i = 0; i < 32; i++) {
+                    float v = wb[32 * j + i];
+                    if (!isfinite(v)) die("non-finite weight");
+                    if (v < lo) lo = v;
+                    if (v > hi) hi = v;
+                }
+                s[j] = (hi - lo) / 15.0f;
+                o[j] = -lo;
+                if (s[j] > smax) smax = s[j];
+                if (o[j] > omax) omax = o[j];
+            }
+            uint16_t dh = orc_f32_to_f16(smax / 63.0f);
+            uint16_t mh = orc_f32_to_f16(omax / 63.0f);
+            float d = orc_f16_to_f32(dh), dmin = orc_f16_to_f32(mh);
+            if (!isfinite(d) || !isfinite(dmin)) die("super-scale overflows fp16");
+            for (int j = 0; j < 8; j++) {
+                sc[j] = (uint8_t)(d > 0.0f ? clampf(rintf(s[j] / d), 0.0f, 63.0f) : 0.0f);
+                m[j] = (uint8_t)(dmin > 0.0f ? clampf(rintf(o[j] / dmin), 0.0f, 63.0f) : 0.0f);
+                float step = d * (float)sc[j];          /* exact: 11 x 6 significant bits */
+                float off = dmin * (float)m[j];         /* exact */
+                for (int i = 0; i < 32; i++) {
+                    float v = wb[32 * j + i];
+                    q[32 * j + i] = (uint8_t)(step > 0.0f
+                        ? clampf(rintf((v + off) / step), 0.0f, 15.0f) : 0.0f);
+                }
+            }
+            orc_q4k_pack_block(dh, mh, sc, m, q, out + (r * nb + b) * Q4K_BYTES);
+        }
+    }
+}
+
+/* Q6_K, per super-block, per sub-block j of 16 weights:
+ *   a_j = max |w|, s_j = a_j / 31, d = fp16(max_j s_j / 127)
+ *   sc_j = clamp(rint(s_j / d), -128, 127)   (0 when d = 0)
+ *   q_i = clamp(rint(w_i / (d*sc_j)), -32, 31) + 32   (32 when sc_j = 0)
+ * negate_scales != 0 gives the equivalent encoding sc' = -sc, q' = 64 - q in
+ * every sub-block that has no code 0 (same dequantized values; it exercises
+ * negative scales).                                                          */
+void orc_quantize_q6k(const float *w, int64_t rows, int64_t cols, uint8_t *bodies,
+                      uint16_t *dplane, int negate_scales) {
+    if (cols % QK) die("cols must be a multiple of 256");
+    int64_t nb = cols / QK;
+    int8_t sc[16];
+    uint8_t q[QK];
+    for (int64_t r = 0; r < rows; r++) {
+        for (int64_t b = 0; b < nb; b++) {
+            const float *wb = w + r * cols + b * QK;
+            float s[16], smax = 0.0f;
+            for (int j = 0; j < 16; j++) {
+                float a = 0.0f;
+                for (int i = 0; i < 16; i++) {
+                    float v = wb[16 * j + i];
+                    if (!isfinite(v)) die("non-finite weight");
+                    if (fabsf(v) > a) a = fabsf(v);
+                }
+                s[j] = a / 31.0f;
+                if (s[j] > smax) smax = s[j];
+            }
+            uint16_t dh = orc_f32_to_f16(smax / 127.0f);
+            float d = orc_f16_to_f32(dh);
+            if (!isfinite(d)) die("super-scale overflows fp16");
+            for (int j = 0; j < 16; j++) {
+                sc[j] = (int8_t)(d > 0.0f ? clampf(rintf(s[j] / d), -128.0f, 127.0f) : 0.0f);
+                float step = d * (float)sc[j];          /* exact: 11 x 8 significant bits */
+                int has_zero = 0;
+                for (int i = 0; i < 16; i++) {
+                    float v = wb[16 * j + i];
+                    int c = step != 0.0f ? (int)clampf(rintf(v / step), -32.0f, 31.0f) + 32 : 32;
+                    q[16 * j + i] = (uint8_t)c;
+                    if (c == 0) has_zero = 1;
+                }
+                if (negate_scales && !has_zero) {
+                    sc[j] = (int8_t)(-sc[j]);
+                    for (int i = 0; i < 16; i++) q[16 * j + i] = (uint8_t)(64 - q[16 * j + i]);
+                }
+            }
+            orc_q6k_pack_block(sc, q, bodies + (r * nb + b) * Q6K_BODY);
+            dplane[r * nb + b] = dh;
+        }
+    }
+}
+
+/* ------------------------------------------------------------ dequantize -- */
+void orc_dequant_q4k(const uint8_t *w, int64_t rows, int64_t cols, double *out) {
+    int64_t nb = cols / QK;
+    for (int64_t r = 0; r < rows; r++)
+        for (int64_t b = 0; b < nb; b++) {
+            const uint8_t *blk = w + (r * nb + b) * Q4K_BYTES;
+            double d = orc_f16_to_f32(rd16(blk)), dmin = orc_f16_to_f32(rd16(blk + 2));
+            for (int i = 0; i < QK; i++) {
+                int j = i / 32;
+                out[r * cols + b * QK + i] = d * q4k_sc(blk, j) * q4k_q(blk, i) - dmin * q4k_m(blk, j);
+            }
+        }
+}
+
+void orc_dequant_q6k(const uint8_t *bodies, const uint16_t *dplane, int64_t rows, int64_t cols,
+                     double *out) {
+    int64_t nb = cols / QK;
+    for (int64_t r = 0; r < rows; r++)
+        for (int64_t b = 0; b < nb; b++) {
+            const uint8_t *body = bodies + (r * nb + b) * Q6K_BODY;
+            double d = orc_f16_to_f32(dplane[r * nb + b]);
+            for (int i = 0; i < QK; i++)
+                out[r * cols + b * QK + i] = d * q6k_sc(body, i / 16) * (q6k_q(body, i) - 32);
+        }
+}
+
+/* ----------------------------------------------------------- integer GEMV - */
+static int32_t checked32(int64_t v) {
+    if (v > INT32_MAX || v < INT32_MIN) die("integer partial leaves int32");
+    return (int32_t)v;
+}
+
+/* Q4_K: for vector v, row r and sub-block j (32 columns, the same columns as
+ * activation block j):
+ *   P[v][r][j] = sum_i q_i * qx_i        (exact integer)
+ *   S[v][j]    = sum_i qx_i              (exact integer)
+ *   y[v][r]    = sum_j xd_j * (d * sc_j * P - dmin * m_j * S)    (float64)
+ *   bound[v][r] = sum_i |dequantized w_i| * |xd_j * qx_i|        (float64)
+ * P (or S, bound) may be NULL. xq is [nvec][cols], xd [nvec][cols/32], y and
+ * bound [nvec][rows], P [nvec][rows][cols/32], S [nvec][cols/32]. */
+void orc_gemv_q4k(const uint8_t *w, int64_t rows, int64_t cols, int32_t nvec,
+                  const int8_t *xq, const float *xd, int32_t *P, int32_t *S,
+                  double *y, double *bound) {
+    if (cols % QK) die("cols must be a multiple of 256");
+    int64_t nb = cols / QK, ns = cols / 32;
+    for (int32_t v = 0; v < nvec; v++) {
+        const int8_t *xv = xq + (int64_t)v * cols;
+        const float *dv = xd + (int64_t)v * ns;
+        if (S)
+            for (int64_t j = 0; j < ns; j++) {
+                int64_t sum = 0;
+                for (int i = 0; i < 32; i++) sum += xv[32 * j + i];
+                S[(int64_t)v * ns + j] = checked32(sum);
+            }
+        for (int64_t r = 0; r < rows; r++) {
+            double acc = 0.0, bnd = 0.0;
+            for (int64_t b = 0; b < nb; b++) {
+                const uint8_t *blk = w + (r * nb + b) * Q4K_BYTES;
+                double d = orc_f16_to_f32(rd16(blk)), dmin = orc_f16_to_f32(rd16(blk + 2));
+                for (int j = 0; j < 8; j++) {
+                    int64_t col0 = b * QK + 32 * j;
+                    int sc = q4k_sc(blk, j), m = q4k_m(blk, j);
+                    int64_t p = 0, s = 0;
+                    for (int i = 0; i < 32; i++) {
+                        int q = q4k_q(blk, 32 * j + i);
+                        p += (int64_t)q * xv[col0 + i];
+                        s += xv[col0 + i];
+                    }
+                    double scale = dv[col0 / 32];
+                    acc += scale * (d * sc * (double)checked32(p) - dmin * m * (double)checked32(s));
+                    if (P) P[((int64_t)v * rows + r) * ns + col0 / 32] = (int32_t)p;
+                    if (bound)
+                        for (int i = 0; i < 32; i++) {
+                            double wh = d * sc * q4k_q(blk, 32 * j + i) - dmin * m;
+                            bnd += fabs(wh) * fabs(scale * xv[col0 + i]);
+                        }
+                }
+            }
+            y[(int64_t)v * rows + r] = acc;
+            if (bound) bound[(int64_t)v * rows + r] = bnd;
+        }
+    }
+}
+
+/* Q6_K: for vector v, row r and sub-block j (16 columns, the half j%2 of
+ * activation block j/2):
+ *   P[v][r][j] = sum_i (q_i - 32) * qx_i                     (exact integer)
+ *   y[v][r]    = sum_j xd_{j/2} * d * sc_j * P               (float64)
+ * P is [nvec][rows][cols/16]; the other arrays as for Q4_K. */
+void orc_gemv_q6k(const uint8_t *bodies, const uint16_t *dplane, int64_t rows, int64_t cols,
+                  int32_t nvec, const int8_t *xq, const float *xd, int32_t *P,
+                  double *y, double *bound) {
+    if (cols % QK) die("cols must be a multiple of 256");
+    int64_t nb = cols / QK, ns = cols / 16;
+    for (int32_t v = 0; v < nvec; v++) {
+        const int8_t *xv = xq + (int64_t)v * cols;
+        const float *dv = xd + (int64_t)v * (cols / 32);
+        for (int64_t r = 0; r < rows; r++) {
+            double acc = 0.0, bnd = 0.0;
+            for (int64_t b = 0; b < nb; b++) {
+                const uint8_t *body = bodies + (r * nb + b) * Q6K_BODY;
+                double d = orc_f16_to_f32(dplane[r * nb + b]);
+                for (int j = 0; j < 16; j++) {
+                    int64_t col0 = b * QK + 16 * j;
+                    int sc = q6k_sc(body, j);
+                    int64_t p = 0;
+                    for (int i = 0; i < 16; i++)
+                        p += (int64_t)(q6k_q(body, 16 * j + i) - 32) * xv[col0 + i];
+                    double scale = dv[col0 / 32];
+                    acc += scale * d * sc * (double)checked32(p);
+                    if (P) P[((int64_t)v * rows + r) * ns + col0 / 16] = (int32_t)p;
+                    if (bound)
+                        for (int i = 0; i < 16; i++) {
+                            double wh = d * sc * (q6k_q(body, 16 * j + i) - 32);
+                            bnd += fabs(wh) * fabs(scale * xv[col0 + i]);
+                        }
+                }
+            }
+            y[(int64_t)v * rows + r] = acc;
+            if (bound) bound[(int64_t)v * rows + r] = bnd;
+        }
+    }
+}
+
+/* -------------------------------------------------------------- brute force */
+/* y[v][r] = sum_i what[r][i] * (xd_{i/32} * qx_i), float64, straight from a
+ * dequantized matrix. Checks the integer formulation above. */
+void orc_bruteforce(const double *what, int64_t rows, int64_t cols, int32_t nvec,
+                    const int8_t *xq, const float *xd, double *y) {
+    for (int32_t v = 0; v < nvec; v++)
+        for (int64_t r = 0; r < rows; r++) {
+            double acc = 0.0;
+            for (int64_t i = 0; i < cols; i++)
+                acc += what[r * cols + i] * ((double)xd[(int64_t)v * (cols / 32) + i / 32] *
+                                             xq[(int64_t)v * cols + i]);
+            y[(int64_t)v * rows + r] = acc;
+        }
+}

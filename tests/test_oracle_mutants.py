@@ -1,0 +1,139 @@
+"""Planted mistakes in the oracle must be caught by its pins.
+
+Each mutant is the oracle's C source with one plausible mistake written in (a dropped
+term, a wrong sign, a swapped index, a different rounding rule). It is compiled on the
+CPU into a temporary library and the pin checks of oracle_pins run against it in a
+child process; at least one check must fail for every mutant. The shipped oracle
+itself must pass all of them (the control case).
+"""
+
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+import oracle
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "qgemv_oracle.c")
+
+MUTANTS = {
+    "q4k_drop_min_term": (
+        "acc += scale * (d * sc * (double)checked32(p) - dmin * m * (double)checked32(s));",
+        "acc += scale * (d * sc * (double)checked32(p));"),
+    "q4k_min_sign": (
+        "acc += scale * (d * sc * (double)checked32(p) - dmin * m * (double)checked32(s));",
+        "acc += scale * (d * sc * (double)checked32(p) + dmin * m * (double)checked32(s));"),
+    "q4k_nibble_swap": (
+        "return (blk[16 + 16 * j + t] >> (4 * h)) & 15;",
+        "return (blk[16 + 16 * j + t] >> (4 * (1 - h))) & 15;"),
+    "q4k_sc_high_from_m": (
+        "int hi = (blk[12 + j / 4] >> (2 * (j % 4))) & 3;\n    return lo | (hi << 4);\n}\n\nstatic int q4k_m",
+        "int hi = (blk[14 + j / 4] >> (2 * (j % 4))) & 3;\n    return lo | (hi << 4);\n}\n\nstatic int q4k_m"),
+    "q4k_act_scale_index": (
+        "double scale = dv[col0 / 32];\n                    acc += scale * (d * sc",
+        "double scale = dv[(col0 / 32) ^ 1];\n                    acc += scale * (d * sc"),
+    "q6k_offset_31": (
+        "p += (int64_t)(q6k_q(body, 16 * j + i) - 32) * xv[col0 + i];",
+        "p += (int64_t)(q6k_q(body, 16 * j + i) - 31) * xv[col0 + i];"),
+    "q6k_high_bits_shift": (
+        "int hi = (body[128 + 8 * k + 4 * g + c] >> (2 * s)) & 3;",
+        "int hi = (body[128 + 8 * k + 4 * g + c] >> (2 * c)) & 3;"),
+    "q6k_scale_unsigned": (
+        "static int q6k_sc(const uint8_t *body, int j) { return (int)(int8_t)body[192 + j]; }",
+        "static int q6k_sc(const uint8_t *body, int j) { return (int)body[192 + j]; }"),
+    "q6k_wrong_sub_block_scale": (
+        "int sc = q6k_sc(body, j);\n                    int64_t p = 0;",
+        "int sc = q6k_sc(body, j ^ 1);\n                    int64_t p = 0;"),
+    "act_round_half_away": (
+        "float code = clampf(rintf(prod), -127.0f, 127.0f);",
+        "float code = clampf(roundf(prod), -127.0f, 127.0f);"),
+    "act_divide_instead": (
+        "float prod = xb[i] * inv;",
+        "float prod = amax > 0.0f ? xb[i] / scale : 0.0f;"),
+    "act_allow_minus_128": (
+        "float code = clampf(rintf(prod), -127.0f, 127.0f);",
+        "float code = clampf(rintf(prod * 1.004f), -128.0f, 127.0f);"),
+    "fp16_subnormal_exponent": (
+        "v = ldexpf((float)m, -24);",
+        "v = ldexpf((float)m, -25);"),
+    "fp16_round_half_up": (
+        "if (rest > half || (rest == half && (kept & 1u)))",
+        "if (rest >= half)"),
+    "q4k_quant_no_offset": (
+        "? clampf(rintf((v + off) / step), 0.0f, 15.0f) : 0.0f);",
+        "? clampf(rintf((v) / step), 0.0f, 15.0f) : 0.0f);"),
+    "q6k_quant_divisor_63": (
+        "uint16_t dh = orc_f32_to_f16(smax / 127.0f);\n            float d = orc_f16_to_f32(dh);",
+        "uint16_t dh = orc_f32_to_f16(smax / 63.0f);\n            float d = orc_f16_to_f32(dh);"),
+    "bound_drops_min": (
+        "double wh = d * sc * q4k_q(blk, 32 * j + i) - dmin * m;",
+        "double wh = d * sc * q4k_q(blk, 32 * j + i);"),
+}
+
+RUNNER = r"""
+import json, sys
+sys.path[:0] = [{root!r}, {tests!r}]
+import numpy as np
+import oracle, oracle_pins as pins
+lib = oracle.load({so!r})
+rng = np.random.default_rng(1)
+w = (rng.standard_normal((6, 512)) * 0.02).astype(np.float32)
+w2 = (rng.standard_normal((6, 512)) * 0.002).astype(np.float32)
+w3 = rng.standard_normal((6, 512)).astype(np.float32)
+x = rng.standard_normal((2, 512)).astype(np.float32)
+checks = {{
+    "fp16": lambda: pins.check_fp16(lib),
+    "layout_goldens": lambda: pins.check_layout_goldens(lib),
+    "layout_probes": lambda: pins.check_layout_probes(lib),
+    "act_cases": lambda: pins.check_act_cases(lib),
+    "act_bounds": lambda: pins.check_act_bounds(lib),
+    "q4k_quantizer": lambda: (pins.check_q4k_quantizer(lib, w), pins.check_q4k_quantizer(lib, w3),
+                              pins.check_q4k_quantizer(lib, w2)),
+    "q6k_quantizer": lambda: (pins.check_q6k_quantizer(lib, w), pins.check_q6k_quantizer(lib, w3),
+                              pins.check_q6k_quantizer(lib, w2, True)),
+    "bf_q4k": lambda: pins.check_gemv_bruteforce(lib, "q4k", w, x),
+    "bf_q6k": lambda: pins.check_gemv_bruteforce(lib, "q6k", w, x),
+    "onehot_q4k": lambda: pins.check_gemv_onehot(lib, "q4k", w),
+    "onehot_q6k": lambda: pins.check_gemv_onehot(lib, "q6k", w),
+    "special": lambda: pins.check_gemv_special(lib),
+    "extremes": lambda: pins.check_gemv_extremes(lib),
+}}
+failed = []
+for name, fn in checks.items():
+    try:
+        fn()
+    except AssertionError:
+        failed.append(name)
+print(json.dumps(failed))
+"""
+
+
+def _run(tmp_path, name, source):
+    src = tmp_path / (name + ".c")
+    src.write_text(source)
+    so = str(tmp_path / (name + ".so"))
+    oracle.build(out=so, src=str(src))
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    code = RUNNER.format(root=root, tests=os.path.join(root, "tests"), so=so)
+    proc = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300)
+    if proc.returncode != 0:
+        # a mutant that aborts (int32 range check, bad code) has been caught as well
+        return ["<crashed: %d>" % proc.returncode]
+    return json.loads(proc.stdout.strip().splitlines()[-1])
+
+
+def test_unmutated_oracle_passes_every_pin(tmp_path):
+    with open(SRC) as f:
+        assert _run(tmp_path, "control", f.read()) == []
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(tmp_path, name):
+    with open(SRC) as f:
+        text = f.read()
+    old, new = MUTANTS[name]
+    assert text.count(old) == 1, "mutation anchor not found once: %s" % name
+    failed = _run(tmp_path, name, text.replace(old, new))
+    assert failed, "no pin caught mutant %s" % name

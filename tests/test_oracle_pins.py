@@ -1,0 +1,91 @@
+"""The CPU oracle against facts fixed outside it (see oracle_pins for what pins what)."""
+
+import numpy as np
+import pytest
+from hypothesis import given, settings, strategies as st
+
+import oracle
+import oracle_pins as pins
+import synth
+
+
+def test_fp16_codec_matches_ieee_binary16(orc):
+    pins.check_fp16(orc)
+
+
+def test_layout_hand_derived_blocks(orc):
+    pins.check_layout_goldens(orc)
+
+
+def test_layout_single_field_probes(orc):
+    pins.check_layout_probes(orc)
+
+
+def test_activation_hand_worked_blocks(orc):
+    pins.check_act_cases(orc)
+
+
+def test_activation_rounding_bound_and_invariants(orc):
+    pins.check_act_bounds(orc)
+
+
+@pytest.mark.parametrize("sigma", [0.02, 0.002, 1.0])
+def test_q4k_quantizer_roundtrip(orc, sigma):
+    rng = np.random.default_rng(int(sigma * 1000) + 1)
+    w = (rng.standard_normal((16, 1024)) * sigma).astype(np.float32)
+    w[3] = np.abs(w[3])                     # all-positive rows: no offset
+    w[4] = -np.abs(w[4])                    # all-negative rows
+    w[5, :256] = 0.0                        # an all-zero super-block
+    w[6, 32:64] = np.float32(-0.01)         # a constant sub-block
+    pins.check_q4k_quantizer(orc, w)
+
+
+@pytest.mark.parametrize("negate", [False, True])
+@pytest.mark.parametrize("sigma", [0.02, 0.002, 1.0])
+def test_q6k_quantizer_roundtrip(orc, sigma, negate):
+    rng = np.random.default_rng(int(sigma * 1000) + 7)
+    w = (rng.standard_normal((16, 1024)) * sigma).astype(np.float32)
+    w[5, :256] = 0.0
+    pins.check_q6k_quantizer(orc, w, negate=negate)
+
+
+def test_q4k_subnormal_super_scale(orc):
+    """sigma 0.002 puts d below fp16's smallest normal (6.1e-5)."""
+    w = synth.normal_f32(99, 0, 8 * 512, 0.002).reshape(8, 512)
+    buf = pins.check_q4k_quantizer(orc, w)
+    d16 = buf.reshape(-1, 144)[:, 0:2].copy().view(np.uint16)[:, 0]
+    assert np.any(d16 < 0x0400)
+
+
+@pytest.mark.parametrize("wtype", ["q4k", "q6k"])
+def test_gemv_equals_bruteforce_on_random(orc, wtype):
+    rng = np.random.default_rng(3)
+    w = (rng.standard_normal((24, 768)) * 0.02).astype(np.float32)
+    x = rng.standard_normal((3, 768)).astype(np.float32)
+    pins.check_gemv_bruteforce(orc, wtype, w, x)
+
+
+@settings(max_examples=40, deadline=None)
+@given(rows=st.integers(1, 8), nb=st.integers(1, 4), nvec=st.integers(1, 3),
+       seed=st.integers(0, 2**31 - 1), wtype=st.sampled_from(["q4k", "q6k"]),
+       wscale=st.sampled_from([0.02, 0.002, 1.0, 30.0]))
+def test_gemv_equals_bruteforce_tiny(orc, rows, nb, nvec, seed, wtype, wscale):
+    rng = np.random.default_rng(seed)
+    w = (rng.standard_normal((rows, 256 * nb)) * wscale).astype(np.float32)
+    x = (rng.standard_normal((nvec, 256 * nb)) * rng.choice([1e-3, 1.0, 50.0])).astype(np.float32)
+    x[:, rng.integers(0, 256 * nb, size=40)] = 0.0
+    pins.check_gemv_bruteforce(orc, wtype, w, x)
+
+
+@pytest.mark.parametrize("wtype", ["q4k", "q6k"])
+def test_gemv_one_hot_column_extraction(orc, wtype):
+    w = synth.normal_f32(42, 0, 5 * 512, 0.02).reshape(5, 512)
+    pins.check_gemv_onehot(orc, wtype, w)
+
+
+def test_gemv_special_cases(orc):
+    pins.check_gemv_special(orc)
+
+
+def test_gemv_int32_extremes(orc):
+    pins.check_gemv_extremes(orc)
