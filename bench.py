@@ -1,0 +1,219 @@
+#!/usr/bin/env python3
+"""Benchmark of the decode hot path on one MI355X: activation quantization + Q4_K GEMV.
+
+One step = qgemv_quantize_act on the float32 activation, then the block-quantized GEMV
+y = W x on the quantized activation (every row of the hot path, on one batch of synthetic
+input). The default workload is the vocabulary projection, Q4_K W 262144 x 1536, batch 1:
+weights N(0, 0.02) with 1% of the rows scaled by 10, quantized once by the library's
+load-time quantizer; x N(0, 1).
+
+Cold weights: the weight tensor is copied until the copies total >= 640 MB and the steps
+rotate through them, so the 256 MB memory-side cache cannot hold the weights between uses
+and the reads come from HBM. Inputs are resident in HBM before the timed region.
+
+Prints ONE JSON line (rank 0, N = 1):
+  value         whole-step algorithmic bytes / step time, GB/s
+  roofline      the GEMV kernel: algorithmic bytes per launch / its average launch duration
+                (HIP events on the launch stream over a run of back-to-back launches),
+                against 8000 GB/s; traffic from the committed rocprofv3 counter summary when
+                it was taken on the current kernel source, else null
+  cpu_baseline  the CPU oracle's integer GEMV on a bounded row sample of the same workload
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+COLD_BYTES = 640 * 10**6
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="q4k_262144x1536")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--warm", action="store_true", help="reuse one weight copy (cache-warm)")
+    return ap.parse_args()
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "block_quantized_weight_act_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def load_traffic(workload: str, per_launch_bytes: int):
+    """HBM bytes per GEMV launch from the committed rocprofv3 counter summary, or None when
+    the summary is missing or was taken on other kernel sources."""
+    path = os.path.join(PROFILES, "gemv_%s_traffic.json" % workload)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def algorithmic_bytes(wl, wbytes: int) -> dict:
+    gemv = wbytes + wl.nvec * wl.cols + wl.nvec * (wl.cols // 32) * 4 + wl.nvec * wl.rows * 4
+    quant = wl.nvec * wl.cols * 4 + wl.nvec * wl.cols + wl.nvec * (wl.cols // 32) * 4
+    return {"gemv": gemv, "quantize_act": quant, "step": gemv + quant}
+
+
+def cpu_baseline(wl, seconds: float) -> dict:
+    import oracle
+    threads = max(1, min(16, os.cpu_count() or 1))
+    rows = min(wl.rows, 32768)
+    sample = np.linspace(0, wl.rows - 1, rows).astype(np.int64)
+    w = wl.weight_rows(sample)
+    wbuf = oracle.quantize_q4k(w) if wl.wtype == "q4k" else oracle.quantize_q6k(w)
+    xq, xd = oracle.quantize_act(wl.activations())
+    oracle.gemv_threaded(wl.wtype, wbuf, rows, wl.cols, xq, xd, threads)       # warm-up
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.gemv_threaded(wl.wtype, wbuf, rows, wl.cols, xq, xd, threads)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    per = el / reps
+    nbytes = wbuf.size + xq.size + xd.size * 4 + wl.nvec * rows * 4
+    return {"value": round(nbytes / per / 1e9, 3), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": "%d of %d rows (evenly spaced), full width, %d reps in %.1f s; "
+                      "integer GEMV only, weights quantized beforehand" % (rows, wl.rows, reps, el),
+            "us_per_gemv_scaled_to_full": round(per * (wl.rows / rows) * 1e6, 1)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import block_quantized_weight_act_amd as qg
+    import synth
+
+    wl = synth.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    t_setup = time.perf_counter()
+
+    # weights: generated on the host in row chunks, quantized on the GPU by the library
+    wbytes = qg.qgemv_weight_bytes(wl.wtype, wl.rows, wl.cols)
+    w0 = torch.empty(wbytes, dtype=torch.uint8, device=dev)
+    chunk = 32768
+    if wl.wtype == "q4k":
+        per_row = wbytes // wl.rows
+        for r0 in range(0, wl.rows, chunk):
+            r1 = min(wl.rows, r0 + chunk)
+            wf = torch.from_numpy(wl.weight_block(r0, r1)).to(dev)
+            qg.qgemv_quantize_weights(wl.wtype, wf, w0[r0 * per_row:r1 * per_row], r1 - r0, wl.cols)
+    else:
+        wf = torch.from_numpy(wl.weight_block(0, wl.rows)).to(dev)
+        qg.qgemv_quantize_weights(wl.wtype, wf, w0, wl.rows, wl.cols)
+    del wf
+    copies = 1 if args.warm else max(1, min(64, math.ceil(COLD_BYTES / wbytes)))
+    ws_list = [w0] + [w0.clone() for _ in range(copies - 1)]
+
+    x = torch.from_numpy(wl.activations()).to(dev)
+    xq = torch.empty((wl.nvec, wl.cols), dtype=torch.int8, device=dev)
+    xd = torch.empty((wl.nvec, wl.cols // 32), dtype=torch.float32, device=dev)
+    y = torch.empty((wl.nvec, wl.rows), dtype=torch.float32, device=dev)
+    wsb = qg.qgemv_workspace_bytes(wl.wtype, wl.rows, wl.cols, wl.nvec)
+    work = torch.empty(wsb, dtype=torch.uint8, device=dev) if wsb else None
+    plan = qg.qgemv_plan_for(wl.wtype, wl.rows, wl.cols, wl.nvec)
+    torch.cuda.synchronize()
+    setup_s = time.perf_counter() - t_setup
+
+    def quantize():
+        qg.qgemv_quantize_act(x, xq, xd, wl.cols, wl.nvec)
+
+    def gemv(i):
+        qg.qgemv_batch(wl.wtype, ws_list[i % copies], xq, xd, y, wl.rows, wl.cols, wl.nvec,
+                       workspace=work)
+
+    def step(i):
+        quantize()
+        gemv(i)
+
+    def timed(fn, n):
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        w0_ = time.perf_counter()
+        e0.record()
+        for i in range(n):
+            fn(i)
+        e1.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - w0_
+        return e0.elapsed_time(e1) / n, wall / n * 1e3
+
+    for i in range(args.warmup):
+        step(i)
+    ms_step, wall_step = timed(step, args.steps)
+    ms_gemv, _ = timed(gemv, args.steps)
+    ms_quant, _ = timed(lambda i: quantize(), args.steps)
+
+    nbytes = algorithmic_bytes(wl, wbytes)
+    value = nbytes["step"] / (ms_step * 1e-3) / 1e9
+    achieved = nbytes["gemv"] / (ms_gemv * 1e-3) / 1e9
+    traffic = load_traffic(args.workload, nbytes["gemv"])
+    out = {
+        "metric": "achieved HBM GB/s and % of roofline, Q4_K GEMV batch-1 (us per GEMV)",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8xq4k" if wl.wtype == "q4k" else "int8xq6k",
+        "data": "synthetic",
+        "config": {"workload": "%s GEMV W %dx%d, batch %d, cold weights (%d rotating copies)"
+                               % (wl.wtype.upper().replace("Q4K", "Q4_K").replace("Q6K", "Q6_K"),
+                                  wl.rows, wl.cols, wl.nvec, copies),
+                   "name": wl.name, "rows": wl.rows, "cols": wl.cols, "nvec": wl.nvec,
+                   "weight_bytes": wbytes, "plan": plan},
+        "us_per_gemv": round(ms_gemv * 1e3, 3),
+        "us_per_quantize_act": round(ms_quant * 1e3, 3),
+        "pct_of_hbm_peak": round(100 * achieved / HBM_PEAK_GBS, 2),
+        "wall_ms_per_step": round(wall_step, 5),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "kernel": "gemv_%s_kernel" % wl.wtype,
+                     "algorithmic_bytes_per_launch": nbytes["gemv"]},
+        "setup_s": round(setup_s, 1),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

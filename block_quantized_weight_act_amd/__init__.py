@@ -1,0 +1,221 @@
+"""Python binding of libqgemv (include/qgemv.h): argument marshalling only.
+
+Every function has the name and the meaning of the C entry point it calls; all work runs in
+the library's HIP kernels on the GPU. torch supplies device memory (tensors) and streams; the
+library is loaded after torch so that both share torch's HIP runtime. There is no fallback:
+if the library is not built, importing a function raises.
+
+Tensors must be CUDA (HIP) tensors, contiguous, with the dtypes the C ABI names; they are
+passed as raw device pointers. `stream=None` means torch's current stream on the tensor's
+device.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "QGEMV_Q4K", "QGEMV_Q6K", "QgemvError", "library_path", "qgemv_version",
+    "qgemv_status_string", "qgemv_weight_bytes", "qgemv_quantize_act",
+    "qgemv_workspace_bytes", "qgemv_q4k", "qgemv_q6k", "qgemv_batch", "qgemv_debug_partials",
+    "qgemv_quantize_weights", "qgemv_plan_for", "qgemv_plan_workspace_bytes", "qgemv_batch_plan",
+]
+
+QGEMV_Q4K = 1
+QGEMV_Q6K = 2
+WTYPES = {"q4k": QGEMV_Q4K, "q6k": QGEMV_Q6K}
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_HERE, "_lib", "libqgemv.so")
+
+
+class QgemvError(RuntimeError):
+    def __init__(self, fn: str, status: int, lib):
+        msg = lib.qgemv_status_string(status).decode()
+        if status == 4:
+            msg += ": " + lib.qgemv_last_error().decode()
+        super().__init__("%s failed with status %d (%s)" % (fn, status, msg))
+        self.status = status
+
+
+class Plan(ctypes.Structure):
+    _fields_ = [("lanes_per_row", ctypes.c_int32), ("chunks_per_lane", ctypes.c_int32),
+                ("waves_per_block", ctypes.c_int32), ("blocks", ctypes.c_int32),
+                ("splits", ctypes.c_int32)]
+
+    def as_dict(self):
+        return {name: int(getattr(self, name)) for name, _ in self._fields_}
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(library_path):
+        raise RuntimeError("libqgemv.so is not built (%s); run __graft_entry__.build()" % library_path)
+    lib = ctypes.CDLL(library_path)
+    vp, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+    sigs = {
+        "qgemv_version": (ctypes.c_int, []),
+        "qgemv_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+        "qgemv_last_error": (ctypes.c_char_p, []),
+        "qgemv_weight_bytes": (sz, [ctypes.c_int, i64, i64]),
+        "qgemv_quantize_act": (ctypes.c_int, [vp, vp, vp, i64, i32, vp]),
+        "qgemv_workspace_bytes": (sz, [ctypes.c_int, i64, i64, i32]),
+        "qgemv_q4k": (ctypes.c_int, [vp, vp, vp, vp, i64, i64, vp, sz, vp]),
+        "qgemv_q6k": (ctypes.c_int, [vp, vp, vp, vp, i64, i64, vp, sz, vp]),
+        "qgemv_batch": (ctypes.c_int, [ctypes.c_int, vp, vp, vp, vp, i64, i64, i32, vp, sz, vp]),
+        "qgemv_debug_partials": (ctypes.c_int, [ctypes.c_int, vp, vp, vp, vp, vp, i64, i64, i32, vp]),
+        "qgemv_quantize_weights": (ctypes.c_int, [ctypes.c_int, vp, vp, i64, i64, vp]),
+        "qgemv_plan_for": (ctypes.c_int, [ctypes.c_int, i64, i64, i32, ctypes.POINTER(Plan)]),
+        "qgemv_plan_workspace_bytes": (sz, [ctypes.POINTER(Plan), i64, i64, i32]),
+        "qgemv_batch_plan": (ctypes.c_int, [ctypes.c_int, vp, vp, vp, vp, i64, i64, i32,
+                                            ctypes.POINTER(Plan), vp, sz, vp]),
+    }
+    for name, (res, args) in sigs.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _ptr(t, dtype=None, name="tensor"):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch tensor or a device pointer" % name)
+    if t.device.type != "cuda":
+        raise ValueError("%s must be a GPU tensor, got %s" % (name, t.device))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    return t.data_ptr()
+
+
+def _stream(stream, *tensors):
+    if stream is None:
+        dev = next((t.device for t in tensors if isinstance(t, torch.Tensor)), None)
+        return torch.cuda.current_stream(dev).cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _nbytes(t):
+    return t.numel() * t.element_size() if isinstance(t, torch.Tensor) else None
+
+
+def _check(fn, status):
+    if status != 0:
+        raise QgemvError(fn, status, _load())
+
+
+def _wtype(wtype):
+    return WTYPES[wtype] if isinstance(wtype, str) else int(wtype)
+
+
+def _ws(workspace):
+    if workspace is None:
+        return None, 0
+    return _ptr(workspace, name="workspace"), _nbytes(workspace) or 0
+
+
+# ------------------------------------------------------------------ info --
+def qgemv_version() -> int:
+    return _load().qgemv_version()
+
+
+def qgemv_status_string(status: int) -> str:
+    return _load().qgemv_status_string(status).decode()
+
+
+def qgemv_weight_bytes(wtype, rows: int, cols: int) -> int:
+    return _load().qgemv_weight_bytes(_wtype(wtype), rows, cols)
+
+
+def qgemv_workspace_bytes(wtype, rows: int, cols: int, nvec: int = 1) -> int:
+    return _load().qgemv_workspace_bytes(_wtype(wtype), rows, cols, nvec)
+
+
+def qgemv_plan_for(wtype, rows: int, cols: int, nvec: int = 1) -> dict:
+    plan = Plan()
+    _check("qgemv_plan_for", _load().qgemv_plan_for(_wtype(wtype), rows, cols, nvec,
+                                                   ctypes.byref(plan)))
+    return plan.as_dict()
+
+
+def qgemv_plan_workspace_bytes(plan: dict, rows: int, cols: int, nvec: int = 1) -> int:
+    p = Plan(**{k: v for k, v in plan.items() if k in dict(Plan._fields_)})
+    return _load().qgemv_plan_workspace_bytes(ctypes.byref(p), rows, cols, nvec)
+
+
+# ------------------------------------------------------------- compute --
+def qgemv_quantize_act(x, xq, xd, cols: int, nvec: int = 1, stream=None) -> None:
+    """x float32 [nvec][cols] -> xq int8 [nvec][cols], xd float32 [nvec][cols/32]."""
+    lib = _load()
+    _check("qgemv_quantize_act", lib.qgemv_quantize_act(
+        _ptr(x, torch.float32, "x"), _ptr(xq, torch.int8, "xq"), _ptr(xd, torch.float32, "xd"),
+        cols, nvec, _stream(stream, x)))
+
+
+def qgemv_q4k(w, xq, xd, y, rows: int, cols: int, workspace=None, stream=None) -> None:
+    lib = _load()
+    wsp, wsb = _ws(workspace)
+    _check("qgemv_q4k", lib.qgemv_q4k(
+        _ptr(w, name="w"), _ptr(xq, torch.int8, "xq"), _ptr(xd, torch.float32, "xd"),
+        _ptr(y, torch.float32, "y"), rows, cols, wsp, wsb, _stream(stream, y)))
+
+
+def qgemv_q6k(w, xq, xd, y, rows: int, cols: int, workspace=None, stream=None) -> None:
+    lib = _load()
+    wsp, wsb = _ws(workspace)
+    _check("qgemv_q6k", lib.qgemv_q6k(
+        _ptr(w, name="w"), _ptr(xq, torch.int8, "xq"), _ptr(xd, torch.float32, "xd"),
+        _ptr(y, torch.float32, "y"), rows, cols, wsp, wsb, _stream(stream, y)))
+
+
+def qgemv_batch(wtype, w, xq, xd, y, rows: int, cols: int, nvec: int, workspace=None,
+                stream=None) -> None:
+    lib = _load()
+    wsp, wsb = _ws(workspace)
+    _check("qgemv_batch", lib.qgemv_batch(
+        _wtype(wtype), _ptr(w, name="w"), _ptr(xq, torch.int8, "xq"),
+        _ptr(xd, torch.float32, "xd"), _ptr(y, torch.float32, "y"), rows, cols, nvec, wsp, wsb,
+        _stream(stream, y)))
+
+
+def qgemv_batch_plan(wtype, w, xq, xd, y, rows: int, cols: int, nvec: int, plan: dict,
+                     workspace=None, stream=None) -> None:
+    lib = _load()
+    wsp, wsb = _ws(workspace)
+    p = Plan(**{k: v for k, v in plan.items() if k in dict(Plan._fields_)})
+    _check("qgemv_batch_plan", lib.qgemv_batch_plan(
+        _wtype(wtype), _ptr(w, name="w"), _ptr(xq, torch.int8, "xq"),
+        _ptr(xd, torch.float32, "xd"), _ptr(y, torch.float32, "y"), rows, cols, nvec,
+        ctypes.byref(p), wsp, wsb, _stream(stream, y)))
+
+
+def qgemv_debug_partials(wtype, w, xq, xd, P, S, rows: int, cols: int, nvec: int = 1,
+                         stream=None) -> None:
+    lib = _load()
+    _check("qgemv_debug_partials", lib.qgemv_debug_partials(
+        _wtype(wtype), _ptr(w, name="w"), _ptr(xq, torch.int8, "xq"),
+        _ptr(xd, torch.float32, "xd"), _ptr(P, torch.int32, "P"), _ptr(S, torch.int32, "S"),
+        rows, cols, nvec, _stream(stream, P)))
+
+
+def qgemv_quantize_weights(wtype, w, out, rows: int, cols: int, stream=None) -> None:
+    lib = _load()
+    _check("qgemv_quantize_weights", lib.qgemv_quantize_weights(
+        _wtype(wtype), _ptr(w, torch.float32, "w"), _ptr(out, name="out"), rows, cols,
+        _stream(stream, out)))

@@ -1,0 +1,304 @@
+// C ABI of libqgemv: argument checks, the per-shape launch plan, and launches on the
+// caller's stream. Declared in include/qgemv.h, which states each operation, its layouts,
+// ownership and error behaviour.
+#include <qgemv.h>
+
+#include <algorithm>
+#include <cstdint>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+
+#include "qgemv_internal.h"
+
+namespace {
+
+using namespace qgemv;
+
+thread_local char g_last_error[256] = "";
+
+int hip_fail(hipError_t e) {
+    std::snprintf(g_last_error, sizeof g_last_error, "%s: %s", hipGetErrorName(e),
+                  hipGetErrorString(e));
+    return QGEMV_EHIP;
+}
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+    return a0 < b0 + nb && b0 < a0 + na;
+}
+
+size_t weight_bytes(int wtype, int64_t rows, int64_t cols) {
+    const int64_t nblocks = rows * (cols / kQK);
+    if (wtype == QGEMV_Q4K) return static_cast<size_t>(nblocks) * kQ4KBytes;
+    if (wtype == QGEMV_Q6K) return static_cast<size_t>(nblocks) * (kQ6KBody + 2);
+    return 0;
+}
+
+bool shape_ok(int64_t rows, int64_t cols, int32_t nvec) {
+    if (rows < 1 || cols < kQK || cols % kQK != 0 || nvec < 1 || nvec > kMaxVec) return false;
+    if (rows > INT32_MAX || cols > (int64_t{1} << 30)) return false;
+    return rows * (cols / kQK) < (int64_t{1} << 31);
+}
+
+bool variant_exists(int lanes, int chunks, int nvec) {
+    const bool lanes_ok = lanes == 8 || lanes == 16 || lanes == 32 || lanes == 64;
+    return lanes_ok && chunks >= 1 && chunks <= 4 && nvec >= 1 && nvec <= kMaxVec &&
+           nvec * chunks <= 8;
+}
+
+int splits_for(int lanes, int chunks, int64_t cols) {
+    const int64_t nchunks = cols / 32;
+    const int64_t per = static_cast<int64_t>(lanes) * chunks;
+    return static_cast<int>((nchunks + per - 1) / per);
+}
+
+// Resident wavefronts the launch aims for: 256 CUs x 16 waves. Enough to keep several
+// kilobytes of weight loads in flight per CU; more waves only re-read the activation slice.
+constexpr int64_t kTargetWaves = 256 * 16;
+
+// The per-shape plan. Lanes per row T and chunks per lane NC are chosen so that one pass of a
+// wave covers a row's chunks with the least idle lanes, preferring more chunks per lane
+// (more 16-byte loads in flight per lane) while the activation slice fits in VGPRs
+// (nvec * NC <= 8). When a row has more than 256 chunks (cols > 8192) or rows alone are too
+// few to give every CU work, the columns are split.
+qgemv_plan make_plan(int wtype, int64_t rows, int64_t cols, int32_t nvec) {
+    (void)wtype;
+    const int64_t nchunks = cols / 32;
+    int best_t = 64, best_nc = 1;
+    double best_cost = 1e30;
+    for (int nc = 1; nc <= 4; nc++) {
+        if (nvec * nc > 8) break;
+        for (int t : {8, 16, 32, 64}) {
+            const int64_t per = static_cast<int64_t>(t) * nc;
+            const int64_t passes = (nchunks + per - 1) / per;
+            const double waste = 1.0 - static_cast<double>(nchunks) / (passes * per);
+            // idle lanes cost bandwidth in flight; split passes cost a workspace round trip
+            const double cost = waste + 0.02 * (passes - 1) - 0.01 * nc;
+            if (cost < best_cost - 1e-12) {
+                best_cost = cost;
+                best_t = t;
+                best_nc = nc;
+            }
+        }
+    }
+    qgemv_plan p{};
+    p.lanes_per_row = best_t;
+    p.chunks_per_lane = best_nc;
+    p.waves_per_block = 4;
+    int splits = splits_for(best_t, best_nc, cols);
+    // Too few rows to fill the GPU: split further (whole chunks per lane kept).
+    const int64_t rows_per_wave = 64 / best_t;
+    int64_t waves = (rows + rows_per_wave - 1) / rows_per_wave * splits;
+    while (waves < kTargetWaves / 2 && best_nc > 1) {
+        best_nc--;
+        splits = splits_for(best_t, best_nc, cols);
+        waves = (rows + rows_per_wave - 1) / rows_per_wave * splits;
+    }
+    p.chunks_per_lane = best_nc;
+    p.splits = splits;
+    const int64_t groups = (rows + rows_per_wave - 1) / rows_per_wave;
+    const int64_t waves_per_split = std::max<int64_t>(1, kTargetWaves / splits);
+    const int64_t want = std::min(groups, waves_per_split);
+    p.blocks = static_cast<int32_t>(std::max<int64_t>(1, (want + p.waves_per_block - 1) /
+                                                             p.waves_per_block));
+    return p;
+}
+
+bool plan_ok(const qgemv_plan &p, int32_t nvec) {
+    return variant_exists(p.lanes_per_row, p.chunks_per_lane, nvec) && p.waves_per_block >= 1 &&
+           p.waves_per_block <= 4 && p.blocks >= 1 && p.blocks <= 65535 * 64;
+}
+
+size_t plan_ws_bytes(const qgemv_plan &p, int64_t rows, int64_t cols, int32_t nvec) {
+    const int splits = splits_for(p.lanes_per_row, p.chunks_per_lane, cols);
+    if (splits <= 1) return 0;
+    return static_cast<size_t>(splits) * nvec * rows * sizeof(float);
+}
+
+int check_gemv_args(int wtype, const void *w, const int8_t *xq, const float *xd, const void *out,
+                    size_t out_bytes, int64_t rows, int64_t cols, int32_t nvec) {
+    if (wtype != QGEMV_Q4K && wtype != QGEMV_Q6K) return QGEMV_EINVAL;
+    if (!w || !xq || !xd || !out) return QGEMV_EINVAL;
+    if (!shape_ok(rows, cols, nvec)) return QGEMV_EINVAL;
+    if (!aligned(w, 16) || !aligned(xq, 16) || !aligned(xd, 4) || !aligned(out, 4))
+        return QGEMV_EALIGN;
+    const size_t wb = weight_bytes(wtype, rows, cols);
+    const size_t xqb = static_cast<size_t>(nvec) * cols;
+    const size_t xdb = static_cast<size_t>(nvec) * (cols / 32) * sizeof(float);
+    if (overlaps(out, out_bytes, w, wb) || overlaps(out, out_bytes, xq, xqb) ||
+        overlaps(out, out_bytes, xd, xdb))
+        return QGEMV_EINVAL;
+    return QGEMV_OK;
+}
+
+int run_gemv(int wtype, const void *w, const int8_t *xq, const float *xd, float *y, int64_t rows,
+             int64_t cols, int32_t nvec, const qgemv_plan &plan_in, void *ws, size_t ws_bytes,
+             hipStream_t stream) {
+    const size_t ybytes = static_cast<size_t>(nvec) * rows * sizeof(float);
+    int st = check_gemv_args(wtype, w, xq, xd, y, ybytes, rows, cols, nvec);
+    if (st != QGEMV_OK) return st;
+    if (!plan_ok(plan_in, nvec)) return QGEMV_EINVAL;
+    qgemv_plan plan = plan_in;
+    plan.splits = splits_for(plan.lanes_per_row, plan.chunks_per_lane, cols);
+    const size_t need = plan_ws_bytes(plan, rows, cols, nvec);
+    if (need > 0) {
+        if (!ws || ws_bytes < need) return QGEMV_EWORKSPACE;
+        if (!aligned(ws, 4)) return QGEMV_EALIGN;
+        const size_t wb = weight_bytes(wtype, rows, cols);
+        if (overlaps(ws, need, w, wb) || overlaps(ws, need, y, ybytes) ||
+            overlaps(ws, need, xq, static_cast<size_t>(nvec) * cols) ||
+            overlaps(ws, need, xd, static_cast<size_t>(nvec) * (cols / 32) * sizeof(float)))
+            return QGEMV_EINVAL;
+    }
+    GemvArgs a{};
+    a.w = static_cast<const uint8_t *>(w);
+    a.xq = xq;
+    a.xd = xd;
+    a.out = need > 0 ? static_cast<float *>(ws) : y;
+    a.rows = static_cast<int32_t>(rows);
+    a.nb = static_cast<int32_t>(cols / kQK);
+    a.nchunks = static_cast<int32_t>(cols / 32);
+    LaunchShape s{plan.lanes_per_row, plan.chunks_per_lane, plan.waves_per_block, plan.blocks,
+                  plan.splits};
+    hipError_t e = wtype == QGEMV_Q4K ? launch_gemv_q4k(a, s, nvec, false, stream)
+                                      : launch_gemv_q6k(a, s, nvec, false, stream);
+    if (e != hipSuccess) return hip_fail(e);
+    if (need > 0) {
+        e = launch_splitk_reduce(static_cast<const float *>(ws), y, static_cast<int64_t>(nvec) * rows,
+                                 plan.splits, stream);
+        if (e != hipSuccess) return hip_fail(e);
+    }
+    return QGEMV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int qgemv_version(void) { return 100; }
+
+const char *qgemv_status_string(int status) {
+    switch (status) {
+        case QGEMV_OK: return "ok";
+        case QGEMV_EINVAL: return "invalid argument (null pointer, shape, type or overlap)";
+        case QGEMV_EALIGN: return "pointer not aligned as required";
+        case QGEMV_EWORKSPACE: return "workspace missing or too small";
+        case QGEMV_EHIP: return "HIP runtime error (see qgemv_last_error)";
+        default: return "unknown status";
+    }
+}
+
+const char *qgemv_last_error(void) { return g_last_error; }
+
+size_t qgemv_weight_bytes(int wtype, int64_t rows, int64_t cols) {
+    if (!shape_ok(rows, cols, 1)) return 0;
+    return weight_bytes(wtype, rows, cols);
+}
+
+int qgemv_quantize_act(const float *x, int8_t *xq, float *xd, int64_t cols, int32_t nvec,
+                       hipStream_t stream) {
+    if (!x || !xq || !xd || cols < 32 || cols % 32 != 0 || nvec < 1) return QGEMV_EINVAL;
+    if (cols * static_cast<int64_t>(nvec) > (int64_t{1} << 34)) return QGEMV_EINVAL;
+    if (!aligned(x, 16) || !aligned(xq, 4) || !aligned(xd, 4)) return QGEMV_EALIGN;
+    const size_t n = static_cast<size_t>(cols) * nvec;
+    if (overlaps(xq, n, x, n * 4) || overlaps(xd, n / 8, x, n * 4) || overlaps(xq, n, xd, n / 8))
+        return QGEMV_EINVAL;
+    const hipError_t e = launch_quantize_act(x, xq, xd, static_cast<int64_t>(n / 32), stream);
+    return e == hipSuccess ? QGEMV_OK : hip_fail(e);
+}
+
+size_t qgemv_workspace_bytes(int wtype, int64_t rows, int64_t cols, int32_t nvec) {
+    if ((wtype != QGEMV_Q4K && wtype != QGEMV_Q6K) || !shape_ok(rows, cols, nvec)) return 0;
+    return plan_ws_bytes(make_plan(wtype, rows, cols, nvec), rows, cols, nvec);
+}
+
+int qgemv_plan_for(int wtype, int64_t rows, int64_t cols, int32_t nvec, qgemv_plan *plan) {
+    if (!plan || (wtype != QGEMV_Q4K && wtype != QGEMV_Q6K) || !shape_ok(rows, cols, nvec))
+        return QGEMV_EINVAL;
+    *plan = make_plan(wtype, rows, cols, nvec);
+    return QGEMV_OK;
+}
+
+size_t qgemv_plan_workspace_bytes(const qgemv_plan *plan, int64_t rows, int64_t cols,
+                                  int32_t nvec) {
+    if (!plan || !shape_ok(rows, cols, nvec) || !plan_ok(*plan, nvec)) return 0;
+    return plan_ws_bytes(*plan, rows, cols, nvec);
+}
+
+int qgemv_batch_plan(int wtype, const void *w, const int8_t *xq, const float *xd, float *y,
+                     int64_t rows, int64_t cols, int32_t nvec, const qgemv_plan *plan,
+                     void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (!plan) return QGEMV_EINVAL;
+    return run_gemv(wtype, w, xq, xd, y, rows, cols, nvec, *plan, workspace, workspace_bytes,
+                    stream);
+}
+
+int qgemv_batch(int wtype, const void *w, const int8_t *xq, const float *xd, float *y,
+                int64_t rows, int64_t cols, int32_t nvec, void *workspace,
+                size_t workspace_bytes, hipStream_t stream) {
+    if ((wtype != QGEMV_Q4K && wtype != QGEMV_Q6K) || !shape_ok(rows, cols, nvec))
+        return QGEMV_EINVAL;
+    return run_gemv(wtype, w, xq, xd, y, rows, cols, nvec, make_plan(wtype, rows, cols, nvec),
+                    workspace, workspace_bytes, stream);
+}
+
+int qgemv_q4k(const void *w, const int8_t *xq, const float *xd, float *y, int64_t rows,
+              int64_t cols, void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    return qgemv_batch(QGEMV_Q4K, w, xq, xd, y, rows, cols, 1, workspace, workspace_bytes, stream);
+}
+
+int qgemv_q6k(const void *w, const int8_t *xq, const float *xd, float *y, int64_t rows,
+              int64_t cols, void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    return qgemv_batch(QGEMV_Q6K, w, xq, xd, y, rows, cols, 1, workspace, workspace_bytes, stream);
+}
+
+int qgemv_debug_partials(int wtype, const void *w, const int8_t *xq, const float *xd,
+                         int32_t *P, int32_t *S, int64_t rows, int64_t cols, int32_t nvec,
+                         hipStream_t stream) {
+    if (!P || !S) return QGEMV_EINVAL;
+    const int64_t nsub = wtype == QGEMV_Q6K ? cols / 16 : cols / 32;
+    const size_t pbytes = static_cast<size_t>(nvec) * rows * nsub * sizeof(int32_t);
+    int st = check_gemv_args(wtype, w, xq, xd, P, pbytes, rows, cols, nvec);
+    if (st != QGEMV_OK) return st;
+    const size_t sbytes = static_cast<size_t>(nvec) * (cols / 32) * sizeof(int32_t);
+    if (!aligned(S, 4)) return QGEMV_EALIGN;
+    if (overlaps(S, sbytes, P, pbytes) || overlaps(S, sbytes, w, weight_bytes(wtype, rows, cols)) ||
+        overlaps(S, sbytes, xq, static_cast<size_t>(nvec) * cols))
+        return QGEMV_EINVAL;
+    // The production plan's kernel instance with the debug stores on; it writes no y.
+    qgemv_plan plan = make_plan(wtype, rows, cols, nvec);
+    GemvArgs a{};
+    a.w = static_cast<const uint8_t *>(w);
+    a.xq = xq;
+    a.xd = xd;
+    a.out = nullptr;
+    a.P = P;
+    a.S = S;
+    a.rows = static_cast<int32_t>(rows);
+    a.nb = static_cast<int32_t>(cols / kQK);
+    a.nchunks = static_cast<int32_t>(cols / 32);
+    LaunchShape s{plan.lanes_per_row, plan.chunks_per_lane, plan.waves_per_block, plan.blocks,
+                  splits_for(plan.lanes_per_row, plan.chunks_per_lane, cols)};
+    const hipError_t e = wtype == QGEMV_Q4K ? launch_gemv_q4k(a, s, nvec, true, stream)
+                                            : launch_gemv_q6k(a, s, nvec, true, stream);
+    return e == hipSuccess ? QGEMV_OK : hip_fail(e);
+}
+
+int qgemv_quantize_weights(int wtype, const float *w, void *out, int64_t rows, int64_t cols,
+                           hipStream_t stream) {
+    if ((wtype != QGEMV_Q4K && wtype != QGEMV_Q6K) || !w || !out || !shape_ok(rows, cols, 1))
+        return QGEMV_EINVAL;
+    if (!aligned(w, 16) || !aligned(out, 16)) return QGEMV_EALIGN;
+    const size_t ob = weight_bytes(wtype, rows, cols);
+    if (overlaps(out, ob, w, static_cast<size_t>(rows) * cols * sizeof(float))) return QGEMV_EINVAL;
+    const hipError_t e =
+        wtype == QGEMV_Q4K
+            ? launch_quantize_q4k(w, static_cast<uint8_t *>(out), rows, cols, stream)
+            : launch_quantize_q6k(w, static_cast<uint8_t *>(out), rows, cols, stream);
+    return e == hipSuccess ? QGEMV_OK : hip_fail(e);
+}
+
+}  // extern "C"

@@ -1,0 +1,208 @@
+// Q4_K weight x int8 activation GEMV for gfx950.
+//
+// genie-ai-runtime (jared-hpc.com), "The decode arc": the Q4_K matrix-vector product is done
+// with int8 4-way dot products instead of dequantizing to floating point, the 4-bit codes are
+// handled as whole 32-bit words, and a row is shared by the lanes of one warp. "v1.3.0": when
+// rows alone cannot fill the GPU, split the reduction dimension and sum the pieces in a
+// separate pass. Here, for a 64-lane gfx950 wavefront:
+//
+//  * A row is cut into 16-byte chunks of codes. In the Q4_K layout one chunk is exactly one
+//    32-column sub-block j, so a lane owns whole sub-blocks: its integer partial
+//    P = sum q * xq is exact inside the lane, its low nibbles meet activation bytes 0..15
+//    and its high nibbles bytes 16..31 of the same activation block (4 codes per
+//    v_dot4_i32_i8 after one AND / shift of a 32-bit word).
+//  * T consecutive lanes share a row; lane t takes chunks t, t + T, ... (NC of them), so its
+//    columns are the same for every row it visits: the activation codes, scales and block
+//    sums it needs stay in VGPRs for the whole kernel and are read from memory once.
+//  * 8 consecutive lanes read the 128 code bytes of one super-block with one 16-byte load
+//    each (a contiguous 128-byte run); the 16-byte header (d, dmin, packed 6-bit scales) is
+//    one more 16-byte load, the same address for those 8 lanes.
+//  * After the chunks of a row, the T lanes' float sums are combined with a log2(T)-step
+//    butterfly; lane t < nvec writes vector t's output.
+//  * Waves walk row groups with a grid-wide stride. blockIdx.y selects a column chunk
+//    (split-K) whose partial sums go to a workspace that a second kernel adds in order.
+//
+// The float32 work per sub-block is xd * (d * (sc * P) - dmin * (m * S)): sc * P and m * S
+// are exact integers below 2^24. The two products can nearly cancel (a dequantized weight
+// d sc q - dmin m close to 0), so the difference is formed with the exact rounding error of
+// the min product (a TwoProduct through fmaf) and carries a relative error of about two
+// float32 roundings of the sub-block's own value; a sub-block whose dequantized weights
+// times activations are all zero contributes exactly zero. The library is built with
+// -ffp-contract=off: every fused multiply-add is an explicit fmaf.
+#include "device_common.h"
+#include "qgemv_internal.h"
+
+namespace qgemv {
+
+template <int V, int T, int NC, bool DBG>
+__global__ void __launch_bounds__(256) gemv_q4k_kernel(GemvArgs a) {
+    constexpr int RPW = 64 / T;              // rows per wave step
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int wpb = blockDim.x >> 6;
+    const int t = lane & (T - 1);
+    const int rsub = lane / T;
+    const int split = blockIdx.y;
+    const int j = t & 7;                     // sub-block inside the super-block
+    const int nsub = a.nchunks;              // 32-column blocks per row
+    const int64_t cols = static_cast<int64_t>(nsub) * 32;
+
+    int g[NC];
+    bool cv[NC];
+#pragma unroll
+    for (int k = 0; k < NC; k++) {
+        g[k] = split * T * NC + t + T * k;
+        cv[k] = g[k] < nsub;
+    }
+
+    // This lane's activation slice: 32 codes, the block scale and the block code sum per chunk.
+    uint32_t xw[V][NC][8];
+    float xs[V][NC];
+    int xsum[V][NC];
+#pragma unroll
+    for (int v = 0; v < V; v++) {
+#pragma unroll
+        for (int k = 0; k < NC; k++) {
+            uint4 lo = make_uint4(0, 0, 0, 0), hi = make_uint4(0, 0, 0, 0);
+            float s = 0.0f;
+            if (cv[k]) {
+                const int8_t *p = a.xq + v * cols + 32 * static_cast<int64_t>(g[k]);
+                lo = load16(p);
+                hi = load16(p + 16);
+                s = a.xd[static_cast<int64_t>(v) * nsub + g[k]];
+            }
+            xw[v][k][0] = lo.x; xw[v][k][1] = lo.y; xw[v][k][2] = lo.z; xw[v][k][3] = lo.w;
+            xw[v][k][4] = hi.x; xw[v][k][5] = hi.y; xw[v][k][6] = hi.z; xw[v][k][7] = hi.w;
+            xs[v][k] = s;
+            int sum = 0;
+#pragma unroll
+            for (int i = 0; i < 8; i++) sum = byte_sum(xw[v][k][i], sum);
+            xsum[v][k] = sum;
+            if (DBG && cv[k] && blockIdx.x == 0 && wave == 0 && rsub == 0)
+                a.S[static_cast<int64_t>(v) * nsub + g[k]] = sum;
+        }
+    }
+
+    const int groups = (a.rows + RPW - 1) / RPW;
+    const int stride = gridDim.x * wpb;
+    for (int grp = blockIdx.x * wpb + wave; grp < groups; grp += stride) {
+        const int row = grp * RPW + rsub;
+        const bool rv = row < a.rows;
+        uint4 hdr[NC], qs[NC];
+#pragma unroll
+        for (int k = 0; k < NC; k++) {
+            hdr[k] = make_uint4(0, 0, 0, 0);
+            qs[k] = make_uint4(0, 0, 0, 0);
+            if (rv && cv[k]) {
+                const uint8_t *blk =
+                    a.w + (static_cast<int64_t>(row) * a.nb + (g[k] >> 3)) * kQ4KBytes;
+                hdr[k] = load16(blk);
+                qs[k] = load16(blk + 16 + 16 * j);
+            }
+        }
+        float acc[V];
+#pragma unroll
+        for (int v = 0; v < V; v++) acc[v] = 0.0f;
+#pragma unroll
+        for (int k = 0; k < NC; k++) {
+            const float d = half_to_float(hdr[k].x & 0xFFFFu);
+            const float dmin = half_to_float(hdr[k].x >> 16);
+            const int sc = static_cast<int>(((hdr[k].y >> (4 * j)) & 15u) |
+                                            (((hdr[k].w >> (2 * j)) & 3u) << 4));
+            const int m = static_cast<int>(((hdr[k].z >> (4 * j)) & 15u) |
+                                           (((hdr[k].w >> (16 + 2 * j)) & 3u) << 4));
+            const uint32_t q[4] = {qs[k].x, qs[k].y, qs[k].z, qs[k].w};
+            uint32_t lo[4], hi[4];
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                lo[i] = q[i] & 0x0F0F0F0Fu;
+                hi[i] = (q[i] >> 4) & 0x0F0F0F0Fu;
+            }
+#pragma unroll
+            for (int v = 0; v < V; v++) {
+                int P = 0;
+#pragma unroll
+                for (int i = 0; i < 4; i++) {
+                    P = dot4(lo[i], xw[v][k][i], P);
+                    P = dot4(hi[i], xw[v][k][4 + i], P);
+                }
+                // d * (sc P) - dmin * (m S) rounded once: pb is the rounded min product and
+                // eb its exact rounding error, so fmaf(d, sc P, -pb) - eb is the exact
+                // difference up to two roundings of quantities no larger than the result
+                // (plus eps^2 |pb|); a sub-block whose terms cancel keeps its relative accuracy.
+                const float fscp = static_cast<float>(sc * P);
+                const float fms = static_cast<float>(m * xsum[v][k]);
+                const float pb = dmin * fms;
+                const float eb = fmaf(dmin, fms, -pb);
+                const float diff = fmaf(d, fscp, -pb) - eb;
+                acc[v] = fmaf(xs[v][k], diff, acc[v]);
+                if (DBG && rv && cv[k])
+                    a.P[(static_cast<int64_t>(v) * a.rows + row) * nsub + g[k]] = P;
+            }
+        }
+#pragma unroll
+        for (int v = 0; v < V; v++) acc[v] = group_sum<T>(acc[v]);
+        if (!DBG && rv && t < V) {   // the debug variant writes P and S only
+            float o = acc[0];
+#pragma unroll
+            for (int v = 1; v < V; v++)
+                if (t == v) o = acc[v];
+            a.out[(static_cast<int64_t>(split) * V + t) * a.rows + row] = o;
+        }
+    }
+}
+
+namespace {
+
+using Launcher = hipError_t (*)(const GemvArgs &, const LaunchShape &, bool, hipStream_t);
+
+template <int V, int T, int NC>
+hipError_t launch_variant(const GemvArgs &a, const LaunchShape &s, bool debug,
+                          hipStream_t stream) {
+    const dim3 grid(static_cast<unsigned>(s.blocks), static_cast<unsigned>(s.splits));
+    const dim3 block(static_cast<unsigned>(64 * s.waves));
+    if (debug)
+        hipLaunchKernelGGL((gemv_q4k_kernel<V, T, NC, true>), grid, block, 0, stream, a);
+    else
+        hipLaunchKernelGGL((gemv_q4k_kernel<V, T, NC, false>), grid, block, 0, stream, a);
+    return hipGetLastError();
+}
+
+template <int V, int T, int NC>
+constexpr Launcher pick() {
+    if constexpr (V * NC <= 8)
+        return &launch_variant<V, T, NC>;
+    else
+        return nullptr;
+}
+
+#define QGEMV_NC_ROW(V, T) {pick<V, T, 1>(), pick<V, T, 2>(), pick<V, T, 3>(), pick<V, T, 4>()}
+#define QGEMV_T_ROW(V) \
+    {QGEMV_NC_ROW(V, 8), QGEMV_NC_ROW(V, 16), QGEMV_NC_ROW(V, 32), QGEMV_NC_ROW(V, 64)}
+const Launcher kTable[8][4][4] = {QGEMV_T_ROW(1), QGEMV_T_ROW(2), QGEMV_T_ROW(3), QGEMV_T_ROW(4),
+                                  QGEMV_T_ROW(5), QGEMV_T_ROW(6), QGEMV_T_ROW(7), QGEMV_T_ROW(8)};
+#undef QGEMV_T_ROW
+#undef QGEMV_NC_ROW
+
+int lanes_index(int lanes) {
+    switch (lanes) {
+        case 8: return 0;
+        case 16: return 1;
+        case 32: return 2;
+        case 64: return 3;
+        default: return -1;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_gemv_q4k(const GemvArgs &a, const LaunchShape &s, int nvec, bool debug,
+                           hipStream_t stream) {
+    const int ti = lanes_index(s.lanes);
+    if (nvec < 1 || nvec > 8 || ti < 0 || s.chunks < 1 || s.chunks > 4) return hipErrorInvalidValue;
+    const Launcher fn = kTable[nvec - 1][ti][s.chunks - 1];
+    if (!fn) return hipErrorInvalidValue;
+    return fn(a, s, debug, stream);
+}
+
+}  // namespace qgemv

@@ -1,0 +1,203 @@
+// Q6_K weight x int8 activation GEMV for gfx950.
+//
+// genie-ai-runtime (jared-hpc.com), "The decode arc": int8 4-way dot-product mat-vec for
+// Q6_K; "v1.3.0": split the reduction dimension when rows alone cannot fill the GPU.
+//
+// Same lane geometry as the Q4_K kernel: a 16-byte chunk of the low-bit plane holds the low
+// 4 bits of one 32-column activation block (sub-blocks 2k and 2k+1 of the super-block, in
+// the low and high nibbles), the 8 matching bytes of the high-bit plane hold their high 2
+// bits arranged so that one shift and mask of a 32-bit word lines them up under the 4 codes
+// of the matching low-bit word. A lane rebuilds 4 codes q in [0, 63] per word with
+// AND / shift / OR, takes v_dot4_i32_i8 against the activation codes and removes the offset
+// of 32 afterwards: sum (q - 32) * x = sum q * x - 32 * sum x, with the activation sums of
+// each 16-column half kept in VGPRs. All integer work is exact: |sc * P| < 2^23 per
+// sub-block and the sum over the two sub-blocks of a chunk stays below 2^24, so its
+// float32 conversion is exact as well.
+//
+// The 208-byte bodies are 16-byte aligned because the fp16 super-scales live in their own
+// plane after the bodies, so every load here is a naturally aligned 16-, 8-, 4- or 2-byte
+// load.
+#include "device_common.h"
+#include "qgemv_internal.h"
+
+namespace qgemv {
+
+template <int V, int T, int NC, bool DBG>
+__global__ void __launch_bounds__(256) gemv_q6k_kernel(GemvArgs a) {
+    constexpr int RPW = 64 / T;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int wpb = blockDim.x >> 6;
+    const int t = lane & (T - 1);
+    const int rsub = lane / T;
+    const int split = blockIdx.y;
+    const int kk = t & 7;                    // chunk inside the super-block
+    const int nsub = a.nchunks;              // 32-column blocks per row
+    const int64_t cols = static_cast<int64_t>(nsub) * 32;
+    const uint16_t *dplane = reinterpret_cast<const uint16_t *>(
+        a.w + static_cast<int64_t>(a.rows) * a.nb * kQ6KBody);
+
+    int g[NC];
+    bool cv[NC];
+#pragma unroll
+    for (int k = 0; k < NC; k++) {
+        g[k] = split * T * NC + t + T * k;
+        cv[k] = g[k] < nsub;
+    }
+
+    uint32_t xw[V][NC][8];
+    float xs[V][NC];
+    int xlo[V][NC], xhi[V][NC];             // activation code sums of the two 16-column halves
+#pragma unroll
+    for (int v = 0; v < V; v++) {
+#pragma unroll
+        for (int k = 0; k < NC; k++) {
+            uint4 lo = make_uint4(0, 0, 0, 0), hi = make_uint4(0, 0, 0, 0);
+            float s = 0.0f;
+            if (cv[k]) {
+                const int8_t *p = a.xq + v * cols + 32 * static_cast<int64_t>(g[k]);
+                lo = load16(p);
+                hi = load16(p + 16);
+                s = a.xd[static_cast<int64_t>(v) * nsub + g[k]];
+            }
+            xw[v][k][0] = lo.x; xw[v][k][1] = lo.y; xw[v][k][2] = lo.z; xw[v][k][3] = lo.w;
+            xw[v][k][4] = hi.x; xw[v][k][5] = hi.y; xw[v][k][6] = hi.z; xw[v][k][7] = hi.w;
+            xs[v][k] = s;
+            int s0 = 0, s1 = 0;
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                s0 = byte_sum(xw[v][k][i], s0);
+                s1 = byte_sum(xw[v][k][4 + i], s1);
+            }
+            xlo[v][k] = s0;
+            xhi[v][k] = s1;
+            if (DBG && cv[k] && blockIdx.x == 0 && wave == 0 && rsub == 0)
+                a.S[static_cast<int64_t>(v) * nsub + g[k]] = s0 + s1;
+        }
+    }
+
+    const int groups = (a.rows + RPW - 1) / RPW;
+    const int stride = gridDim.x * wpb;
+    for (int grp = blockIdx.x * wpb + wave; grp < groups; grp += stride) {
+        const int row = grp * RPW + rsub;
+        const bool rv = row < a.rows;
+        uint4 ql[NC];
+        uint2 qh[NC];
+        uint32_t scw[NC];
+        uint32_t dbits[NC];
+#pragma unroll
+        for (int k = 0; k < NC; k++) {
+            ql[k] = make_uint4(0, 0, 0, 0);
+            qh[k] = make_uint2(0, 0);
+            scw[k] = 0;
+            dbits[k] = 0;
+            if (rv && cv[k]) {
+                const int64_t b = static_cast<int64_t>(row) * a.nb + (g[k] >> 3);
+                const uint8_t *body = a.w + b * kQ6KBody;
+                ql[k] = load16(body + 16 * kk);
+                qh[k] = *reinterpret_cast<const uint2 *>(body + 128 + 8 * kk);
+                scw[k] = *reinterpret_cast<const uint32_t *>(body + 192 + 4 * (kk >> 1));
+                dbits[k] = dplane[b];
+            }
+        }
+        float acc[V];
+#pragma unroll
+        for (int v = 0; v < V; v++) acc[v] = 0.0f;
+#pragma unroll
+        for (int k = 0; k < NC; k++) {
+            const float d = half_to_float(dbits[k]);
+            const int sh = 16 * (kk & 1);
+            const int sc_lo = static_cast<int>(static_cast<int8_t>(scw[k] >> sh));
+            const int sc_hi = static_cast<int>(static_cast<int8_t>(scw[k] >> (sh + 8)));
+            const uint32_t w4[4] = {ql[k].x, ql[k].y, ql[k].z, ql[k].w};
+            uint32_t lo[4], hi[4];
+#pragma unroll
+            for (int s = 0; s < 4; s++) {
+                lo[s] = (w4[s] & 0x0F0F0F0Fu) | (((qh[k].x >> (2 * s)) & 0x03030303u) << 4);
+                hi[s] = ((w4[s] >> 4) & 0x0F0F0F0Fu) | (((qh[k].y >> (2 * s)) & 0x03030303u) << 4);
+            }
+#pragma unroll
+            for (int v = 0; v < V; v++) {
+                int plo = 0, phi = 0;
+#pragma unroll
+                for (int s = 0; s < 4; s++) {
+                    plo = dot4(lo[s], xw[v][k][s], plo);
+                    phi = dot4(hi[s], xw[v][k][4 + s], phi);
+                }
+                plo -= 32 * xlo[v][k];
+                phi -= 32 * xhi[v][k];
+                const int scp = sc_lo * plo + sc_hi * phi;
+                acc[v] = fmaf(xs[v][k] * d, static_cast<float>(scp), acc[v]);
+                if (DBG && rv && cv[k]) {
+                    int32_t *pp = a.P + (static_cast<int64_t>(v) * a.rows + row) * (2 * nsub);
+                    pp[2 * g[k]] = plo;
+                    pp[2 * g[k] + 1] = phi;
+                }
+            }
+        }
+#pragma unroll
+        for (int v = 0; v < V; v++) acc[v] = group_sum<T>(acc[v]);
+        if (!DBG && rv && t < V) {   // the debug variant writes P and S only
+            float o = acc[0];
+#pragma unroll
+            for (int v = 1; v < V; v++)
+                if (t == v) o = acc[v];
+            a.out[(static_cast<int64_t>(split) * V + t) * a.rows + row] = o;
+        }
+    }
+}
+
+namespace {
+
+using Launcher = hipError_t (*)(const GemvArgs &, const LaunchShape &, bool, hipStream_t);
+
+template <int V, int T, int NC>
+hipError_t launch_variant(const GemvArgs &a, const LaunchShape &s, bool debug,
+                          hipStream_t stream) {
+    const dim3 grid(static_cast<unsigned>(s.blocks), static_cast<unsigned>(s.splits));
+    const dim3 block(static_cast<unsigned>(64 * s.waves));
+    if (debug)
+        hipLaunchKernelGGL((gemv_q6k_kernel<V, T, NC, true>), grid, block, 0, stream, a);
+    else
+        hipLaunchKernelGGL((gemv_q6k_kernel<V, T, NC, false>), grid, block, 0, stream, a);
+    return hipGetLastError();
+}
+
+template <int V, int T, int NC>
+constexpr Launcher pick() {
+    if constexpr (V * NC <= 8)
+        return &launch_variant<V, T, NC>;
+    else
+        return nullptr;
+}
+
+#define QGEMV_NC_ROW(V, T) {pick<V, T, 1>(), pick<V, T, 2>(), pick<V, T, 3>(), pick<V, T, 4>()}
+#define QGEMV_T_ROW(V) \
+    {QGEMV_NC_ROW(V, 8), QGEMV_NC_ROW(V, 16), QGEMV_NC_ROW(V, 32), QGEMV_NC_ROW(V, 64)}
+const Launcher kTable[8][4][4] = {QGEMV_T_ROW(1), QGEMV_T_ROW(2), QGEMV_T_ROW(3), QGEMV_T_ROW(4),
+                                  QGEMV_T_ROW(5), QGEMV_T_ROW(6), QGEMV_T_ROW(7), QGEMV_T_ROW(8)};
+#undef QGEMV_T_ROW
+#undef QGEMV_NC_ROW
+
+int lanes_index(int lanes) {
+    switch (lanes) {
+        case 8: return 0;
+        case 16: return 1;
+        case 32: return 2;
+        case 64: return 3;
+        default: return -1;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_gemv_q6k(const GemvArgs &a, const LaunchShape &s, int nvec, bool debug,
+                           hipStream_t stream) {
+    const int ti = lanes_index(s.lanes);
+    if (nvec < 1 || nvec > 8 || ti < 0 || s.chunks < 1 || s.chunks > 4) return hipErrorInvalidValue;
+    const Launcher fn = kTable[nvec - 1][ti][s.chunks - 1];
+    if (!fn) return hipErrorInvalidValue;
+    return fn(a, s, debug, stream);
+}
+
+}  // namespace qgemv

@@ -1,0 +1,54 @@
+// Internal declarations shared by the kernel files and the C ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace qgemv {
+
+constexpr int kQK = 256;           // weights per super-block
+constexpr int kQ4KBytes = 144;     // Q4_K super-block
+constexpr int kQ6KBody = 208;      // Q6_K super-block body (fp16 d in a separate plane)
+constexpr int kChunksPerBlock = 8; // 16-byte code chunks (32 columns each) per super-block
+constexpr int kMaxVec = 8;
+
+// One GEMV launch: the kernels read everything they need from here.
+struct GemvArgs {
+    const uint8_t *w;      // weight tensor (Q4_K blocks, or Q6_K bodies followed by the d plane)
+    const int8_t *xq;      // [nvec][cols]
+    const float *xd;       // [nvec][cols/32]
+    float *out;            // [splits][nvec][rows] (y itself when splits == 1)
+    int32_t *P;            // debug partials or nullptr
+    int32_t *S;            // debug activation block sums or nullptr
+    int32_t rows;
+    int32_t nb;            // super-blocks per row
+    int32_t nchunks;       // 16-byte chunks per row = 8 * nb
+};
+
+struct LaunchShape {
+    int lanes;             // lanes per row (T)
+    int chunks;            // chunks per lane (NC)
+    int waves;             // waves per workgroup
+    int blocks;            // workgroups per column chunk
+    int splits;            // column chunks
+};
+
+// Kernel launchers; each returns the HIP status of its launch.
+hipError_t launch_quantize_act(const float *x, int8_t *xq, float *xd, int64_t nblocks32,
+                               hipStream_t stream);
+hipError_t launch_gemv_q4k(const GemvArgs &a, const LaunchShape &s, int nvec, bool debug,
+                           hipStream_t stream);
+hipError_t launch_gemv_q6k(const GemvArgs &a, const LaunchShape &s, int nvec, bool debug,
+                           hipStream_t stream);
+hipError_t launch_splitk_reduce(const float *part, float *y, int64_t n, int splits,
+                                hipStream_t stream);
+hipError_t launch_quantize_q4k(const float *w, uint8_t *out, int64_t rows, int64_t cols,
+                               hipStream_t stream);
+hipError_t launch_quantize_q6k(const float *w, uint8_t *out, int64_t rows, int64_t cols,
+                               hipStream_t stream);
+
+// Whether a (lanes, chunks, nvec) combination has a compiled kernel.
+bool gemv_variant_exists(int lanes, int chunks, int nvec);
+
+}  // namespace qgemv

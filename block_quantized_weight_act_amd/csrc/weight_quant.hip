@@ -1,0 +1,149 @@
+// Load-time weight quantization into the Q4_K and Q6_K layouts (oxinfer README, "How it
+// works", quant.rs: weights are block-quantized once when the model is loaded). Not on the
+// per-token path; written for clarity: one 64-lane wavefront per 256-weight super-block,
+// 4 consecutive weights per lane.
+//
+// Every decision that yields an integer (a code, a sub-scale, an fp16 super-scale) is an
+// IEEE float32 operation with round-to-nearest-even, so the bytes are reproducible on any
+// IEEE machine. Maxima and minima start from +0 and never produce -0, so the fp16
+// super-scale of an all-zero block is +0.
+#include "device_common.h"
+#include "qgemv_internal.h"
+
+namespace qgemv {
+
+__device__ __forceinline__ float clampf(float v, float lo, float hi) {
+    return v < lo ? lo : (v > hi ? hi : v);
+}
+
+// Q4_K: sub-block j (32 weights) = lanes 8j .. 8j+7.
+__global__ void __launch_bounds__(256) quantize_q4k_kernel(const float *__restrict__ w,
+                                                           uint8_t *__restrict__ out,
+                                                           int64_t nblocks, int nb, int64_t cols) {
+    const int lane = threadIdx.x & 63;
+    const int64_t blk = static_cast<int64_t>(blockIdx.x) * (blockDim.x >> 6) + (threadIdx.x >> 6);
+    if (blk >= nblocks) return;                      // uniform over the wavefront
+    const int64_t row = blk / nb, b = blk % nb;
+    const float4 v4 = *reinterpret_cast<const float4 *>(w + row * cols + b * kQK + 4 * lane);
+    const float v[4] = {v4.x, v4.y, v4.z, v4.w};
+    const int j = lane >> 3;
+
+    // sub-block range: lo = min(0, min w), hi = max w
+    float lo = 0.0f, hi = v[0];
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        lo = v[i] < lo ? v[i] : lo;
+        hi = v[i] > hi ? v[i] : hi;
+    }
+    lo = group_min<8>(lo);
+    hi = group_max<8>(hi);
+    const float s = (hi - lo) / 15.0f;
+    const float o = -lo;
+    // super-scales from the largest sub-block step and offset (compared against +0)
+    const float smax = group_max<64>(s > 0.0f ? s : 0.0f);
+    const float omax = group_max<64>(o > 0.0f ? o : 0.0f);
+    const uint32_t dh = float_to_half(smax / 63.0f);
+    const uint32_t mh = float_to_half(omax / 63.0f);
+    const float d = half_to_float(dh), dmin = half_to_float(mh);
+    const int sc = static_cast<int>(d > 0.0f ? clampf(rintf(s / d), 0.0f, 63.0f) : 0.0f);
+    const int m = static_cast<int>(dmin > 0.0f ? clampf(rintf(o / dmin), 0.0f, 63.0f) : 0.0f);
+    const float step = d * static_cast<float>(sc);    // exact
+    const float off = dmin * static_cast<float>(m);   // exact
+    uint32_t codes = 0;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        const float q = step > 0.0f ? clampf(rintf((v[i] + off) / step), 0.0f, 15.0f) : 0.0f;
+        codes |= static_cast<uint32_t>(q) << (8 * i);
+    }
+    uint8_t *dst = out + blk * kQ4KBytes;
+    // Weights 32j + 4(lane%8) + i: lanes with lane%8 < 4 hold the low nibbles (columns
+    // 32j + t, t < 16) and their partner lane + 4 the high nibbles (32j + 16 + t) of the
+    // same 4 bytes 16 + 16j + 4(lane%4) .. +3.
+    const uint32_t partner = __shfl_xor(codes, 4, 64);
+    if ((lane & 4) == 0)
+        *reinterpret_cast<uint32_t *>(dst + 16 + 16 * j + 4 * (lane & 3)) = codes | (partner << 4);
+    // Header: sc/m low nibbles at bits 4j of words 1 and 2, high 2 bits at bits 2j and
+    // 16 + 2j of word 3. Lane 8j holds sub-block j's values.
+    const bool lead = (lane & 7) == 0;
+    const uint32_t wa = group_or<64>(lead ? (static_cast<uint32_t>(sc) & 15u) << (4 * j) : 0u);
+    const uint32_t wb = group_or<64>(lead ? (static_cast<uint32_t>(m) & 15u) << (4 * j) : 0u);
+    const uint32_t wc = group_or<64>(
+        lead ? ((static_cast<uint32_t>(sc) >> 4) << (2 * j)) |
+                   ((static_cast<uint32_t>(m) >> 4) << (16 + 2 * j))
+             : 0u);
+    if (lane == 0) *reinterpret_cast<uint4 *>(dst) = make_uint4(dh | (mh << 16), wa, wb, wc);
+}
+
+// Q6_K: sub-block j (16 weights) = lanes 4j .. 4j+3.
+__global__ void __launch_bounds__(256) quantize_q6k_kernel(const float *__restrict__ w,
+                                                           uint8_t *__restrict__ out,
+                                                           int64_t nblocks, int nb, int64_t cols) {
+    const int lane = threadIdx.x & 63;
+    const int64_t blk = static_cast<int64_t>(blockIdx.x) * (blockDim.x >> 6) + (threadIdx.x >> 6);
+    if (blk >= nblocks) return;
+    const int64_t row = blk / nb, b = blk % nb;
+    const float4 v4 = *reinterpret_cast<const float4 *>(w + row * cols + b * kQK + 4 * lane);
+    const float v[4] = {v4.x, v4.y, v4.z, v4.w};
+
+    float a = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; i++) a = fabsf(v[i]) > a ? fabsf(v[i]) : a;
+    a = group_max<4>(a);
+    const float s = a / 31.0f;
+    const float smax = group_max<64>(s);
+    const uint32_t dh = float_to_half(smax / 127.0f);
+    const float d = half_to_float(dh);
+    const int sc = static_cast<int>(d > 0.0f ? clampf(rintf(s / d), -128.0f, 127.0f) : 0.0f);
+    const float step = d * static_cast<float>(sc);    // exact
+    int q[4];
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+        q[i] = step != 0.0f ? static_cast<int>(clampf(rintf(v[i] / step), -32.0f, 31.0f)) + 32 : 32;
+
+    uint8_t *body = out + blk * kQ6KBody;
+    // Weight 4*lane + i = 32k + 16g + t with k = lane/8, g = (lane%8)/4, t = 4(lane%4) + i.
+    const int k = lane >> 3, g = (lane >> 2) & 1, s4 = lane & 3;
+    uint32_t low = 0, high = 0;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        low |= static_cast<uint32_t>(q[i] & 15) << (8 * i);
+        // high 2 bits of weight 32k + 16g + 4*s4 + i: bits 2*s4 of byte 128 + 8k + 4g + i
+        high |= static_cast<uint32_t>((q[i] >> 4) & 3) << (8 * i + 2 * s4);
+    }
+    const uint32_t partner = __shfl_xor(low, 4, 64);
+    if (g == 0) *reinterpret_cast<uint32_t *>(body + 16 * k + 4 * s4) = low | (partner << 4);
+    high = group_or<4>(high);
+    if (s4 == 0) *reinterpret_cast<uint32_t *>(body + 128 + 8 * k + 4 * g) = high;
+    // sub-scales: lane 4j holds sc_j; bytes 192 + j, four per 32-bit word
+    const int jj = lane >> 2;
+    const uint32_t scb = group_or<16>((lane & 3) == 0
+                                          ? (static_cast<uint32_t>(sc) & 0xFFu) << (8 * (jj & 3))
+                                          : 0u);
+    if ((lane & 15) == 0) *reinterpret_cast<uint32_t *>(body + 192 + 4 * (lane >> 4)) = scb;
+    if (lane == 0) {
+        uint16_t *dplane = reinterpret_cast<uint16_t *>(out + nblocks * kQ6KBody);
+        dplane[blk] = static_cast<uint16_t>(dh);
+    }
+}
+
+hipError_t launch_quantize_q4k(const float *w, uint8_t *out, int64_t rows, int64_t cols,
+                               hipStream_t stream) {
+    const int64_t nb = cols / kQK, nblocks = rows * nb;
+    const int waves = 4;
+    const int64_t grid = (nblocks + waves - 1) / waves;
+    hipLaunchKernelGGL(quantize_q4k_kernel, dim3(static_cast<unsigned>(grid)), dim3(64 * waves), 0,
+                       stream, w, out, nblocks, static_cast<int>(nb), cols);
+    return hipGetLastError();
+}
+
+hipError_t launch_quantize_q6k(const float *w, uint8_t *out, int64_t rows, int64_t cols,
+                               hipStream_t stream) {
+    const int64_t nb = cols / kQK, nblocks = rows * nb;
+    const int waves = 4;
+    const int64_t grid = (nblocks + waves - 1) / waves;
+    hipLaunchKernelGGL(quantize_q6k_kernel, dim3(static_cast<unsigned>(grid)), dim3(64 * waves), 0,
+                       stream, w, out, nblocks, static_cast<int>(nb), cols);
+    return hipGetLastError();
+}
+
+}  // namespace qgemv

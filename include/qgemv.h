@@ -1,0 +1,220 @@
+/*
+ * qgemv — block-quantized weight x int8-activation matrix-vector products for
+ * AMD Instinct MI355X (gfx950). C ABI.
+ *
+ * The operation is the decode-time product y = W x of a large language model:
+ * one token per pass, so every weight byte is read once per product and the
+ * product is bound by HBM bandwidth (oxinfer README, "Performance"; the
+ * genie-ai-runtime post, "The decode arc"). W is stored in 256-weight
+ * super-blocks, x is quantized to int8 codes in blocks of 32 with one float32
+ * scale each (oxinfer README, "Build and run", --quant q8; "How it works",
+ * quant.rs: per-matmul activation quantization). The product is formed from
+ * exact int32 dot products of weight codes with activation codes per
+ * sub-block, which are then scaled and summed in float32 (genie-ai-runtime,
+ * "The decode arc": int8 dot products for Q4_K and Q6_K instead of
+ * dequantizing to floating point; "v1.2.0": one q8_1 activation shared by
+ * several products).
+ *
+ * Formats (all multi-byte fields little-endian):
+ *
+ *  Q4_K tensor: rows x (cols/256) super-blocks of 144 bytes, row-major. One
+ *  super-block covers 256 consecutive weights of a row; sub-block j
+ *  (j = 0..7) is weights 32j .. 32j+31.
+ *    [0,2)    d     fp16 super-scale of the sub-scales
+ *    [2,4)    dmin  fp16 super-scale of the sub-mins
+ *    [4,8)    low 4 bits of sc_j at byte 4 + j/2, bit 4*(j%2)
+ *    [8,12)   low 4 bits of m_j  at byte 8 + j/2, bit 4*(j%2)
+ *    [12,14)  high 2 bits of sc_j at byte 12 + j/4, bit 2*(j%4)
+ *    [14,16)  high 2 bits of m_j  at byte 14 + j/4, bit 2*(j%4)
+ *    [16,144) 4-bit codes: weight 32j + 16h + t (h = 0,1; t < 16) is the
+ *             low (h = 0) or high (h = 1) nibble of byte 16 + 16j + t
+ *    weight = d * sc_j * q - dmin * m_j
+ *
+ *  Q6_K tensor: two planes. First rows x (cols/256) bodies of 208 bytes
+ *  (block (r, b) at byte 208 * (r * cols/256 + b)), then as many fp16
+ *  super-scales d (block (r, b) at element r * cols/256 + b). 210 bytes per
+ *  256 weights in total. Sub-block j (j = 0..15) is weights 16j .. 16j+15.
+ *    [0,128)   low 4 bits: weight 32k + 16g + t (k < 8, g = 0,1, t < 16) is
+ *              nibble g of byte 16k + t
+ *    [128,192) high 2 bits: weight 32k + 16g + 4s + c (s, c < 4) is bits
+ *              2s .. 2s+1 of byte 128 + 8k + 4g + c
+ *    [192,208) sc_j, signed int8, at byte 192 + j
+ *    weight = d * sc_j * (q - 32), q in [0, 63]
+ *
+ *  Activations: codes xq int8 [nvec][cols] in [-127, 127] and scales xd
+ *  float32 [nvec][cols/32]; element i of vector v stands for
+ *  xd[v][i/32] * xq[v][i].
+ *
+ *  Output: y float32 [nvec][rows].
+ *
+ * Conventions for every entry point:
+ *  - All data pointers are device pointers owned by the caller. The library
+ *    allocates and frees nothing and never synchronizes; work is enqueued on
+ *    `stream` (0 = the null stream) and runs asynchronously.
+ *  - Arguments are checked on the host before anything is enqueued; on a
+ *    failed check nothing is launched and an error status is returned.
+ *    Launch failures return QGEMV_EHIP with the HIP message available from
+ *    qgemv_last_error() (per thread). Faults inside a kernel surface at the
+ *    caller's next synchronization.
+ *  - Shapes: cols a positive multiple of 256, rows >= 1, 1 <= nvec <= 8,
+ *    rows * cols / 256 < 2^31 super-blocks.
+ *  - Alignment: w and xq 16 bytes, xd and y 4 bytes.
+ *  - Outputs must not overlap inputs.
+ *  - The functions are safe to call from several host threads.
+ */
+#ifndef QGEMV_H
+#define QGEMV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum qgemv_status {
+    QGEMV_OK = 0,
+    QGEMV_EINVAL = 1,       /* null pointer, bad shape, bad type, overlapping buffers */
+    QGEMV_EALIGN = 2,       /* pointer not aligned as required */
+    QGEMV_EWORKSPACE = 3,   /* workspace smaller than qgemv_workspace_bytes() */
+    QGEMV_EHIP = 4          /* the HIP runtime refused a launch */
+};
+
+enum qgemv_wtype {
+    QGEMV_Q4K = 1,
+    QGEMV_Q6K = 2
+};
+
+#define QGEMV_MAX_NVEC 8
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int qgemv_version(void);
+
+/* Static text for a status code. */
+const char *qgemv_status_string(int status);
+
+/* Text of the last HIP error seen by this thread ("" if none). */
+const char *qgemv_last_error(void);
+
+/* Bytes of a weight tensor of the given type and shape (0 on a bad shape). */
+size_t qgemv_weight_bytes(int wtype, int64_t rows, int64_t cols);
+
+/*
+ * Activation quantization (oxinfer README, "How it works": per-matmul
+ * activation quantization; "Build and run": blocks of 32, f32 scales).
+ * x float32 [nvec][cols] -> xq int8 [nvec][cols], xd float32 [nvec][cols/32].
+ * Per block of 32: amax = max |x|, xd = amax / 127 (IEEE float32 division),
+ * inverse 127 / amax (0 when amax = 0), code = rint(x * inverse) with one
+ * float32 multiply and round-to-nearest-even, clamped to [-127, 127].
+ * Here cols only needs to be a positive multiple of 32. x 16-byte aligned,
+ * xq 4-byte aligned, xd 4-byte aligned. Inputs must be finite.
+ */
+int qgemv_quantize_act(const float *x, int8_t *xq, float *xd, int64_t cols, int32_t nvec,
+                       hipStream_t stream);
+
+/*
+ * Workspace needed by qgemv_q4k / qgemv_q6k / qgemv_batch for this shape, in
+ * bytes; 0 when the chosen plan does not split the columns. The planner splits
+ * the columns into S chunks of whole super-blocks when rows alone cannot fill
+ * the GPU; the workspace then holds S partial results per output, summed in
+ * a second pass in ascending chunk order (no atomics; genie-ai-runtime
+ * "v1.3.0": split-K with a separate reduce, chosen per shape).
+ */
+size_t qgemv_workspace_bytes(int wtype, int64_t rows, int64_t cols, int32_t nvec);
+
+/*
+ * y = W x for one activation vector, W in Q4_K (genie-ai-runtime, "The decode
+ * arc": int8 dot-product mat-vec for Q4_K). Per sub-block j of a super-block:
+ * P = sum of q * xq over its 32 columns (exact int32), S = sum of xq over the
+ * same 32 columns, and the term xd * (d * sc_j * P - dmin * m_j * S) is added
+ * to y in float32. w: Q4_K tensor [rows][cols]; xq, xd: one quantized vector;
+ * y: [rows]. workspace may be NULL when qgemv_workspace_bytes() is 0.
+ */
+int qgemv_q4k(const void *w, const int8_t *xq, const float *xd, float *y, int64_t rows,
+              int64_t cols, void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * y = W x for one activation vector, W in Q6_K (genie-ai-runtime, "The decode
+ * arc": int8 dot-product mat-vec for Q6_K). Per sub-block j of 16 columns:
+ * P = sum of (q - 32) * xq (exact int32) and the term xd * d * sc_j * P is
+ * added to y in float32. Arguments as for qgemv_q4k.
+ */
+int qgemv_q6k(const void *w, const int8_t *xq, const float *xd, float *y, int64_t rows,
+              int64_t cols, void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * The same product for nvec = 1..8 activation vectors sharing one pass over
+ * the weights (several sequences decoded together; oxinfer README, "How it
+ * works": multi-token int8 decode variants). xq [nvec][cols],
+ * xd [nvec][cols/32], y [nvec][rows]. wtype is QGEMV_Q4K or QGEMV_Q6K.
+ */
+int qgemv_batch(int wtype, const void *w, const int8_t *xq, const float *xd, float *y,
+                int64_t rows, int64_t cols, int32_t nvec, void *workspace,
+                size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Test hook: the exact integer partials of the same kernels.
+ * P int32: Q4_K [nvec][rows][cols/32] (sum of q * xq per 32-column
+ * sub-block), Q6_K [nvec][rows][cols/16] (sum of (q - 32) * xq per 16-column
+ * sub-block). S int32 [nvec][cols/32]: sum of xq per activation block.
+ * P and S 4-byte aligned. y is not written.
+ */
+int qgemv_debug_partials(int wtype, const void *w, const int8_t *xq, const float *xd,
+                         int32_t *P, int32_t *S, int64_t rows, int64_t cols, int32_t nvec,
+                         hipStream_t stream);
+
+/*
+ * Load-time weight quantization, float32 [rows][cols] -> Q4_K or Q6_K tensor
+ * (oxinfer README, "How it works", quant.rs: weights are block-quantized when
+ * the model is loaded). Not on the per-token path. Every decision is taken in
+ * float32 with round-to-nearest-even:
+ *  Q4_K, per sub-block of 32: lo = min(0, min w), hi = max w,
+ *    s = (hi - lo) / 15, o = -lo; d = fp16(max s / 63), dmin = fp16(max o / 63);
+ *    sc = clamp(rint(s / d), 0, 63), m = clamp(rint(o / dmin), 0, 63) (0 for a
+ *    zero divisor); q = clamp(rint((w + dmin * m) / (d * sc)), 0, 15).
+ *  Q6_K, per sub-block of 16: s = max |w| / 31; d = fp16(max s / 127);
+ *    sc = clamp(rint(s / d), -128, 127); q = clamp(rint(w / (d * sc)), -32, 31) + 32
+ *    (32 when sc = 0).
+ * w 16-byte aligned, out 16-byte aligned with qgemv_weight_bytes() bytes.
+ * Inputs must be finite and small enough for the fp16 super-scales.
+ */
+int qgemv_quantize_weights(int wtype, const float *w, void *out, int64_t rows, int64_t cols,
+                           hipStream_t stream);
+
+/*
+ * Launch plan of the GEMV kernels. Each row is cut into 16-byte chunks of
+ * weight codes (one 32-column activation block each); a group of
+ * lanes_per_row lanes of a 64-lane wavefront shares a row, each lane taking
+ * chunks_per_lane chunks, so one pass covers lanes_per_row * chunks_per_lane
+ * chunks and the row is split into ceil(cols/32 / that) column chunks
+ * ("splits"; > 1 needs a workspace and a second pass). waves_per_block
+ * wavefronts form a workgroup; blocks is the number of workgroups per column
+ * chunk, each looping over row groups.
+ */
+typedef struct qgemv_plan {
+    int32_t lanes_per_row;    /* 8, 16, 32 or 64 */
+    int32_t chunks_per_lane;  /* 1 .. 4 */
+    int32_t waves_per_block;  /* 1 .. 4 */
+    int32_t blocks;           /* workgroups per column chunk, >= 1 */
+    int32_t splits;           /* derived: column chunks (output of qgemv_plan_for) */
+} qgemv_plan;
+
+/* The plan the library uses for a shape (filled into *plan). */
+int qgemv_plan_for(int wtype, int64_t rows, int64_t cols, int32_t nvec, qgemv_plan *plan);
+
+/* Workspace bytes for an explicit plan (0 when it does not split). */
+size_t qgemv_plan_workspace_bytes(const qgemv_plan *plan, int64_t rows, int64_t cols,
+                                  int32_t nvec);
+
+/* qgemv_batch with an explicit plan (for tuning); splits is recomputed. */
+int qgemv_batch_plan(int wtype, const void *w, const int8_t *xq, const float *xd, float *y,
+                     int64_t rows, int64_t cols, int32_t nvec, const qgemv_plan *plan,
+                     void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QGEMV_H */

@@ -1,0 +1,99 @@
+"""The C-ABI library on the CPU: it loads, exports every entry point include/qgemv.h declares,
+and rejects bad arguments on the host before anything reaches the GPU. No call here passes
+validation, so nothing is ever launched (these tests need no GPU)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_quantized_weight_act_amd as qg
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qgemv.h")
+
+EINVAL, EALIGN, EWORKSPACE = 1, 2, 3
+A = 1 << 40          # a fake, 256-byte aligned "device address" (never dereferenced)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(qgemv_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    lib = ctypes.CDLL(qg.library_path)
+    names = declared_functions()
+    assert len(names) >= 14
+    missing = [n for n in names if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_binding_covers_every_declared_function():
+    names = set(declared_functions()) - {"qgemv_last_error"}
+    assert names <= set(qg.__all__), names - set(qg.__all__)
+
+
+def test_status_strings_and_sizes():
+    lib = qg._load()
+    assert qg.qgemv_version() >= 100
+    for s in range(5):
+        assert lib.qgemv_status_string(s)
+    assert qg.qgemv_weight_bytes("q4k", 3, 512) == 3 * 2 * 144
+    assert qg.qgemv_weight_bytes("q6k", 3, 512) == 3 * 2 * 210
+    assert qg.qgemv_weight_bytes("q4k", 3, 500) == 0
+    assert qg.qgemv_workspace_bytes("q4k", 262144, 1536, 1) == 0
+
+
+def _call_batch(wtype=1, w=A, xq=A + (1 << 30), xd=A + (2 << 30), y=A + (3 << 30), rows=64,
+                cols=1024, nvec=1, ws=None, wsb=0):
+    lib = qg._load()
+    return lib.qgemv_batch(wtype, w, xq, xd, y, rows, cols, nvec, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(wtype=3), EINVAL), (dict(w=None), EINVAL), (dict(y=None), EINVAL),
+    (dict(cols=1000), EINVAL), (dict(cols=0), EINVAL), (dict(rows=0), EINVAL),
+    (dict(nvec=0), EINVAL), (dict(nvec=9), EINVAL), (dict(w=A + 8), EALIGN),
+    (dict(xq=A + (1 << 30) + 4), EALIGN), (dict(y=A + (3 << 30) + 2), EALIGN),
+    (dict(y=A + 64), EINVAL),              # output overlapping the weights
+    (dict(rows=1 << 31), EINVAL),
+])
+def test_batch_rejects_bad_arguments(kw, status):
+    assert _call_batch(**kw) == status
+
+
+def test_split_plan_without_workspace_is_rejected():
+    lib = qg._load()
+    plan = qg.Plan(16, 1, 4, 4, 0)
+    rows, cols = 64, 4096
+    assert lib.qgemv_plan_workspace_bytes(ctypes.byref(plan), rows, cols, 1) == 8 * rows * 4
+    st = lib.qgemv_batch_plan(1, A, A + (1 << 30), A + (2 << 30), A + (3 << 30), rows, cols, 1,
+                              ctypes.byref(plan), None, 0, None)
+    assert st == EWORKSPACE
+    st = lib.qgemv_batch_plan(1, A, A + (1 << 30), A + (2 << 30), A + (3 << 30), rows, cols, 1,
+                              ctypes.byref(plan), A + (4 << 30), 100, None)
+    assert st == EWORKSPACE
+    bad = qg.Plan(12, 1, 4, 4, 0)
+    assert lib.qgemv_batch_plan(1, A, A + (1 << 30), A + (2 << 30), A + (3 << 30), rows, cols, 1,
+                                ctypes.byref(bad), None, 0, None) == EINVAL
+    toomany = qg.Plan(16, 4, 4, 4, 0)                  # 3 vectors x 4 chunks: not compiled
+    assert lib.qgemv_batch_plan(1, A, A + (1 << 30), A + (2 << 30), A + (3 << 30), rows, cols, 3,
+                                ctypes.byref(toomany), None, 0, None) == EINVAL
+
+
+def test_other_entry_points_reject_bad_arguments():
+    lib = qg._load()
+    assert lib.qgemv_quantize_act(A, A + (1 << 30), A + (2 << 30), 48, 1, None) == EINVAL
+    assert lib.qgemv_quantize_act(A + 4, A + (1 << 30), A + (2 << 30), 64, 1, None) == EALIGN
+    assert lib.qgemv_quantize_act(None, A, A, 64, 1, None) == EINVAL
+    assert lib.qgemv_q4k(A, A + (1 << 30), A + (2 << 30), None, 8, 256, None, 0, None) == EINVAL
+    assert lib.qgemv_q6k(A + 2, A + (1 << 30), A + (2 << 30), A + (3 << 30), 8, 256, None, 0,
+                         None) == EALIGN
+    assert lib.qgemv_debug_partials(1, A, A + (1 << 30), A + (2 << 30), None, A, 8, 256, 1,
+                                    None) == EINVAL
+    assert lib.qgemv_quantize_weights(2, A, A + 64, 8, 256, None) == EINVAL   # overlap
+    assert lib.qgemv_quantize_weights(2, A + 4, A + (1 << 30), 8, 256, None) == EALIGN
+    assert lib.qgemv_quantize_weights(5, A, A + (1 << 30), 8, 256, None) == EINVAL

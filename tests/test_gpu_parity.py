@@ -1,0 +1,235 @@
+"""GPU parity: the HIP library (called through its C ABI) against the CPU oracle.
+
+Bars: activation codes and scales, weight bytes and the integer partials P and S are
+bit-exact; y satisfies |y - y_ref| <= 1e-5 * sum_i |w_i| |x_i| per output (w the
+dequantized weights, x the dequantized activations), with y_ref and the bound computed by
+the oracle in float64.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+gu = pytest.importorskip("gpu_util")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    gu.require_gpu()
+
+
+def _say(*a):
+    print("[parity]", *a, flush=True)
+
+
+# --------------------------------------------------------------- activations --
+@pytest.mark.parametrize("nvec,cols", [(1, 32), (1, 96), (2, 1536), (8, 2048), (3, 8192),
+                                       (1, 32 * 1001)])
+def test_quantize_act_bitexact(nvec, cols):
+    _say("quantize_act", nvec, cols)
+    rng = np.random.default_rng(cols + nvec)
+    x = rng.standard_normal((nvec, cols)).astype(np.float32)
+    x[0, :32] = 0.0                                    # all-zero block
+    if cols >= 96:
+        x[0, 32:64] *= np.float32(1e-30)               # tiny block
+        x[0, 64:96] = np.float32(7.0)                  # constant block
+    if nvec > 1:
+        x[1] *= np.float32(1e4)
+    xq, xd = gu.quantize_act(x)
+    rq, rd = oracle.quantize_act(x)
+    assert np.array_equal(gu.host(xq), rq)
+    assert np.array_equal(gu.host(xd).view(np.uint32), rd.view(np.uint32))
+
+
+def test_quantize_act_hand_worked_ties():
+    import oracle_pins
+    cases = oracle_pins.read_act_cases()
+    x = np.stack([c[0] for c in cases]).reshape(1, -1)
+    xq, xd = gu.quantize_act(x)
+    assert np.array_equal(gu.host(xq).reshape(len(cases), 32), np.stack([c[1] for c in cases]))
+    assert np.array_equal(gu.host(xd)[0], np.array([c[2] for c in cases], np.float32))
+
+
+# ---------------------------------------------------------------- weights --
+@pytest.mark.parametrize("wtype", ["q4k", "q6k"])
+@pytest.mark.parametrize("sigma", [0.02, 0.002, 1.0, 40.0])
+def test_quantize_weights_bitexact(wtype, sigma):
+    _say("quantize_weights", wtype, sigma)
+    rng = np.random.default_rng(int(sigma * 1000))
+    w = (rng.standard_normal((37, 768)) * sigma).astype(np.float32)
+    w[1] = np.abs(w[1])
+    w[2] = -np.abs(w[2])
+    w[3, :256] = 0.0
+    w[4, 32:64] = np.float32(-0.25 * sigma)
+    w[5, 0:16] = np.float32(0.0)
+    w[5, 16] = np.float32(-0.0)
+    got = gu.host(gu.quantize_weights(wtype, w))
+    ref = oracle.quantize_q4k(w) if wtype == "q4k" else oracle.quantize_q6k(w)
+    assert np.array_equal(got, ref)
+
+
+# ---------------------------------------------------------------- GEMV ------
+def _check_gemv(wtype, wbuf, rows, cols, x, plan=None, debug=True):
+    nvec = x.shape[0]
+    rq, rd = oracle.quantize_act(x)
+    xq, xd = gu.quantize_act(x)
+    assert np.array_equal(gu.host(xq), rq)
+    ref = oracle.gemv(wtype, wbuf, rows, cols, rq, rd, partials=debug)
+    wt = gu.dev(wbuf)
+    y = gu.gemv(wtype, wt, xq, xd, rows, cols, nvec, plan=plan)
+    gu.assert_within_bound(y, ref)
+    if debug:
+        P, S = gu.partials(wtype, wt, xq, xd, rows, cols, nvec)
+        assert np.array_equal(P, ref["P"])
+        assert np.array_equal(S, oracle.block_sums(rq))
+    return y, ref
+
+
+@pytest.mark.parametrize("name", list(synth.WORKLOADS))
+def test_workload_parity_full_size(name):
+    """Each decode workload at its full size: the GPU-quantized weights equal the oracle's
+    bytes, y is inside the bound for every row and vector, P and S are bit-exact."""
+    wl = synth.WORKLOADS[name]
+    _say("workload", name, wl.rows, wl.cols, wl.nvec)
+    x = wl.activations()
+    chunk = 16384
+    parts = []
+    for r0 in range(0, wl.rows, chunk):
+        r1 = min(wl.rows, r0 + chunk)
+        w = wl.weight_block(r0, r1)
+        ref = oracle.quantize_q4k(w) if wl.wtype == "q4k" else oracle.quantize_q6k(w)
+        got = gu.host(gu.quantize_weights(wl.wtype, w))
+        assert np.array_equal(got, ref), "weight bytes differ in rows %d..%d" % (r0, r1)
+        parts.append(ref)
+    if wl.wtype == "q4k":
+        wbuf = np.concatenate(parts)
+    else:
+        planes = [oracle.q6k_planes(p, min(chunk, wl.rows - i * chunk), wl.cols)
+                  for i, p in enumerate(parts)]
+        wbuf = oracle.q6k_join(np.concatenate([b for b, _ in planes]),
+                               np.concatenate([d for _, d in planes]))
+    _check_gemv(wl.wtype, wbuf, wl.rows, wl.cols, x)
+
+
+@pytest.mark.parametrize("wtype", ["q4k", "q6k"])
+@pytest.mark.parametrize("rows,cols,nvec", [(1, 256, 1), (3, 512, 1), (17, 768, 2), (100, 1280, 3),
+                                            (257, 2304, 1), (64, 8448, 1), (33, 256 * 33, 2),
+                                            (5, 1536, 8), (999, 1024, 5)])
+def test_ragged_shapes(wtype, rows, cols, nvec):
+    _say("ragged", wtype, rows, cols, nvec)
+    rng = np.random.default_rng(rows * 7 + cols + nvec)
+    w = (rng.standard_normal((rows, cols)) * 0.02).astype(np.float32)
+    wbuf = oracle.quantize_q4k(w) if wtype == "q4k" else oracle.quantize_q6k(w, negate_scales=True)
+    x = rng.standard_normal((nvec, cols)).astype(np.float32)
+    _check_gemv(wtype, wbuf, rows, cols, x)
+
+
+PLANS = [dict(lanes_per_row=t, chunks_per_lane=nc, waves_per_block=wv, blocks=b)
+         for t, nc, wv, b in [(8, 1, 1, 1), (8, 4, 4, 3), (16, 1, 2, 7), (16, 3, 4, 64),
+                              (32, 2, 4, 5), (64, 1, 4, 100), (64, 4, 1, 2), (64, 2, 3, 1000)]]
+
+
+@pytest.mark.parametrize("plan", PLANS, ids=lambda p: "T%d_NC%d_W%d_B%d" % (
+    p["lanes_per_row"], p["chunks_per_lane"], p["waves_per_block"], p["blocks"]))
+@pytest.mark.parametrize("wtype", ["q4k", "q6k"])
+def test_explicit_plans_and_splits(wtype, plan):
+    """Every lane geometry, including column splits with the two-pass reduce."""
+    rows, cols, nvec = 203, 2560, 2
+    rng = np.random.default_rng(11)
+    w = (rng.standard_normal((rows, cols)) * 0.02).astype(np.float32)
+    wbuf = oracle.quantize_q4k(w) if wtype == "q4k" else oracle.quantize_q6k(w)
+    x = rng.standard_normal((nvec, cols)).astype(np.float32)
+    nv = nvec if nvec * plan["chunks_per_lane"] <= 8 else 1
+    _check_gemv(wtype, wbuf, rows, cols, x[:nv], plan=plan, debug=False)
+
+
+@pytest.mark.parametrize("wtype", ["q4k", "q6k"])
+def test_special_inputs(wtype):
+    rows, cols = 64, 1024
+    rng = np.random.default_rng(3)
+    w = (rng.standard_normal((rows, cols)) * 0.02).astype(np.float32)
+    wbuf = oracle.quantize_q4k(w) if wtype == "q4k" else oracle.quantize_q6k(w, negate_scales=True)
+    what = oracle.dequantize(wtype, wbuf, rows, cols)
+    # zero activation: y is exactly zero
+    y, _ = _check_gemv(wtype, wbuf, rows, cols, np.zeros((1, cols), np.float32))
+    assert np.all(y == 0)
+    # one-hot activation: column extraction, y = w[:, k] * x_k; the Q4_K term of a small
+    # dequantized weight cancels between its scale and min parts
+    for k in list(range(0, cols, 13)) + [31, 32, cols - 1]:
+        x = np.zeros((1, cols), np.float32)
+        x[0, k] = -2.5
+        y, ref = _check_gemv(wtype, wbuf, rows, cols, x)
+        xq, xd = oracle.quantize_act(x)
+        assert np.allclose(y[0], what[:, k] * (float(xd[0, k // 32]) * int(xq[0, k])),
+                           rtol=1e-6, atol=0)
+    # constant activation
+    _check_gemv(wtype, wbuf, rows, cols, np.full((2, cols), 0.7, np.float32))
+    # zero weights: y is exactly zero
+    zbuf = oracle.quantize_q4k(np.zeros((rows, cols), np.float32)) if wtype == "q4k" else \
+        oracle.quantize_q6k(np.zeros((rows, cols), np.float32))
+    y, _ = _check_gemv(wtype, zbuf, rows, cols, rng.standard_normal((1, cols)).astype(np.float32))
+    assert np.all(y == 0)
+
+
+@pytest.mark.parametrize("sigma", [0.002, 30.0])
+@pytest.mark.parametrize("wtype", ["q4k", "q6k"])
+def test_scale_extremes(wtype, sigma):
+    """Subnormal fp16 super-scales (sigma 0.002) and large ones (sigma 30)."""
+    rows, cols = 128, 2048
+    w = synth.normal_f32(77, 0, rows * cols, sigma).reshape(rows, cols)
+    wbuf = oracle.quantize_q4k(w) if wtype == "q4k" else oracle.quantize_q6k(w, negate_scales=True)
+    x = synth.normal_f32(78, 0, 2 * cols, 1.0).reshape(2, cols)
+    _check_gemv(wtype, wbuf, rows, cols, x)
+
+
+def test_integer_extremes():
+    cols = 512
+    blk = oracle.q4k_pack_block(0x3C00, 0x3C00, np.full(8, 63, np.uint8), np.full(8, 63, np.uint8),
+                                np.full(256, 15, np.uint8))
+    wbuf = np.tile(blk, 2 * 5)
+    _check_gemv("q4k", wbuf, 5, cols, np.full((1, cols), 3.0, np.float32))
+    body = oracle.q6k_pack_block(np.full(16, -128, np.int8), np.zeros(256, np.uint8))
+    t6 = oracle.q6k_join(np.tile(body, 2 * 5), np.full(2 * 5, 0x3C00, np.uint16))
+    _check_gemv("q6k", t6, 5, cols, np.full((1, cols), -3.0, np.float32))
+
+
+@pytest.mark.parametrize("wtype", ["q4k", "q6k"])
+def test_determinism_permutation_and_batch(wtype):
+    rows, cols = 300, 3072
+    rng = np.random.default_rng(21)
+    w = (rng.standard_normal((rows, cols)) * 0.02).astype(np.float32)
+    wbuf = oracle.quantize_q4k(w) if wtype == "q4k" else oracle.quantize_q6k(w)
+    x = rng.standard_normal((1, cols)).astype(np.float32)
+    xq, xd = gu.quantize_act(x)
+    wt = gu.dev(wbuf)
+    y1 = gu.gemv(wtype, wt, xq, xd, rows, cols, 1)
+    y2 = gu.gemv(wtype, wt, xq, xd, rows, cols, 1)
+    assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32))      # run-to-run identical
+    perm = rng.permutation(rows)
+    wp = oracle.quantize_q4k(w[perm]) if wtype == "q4k" else oracle.quantize_q6k(w[perm])
+    yp = gu.gemv(wtype, gu.dev(wp), xq, xd, rows, cols, 1)
+    assert np.array_equal(yp[0].view(np.uint32), y1[0, perm].view(np.uint32))
+    # a batch of identical vectors gives identical rows
+    xb = np.repeat(x, 6, axis=0)
+    xqb, xdb = gu.quantize_act(xb)
+    yb = gu.gemv(wtype, wt, xqb, xdb, rows, cols, 6)
+    for v in range(1, 6):
+        assert np.array_equal(yb[v].view(np.uint32), yb[0].view(np.uint32))
+
+
+def test_workspace_required_when_split():
+    import block_quantized_weight_act_amd as qg
+    rows, cols = 64, 4096
+    plan = dict(lanes_per_row=16, chunks_per_lane=1, waves_per_block=4, blocks=4)
+    assert qg.qgemv_plan_workspace_bytes(plan, rows, cols, 1) == 8 * rows * 4
+    w = gu.dev(np.zeros(qg.qgemv_weight_bytes("q4k", rows, cols), np.uint8))
+    xq, xd = gu.quantize_act(np.ones((1, cols), np.float32))
+    import torch
+    y = torch.empty((1, rows), dtype=torch.float32, device=gu.DEV)
+    with pytest.raises(qg.QgemvError) as e:
+        qg.qgemv_batch_plan("q4k", w, xq, xd, y, rows, cols, 1, plan)
+    assert e.value.status == 3
