@@ -172,11 +172,35 @@ def main():
         wall = time.perf_counter() - w0_
         return e0.elapsed_time(e1) / n, wall / n * 1e3
 
+    def graph_timed(fn, n):
+        """The same launches captured once into a HIP graph and replayed: GPU time per launch
+        without the host's per-call overhead (what a decode loop that replays a graph sees)."""
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            fn(0)
+        torch.cuda.current_stream().wait_stream(side)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(n):
+                fn(i)
+        g.replay()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
     for i in range(args.warmup):
         step(i)
     ms_step, wall_step = timed(step, args.steps)
     ms_gemv, _ = timed(gemv, args.steps)
     ms_quant, _ = timed(lambda i: quantize(), args.steps)
+    ms_step_graph = graph_timed(step, args.steps)
+    ms_gemv_graph = graph_timed(gemv, args.steps)
 
     nbytes = algorithmic_bytes(wl, wbytes)
     value = nbytes["step"] / (ms_step * 1e-3) / 1e9
@@ -202,6 +226,10 @@ def main():
                    "weight_bytes": wbytes, "plan": plan},
         "us_per_gemv": round(ms_gemv * 1e3, 3),
         "us_per_quantize_act": round(ms_quant * 1e3, 3),
+        "graph_replay": {"us_per_step": round(ms_step_graph * 1e3, 3),
+                         "us_per_gemv": round(ms_gemv_graph * 1e3, 3),
+                         "gemv_gbs": round(nbytes["gemv"] / (ms_gemv_graph * 1e-3) / 1e9, 1),
+                         "step_gbs": round(nbytes["step"] / (ms_step_graph * 1e-3) / 1e9, 1)},
         "pct_of_hbm_peak": round(100 * achieved / HBM_PEAK_GBS, 2),
         "wall_ms_per_step": round(wall_step, 5),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,

@@ -22,6 +22,7 @@ __all__ = [
     "qgemv_status_string", "qgemv_weight_bytes", "qgemv_quantize_act",
     "qgemv_workspace_bytes", "qgemv_q4k", "qgemv_q6k", "qgemv_batch", "qgemv_debug_partials",
     "qgemv_quantize_weights", "qgemv_plan_for", "qgemv_plan_workspace_bytes", "qgemv_batch_plan",
+    "qgemv_read_probe",
 ]
 
 QGEMV_Q4K = 1
@@ -77,6 +78,7 @@ def _load():
         "qgemv_plan_workspace_bytes": (sz, [ctypes.POINTER(Plan), i64, i64, i32]),
         "qgemv_batch_plan": (ctypes.c_int, [ctypes.c_int, vp, vp, vp, vp, i64, i64, i32,
                                             ctypes.POINTER(Plan), vp, sz, vp]),
+        "qgemv_read_probe": (ctypes.c_int, [vp, sz, vp, i32, vp]),
     }
     for name, (res, args) in sigs.items():
         fn = getattr(lib, name)
@@ -219,3 +221,11 @@ def qgemv_quantize_weights(wtype, w, out, rows: int, cols: int, stream=None) -> 
     _check("qgemv_quantize_weights", lib.qgemv_quantize_weights(
         _wtype(wtype), _ptr(w, torch.float32, "w"), _ptr(out, name="out"), rows, cols,
         _stream(stream, out)))
+
+
+def qgemv_read_probe(buf, sink, blocks: int = 2048, nbytes: int | None = None, stream=None) -> None:
+    """Read `nbytes` (default: all) of `buf` once; a measurement of the read ceiling."""
+    lib = _load()
+    n = _nbytes(buf) if nbytes is None else nbytes
+    _check("qgemv_read_probe", lib.qgemv_read_probe(_ptr(buf, name="buf"), n, _ptr(sink, name="sink"),
+                                                    blocks, _stream(stream, buf)))

@@ -39,7 +39,7 @@ size_t weight_bytes(int wtype, int64_t rows, int64_t cols) {
 
 bool shape_ok(int64_t rows, int64_t cols, int32_t nvec) {
     if (rows < 1 || cols < kQK || cols % kQK != 0 || nvec < 1 || nvec > kMaxVec) return false;
-    if (rows > INT32_MAX || cols > (int64_t{1} << 30)) return false;
+    if (rows > (int64_t{1} << 30) || cols > (int64_t{1} << 30)) return false;
     return rows * (cols / kQK) < (int64_t{1} << 31);
 }
 
@@ -298,6 +298,17 @@ int qgemv_quantize_weights(int wtype, const float *w, void *out, int64_t rows, i
         wtype == QGEMV_Q4K
             ? launch_quantize_q4k(w, static_cast<uint8_t *>(out), rows, cols, stream)
             : launch_quantize_q6k(w, static_cast<uint8_t *>(out), rows, cols, stream);
+    return e == hipSuccess ? QGEMV_OK : hip_fail(e);
+}
+
+int qgemv_read_probe(const void *buf, size_t bytes, uint32_t *sink, int32_t blocks,
+                     hipStream_t stream) {
+    if (!buf || !sink || bytes < 16 || bytes % 16 != 0 || blocks < 1 || blocks > (1 << 20))
+        return QGEMV_EINVAL;
+    if (!aligned(buf, 16) || !aligned(sink, 4)) return QGEMV_EALIGN;
+    if (overlaps(sink, 4, buf, bytes)) return QGEMV_EINVAL;
+    const hipError_t e =
+        launch_read_probe(buf, static_cast<int64_t>(bytes), sink, blocks, stream);
     return e == hipSuccess ? QGEMV_OK : hip_fail(e);
 }
 

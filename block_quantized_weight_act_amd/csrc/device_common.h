@@ -25,12 +25,40 @@ __device__ __forceinline__ uint32_t float_to_half(float f) {
     return __builtin_bit_cast(uint16_t, static_cast<_Float16>(f));
 }
 
-// Sum over aligned groups of `width` consecutive lanes (width a power of two <= 64); every
-// lane of the group receives the group's sum.
+// Lane permutations inside a row of 16 lanes (DPP): each is a modifier on one VALU op.
+enum : int {
+    kDppXor1 = 0xB1,         // quad_perm [1,0,3,2]
+    kDppXor2 = 0x4E,         // quad_perm [2,3,0,1]
+    kDppHalfMirror = 0x141,  // lane i <-> 7 - i inside each half row of 8
+    kDppMirror = 0x140,      // lane i <-> 15 - i inside each row of 16
+};
+
+template <int ctrl>
+__device__ __forceinline__ float dpp(float v) {
+    return __builtin_bit_cast(
+        float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), ctrl, 0xF, 0xF, false));
+}
+
+// Sum over aligned groups of `width` consecutive lanes (width 8, 16, 32 or 64); every lane of
+// the group receives the same sum. Within a row of 16 the butterfly uses DPP (xor 1, xor 2,
+// then the two mirrors, which pair every partial sum with the one it lacks); across rows it
+// uses one ds_swizzle (xor 16) and, for the whole wave, the two half-wave sums read as
+// scalars. Every pairwise add is commutative, so all lanes hold bit-identical results.
 template <int width>
 __device__ __forceinline__ float group_sum(float v) {
-#pragma unroll
-    for (int off = width / 2; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+    static_assert(width == 8 || width == 16 || width == 32 || width == 64, "group width");
+    v += dpp<kDppXor1>(v);
+    v += dpp<kDppXor2>(v);
+    v += dpp<kDppHalfMirror>(v);
+    if constexpr (width >= 16) v += dpp<kDppMirror>(v);
+    if constexpr (width >= 32)
+        v += __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v),
+                                                                   0x401F));  // xor 16
+    if constexpr (width == 64) {
+        const int b = __builtin_bit_cast(int, v);
+        v = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 0)) +
+            __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 32));
+    }
     return v;
 }
 
@@ -56,5 +84,24 @@ __device__ __forceinline__ uint32_t group_or(uint32_t v) {
 }
 
 __device__ __forceinline__ uint4 load16(const void *p) { return *reinterpret_cast<const uint4 *>(p); }
+
+// 16-byte load marked nontemporal: the weights are read once per product, so they are
+// streamed past the caches instead of displacing the activation slice and other data.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load16_stream(const void *p) {
+    const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint2 load8_stream(const void *p) {
+    const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t *>(p));
+    return make_uint2(v.x, v.y);
+}
+__device__ __forceinline__ uint32_t load4_stream(const void *p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(p));
+}
+__device__ __forceinline__ uint32_t load2_stream(const void *p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const uint16_t *>(p));
+}
 
 }  // namespace qgemv

@@ -49,10 +49,15 @@ __global__ void __launch_bounds__(256) gemv_q4k_kernel(GemvArgs a) {
 
     int g[NC];
     bool cv[NC];
+    uint32_t hoff[NC], qoff[NC];             // byte offsets of this lane's header and codes in a row
 #pragma unroll
     for (int k = 0; k < NC; k++) {
         g[k] = split * T * NC + t + T * k;
         cv[k] = g[k] < nsub;
+        // A chunk past the end of the row reads the row's first block instead (always valid
+        // memory) and meets an all-zero activation slice below, so it adds exactly zero.
+        hoff[k] = cv[k] ? static_cast<uint32_t>(g[k] >> 3) * kQ4KBytes : 0u;
+        qoff[k] = hoff[k] + 16 + 16 * j;
     }
 
     // This lane's activation slice: 32 codes, the block scale and the block code sum per chunk.
@@ -83,23 +88,25 @@ __global__ void __launch_bounds__(256) gemv_q4k_kernel(GemvArgs a) {
         }
     }
 
+    // Row groups: this wave takes groups wave_id, wave_id + stride, ... All loads are
+    // unconditional: a row past the end of the matrix is clamped to the last row (its result
+    // is not stored), so the loop has no divergent branches around its loads.
     const int groups = (a.rows + RPW - 1) / RPW;
     const int stride = gridDim.x * wpb;
+    const int64_t row_bytes = static_cast<int64_t>(a.nb) * kQ4KBytes;
     for (int grp = blockIdx.x * wpb + wave; grp < groups; grp += stride) {
         const int row = grp * RPW + rsub;
         const bool rv = row < a.rows;
+        const uint8_t *wrow = a.w + static_cast<int64_t>(rv ? row : a.rows - 1) * row_bytes;
         uint4 hdr[NC], qs[NC];
 #pragma unroll
         for (int k = 0; k < NC; k++) {
-            hdr[k] = make_uint4(0, 0, 0, 0);
-            qs[k] = make_uint4(0, 0, 0, 0);
-            if (rv && cv[k]) {
-                const uint8_t *blk =
-                    a.w + (static_cast<int64_t>(row) * a.nb + (g[k] >> 3)) * kQ4KBytes;
-                hdr[k] = load16(blk);
-                qs[k] = load16(blk + 16 + 16 * j);
-            }
+            hdr[k] = load16(wrow + hoff[k]);
+            qs[k] = load16(wrow + qoff[k]);
         }
+        // Keep every load of the group ahead of the arithmetic: without this fence the
+        // scheduler interleaves them to save registers and waits for each load in turn.
+        __builtin_amdgcn_sched_barrier(0);
         float acc[V];
 #pragma unroll
         for (int v = 0; v < V; v++) acc[v] = 0.0f;

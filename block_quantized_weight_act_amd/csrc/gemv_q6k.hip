@@ -39,10 +39,14 @@ __global__ void __launch_bounds__(256) gemv_q6k_kernel(GemvArgs a) {
 
     int g[NC];
     bool cv[NC];
+    uint32_t boff[NC];                       // index of this lane's block body within a row
 #pragma unroll
     for (int k = 0; k < NC; k++) {
         g[k] = split * T * NC + t + T * k;
         cv[k] = g[k] < nsub;
+        // A chunk past the end of the row reads the row's first block instead (always valid
+        // memory) and meets an all-zero activation slice below, so it adds exactly zero.
+        boff[k] = cv[k] ? static_cast<uint32_t>(g[k] >> 3) : 0u;
     }
 
     uint32_t xw[V][NC][8];
@@ -76,30 +80,27 @@ __global__ void __launch_bounds__(256) gemv_q6k_kernel(GemvArgs a) {
         }
     }
 
+    // Row groups as in the Q4_K kernel: unconditional loads, the row clamped to the last one.
     const int groups = (a.rows + RPW - 1) / RPW;
     const int stride = gridDim.x * wpb;
     for (int grp = blockIdx.x * wpb + wave; grp < groups; grp += stride) {
         const int row = grp * RPW + rsub;
         const bool rv = row < a.rows;
+        const int64_t brow = static_cast<int64_t>(rv ? row : a.rows - 1) * a.nb;
         uint4 ql[NC];
         uint2 qh[NC];
-        uint32_t scw[NC];
-        uint32_t dbits[NC];
+        uint32_t scw[NC], dbits[NC];
 #pragma unroll
         for (int k = 0; k < NC; k++) {
-            ql[k] = make_uint4(0, 0, 0, 0);
-            qh[k] = make_uint2(0, 0);
-            scw[k] = 0;
-            dbits[k] = 0;
-            if (rv && cv[k]) {
-                const int64_t b = static_cast<int64_t>(row) * a.nb + (g[k] >> 3);
-                const uint8_t *body = a.w + b * kQ6KBody;
-                ql[k] = load16(body + 16 * kk);
-                qh[k] = *reinterpret_cast<const uint2 *>(body + 128 + 8 * kk);
-                scw[k] = *reinterpret_cast<const uint32_t *>(body + 192 + 4 * (kk >> 1));
-                dbits[k] = dplane[b];
-            }
+            const int64_t b = brow + boff[k];
+            const uint8_t *body = a.w + b * kQ6KBody;
+            ql[k] = load16(body + 16 * kk);
+            qh[k] = *reinterpret_cast<const uint2 *>(body + 128 + 8 * kk);
+            scw[k] = *reinterpret_cast<const uint32_t *>(body + 192 + 4 * (kk >> 1));
+            dbits[k] = dplane[b];
         }
+        // all of the group's loads stay ahead of the arithmetic
+        __builtin_amdgcn_sched_barrier(0);
         float acc[V];
 #pragma unroll
         for (int v = 0; v < V; v++) acc[v] = 0.0f;

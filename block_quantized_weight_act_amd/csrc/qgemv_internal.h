@@ -48,6 +48,9 @@ hipError_t launch_quantize_q4k(const float *w, uint8_t *out, int64_t rows, int64
 hipError_t launch_quantize_q6k(const float *w, uint8_t *out, int64_t rows, int64_t cols,
                                hipStream_t stream);
 
+hipError_t launch_read_probe(const void *buf, int64_t bytes, uint32_t *sink, int blocks,
+                             hipStream_t stream);
+
 // Whether a (lanes, chunks, nvec) combination has a compiled kernel.
 bool gemv_variant_exists(int lanes, int chunks, int nvec);
 

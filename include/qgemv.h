@@ -56,7 +56,7 @@
  *    Launch failures return QGEMV_EHIP with the HIP message available from
  *    qgemv_last_error() (per thread). Faults inside a kernel surface at the
  *    caller's next synchronization.
- *  - Shapes: cols a positive multiple of 256, rows >= 1, 1 <= nvec <= 8,
+ *  - Shapes: cols a positive multiple of 256, 1 <= rows <= 2^30, 1 <= nvec <= 8,
  *    rows * cols / 256 < 2^31 super-blocks.
  *  - Alignment: w and xq 16 bytes, xd and y 4 bytes.
  *  - Outputs must not overlap inputs.
@@ -212,6 +212,16 @@ size_t qgemv_plan_workspace_bytes(const qgemv_plan *plan, int64_t rows, int64_t 
 int qgemv_batch_plan(int wtype, const void *w, const int8_t *xq, const float *xd, float *y,
                      int64_t rows, int64_t cols, int32_t nvec, const qgemv_plan *plan,
                      void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Measurement: read `bytes` (a multiple of 16) of device memory once with 16-byte loads
+ * and nothing else, on `blocks` workgroups of 256 threads (a grid-stride loop). Its rate
+ * is the practical read ceiling the GEMV is compared with (oxinfer README, "Performance":
+ * machine read bandwidth measured apart from the kernels). sink: one device uint32 that is
+ * written only for an input whose XOR is a fixed unlikely value.
+ */
+int qgemv_read_probe(const void *buf, size_t bytes, uint32_t *sink, int32_t blocks,
+                     hipStream_t stream);
 
 #ifdef __cplusplus
 }
