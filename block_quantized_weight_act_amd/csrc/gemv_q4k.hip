@@ -14,9 +14,12 @@
 //  * T consecutive lanes share a row; lane t takes chunks t, t + T, ... (NC of them), so its
 //    columns are the same for every row it visits: the activation codes, scales and block
 //    sums it needs stay in VGPRs for the whole kernel and are read from memory once.
-//  * 8 consecutive lanes read the 128 code bytes of one super-block with one 16-byte load
-//    each (a contiguous 128-byte run); the 16-byte header (d, dmin, packed 6-bit scales) is
-//    one more 16-byte load, the same address for those 8 lanes.
+//  * The tensor keeps codes and headers in separate planes. 8 consecutive lanes read the 128
+//    code bytes of one super-block with one 16-byte load each (a contiguous 128-byte run that
+//    no other load touches, so it is read with a nontemporal load and streamed past the
+//    caches); the 16-byte header (d, dmin, packed 6-bit scales) is one ordinary 16-byte load
+//    from the header plane, the same address for those 8 lanes, and stays cached for the
+//    neighbouring blocks whose headers share its cache line.
 //  * After the chunks of a row, the T lanes' float sums are combined with a log2(T)-step
 //    butterfly; lane t < nvec writes vector t's output.
 //  * Waves walk row groups with a grid-wide stride. blockIdx.y selects a column chunk
@@ -49,15 +52,16 @@ __global__ void __launch_bounds__(256) gemv_q4k_kernel(GemvArgs a) {
 
     int g[NC];
     bool cv[NC];
-    uint32_t hoff[NC], qoff[NC];             // byte offsets of this lane's header and codes in a row
+    uint32_t hoff[NC], qoff[NC];             // byte offsets of this lane's header / codes in a row
 #pragma unroll
     for (int k = 0; k < NC; k++) {
         g[k] = split * T * NC + t + T * k;
         cv[k] = g[k] < nsub;
         // A chunk past the end of the row reads the row's first block instead (always valid
         // memory) and meets an all-zero activation slice below, so it adds exactly zero.
-        hoff[k] = cv[k] ? static_cast<uint32_t>(g[k] >> 3) * kQ4KBytes : 0u;
-        qoff[k] = hoff[k] + 16 + 16 * j;
+        const uint32_t b = cv[k] ? static_cast<uint32_t>(g[k] >> 3) : 0u;
+        hoff[k] = b * 16;
+        qoff[k] = b * 128 + 16 * j;
     }
 
     // This lane's activation slice: 32 codes, the block scale and the block code sum per chunk.
@@ -93,16 +97,18 @@ __global__ void __launch_bounds__(256) gemv_q4k_kernel(GemvArgs a) {
     // is not stored), so the loop has no divergent branches around its loads.
     const int groups = (a.rows + RPW - 1) / RPW;
     const int stride = gridDim.x * wpb;
-    const int64_t row_bytes = static_cast<int64_t>(a.nb) * kQ4KBytes;
+    const uint8_t *hplane = a.w + static_cast<int64_t>(a.rows) * a.nb * 128;
     for (int grp = blockIdx.x * wpb + wave; grp < groups; grp += stride) {
         const int row = grp * RPW + rsub;
         const bool rv = row < a.rows;
-        const uint8_t *wrow = a.w + static_cast<int64_t>(rv ? row : a.rows - 1) * row_bytes;
+        const int64_t brow = static_cast<int64_t>(rv ? row : a.rows - 1) * a.nb;
+        const uint8_t *qrow = a.w + brow * 128;
+        const uint8_t *hrow = hplane + brow * 16;
         uint4 hdr[NC], qs[NC];
 #pragma unroll
         for (int k = 0; k < NC; k++) {
-            hdr[k] = load16(wrow + hoff[k]);
-            qs[k] = load16(wrow + qoff[k]);
+            hdr[k] = load16(hrow + hoff[k]);
+            qs[k] = load16_stream(qrow + qoff[k]);
         }
         // Keep every load of the group ahead of the arithmetic: without this fence the
         // scheduler interleaves them to save registers and waits for each load in turn.

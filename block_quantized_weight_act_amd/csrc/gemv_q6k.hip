@@ -14,9 +14,11 @@
 // sub-block and the sum over the two sub-blocks of a chunk stays below 2^24, so its
 // float32 conversion is exact as well.
 //
-// The 208-byte bodies are 16-byte aligned because the fp16 super-scales live in their own
-// plane after the bodies, so every load here is a naturally aligned 16-, 8-, 4- or 2-byte
-// load.
+// The tensor keeps each field in its own plane (low bits, high bits, scales, super-scales),
+// so every load is naturally aligned, and the low- and high-bit runs that 8 consecutive lanes
+// read (128 and 64 contiguous bytes) are touched by no other load: they are read with
+// nontemporal loads and streamed past the caches, while the small scale and super-scale
+// loads stay cached for the neighbouring blocks that share their lines.
 #include "device_common.h"
 #include "qgemv_internal.h"
 
@@ -34,12 +36,14 @@ __global__ void __launch_bounds__(256) gemv_q6k_kernel(GemvArgs a) {
     const int kk = t & 7;                    // chunk inside the super-block
     const int nsub = a.nchunks;              // 32-column blocks per row
     const int64_t cols = static_cast<int64_t>(nsub) * 32;
-    const uint16_t *dplane = reinterpret_cast<const uint16_t *>(
-        a.w + static_cast<int64_t>(a.rows) * a.nb * kQ6KBody);
+    const int64_t nblocks = static_cast<int64_t>(a.rows) * a.nb;
+    const uint8_t *hplane = a.w + nblocks * 128;      // high bits, 64 bytes per block
+    const uint8_t *splane = a.w + nblocks * 192;      // sub-scales, 16 bytes per block
+    const uint16_t *dplane = reinterpret_cast<const uint16_t *>(a.w + nblocks * 208);
 
     int g[NC];
     bool cv[NC];
-    uint32_t boff[NC];                       // index of this lane's block body within a row
+    uint32_t boff[NC];                       // index of this lane's block within a row
 #pragma unroll
     for (int k = 0; k < NC; k++) {
         g[k] = split * T * NC + t + T * k;
@@ -93,10 +97,9 @@ __global__ void __launch_bounds__(256) gemv_q6k_kernel(GemvArgs a) {
 #pragma unroll
         for (int k = 0; k < NC; k++) {
             const int64_t b = brow + boff[k];
-            const uint8_t *body = a.w + b * kQ6KBody;
-            ql[k] = load16(body + 16 * kk);
-            qh[k] = *reinterpret_cast<const uint2 *>(body + 128 + 8 * kk);
-            scw[k] = *reinterpret_cast<const uint32_t *>(body + 192 + 4 * (kk >> 1));
+            ql[k] = load16_stream(a.w + b * 128 + 16 * kk);
+            qh[k] = load8_stream(hplane + b * 64 + 8 * kk);
+            scw[k] = *reinterpret_cast<const uint32_t *>(splane + b * 16 + 4 * (kk >> 1));
             dbits[k] = dplane[b];
         }
         // all of the group's loads stay ahead of the arithmetic

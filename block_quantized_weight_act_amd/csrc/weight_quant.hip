@@ -55,13 +55,13 @@ __global__ void __launch_bounds__(256) quantize_q4k_kernel(const float *__restri
         const float q = step > 0.0f ? clampf(rintf((v[i] + off) / step), 0.0f, 15.0f) : 0.0f;
         codes |= static_cast<uint32_t>(q) << (8 * i);
     }
-    uint8_t *dst = out + blk * kQ4KBytes;
-    // Weights 32j + 4(lane%8) + i: lanes with lane%8 < 4 hold the low nibbles (columns
-    // 32j + t, t < 16) and their partner lane + 4 the high nibbles (32j + 16 + t) of the
-    // same 4 bytes 16 + 16j + 4(lane%4) .. +3.
+    // Codes plane: block blk's 128 code bytes at 128 * blk. Weights 32j + 4(lane%8) + i: lanes
+    // with lane%8 < 4 hold the low nibbles (columns 32j + t, t < 16) and their partner lane + 4
+    // the high nibbles (32j + 16 + t) of the same 4 code bytes 16j + 4(lane%4) .. +3.
+    uint8_t *codes_out = out + blk * 128;
     const uint32_t partner = __shfl_xor(codes, 4, 64);
     if ((lane & 4) == 0)
-        *reinterpret_cast<uint32_t *>(dst + 16 + 16 * j + 4 * (lane & 3)) = codes | (partner << 4);
+        *reinterpret_cast<uint32_t *>(codes_out + 16 * j + 4 * (lane & 3)) = codes | (partner << 4);
     // Header: sc/m low nibbles at bits 4j of words 1 and 2, high 2 bits at bits 2j and
     // 16 + 2j of word 3. Lane 8j holds sub-block j's values.
     const bool lead = (lane & 7) == 0;
@@ -71,7 +71,10 @@ __global__ void __launch_bounds__(256) quantize_q4k_kernel(const float *__restri
         lead ? ((static_cast<uint32_t>(sc) >> 4) << (2 * j)) |
                    ((static_cast<uint32_t>(m) >> 4) << (16 + 2 * j))
              : 0u);
-    if (lane == 0) *reinterpret_cast<uint4 *>(dst) = make_uint4(dh | (mh << 16), wa, wb, wc);
+    // Header plane: block blk's 16 header bytes at 128 * nblocks + 16 * blk.
+    if (lane == 0)
+        *reinterpret_cast<uint4 *>(out + nblocks * 128 + blk * 16) =
+            make_uint4(dh | (mh << 16), wa, wb, wc);
 }
 
 // Q6_K: sub-block j (16 weights) = lanes 4j .. 4j+3.
@@ -100,30 +103,31 @@ __global__ void __launch_bounds__(256) quantize_q6k_kernel(const float *__restri
     for (int i = 0; i < 4; i++)
         q[i] = step != 0.0f ? static_cast<int>(clampf(rintf(v[i] / step), -32.0f, 31.0f)) + 32 : 32;
 
-    uint8_t *body = out + blk * kQ6KBody;
+    // Planes of block blk: low bits at 128 * blk, high bits at 128 N + 64 * blk, sub-scales at
+    // 192 N + 16 * blk, d at 208 N + 2 * blk (N = nblocks).
+    uint8_t *low_out = out + blk * 128;
+    uint8_t *high_out = out + nblocks * 128 + blk * 64;
+    uint8_t *sc_out = out + nblocks * 192 + blk * 16;
     // Weight 4*lane + i = 32k + 16g + t with k = lane/8, g = (lane%8)/4, t = 4(lane%4) + i.
     const int k = lane >> 3, g = (lane >> 2) & 1, s4 = lane & 3;
     uint32_t low = 0, high = 0;
 #pragma unroll
     for (int i = 0; i < 4; i++) {
         low |= static_cast<uint32_t>(q[i] & 15) << (8 * i);
-        // high 2 bits of weight 32k + 16g + 4*s4 + i: bits 2*s4 of byte 128 + 8k + 4g + i
+        // high 2 bits of weight 32k + 16g + 4*s4 + i: bits 2*s4 of high-bit byte 8k + 4g + i
         high |= static_cast<uint32_t>((q[i] >> 4) & 3) << (8 * i + 2 * s4);
     }
     const uint32_t partner = __shfl_xor(low, 4, 64);
-    if (g == 0) *reinterpret_cast<uint32_t *>(body + 16 * k + 4 * s4) = low | (partner << 4);
+    if (g == 0) *reinterpret_cast<uint32_t *>(low_out + 16 * k + 4 * s4) = low | (partner << 4);
     high = group_or<4>(high);
-    if (s4 == 0) *reinterpret_cast<uint32_t *>(body + 128 + 8 * k + 4 * g) = high;
-    // sub-scales: lane 4j holds sc_j; bytes 192 + j, four per 32-bit word
+    if (s4 == 0) *reinterpret_cast<uint32_t *>(high_out + 8 * k + 4 * g) = high;
+    // sub-scales: lane 4j holds sc_j, sub-scale byte j; four per 32-bit word
     const int jj = lane >> 2;
     const uint32_t scb = group_or<16>((lane & 3) == 0
                                           ? (static_cast<uint32_t>(sc) & 0xFFu) << (8 * (jj & 3))
                                           : 0u);
-    if ((lane & 15) == 0) *reinterpret_cast<uint32_t *>(body + 192 + 4 * (lane >> 4)) = scb;
-    if (lane == 0) {
-        uint16_t *dplane = reinterpret_cast<uint16_t *>(out + nblocks * kQ6KBody);
-        dplane[blk] = static_cast<uint16_t>(dh);
-    }
+    if ((lane & 15) == 0) *reinterpret_cast<uint32_t *>(sc_out + 4 * (lane >> 4)) = scb;
+    if (lane == 0) reinterpret_cast<uint16_t *>(out + nblocks * 208)[blk] = static_cast<uint16_t>(dh);
 }
 
 hipError_t launch_quantize_q4k(const float *w, uint8_t *out, int64_t rows, int64_t cols,

@@ -17,28 +17,34 @@
  *
  * Formats (all multi-byte fields little-endian):
  *
- *  Q4_K tensor: rows x (cols/256) super-blocks of 144 bytes, row-major. One
- *  super-block covers 256 consecutive weights of a row; sub-block j
- *  (j = 0..7) is weights 32j .. 32j+31.
- *    [0,2)    d     fp16 super-scale of the sub-scales
- *    [2,4)    dmin  fp16 super-scale of the sub-mins
- *    [4,8)    low 4 bits of sc_j at byte 4 + j/2, bit 4*(j%2)
- *    [8,12)   low 4 bits of m_j  at byte 8 + j/2, bit 4*(j%2)
- *    [12,14)  high 2 bits of sc_j at byte 12 + j/4, bit 2*(j%4)
- *    [14,16)  high 2 bits of m_j  at byte 14 + j/4, bit 2*(j%4)
- *    [16,144) 4-bit codes: weight 32j + 16h + t (h = 0,1; t < 16) is the
- *             low (h = 0) or high (h = 1) nibble of byte 16 + 16j + t
+ *  A super-block covers 256 consecutive weights of a row; block i of a
+ *  tensor is block b of row r with i = r * cols/256 + b, and N = rows *
+ *  cols/256 is the number of blocks. Each field of a block lives in a plane of
+ *  its own, in block order, so that every plane is read with aligned,
+ *  contiguous loads.
+ *
+ *  Q4_K tensor (144 bytes per block): codes plane [0, 128 N), header plane
+ *  [128 N, 144 N). Sub-block j (j = 0..7) is weights 32j .. 32j+31.
+ *    header of block i, at 128 N + 16 i:
+ *      [0,2)    d     fp16 super-scale of the sub-scales
+ *      [2,4)    dmin  fp16 super-scale of the sub-mins
+ *      [4,8)    low 4 bits of sc_j at byte 4 + j/2, bit 4*(j%2)
+ *      [8,12)   low 4 bits of m_j  at byte 8 + j/2, bit 4*(j%2)
+ *      [12,14)  high 2 bits of sc_j at byte 12 + j/4, bit 2*(j%4)
+ *      [14,16)  high 2 bits of m_j  at byte 14 + j/4, bit 2*(j%4)
+ *    codes of block i, at 128 i: weight 32j + 16h + t (h = 0,1; t < 16) is
+ *      the low (h = 0) or high (h = 1) nibble of byte 16j + t
  *    weight = d * sc_j * q - dmin * m_j
  *
- *  Q6_K tensor: two planes. First rows x (cols/256) bodies of 208 bytes
- *  (block (r, b) at byte 208 * (r * cols/256 + b)), then as many fp16
- *  super-scales d (block (r, b) at element r * cols/256 + b). 210 bytes per
- *  256 weights in total. Sub-block j (j = 0..15) is weights 16j .. 16j+15.
- *    [0,128)   low 4 bits: weight 32k + 16g + t (k < 8, g = 0,1, t < 16) is
- *              nibble g of byte 16k + t
- *    [128,192) high 2 bits: weight 32k + 16g + 4s + c (s, c < 4) is bits
- *              2s .. 2s+1 of byte 128 + 8k + 4g + c
- *    [192,208) sc_j, signed int8, at byte 192 + j
+ *  Q6_K tensor (210 bytes per block): low-bit plane [0, 128 N), high-bit
+ *  plane [128 N, 192 N), sub-scale plane [192 N, 208 N), super-scale plane
+ *  [208 N, 210 N). Sub-block j (j = 0..15) is weights 16j .. 16j+15.
+ *    low bits of block i, at 128 i: weight 32k + 16g + t (k < 8, g = 0,1,
+ *      t < 16) is nibble g of byte 16k + t
+ *    high bits of block i, at 128 N + 64 i: weight 32k + 16g + 4s + c
+ *      (s, c < 4) is bits 2s .. 2s+1 of byte 8k + 4g + c
+ *    sub-scales of block i, at 192 N + 16 i: sc_j, signed int8, at byte j
+ *    d of block i: fp16 at 208 N + 2 i
  *    weight = d * sc_j * (q - 32), q in [0, 63]
  *
  *  Activations: codes xq int8 [nvec][cols] in [-127, 127] and scales xd

@@ -8,10 +8,11 @@ integer partials). The arithmetic lives in the C file; this module only moves
 numpy arrays in and out. `build()` compiles the C file with gcc into
 `oracle/_build/liboracle.so`; loading builds it when it is missing.
 
-Byte layouts (restated in the C file):
-  Q4_K tensor  = rows x (cols/256) blocks of 144 bytes, row-major.
-  Q6_K tensor  = rows x (cols/256) bodies of 208 bytes, then the same number of
-                 fp16 super-scales d (two planes, 210 bytes per 256 weights).
+Byte layouts (restated in the C file). N = rows * cols/256 super-blocks, block i = r*cols/256 + b:
+  Q4_K tensor  = codes plane (128 bytes per block) then header plane (16 bytes per block);
+                 one block's "image" is its 16 header bytes followed by its 128 code bytes.
+  Q6_K tensor  = low-bit plane (128), high-bit plane (64), scale plane (16), d plane (2 bytes
+                 per block); one block's "body" is its low bits, high bits and scales (208 bytes).
   activations  = int8 codes [nvec][cols] and float32 scales [nvec][cols/32].
 """
 
@@ -80,11 +81,15 @@ def load(path: str | None = None):
             "orc_q6k_pack_block": (None, [i8p, u8p, u8p]),
             "orc_q6k_unpack_block": (None, [u8p, i8p, u8p]),
             "orc_quantize_q4k": (None, [f32p, i64, i64, u8p]),
-            "orc_quantize_q6k": (None, [f32p, i64, i64, u8p, u16p, ctypes.c_int]),
+            "orc_quantize_q6k": (None, [f32p, i64, i64, u8p, ctypes.c_int]),
             "orc_dequant_q4k": (None, [u8p, i64, i64, f64p]),
-            "orc_dequant_q6k": (None, [u8p, u16p, i64, i64, f64p]),
+            "orc_dequant_q6k": (None, [u8p, i64, i64, f64p]),
             "orc_gemv_q4k": (None, [u8p, i64, i64, i32, i8p, f32p, i32p, i32p, f64p, f64p]),
-            "orc_gemv_q6k": (None, [u8p, u16p, i64, i64, i32, i8p, f32p, i32p, f64p, f64p]),
+            "orc_gemv_q6k": (None, [u8p, i64, i64, i32, i8p, f32p, i32p, f64p, f64p]),
+            "orc_q4k_get_block": (None, [u8p, i64, i64, u8p]),
+            "orc_q4k_put_block": (None, [u8p, i64, i64, u8p]),
+            "orc_q6k_get_block": (None, [u8p, i64, i64, u8p, u16p]),
+            "orc_q6k_put_block": (None, [u8p, i64, i64, u8p, ctypes.c_uint16]),
             "orc_bruteforce": (None, [f64p, i64, i64, i32, i8p, f32p, f64p]),
         }
         for name, (res, args) in sig.items():
@@ -173,20 +178,61 @@ def q6k_unpack_block(body, lib=None):
     return sc, q
 
 
-def q6k_planes(buf, rows: int, cols: int):
-    """Split a Q6_K tensor (uint8, 210 bytes per 256 weights) into (bodies, d plane)."""
-    nb = cols // QK
-    buf = np.ascontiguousarray(buf, dtype=np.uint8).reshape(-1)
-    if buf.size != rows * nb * Q6K_BYTES:
-        raise ValueError("Q6_K tensor has %d bytes, expected %d" % (buf.size, rows * nb * Q6K_BYTES))
-    bodies = buf[:rows * nb * Q6K_BODY]
-    dplane = buf[rows * nb * Q6K_BODY:].view(np.uint16)
-    return bodies, dplane
+def tensor_bytes(wtype: str, rows: int, cols: int) -> int:
+    return rows * (cols // QK) * (Q4K_BYTES if wtype == "q4k" else Q6K_BYTES)
 
 
-def q6k_join(bodies, dplane) -> np.ndarray:
-    return np.concatenate([np.ascontiguousarray(bodies, np.uint8).reshape(-1),
-                           np.ascontiguousarray(dplane, np.uint16).reshape(-1).view(np.uint8)])
+def q4k_get_block(buf, nblocks: int, i: int, lib=None) -> np.ndarray:
+    """The 144-byte image (header, codes) of block i of a Q4_K tensor of nblocks blocks."""
+    lib = lib or load()
+    buf = np.ascontiguousarray(buf, dtype=np.uint8)
+    assert buf.size == nblocks * Q4K_BYTES
+    img = np.empty(Q4K_BYTES, dtype=np.uint8)
+    lib.orc_q4k_get_block(_p(buf, ctypes.c_uint8), nblocks, i, _p(img, ctypes.c_uint8))
+    return img
+
+
+def q4k_tensor(images, lib=None) -> np.ndarray:
+    """A Q4_K tensor from a list of 144-byte block images (block i = images[i])."""
+    lib = lib or load()
+    n = len(images)
+    out = np.zeros(n * Q4K_BYTES, dtype=np.uint8)
+    for i, img in enumerate(images):
+        img = np.ascontiguousarray(img, dtype=np.uint8)
+        lib.orc_q4k_put_block(_p(out, ctypes.c_uint8), n, i, _p(img, ctypes.c_uint8))
+    return out
+
+
+def q6k_get_block(buf, nblocks: int, i: int, lib=None):
+    """(208-byte body, fp16 bits of d) of block i of a Q6_K tensor of nblocks blocks."""
+    lib = lib or load()
+    buf = np.ascontiguousarray(buf, dtype=np.uint8)
+    assert buf.size == nblocks * Q6K_BYTES
+    body = np.empty(Q6K_BODY, dtype=np.uint8)
+    d = np.zeros(1, dtype=np.uint16)
+    lib.orc_q6k_get_block(_p(buf, ctypes.c_uint8), nblocks, i, _p(body, ctypes.c_uint8),
+                          _p(d, ctypes.c_uint16))
+    return body, int(d[0])
+
+
+def q6k_tensor(bodies, d16s, lib=None) -> np.ndarray:
+    """A Q6_K tensor from lists of 208-byte bodies and fp16 bits of d (block i = index i)."""
+    lib = lib or load()
+    n = len(bodies)
+    out = np.zeros(n * Q6K_BYTES, dtype=np.uint8)
+    for i, (body, d) in enumerate(zip(bodies, d16s)):
+        body = np.ascontiguousarray(body, dtype=np.uint8)
+        lib.orc_q6k_put_block(_p(out, ctypes.c_uint8), n, i, _p(body, ctypes.c_uint8), int(d))
+    return out
+
+
+def blocks_of(wtype: str, buf, rows: int, cols: int, lib=None):
+    """All blocks of a tensor: Q4_K -> [N][144] images; Q6_K -> ([N][208] bodies, [N] d bits)."""
+    n = rows * (cols // QK)
+    if wtype == "q4k":
+        return np.stack([q4k_get_block(buf, n, i, lib=lib) for i in range(n)])
+    got = [q6k_get_block(buf, n, i, lib=lib) for i in range(n)]
+    return np.stack([g[0] for g in got]), np.array([g[1] for g in got], dtype=np.uint16)
 
 
 # ------------------------------------------------------ weight quantizers --
@@ -201,29 +247,25 @@ def quantize_q4k(w, lib=None) -> np.ndarray:
 
 
 def quantize_q6k(w, negate_scales: bool = False, lib=None) -> np.ndarray:
-    """w float32 [rows][cols] -> Q6_K tensor, uint8 [rows * cols/256 * 210] (two planes)."""
+    """w float32 [rows][cols] -> Q6_K tensor, uint8 [rows * cols/256 * 210] (four planes)."""
     lib = lib or load()
     w = np.ascontiguousarray(w, dtype=np.float32)
     rows, cols = w.shape
-    nb = cols // QK
-    bodies = np.empty(rows * nb * Q6K_BODY, dtype=np.uint8)
-    dplane = np.empty(rows * nb, dtype=np.uint16)
-    lib.orc_quantize_q6k(_p(w, ctypes.c_float), rows, cols, _p(bodies, ctypes.c_uint8),
-                         _p(dplane, ctypes.c_uint16), int(bool(negate_scales)))
-    return q6k_join(bodies, dplane)
+    out = np.empty(rows * (cols // QK) * Q6K_BYTES, dtype=np.uint8)
+    lib.orc_quantize_q6k(_p(w, ctypes.c_float), rows, cols, _p(out, ctypes.c_uint8),
+                         int(bool(negate_scales)))
+    return out
 
 
 def dequantize(wtype: str, wbuf, rows: int, cols: int, lib=None) -> np.ndarray:
     """Dequantized weights, float64 [rows][cols]."""
     lib = lib or load()
     out = np.empty((rows, cols), dtype=np.float64)
-    if wtype == "q4k":
-        wbuf = np.ascontiguousarray(wbuf, dtype=np.uint8)
-        lib.orc_dequant_q4k(_p(wbuf, ctypes.c_uint8), rows, cols, _p(out, ctypes.c_double))
-    else:
-        bodies, dplane = q6k_planes(wbuf, rows, cols)
-        lib.orc_dequant_q6k(_p(bodies, ctypes.c_uint8), _p(dplane, ctypes.c_uint16), rows, cols,
-                            _p(out, ctypes.c_double))
+    wbuf = np.ascontiguousarray(wbuf, dtype=np.uint8).reshape(-1)
+    if wbuf.size != tensor_bytes(wtype, rows, cols):
+        raise ValueError("tensor has %d bytes, expected %d" % (wbuf.size, tensor_bytes(wtype, rows, cols)))
+    fn = lib.orc_dequant_q4k if wtype == "q4k" else lib.orc_dequant_q6k
+    fn(_p(wbuf, ctypes.c_uint8), rows, cols, _p(out, ctypes.c_double))
     return out
 
 
@@ -242,10 +284,12 @@ def gemv(wtype: str, wbuf, rows: int, cols: int, xq, xd, partials: bool = False,
     y = np.empty((nvec, rows), dtype=np.float64)
     bnd = np.empty((nvec, rows), dtype=np.float64) if bound else None
     out = {"y": y}
+    wbuf = np.ascontiguousarray(wbuf, dtype=np.uint8).reshape(-1)
+    if wbuf.size != tensor_bytes(wtype, rows, cols):
+        raise ValueError("tensor has %d bytes, expected %d" % (wbuf.size, tensor_bytes(wtype, rows, cols)))
     if wtype == "q4k":
         P = np.empty((nvec, rows, cols // 32), dtype=np.int32) if partials else None
         S = np.empty((nvec, cols // 32), dtype=np.int32) if partials else None
-        wbuf = np.ascontiguousarray(wbuf, dtype=np.uint8)
         lib.orc_gemv_q4k(_p(wbuf, ctypes.c_uint8), rows, cols, nvec, _p(xq, ctypes.c_int8),
                          _p(xd, ctypes.c_float), _p(P, ctypes.c_int32), _p(S, ctypes.c_int32),
                          _p(y, ctypes.c_double), _p(bnd, ctypes.c_double))
@@ -253,10 +297,9 @@ def gemv(wtype: str, wbuf, rows: int, cols: int, xq, xd, partials: bool = False,
             out["P"], out["S"] = P, S
     elif wtype == "q6k":
         P = np.empty((nvec, rows, cols // 16), dtype=np.int32) if partials else None
-        bodies, dplane = q6k_planes(wbuf, rows, cols)
-        lib.orc_gemv_q6k(_p(bodies, ctypes.c_uint8), _p(dplane, ctypes.c_uint16), rows, cols,
-                         nvec, _p(xq, ctypes.c_int8), _p(xd, ctypes.c_float),
-                         _p(P, ctypes.c_int32), _p(y, ctypes.c_double), _p(bnd, ctypes.c_double))
+        lib.orc_gemv_q6k(_p(wbuf, ctypes.c_uint8), rows, cols, nvec, _p(xq, ctypes.c_int8),
+                         _p(xd, ctypes.c_float), _p(P, ctypes.c_int32), _p(y, ctypes.c_double),
+                         _p(bnd, ctypes.c_double))
         if partials:
             out["P"] = P
     else:
@@ -287,13 +330,33 @@ def bruteforce(what, xq, xd, lib=None) -> np.ndarray:
     return y
 
 
+def planes(wtype: str, wbuf, rows: int, cols: int) -> list:
+    """The planes of a tensor as [rows][bytes per row] views (Q4_K: codes, headers; Q6_K: low
+    bits, high bits, scales, d)."""
+    nb = cols // QK
+    n = rows * nb
+    wbuf = np.ascontiguousarray(wbuf, dtype=np.uint8).reshape(-1)
+    widths = [128, 16] if wtype == "q4k" else [128, 64, 16, 2]
+    out, off = [], 0
+    for wdt in widths:
+        out.append(wbuf[off:off + n * wdt].reshape(rows, nb * wdt))
+        off += n * wdt
+    return out
+
+
+def from_planes(parts) -> np.ndarray:
+    return np.concatenate([np.ascontiguousarray(p).reshape(-1) for p in parts])
+
+
 def row_slice(wtype: str, wbuf, rows: int, cols: int, r0: int, r1: int) -> np.ndarray:
     """The tensor of rows r0 .. r1 - 1 of a quantized tensor, in the same format."""
-    nb = cols // QK
-    if wtype == "q4k":
-        return np.ascontiguousarray(wbuf, np.uint8).reshape(rows, nb * Q4K_BYTES)[r0:r1].reshape(-1)
-    bodies, dplane = q6k_planes(wbuf, rows, cols)
-    return q6k_join(bodies.reshape(rows, nb * Q6K_BODY)[r0:r1], dplane.reshape(rows, nb)[r0:r1])
+    return from_planes([p[r0:r1] for p in planes(wtype, wbuf, rows, cols)])
+
+
+def concat_rows(wtype: str, parts, cols: int) -> np.ndarray:
+    """One tensor from tensors of consecutive row ranges [(buf, rows), ...]."""
+    per = [planes(wtype, b, r, cols) for b, r in parts]
+    return from_planes([np.concatenate([p[k] for p in per]) for k in range(len(per[0]))])
 
 
 def gemv_threaded(wtype: str, wbuf, rows: int, cols: int, xq, xd, threads: int) -> np.ndarray:

@@ -139,16 +139,22 @@ void orc_quantize_act(const float *x, int64_t cols, int32_t nvec, int8_t *xq, fl
 }
 
 /* ---------------------------------------------------------- Q4_K layout --- */
-/* One 144-byte super-block of 256 weights (sub-block j = weights 32j..32j+31):
- *   bytes [0,2)    d    (fp16, little-endian)  super-scale of the sub-scales
- *   bytes [2,4)    dmin (fp16)                 super-scale of the sub-mins
- *   bytes [4,8)    low 4 bits of sc_j: byte 4 + j/2, bits 4*(j%2) .. +3
- *   bytes [8,12)   low 4 bits of m_j : byte 8 + j/2, bits 4*(j%2) .. +3
- *   bytes [12,14)  high 2 bits of sc_j: byte 12 + j/4, bits 2*(j%4) .. +1
- *   bytes [14,16)  high 2 bits of m_j : byte 14 + j/4, bits 2*(j%4) .. +1
- *   bytes [16,144) codes: weight i = 32j + 16h + t (h in {0,1}, t < 16) is
+/* One Q4_K super-block of 256 weights (sub-block j = weights 32j..32j+31) is
+ * 144 bytes, written here as its "block image": a 16-byte header, then 128
+ * bytes of codes.
+ *   image [0,2)    d    (fp16, little-endian)  super-scale of the sub-scales
+ *   image [2,4)    dmin (fp16)                 super-scale of the sub-mins
+ *   image [4,8)    low 4 bits of sc_j: byte 4 + j/2, bits 4*(j%2) .. +3
+ *   image [8,12)   low 4 bits of m_j : byte 8 + j/2, bits 4*(j%2) .. +3
+ *   image [12,14)  high 2 bits of sc_j: byte 12 + j/4, bits 2*(j%4) .. +1
+ *   image [14,16)  high 2 bits of m_j : byte 14 + j/4, bits 2*(j%4) .. +1
+ *   image [16,144) codes: weight i = 32j + 16h + t (h in {0,1}, t < 16) is
  *                  nibble h (h=0 low, h=1 high) of byte 16 + 16j + t.
- * Dequantized weight: d * sc_j * q_i - dmin * m_j.                          */
+ * Dequantized weight: d * sc_j * q_i - dmin * m_j.
+ *
+ * A Q4_K tensor of N = rows * cols/256 blocks (block i = r * cols/256 + b)
+ * keeps the two parts in two planes: the 128 code bytes of block i at
+ * 128 * i, then the 16 header bytes of block i at 128 * N + 16 * i.         */
 
 static int q4k_sc(const uint8_t *blk, int j) {
     int lo = (blk[4 + j / 2] >> (4 * (j % 2))) & 15;
@@ -195,15 +201,18 @@ void orc_q4k_unpack_block(const uint8_t *blk, uint16_t *d, uint16_t *dmin, uint8
 }
 
 /* ---------------------------------------------------------- Q6_K layout --- */
-/* A Q6_K tensor of R rows x nb super-blocks is two planes: R*nb bodies of 208
- * bytes (block (r, b) at offset 208 * (r*nb + b)), then R*nb fp16 super-scales
- * d. One body (sub-block j = weights 16j..16j+15, signed scale sc_j):
- *   bytes [0,128)   low 4 bits: weight i = 32k + 16g + t (k < 8, g in {0,1},
- *                   t < 16) is nibble g of byte 16k + t
- *   bytes [128,192) high 2 bits: weight i = 32k + 16g + 4s + c (s, c < 4) is
- *                   bits 2s .. 2s+1 of byte 128 + 8k + 4g + c
- *   bytes [192,208) sc_j as int8 at byte 192 + j
- * Code q_i in [0, 63]; dequantized weight: d * sc_j * (q_i - 32).            */
+/* One Q6_K super-block (sub-block j = weights 16j..16j+15, signed scale
+ * sc_j) is a 208-byte "body" plus an fp16 super-scale d:
+ *   body [0,128)   low 4 bits: weight i = 32k + 16g + t (k < 8, g in {0,1},
+ *                  t < 16) is nibble g of byte 16k + t
+ *   body [128,192) high 2 bits: weight i = 32k + 16g + 4s + c (s, c < 4) is
+ *                  bits 2s .. 2s+1 of byte 128 + 8k + 4g + c
+ *   body [192,208) sc_j as int8 at byte 192 + j
+ * Code q_i in [0, 63]; dequantized weight: d * sc_j * (q_i - 32).
+ *
+ * A Q6_K tensor of N blocks keeps four planes, 210 bytes per block in all:
+ * low bits of block i at 128 * i, high bits at 128 * N + 64 * i, scales at
+ * 192 * N + 16 * i, d at 208 * N + 2 * i.                                    */
 
 static int q6k_q(const uint8_t *body, int i) {
     int k = i / 32, g = (i % 32) / 16, t = i % 16, s = t / 4, c = t % 4;
@@ -230,6 +239,45 @@ void orc_q6k_unpack_block(const uint8_t *body, int8_t *sc, uint8_t *q) {
     for (int i = 0; i < QK; i++) q[i] = (uint8_t)q6k_q(body, i);
 }
 
+
+/* ------------------------------------------------ tensor planes <-> blocks - */
+static void q4k_get(const uint8_t *t, int64_t N, int64_t i, uint8_t *img) {
+    memcpy(img, t + 128 * N + 16 * i, 16);
+    memcpy(img + 16, t + 128 * i, 128);
+}
+
+static void q4k_put(uint8_t *t, int64_t N, int64_t i, const uint8_t *img) {
+    memcpy(t + 128 * N + 16 * i, img, 16);
+    memcpy(t + 128 * i, img + 16, 128);
+}
+
+static void q6k_get(const uint8_t *t, int64_t N, int64_t i, uint8_t *body, uint16_t *d) {
+    memcpy(body, t + 128 * i, 128);
+    memcpy(body + 128, t + 128 * N + 64 * i, 64);
+    memcpy(body + 192, t + 192 * N + 16 * i, 16);
+    *d = rd16(t + 208 * N + 2 * i);
+}
+
+static void q6k_put(uint8_t *t, int64_t N, int64_t i, const uint8_t *body, uint16_t d) {
+    memcpy(t + 128 * i, body, 128);
+    memcpy(t + 128 * N + 64 * i, body + 128, 64);
+    memcpy(t + 192 * N + 16 * i, body + 192, 16);
+    wr16(t + 208 * N + 2 * i, d);
+}
+
+void orc_q4k_get_block(const uint8_t *t, int64_t nblocks, int64_t i, uint8_t *img) {
+    q4k_get(t, nblocks, i, img);
+}
+void orc_q4k_put_block(uint8_t *t, int64_t nblocks, int64_t i, const uint8_t *img) {
+    q4k_put(t, nblocks, i, img);
+}
+void orc_q6k_get_block(const uint8_t *t, int64_t nblocks, int64_t i, uint8_t *body, uint16_t *d) {
+    q6k_get(t, nblocks, i, body, d);
+}
+void orc_q6k_put_block(uint8_t *t, int64_t nblocks, int64_t i, const uint8_t *body, uint16_t d) {
+    q6k_put(t, nblocks, i, body, d);
+}
+
 /* ------------------------------------------------------ weight quantizers - */
 /* Used to make test data; the GEMV never quantizes weights. Every decision
  * that yields an integer is taken in float32 with round-to-nearest-even.
@@ -244,7 +292,7 @@ void orc_q6k_unpack_block(const uint8_t *body, int8_t *sc, uint8_t *q) {
 void orc_quantize_q4k(const float *w, int64_t rows, int64_t cols, uint8_t *out) {
     if (cols % QK) die("cols must be a multiple of 256");
     int64_t nb = cols / QK;
-    uint8_t sc[8], m[8], q[QK];
+    uint8_t sc[8], m[8], q[QK], img[Q4K_BYTES];
     for (int64_t r = 0; r < rows; r++) {
         for (int64_t b = 0; b < nb; b++) {
             const float *wb = w + r * cols + b * QK;
@@ -277,7 +325,8 @@ void orc_quantize_q4k(const float *w, int64_t rows, int64_t cols, uint8_t *out) 
                         ? clampf(rintf((v + off) / step), 0.0f, 15.0f) : 0.0f);
                 }
             }
-            orc_q4k_pack_block(dh, mh, sc, m, q, out + (r * nb + b) * Q4K_BYTES);
+            orc_q4k_pack_block(dh, mh, sc, m, q, img);
+            q4k_put(out, rows * nb, r * nb + b, img);
         }
     }
 }
@@ -289,12 +338,12 @@ void orc_quantize_q4k(const float *w, int64_t rows, int64_t cols, uint8_t *out) 
  * negate_scales != 0 gives the equivalent encoding sc' = -sc, q' = 64 - q in
  * every sub-block that has no code 0 (same dequantized values; it exercises
  * negative scales).                                                          */
-void orc_quantize_q6k(const float *w, int64_t rows, int64_t cols, uint8_t *bodies,
-                      uint16_t *dplane, int negate_scales) {
+void orc_quantize_q6k(const float *w, int64_t rows, int64_t cols, uint8_t *out,
+                      int negate_scales) {
     if (cols % QK) die("cols must be a multiple of 256");
     int64_t nb = cols / QK;
     int8_t sc[16];
-    uint8_t q[QK];
+    uint8_t q[QK], body[Q6K_BODY];
     for (int64_t r = 0; r < rows; r++) {
         for (int64_t b = 0; b < nb; b++) {
             const float *wb = w + r * cols + b * QK;
@@ -327,8 +376,8 @@ void orc_quantize_q6k(const float *w, int64_t rows, int64_t cols, uint8_t *bodie
                     for (int i = 0; i < 16; i++) q[16 * j + i] = (uint8_t)(64 - q[16 * j + i]);
                 }
             }
-            orc_q6k_pack_block(sc, q, bodies + (r * nb + b) * Q6K_BODY);
-            dplane[r * nb + b] = dh;
+            orc_q6k_pack_block(sc, q, body);
+            q6k_put(out, rows * nb, r * nb + b, body, dh);
         }
     }
 }
@@ -336,9 +385,10 @@ void orc_quantize_q6k(const float *w, int64_t rows, int64_t cols, uint8_t *bodie
 /* ------------------------------------------------------------ dequantize -- */
 void orc_dequant_q4k(const uint8_t *w, int64_t rows, int64_t cols, double *out) {
     int64_t nb = cols / QK;
+    uint8_t blk[Q4K_BYTES];
     for (int64_t r = 0; r < rows; r++)
         for (int64_t b = 0; b < nb; b++) {
-            const uint8_t *blk = w + (r * nb + b) * Q4K_BYTES;
+            q4k_get(w, rows * nb, r * nb + b, blk);
             double d = orc_f16_to_f32(rd16(blk)), dmin = orc_f16_to_f32(rd16(blk + 2));
             for (int i = 0; i < QK; i++) {
                 int j = i / 32;
@@ -347,13 +397,14 @@ void orc_dequant_q4k(const uint8_t *w, int64_t rows, int64_t cols, double *out) 
         }
 }
 
-void orc_dequant_q6k(const uint8_t *bodies, const uint16_t *dplane, int64_t rows, int64_t cols,
-                     double *out) {
+void orc_dequant_q6k(const uint8_t *w, int64_t rows, int64_t cols, double *out) {
     int64_t nb = cols / QK;
+    uint8_t body[Q6K_BODY];
+    uint16_t dh;
     for (int64_t r = 0; r < rows; r++)
         for (int64_t b = 0; b < nb; b++) {
-            const uint8_t *body = bodies + (r * nb + b) * Q6K_BODY;
-            double d = orc_f16_to_f32(dplane[r * nb + b]);
+            q6k_get(w, rows * nb, r * nb + b, body, &dh);
+            double d = orc_f16_to_f32(dh);
             for (int i = 0; i < QK; i++)
                 out[r * cols + b * QK + i] = d * q6k_sc(body, i / 16) * (q6k_q(body, i) - 32);
         }
@@ -390,7 +441,8 @@ void orc_gemv_q4k(const uint8_t *w, int64_t rows, int64_t cols, int32_t nvec,
         for (int64_t r = 0; r < rows; r++) {
             double acc = 0.0, bnd = 0.0;
             for (int64_t b = 0; b < nb; b++) {
-                const uint8_t *blk = w + (r * nb + b) * Q4K_BYTES;
+                uint8_t blk[Q4K_BYTES];
+                q4k_get(w, rows * nb, r * nb + b, blk);
                 double d = orc_f16_to_f32(rd16(blk)), dmin = orc_f16_to_f32(rd16(blk + 2));
                 for (int j = 0; j < 8; j++) {
                     int64_t col0 = b * QK + 32 * j;
@@ -422,9 +474,8 @@ void orc_gemv_q4k(const uint8_t *w, int64_t rows, int64_t cols, int32_t nvec,
  *   P[v][r][j] = sum_i (q_i - 32) * qx_i                     (exact integer)
  *   y[v][r]    = sum_j xd_{j/2} * d * sc_j * P               (float64)
  * P is [nvec][rows][cols/16]; the other arrays as for Q4_K. */
-void orc_gemv_q6k(const uint8_t *bodies, const uint16_t *dplane, int64_t rows, int64_t cols,
-                  int32_t nvec, const int8_t *xq, const float *xd, int32_t *P,
-                  double *y, double *bound) {
+void orc_gemv_q6k(const uint8_t *w, int64_t rows, int64_t cols, int32_t nvec,
+                  const int8_t *xq, const float *xd, int32_t *P, double *y, double *bound) {
     if (cols % QK) die("cols must be a multiple of 256");
     int64_t nb = cols / QK, ns = cols / 16;
     for (int32_t v = 0; v < nvec; v++) {
@@ -433,8 +484,10 @@ void orc_gemv_q6k(const uint8_t *bodies, const uint16_t *dplane, int64_t rows, i
         for (int64_t r = 0; r < rows; r++) {
             double acc = 0.0, bnd = 0.0;
             for (int64_t b = 0; b < nb; b++) {
-                const uint8_t *body = bodies + (r * nb + b) * Q6K_BODY;
-                double d = orc_f16_to_f32(dplane[r * nb + b]);
+                uint8_t body[Q6K_BODY];
+                uint16_t dh;
+                q6k_get(w, rows * nb, r * nb + b, body, &dh);
+                double d = orc_f16_to_f32(dh);
                 for (int j = 0; j < 16; j++) {
                     int64_t col0 = b * QK + 16 * j;
                     int sc = q6k_sc(body, j);

@@ -136,7 +136,7 @@ def check_layout_goldens(lib):
         dmin = float(np.array([m16], np.uint16).view(np.float16)[0])
         j = np.arange(256) // 32
         want = d * sc[j].astype(np.float64) * q - dmin * m[j].astype(np.float64)
-        got = oracle.dequantize("q4k", blk, 1, 256, lib=lib)[0]
+        got = oracle.dequantize("q4k", oracle.q4k_tensor([blk], lib=lib), 1, 256, lib=lib)[0]
         assert np.array_equal(got, want), name
 
     p, body = read_hex_fixture("q6k_block_a.txt")
@@ -148,7 +148,7 @@ def check_layout_goldens(lib):
     gsc, gq = oracle.q6k_unpack_block(body, lib=lib)
     assert np.array_equal(gsc, sc) and np.array_equal(gq, q)
     d16 = int(p["d16"], 16)
-    tensor = oracle.q6k_join(body, np.array([d16], np.uint16))
+    tensor = oracle.q6k_tensor([body], [d16], lib=lib)
     want = 0.25 * sc[i // 16].astype(np.float64) * (q.astype(np.float64) - 32)
     assert np.array_equal(oracle.dequantize("q6k", tensor, 1, 256, lib=lib)[0], want)
 
@@ -215,7 +215,7 @@ def check_q4k_quantizer(lib, w):
     rows, cols = w.shape
     buf = oracle.quantize_q4k(w, lib=lib)
     nb = cols // 256
-    blocks = buf.reshape(rows * nb, 144)
+    blocks = oracle.blocks_of("q4k", buf, rows, cols, lib=lib)
     what = oracle.dequantize("q4k", buf, rows, cols, lib=lib).reshape(rows * nb, 8, 32)
     wb = w.astype(np.float64).reshape(rows * nb, 8, 32)
     d = _f16(blocks[:, 0:2].copy().view(np.uint16)[:, 0])
@@ -260,19 +260,19 @@ def check_q6k_quantizer(lib, w, negate=False):
         ref = oracle.quantize_q6k(w, negate_scales=False, lib=lib)
         assert np.array_equal(oracle.dequantize("q6k", buf, rows, cols, lib=lib),
                               oracle.dequantize("q6k", ref, rows, cols, lib=lib))
-        bodies, _ = oracle.q6k_planes(buf, rows, cols)
-        assert (bodies.reshape(-1, 208)[:, 192:].view(np.int8) < 0).any()
+        bodies, _ = oracle.blocks_of("q6k", buf, rows, cols, lib=lib)
+        assert (bodies[:, 192:].view(np.int8) < 0).any()
         check_q6k_quantizer(lib, w, negate=False)
         return buf
     buf = oracle.quantize_q6k(w, negate_scales=False, lib=lib)
     nb = cols // 256
-    bodies, dplane = oracle.q6k_planes(buf, rows, cols)
+    bodies, dplane = oracle.blocks_of("q6k", buf, rows, cols, lib=lib)
     d = _f16(dplane)
     what = oracle.dequantize("q6k", buf, rows, cols, lib=lib).reshape(rows * nb, 16, 16)
     wb = w.astype(np.float64).reshape(rows * nb, 16, 16)
     sc = np.zeros((rows * nb, 16))
     for b in range(rows * nb):
-        s_, _ = oracle.q6k_unpack_block(bodies[b * 208:(b + 1) * 208], lib=lib)
+        s_, _ = oracle.q6k_unpack_block(bodies[b], lib=lib)
         sc[b] = s_
     assert np.all(sc >= 0)
     step = d[:, None] * sc
@@ -341,12 +341,12 @@ def check_gemv_onehot(lib, wtype, w, cols_to_probe=(0, 17, 255, 256 + 130)):
             codes = []
             nb = cols // 256
             for r in range(rows):
+                i = r * nb + k // 256
                 if wtype == "q4k":
-                    blk = buf[(r * nb + k // 256) * 144:(r * nb + k // 256 + 1) * 144]
+                    blk = oracle.q4k_get_block(buf, rows * nb, i, lib=lib)
                     codes.append(int(oracle.q4k_unpack_block(blk, lib=lib)[4][k % 256]))
                 else:
-                    bodies, _ = oracle.q6k_planes(buf, rows, cols)
-                    body = bodies[(r * nb + k // 256) * 208:(r * nb + k // 256 + 1) * 208]
+                    body, _ = oracle.q6k_get_block(buf, rows * nb, i, lib=lib)
                     codes.append(int(oracle.q6k_unpack_block(body, lib=lib)[1][k % 256]) - 32)
             assert np.array_equal(P[:, j], np.array(codes) * int(xq[0, k]))
             assert ns == P.shape[1]
@@ -380,17 +380,18 @@ def check_gemv_special(lib):
     S = oracle.block_sums(xq)[0].astype(np.float64)
     dmin = float(np.array([0x2E66], np.uint16).view(np.float16)[0])
     want = -np.sum(xd[0].astype(np.float64) * dmin * m * S)
-    got = oracle.gemv("q4k", blk, 1, 256, xq, xd, lib=lib)["y"][0, 0]
+    got = oracle.gemv("q4k", oracle.q4k_tensor([blk], lib=lib), 1, 256, xq, xd, lib=lib)["y"][0, 0]
     assert abs(got - want) <= 1e-15 * abs(want)
     # Q4_K with dmin = 0: the pure scale path d * sc_j * P_j
     blk = oracle.q4k_pack_block(0x3C00, 0x0000, np.arange(8, dtype=np.uint8) + 1, m,
                                 np.arange(256, dtype=np.uint8) % 16, lib=lib)
-    res = oracle.gemv("q4k", blk, 1, 256, xq, xd, partials=True, lib=lib)
+    res = oracle.gemv("q4k", oracle.q4k_tensor([blk], lib=lib), 1, 256, xq, xd, partials=True,
+                      lib=lib)
     want = np.sum(xd[0].astype(np.float64) * (np.arange(8) + 1) * res["P"][0, 0])
     assert abs(res["y"][0, 0] - want) <= 1e-15 * abs(want)
     # Q6_K with every code 32: P = 0 and y = 0 exactly
     body = oracle.q6k_pack_block(np.full(16, 77, np.int8), np.full(256, 32, np.uint8), lib=lib)
-    tensor = oracle.q6k_join(body, np.array([0x3C00], np.uint16))
+    tensor = oracle.q6k_tensor([body], [0x3C00], lib=lib)
     res = oracle.gemv("q6k", tensor, 1, 256, xq, xd, partials=True, lib=lib)
     assert np.all(res["P"] == 0) and res["y"][0, 0] == 0.0
 
@@ -402,13 +403,13 @@ def check_gemv_extremes(lib):
     # Q4_K: every code 15 against every activation code 127: P = 15 * 127 * 32 = 60960
     blk = oracle.q4k_pack_block(0x3C00, 0x3C00, np.full(8, 63, np.uint8), np.full(8, 63, np.uint8),
                                 np.full(256, 15, np.uint8), lib=lib)
-    buf = np.concatenate([blk, blk])
+    buf = oracle.q4k_tensor([blk, blk], lib=lib)
     xq, xd = oracle.quantize_act(x_pos, lib=lib)
     res = oracle.gemv("q4k", buf, 1, cols, xq, xd, partials=True, lib=lib)
     assert np.all(res["P"] == 60960) and np.all(res["S"] == 127 * 32)
     # Q6_K: every code 0 (value -32) against every activation code -127: P = 32 * 127 * 16 = 65024
     body = oracle.q6k_pack_block(np.full(16, -128, np.int8), np.zeros(256, np.uint8), lib=lib)
-    tensor = oracle.q6k_join(np.concatenate([body, body]), np.array([0x3C00] * 2, np.uint16))
+    tensor = oracle.q6k_tensor([body, body], [0x3C00] * 2, lib=lib)
     xq, xd = oracle.quantize_act(x_neg, lib=lib)
     res = oracle.gemv("q6k", tensor, 1, cols, xq, xd, partials=True, lib=lib)
     assert np.all(res["P"] == 65024)

@@ -105,13 +105,8 @@ def test_workload_parity_full_size(name):
         got = gu.host(gu.quantize_weights(wl.wtype, w))
         assert np.array_equal(got, ref), "weight bytes differ in rows %d..%d" % (r0, r1)
         parts.append(ref)
-    if wl.wtype == "q4k":
-        wbuf = np.concatenate(parts)
-    else:
-        planes = [oracle.q6k_planes(p, min(chunk, wl.rows - i * chunk), wl.cols)
-                  for i, p in enumerate(parts)]
-        wbuf = oracle.q6k_join(np.concatenate([b for b, _ in planes]),
-                               np.concatenate([d for _, d in planes]))
+    wbuf = oracle.concat_rows(wl.wtype, [(p, min(chunk, wl.rows - i * chunk))
+                                         for i, p in enumerate(parts)], wl.cols)
     _check_gemv(wl.wtype, wbuf, wl.rows, wl.cols, x)
 
 
@@ -190,10 +185,10 @@ def test_integer_extremes():
     cols = 512
     blk = oracle.q4k_pack_block(0x3C00, 0x3C00, np.full(8, 63, np.uint8), np.full(8, 63, np.uint8),
                                 np.full(256, 15, np.uint8))
-    wbuf = np.tile(blk, 2 * 5)
+    wbuf = oracle.q4k_tensor([blk] * (2 * 5))
     _check_gemv("q4k", wbuf, 5, cols, np.full((1, cols), 3.0, np.float32))
     body = oracle.q6k_pack_block(np.full(16, -128, np.int8), np.zeros(256, np.uint8))
-    t6 = oracle.q6k_join(np.tile(body, 2 * 5), np.full(2 * 5, 0x3C00, np.uint16))
+    t6 = oracle.q6k_tensor([body] * (2 * 5), [0x3C00] * (2 * 5))
     _check_gemv("q6k", t6, 5, cols, np.full((1, cols), -3.0, np.float32))
 
 

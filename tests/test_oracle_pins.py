@@ -53,7 +53,7 @@ def test_q4k_subnormal_super_scale(orc):
     """sigma 0.002 puts d below fp16's smallest normal (6.1e-5)."""
     w = synth.normal_f32(99, 0, 8 * 512, 0.002).reshape(8, 512)
     buf = pins.check_q4k_quantizer(orc, w)
-    d16 = buf.reshape(-1, 144)[:, 0:2].copy().view(np.uint16)[:, 0]
+    d16 = oracle.planes("q4k", buf, 8, 512)[1].reshape(-1, 16)[:, 0:2].copy().view(np.uint16)[:, 0]
     assert np.any(d16 < 0x0400)
 
 

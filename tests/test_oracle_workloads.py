@@ -42,7 +42,9 @@ def test_outlier_rows_have_larger_super_scales(orc):
     cold = np.setdiff1d(np.arange(64), hot)[:16]
     wh = oracle.quantize_q4k(wl.weight_rows(hot[:16]))
     wc = oracle.quantize_q4k(wl.weight_rows(cold))
-    dh = oracle.f16_to_f32(wh.reshape(-1, 144)[:, :2].copy().view(np.uint16)[:, 0])
-    dc = oracle.f16_to_f32(wc.reshape(-1, 144)[:, :2].copy().view(np.uint16)[:, 0])
+    hdr_h = oracle.planes("q4k", wh, 16, wl.cols)[1].reshape(-1, 16)
+    hdr_c = oracle.planes("q4k", wc, len(cold), wl.cols)[1].reshape(-1, 16)
+    dh = oracle.f16_to_f32(hdr_h[:, :2].copy().view(np.uint16)[:, 0])
+    dc = oracle.f16_to_f32(hdr_c[:, :2].copy().view(np.uint16)[:, 0])
     ratio = np.median(dh) / np.median(dc)
     assert 8.0 < ratio < 12.5
