@@ -36,12 +36,18 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+CALIB_COPY_BYTES = 256 << 20
 COLD_BYTES = 640 * 10**6
 PROFILES = os.path.join(ROOT, "profiles")
 
 
 def parse():
     ap = argparse.ArgumentParser()
+    ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of "
+                         "'bench.py --traffic-calibration' into profiles/gemv_<workload>_traffic.json")
+    ap.add_argument("--summarize-trace", metavar="KERNEL_STATS_CSV",
+                    help="print a markdown table of a rocprofv3 --kernel-trace --stats summary")
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
@@ -49,6 +55,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--warm", action="store_true", help="reuse one weight copy (cache-warm)")
+    ap.add_argument("--traffic-calibration", action="store_true",
+                    help="also run the read probe over one weight copy and a plain 256 MiB "
+                         "device copy, the known-size kernels the HBM counters are scaled by")
     return ap.parse_args()
 
 
@@ -105,8 +114,75 @@ def cpu_baseline(wl, seconds: float) -> dict:
             "us_per_gemv_scaled_to_full": round(per * (wl.rows / rows) * 1e6, 1)}
 
 
+def _counter_rows(path):
+    import csv
+    with open(path) as f:
+        return list(csv.DictReader(f))
+
+
+def summarize_traffic(args) -> None:
+    """HBM bytes per GEMV launch from FETCH_SIZE / WRITE_SIZE (KiB per dispatch), each scaled by
+    what the same counter reads for kernels of known size in the same run: the read probe over
+    one weight copy (FETCH_SIZE) and the last ten plain 256 MiB device copies (WRITE_SIZE)."""
+    import synth
+    wl = synth.WORKLOADS[args.workload]
+    from block_quantized_weight_act_amd import qgemv_weight_bytes
+    wbytes = qgemv_weight_bytes(wl.wtype, wl.rows, wl.cols)
+    per = {}
+    for path, counter in zip(args.summarize_traffic, ("FETCH_SIZE", "WRITE_SIZE")):
+        rows = [r for r in _counter_rows(path) if r["Counter_Name"] == counter]
+        gemv = [float(r["Counter_Value"]) for r in rows if "gemv_%s_kernel" % wl.wtype in r["Kernel_Name"]]
+        probe = [float(r["Counter_Value"]) for r in rows if "read_probe_kernel" in r["Kernel_Name"]]
+        copies = [float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"]][-10:]
+        per[counter] = {"gemv_kib": sum(gemv) / len(gemv), "gemv_dispatches": len(gemv),
+                        "probe_kib": sum(probe) / len(probe), "copy_kib": sum(copies) / len(copies)}
+    f = per["FETCH_SIZE"]
+    w = per["WRITE_SIZE"]
+    fetch_factor = wbytes / (f["probe_kib"] * 1024)
+    fetch_factor_copy = CALIB_COPY_BYTES / (f["copy_kib"] * 1024)
+    write_factor = CALIB_COPY_BYTES / (w["copy_kib"] * 1024)
+    hbm = f["gemv_kib"] * 1024 * fetch_factor + w["gemv_kib"] * 1024 * write_factor
+    alg = algorithmic_bytes(wl, wbytes)["gemv"]
+    rec = {
+        "workload": wl.name, "kernel": "gemv_%s_kernel" % wl.wtype,
+        "kernel_source_sha256": kernel_source_hash(),
+        "fetch_size_kib_per_dispatch": round(f["gemv_kib"], 3),
+        "write_size_kib_per_dispatch": round(w["gemv_kib"], 3),
+        "fetch_factor": round(fetch_factor, 6),
+        "fetch_factor_from_copy": round(fetch_factor_copy, 6),
+        "write_factor": round(write_factor, 6),
+        "hbm_bytes_per_launch": int(round(hbm)),
+        "algorithmic_bytes_per_launch": alg,
+        "ratio_to_algorithmic": round(hbm / alg, 5),
+        "dispatches": f["gemv_dispatches"],
+    }
+    path = os.path.join(PROFILES, "gemv_%s_traffic.json" % wl.name)
+    with open(path, "w") as fh:
+        json.dump(rec, fh, indent=1)
+        fh.write("\n")
+    print(json.dumps(rec))
+
+
+def summarize_trace(path: str) -> None:
+    import csv
+    with open(path) as f:
+        rows = list(csv.DictReader(f))
+    print("| kernel | calls | average us | min us | max us | stddev us | % of GPU time |")
+    print("|---|---|---|---|---|---|---|")
+    for r in rows:
+        print("| `%s` | %s | %.3f | %.3f | %.3f | %.3f | %s |" % (
+            r["Name"], r["Calls"], float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
+            float(r["MaxNs"]) / 1e3, float(r["StdDev"]) / 1e3, r["Percentage"]))
+
+
 def main():
     args = parse()
+    if args.summarize_traffic:
+        summarize_traffic(args)
+        return
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
@@ -238,6 +314,16 @@ def main():
                      "algorithmic_bytes_per_launch": nbytes["gemv"]},
         "setup_s": round(setup_s, 1),
     }
+    if args.traffic_calibration:
+        sink = torch.zeros(1, dtype=torch.int32, device=dev)
+        for i in range(10):
+            qg.qgemv_read_probe(ws_list[i % copies], sink, blocks=4096)
+        src = torch.empty(CALIB_COPY_BYTES, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(10):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        out["traffic_calibration"] = {"read_probe_bytes": wbytes, "copy_bytes": CALIB_COPY_BYTES}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
     print(json.dumps(out), flush=True)

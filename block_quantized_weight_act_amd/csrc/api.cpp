@@ -55,9 +55,11 @@ int splits_for(int lanes, int chunks, int64_t cols) {
     return static_cast<int>((nchunks + per - 1) / per);
 }
 
-// Resident wavefronts the launch aims for: 256 CUs x 16 waves. Enough to keep several
-// kilobytes of weight loads in flight per CU; more waves only re-read the activation slice.
-constexpr int64_t kTargetWaves = 256 * 16;
+// Wavefronts a launch aims for. With one or two vectors a wave needs under 100 VGPRs, the GPU
+// holds about 256 CUs x 20 waves, and a grid of 16384 waves (about three rounds) gave the best
+// streaming rate on the 262144 x 1536 vocabulary projection. With more vectors the activation
+// slice raises register use to ~120 VGPRs (16 waves per CU) and one round of 4096 waves is best.
+int64_t target_waves(int32_t nvec) { return nvec <= 2 ? 256 * 64 : 256 * 16; }
 
 // The per-shape plan. Lanes per row T and chunks per lane NC are chosen so that one pass of a
 // wave covers a row's chunks with the least idle lanes, preferring more chunks per lane
@@ -92,7 +94,7 @@ qgemv_plan make_plan(int wtype, int64_t rows, int64_t cols, int32_t nvec) {
     // Too few rows to fill the GPU: split further (whole chunks per lane kept).
     const int64_t rows_per_wave = 64 / best_t;
     int64_t waves = (rows + rows_per_wave - 1) / rows_per_wave * splits;
-    while (waves < kTargetWaves / 2 && best_nc > 1) {
+    while (waves < target_waves(nvec) / 8 && best_nc > 1) {
         best_nc--;
         splits = splits_for(best_t, best_nc, cols);
         waves = (rows + rows_per_wave - 1) / rows_per_wave * splits;
@@ -100,7 +102,7 @@ qgemv_plan make_plan(int wtype, int64_t rows, int64_t cols, int32_t nvec) {
     p.chunks_per_lane = best_nc;
     p.splits = splits;
     const int64_t groups = (rows + rows_per_wave - 1) / rows_per_wave;
-    const int64_t waves_per_split = std::max<int64_t>(1, kTargetWaves / splits);
+    const int64_t waves_per_split = std::max<int64_t>(1, target_waves(nvec) / splits);
     const int64_t want = std::min(groups, waves_per_split);
     p.blocks = static_cast<int32_t>(std::max<int64_t>(1, (want + p.waves_per_block - 1) /
                                                              p.waves_per_block));
