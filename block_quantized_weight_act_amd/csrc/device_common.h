@@ -31,6 +31,7 @@ enum : int {
     kDppXor2 = 0x4E,         // quad_perm [2,3,0,1]
     kDppHalfMirror = 0x141,  // lane i <-> 7 - i inside each half row of 8
     kDppMirror = 0x140,      // lane i <-> 15 - i inside each row of 16
+    kDppRowRor8 = 0x128,     // rotate by 8 inside each row of 16 (lane i <-> i ^ 8)
 };
 
 template <int ctrl>
@@ -60,6 +61,52 @@ __device__ __forceinline__ float group_sum(float v) {
             __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 32));
     }
     return v;
+}
+
+// Sums of up to 8 values per lane over all 64 lanes, scattered: afterwards lane l holds the
+// full sum of value number scatter_index(l) (all 8 lanes of each aligned group of 8 agree).
+// Step 1 swaps the upper half of value k with the lower half of value k + 4
+// (v_permlane32_swap), so one add leaves value k's pair sum in lanes 0-31 and value k + 4's
+// in lanes 32-63; step 2 does the same between odd and even rows of 16 (v_permlane16_swap);
+// step 3 exchanges across 8 lanes inside a row (DPP row rotate by 8) keeping one value per
+// lane; the last three DPP steps sum the remaining 8 lanes. 18 VALU ops instead of 8 full
+// butterflies; values past `n` are taken as zero.
+__device__ __forceinline__ int scatter_index(int lane) {
+    return 4 * ((lane >> 5) & 1) + 2 * ((lane >> 3) & 1) + ((lane >> 4) & 1);
+}
+
+template <int n>
+__device__ __forceinline__ float wave_reduce_scatter8(const float (&v)[n]) {
+    static_assert(n >= 1 && n <= 8, "at most 8 values");
+    float u[4];
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+        const float a = k < n ? v[k] : 0.0f;
+        const float b = k + 4 < n ? v[k + 4] : 0.0f;
+        const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(int, a),
+                                                        __builtin_bit_cast(int, b), false, false);
+        // copy the two results to scalars first: bit-casting r[0] and r[1] in place has been
+        // compiled as r[0] + r[0] by this toolchain
+        const int r0 = r[0], r1 = r[1];
+        u[k] = __builtin_bit_cast(float, r0) + __builtin_bit_cast(float, r1);
+    }
+    float w[2];
+#pragma unroll
+    for (int k = 0; k < 2; k++) {
+        const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(int, u[2 * k]),
+                                                        __builtin_bit_cast(int, u[2 * k + 1]),
+                                                        false, false);
+        const int r0 = r[0], r1 = r[1];
+        w[k] = __builtin_bit_cast(float, r0) + __builtin_bit_cast(float, r1);
+    }
+    const bool upper8 = (__lane_id() & 8) != 0;
+    const float keep = upper8 ? w[1] : w[0];
+    const float send = upper8 ? w[0] : w[1];
+    float z = keep + dpp<kDppRowRor8>(send);
+    z += dpp<kDppXor1>(z);
+    z += dpp<kDppXor2>(z);
+    z += dpp<kDppHalfMirror>(z);
+    return z;
 }
 
 template <int width>

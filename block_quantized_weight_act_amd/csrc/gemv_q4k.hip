@@ -68,6 +68,7 @@ __global__ void __launch_bounds__(256) gemv_q4k_kernel(GemvArgs a) {
     uint32_t xw[V][NC][8];
     float xs[V][NC];
     int xsum[V][NC];
+    float xsumf[V][NC];                      // the same sums as float (exact: |S| <= 4064)
 #pragma unroll
     for (int v = 0; v < V; v++) {
 #pragma unroll
@@ -87,6 +88,7 @@ __global__ void __launch_bounds__(256) gemv_q4k_kernel(GemvArgs a) {
 #pragma unroll
             for (int i = 0; i < 8; i++) sum = byte_sum(xw[v][k][i], sum);
             xsum[v][k] = sum;
+            xsumf[v][k] = static_cast<float>(sum);
             if (DBG && cv[k] && blockIdx.x == 0 && wave == 0 && rsub == 0)
                 a.S[static_cast<int64_t>(v) * nsub + g[k]] = sum;
         }
@@ -124,6 +126,10 @@ __global__ void __launch_bounds__(256) gemv_q4k_kernel(GemvArgs a) {
                                             (((hdr[k].w >> (2 * j)) & 3u) << 4));
             const int m = static_cast<int>(((hdr[k].z >> (4 * j)) & 15u) |
                                            (((hdr[k].w >> (16 + 2 * j)) & 3u) << 4));
+            // d * sc and dmin * m are exact in float32 (11-bit fp16 significand times a 6-bit
+            // integer) and shared by every vector.
+            const float dsc = d * static_cast<float>(sc);
+            const float dm = dmin * static_cast<float>(m);
             const uint32_t q[4] = {qs[k].x, qs[k].y, qs[k].z, qs[k].w};
             uint32_t lo[4], hi[4];
 #pragma unroll
@@ -139,28 +145,34 @@ __global__ void __launch_bounds__(256) gemv_q4k_kernel(GemvArgs a) {
                     P = dot4(lo[i], xw[v][k][i], P);
                     P = dot4(hi[i], xw[v][k][4 + i], P);
                 }
-                // d * (sc P) - dmin * (m S) rounded once: pb is the rounded min product and
-                // eb its exact rounding error, so fmaf(d, sc P, -pb) - eb is the exact
-                // difference up to two roundings of quantities no larger than the result
-                // (plus eps^2 |pb|); a sub-block whose terms cancel keeps its relative accuracy.
-                const float fscp = static_cast<float>(sc * P);
-                const float fms = static_cast<float>(m * xsum[v][k]);
-                const float pb = dmin * fms;
-                const float eb = fmaf(dmin, fms, -pb);
-                const float diff = fmaf(d, fscp, -pb) - eb;
+                // (d sc) P - (dmin m) S rounded once: pb is the rounded min product and eb
+                // its exact rounding error, so fmaf(d sc, P, -pb) - eb is the exact difference
+                // up to two roundings of quantities no larger than the result (plus
+                // eps^2 |pb|); a sub-block whose terms cancel keeps its relative accuracy.
+                const float pb = dm * xsumf[v][k];
+                const float eb = fmaf(dm, xsumf[v][k], -pb);
+                const float diff = fmaf(dsc, static_cast<float>(P), -pb) - eb;
                 acc[v] = fmaf(xs[v][k], diff, acc[v]);
                 if (DBG && rv && cv[k])
                     a.P[(static_cast<int64_t>(v) * a.rows + row) * nsub + g[k]] = P;
             }
         }
+        if constexpr (T == 64 && V >= 3) {
+            // one row per wave: scatter the vectors' sums over groups of 8 lanes
+            const float o = wave_reduce_scatter8(acc);
+            const int vi = scatter_index(lane);
+            if (!DBG && rv && (lane & 7) == 0 && vi < V)
+                a.out[(static_cast<int64_t>(split) * V + vi) * a.rows + row] = o;
+        } else {
 #pragma unroll
-        for (int v = 0; v < V; v++) acc[v] = group_sum<T>(acc[v]);
-        if (!DBG && rv && t < V) {   // the debug variant writes P and S only
-            float o = acc[0];
+            for (int v = 0; v < V; v++) acc[v] = group_sum<T>(acc[v]);
+            if (!DBG && rv && t < V) {   // the debug variant writes P and S only
+                float o = acc[0];
 #pragma unroll
-            for (int v = 1; v < V; v++)
-                if (t == v) o = acc[v];
-            a.out[(static_cast<int64_t>(split) * V + t) * a.rows + row] = o;
+                for (int v = 1; v < V; v++)
+                    if (t == v) o = acc[v];
+                a.out[(static_cast<int64_t>(split) * V + t) * a.rows + row] = o;
+            }
         }
     }
 }

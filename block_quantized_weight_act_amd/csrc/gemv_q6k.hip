@@ -139,14 +139,22 @@ __global__ void __launch_bounds__(256) gemv_q6k_kernel(GemvArgs a) {
                 }
             }
         }
+        if constexpr (T == 64 && V >= 3) {
+            // one row per wave: scatter the vectors' sums over groups of 8 lanes
+            const float o = wave_reduce_scatter8(acc);
+            const int vi = scatter_index(lane);
+            if (!DBG && rv && (lane & 7) == 0 && vi < V)
+                a.out[(static_cast<int64_t>(split) * V + vi) * a.rows + row] = o;
+        } else {
 #pragma unroll
-        for (int v = 0; v < V; v++) acc[v] = group_sum<T>(acc[v]);
-        if (!DBG && rv && t < V) {   // the debug variant writes P and S only
-            float o = acc[0];
+            for (int v = 0; v < V; v++) acc[v] = group_sum<T>(acc[v]);
+            if (!DBG && rv && t < V) {   // the debug variant writes P and S only
+                float o = acc[0];
 #pragma unroll
-            for (int v = 1; v < V; v++)
-                if (t == v) o = acc[v];
-            a.out[(static_cast<int64_t>(split) * V + t) * a.rows + row] = o;
+                for (int v = 1; v < V; v++)
+                    if (t == v) o = acc[v];
+                a.out[(static_cast<int64_t>(split) * V + t) * a.rows + row] = o;
+            }
         }
     }
 }
