@@ -22,7 +22,7 @@ __all__ = [
     "qgemv_status_string", "qgemv_weight_bytes", "qgemv_quantize_act",
     "qgemv_workspace_bytes", "qgemv_q4k", "qgemv_q6k", "qgemv_batch", "qgemv_debug_partials",
     "qgemv_quantize_weights", "qgemv_plan_for", "qgemv_plan_workspace_bytes", "qgemv_batch_plan",
-    "qgemv_read_probe",
+    "qgemv_read_probe", "qgemv_fused",
 ]
 
 QGEMV_Q4K = 1
@@ -79,6 +79,7 @@ def _load():
         "qgemv_batch_plan": (ctypes.c_int, [ctypes.c_int, vp, vp, vp, vp, i64, i64, i32,
                                             ctypes.POINTER(Plan), vp, sz, vp]),
         "qgemv_read_probe": (ctypes.c_int, [vp, sz, vp, i32, vp]),
+        "qgemv_fused": (ctypes.c_int, [ctypes.c_int, vp, vp, vp, vp, vp, i64, i64, i32, vp, sz, vp]),
     }
     for name, (res, args) in sigs.items():
         fn = getattr(lib, name)
@@ -205,6 +206,18 @@ def qgemv_batch_plan(wtype, w, xq, xd, y, rows: int, cols: int, nvec: int, plan:
         _wtype(wtype), _ptr(w, name="w"), _ptr(xq, torch.int8, "xq"),
         _ptr(xd, torch.float32, "xd"), _ptr(y, torch.float32, "y"), rows, cols, nvec,
         ctypes.byref(p), wsp, wsb, _stream(stream, y)))
+
+
+def qgemv_fused(wtype, w, x, y, rows: int, cols: int, nvec: int, xq_out=None, xd_out=None,
+                workspace=None, stream=None) -> None:
+    """Quantize x (float32 [nvec][cols]) and compute y = W x in one launch; xq_out / xd_out
+    optionally receive the codes and scales."""
+    lib = _load()
+    wsp, wsb = _ws(workspace)
+    _check("qgemv_fused", lib.qgemv_fused(
+        _wtype(wtype), _ptr(w, name="w"), _ptr(x, torch.float32, "x"),
+        _ptr(xq_out, torch.int8, "xq_out"), _ptr(xd_out, torch.float32, "xd_out"),
+        _ptr(y, torch.float32, "y"), rows, cols, nvec, wsp, wsb, _stream(stream, y)))
 
 
 def qgemv_debug_partials(wtype, w, xq, xd, P, S, rows: int, cols: int, nvec: int = 1,

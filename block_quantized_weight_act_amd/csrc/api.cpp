@@ -102,8 +102,9 @@ qgemv_plan make_plan(int wtype, int64_t rows, int64_t cols, int32_t nvec) {
     p.chunks_per_lane = best_nc;
     p.splits = splits;
     const int64_t groups = (rows + rows_per_wave - 1) / rows_per_wave;
+    const int64_t steps = (groups + groups_per_step(best_nc) - 1) / groups_per_step(best_nc);
     const int64_t waves_per_split = std::max<int64_t>(1, target_waves(nvec) / splits);
-    const int64_t want = std::min(groups, waves_per_split);
+    const int64_t want = std::min(steps, waves_per_split);
     p.blocks = static_cast<int32_t>(std::max<int64_t>(1, (want + p.waves_per_block - 1) /
                                                              p.waves_per_block));
     return p;
@@ -136,11 +137,51 @@ int check_gemv_args(int wtype, const void *w, const int8_t *xq, const float *xd,
     return QGEMV_OK;
 }
 
-int run_gemv(int wtype, const void *w, const int8_t *xq, const float *xd, float *y, int64_t rows,
+// The activation of one GEMV launch: either quantized codes and scales (xq, xd), or the float32
+// activation x that the kernel quantizes itself, optionally storing the codes and scales.
+struct Activation {
+    const int8_t *xq = nullptr;
+    const float *xd = nullptr;
+    const float *x = nullptr;
+    int8_t *xq_out = nullptr;
+    float *xd_out = nullptr;
+};
+
+int check_fused_act(const Activation &act, const void *w, size_t wbytes, const void *y,
+                    size_t ybytes, int64_t cols, int32_t nvec) {
+    if (!act.x) return QGEMV_EINVAL;
+    if ((act.xq_out == nullptr) != (act.xd_out == nullptr)) return QGEMV_EINVAL;
+    if (!aligned(act.x, 16)) return QGEMV_EALIGN;
+    const size_t xb = static_cast<size_t>(nvec) * cols * sizeof(float);
+    if (overlaps(y, ybytes, act.x, xb)) return QGEMV_EINVAL;
+    if (act.xq_out) {
+        if (!aligned(act.xq_out, 4) || !aligned(act.xd_out, 4)) return QGEMV_EALIGN;
+        const size_t qb = static_cast<size_t>(nvec) * cols;
+        const size_t db = static_cast<size_t>(nvec) * (cols / 32) * sizeof(float);
+        if (overlaps(act.xq_out, qb, act.x, xb) || overlaps(act.xq_out, qb, w, wbytes) ||
+            overlaps(act.xq_out, qb, y, ybytes) || overlaps(act.xd_out, db, act.x, xb) ||
+            overlaps(act.xd_out, db, w, wbytes) || overlaps(act.xd_out, db, y, ybytes) ||
+            overlaps(act.xd_out, db, act.xq_out, qb))
+            return QGEMV_EINVAL;
+    }
+    return QGEMV_OK;
+}
+
+int run_gemv(int wtype, const void *w, const Activation &act, float *y, int64_t rows,
              int64_t cols, int32_t nvec, const qgemv_plan &plan_in, void *ws, size_t ws_bytes,
              hipStream_t stream) {
     const size_t ybytes = static_cast<size_t>(nvec) * rows * sizeof(float);
-    int st = check_gemv_args(wtype, w, xq, xd, y, ybytes, rows, cols, nvec);
+    int st;
+    if (act.x) {
+        // check the weights and y as for the unfused form (the codes' places are unused)
+        if (wtype != QGEMV_Q4K && wtype != QGEMV_Q6K) return QGEMV_EINVAL;
+        if (!w || !y || !shape_ok(rows, cols, nvec)) return QGEMV_EINVAL;
+        if (!aligned(w, 16) || !aligned(y, 4)) return QGEMV_EALIGN;
+        if (overlaps(y, ybytes, w, weight_bytes(wtype, rows, cols))) return QGEMV_EINVAL;
+        st = check_fused_act(act, w, weight_bytes(wtype, rows, cols), y, ybytes, cols, nvec);
+    } else {
+        st = check_gemv_args(wtype, w, act.xq, act.xd, y, ybytes, rows, cols, nvec);
+    }
     if (st != QGEMV_OK) return st;
     if (!plan_ok(plan_in, nvec)) return QGEMV_EINVAL;
     qgemv_plan plan = plan_in;
@@ -150,15 +191,21 @@ int run_gemv(int wtype, const void *w, const int8_t *xq, const float *xd, float 
         if (!ws || ws_bytes < need) return QGEMV_EWORKSPACE;
         if (!aligned(ws, 4)) return QGEMV_EALIGN;
         const size_t wb = weight_bytes(wtype, rows, cols);
+        const size_t qb = static_cast<size_t>(nvec) * cols;
+        const size_t db = static_cast<size_t>(nvec) * (cols / 32) * sizeof(float);
         if (overlaps(ws, need, w, wb) || overlaps(ws, need, y, ybytes) ||
-            overlaps(ws, need, xq, static_cast<size_t>(nvec) * cols) ||
-            overlaps(ws, need, xd, static_cast<size_t>(nvec) * (cols / 32) * sizeof(float)))
+            (act.xq && overlaps(ws, need, act.xq, qb)) || (act.xd && overlaps(ws, need, act.xd, db)) ||
+            (act.x && overlaps(ws, need, act.x, qb * sizeof(float))) ||
+            (act.xq_out && (overlaps(ws, need, act.xq_out, qb) || overlaps(ws, need, act.xd_out, db))))
             return QGEMV_EINVAL;
     }
     GemvArgs a{};
     a.w = static_cast<const uint8_t *>(w);
-    a.xq = xq;
-    a.xd = xd;
+    a.xq = act.xq;
+    a.xd = act.xd;
+    a.x = act.x;
+    a.xq_out = act.xq_out;
+    a.xd_out = act.xd_out;
     a.out = need > 0 ? static_cast<float *>(ws) : y;
     a.rows = static_cast<int32_t>(rows);
     a.nb = static_cast<int32_t>(cols / kQK);
@@ -234,8 +281,10 @@ int qgemv_batch_plan(int wtype, const void *w, const int8_t *xq, const float *xd
                      int64_t rows, int64_t cols, int32_t nvec, const qgemv_plan *plan,
                      void *workspace, size_t workspace_bytes, hipStream_t stream) {
     if (!plan) return QGEMV_EINVAL;
-    return run_gemv(wtype, w, xq, xd, y, rows, cols, nvec, *plan, workspace, workspace_bytes,
-                    stream);
+    Activation act;
+    act.xq = xq;
+    act.xd = xd;
+    return run_gemv(wtype, w, act, y, rows, cols, nvec, *plan, workspace, workspace_bytes, stream);
 }
 
 int qgemv_batch(int wtype, const void *w, const int8_t *xq, const float *xd, float *y,
@@ -243,8 +292,43 @@ int qgemv_batch(int wtype, const void *w, const int8_t *xq, const float *xd, flo
                 size_t workspace_bytes, hipStream_t stream) {
     if ((wtype != QGEMV_Q4K && wtype != QGEMV_Q6K) || !shape_ok(rows, cols, nvec))
         return QGEMV_EINVAL;
-    return run_gemv(wtype, w, xq, xd, y, rows, cols, nvec, make_plan(wtype, rows, cols, nvec),
+    Activation act;
+    act.xq = xq;
+    act.xd = xd;
+    return run_gemv(wtype, w, act, y, rows, cols, nvec, make_plan(wtype, rows, cols, nvec),
                     workspace, workspace_bytes, stream);
+}
+
+int qgemv_fused(int wtype, const void *w, const float *x, int8_t *xq_out, float *xd_out, float *y,
+                int64_t rows, int64_t cols, int32_t nvec, void *workspace, size_t workspace_bytes,
+                hipStream_t stream) {
+    if ((wtype != QGEMV_Q4K && wtype != QGEMV_Q6K) || !shape_ok(rows, cols, nvec))
+        return QGEMV_EINVAL;
+    const qgemv_plan plan = make_plan(wtype, rows, cols, nvec);
+    Activation act;
+    act.x = x;
+    act.xq_out = xq_out;
+    act.xd_out = xd_out;
+    // Every workgroup of the fused kernel quantizes the whole activation slice its lanes read.
+    // When that slice is large next to the workgroup's share of the weights (wide rows, many
+    // vectors, few rows per workgroup), the repeated quantization costs more than a second
+    // launch: then, if the caller gave places for the codes, quantize once into them and run
+    // the product from them. Both forms give the same codes and the same y, bit for bit.
+    const double slice = static_cast<double>(nvec) * plan.lanes_per_row * plan.chunks_per_lane * 32;
+    const double share = static_cast<double>(weight_bytes(wtype, rows, cols)) /
+                         (static_cast<double>(plan.blocks) * plan.splits);
+    if (xq_out && xd_out && slice > 0.15 * share) {
+        int st = check_fused_act(act, w, weight_bytes(wtype, rows, cols), y,
+                                 static_cast<size_t>(nvec) * rows * sizeof(float), cols, nvec);
+        if (st != QGEMV_OK) return st;
+        st = qgemv_quantize_act(x, xq_out, xd_out, cols, nvec, stream);
+        if (st != QGEMV_OK) return st;
+        Activation q;
+        q.xq = xq_out;
+        q.xd = xd_out;
+        return run_gemv(wtype, w, q, y, rows, cols, nvec, plan, workspace, workspace_bytes, stream);
+    }
+    return run_gemv(wtype, w, act, y, rows, cols, nvec, plan, workspace, workspace_bytes, stream);
 }
 
 int qgemv_q4k(const void *w, const int8_t *xq, const float *xd, float *y, int64_t rows,

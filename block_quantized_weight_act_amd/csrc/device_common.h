@@ -132,6 +132,33 @@ __device__ __forceinline__ uint32_t group_or(uint32_t v) {
 
 __device__ __forceinline__ uint4 load16(const void *p) { return *reinterpret_cast<const uint4 *>(p); }
 
+// Activation quantization of one block of 32 elements held by 8 consecutive lanes, 4 elements
+// each (oxinfer README, "How it works": per-matmul activation quantization; "Build and run":
+// blocks of 32 with an f32 scale): amax over the block, scale = amax / 127, inverse
+// 127 / amax (0 when amax = 0), code = clamp(rint(x * inverse), -127, 127). Both divisions
+// are IEEE float32 divisions, the product one float32 multiply, rint rounds to nearest even:
+// the codes are the same on every IEEE machine. All 64 lanes of the wave must call it.
+struct ActQuad {
+    uint32_t codes;   // 4 int8 codes, element 0 in the low byte
+    float scale;      // the block's scale (the same in all 8 lanes)
+};
+
+__device__ __forceinline__ ActQuad quantize_act_quad(const float4 v) {
+    float amax = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+#pragma unroll
+    for (int off = 4; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
+    const float scale = amax / 127.0f;
+    const float inv = amax > 0.0f ? 127.0f / amax : 0.0f;
+    const float e[4] = {v.x, v.y, v.z, v.w};
+    uint32_t packed = 0;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        const float code = fminf(fmaxf(rintf(e[i] * inv), -127.0f), 127.0f);
+        packed |= (static_cast<uint32_t>(static_cast<int>(code)) & 0xFFu) << (8 * i);
+    }
+    return {packed, scale};
+}
+
 // 16-byte load marked nontemporal: the weights are read once per product, so they are
 // streamed past the caches instead of displacing the activation slice and other data.
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));

@@ -32,6 +32,7 @@
 // float32 roundings of the sub-block's own value; a sub-block whose dequantized weights
 // times activations are all zero contributes exactly zero. The library is built with
 // -ffp-contract=off: every fused multiply-add is an explicit fmaf.
+#include "act_slice.h"
 #include "device_common.h"
 #include "qgemv_internal.h"
 
@@ -64,114 +65,119 @@ __global__ void __launch_bounds__(256) gemv_q4k_kernel(GemvArgs a) {
         qoff[k] = b * 128 + 16 * j;
     }
 
+    // Steps of G consecutive row groups: this wave takes steps wave_id, wave_id + stride, ...
+    // All loads of a step are issued first and are unconditional: a row past the end of the
+    // matrix is clamped to the last row (its result is not stored), so there are no divergent
+    // branches around the loads.
+    constexpr int G = groups_per_step(NC);
+    const int groups = (a.rows + RPW - 1) / RPW;
+    const int steps = (groups + G - 1) / G;
+    const int stride = gridDim.x * wpb;
+    const uint8_t *hplane = a.w + static_cast<int64_t>(a.rows) * a.nb * 128;
+    uint4 hdr_s[G][NC], qs_s[G][NC];
+    auto issue_step = [&](int st) {
+#pragma unroll
+        for (int gg = 0; gg < G; gg++) {
+            const int row = (st * G + gg) * RPW + rsub;
+            const int64_t brow = static_cast<int64_t>(row < a.rows ? row : a.rows - 1) * a.nb;
+            const uint8_t *qrow = a.w + brow * 128;
+            const uint8_t *hrow = hplane + brow * 16;
+#pragma unroll
+            for (int k = 0; k < NC; k++) {
+                hdr_s[gg][k] = load16(hrow + hoff[k]);
+                qs_s[gg][k] = load16_stream(qrow + qoff[k]);
+            }
+        }
+    };
+
     // This lane's activation slice: 32 codes, the block scale and the block code sum per chunk.
     uint32_t xw[V][NC][8];
     float xs[V][NC];
-    int xsum[V][NC];
-    float xsumf[V][NC];                      // the same sums as float (exact: |S| <= 4064)
+    float xsumf[V][NC];                      // code sums as float (exact: |S| <= 4064)
+    load_act_slice<V, T, NC>(a, g, cv, t, xw, xs);
 #pragma unroll
     for (int v = 0; v < V; v++) {
 #pragma unroll
         for (int k = 0; k < NC; k++) {
-            uint4 lo = make_uint4(0, 0, 0, 0), hi = make_uint4(0, 0, 0, 0);
-            float s = 0.0f;
-            if (cv[k]) {
-                const int8_t *p = a.xq + v * cols + 32 * static_cast<int64_t>(g[k]);
-                lo = load16(p);
-                hi = load16(p + 16);
-                s = a.xd[static_cast<int64_t>(v) * nsub + g[k]];
-            }
-            xw[v][k][0] = lo.x; xw[v][k][1] = lo.y; xw[v][k][2] = lo.z; xw[v][k][3] = lo.w;
-            xw[v][k][4] = hi.x; xw[v][k][5] = hi.y; xw[v][k][6] = hi.z; xw[v][k][7] = hi.w;
-            xs[v][k] = s;
             int sum = 0;
 #pragma unroll
             for (int i = 0; i < 8; i++) sum = byte_sum(xw[v][k][i], sum);
-            xsum[v][k] = sum;
             xsumf[v][k] = static_cast<float>(sum);
             if (DBG && cv[k] && blockIdx.x == 0 && wave == 0 && rsub == 0)
                 a.S[static_cast<int64_t>(v) * nsub + g[k]] = sum;
         }
     }
 
-    // Row groups: this wave takes groups wave_id, wave_id + stride, ... All loads are
-    // unconditional: a row past the end of the matrix is clamped to the last row (its result
-    // is not stored), so the loop has no divergent branches around its loads.
-    const int groups = (a.rows + RPW - 1) / RPW;
-    const int stride = gridDim.x * wpb;
-    const uint8_t *hplane = a.w + static_cast<int64_t>(a.rows) * a.nb * 128;
-    for (int grp = blockIdx.x * wpb + wave; grp < groups; grp += stride) {
-        const int row = grp * RPW + rsub;
-        const bool rv = row < a.rows;
-        const int64_t brow = static_cast<int64_t>(rv ? row : a.rows - 1) * a.nb;
-        const uint8_t *qrow = a.w + brow * 128;
-        const uint8_t *hrow = hplane + brow * 16;
-        uint4 hdr[NC], qs[NC];
-#pragma unroll
-        for (int k = 0; k < NC; k++) {
-            hdr[k] = load16(hrow + hoff[k]);
-            qs[k] = load16_stream(qrow + qoff[k]);
-        }
-        // Keep every load of the group ahead of the arithmetic: without this fence the
+    for (int st = blockIdx.x * wpb + wave; st < steps; st += stride) {
+        issue_step(st);
+        // Keep every load of the step ahead of the arithmetic: without this fence the
         // scheduler interleaves them to save registers and waits for each load in turn.
         __builtin_amdgcn_sched_barrier(0);
-        float acc[V];
 #pragma unroll
-        for (int v = 0; v < V; v++) acc[v] = 0.0f;
+        for (int gg = 0; gg < G; gg++) {
+            const int row = (st * G + gg) * RPW + rsub;
+            const bool rv = row < a.rows;
+            const uint4 *hdr = hdr_s[gg];
+            const uint4 *qs = qs_s[gg];
+            float acc[V];
 #pragma unroll
-        for (int k = 0; k < NC; k++) {
-            const float d = half_to_float(hdr[k].x & 0xFFFFu);
-            const float dmin = half_to_float(hdr[k].x >> 16);
-            const int sc = static_cast<int>(((hdr[k].y >> (4 * j)) & 15u) |
-                                            (((hdr[k].w >> (2 * j)) & 3u) << 4));
-            const int m = static_cast<int>(((hdr[k].z >> (4 * j)) & 15u) |
-                                           (((hdr[k].w >> (16 + 2 * j)) & 3u) << 4));
-            // d * sc and dmin * m are exact in float32 (11-bit fp16 significand times a 6-bit
-            // integer) and shared by every vector.
-            const float dsc = d * static_cast<float>(sc);
-            const float dm = dmin * static_cast<float>(m);
-            const uint32_t q[4] = {qs[k].x, qs[k].y, qs[k].z, qs[k].w};
-            uint32_t lo[4], hi[4];
+            for (int v = 0; v < V; v++) acc[v] = 0.0f;
 #pragma unroll
-            for (int i = 0; i < 4; i++) {
-                lo[i] = q[i] & 0x0F0F0F0Fu;
-                hi[i] = (q[i] >> 4) & 0x0F0F0F0Fu;
-            }
-#pragma unroll
-            for (int v = 0; v < V; v++) {
-                int P = 0;
+            for (int k = 0; k < NC; k++) {
+                const float d = half_to_float(hdr[k].x & 0xFFFFu);
+                const float dmin = half_to_float(hdr[k].x >> 16);
+                const int sc = static_cast<int>(((hdr[k].y >> (4 * j)) & 15u) |
+                                                (((hdr[k].w >> (2 * j)) & 3u) << 4));
+                const int m = static_cast<int>(((hdr[k].z >> (4 * j)) & 15u) |
+                                               (((hdr[k].w >> (16 + 2 * j)) & 3u) << 4));
+                // d * sc and dmin * m are exact in float32 (11-bit fp16 significand times a
+                // 6-bit integer) and shared by every vector.
+                const float dsc = d * static_cast<float>(sc);
+                const float dm = dmin * static_cast<float>(m);
+                const uint32_t q[4] = {qs[k].x, qs[k].y, qs[k].z, qs[k].w};
+                uint32_t lo[4], hi[4];
 #pragma unroll
                 for (int i = 0; i < 4; i++) {
-                    P = dot4(lo[i], xw[v][k][i], P);
-                    P = dot4(hi[i], xw[v][k][4 + i], P);
+                    lo[i] = q[i] & 0x0F0F0F0Fu;
+                    hi[i] = (q[i] >> 4) & 0x0F0F0F0Fu;
                 }
-                // (d sc) P - (dmin m) S rounded once: pb is the rounded min product and eb
-                // its exact rounding error, so fmaf(d sc, P, -pb) - eb is the exact difference
-                // up to two roundings of quantities no larger than the result (plus
-                // eps^2 |pb|); a sub-block whose terms cancel keeps its relative accuracy.
-                const float pb = dm * xsumf[v][k];
-                const float eb = fmaf(dm, xsumf[v][k], -pb);
-                const float diff = fmaf(dsc, static_cast<float>(P), -pb) - eb;
-                acc[v] = fmaf(xs[v][k], diff, acc[v]);
-                if (DBG && rv && cv[k])
-                    a.P[(static_cast<int64_t>(v) * a.rows + row) * nsub + g[k]] = P;
+#pragma unroll
+                for (int v = 0; v < V; v++) {
+                    int P = 0;
+#pragma unroll
+                    for (int i = 0; i < 4; i++) {
+                        P = dot4(lo[i], xw[v][k][i], P);
+                        P = dot4(hi[i], xw[v][k][4 + i], P);
+                    }
+                    // (d sc) P - (dmin m) S rounded once: pb is the rounded min product and
+                    // eb its exact rounding error, so fmaf(d sc, P, -pb) - eb is the exact
+                    // difference up to two roundings of quantities no larger than the result
+                    // (plus eps^2 |pb|); a sub-block whose terms cancel keeps its relative
+                    // accuracy.
+                    const float pb = dm * xsumf[v][k];
+                    const float eb = fmaf(dm, xsumf[v][k], -pb);
+                    const float diff = fmaf(dsc, static_cast<float>(P), -pb) - eb;
+                    acc[v] = fmaf(xs[v][k], diff, acc[v]);
+                    if (DBG && rv && cv[k])
+                        a.P[(static_cast<int64_t>(v) * a.rows + row) * nsub + g[k]] = P;
+                }
             }
-        }
-        if constexpr (T == 64 && V >= 3) {
-            // one row per wave: scatter the vectors' sums over groups of 8 lanes
-            const float o = wave_reduce_scatter8(acc);
-            const int vi = scatter_index(lane);
-            if (!DBG && rv && (lane & 7) == 0 && vi < V)
-                a.out[(static_cast<int64_t>(split) * V + vi) * a.rows + row] = o;
-        } else {
+            if constexpr (T == 64 && V >= 3) {
+                // one row per wave: scatter the vectors' sums over groups of 8 lanes
+                const float o = wave_reduce_scatter8(acc);
+                const int vi = scatter_index(lane);
+                if (!DBG && rv && (lane & 7) == 0 && vi < V)
+                    a.out[(static_cast<int64_t>(split) * V + vi) * a.rows + row] = o;
+            } else {
 #pragma unroll
-            for (int v = 0; v < V; v++) acc[v] = group_sum<T>(acc[v]);
-            if (!DBG && rv && t < V) {   // the debug variant writes P and S only
-                float o = acc[0];
+                for (int v = 0; v < V; v++) acc[v] = group_sum<T>(acc[v]);
+                if (!DBG && rv && t < V) {   // the debug variant writes P and S only
+                    float o = acc[0];
 #pragma unroll
-                for (int v = 1; v < V; v++)
-                    if (t == v) o = acc[v];
-                a.out[(static_cast<int64_t>(split) * V + t) * a.rows + row] = o;
+                    for (int v = 1; v < V; v++)
+                        if (t == v) o = acc[v];
+                    a.out[(static_cast<int64_t>(split) * V + t) * a.rows + row] = o;
+                }
             }
         }
     }
@@ -186,10 +192,11 @@ hipError_t launch_variant(const GemvArgs &a, const LaunchShape &s, bool debug,
                           hipStream_t stream) {
     const dim3 grid(static_cast<unsigned>(s.blocks), static_cast<unsigned>(s.splits));
     const dim3 block(static_cast<unsigned>(64 * s.waves));
+    const size_t lds = a.x != nullptr ? act_slice_lds_bytes<V, T, NC>() : 0;
     if (debug)
-        hipLaunchKernelGGL((gemv_q4k_kernel<V, T, NC, true>), grid, block, 0, stream, a);
+        hipLaunchKernelGGL((gemv_q4k_kernel<V, T, NC, true>), grid, block, lds, stream, a);
     else
-        hipLaunchKernelGGL((gemv_q4k_kernel<V, T, NC, false>), grid, block, 0, stream, a);
+        hipLaunchKernelGGL((gemv_q4k_kernel<V, T, NC, false>), grid, block, lds, stream, a);
     return hipGetLastError();
 }
 

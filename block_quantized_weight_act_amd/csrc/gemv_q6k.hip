@@ -19,6 +19,7 @@
 // read (128 and 64 contiguous bytes) are touched by no other load: they are read with
 // nontemporal loads and streamed past the caches, while the small scale and super-scale
 // loads stay cached for the neighbouring blocks that share their lines.
+#include "act_slice.h"
 #include "device_common.h"
 #include "qgemv_internal.h"
 
@@ -53,24 +54,39 @@ __global__ void __launch_bounds__(256) gemv_q6k_kernel(GemvArgs a) {
         boff[k] = cv[k] ? static_cast<uint32_t>(g[k] >> 3) : 0u;
     }
 
+    // Steps of G row groups as in the Q4_K kernel: unconditional loads, rows clamped to the
+    // last one, every load of a step issued before its arithmetic.
+    constexpr int G = groups_per_step(NC);
+    const int groups = (a.rows + RPW - 1) / RPW;
+    const int steps = (groups + G - 1) / G;
+    const int stride = gridDim.x * wpb;
+    uint4 ql_s[G][NC];
+    uint2 qh_s[G][NC];
+    uint32_t scw_s[G][NC], dbits_s[G][NC];
+    auto issue_step = [&](int st) {
+#pragma unroll
+        for (int gg = 0; gg < G; gg++) {
+            const int row = (st * G + gg) * RPW + rsub;
+            const int64_t brow = static_cast<int64_t>(row < a.rows ? row : a.rows - 1) * a.nb;
+#pragma unroll
+            for (int k = 0; k < NC; k++) {
+                const int64_t b = brow + boff[k];
+                ql_s[gg][k] = load16_stream(a.w + b * 128 + 16 * kk);
+                qh_s[gg][k] = load8_stream(hplane + b * 64 + 8 * kk);
+                scw_s[gg][k] = *reinterpret_cast<const uint32_t *>(splane + b * 16 + 4 * (kk >> 1));
+                dbits_s[gg][k] = dplane[b];
+            }
+        }
+    };
+
     uint32_t xw[V][NC][8];
     float xs[V][NC];
     int xlo[V][NC], xhi[V][NC];             // activation code sums of the two 16-column halves
+    load_act_slice<V, T, NC>(a, g, cv, t, xw, xs);
 #pragma unroll
     for (int v = 0; v < V; v++) {
 #pragma unroll
         for (int k = 0; k < NC; k++) {
-            uint4 lo = make_uint4(0, 0, 0, 0), hi = make_uint4(0, 0, 0, 0);
-            float s = 0.0f;
-            if (cv[k]) {
-                const int8_t *p = a.xq + v * cols + 32 * static_cast<int64_t>(g[k]);
-                lo = load16(p);
-                hi = load16(p + 16);
-                s = a.xd[static_cast<int64_t>(v) * nsub + g[k]];
-            }
-            xw[v][k][0] = lo.x; xw[v][k][1] = lo.y; xw[v][k][2] = lo.z; xw[v][k][3] = lo.w;
-            xw[v][k][4] = hi.x; xw[v][k][5] = hi.y; xw[v][k][6] = hi.z; xw[v][k][7] = hi.w;
-            xs[v][k] = s;
             int s0 = 0, s1 = 0;
 #pragma unroll
             for (int i = 0; i < 4; i++) {
@@ -84,76 +100,66 @@ __global__ void __launch_bounds__(256) gemv_q6k_kernel(GemvArgs a) {
         }
     }
 
-    // Row groups as in the Q4_K kernel: unconditional loads, the row clamped to the last one.
-    const int groups = (a.rows + RPW - 1) / RPW;
-    const int stride = gridDim.x * wpb;
-    for (int grp = blockIdx.x * wpb + wave; grp < groups; grp += stride) {
-        const int row = grp * RPW + rsub;
-        const bool rv = row < a.rows;
-        const int64_t brow = static_cast<int64_t>(rv ? row : a.rows - 1) * a.nb;
-        uint4 ql[NC];
-        uint2 qh[NC];
-        uint32_t scw[NC], dbits[NC];
-#pragma unroll
-        for (int k = 0; k < NC; k++) {
-            const int64_t b = brow + boff[k];
-            ql[k] = load16_stream(a.w + b * 128 + 16 * kk);
-            qh[k] = load8_stream(hplane + b * 64 + 8 * kk);
-            scw[k] = *reinterpret_cast<const uint32_t *>(splane + b * 16 + 4 * (kk >> 1));
-            dbits[k] = dplane[b];
-        }
-        // all of the group's loads stay ahead of the arithmetic
+    for (int st = blockIdx.x * wpb + wave; st < steps; st += stride) {
+        issue_step(st);
         __builtin_amdgcn_sched_barrier(0);
-        float acc[V];
 #pragma unroll
-        for (int v = 0; v < V; v++) acc[v] = 0.0f;
+        for (int gg = 0; gg < G; gg++) {
+            const int row = (st * G + gg) * RPW + rsub;
+            const bool rv = row < a.rows;
+            float acc[V];
 #pragma unroll
-        for (int k = 0; k < NC; k++) {
-            const float d = half_to_float(dbits[k]);
-            const int sh = 16 * (kk & 1);
-            const int sc_lo = static_cast<int>(static_cast<int8_t>(scw[k] >> sh));
-            const int sc_hi = static_cast<int>(static_cast<int8_t>(scw[k] >> (sh + 8)));
-            const uint32_t w4[4] = {ql[k].x, ql[k].y, ql[k].z, ql[k].w};
-            uint32_t lo[4], hi[4];
+            for (int v = 0; v < V; v++) acc[v] = 0.0f;
 #pragma unroll
-            for (int s = 0; s < 4; s++) {
-                lo[s] = (w4[s] & 0x0F0F0F0Fu) | (((qh[k].x >> (2 * s)) & 0x03030303u) << 4);
-                hi[s] = ((w4[s] >> 4) & 0x0F0F0F0Fu) | (((qh[k].y >> (2 * s)) & 0x03030303u) << 4);
-            }
-#pragma unroll
-            for (int v = 0; v < V; v++) {
-                int plo = 0, phi = 0;
+            for (int k = 0; k < NC; k++) {
+                const float d = half_to_float(dbits_s[gg][k]);
+                const int sh = 16 * (kk & 1);
+                const int sc_lo = static_cast<int>(static_cast<int8_t>(scw_s[gg][k] >> sh));
+                const int sc_hi = static_cast<int>(static_cast<int8_t>(scw_s[gg][k] >> (sh + 8)));
+                const uint4 l4 = ql_s[gg][k];
+                const uint2 h2 = qh_s[gg][k];
+                const uint32_t w4[4] = {l4.x, l4.y, l4.z, l4.w};
+                uint32_t lo[4], hi[4];
 #pragma unroll
                 for (int s = 0; s < 4; s++) {
-                    plo = dot4(lo[s], xw[v][k][s], plo);
-                    phi = dot4(hi[s], xw[v][k][4 + s], phi);
+                    lo[s] = (w4[s] & 0x0F0F0F0Fu) | (((h2.x >> (2 * s)) & 0x03030303u) << 4);
+                    hi[s] = ((w4[s] >> 4) & 0x0F0F0F0Fu) | (((h2.y >> (2 * s)) & 0x03030303u) << 4);
                 }
-                plo -= 32 * xlo[v][k];
-                phi -= 32 * xhi[v][k];
-                const int scp = sc_lo * plo + sc_hi * phi;
-                acc[v] = fmaf(xs[v][k] * d, static_cast<float>(scp), acc[v]);
-                if (DBG && rv && cv[k]) {
-                    int32_t *pp = a.P + (static_cast<int64_t>(v) * a.rows + row) * (2 * nsub);
-                    pp[2 * g[k]] = plo;
-                    pp[2 * g[k] + 1] = phi;
+#pragma unroll
+                for (int v = 0; v < V; v++) {
+                    int plo = 0, phi = 0;
+#pragma unroll
+                    for (int s = 0; s < 4; s++) {
+                        plo = dot4(lo[s], xw[v][k][s], plo);
+                        phi = dot4(hi[s], xw[v][k][4 + s], phi);
+                    }
+                    plo -= 32 * xlo[v][k];
+                    phi -= 32 * xhi[v][k];
+                    const int scp = sc_lo * plo + sc_hi * phi;
+                    acc[v] = fmaf(xs[v][k] * d, static_cast<float>(scp), acc[v]);
+                    if (DBG && rv && cv[k]) {
+                        int32_t *pp = a.P + (static_cast<int64_t>(v) * a.rows + row) * (2 * nsub);
+                        pp[2 * g[k]] = plo;
+                        pp[2 * g[k] + 1] = phi;
+                    }
                 }
             }
-        }
-        if constexpr (T == 64 && V >= 3) {
-            // one row per wave: scatter the vectors' sums over groups of 8 lanes
-            const float o = wave_reduce_scatter8(acc);
-            const int vi = scatter_index(lane);
-            if (!DBG && rv && (lane & 7) == 0 && vi < V)
-                a.out[(static_cast<int64_t>(split) * V + vi) * a.rows + row] = o;
-        } else {
+            if constexpr (T == 64 && V >= 3) {
+                // one row per wave: scatter the vectors' sums over groups of 8 lanes
+                const float o = wave_reduce_scatter8(acc);
+                const int vi = scatter_index(lane);
+                if (!DBG && rv && (lane & 7) == 0 && vi < V)
+                    a.out[(static_cast<int64_t>(split) * V + vi) * a.rows + row] = o;
+            } else {
 #pragma unroll
-            for (int v = 0; v < V; v++) acc[v] = group_sum<T>(acc[v]);
-            if (!DBG && rv && t < V) {   // the debug variant writes P and S only
-                float o = acc[0];
+                for (int v = 0; v < V; v++) acc[v] = group_sum<T>(acc[v]);
+                if (!DBG && rv && t < V) {   // the debug variant writes P and S only
+                    float o = acc[0];
 #pragma unroll
-                for (int v = 1; v < V; v++)
-                    if (t == v) o = acc[v];
-                a.out[(static_cast<int64_t>(split) * V + t) * a.rows + row] = o;
+                    for (int v = 1; v < V; v++)
+                        if (t == v) o = acc[v];
+                    a.out[(static_cast<int64_t>(split) * V + t) * a.rows + row] = o;
+                }
             }
         }
     }
@@ -168,10 +174,11 @@ hipError_t launch_variant(const GemvArgs &a, const LaunchShape &s, bool debug,
                           hipStream_t stream) {
     const dim3 grid(static_cast<unsigned>(s.blocks), static_cast<unsigned>(s.splits));
     const dim3 block(static_cast<unsigned>(64 * s.waves));
+    const size_t lds = a.x != nullptr ? act_slice_lds_bytes<V, T, NC>() : 0;
     if (debug)
-        hipLaunchKernelGGL((gemv_q6k_kernel<V, T, NC, true>), grid, block, 0, stream, a);
+        hipLaunchKernelGGL((gemv_q6k_kernel<V, T, NC, true>), grid, block, lds, stream, a);
     else
-        hipLaunchKernelGGL((gemv_q6k_kernel<V, T, NC, false>), grid, block, 0, stream, a);
+        hipLaunchKernelGGL((gemv_q6k_kernel<V, T, NC, false>), grid, block, lds, stream, a);
     return hipGetLastError();
 }
 

@@ -13,6 +13,13 @@ constexpr int kQ6KBody = 208;      // Q6_K super-block body (fp16 d in a separat
 constexpr int kChunksPerBlock = 8; // 16-byte code chunks (32 columns each) per super-block
 constexpr int kMaxVec = 8;
 
+// Row groups whose loads a wave issues together before computing any of them. A group costs
+// 8 * chunks_per_lane VGPRs of loaded data; up to ~32 VGPRs of loads per step are in flight
+// without cutting occupancy much, so lanes with fewer chunks load more groups at once.
+constexpr int groups_per_step(int chunks_per_lane) {
+    return chunks_per_lane == 1 ? 4 : (chunks_per_lane == 2 ? 2 : 1);
+}
+
 // One GEMV launch: the kernels read everything they need from here.
 struct GemvArgs {
     const uint8_t *w;      // weight tensor (Q4_K blocks, or Q6_K bodies followed by the d plane)
@@ -21,6 +28,9 @@ struct GemvArgs {
     float *out;            // [splits][nvec][rows] (y itself when splits == 1)
     int32_t *P;            // debug partials or nullptr
     int32_t *S;            // debug activation block sums or nullptr
+    const float *x;        // float32 activations [nvec][cols] to quantize in the kernel, or nullptr
+    int8_t *xq_out;        // where the fused kernel also stores the codes (may be nullptr)
+    float *xd_out;         // ... and the scales (nullptr exactly when xq_out is)
     int32_t rows;
     int32_t nb;            // super-blocks per row
     int32_t nchunks;       // 16-byte chunks per row = 8 * nb

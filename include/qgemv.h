@@ -161,6 +161,24 @@ int qgemv_batch(int wtype, const void *w, const int8_t *xq, const float *xd, flo
                 size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Activation quantization and the product in one launch: x float32 [nvec][cols]
+ * is quantized exactly as qgemv_quantize_act does (the same codes and scales,
+ * bit for bit) by each workgroup for the columns it reads, then y = W x as in
+ * qgemv_batch. For the common decode step where one activation feeds one
+ * matrix this saves the separate quantization launch (oxinfer README, "How it
+ * works": per-matmul activation quantization). xq_out [nvec][cols] and xd_out
+ * [nvec][cols/32] optionally receive the codes and scales (both NULL or both
+ * set; 4-byte aligned). x 16-byte aligned. Other arguments as for qgemv_batch.
+ * Each workgroup repeats the quantization of the columns it reads; when that
+ * is large next to its share of the weights (wide rows, several vectors) and
+ * xq_out / xd_out are given, the library instead quantizes once into them and
+ * runs the product from them (two launches, identical results).
+ */
+int qgemv_fused(int wtype, const void *w, const float *x, int8_t *xq_out, float *xd_out, float *y,
+                int64_t rows, int64_t cols, int32_t nvec, void *workspace,
+                size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Test hook: the exact integer partials of the same kernels.
  * P int32: Q4_K [nvec][rows][cols/32] (sum of q * xq per 32-column
  * sub-block), Q6_K [nvec][rows][cols/16] (sum of (q - 32) * xq per 16-column

@@ -97,3 +97,15 @@ def test_other_entry_points_reject_bad_arguments():
     assert lib.qgemv_quantize_weights(2, A, A + 64, 8, 256, None) == EINVAL   # overlap
     assert lib.qgemv_quantize_weights(2, A + 4, A + (1 << 30), 8, 256, None) == EALIGN
     assert lib.qgemv_quantize_weights(5, A, A + (1 << 30), 8, 256, None) == EINVAL
+
+
+def test_fused_rejects_bad_arguments():
+    lib = qg._load()
+    X, Q, D, Y = A + (1 << 30), A + (2 << 30), A + (5 << 30), A + (3 << 30)
+    assert lib.qgemv_fused(1, A, None, None, None, Y, 8, 256, 1, None, 0, None) == EINVAL
+    assert lib.qgemv_fused(1, A, X + 4, None, None, Y, 8, 256, 1, None, 0, None) == EALIGN
+    assert lib.qgemv_fused(1, A, X, Q, None, Y, 8, 256, 1, None, 0, None) == EINVAL   # half the outputs
+    assert lib.qgemv_fused(1, A, X, Q + 2, D, Y, 8, 256, 1, None, 0, None) == EALIGN
+    assert lib.qgemv_fused(1, A, X, Q, D, X + 64, 8, 256, 1, None, 0, None) == EINVAL  # y over x
+    assert lib.qgemv_fused(1, A, X, X + 16, D, Y, 8, 256, 1, None, 0, None) == EINVAL  # codes over x
+    assert lib.qgemv_fused(3, A, X, None, None, Y, 8, 256, 1, None, 0, None) == EINVAL

@@ -228,3 +228,38 @@ def test_workspace_required_when_split():
     with pytest.raises(qg.QgemvError) as e:
         qg.qgemv_batch_plan("q4k", w, xq, xd, y, rows, cols, 1, plan)
     assert e.value.status == 3
+
+
+@pytest.mark.parametrize("wtype,rows,cols,nvec", [
+    ("q4k", 262144, 1536, 1), ("q4k", 8192, 2048, 1), ("q6k", 2048, 8192, 1),
+    ("q4k", 16384, 2048, 8), ("q4k", 512, 512, 1), ("q6k", 333, 8448, 3), ("q4k", 77, 8448, 2),
+])
+def test_fused_quantize_and_gemv(wtype, rows, cols, nvec):
+    """qgemv_fused: its codes and scales are the oracle's bit for bit, and its y is
+    bit-identical to quantize-then-GEMV with the same plan, including shapes whose plan splits
+    the columns. With code outputs the library may take the two-launch route; without them it
+    always runs the one-launch kernel (each workgroup quantizing its own slice)."""
+    import torch
+    import block_quantized_weight_act_amd as qg
+    _say("fused", wtype, rows, cols, nvec)
+    rng = np.random.default_rng(rows + cols + nvec)
+    x = (rng.standard_normal((nvec, cols)) * rng.choice([1e-3, 1.0, 40.0], size=(nvec, 1))).astype(np.float32)
+    x[0, 32:64] = 0.0
+    w = gu.quantize_weights(wtype, (rng.standard_normal((rows, cols)) * 0.02).astype(np.float32))
+    xt = gu.dev(x)
+    xq, xd = gu.quantize_act(x)
+    y_two = gu.gemv(wtype, w, xq, xd, rows, cols, nvec)
+    y = torch.full((nvec, rows), float("nan"), dtype=torch.float32, device=gu.DEV)
+    xq_out = torch.zeros((nvec, cols), dtype=torch.int8, device=gu.DEV)
+    xd_out = torch.zeros((nvec, cols // 32), dtype=torch.float32, device=gu.DEV)
+    nbytes = qg.qgemv_workspace_bytes(wtype, rows, cols, nvec)
+    ws = torch.empty(max(nbytes, 4), dtype=torch.uint8, device=gu.DEV) if nbytes else None
+    qg.qgemv_fused(wtype, w, xt, y, rows, cols, nvec, xq_out=xq_out, xd_out=xd_out, workspace=ws)
+    y_fused = gu.host(y)
+    assert np.array_equal(y_fused.view(np.uint32), y_two.view(np.uint32))
+    rq, rd = oracle.quantize_act(x)
+    assert np.array_equal(gu.host(xq_out), rq)
+    assert np.array_equal(gu.host(xd_out).view(np.uint32), rd.view(np.uint32))
+    y2 = torch.full_like(y, float("nan"))
+    qg.qgemv_fused(wtype, w, xt, y2, rows, cols, nvec, workspace=ws)      # without code outputs
+    assert np.array_equal(gu.host(y2).view(np.uint32), y_two.view(np.uint32))
