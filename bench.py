@@ -87,13 +87,26 @@ def load_traffic(workload: str, per_launch_bytes: int):
 
 
 def algorithmic_bytes(wl, wbytes: int) -> dict:
-    """Bytes each kernel must move at least once: the weights, its activation input, its output."""
-    gemv = wbytes + wl.nvec * wl.cols + wl.nvec * (wl.cols // 32) * 4 + wl.nvec * wl.rows * 4
-    quant = wl.nvec * wl.cols * 4 + wl.nvec * wl.cols + wl.nvec * (wl.cols // 32) * 4
-    return {"gemv": gemv, "quantize_act": quant, "step": gemv + quant}
+    """Bytes each piece must move at least once. GEMV: the weights, the activation codes and
+    scales, y. Quantization: the float32 activation in, codes and scales out. Step (the whole
+    path): the weights and the float32 activation in, codes, scales and y out."""
+    codes = wl.nvec * wl.cols + wl.nvec * (wl.cols // 32) * 4
+    gemv = wbytes + codes + wl.nvec * wl.rows * 4
+    quant = wl.nvec * wl.cols * 4 + codes
+    step = wbytes + wl.nvec * wl.cols * 4 + codes + wl.nvec * wl.rows * 4
+    return {"gemv": gemv, "quantize_act": quant, "step": step}
 
 
-def cpu_baseline(wl, seconds: float) -> dict:
+def plain_kernel_name(wtype: str, plan: dict) -> str:
+    """Template instance of the GEMV kernel that qgemv_batch launches for this plan (form 0:
+    codes read from memory), as it appears in kernel traces."""
+    return "gemv_%s_kernel<%d, %d, %d, 0>" % (wtype, plan["nvec"], plan["lanes_per_row"],
+                                              plan["chunks_per_lane"])
+
+
+def cpu_baseline(wl, seconds: float, y_gpu: np.ndarray) -> dict:
+    """The oracle's GEMV timed on a bounded sample of rows; on the way it also checks the
+    GPU's y on those rows against the oracle's error bound (untimed)."""
     import oracle
     threads = max(1, min(16, os.cpu_count() or 1))
     rows = min(wl.rows, 32768)
@@ -101,6 +114,9 @@ def cpu_baseline(wl, seconds: float) -> dict:
     w = wl.weight_rows(sample)
     wbuf = oracle.quantize_q4k(w) if wl.wtype == "q4k" else oracle.quantize_q6k(w)
     xq, xd = oracle.quantize_act(wl.activations())
+    ref = oracle.gemv(wl.wtype, wbuf, rows, wl.cols, xq, xd)
+    err = np.abs(y_gpu[:, sample].astype(np.float64) - ref["y"])
+    ratio = float(np.max(err / np.maximum(ref["bound"], np.finfo(np.float64).tiny)))
     oracle.gemv_threaded(wl.wtype, wbuf, rows, wl.cols, xq, xd, threads)       # warm-up
     reps, t0 = 0, time.perf_counter()
     while True:
@@ -115,7 +131,8 @@ def cpu_baseline(wl, seconds: float) -> dict:
             "kind": "oracle",
             "sample": "%d of %d rows (evenly spaced), full width, %d reps in %.1f s; "
                       "integer GEMV only, weights quantized beforehand" % (rows, wl.rows, reps, el),
-            "us_per_gemv_scaled_to_full": round(per * (wl.rows / rows) * 1e6, 1)}
+            "us_per_gemv_scaled_to_full": round(per * (wl.rows / rows) * 1e6, 1),
+            "gpu_y_check": {"rows": rows, "max_err_over_bound": ratio, "ok": ratio <= 1.0}}
 
 
 def _counter_rows(path):
@@ -130,12 +147,14 @@ def summarize_traffic(args) -> None:
     one weight copy (FETCH_SIZE) and the last ten plain 256 MiB device copies (WRITE_SIZE)."""
     import synth
     wl = synth.WORKLOADS[args.workload]
-    from block_quantized_weight_act_amd import qgemv_weight_bytes
+    from block_quantized_weight_act_amd import qgemv_plan_for, qgemv_weight_bytes
     wbytes = qgemv_weight_bytes(wl.wtype, wl.rows, wl.cols)
+    kname = plain_kernel_name(wl.wtype, dict(qgemv_plan_for(wl.wtype, wl.rows, wl.cols, wl.nvec),
+                                             nvec=wl.nvec))
     per = {}
     for path, counter in zip(args.summarize_traffic, ("FETCH_SIZE", "WRITE_SIZE")):
         rows = [r for r in _counter_rows(path) if r["Counter_Name"] == counter]
-        gemv = [float(r["Counter_Value"]) for r in rows if "gemv_%s_kernel" % wl.wtype in r["Kernel_Name"]]
+        gemv = [float(r["Counter_Value"]) for r in rows if kname in r["Kernel_Name"]]
         probe = [float(r["Counter_Value"]) for r in rows if "read_probe_kernel" in r["Kernel_Name"]]
         copies = [float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"]][-10:]
         per[counter] = {"gemv_kib": sum(gemv) / len(gemv), "gemv_dispatches": len(gemv),
@@ -148,7 +167,7 @@ def summarize_traffic(args) -> None:
     hbm = f["gemv_kib"] * 1024 * fetch_factor + w["gemv_kib"] * 1024 * write_factor
     alg = algorithmic_bytes(wl, wbytes)["gemv"]
     rec = {
-        "workload": wl.name, "kernel": "gemv_%s_kernel" % wl.wtype,
+        "workload": wl.name, "kernel": kname,
         "kernel_source_sha256": kernel_source_hash(),
         "fetch_size_kib_per_dispatch": round(f["gemv_kib"], 3),
         "write_size_kib_per_dispatch": round(w["gemv_kib"], 3),
@@ -201,20 +220,15 @@ def main():
     torch.cuda.set_device(dev)
     t_setup = time.perf_counter()
 
-    # weights: generated on the host in row chunks, quantized on the GPU by the library
+    # weights: generated on the host in row chunks, each quantized on the GPU into its place
     wbytes = qg.qgemv_weight_bytes(wl.wtype, wl.rows, wl.cols)
     w0 = torch.empty(wbytes, dtype=torch.uint8, device=dev)
     chunk = 32768
-    if wl.wtype == "q4k":
-        per_row = wbytes // wl.rows
-        for r0 in range(0, wl.rows, chunk):
-            r1 = min(wl.rows, r0 + chunk)
-            wf = torch.from_numpy(wl.weight_block(r0, r1)).to(dev)
-            qg.qgemv_quantize_weights(wl.wtype, wf, w0[r0 * per_row:r1 * per_row], r1 - r0, wl.cols)
-    else:
-        wf = torch.from_numpy(wl.weight_block(0, wl.rows)).to(dev)
-        qg.qgemv_quantize_weights(wl.wtype, wf, w0, wl.rows, wl.cols)
-    del wf
+    for r0 in range(0, wl.rows, chunk):
+        r1 = min(wl.rows, r0 + chunk)
+        wf = torch.from_numpy(wl.weight_block(r0, r1)).to(dev)
+        qg.qgemv_quantize_weights_rows(wl.wtype, wf, w0, wl.rows, wl.cols, r0, r1 - r0)
+        del wf
     copies = 1 if args.warm else max(1, min(64, math.ceil(COLD_BYTES / wbytes)))
     ws_list = [w0] + [w0.clone() for _ in range(copies - 1)]
 
@@ -289,6 +303,13 @@ def main():
     ms_gemv_graph = graph_timed(gemv, args.steps)
     ms_two_graph = graph_timed(two_launch, args.steps)
 
+    # the step's result must be usable: every output finite
+    step(0)
+    torch.cuda.synchronize()
+    if not bool(torch.isfinite(y).all()):
+        print("bench.py: the product gave non-finite outputs", file=sys.stderr)
+        sys.exit(1)
+
     nbytes = algorithmic_bytes(wl, wbytes)
     value = nbytes["step"] / (ms_step * 1e-3) / 1e9
     achieved = nbytes["gemv"] / (ms_gemv * 1e-3) / 1e9
@@ -323,7 +344,8 @@ def main():
         "wall_ms_per_step": round(wall_step, 5),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "kernel": "gemv_%s_kernel" % wl.wtype,
+                     "traffic": traffic,
+                     "kernel": plain_kernel_name(wl.wtype, dict(plan, nvec=wl.nvec)),
                      "algorithmic_bytes_per_launch": nbytes["gemv"]},
         "setup_s": round(setup_s, 1),
     }
@@ -338,7 +360,7 @@ def main():
         torch.cuda.synchronize()
         out["traffic_calibration"] = {"read_probe_bytes": wbytes, "copy_bytes": CALIB_COPY_BYTES}
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds, y.cpu().numpy())
     print(json.dumps(out), flush=True)
 
 

@@ -22,7 +22,7 @@ __all__ = [
     "qgemv_status_string", "qgemv_weight_bytes", "qgemv_quantize_act",
     "qgemv_workspace_bytes", "qgemv_q4k", "qgemv_q6k", "qgemv_batch", "qgemv_debug_partials",
     "qgemv_quantize_weights", "qgemv_plan_for", "qgemv_plan_workspace_bytes", "qgemv_batch_plan",
-    "qgemv_read_probe", "qgemv_fused",
+    "qgemv_read_probe", "qgemv_fused", "qgemv_quantize_weights_rows",
 ]
 
 QGEMV_Q4K = 1
@@ -74,6 +74,7 @@ def _load():
         "qgemv_batch": (ctypes.c_int, [ctypes.c_int, vp, vp, vp, vp, i64, i64, i32, vp, sz, vp]),
         "qgemv_debug_partials": (ctypes.c_int, [ctypes.c_int, vp, vp, vp, vp, vp, i64, i64, i32, vp]),
         "qgemv_quantize_weights": (ctypes.c_int, [ctypes.c_int, vp, vp, i64, i64, vp]),
+        "qgemv_quantize_weights_rows": (ctypes.c_int, [ctypes.c_int, vp, vp, i64, i64, i64, i64, vp]),
         "qgemv_plan_for": (ctypes.c_int, [ctypes.c_int, i64, i64, i32, ctypes.POINTER(Plan)]),
         "qgemv_plan_workspace_bytes": (sz, [ctypes.POINTER(Plan), i64, i64, i32]),
         "qgemv_batch_plan": (ctypes.c_int, [ctypes.c_int, vp, vp, vp, vp, i64, i64, i32,
@@ -234,6 +235,16 @@ def qgemv_quantize_weights(wtype, w, out, rows: int, cols: int, stream=None) -> 
     _check("qgemv_quantize_weights", lib.qgemv_quantize_weights(
         _wtype(wtype), _ptr(w, torch.float32, "w"), _ptr(out, name="out"), rows, cols,
         _stream(stream, out)))
+
+
+def qgemv_quantize_weights_rows(wtype, w, out, rows: int, cols: int, row0: int, nrows: int,
+                                stream=None) -> None:
+    """Rows [row0, row0 + nrows) (w: float32 [nrows][cols]) into their places in the whole
+    rows x cols tensor `out`."""
+    lib = _load()
+    _check("qgemv_quantize_weights_rows", lib.qgemv_quantize_weights_rows(
+        _wtype(wtype), _ptr(w, torch.float32, "w"), _ptr(out, name="out"), rows, cols, row0,
+        nrows, _stream(stream, out)))
 
 
 def qgemv_read_probe(buf, sink, blocks: int = 2048, nbytes: int | None = None, stream=None) -> None:

@@ -1,8 +1,13 @@
 // The per-lane activation slice of the GEMV kernels: for each of a lane's NC chunks and each
 // vector, the 32 int8 codes (8 words) and the float32 scale of that 32-column activation
-// block. Either read from memory (codes and scales made by qgemv_quantize_act) or, when the
-// kernel is given the float32 activation, quantized by the workgroup itself into LDS with the
-// same arithmetic (quantize_act_quad), so one launch does both steps of the product.
+// block. Either read from memory (codes and scales made by qgemv_quantize_act) or, in the
+// fused form, quantized by the workgroup itself into LDS with the same arithmetic
+// (quantize_act_quad), so one launch does both steps of the product.
+//
+// Getting the slice is split in two so that a kernel can put its first weight loads between
+// the halves: act_slice_issue starts the slice's global loads, act_slice_finish consumes
+// them. Loads complete in issue order, so the slice is waited for without waiting for the
+// weight loads issued after it, and the weights' HBM latency overlaps the slice's work.
 #pragma once
 
 #include "device_common.h"
@@ -10,48 +15,140 @@
 
 namespace qgemv {
 
+// Shape of the fused form's work: the workgroup's column chunk holds kBlocks activation
+// blocks (all vectors), kQuads groups of 4 elements; each lane takes up to kSlots quads per
+// round (quad base + i * blockDim.x + threadIdx.x of round base). kSlots is sized so that
+// one round of a 256-thread workgroup covers the chunk (at most 4 quads per lane; smaller
+// workgroups and larger chunks take more rounds).
+template <int V, int T, int NC>
+struct FusedAct {
+    static constexpr int kBlocks = V * T * NC;
+    static constexpr int kQuads = kBlocks * 8;
+    static constexpr int kSlots = kQuads >= 4 * 256 ? 4 : (kQuads + 255) / 256;
+};
+
 // LDS bytes the fused form needs: 32 code bytes and one float32 scale per block of the slice.
 template <int V, int T, int NC>
 constexpr int act_slice_lds_bytes() {
-    return V * T * NC * (32 + 4);
+    return FusedAct<V, T, NC>::kBlocks * (32 + 4);
+}
+
+// What act_slice_issue leaves in flight for act_slice_finish: the fused form's first round of
+// float32 quads (the plain form loads straight into the slice registers).
+template <int V, int T, int NC, bool FUSED>
+struct ActPending {
+    float4 xv[FUSED ? FusedAct<V, T, NC>::kSlots : 1];
+};
+
+namespace fused_detail {
+
+// Quad qd of the chunk: block blk = qd / 8 is vector blk / (T NC) and column block
+// chunk0 + blk % (T NC); elem is the offset of its 4 floats in x (and of its codes in
+// xq_out). True when the quad exists.
+template <int V, int T, int NC>
+__device__ __forceinline__ bool quad_at(const GemvArgs &a, int qd, int64_t &elem, int &v,
+                                        int &gc) {
+    const int blk = qd >> 3;
+    v = blk / (T * NC);
+    gc = static_cast<int>(blockIdx.y) * T * NC + blk % (T * NC);
+    elem = v * (static_cast<int64_t>(a.nchunks) * 32) + 32 * static_cast<int64_t>(gc) +
+           4 * (qd & 7);
+    return qd < FusedAct<V, T, NC>::kQuads && gc < a.nchunks;
 }
 
 template <int V, int T, int NC>
-__device__ __forceinline__ void load_act_slice(const GemvArgs &a, const int (&g)[NC],
-                                               const bool (&cv)[NC], int t,
-                                               uint32_t (&xw)[V][NC][8], float (&xs)[V][NC]) {
-    const int nsub = a.nchunks;
-    const int64_t cols = static_cast<int64_t>(nsub) * 32;
-    if (a.x != nullptr) {
-        // The workgroup quantizes the blocks of its column chunk (all vectors) once: quad qd
-        // (4 elements) of block blk = qd / 8; block blk is vector blk / (T NC), local block
-        // blk % (T NC) = column block chunk0 + local. Blocks past the end of the row are zero.
-        constexpr int kBlocks = V * T * NC;
-        extern __shared__ uint4 lds[];
-        uint32_t *s_codes = reinterpret_cast<uint32_t *>(lds);
-        float *s_scale = reinterpret_cast<float *>(lds + 2 * kBlocks);
-        const int chunk0 = static_cast<int>(blockIdx.y) * T * NC;
-        for (int base = 0; base < kBlocks * 8; base += blockDim.x) {
-            const int qd = base + static_cast<int>(threadIdx.x);
-            const int blk = qd >> 3;
-            const int v = blk / (T * NC), lb = blk % (T * NC);
-            const int gc = chunk0 + lb;
-            const bool in_slice = qd < kBlocks * 8;
-            const bool ok = in_slice && gc < nsub;
-            const int64_t elem = v * cols + 32 * static_cast<int64_t>(gc) + 4 * (qd & 7);
-            const float4 xv = ok ? *reinterpret_cast<const float4 *>(a.x + elem)
-                                 : make_float4(0.f, 0.f, 0.f, 0.f);
-            const ActQuad q = quantize_act_quad(xv);
-            if (in_slice) {
-                s_codes[qd] = q.codes;
-                if ((qd & 7) == 0) s_scale[blk] = q.scale;
-            }
-            if (ok && blockIdx.x == 0 && a.xq_out != nullptr) {
-                *reinterpret_cast<uint32_t *>(a.xq_out + elem) = q.codes;
-                if ((qd & 7) == 0) a.xd_out[static_cast<int64_t>(v) * nsub + gc] = q.scale;
+__device__ __forceinline__ void load_round(const GemvArgs &a, int base,
+                                           float4 (&xv)[FusedAct<V, T, NC>::kSlots]) {
+#pragma unroll
+    for (int i = 0; i < FusedAct<V, T, NC>::kSlots; i++) {
+        int64_t elem;
+        int v, gc;
+        const bool ok = quad_at<V, T, NC>(
+            a, base + i * static_cast<int>(blockDim.x) + static_cast<int>(threadIdx.x), elem, v,
+            gc);
+        xv[i] = ok ? *reinterpret_cast<const float4 *>(a.x + elem)
+                   : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+}
+
+// Quantize one round into LDS (codes word qd, then the scale of block qd / 8 after all the
+// codes); the first workgroup of the column chunk also stores them to xq_out / xd_out.
+template <int V, int T, int NC>
+__device__ __forceinline__ void store_round(const GemvArgs &a, int base,
+                                            const float4 (&xv)[FusedAct<V, T, NC>::kSlots]) {
+    using F = FusedAct<V, T, NC>;
+    extern __shared__ uint4 lds[];
+    uint32_t *s_codes = reinterpret_cast<uint32_t *>(lds);
+    float *s_scale = reinterpret_cast<float *>(lds + 2 * F::kBlocks);
+#pragma unroll
+    for (int i = 0; i < F::kSlots; i++) {
+        const int first = base + i * static_cast<int>(blockDim.x);   // the same for the workgroup
+        if (first >= F::kQuads) break;
+        const int qd = first + static_cast<int>(threadIdx.x);
+        int64_t elem;
+        int v, gc;
+        const bool ok = quad_at<V, T, NC>(a, qd, elem, v, gc);
+        const ActQuad q = quantize_act_quad(xv[i]);   // every lane: the block max is cross-lane
+        if (qd < F::kQuads) {
+            s_codes[qd] = q.codes;
+            if ((qd & 7) == 0) s_scale[qd >> 3] = q.scale;
+        }
+        if (ok && blockIdx.x == 0 && a.xq_out != nullptr) {
+            *reinterpret_cast<uint32_t *>(a.xq_out + elem) = q.codes;
+            if ((qd & 7) == 0) a.xd_out[static_cast<int64_t>(v) * a.nchunks + gc] = q.scale;
+        }
+    }
+}
+
+}  // namespace fused_detail
+
+template <int V, int T, int NC, bool FUSED>
+__device__ __forceinline__ void act_slice_issue(const GemvArgs &a, const int (&g)[NC],
+                                                const bool (&cv)[NC], uint32_t (&xw)[V][NC][8],
+                                                float (&xs)[V][NC],
+                                                ActPending<V, T, NC, FUSED> &pend) {
+    if constexpr (FUSED) {
+        (void)g; (void)cv; (void)xw; (void)xs;
+        fused_detail::load_round<V, T, NC>(a, 0, pend.xv);
+    } else {
+        (void)pend;
+        const int nsub = a.nchunks;
+        const int64_t cols = static_cast<int64_t>(nsub) * 32;
+#pragma unroll
+        for (int v = 0; v < V; v++) {
+#pragma unroll
+            for (int k = 0; k < NC; k++) {
+                uint4 lo = make_uint4(0, 0, 0, 0), hi = make_uint4(0, 0, 0, 0);
+                float s = 0.0f;
+                if (cv[k]) {
+                    const int8_t *p = a.xq + v * cols + 32 * static_cast<int64_t>(g[k]);
+                    lo = load16(p);
+                    hi = load16(p + 16);
+                    s = a.xd[static_cast<int64_t>(v) * nsub + g[k]];
+                }
+                xw[v][k][0] = lo.x; xw[v][k][1] = lo.y; xw[v][k][2] = lo.z; xw[v][k][3] = lo.w;
+                xw[v][k][4] = hi.x; xw[v][k][5] = hi.y; xw[v][k][6] = hi.z; xw[v][k][7] = hi.w;
+                xs[v][k] = s;
             }
         }
+    }
+}
+
+template <int V, int T, int NC, bool FUSED>
+__device__ __forceinline__ void act_slice_finish(const GemvArgs &a, const bool (&cv)[NC], int t,
+                                                 uint32_t (&xw)[V][NC][8], float (&xs)[V][NC],
+                                                 ActPending<V, T, NC, FUSED> &pend) {
+    if constexpr (FUSED) {
+        using F = FusedAct<V, T, NC>;
+        const int round = F::kSlots * static_cast<int>(blockDim.x);
+        fused_detail::store_round<V, T, NC>(a, 0, pend.xv);
+        for (int base = round; base < F::kQuads; base += round) {
+            fused_detail::load_round<V, T, NC>(a, base, pend.xv);
+            fused_detail::store_round<V, T, NC>(a, base, pend.xv);
+        }
         __syncthreads();
+        extern __shared__ uint4 lds[];
+        const float *s_scale = reinterpret_cast<const float *>(lds + 2 * F::kBlocks);
 #pragma unroll
         for (int v = 0; v < V; v++) {
 #pragma unroll
@@ -64,24 +161,8 @@ __device__ __forceinline__ void load_act_slice(const GemvArgs &a, const int (&g)
                 xs[v][k] = cv[k] ? s_scale[blk] : 0.0f;
             }
         }
-        return;
-    }
-#pragma unroll
-    for (int v = 0; v < V; v++) {
-#pragma unroll
-        for (int k = 0; k < NC; k++) {
-            uint4 lo = make_uint4(0, 0, 0, 0), hi = make_uint4(0, 0, 0, 0);
-            float s = 0.0f;
-            if (cv[k]) {
-                const int8_t *p = a.xq + v * cols + 32 * static_cast<int64_t>(g[k]);
-                lo = load16(p);
-                hi = load16(p + 16);
-                s = a.xd[static_cast<int64_t>(v) * nsub + g[k]];
-            }
-            xw[v][k][0] = lo.x; xw[v][k][1] = lo.y; xw[v][k][2] = lo.z; xw[v][k][3] = lo.w;
-            xw[v][k][4] = hi.x; xw[v][k][5] = hi.y; xw[v][k][6] = hi.z; xw[v][k][7] = hi.w;
-            xs[v][k] = s;
-        }
+    } else {
+        (void)a; (void)cv; (void)t; (void)xw; (void)xs; (void)pend;
     }
 }
 

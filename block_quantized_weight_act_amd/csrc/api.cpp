@@ -373,18 +373,24 @@ int qgemv_debug_partials(int wtype, const void *w, const int8_t *xq, const float
     return e == hipSuccess ? QGEMV_OK : hip_fail(e);
 }
 
-int qgemv_quantize_weights(int wtype, const float *w, void *out, int64_t rows, int64_t cols,
-                           hipStream_t stream) {
-    if ((wtype != QGEMV_Q4K && wtype != QGEMV_Q6K) || !w || !out || !shape_ok(rows, cols, 1))
+int qgemv_quantize_weights_rows(int wtype, const float *w, void *out, int64_t rows,
+                                int64_t cols, int64_t row0, int64_t nrows, hipStream_t stream) {
+    if ((wtype != QGEMV_Q4K && wtype != QGEMV_Q6K) || !w || !out || !shape_ok(rows, cols, 1) ||
+        row0 < 0 || nrows < 1 || row0 > rows - nrows)
         return QGEMV_EINVAL;
     if (!aligned(w, 16) || !aligned(out, 16)) return QGEMV_EALIGN;
     const size_t ob = weight_bytes(wtype, rows, cols);
-    if (overlaps(out, ob, w, static_cast<size_t>(rows) * cols * sizeof(float))) return QGEMV_EINVAL;
+    if (overlaps(out, ob, w, static_cast<size_t>(nrows) * cols * sizeof(float))) return QGEMV_EINVAL;
     const hipError_t e =
         wtype == QGEMV_Q4K
-            ? launch_quantize_q4k(w, static_cast<uint8_t *>(out), rows, cols, stream)
-            : launch_quantize_q6k(w, static_cast<uint8_t *>(out), rows, cols, stream);
+            ? launch_quantize_q4k(w, static_cast<uint8_t *>(out), rows, cols, row0, nrows, stream)
+            : launch_quantize_q6k(w, static_cast<uint8_t *>(out), rows, cols, row0, nrows, stream);
     return e == hipSuccess ? QGEMV_OK : hip_fail(e);
+}
+
+int qgemv_quantize_weights(int wtype, const float *w, void *out, int64_t rows, int64_t cols,
+                           hipStream_t stream) {
+    return qgemv_quantize_weights_rows(wtype, w, out, rows, cols, 0, rows, stream);
 }
 
 int qgemv_read_probe(const void *buf, size_t bytes, uint32_t *sink, int32_t blocks,

@@ -145,8 +145,11 @@ struct ActQuad {
 
 __device__ __forceinline__ ActQuad quantize_act_quad(const float4 v) {
     float amax = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
-#pragma unroll
-    for (int off = 4; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
+    // the maximum over the block's 8 lanes: xor 1, xor 2, then the half-row mirror pairs
+    // each quad with the other one
+    amax = fmaxf(amax, dpp<kDppXor1>(amax));
+    amax = fmaxf(amax, dpp<kDppXor2>(amax));
+    amax = fmaxf(amax, dpp<kDppHalfMirror>(amax));
     const float scale = amax / 127.0f;
     const float inv = amax > 0.0f ? 127.0f / amax : 0.0f;
     const float e[4] = {v.x, v.y, v.z, v.w};

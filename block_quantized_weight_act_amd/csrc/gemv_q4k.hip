@@ -38,8 +38,9 @@
 
 namespace qgemv {
 
-template <int V, int T, int NC, bool DBG>
+template <int V, int T, int NC, int MODE>
 __global__ void __launch_bounds__(256) gemv_q4k_kernel(GemvArgs a) {
+    constexpr bool DBG = MODE == kModeDebug;
     constexpr int RPW = 64 / T;              // rows per wave step
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -91,10 +92,19 @@ __global__ void __launch_bounds__(256) gemv_q4k_kernel(GemvArgs a) {
     };
 
     // This lane's activation slice: 32 codes, the block scale and the block code sum per chunk.
+    // Its loads go out first, then the first step's weight loads, then the slice is finished
+    // while the weights are in flight.
+    constexpr bool FUSED = MODE == kModeFused;
     uint32_t xw[V][NC][8];
     float xs[V][NC];
     float xsumf[V][NC];                      // code sums as float (exact: |S| <= 4064)
-    load_act_slice<V, T, NC>(a, g, cv, t, xw, xs);
+    ActPending<V, T, NC, FUSED> pend;
+    act_slice_issue<V, T, NC, FUSED>(a, g, cv, xw, xs, pend);
+    const int st0 = blockIdx.x * wpb + wave;
+    __builtin_amdgcn_sched_barrier(0);
+    issue_step(st0);                         // rows (>= 1) clamped: valid even when st0 >= steps
+    __builtin_amdgcn_sched_barrier(0);
+    act_slice_finish<V, T, NC, FUSED>(a, cv, t, xw, xs, pend);
 #pragma unroll
     for (int v = 0; v < V; v++) {
 #pragma unroll
@@ -108,8 +118,7 @@ __global__ void __launch_bounds__(256) gemv_q4k_kernel(GemvArgs a) {
         }
     }
 
-    for (int st = blockIdx.x * wpb + wave; st < steps; st += stride) {
-        issue_step(st);
+    for (int st = st0; st < steps; st += stride) {
         // Keep every load of the step ahead of the arithmetic: without this fence the
         // scheduler interleaves them to save registers and waits for each load in turn.
         __builtin_amdgcn_sched_barrier(0);
@@ -180,6 +189,10 @@ __global__ void __launch_bounds__(256) gemv_q4k_kernel(GemvArgs a) {
                 }
             }
         }
+        // The next step's loads go out as soon as this step's arithmetic is done, so the
+        // values of one step are never live across the loop's back edge with the next ones.
+        __builtin_amdgcn_sched_barrier(0);
+        if (st + stride < steps) issue_step(st + stride);
     }
 }
 
@@ -192,11 +205,13 @@ hipError_t launch_variant(const GemvArgs &a, const LaunchShape &s, bool debug,
                           hipStream_t stream) {
     const dim3 grid(static_cast<unsigned>(s.blocks), static_cast<unsigned>(s.splits));
     const dim3 block(static_cast<unsigned>(64 * s.waves));
-    const size_t lds = a.x != nullptr ? act_slice_lds_bytes<V, T, NC>() : 0;
+    const size_t lds = act_slice_lds_bytes<V, T, NC>();
     if (debug)
-        hipLaunchKernelGGL((gemv_q4k_kernel<V, T, NC, true>), grid, block, lds, stream, a);
+        hipLaunchKernelGGL((gemv_q4k_kernel<V, T, NC, kModeDebug>), grid, block, 0, stream, a);
+    else if (a.x != nullptr)
+        hipLaunchKernelGGL((gemv_q4k_kernel<V, T, NC, kModeFused>), grid, block, lds, stream, a);
     else
-        hipLaunchKernelGGL((gemv_q4k_kernel<V, T, NC, false>), grid, block, lds, stream, a);
+        hipLaunchKernelGGL((gemv_q4k_kernel<V, T, NC, kModePlain>), grid, block, 0, stream, a);
     return hipGetLastError();
 }
 

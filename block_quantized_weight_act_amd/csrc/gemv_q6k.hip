@@ -25,8 +25,9 @@
 
 namespace qgemv {
 
-template <int V, int T, int NC, bool DBG>
+template <int V, int T, int NC, int MODE>
 __global__ void __launch_bounds__(256) gemv_q6k_kernel(GemvArgs a) {
+    constexpr bool DBG = MODE == kModeDebug;
     constexpr int RPW = 64 / T;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -79,10 +80,19 @@ __global__ void __launch_bounds__(256) gemv_q6k_kernel(GemvArgs a) {
         }
     };
 
+    // The activation slice's loads, then the first step's weight loads, then the slice is
+    // finished while the weights are in flight.
+    constexpr bool FUSED = MODE == kModeFused;
     uint32_t xw[V][NC][8];
     float xs[V][NC];
     int xlo[V][NC], xhi[V][NC];             // activation code sums of the two 16-column halves
-    load_act_slice<V, T, NC>(a, g, cv, t, xw, xs);
+    ActPending<V, T, NC, FUSED> pend;
+    act_slice_issue<V, T, NC, FUSED>(a, g, cv, xw, xs, pend);
+    const int st0 = blockIdx.x * wpb + wave;
+    __builtin_amdgcn_sched_barrier(0);
+    issue_step(st0);                         // rows (>= 1) clamped: valid even when st0 >= steps
+    __builtin_amdgcn_sched_barrier(0);
+    act_slice_finish<V, T, NC, FUSED>(a, cv, t, xw, xs, pend);
 #pragma unroll
     for (int v = 0; v < V; v++) {
 #pragma unroll
@@ -100,8 +110,7 @@ __global__ void __launch_bounds__(256) gemv_q6k_kernel(GemvArgs a) {
         }
     }
 
-    for (int st = blockIdx.x * wpb + wave; st < steps; st += stride) {
-        issue_step(st);
+    for (int st = st0; st < steps; st += stride) {
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int gg = 0; gg < G; gg++) {
@@ -162,6 +171,10 @@ __global__ void __launch_bounds__(256) gemv_q6k_kernel(GemvArgs a) {
                 }
             }
         }
+        // The next step's loads go out as soon as this step's arithmetic is done, so the
+        // values of one step are never live across the loop's back edge with the next ones.
+        __builtin_amdgcn_sched_barrier(0);
+        if (st + stride < steps) issue_step(st + stride);
     }
 }
 
@@ -174,11 +187,13 @@ hipError_t launch_variant(const GemvArgs &a, const LaunchShape &s, bool debug,
                           hipStream_t stream) {
     const dim3 grid(static_cast<unsigned>(s.blocks), static_cast<unsigned>(s.splits));
     const dim3 block(static_cast<unsigned>(64 * s.waves));
-    const size_t lds = a.x != nullptr ? act_slice_lds_bytes<V, T, NC>() : 0;
+    const size_t lds = act_slice_lds_bytes<V, T, NC>();
     if (debug)
-        hipLaunchKernelGGL((gemv_q6k_kernel<V, T, NC, true>), grid, block, lds, stream, a);
+        hipLaunchKernelGGL((gemv_q6k_kernel<V, T, NC, kModeDebug>), grid, block, 0, stream, a);
+    else if (a.x != nullptr)
+        hipLaunchKernelGGL((gemv_q6k_kernel<V, T, NC, kModeFused>), grid, block, lds, stream, a);
     else
-        hipLaunchKernelGGL((gemv_q6k_kernel<V, T, NC, false>), grid, block, lds, stream, a);
+        hipLaunchKernelGGL((gemv_q6k_kernel<V, T, NC, kModePlain>), grid, block, 0, stream, a);
     return hipGetLastError();
 }
 

@@ -36,6 +36,12 @@ struct GemvArgs {
     int32_t nchunks;       // 16-byte chunks per row = 8 * nb
 };
 
+// Kernel forms, a template parameter so that each has its own name in kernel traces:
+// kModePlain reads the activation codes made by qgemv_quantize_act; kModeDebug does the same
+// and writes the integer partials instead of y; kModeFused quantizes the float32 activation
+// itself (GemvArgs::x).
+enum KernelMode : int { kModePlain = 0, kModeDebug = 1, kModeFused = 2 };
+
 struct LaunchShape {
     int lanes;             // lanes per row (T)
     int chunks;            // chunks per lane (NC)
@@ -53,10 +59,12 @@ hipError_t launch_gemv_q6k(const GemvArgs &a, const LaunchShape &s, int nvec, bo
                            hipStream_t stream);
 hipError_t launch_splitk_reduce(const float *part, float *y, int64_t n, int splits,
                                 hipStream_t stream);
+// Rows [row0, row0 + nrows) of a rows x cols matrix (w points at row row0) into their places
+// in the whole tensor `out`.
 hipError_t launch_quantize_q4k(const float *w, uint8_t *out, int64_t rows, int64_t cols,
-                               hipStream_t stream);
+                               int64_t row0, int64_t nrows, hipStream_t stream);
 hipError_t launch_quantize_q6k(const float *w, uint8_t *out, int64_t rows, int64_t cols,
-                               hipStream_t stream);
+                               int64_t row0, int64_t nrows, hipStream_t stream);
 
 hipError_t launch_read_probe(const void *buf, int64_t bytes, uint32_t *sink, int blocks,
                              hipStream_t stream);

@@ -1,7 +1,9 @@
 // Load-time weight quantization into the Q4_K and Q6_K layouts (oxinfer README, "How it
 // works", quant.rs: weights are block-quantized once when the model is loaded). Not on the
 // per-token path; written for clarity: one 64-lane wavefront per 256-weight super-block,
-// 4 consecutive weights per lane.
+// 4 consecutive weights per lane. A launch may cover a range of rows: w holds those rows,
+// blk0 is the index of their first super-block in the whole tensor and ntotal the tensor's
+// super-block count, which fixes where each plane starts.
 //
 // Every decision that yields an integer (a code, a sub-scale, an fp16 super-scale) is an
 // IEEE float32 operation with round-to-nearest-even, so the bytes are reproducible on any
@@ -19,11 +21,13 @@ __device__ __forceinline__ float clampf(float v, float lo, float hi) {
 // Q4_K: sub-block j (32 weights) = lanes 8j .. 8j+7.
 __global__ void __launch_bounds__(256) quantize_q4k_kernel(const float *__restrict__ w,
                                                            uint8_t *__restrict__ out,
-                                                           int64_t nblocks, int nb, int64_t cols) {
+                                                           int64_t nblocks, int nb, int64_t cols,
+                                                           int64_t blk0, int64_t ntotal) {
     const int lane = threadIdx.x & 63;
-    const int64_t blk = static_cast<int64_t>(blockIdx.x) * (blockDim.x >> 6) + (threadIdx.x >> 6);
-    if (blk >= nblocks) return;                      // uniform over the wavefront
-    const int64_t row = blk / nb, b = blk % nb;
+    const int64_t local = static_cast<int64_t>(blockIdx.x) * (blockDim.x >> 6) + (threadIdx.x >> 6);
+    if (local >= nblocks) return;                    // uniform over the wavefront
+    const int64_t row = local / nb, b = local % nb;
+    const int64_t blk = blk0 + local;                // index in the whole tensor
     const float4 v4 = *reinterpret_cast<const float4 *>(w + row * cols + b * kQK + 4 * lane);
     const float v[4] = {v4.x, v4.y, v4.z, v4.w};
     const int j = lane >> 3;
@@ -71,20 +75,22 @@ __global__ void __launch_bounds__(256) quantize_q4k_kernel(const float *__restri
         lead ? ((static_cast<uint32_t>(sc) >> 4) << (2 * j)) |
                    ((static_cast<uint32_t>(m) >> 4) << (16 + 2 * j))
              : 0u);
-    // Header plane: block blk's 16 header bytes at 128 * nblocks + 16 * blk.
+    // Header plane: block blk's 16 header bytes at 128 * ntotal + 16 * blk.
     if (lane == 0)
-        *reinterpret_cast<uint4 *>(out + nblocks * 128 + blk * 16) =
+        *reinterpret_cast<uint4 *>(out + ntotal * 128 + blk * 16) =
             make_uint4(dh | (mh << 16), wa, wb, wc);
 }
 
 // Q6_K: sub-block j (16 weights) = lanes 4j .. 4j+3.
 __global__ void __launch_bounds__(256) quantize_q6k_kernel(const float *__restrict__ w,
                                                            uint8_t *__restrict__ out,
-                                                           int64_t nblocks, int nb, int64_t cols) {
+                                                           int64_t nblocks, int nb, int64_t cols,
+                                                           int64_t blk0, int64_t ntotal) {
     const int lane = threadIdx.x & 63;
-    const int64_t blk = static_cast<int64_t>(blockIdx.x) * (blockDim.x >> 6) + (threadIdx.x >> 6);
-    if (blk >= nblocks) return;
-    const int64_t row = blk / nb, b = blk % nb;
+    const int64_t local = static_cast<int64_t>(blockIdx.x) * (blockDim.x >> 6) + (threadIdx.x >> 6);
+    if (local >= nblocks) return;
+    const int64_t row = local / nb, b = local % nb;
+    const int64_t blk = blk0 + local;
     const float4 v4 = *reinterpret_cast<const float4 *>(w + row * cols + b * kQK + 4 * lane);
     const float v[4] = {v4.x, v4.y, v4.z, v4.w};
 
@@ -104,10 +110,10 @@ __global__ void __launch_bounds__(256) quantize_q6k_kernel(const float *__restri
         q[i] = step != 0.0f ? static_cast<int>(clampf(rintf(v[i] / step), -32.0f, 31.0f)) + 32 : 32;
 
     // Planes of block blk: low bits at 128 * blk, high bits at 128 N + 64 * blk, sub-scales at
-    // 192 N + 16 * blk, d at 208 N + 2 * blk (N = nblocks).
+    // 192 N + 16 * blk, d at 208 N + 2 * blk (N = ntotal).
     uint8_t *low_out = out + blk * 128;
-    uint8_t *high_out = out + nblocks * 128 + blk * 64;
-    uint8_t *sc_out = out + nblocks * 192 + blk * 16;
+    uint8_t *high_out = out + ntotal * 128 + blk * 64;
+    uint8_t *sc_out = out + ntotal * 192 + blk * 16;
     // Weight 4*lane + i = 32k + 16g + t with k = lane/8, g = (lane%8)/4, t = 4(lane%4) + i.
     const int k = lane >> 3, g = (lane >> 2) & 1, s4 = lane & 3;
     uint32_t low = 0, high = 0;
@@ -127,26 +133,26 @@ __global__ void __launch_bounds__(256) quantize_q6k_kernel(const float *__restri
                                           ? (static_cast<uint32_t>(sc) & 0xFFu) << (8 * (jj & 3))
                                           : 0u);
     if ((lane & 15) == 0) *reinterpret_cast<uint32_t *>(sc_out + 4 * (lane >> 4)) = scb;
-    if (lane == 0) reinterpret_cast<uint16_t *>(out + nblocks * 208)[blk] = static_cast<uint16_t>(dh);
+    if (lane == 0) reinterpret_cast<uint16_t *>(out + ntotal * 208)[blk] = static_cast<uint16_t>(dh);
 }
 
 hipError_t launch_quantize_q4k(const float *w, uint8_t *out, int64_t rows, int64_t cols,
-                               hipStream_t stream) {
-    const int64_t nb = cols / kQK, nblocks = rows * nb;
+                               int64_t row0, int64_t nrows, hipStream_t stream) {
+    const int64_t nb = cols / kQK, nblocks = nrows * nb;
     const int waves = 4;
     const int64_t grid = (nblocks + waves - 1) / waves;
     hipLaunchKernelGGL(quantize_q4k_kernel, dim3(static_cast<unsigned>(grid)), dim3(64 * waves), 0,
-                       stream, w, out, nblocks, static_cast<int>(nb), cols);
+                       stream, w, out, nblocks, static_cast<int>(nb), cols, row0 * nb, rows * nb);
     return hipGetLastError();
 }
 
 hipError_t launch_quantize_q6k(const float *w, uint8_t *out, int64_t rows, int64_t cols,
-                               hipStream_t stream) {
-    const int64_t nb = cols / kQK, nblocks = rows * nb;
+                               int64_t row0, int64_t nrows, hipStream_t stream) {
+    const int64_t nb = cols / kQK, nblocks = nrows * nb;
     const int waves = 4;
     const int64_t grid = (nblocks + waves - 1) / waves;
     hipLaunchKernelGGL(quantize_q6k_kernel, dim3(static_cast<unsigned>(grid)), dim3(64 * waves), 0,
-                       stream, w, out, nblocks, static_cast<int>(nb), cols);
+                       stream, w, out, nblocks, static_cast<int>(nb), cols, row0 * nb, rows * nb);
     return hipGetLastError();
 }
 

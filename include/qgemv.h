@@ -208,6 +208,18 @@ int qgemv_quantize_weights(int wtype, const float *w, void *out, int64_t rows, i
                            hipStream_t stream);
 
 /*
+ * The same quantization for rows [row0, row0 + nrows) of a rows x cols matrix, so
+ * a large matrix can be loaded in pieces: w holds only those rows (float32
+ * [nrows][cols], 16-byte aligned), out is the whole tensor (qgemv_weight_bytes(
+ * wtype, rows, cols) bytes, 16-byte aligned) and only the bytes of those rows'
+ * super-blocks are written, in every plane. The pieces of one matrix give the
+ * same bytes as one call over all rows. QGEMV_EINVAL for an empty or
+ * out-of-range row range.
+ */
+int qgemv_quantize_weights_rows(int wtype, const float *w, void *out, int64_t rows,
+                                int64_t cols, int64_t row0, int64_t nrows, hipStream_t stream);
+
+/*
  * Launch plan of the GEMV kernels. Each row is cut into 16-byte chunks of
  * weight codes (one 32-column activation block each); a group of
  * lanes_per_row lanes of a 64-lane wavefront shares a row, each lane taking

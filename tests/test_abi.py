@@ -97,6 +97,14 @@ def test_other_entry_points_reject_bad_arguments():
     assert lib.qgemv_quantize_weights(2, A, A + 64, 8, 256, None) == EINVAL   # overlap
     assert lib.qgemv_quantize_weights(2, A + 4, A + (1 << 30), 8, 256, None) == EALIGN
     assert lib.qgemv_quantize_weights(5, A, A + (1 << 30), 8, 256, None) == EINVAL
+    W = A + (1 << 30)
+    rows = lib.qgemv_quantize_weights_rows
+    assert rows(1, A, W, 8, 256, 0, 0, None) == EINVAL        # empty range
+    assert rows(1, A, W, 8, 256, -1, 2, None) == EINVAL       # starts before row 0
+    assert rows(1, A, W, 8, 256, 7, 2, None) == EINVAL        # ends past the last row
+    assert rows(1, A, W, 8, 256, 1 << 40, 2, None) == EINVAL
+    assert rows(2, A + 4, W, 8, 256, 0, 8, None) == EALIGN
+    assert rows(2, A, A + 64, 8, 256, 4, 4, None) == EINVAL   # tensor over the rows
 
 
 def test_fused_rejects_bad_arguments():

@@ -72,6 +72,30 @@ def test_quantize_weights_bitexact(wtype, sigma):
     assert np.array_equal(got, ref)
 
 
+@pytest.mark.parametrize("wtype", ["q4k", "q6k"])
+def test_quantize_weights_rows_pieces(wtype):
+    """Row ranges quantized in pieces, in any order, give the one-call tensor byte for byte,
+    and one piece writes only its own rows' bytes in every plane."""
+    import torch
+    import block_quantized_weight_act_amd as qg
+    rows, cols = 37, 768
+    _say("quantize_weights_rows", wtype, rows, cols)
+    rng = np.random.default_rng(5)
+    w = (rng.standard_normal((rows, cols)) * 0.03).astype(np.float32)
+    ref = oracle.quantize_q4k(w) if wtype == "q4k" else oracle.quantize_q6k(w)
+    out = torch.full((qg.qgemv_weight_bytes(wtype, rows, cols),), 0xAB, dtype=torch.uint8,
+                     device=gu.DEV)
+    for r0, r1 in [(6, 37), (0, 5), (5, 6)]:
+        qg.qgemv_quantize_weights_rows(wtype, gu.dev(w[r0:r1]), out, rows, cols, r0, r1 - r0)
+    assert np.array_equal(gu.host(out), ref)
+    out.fill_(0xAB)
+    qg.qgemv_quantize_weights_rows(wtype, gu.dev(w[9:14]), out, rows, cols, 9, 5)
+    got_planes = oracle.planes(wtype, gu.host(out), rows, cols)
+    for got, want in zip(got_planes, oracle.planes(wtype, ref, rows, cols)):
+        assert np.array_equal(got[9:14], want[9:14])
+        assert (got[:9] == 0xAB).all() and (got[14:] == 0xAB).all()
+
+
 # ---------------------------------------------------------------- GEMV ------
 def _check_gemv(wtype, wbuf, rows, cols, x, plan=None, debug=True):
     nvec = x.shape[0]
