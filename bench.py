@@ -16,7 +16,8 @@ and the reads come from HBM. Inputs are resident in HBM before the timed region.
 
 Prints ONE JSON line (rank 0, N = 1):
   value         whole-step algorithmic bytes / step time, GB/s
-  roofline      the step's GEMV kernel: algorithmic bytes per launch / its average launch duration
+  roofline      the step's dominant kernel (the fused kernel when the step is one launch, else
+                its GEMV launch): algorithmic bytes per launch / its average launch duration
                 (HIP events on the launch stream over a run of back-to-back launches),
                 against 8000 GB/s; traffic from the committed rocprofv3 counter summary when
                 it was taken on the current kernel source, else null
@@ -49,11 +50,13 @@ def parse():
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of "
                          "'bench.py --traffic-calibration' into profiles/gemv_<workload>_traffic.json")
-    ap.add_argument("--summarize-trace", metavar="KERNEL_STATS_CSV",
-                    help="print a markdown table of a rocprofv3 --kernel-trace --stats summary")
+    ap.add_argument("--summarize-trace", nargs="+", metavar="CSV",
+                    help="print a markdown table of a rocprofv3 --kernel-trace --stats summary "
+                         "(KERNEL_STATS_CSV); with the run's KERNEL_TRACE_CSV as well, also the "
+                         "average of each kernel over its dispatches after the warmup")
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=2000)
     ap.add_argument("--workload", default="q4k_262144x1536")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -97,11 +100,12 @@ def algorithmic_bytes(wl, wbytes: int) -> dict:
     return {"gemv": gemv, "quantize_act": quant, "step": step}
 
 
-def plain_kernel_name(wtype: str, plan: dict) -> str:
-    """Template instance of the GEMV kernel that qgemv_batch launches for this plan (form 0:
-    codes read from memory), as it appears in kernel traces."""
-    return "gemv_%s_kernel<%d, %d, %d, 0>" % (wtype, plan["nvec"], plan["lanes_per_row"],
-                                              plan["chunks_per_lane"])
+def roofline_kernel(wtype: str, plan: dict, nvec: int, launches: int) -> str:
+    """The step's dominant kernel, as its template instance appears in kernel traces: the
+    one-launch fused kernel (form 2) when qgemv_fused makes one launch for this shape, else the
+    GEMV kernel of the two-launch route (form 0, codes read from memory)."""
+    return "gemv_%s_kernel<%d, %d, %d, %d>" % (wtype, nvec, plan["lanes_per_row"],
+                                               plan["chunks_per_lane"], 2 if launches == 1 else 0)
 
 
 def cpu_baseline(wl, seconds: float, y_gpu: np.ndarray) -> dict:
@@ -117,21 +121,35 @@ def cpu_baseline(wl, seconds: float, y_gpu: np.ndarray) -> dict:
     ref = oracle.gemv(wl.wtype, wbuf, rows, wl.cols, xq, xd)
     err = np.abs(y_gpu[:, sample].astype(np.float64) - ref["y"])
     ratio = float(np.max(err / np.maximum(ref["bound"], np.finfo(np.float64).tiny)))
-    oracle.gemv_threaded(wl.wtype, wbuf, rows, wl.cols, xq, xd, threads)       # warm-up
-    reps, t0 = 0, time.perf_counter()
-    while True:
-        oracle.gemv_threaded(wl.wtype, wbuf, rows, wl.cols, xq, xd, threads)
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= seconds:
-            break
-    per = el / reps
     nbytes = wbuf.size + xq.size + xd.size * 4 + wl.nvec * rows * 4
+
+    def rate(nthreads, budget):
+        oracle.gemv_threaded(wl.wtype, wbuf, rows, wl.cols, xq, xd, nthreads)   # warm-up
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            oracle.gemv_threaded(wl.wtype, wbuf, rows, wl.cols, xq, xd, nthreads)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= budget:
+                return el / reps, reps, el
+
+    per, reps, el = rate(threads, seconds)
+    per1, reps1, el1 = rate(1, seconds / 2)
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
+    except OSError:
+        pass
     return {"value": round(nbytes / per / 1e9, 3), "unit": "GB/s", "cores": threads,
             "kind": "oracle",
-            "sample": "%d of %d rows (evenly spaced), full width, %d reps in %.1f s; "
-                      "integer GEMV only, weights quantized beforehand" % (rows, wl.rows, reps, el),
+            "sample": "%d of %d rows (evenly spaced), full width, %d reps in %.1f s on %d threads; "
+                      "integer GEMV only, weights quantized beforehand" % (rows, wl.rows, reps, el,
+                                                                          threads),
             "us_per_gemv_scaled_to_full": round(per * (wl.rows / rows) * 1e6, 1),
+            "one_core": {"value": round(nbytes / per1 / 1e9, 3), "unit": "GB/s", "reps": reps1,
+                         "seconds": round(el1, 1)},
+            "cpu_model": model,
             "gpu_y_check": {"rows": rows, "max_err_over_bound": ratio, "ok": ratio <= 1.0}}
 
 
@@ -147,15 +165,18 @@ def summarize_traffic(args) -> None:
     one weight copy (FETCH_SIZE) and the last ten plain 256 MiB device copies (WRITE_SIZE)."""
     import synth
     wl = synth.WORKLOADS[args.workload]
-    from block_quantized_weight_act_amd import qgemv_plan_for, qgemv_weight_bytes
-    wbytes = qgemv_weight_bytes(wl.wtype, wl.rows, wl.cols)
-    kname = plain_kernel_name(wl.wtype, dict(qgemv_plan_for(wl.wtype, wl.rows, wl.cols, wl.nvec),
-                                             nvec=wl.nvec))
+    import block_quantized_weight_act_amd as qg
+    wbytes = qg.qgemv_weight_bytes(wl.wtype, wl.rows, wl.cols)
+    launches = qg.qgemv_fused_launches(wl.wtype, wl.rows, wl.cols, wl.nvec, True)
+    kname = roofline_kernel(wl.wtype, qg.qgemv_plan_for(wl.wtype, wl.rows, wl.cols, wl.nvec),
+                            wl.nvec, launches)
     per = {}
     for path, counter in zip(args.summarize_traffic, ("FETCH_SIZE", "WRITE_SIZE")):
         rows = [r for r in _counter_rows(path) if r["Counter_Name"] == counter]
         gemv = [float(r["Counter_Value"]) for r in rows if kname in r["Kernel_Name"]]
-        probe = [float(r["Counter_Value"]) for r in rows if "read_probe_kernel" in r["Kernel_Name"]]
+        # read probes over one whole weight copy (not the one-workgroup warmup marker)
+        probe = [float(r["Counter_Value"]) for r in rows if "read_probe_kernel" in r["Kernel_Name"]
+                 and int(r["Grid_Size"]) > int(r["Workgroup_Size"])]
         copies = [float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"]][-10:]
         per[counter] = {"gemv_kib": sum(gemv) / len(gemv), "gemv_dispatches": len(gemv),
                         "probe_kib": sum(probe) / len(probe), "copy_kib": sum(copies) / len(copies)}
@@ -165,7 +186,7 @@ def summarize_traffic(args) -> None:
     fetch_factor_copy = CALIB_COPY_BYTES / (f["copy_kib"] * 1024)
     write_factor = CALIB_COPY_BYTES / (w["copy_kib"] * 1024)
     hbm = f["gemv_kib"] * 1024 * fetch_factor + w["gemv_kib"] * 1024 * write_factor
-    alg = algorithmic_bytes(wl, wbytes)["gemv"]
+    alg = algorithmic_bytes(wl, wbytes)["step" if launches == 1 else "gemv"]
     rec = {
         "workload": wl.name, "kernel": kname,
         "kernel_source_sha256": kernel_source_hash(),
@@ -186,16 +207,33 @@ def summarize_traffic(args) -> None:
     print(json.dumps(rec))
 
 
-def summarize_trace(path: str) -> None:
-    import csv
-    with open(path) as f:
-        rows = list(csv.DictReader(f))
+def summarize_trace(paths: list) -> None:
+    rows = _counter_rows(paths[0])
     print("| kernel | calls | average us | min us | max us | stddev us | % of GPU time |")
     print("|---|---|---|---|---|---|---|")
     for r in rows:
         print("| `%s` | %s | %.3f | %.3f | %.3f | %.3f | %s |" % (
             r["Name"], r["Calls"], float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
             float(r["MaxNs"]) / 1e3, float(r["StdDev"]) / 1e3, r["Percentage"]))
+    if len(paths) < 2:
+        return
+    # per-dispatch durations after the end of the warmup (first touch of buffers, clocks
+    # settling), which the run marks with a one-workgroup read probe
+    trace = sorted(_counter_rows(paths[1]), key=lambda r: int(r["Start_Timestamp"]))
+    marks = [int(r["Start_Timestamp"]) for r in trace if "read_probe_kernel" in r["Kernel_Name"]
+             and r["Grid_Size_X"] == r["Workgroup_Size_X"]]
+    start = marks[-1] if marks else 0
+    per = {}
+    for r in trace:
+        if int(r["Start_Timestamp"]) > start:
+            d = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+            per.setdefault(r["Kernel_Name"], []).append(d)
+    print()
+    print("| kernel (dispatches after the warmup) | dispatches | average us | median us |")
+    print("|---|---|---|---|")
+    for name, ds in sorted(per.items(), key=lambda kv: -sum(kv[1])):
+        ds = sorted(ds)
+        print("| `%s` | %d | %.3f | %.3f |" % (name, len(ds), sum(ds) / len(ds), ds[len(ds) // 2]))
 
 
 def main():
@@ -258,6 +296,8 @@ def main():
         gemv(i)
 
     def timed(fn, n):
+        for i in range(min(n, 50)):           # this form's own short warmup
+            fn(i)
         torch.cuda.synchronize()
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
@@ -270,9 +310,28 @@ def main():
         wall = time.perf_counter() - w0_
         return e0.elapsed_time(e1) / n, wall / n * 1e3
 
-    def graph_timed(fn, n):
-        """The same launches captured once into a HIP graph and replayed: GPU time per launch
-        without the host's per-call overhead (what a decode loop that replays a graph sees)."""
+    def spread(fn, n, batches=20):
+        """Per-launch time in each of `batches` consecutive batches of back-to-back launches
+        (one event pair per batch, so no per-launch event overhead): p10, median, p90 (us)."""
+        per = max(1, n // batches)
+        for i in range(min(n, 50)):
+            fn(i)
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(batches + 1)]
+        torch.cuda.synchronize()
+        evs[0].record()
+        for b in range(batches):
+            for i in range(per):
+                fn(b * per + i)
+            evs[b + 1].record()
+        torch.cuda.synchronize()
+        d = sorted(evs[b].elapsed_time(evs[b + 1]) * 1e3 / per for b in range(batches))
+        return {"batches": batches, "launches_per_batch": per, "p10": round(d[batches // 10], 3),
+                "median": round(d[batches // 2], 3), "p90": round(d[(9 * batches) // 10], 3)}
+
+    def capture(fn, n):
+        """The same launches captured once into a HIP graph (replayed, they give the GPU time
+        per launch without the host's per-call overhead, as a decode loop replaying a graph
+        sees it)."""
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
@@ -282,8 +341,11 @@ def main():
         with torch.cuda.graph(g):
             for i in range(n):
                 fn(i)
-        g.replay()
         torch.cuda.synchronize()
+        return g
+
+    def replay_timed(g, n):
+        g.replay()
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record()
@@ -292,16 +354,34 @@ def main():
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / n
 
+    # The GPU's clocks dip for some 10-20 ms whenever work resumes after an idle stretch of a
+    # few ms (launch durations rise by up to 20% and recover), so every host-side preparation
+    # (graph capture) is done first and the measured phases then run back to back after the
+    # warmup steps.
+    graphs = {name: capture(fn, args.steps)
+              for name, fn in (("step", step), ("gemv", gemv), ("two", two_launch))}
+    # first touch of every weight copy (page mappings) before any measured kernel runs
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    sink_mark = torch.zeros(16, dtype=torch.uint8, device=dev)
+    for _ in range(2):
+        for wc in ws_list:
+            qg.qgemv_read_probe(wc, sink, blocks=4096)
     for i in range(args.warmup):
         step(i)
-        two_launch(i)
+    # a one-workgroup read of 16 bytes marks the end of the warmup in kernel traces
+    qg.qgemv_read_probe(sink_mark, sink, blocks=1, nbytes=16)
     ms_step, wall_step = timed(step, args.steps)
     ms_gemv, _ = timed(gemv, args.steps)
     ms_quant, _ = timed(lambda i: quantize(), args.steps)
     ms_two, _ = timed(two_launch, args.steps)
-    ms_step_graph = graph_timed(step, args.steps)
-    ms_gemv_graph = graph_timed(gemv, args.steps)
-    ms_two_graph = graph_timed(two_launch, args.steps)
+    ms_step_graph = replay_timed(graphs["step"], args.steps)
+    ms_gemv_graph = replay_timed(graphs["gemv"], args.steps)
+    ms_two_graph = replay_timed(graphs["two"], args.steps)
+    step_dist = spread(step, args.steps)
+    # the practical read ceiling: a plain streaming read of the same (cold, rotating) copies
+    ms_probe, _ = timed(lambda i: qg.qgemv_read_probe(ws_list[i % copies], sink, blocks=4096),
+                        args.steps)
+    probe_gbs = wbytes / (ms_probe * 1e-3) / 1e9
 
     # the step's result must be usable: every output finite
     step(0)
@@ -312,8 +392,11 @@ def main():
 
     nbytes = algorithmic_bytes(wl, wbytes)
     value = nbytes["step"] / (ms_step * 1e-3) / 1e9
-    achieved = nbytes["gemv"] / (ms_gemv * 1e-3) / 1e9
-    traffic = load_traffic(args.workload, nbytes["gemv"])
+    launches = qg.qgemv_fused_launches(wl.wtype, wl.rows, wl.cols, wl.nvec, True)
+    # the dominant kernel: the step itself when it is one launch, else its GEMV launch
+    rk_bytes, rk_ms = (nbytes["step"], ms_step) if launches == 1 else (nbytes["gemv"], ms_gemv)
+    achieved = rk_bytes / (rk_ms * 1e-3) / 1e9
+    traffic = load_traffic(args.workload, rk_bytes)
     out = {
         "metric": "achieved HBM GB/s and % of roofline, Q4_K GEMV batch-1 (us per GEMV)",
         "value": round(value, 1),
@@ -345,8 +428,12 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic,
-                     "kernel": plain_kernel_name(wl.wtype, dict(plan, nvec=wl.nvec)),
-                     "algorithmic_bytes_per_launch": nbytes["gemv"]},
+                     "kernel": roofline_kernel(wl.wtype, plan, wl.nvec, launches),
+                     "algorithmic_bytes_per_launch": rk_bytes, "us_per_launch": round(rk_ms * 1e3, 3)},
+        "step_launches": launches,
+        "us_per_step_distribution": step_dist,
+        "read_probe": {"gbs": round(probe_gbs, 1), "us": round(ms_probe * 1e3, 3),
+                       "roofline_achieved_pct_of_probe": round(100 * achieved / probe_gbs, 2)},
         "setup_s": round(setup_s, 1),
     }
     if args.traffic_calibration:

@@ -22,7 +22,7 @@ __all__ = [
     "qgemv_status_string", "qgemv_weight_bytes", "qgemv_quantize_act",
     "qgemv_workspace_bytes", "qgemv_q4k", "qgemv_q6k", "qgemv_batch", "qgemv_debug_partials",
     "qgemv_quantize_weights", "qgemv_plan_for", "qgemv_plan_workspace_bytes", "qgemv_batch_plan",
-    "qgemv_read_probe", "qgemv_fused", "qgemv_quantize_weights_rows",
+    "qgemv_read_probe", "qgemv_fused", "qgemv_quantize_weights_rows", "qgemv_fused_launches",
 ]
 
 QGEMV_Q4K = 1
@@ -75,6 +75,7 @@ def _load():
         "qgemv_debug_partials": (ctypes.c_int, [ctypes.c_int, vp, vp, vp, vp, vp, i64, i64, i32, vp]),
         "qgemv_quantize_weights": (ctypes.c_int, [ctypes.c_int, vp, vp, i64, i64, vp]),
         "qgemv_quantize_weights_rows": (ctypes.c_int, [ctypes.c_int, vp, vp, i64, i64, i64, i64, vp]),
+        "qgemv_fused_launches": (ctypes.c_int, [ctypes.c_int, i64, i64, i32, ctypes.c_int]),
         "qgemv_plan_for": (ctypes.c_int, [ctypes.c_int, i64, i64, i32, ctypes.POINTER(Plan)]),
         "qgemv_plan_workspace_bytes": (sz, [ctypes.POINTER(Plan), i64, i64, i32]),
         "qgemv_batch_plan": (ctypes.c_int, [ctypes.c_int, vp, vp, vp, vp, i64, i64, i32,
@@ -235,6 +236,15 @@ def qgemv_quantize_weights(wtype, w, out, rows: int, cols: int, stream=None) -> 
     _check("qgemv_quantize_weights", lib.qgemv_quantize_weights(
         _wtype(wtype), _ptr(w, torch.float32, "w"), _ptr(out, name="out"), rows, cols,
         _stream(stream, out)))
+
+
+def qgemv_fused_launches(wtype, rows: int, cols: int, nvec: int = 1,
+                         with_outputs: bool = True) -> int:
+    """1 or 2: the kernel launches qgemv_fused makes for this shape."""
+    n = _load().qgemv_fused_launches(_wtype(wtype), rows, cols, nvec, int(bool(with_outputs)))
+    if n == 0:
+        raise ValueError("invalid weight type or shape")
+    return n
 
 
 def qgemv_quantize_weights_rows(wtype, w, out, rows: int, cols: int, row0: int, nrows: int,

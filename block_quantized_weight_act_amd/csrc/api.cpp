@@ -299,6 +299,21 @@ int qgemv_batch(int wtype, const void *w, const int8_t *xq, const float *xd, flo
                     workspace, workspace_bytes, stream);
 }
 
+int qgemv_fused_launches(int wtype, int64_t rows, int64_t cols, int32_t nvec, int with_outputs) {
+    if ((wtype != QGEMV_Q4K && wtype != QGEMV_Q6K) || !shape_ok(rows, cols, nvec)) return 0;
+    if (!with_outputs) return 1;
+    // Every workgroup of the fused kernel quantizes the whole activation slice its lanes read.
+    // When that slice is large next to the workgroup's share of the weights (wide rows, many
+    // vectors, few rows per workgroup), the repeated quantization costs more than a second
+    // launch: then, if the caller gave places for the codes, the library quantizes once into
+    // them and runs the product from them. Both forms give the same codes and the same y.
+    const qgemv_plan plan = make_plan(wtype, rows, cols, nvec);
+    const double slice = static_cast<double>(nvec) * plan.lanes_per_row * plan.chunks_per_lane * 32;
+    const double share = static_cast<double>(weight_bytes(wtype, rows, cols)) /
+                         (static_cast<double>(plan.blocks) * plan.splits);
+    return slice > 0.15 * share ? 2 : 1;
+}
+
 int qgemv_fused(int wtype, const void *w, const float *x, int8_t *xq_out, float *xd_out, float *y,
                 int64_t rows, int64_t cols, int32_t nvec, void *workspace, size_t workspace_bytes,
                 hipStream_t stream) {
@@ -309,15 +324,7 @@ int qgemv_fused(int wtype, const void *w, const float *x, int8_t *xq_out, float 
     act.x = x;
     act.xq_out = xq_out;
     act.xd_out = xd_out;
-    // Every workgroup of the fused kernel quantizes the whole activation slice its lanes read.
-    // When that slice is large next to the workgroup's share of the weights (wide rows, many
-    // vectors, few rows per workgroup), the repeated quantization costs more than a second
-    // launch: then, if the caller gave places for the codes, quantize once into them and run
-    // the product from them. Both forms give the same codes and the same y, bit for bit.
-    const double slice = static_cast<double>(nvec) * plan.lanes_per_row * plan.chunks_per_lane * 32;
-    const double share = static_cast<double>(weight_bytes(wtype, rows, cols)) /
-                         (static_cast<double>(plan.blocks) * plan.splits);
-    if (xq_out && xd_out && slice > 0.15 * share) {
+    if (xq_out && xd_out && qgemv_fused_launches(wtype, rows, cols, nvec, 1) == 2) {
         int st = check_fused_act(act, w, weight_bytes(wtype, rows, cols), y,
                                  static_cast<size_t>(nvec) * rows * sizeof(float), cols, nvec);
         if (st != QGEMV_OK) return st;

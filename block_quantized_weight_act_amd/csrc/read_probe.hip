@@ -3,27 +3,33 @@
 // kernel that must read the same bytes, the way oxinfer's membench measures the machine's
 // read bandwidth before judging its decode kernels (oxinfer README, "Performance").
 //
-// Each lane keeps four independent 16-byte loads in flight per step of a grid-stride loop;
-// the XOR of everything read is stored only if it equals a value that random data does not
-// produce, which keeps the loads alive without adding write traffic.
+// Each wave reads kRuns runs of 64 consecutive 16-byte words (8 KB) per iteration, all
+// issued before any is used and marked nontemporal, and the waves stride over the buffer: the
+// access pattern of the GEMV's code plane without its arithmetic. The XOR of everything read is
+// stored only if it equals a value that random data does not produce, which keeps the loads
+// alive without adding write traffic.
 #include "device_common.h"
 #include "qgemv_internal.h"
 
 namespace qgemv {
 
+constexpr int kRuns = 8;
+
 __global__ void __launch_bounds__(256) read_probe_kernel(const uint4 *__restrict__ buf,
                                                          int64_t n16, uint32_t *__restrict__ sink) {
-    const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
-    int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    const int lane = threadIdx.x & 63;
+    const int64_t wave = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) >> 6;
+    const int64_t nwaves = (static_cast<int64_t>(gridDim.x) * blockDim.x) >> 6;
     uint32_t acc = 0;
-    for (; i + 3 * stride < n16; i += 4 * stride) {
-        const uint4 a = buf[i], b = buf[i + stride], c = buf[i + 2 * stride], d = buf[i + 3 * stride];
-        acc ^= a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w ^ c.x ^ c.y ^ c.z ^ c.w ^ d.x ^ d.y ^
-               d.z ^ d.w;
-    }
-    for (; i < n16; i += stride) {
-        const uint4 a = buf[i];
-        acc ^= a.x ^ a.y ^ a.z ^ a.w;
+    for (int64_t base = wave * (kRuns * 64); base < n16; base += nwaves * (kRuns * 64)) {
+        uint4 v[kRuns];
+#pragma unroll
+        for (int u = 0; u < kRuns; u++) {
+            const int64_t idx = base + u * 64 + lane;
+            v[u] = idx < n16 ? load16_stream(buf + idx) : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int u = 0; u < kRuns; u++) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
     }
     if (acc == 0x9E3779B9u) sink[0] = acc;
 }

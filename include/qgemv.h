@@ -179,6 +179,14 @@ int qgemv_fused(int wtype, const void *w, const float *x, int8_t *xq_out, float 
                 size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * How many kernel launches qgemv_fused makes for this shape: 1 (the one-launch
+ * kernel) or 2 (qgemv_quantize_act, then the product); with_outputs says whether
+ * xq_out / xd_out are given (without them it is always 1). 0 for an invalid
+ * type or shape. Host only; no device work.
+ */
+int qgemv_fused_launches(int wtype, int64_t rows, int64_t cols, int32_t nvec, int with_outputs);
+
+/*
  * Test hook: the exact integer partials of the same kernels.
  * P int32: Q4_K [nvec][rows][cols/32] (sum of q * xq per 32-column
  * sub-block), Q6_K [nvec][rows][cols/16] (sum of (q - 32) * xq per 16-column

@@ -107,6 +107,18 @@ def test_other_entry_points_reject_bad_arguments():
     assert rows(2, A, A + 64, 8, 256, 4, 4, None) == EINVAL   # tensor over the rows
 
 
+def test_fused_launch_count():
+    """The one-launch kernel unless code outputs are wanted and the activation slice is large
+    next to a workgroup's share of the weights (then quantize once, then the product)."""
+    assert qg.qgemv_fused_launches("q4k", 262144, 1536, 1) == 1
+    assert qg.qgemv_fused_launches("q4k", 8192, 2048, 1) == 1
+    assert qg.qgemv_fused_launches("q6k", 2048, 8192, 1) == 2
+    assert qg.qgemv_fused_launches("q4k", 16384, 2048, 8) == 2
+    assert qg.qgemv_fused_launches("q4k", 16384, 2048, 8, with_outputs=False) == 1
+    assert qg._load().qgemv_fused_launches(1, 0, 256, 1, 1) == 0
+    assert qg._load().qgemv_fused_launches(3, 8, 256, 1, 1) == 0
+
+
 def test_fused_rejects_bad_arguments():
     lib = qg._load()
     X, Q, D, Y = A + (1 << 30), A + (2 << 30), A + (5 << 30), A + (3 << 30)
