@@ -67,7 +67,6 @@ int64_t target_waves(int32_t nvec) { return nvec <= 2 ? 256 * 64 : 256 * 16; }
 // (nvec * NC <= 8). When a row has more than 256 chunks (cols > 8192) or rows alone are too
 // few to give every CU work, the columns are split.
 qgemv_plan make_plan(int wtype, int64_t rows, int64_t cols, int32_t nvec) {
-    (void)wtype;
     const int64_t nchunks = cols / 32;
     int best_t = 64, best_nc = 1;
     double best_cost = 1e30;
@@ -91,10 +90,13 @@ qgemv_plan make_plan(int wtype, int64_t rows, int64_t cols, int32_t nvec) {
     p.chunks_per_lane = best_nc;
     p.waves_per_block = 4;
     int splits = splits_for(best_t, best_nc, cols);
-    // Too few rows to fill the GPU: split further (whole chunks per lane kept).
+    // Too few rows to fill the GPU: split further (whole chunks per lane kept). Not for small
+    // matrices, which are latency-bound: there the second (reduce) launch costs more than the
+    // extra waves win (512 x 512: 3.7 us split against 2.0 us whole).
     const int64_t rows_per_wave = 64 / best_t;
     int64_t waves = (rows + rows_per_wave - 1) / rows_per_wave * splits;
-    while (waves < target_waves(nvec) / 8 && best_nc > 1) {
+    const bool small = weight_bytes(wtype, rows, cols) < (size_t{16} << 20);
+    while (!small && waves < target_waves(nvec) / 8 && best_nc > 1) {
         best_nc--;
         splits = splits_for(best_t, best_nc, cols);
         waves = (rows + rows_per_wave - 1) / rows_per_wave * splits;
