@@ -236,6 +236,232 @@ def summarize_trace(paths: list) -> None:
         print("| `%s` | %d | %.3f | %.3f |" % (name, len(ds), sum(ds) / len(ds), ds[len(ds) // 2]))
 
 
+def timed(fn, n):
+    """ms per launch (HIP events on the current stream) and host wall ms per launch of n
+    back-to-back launches, after 50 of the same."""
+    import torch
+    for i in range(min(n, 50)):           # this form's own short warmup
+        fn(i)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    w0_ = time.perf_counter()
+    e0.record()
+    for i in range(n):
+        fn(i)
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0_
+    return e0.elapsed_time(e1) / n, wall / n * 1e3
+
+def spread(fn, n, batches=20):
+    """Per-launch time in each of `batches` consecutive batches of back-to-back launches
+    (one event pair per batch, so no per-launch event overhead): p10, median, p90 (us)."""
+    import torch
+    per = max(1, n // batches)
+    for i in range(min(n, 50)):
+        fn(i)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(batches + 1)]
+    torch.cuda.synchronize()
+    evs[0].record()
+    for b in range(batches):
+        for i in range(per):
+            fn(b * per + i)
+        evs[b + 1].record()
+    torch.cuda.synchronize()
+    d = sorted(evs[b].elapsed_time(evs[b + 1]) * 1e3 / per for b in range(batches))
+    return {"batches": batches, "launches_per_batch": per, "p10": round(d[batches // 10], 3),
+            "median": round(d[batches // 2], 3), "p90": round(d[(9 * batches) // 10], 3)}
+
+def capture(fn, n):
+    """The same launches captured once into a HIP graph (replayed, they give the GPU time
+    per launch without the host's per-call overhead, as a decode loop replaying a graph
+    sees it)."""
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn(0)
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(n):
+            fn(i)
+    torch.cuda.synchronize()
+    return g
+
+def replay_timed(g, n):
+    import torch
+    g.replay()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n
+
+
+def bench_group(args) -> dict:
+    """Several matrices sharing one activation (a multi-matrix workload). Step = one launch of
+    qgemv_multi_fused (the float32 activation quantized inside, every matrix's y out). Beside
+    it: the same product from codes (qgemv_multi), one qgemv_fused per matrix, and
+    quantize-then-one-GEMV-per-matrix."""
+    import torch
+
+    import block_quantized_weight_act_amd as qg
+    import synth
+
+    grp = synth.GROUPS[args.workload]
+    cols, nvec = grp.cols, grp.nvec
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    t_setup = time.perf_counter()
+    tensors = []
+    for p in grp.parts:
+        wb = qg.qgemv_weight_bytes(p.wtype, p.rows, cols)
+        w0 = torch.empty(wb, dtype=torch.uint8, device=dev)
+        for r0 in range(0, p.rows, 32768):
+            r1 = min(p.rows, r0 + 32768)
+            wf = torch.from_numpy(p.weight_block(r0, r1)).to(dev)
+            qg.qgemv_quantize_weights_rows(p.wtype, wf, w0, p.rows, cols, r0, r1 - r0)
+            del wf
+        tensors.append(w0)
+    wbytes = sum(t.numel() for t in tensors)
+    copies = 1 if args.warm else max(1, min(256, math.ceil(COLD_BYTES / wbytes)))
+    sets = [tensors] + [[t.clone() for t in tensors] for _ in range(copies - 1)]
+    x = torch.from_numpy(grp.activations()).to(dev)
+    xq = torch.empty((nvec, cols), dtype=torch.int8, device=dev)
+    xd = torch.empty((nvec, cols // 32), dtype=torch.float32, device=dev)
+    ys = [torch.empty((nvec, p.rows), dtype=torch.float32, device=dev) for p in grp.parts]
+    work = [torch.empty(max(4, qg.qgemv_workspace_bytes(p.wtype, p.rows, cols, nvec)),
+                        dtype=torch.uint8, device=dev) for p in grp.parts]
+    mats = [[(p.wtype, st[k], p.rows, ys[k]) for k, p in enumerate(grp.parts)] for st in sets]
+    torch.cuda.synchronize()
+    setup_s = time.perf_counter() - t_setup
+
+    def step(i):
+        qg.qgemv_multi_fused(mats[i % copies], x, cols, nvec)
+
+    def multi(i):
+        qg.qgemv_multi(mats[i % copies], xq, xd, cols, nvec)
+
+    def fused_each(i):
+        for k, p in enumerate(grp.parts):
+            qg.qgemv_fused(p.wtype, sets[i % copies][k], x, ys[k], p.rows, cols, nvec,
+                           workspace=work[k])
+
+    def separate(i):
+        qg.qgemv_quantize_act(x, xq, xd, cols, nvec)
+        for k, p in enumerate(grp.parts):
+            qg.qgemv_batch(p.wtype, sets[i % copies][k], xq, xd, ys[k], p.rows, cols, nvec,
+                           workspace=work[k])
+
+    forms = (("step", step), ("multi", multi), ("fused_each", fused_each), ("separate", separate))
+    graphs = {name: capture(fn, args.steps) for name, fn in forms}
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    sink_mark = torch.zeros(16, dtype=torch.uint8, device=dev)
+    for _ in range(2):
+        for st in sets:
+            for t in st:
+                qg.qgemv_read_probe(t, sink, blocks=4096)
+    separate(0)            # makes the codes the multi form reads
+    for i in range(args.warmup):
+        step(i)
+    qg.qgemv_read_probe(sink_mark, sink, blocks=1, nbytes=16)
+    ms = {name: timed(fn, args.steps)[0] for name, fn in forms}
+    ms_graph = {name: replay_timed(graphs[name], args.steps) for name, _ in forms}
+    step_dist = spread(step, args.steps)
+    step(0)
+    torch.cuda.synchronize()
+    if not all(bool(torch.isfinite(y).all()) for y in ys):
+        print("bench.py: the product gave non-finite outputs", file=sys.stderr)
+        sys.exit(1)
+
+    codes = nvec * cols + nvec * (cols // 32) * 4
+    ybytes = sum(nvec * p.rows * 4 for p in grp.parts)
+    step_bytes = wbytes + nvec * cols * 4 + ybytes
+    multi_bytes = wbytes + codes + ybytes
+    t, nc = qg.qgemv_multi_geometry(cols, nvec)
+    achieved = step_bytes / (ms["step"] * 1e-3) / 1e9
+    out = {
+        "metric": "achieved HBM GB/s and % of roofline, multi-matrix GEMV sharing one activation",
+        "value": round(achieved, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms["step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8xq4k/q6k",
+        "data": "synthetic",
+        "config": {"workload": "%d matrices sharing one activation, %s, cols %d, batch %d, cold "
+                               "weights (%d rotating copies)" % (
+                                   len(grp.parts), " + ".join("%s %d" % (p.wtype.upper(), p.rows)
+                                                              for p in grp.parts),
+                                   cols, nvec, copies),
+                   "name": grp.name, "cols": cols, "nvec": nvec, "weight_bytes": wbytes,
+                   "lanes_per_row": t, "chunks_per_lane": nc},
+        "us_per_step": round(ms["step"] * 1e3, 3),
+        "us_per_multi_from_codes": round(ms["multi"] * 1e3, 3),
+        "us_per_fused_each": round(ms["fused_each"] * 1e3, 3),
+        "us_per_separate": round(ms["separate"] * 1e3, 3),
+        "graph_replay": {"us_per_step": round(ms_graph["step"] * 1e3, 3),
+                         "us_per_multi_from_codes": round(ms_graph["multi"] * 1e3, 3),
+                         "us_per_fused_each": round(ms_graph["fused_each"] * 1e3, 3),
+                         "us_per_separate": round(ms_graph["separate"] * 1e3, 3)},
+        "us_per_step_distribution": step_dist,
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "gemv_multi_kernel<%d, %d, %d, 2>" % (nvec, t, nc),
+                     "algorithmic_bytes_per_launch": step_bytes,
+                     "us_per_launch": round(ms["step"] * 1e3, 3)},
+        "multi_from_codes_gbs": round(multi_bytes / (ms["multi"] * 1e-3) / 1e9, 1),
+        "setup_s": round(setup_s, 1),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_group(grp, args.cpu_seconds,
+                                                 [y.cpu().numpy() for y in ys])
+    return out
+
+
+def cpu_baseline_group(grp, seconds: float, y_gpu: list) -> dict:
+    """The oracle's GEMV over every matrix of the group (all rows), timed; on the way each
+    GPU y is checked against the oracle's error bound (untimed)."""
+    import oracle
+    threads = max(1, min(16, os.cpu_count() or 1))
+    xq, xd = oracle.quantize_act(grp.activations())
+    bufs, ratio = [], 0.0
+    for p, yg in zip(grp.parts, y_gpu):
+        w = p.weight_block(0, p.rows)
+        buf = oracle.quantize_q4k(w) if p.wtype == "q4k" else oracle.quantize_q6k(w)
+        ref = oracle.gemv(p.wtype, buf, p.rows, grp.cols, xq, xd)
+        err = np.abs(yg.astype(np.float64) - ref["y"])
+        ratio = max(ratio, float(np.max(err / np.maximum(ref["bound"], np.finfo(np.float64).tiny))))
+        bufs.append(buf)
+    nbytes = sum(b.size for b in bufs) + xq.size + xd.size * 4 + sum(grp.nvec * p.rows * 4
+                                                                    for p in grp.parts)
+
+    def once():
+        for p, b in zip(grp.parts, bufs):
+            oracle.gemv_threaded(p.wtype, b, p.rows, grp.cols, xq, xd, threads)
+
+    once()
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        once()
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {"value": round(nbytes / (el / reps) / 1e9, 3), "unit": "GB/s", "cores": threads,
+            "kind": "oracle", "sample": "every row of every matrix, %d reps in %.1f s on %d "
+                                        "threads" % (reps, el, threads),
+            "gpu_y_check": {"max_err_over_bound": ratio, "ok": ratio <= 1.0}}
+
+
 def main():
     args = parse()
     if args.summarize_traffic:
@@ -248,10 +474,13 @@ def main():
         print("bench.py measures one GPU: this build has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
+    import synth
+    if args.workload in synth.GROUPS:
+        print(json.dumps(bench_group(args)), flush=True)
+        return
     import torch
 
     import block_quantized_weight_act_amd as qg
-    import synth
 
     wl = synth.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
@@ -294,65 +523,6 @@ def main():
     def two_launch(i):
         quantize()
         gemv(i)
-
-    def timed(fn, n):
-        for i in range(min(n, 50)):           # this form's own short warmup
-            fn(i)
-        torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        w0_ = time.perf_counter()
-        e0.record()
-        for i in range(n):
-            fn(i)
-        e1.record()
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - w0_
-        return e0.elapsed_time(e1) / n, wall / n * 1e3
-
-    def spread(fn, n, batches=20):
-        """Per-launch time in each of `batches` consecutive batches of back-to-back launches
-        (one event pair per batch, so no per-launch event overhead): p10, median, p90 (us)."""
-        per = max(1, n // batches)
-        for i in range(min(n, 50)):
-            fn(i)
-        evs = [torch.cuda.Event(enable_timing=True) for _ in range(batches + 1)]
-        torch.cuda.synchronize()
-        evs[0].record()
-        for b in range(batches):
-            for i in range(per):
-                fn(b * per + i)
-            evs[b + 1].record()
-        torch.cuda.synchronize()
-        d = sorted(evs[b].elapsed_time(evs[b + 1]) * 1e3 / per for b in range(batches))
-        return {"batches": batches, "launches_per_batch": per, "p10": round(d[batches // 10], 3),
-                "median": round(d[batches // 2], 3), "p90": round(d[(9 * batches) // 10], 3)}
-
-    def capture(fn, n):
-        """The same launches captured once into a HIP graph (replayed, they give the GPU time
-        per launch without the host's per-call overhead, as a decode loop replaying a graph
-        sees it)."""
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(side):
-            fn(0)
-        torch.cuda.current_stream().wait_stream(side)
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for i in range(n):
-                fn(i)
-        torch.cuda.synchronize()
-        return g
-
-    def replay_timed(g, n):
-        g.replay()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record()
-        g.replay()
-        e1.record()
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / n
 
     # The GPU's clocks dip for some 10-20 ms whenever work resumes after an idle stretch of a
     # few ms (launch durations rise by up to 20% and recover), so every host-side preparation

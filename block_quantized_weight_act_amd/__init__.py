@@ -23,6 +23,7 @@ __all__ = [
     "qgemv_workspace_bytes", "qgemv_q4k", "qgemv_q6k", "qgemv_batch", "qgemv_debug_partials",
     "qgemv_quantize_weights", "qgemv_plan_for", "qgemv_plan_workspace_bytes", "qgemv_batch_plan",
     "qgemv_read_probe", "qgemv_fused", "qgemv_quantize_weights_rows", "qgemv_fused_launches",
+    "qgemv_multi", "qgemv_multi_fused", "qgemv_multi_geometry",
 ]
 
 QGEMV_Q4K = 1
@@ -51,6 +52,14 @@ class Plan(ctypes.Structure):
         return {name: int(getattr(self, name)) for name, _ in self._fields_}
 
 
+class Matrix(ctypes.Structure):
+    """One matrix of qgemv_multi / qgemv_multi_fused (the ABI's qgemv_matrix)."""
+    _fields_ = [("wtype", ctypes.c_int32), ("reserved", ctypes.c_int32), ("rows", ctypes.c_int64),
+                ("w", ctypes.c_void_p), ("y", ctypes.c_void_p)]
+
+
+MAX_MATRICES = 8
+
 _lib = None
 
 
@@ -76,6 +85,10 @@ def _load():
         "qgemv_quantize_weights": (ctypes.c_int, [ctypes.c_int, vp, vp, i64, i64, vp]),
         "qgemv_quantize_weights_rows": (ctypes.c_int, [ctypes.c_int, vp, vp, i64, i64, i64, i64, vp]),
         "qgemv_fused_launches": (ctypes.c_int, [ctypes.c_int, i64, i64, i32, ctypes.c_int]),
+        "qgemv_multi": (ctypes.c_int, [ctypes.POINTER(Matrix), i32, vp, vp, i64, i32, vp]),
+        "qgemv_multi_geometry": (ctypes.c_int, [i64, i32, ctypes.POINTER(ctypes.c_int32),
+                                                ctypes.POINTER(ctypes.c_int32)]),
+        "qgemv_multi_fused": (ctypes.c_int, [ctypes.POINTER(Matrix), i32, vp, vp, vp, i64, i32, vp]),
         "qgemv_plan_for": (ctypes.c_int, [ctypes.c_int, i64, i64, i32, ctypes.POINTER(Plan)]),
         "qgemv_plan_workspace_bytes": (sz, [ctypes.POINTER(Plan), i64, i64, i32]),
         "qgemv_batch_plan": (ctypes.c_int, [ctypes.c_int, vp, vp, vp, vp, i64, i64, i32,
@@ -220,6 +233,40 @@ def qgemv_fused(wtype, w, x, y, rows: int, cols: int, nvec: int, xq_out=None, xd
         _wtype(wtype), _ptr(w, name="w"), _ptr(x, torch.float32, "x"),
         _ptr(xq_out, torch.int8, "xq_out"), _ptr(xd_out, torch.float32, "xd_out"),
         _ptr(y, torch.float32, "y"), rows, cols, nvec, wsp, wsb, _stream(stream, y)))
+
+
+def _matrices(mats):
+    """[(wtype, w, rows, y), ...] -> a ctypes array of Matrix."""
+    arr = (Matrix * max(1, len(mats)))()
+    for i, (wtype, w, rows, y) in enumerate(mats):
+        arr[i] = Matrix(_wtype(wtype), 0, rows, _ptr(w, name="w"), _ptr(y, torch.float32, "y"))
+    return arr
+
+
+def qgemv_multi_geometry(cols: int, nvec: int = 1) -> tuple:
+    """(lanes_per_row, chunks_per_lane) of a multi-matrix launch for this row width."""
+    t, nc = ctypes.c_int32(), ctypes.c_int32()
+    _check("qgemv_multi_geometry", _load().qgemv_multi_geometry(cols, nvec, ctypes.byref(t),
+                                                               ctypes.byref(nc)))
+    return t.value, nc.value
+
+
+def qgemv_multi(mats, xq, xd, cols: int, nvec: int = 1, stream=None) -> None:
+    """y_m = W_m x for every (wtype, w, rows, y) in mats, one launch, from codes and scales."""
+    lib = _load()
+    _check("qgemv_multi", lib.qgemv_multi(
+        _matrices(mats), len(mats), _ptr(xq, torch.int8, "xq"), _ptr(xd, torch.float32, "xd"),
+        cols, nvec, _stream(stream, xq)))
+
+
+def qgemv_multi_fused(mats, x, cols: int, nvec: int = 1, xq_out=None, xd_out=None,
+                      stream=None) -> None:
+    """The same from the float32 activation, quantized inside."""
+    lib = _load()
+    _check("qgemv_multi_fused", lib.qgemv_multi_fused(
+        _matrices(mats), len(mats), _ptr(x, torch.float32, "x"),
+        _ptr(xq_out, torch.int8, "xq_out"), _ptr(xd_out, torch.float32, "xd_out"), cols, nvec,
+        _stream(stream, x)))
 
 
 def qgemv_debug_partials(wtype, w, xq, xd, P, S, rows: int, cols: int, nvec: int = 1,

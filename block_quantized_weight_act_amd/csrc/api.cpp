@@ -66,15 +66,18 @@ int64_t target_waves(int32_t nvec) { return nvec <= 2 ? 256 * 64 : 256 * 16; }
 // (more 16-byte loads in flight per lane) while the activation slice fits in VGPRs
 // (nvec * NC <= 8). When a row has more than 256 chunks (cols > 8192) or rows alone are too
 // few to give every CU work, the columns are split.
-qgemv_plan make_plan(int wtype, int64_t rows, int64_t cols, int32_t nvec) {
+// Lanes per row and chunks per lane for a row of `cols` columns (see make_plan). With
+// one_pass set, only geometries that cover the whole row in one pass; false if there is none.
+bool choose_geometry(int64_t cols, int32_t nvec, bool one_pass, int &best_t, int &best_nc) {
     const int64_t nchunks = cols / 32;
-    int best_t = 64, best_nc = 1;
+    bool found = false;
     double best_cost = 1e30;
     for (int nc = 1; nc <= 4; nc++) {
         if (nvec * nc > 8) break;
         for (int t : {8, 16, 32, 64}) {
             const int64_t per = static_cast<int64_t>(t) * nc;
             const int64_t passes = (nchunks + per - 1) / per;
+            if (one_pass && passes > 1) continue;
             const double waste = 1.0 - static_cast<double>(nchunks) / (passes * per);
             // idle lanes cost bandwidth in flight; split passes cost a workspace round trip
             const double cost = waste + 0.02 * (passes - 1) - 0.01 * nc;
@@ -82,9 +85,16 @@ qgemv_plan make_plan(int wtype, int64_t rows, int64_t cols, int32_t nvec) {
                 best_cost = cost;
                 best_t = t;
                 best_nc = nc;
+                found = true;
             }
         }
     }
+    return found;
+}
+
+qgemv_plan make_plan(int wtype, int64_t rows, int64_t cols, int32_t nvec) {
+    int best_t = 64, best_nc = 1;
+    choose_geometry(cols, nvec, false, best_t, best_nc);
     qgemv_plan p{};
     p.lanes_per_row = best_t;
     p.chunks_per_lane = best_nc;
@@ -225,6 +235,102 @@ int run_gemv(int wtype, const void *w, const Activation &act, float *y, int64_t 
     return QGEMV_OK;
 }
 
+// Several matrices with one activation (plain: act.xq / act.xd; fused: act.x and optionally
+// act.xq_out / act.xd_out): every check, then the launch description in a and s.
+int prepare_multi(const qgemv_matrix *mats, int32_t nmats, const Activation &act, int64_t cols,
+                  int32_t nvec, MultiArgs &a, LaunchShape &s, double &wbytes) {
+    if (!mats || nmats < 1 || nmats > kMaxMats || !shape_ok(1, cols, nvec)) return QGEMV_EINVAL;
+    int t = 0, nc = 0;
+    if (!choose_geometry(cols, nvec, true, t, nc)) return QGEMV_EINVAL;
+    const size_t qb = static_cast<size_t>(nvec) * cols;
+    const size_t db = static_cast<size_t>(nvec) * (cols / 32) * sizeof(float);
+    const size_t xb = qb * sizeof(float);
+    // the activation buffers (the fused form's are written, so they must not overlap)
+    struct Buf {
+        const void *p;
+        size_t n;
+    };
+    Buf acts[3];
+    int nacts = 0;
+    if (act.x) {
+        if ((act.xq_out == nullptr) != (act.xd_out == nullptr)) return QGEMV_EINVAL;
+        if (!aligned(act.x, 16)) return QGEMV_EALIGN;
+        acts[nacts++] = {act.x, xb};
+        if (act.xq_out) {
+            if (!aligned(act.xq_out, 4) || !aligned(act.xd_out, 4)) return QGEMV_EALIGN;
+            acts[nacts++] = {act.xq_out, qb};
+            acts[nacts++] = {act.xd_out, db};
+        }
+        for (int i = 0; i < nacts; i++)
+            for (int k = i + 1; k < nacts; k++)
+                if (overlaps(acts[i].p, acts[i].n, acts[k].p, acts[k].n)) return QGEMV_EINVAL;
+    } else {
+        if (!act.xq || !act.xd) return QGEMV_EINVAL;
+        if (!aligned(act.xq, 16) || !aligned(act.xd, 4)) return QGEMV_EALIGN;
+        acts[nacts++] = {act.xq, qb};
+        acts[nacts++] = {act.xd, db};
+    }
+    for (int i = 0; i < nmats; i++) {
+        const qgemv_matrix &m = mats[i];
+        if ((m.wtype != QGEMV_Q4K && m.wtype != QGEMV_Q6K) || m.reserved != 0 || !m.w || !m.y ||
+            !shape_ok(m.rows, cols, nvec))
+            return QGEMV_EINVAL;
+        if (!aligned(m.w, 16) || !aligned(m.y, 4)) return QGEMV_EALIGN;
+    }
+    // each output overlaps no weights, no activation buffer and no other output; the fused
+    // form's code outputs overlap no weights
+    wbytes = 0;
+    for (int i = 0; i < nmats; i++) {
+        const size_t yb = static_cast<size_t>(nvec) * mats[i].rows * sizeof(float);
+        const size_t wb = weight_bytes(mats[i].wtype, mats[i].rows, cols);
+        wbytes += static_cast<double>(wb);
+        for (int k = 0; k < nmats; k++) {
+            if (overlaps(mats[i].y, yb, mats[k].w, weight_bytes(mats[k].wtype, mats[k].rows, cols)))
+                return QGEMV_EINVAL;
+            if (k != i && overlaps(mats[i].y, yb, mats[k].y,
+                                   static_cast<size_t>(nvec) * mats[k].rows * sizeof(float)))
+                return QGEMV_EINVAL;
+        }
+        for (int k = 0; k < nacts; k++) {
+            if (overlaps(mats[i].y, yb, acts[k].p, acts[k].n)) return QGEMV_EINVAL;
+            if (act.x && k > 0 && overlaps(acts[k].p, acts[k].n, mats[i].w, wb)) return QGEMV_EINVAL;
+        }
+    }
+    // the step numbering and the grid
+    const int rpw = 64 / t, g = groups_per_step(nc);
+    a = MultiArgs{};
+    a.act.xq = act.xq;
+    a.act.xd = act.xd;
+    a.act.x = act.x;
+    a.act.xq_out = act.xq_out;
+    a.act.xd_out = act.xd_out;
+    a.act.nb = static_cast<int32_t>(cols / kQK);
+    a.act.nchunks = static_cast<int32_t>(cols / 32);
+    int64_t steps = 0;
+    for (int i = 0; i < nmats; i++) {
+        MatDesc &d = a.m[i];
+        d.w = static_cast<const uint8_t *>(mats[i].w);
+        d.out = mats[i].y;
+        d.rows = static_cast<int32_t>(mats[i].rows);
+        d.nb = static_cast<int32_t>(cols / kQK);
+        d.wtype = mats[i].wtype;
+        d.step0 = static_cast<int32_t>(steps);
+        steps += ((mats[i].rows + rpw - 1) / rpw + g - 1) / g;
+        if (steps >= (int64_t{1} << 30)) return QGEMV_EINVAL;
+    }
+    a.nmats = nmats;
+    a.steps = static_cast<int32_t>(steps);
+    const int waves = 4;
+    const int64_t want = std::min<int64_t>(steps, target_waves(nvec));
+    s = LaunchShape{t, nc, waves, static_cast<int>((want + waves - 1) / waves), 1};
+    return QGEMV_OK;
+}
+
+int launch_multi(const MultiArgs &a, const LaunchShape &s, int32_t nvec, hipStream_t stream) {
+    const hipError_t e = launch_gemv_multi(a, s, nvec, stream);
+    return e == hipSuccess ? QGEMV_OK : hip_fail(e);
+}
+
 }  // namespace
 
 extern "C" {
@@ -326,7 +432,8 @@ int qgemv_fused(int wtype, const void *w, const float *x, int8_t *xq_out, float 
     act.x = x;
     act.xq_out = xq_out;
     act.xd_out = xd_out;
-    if (xq_out && xd_out && qgemv_fused_launches(wtype, rows, cols, nvec, 1) == 2) {
+    if (xq_out && xd_out && aligned(xq_out, 16) &&
+        qgemv_fused_launches(wtype, rows, cols, nvec, 1) == 2) {
         int st = check_fused_act(act, w, weight_bytes(wtype, rows, cols), y,
                                  static_cast<size_t>(nvec) * rows * sizeof(float), cols, nvec);
         if (st != QGEMV_OK) return st;
@@ -338,6 +445,57 @@ int qgemv_fused(int wtype, const void *w, const float *x, int8_t *xq_out, float 
         return run_gemv(wtype, w, q, y, rows, cols, nvec, plan, workspace, workspace_bytes, stream);
     }
     return run_gemv(wtype, w, act, y, rows, cols, nvec, plan, workspace, workspace_bytes, stream);
+}
+
+int qgemv_multi_geometry(int64_t cols, int32_t nvec, int32_t *lanes_per_row,
+                         int32_t *chunks_per_lane) {
+    int t = 0, nc = 0;
+    if (!lanes_per_row || !chunks_per_lane || !shape_ok(1, cols, nvec) ||
+        !choose_geometry(cols, nvec, true, t, nc))
+        return QGEMV_EINVAL;
+    *lanes_per_row = t;
+    *chunks_per_lane = nc;
+    return QGEMV_OK;
+}
+
+int qgemv_multi(const qgemv_matrix *mats, int32_t nmats, const int8_t *xq, const float *xd,
+                int64_t cols, int32_t nvec, hipStream_t stream) {
+    Activation act;
+    act.xq = xq;
+    act.xd = xd;
+    MultiArgs a;
+    LaunchShape s;
+    double wbytes = 0;
+    const int st = prepare_multi(mats, nmats, act, cols, nvec, a, s, wbytes);
+    return st != QGEMV_OK ? st : launch_multi(a, s, nvec, stream);
+}
+
+int qgemv_multi_fused(const qgemv_matrix *mats, int32_t nmats, const float *x, int8_t *xq_out,
+                      float *xd_out, int64_t cols, int32_t nvec, hipStream_t stream) {
+    if (!x) return QGEMV_EINVAL;
+    Activation act;
+    act.x = x;
+    act.xq_out = xq_out;
+    act.xd_out = xd_out;
+    MultiArgs a;
+    LaunchShape s;
+    double wbytes = 0;
+    int st = prepare_multi(mats, nmats, act, cols, nvec, a, s, wbytes);
+    if (st != QGEMV_OK) return st;
+    // As for one matrix: with code outputs (16-byte aligned, as the product reads them) and a
+    // slice that is large next to a workgroup's share of the weights, quantize once and run
+    // the product from the codes.
+    const double slice = static_cast<double>(nvec) * s.lanes * s.chunks * 32;
+    if (xq_out && aligned(xq_out, 16) && slice > 0.15 * wbytes / s.blocks) {
+        st = qgemv_quantize_act(x, xq_out, xd_out, cols, nvec, stream);
+        if (st != QGEMV_OK) return st;
+        a.act.x = nullptr;
+        a.act.xq_out = nullptr;
+        a.act.xd_out = nullptr;
+        a.act.xq = xq_out;
+        a.act.xd = xd_out;
+    }
+    return launch_multi(a, s, nvec, stream);
 }
 
 int qgemv_q4k(const void *w, const int8_t *xq, const float *xd, float *y, int64_t rows,

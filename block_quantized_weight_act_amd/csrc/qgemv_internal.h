@@ -42,6 +42,25 @@ struct GemvArgs {
 // itself (GemvArgs::x).
 enum KernelMode : int { kModePlain = 0, kModeDebug = 1, kModeFused = 2 };
 
+// Several matrices sharing one activation in one launch (gemv_multi.hip).
+constexpr int kMaxMats = 8;
+constexpr int kTypeQ4K = 1;        // the ABI's QGEMV_Q4K
+constexpr int kTypeQ6K = 2;        // the ABI's QGEMV_Q6K
+struct MatDesc {
+    const uint8_t *w;      // planar tensor of rows x cols
+    float *out;            // y of this matrix, [nvec][rows]
+    int32_t rows;
+    int32_t nb;            // super-blocks per row
+    int32_t wtype;         // kTypeQ4K or kTypeQ6K
+    int32_t step0;         // the matrix's first step in the launch's step numbering
+};
+struct MultiArgs {
+    GemvArgs act;          // the activation fields (xq, xd or x, xq_out, xd_out, nchunks)
+    int32_t nmats;
+    int32_t steps;         // steps of all matrices together
+    MatDesc m[kMaxMats];
+};
+
 struct LaunchShape {
     int lanes;             // lanes per row (T)
     int chunks;            // chunks per lane (NC)
@@ -57,6 +76,8 @@ hipError_t launch_gemv_q4k(const GemvArgs &a, const LaunchShape &s, int nvec, bo
                            hipStream_t stream);
 hipError_t launch_gemv_q6k(const GemvArgs &a, const LaunchShape &s, int nvec, bool debug,
                            hipStream_t stream);
+hipError_t launch_gemv_multi(const MultiArgs &a, const LaunchShape &s, int nvec,
+                             hipStream_t stream);
 hipError_t launch_splitk_reduce(const float *part, float *y, int64_t n, int splits,
                                 hipStream_t stream);
 // Rows [row0, row0 + nrows) of a rows x cols matrix (w points at row row0) into their places

@@ -171,8 +171,9 @@ int qgemv_batch(int wtype, const void *w, const int8_t *xq, const float *xd, flo
  * set; 4-byte aligned). x 16-byte aligned. Other arguments as for qgemv_batch.
  * Each workgroup repeats the quantization of the columns it reads; when that
  * is large next to its share of the weights (wide rows, several vectors) and
- * xq_out / xd_out are given, the library instead quantizes once into them and
- * runs the product from them (two launches, identical results).
+ * xq_out / xd_out are given (xq_out 16-byte aligned), the library instead
+ * quantizes once into them and runs the product from them (two launches,
+ * identical results).
  */
 int qgemv_fused(int wtype, const void *w, const float *x, int8_t *xq_out, float *xd_out, float *y,
                 int64_t rows, int64_t cols, int32_t nvec, void *workspace,
@@ -181,10 +182,58 @@ int qgemv_fused(int wtype, const void *w, const float *x, int8_t *xq_out, float 
 /*
  * How many kernel launches qgemv_fused makes for this shape: 1 (the one-launch
  * kernel) or 2 (qgemv_quantize_act, then the product); with_outputs says whether
- * xq_out / xd_out are given (without them it is always 1). 0 for an invalid
- * type or shape. Host only; no device work.
+ * xq_out / xd_out are given (without them it is always 1; with an xq_out that is
+ * not 16-byte aligned it is 1 as well). 0 for an invalid type or shape. Host
+ * only; no device work.
  */
 int qgemv_fused_launches(int wtype, int64_t rows, int64_t cols, int32_t nvec, int with_outputs);
+
+/*
+ * Several matrices that multiply the same activation, in one launch
+ * (genie-ai-runtime, "v1.2.0": the attention projections of a decode step share
+ * one quantized activation). Every matrix has `cols` columns; formats may be
+ * mixed. For each matrix m: y_m[v][r] = sum over columns of W_m[r][c] * x_v[c],
+ * computed exactly as qgemv_batch does for W_m alone with the same lanes per row
+ * and chunks per lane (so the integer partials are the same and y_m lies within
+ * the same bound).
+ *
+ * mats: HOST array of nmats (1..QGEMV_MAX_MATRICES) descriptors, read during the
+ * call only. Each: wtype QGEMV_Q4K or QGEMV_Q6K, reserved = 0, rows >= 1, w the
+ * device planar tensor (16-byte aligned), y device float32 [nvec][rows]
+ * (4-byte aligned; no y may overlap any weights, the activation or another y).
+ * The row is covered by one pass of lanes, so cols is at most 8192 for 1-2
+ * vectors, 4096 for 3-4 and 2048 for 5-8 (QGEMV_EINVAL beyond). No workspace.
+ */
+#define QGEMV_MAX_MATRICES 8
+typedef struct qgemv_matrix {
+    int32_t wtype;
+    int32_t reserved;
+    int64_t rows;
+    const void *w;
+    float *y;
+} qgemv_matrix;
+
+/* The lanes per row and chunks per lane a multi-matrix launch uses for this
+ * row width: the fewest idle lanes among the geometries that cover a row in one
+ * pass, more chunks per lane preferred. QGEMV_EINVAL when no geometry covers
+ * the row (cols too wide for nvec). Host only. */
+int qgemv_multi_geometry(int64_t cols, int32_t nvec, int32_t *lanes_per_row,
+                         int32_t *chunks_per_lane);
+
+/* The product from codes and scales made by qgemv_quantize_act (xq 16-byte,
+ * xd 4-byte aligned). */
+int qgemv_multi(const qgemv_matrix *mats, int32_t nmats, const int8_t *xq, const float *xd,
+                int64_t cols, int32_t nvec, hipStream_t stream);
+
+/* The same from the float32 activation x (16-byte aligned) with the quantization
+ * done inside, as qgemv_fused does for one matrix; xq_out / xd_out (both NULL or
+ * both set, 4-byte aligned, overlapping no input) optionally receive the codes
+ * and scales. With code outputs that are 16-byte aligned and an activation
+ * slice that is large next to a workgroup's share of the weights, the library
+ * quantizes once and runs qgemv_multi's kernel from them (two launches, the
+ * same results). */
+int qgemv_multi_fused(const qgemv_matrix *mats, int32_t nmats, const float *x, int8_t *xq_out,
+                      float *xd_out, int64_t cols, int32_t nvec, hipStream_t stream);
 
 /*
  * Test hook: the exact integer partials of the same kernels.

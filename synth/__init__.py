@@ -175,3 +175,40 @@ WORKLOADS = {
                                 outlier_frac=0.01, seed_rows=3003),
     "q4k_16384x2048_b8": Workload("q4k_16384x2048_b8", "q4k", 16384, 2048, 8, 1004, 2400),
 }
+
+
+@dataclasses.dataclass(frozen=True)
+class WorkloadGroup:
+    """Several weight matrices that multiply the same activation vectors (one multi-matrix
+    product). The parts share cols, nvec and the activation seed."""
+
+    name: str
+    parts: tuple
+
+    @property
+    def cols(self) -> int:
+        return self.parts[0].cols
+
+    @property
+    def nvec(self) -> int:
+        return self.parts[0].nvec
+
+    def activations(self) -> np.ndarray:
+        return self.parts[0].activations()
+
+
+def _group(name, cols, nvec, seed_x, parts):
+    return WorkloadGroup(name, tuple(Workload("%s.%s" % (name, p), wtype, rows, cols, nvec, seed_w,
+                                              seed_x) for p, wtype, rows, seed_w in parts))
+
+
+# Multi-matrix workloads: shaped like one decoder layer's projections at width 1536 (the width
+# of the 262144 x 1536 projection above), weights N(0, 0.02), x N(0, 1). Weight seeds 1010+,
+# activation seeds 2500+.
+GROUPS = {
+    "qkv_1536": _group("qkv_1536", 1536, 1, 2500, [("q", "q4k", 2048, 1010),
+                                                   ("k", "q4k", 512, 1011),
+                                                   ("v", "q6k", 512, 1012)]),
+    "gate_up_1536": _group("gate_up_1536", 1536, 1, 2600, [("gate", "q4k", 6144, 1013),
+                                                           ("up", "q4k", 6144, 1014)]),
+}

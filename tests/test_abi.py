@@ -129,3 +129,67 @@ def test_fused_rejects_bad_arguments():
     assert lib.qgemv_fused(1, A, X, Q, D, X + 64, 8, 256, 1, None, 0, None) == EINVAL  # y over x
     assert lib.qgemv_fused(1, A, X, X + 16, D, Y, 8, 256, 1, None, 0, None) == EINVAL  # codes over x
     assert lib.qgemv_fused(3, A, X, None, None, Y, 8, 256, 1, None, 0, None) == EINVAL
+
+
+def _mats(*specs):
+    """ctypes array from (wtype, rows, w, y, reserved) tuples."""
+    arr = (qg.Matrix * max(1, len(specs)))()
+    for i, (t, rows, w, y, *rest) in enumerate(specs):
+        arr[i] = qg.Matrix(t, rest[0] if rest else 0, rows, w, y)
+    return arr
+
+
+def test_multi_rejects_bad_arguments():
+    lib = qg._load()
+    XQ, XD = A + (1 << 30), A + (2 << 30)
+    W1, W2, Y1, Y2 = A + (3 << 30), A + (4 << 30), A + (5 << 30), A + (6 << 30)
+    good = [(1, 64, W1, Y1), (2, 32, W2, Y2)]
+
+    def call(specs, n=None, cols=1536, nvec=1, xq=XQ, xd=XD):
+        return lib.qgemv_multi(_mats(*specs), len(specs) if n is None else n, xq, xd, cols, nvec,
+                               None)
+
+    assert call(good, n=0) == EINVAL
+    assert call(good * 5, n=9) == EINVAL                            # more than 8 matrices
+    assert lib.qgemv_multi(None, 1, XQ, XD, 1536, 1, None) == EINVAL
+    assert call([(3, 64, W1, Y1)]) == EINVAL                        # weight type
+    assert call([(1, 64, W1, Y1, 1)]) == EINVAL                     # reserved field set
+    assert call([(1, 0, W1, Y1)]) == EINVAL                         # no rows
+    assert call([(1, 64, None, Y1)]) == EINVAL
+    assert call([(1, 64, W1, None)]) == EINVAL
+    assert call(good, cols=1000) == EINVAL
+    assert call(good, cols=8448) == EINVAL                          # wider than one pass
+    assert call(good, cols=8192, nvec=3) == EINVAL                  # 3-4 vectors: <= 4096
+    assert call(good, cols=4096, nvec=5) == EINVAL                  # 5-8 vectors: <= 2048
+    assert call(good, xq=None) == EINVAL
+    assert call(good, xq=XQ + 4) == EALIGN
+    assert call([(1, 64, W1 + 8, Y1)]) == EALIGN
+    assert call([(1, 64, W1, Y1 + 2)]) == EALIGN
+    assert call([(1, 64, W1, W1 + 64)]) == EINVAL                   # y over the weights
+    assert call([(1, 64, W1, Y1), (2, 32, W2, W1 + 256)]) == EINVAL # y over another's weights
+    assert call([(1, 64, W1, Y1), (2, 32, W2, Y1 + 64)]) == EINVAL  # two outputs overlap
+    assert call([(1, 64, W1, XQ + 64)]) == EINVAL                   # y over the codes
+    # the fused form
+    X, Q, D = A + (7 << 30), A + (8 << 30), A + (9 << 30)
+    f = lib.qgemv_multi_fused
+    assert f(_mats(*good), 2, None, None, None, 1536, 1, None) == EINVAL
+    assert f(_mats(*good), 2, X + 4, None, None, 1536, 1, None) == EALIGN
+    assert f(_mats(*good), 2, X, Q, None, 1536, 1, None) == EINVAL      # half the outputs
+    assert f(_mats(*good), 2, X, Q + 2, D, 1536, 1, None) == EALIGN
+    assert f(_mats(*good), 2, X, X + 16, D, 1536, 1, None) == EINVAL    # codes over x
+    assert f(_mats(*good), 2, X, W1 + 16, D, 1536, 1, None) == EINVAL   # codes over weights
+    assert f(_mats((1, 64, W1, X + 64)), 1, X, None, None, 1536, 1, None) == EINVAL  # y over x
+
+
+def test_multi_geometry():
+    """One pass over the row, fewest idle lanes, more chunks per lane preferred."""
+    assert qg.qgemv_multi_geometry(1536, 1) == (16, 3)
+    assert qg.qgemv_multi_geometry(8192, 1) == (64, 4)
+    assert qg.qgemv_multi_geometry(2048, 8) == (64, 1)
+    assert qg.qgemv_multi_geometry(256, 1) == (8, 1)
+    assert qg.qgemv_multi_geometry(4096, 3) == (64, 2)
+    lib = qg._load()
+    t, nc = ctypes.c_int32(), ctypes.c_int32()
+    assert lib.qgemv_multi_geometry(8448, 1, ctypes.byref(t), ctypes.byref(nc)) == EINVAL
+    assert lib.qgemv_multi_geometry(4096, 5, ctypes.byref(t), ctypes.byref(nc)) == EINVAL
+    assert lib.qgemv_multi_geometry(1536, 1, None, ctypes.byref(nc)) == EINVAL
