@@ -13,6 +13,10 @@ Byte layouts (restated in the C file). N = rows * cols/256 super-blocks, block i
                  one block's "image" is its 16 header bytes followed by its 128 code bytes.
   Q6_K tensor  = low-bit plane (128), high-bit plane (64), scale plane (16), d plane (2 bytes
                  per block); one block's "body" is its low bits, high bits and scales (208 bytes).
+  Q4_0 tensor  = codes plane (16 bytes per 32-weight block) then fp16 scale plane (2 bytes);
+                 one block's "image" is its fp16 d followed by its 16 code bytes.
+  Q8_0 tensor  = codes plane (32 int8 per block) then float32 scale plane (4 bytes); the
+                 image is d followed by the 32 codes.
   activations  = int8 codes [nvec][cols] and float32 scales [nvec][cols/32].
 """
 
@@ -33,6 +37,10 @@ Q4K_BYTES = 144
 Q6K_BODY = 208
 Q6K_BYTES = 210
 QK = 256
+QB = 32              # weights per Q4_0 / Q8_0 block
+Q40_BYTES = 18
+Q80_BYTES = 36
+WTYPES = ("q4k", "q6k", "q40", "q80")
 
 CFLAGS = ["-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off", "-fno-fast-math",
           "-Wall", "-Wextra"]
@@ -91,6 +99,20 @@ def load(path: str | None = None):
             "orc_q6k_get_block": (None, [u8p, i64, i64, u8p, u16p]),
             "orc_q6k_put_block": (None, [u8p, i64, i64, u8p, ctypes.c_uint16]),
             "orc_bruteforce": (None, [f64p, i64, i64, i32, i8p, f32p, f64p]),
+            "orc_q40_pack_block": (None, [ctypes.c_uint16, u8p, u8p]),
+            "orc_q40_unpack_block": (None, [u8p, u16p, u8p]),
+            "orc_q80_pack_block": (None, [ctypes.c_float, i8p, u8p]),
+            "orc_q80_unpack_block": (None, [u8p, f32p, i8p]),
+            "orc_q40_get_block": (None, [u8p, i64, i64, u8p]),
+            "orc_q40_put_block": (None, [u8p, i64, i64, u8p]),
+            "orc_q80_get_block": (None, [u8p, i64, i64, u8p]),
+            "orc_q80_put_block": (None, [u8p, i64, i64, u8p]),
+            "orc_quantize_q40": (None, [f32p, i64, i64, u8p]),
+            "orc_quantize_q80": (None, [f32p, i64, i64, u8p]),
+            "orc_dequant_q40": (None, [u8p, i64, i64, f64p]),
+            "orc_dequant_q80": (None, [u8p, i64, i64, f64p]),
+            "orc_gemv_q40": (None, [u8p, i64, i64, i32, i8p, f32p, i32p, f64p, f64p]),
+            "orc_gemv_q80": (None, [u8p, i64, i64, i32, i8p, f32p, i32p, f64p, f64p]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(lib, name)
@@ -179,7 +201,72 @@ def q6k_unpack_block(body, lib=None):
 
 
 def tensor_bytes(wtype: str, rows: int, cols: int) -> int:
+    if wtype in ("q40", "q80"):
+        return rows * (cols // QB) * (Q40_BYTES if wtype == "q40" else Q80_BYTES)
     return rows * (cols // QK) * (Q4K_BYTES if wtype == "q4k" else Q6K_BYTES)
+
+
+def q40_pack_block(d16: int, q, lib=None) -> np.ndarray:
+    """18-byte Q4_0 image from fp16 bits of d and 32 codes in [0, 15]."""
+    lib = lib or load()
+    q = np.ascontiguousarray(q, dtype=np.uint8)
+    out = np.empty(Q40_BYTES, dtype=np.uint8)
+    lib.orc_q40_pack_block(int(d16), _p(q, ctypes.c_uint8), _p(out, ctypes.c_uint8))
+    return out
+
+
+def q40_unpack_block(img, lib=None):
+    """-> (fp16 bits of d, q uint8[32])"""
+    lib = lib or load()
+    img = np.ascontiguousarray(img, dtype=np.uint8)
+    d = np.zeros(1, np.uint16)
+    q = np.zeros(QB, np.uint8)
+    lib.orc_q40_unpack_block(_p(img, ctypes.c_uint8), _p(d, ctypes.c_uint16), _p(q, ctypes.c_uint8))
+    return int(d[0]), q
+
+
+def q80_pack_block(d: float, q, lib=None) -> np.ndarray:
+    """36-byte Q8_0 image from a float32 d and 32 int8 codes."""
+    lib = lib or load()
+    q = np.ascontiguousarray(q, dtype=np.int8)
+    out = np.empty(Q80_BYTES, dtype=np.uint8)
+    lib.orc_q80_pack_block(float(d), _p(q, ctypes.c_int8), _p(out, ctypes.c_uint8))
+    return out
+
+
+def q80_unpack_block(img, lib=None):
+    """-> (d float32, q int8[32])"""
+    lib = lib or load()
+    img = np.ascontiguousarray(img, dtype=np.uint8)
+    d = np.zeros(1, np.float32)
+    q = np.zeros(QB, np.int8)
+    lib.orc_q80_unpack_block(_p(img, ctypes.c_uint8), _p(d, ctypes.c_float), _p(q, ctypes.c_int8))
+    return np.float32(d[0]), q
+
+
+def q32_get_block(wtype: str, buf, nblocks: int, i: int, lib=None) -> np.ndarray:
+    """The image of block i of a Q4_0 / Q8_0 tensor of nblocks blocks."""
+    lib = lib or load()
+    buf = np.ascontiguousarray(buf, dtype=np.uint8)
+    size = Q40_BYTES if wtype == "q40" else Q80_BYTES
+    assert buf.size == nblocks * size
+    img = np.empty(size, dtype=np.uint8)
+    fn = lib.orc_q40_get_block if wtype == "q40" else lib.orc_q80_get_block
+    fn(_p(buf, ctypes.c_uint8), nblocks, i, _p(img, ctypes.c_uint8))
+    return img
+
+
+def q32_tensor(wtype: str, images, lib=None) -> np.ndarray:
+    """A Q4_0 / Q8_0 tensor from a list of block images (block i = images[i])."""
+    lib = lib or load()
+    n = len(images)
+    size = Q40_BYTES if wtype == "q40" else Q80_BYTES
+    out = np.zeros(n * size, dtype=np.uint8)
+    fn = lib.orc_q40_put_block if wtype == "q40" else lib.orc_q80_put_block
+    for i, img in enumerate(images):
+        img = np.ascontiguousarray(img, dtype=np.uint8)
+        fn(_p(out, ctypes.c_uint8), n, i, _p(img, ctypes.c_uint8))
+    return out
 
 
 def q4k_get_block(buf, nblocks: int, i: int, lib=None) -> np.ndarray:
@@ -246,6 +333,32 @@ def quantize_q4k(w, lib=None) -> np.ndarray:
     return out
 
 
+def quantize_q40(w, lib=None) -> np.ndarray:
+    """w float32 [rows][cols] -> Q4_0 tensor, uint8 [rows * cols/32 * 18] (two planes)."""
+    lib = lib or load()
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    rows, cols = w.shape
+    out = np.empty(rows * (cols // QB) * Q40_BYTES, dtype=np.uint8)
+    lib.orc_quantize_q40(_p(w, ctypes.c_float), rows, cols, _p(out, ctypes.c_uint8))
+    return out
+
+
+def quantize_q80(w, lib=None) -> np.ndarray:
+    """w float32 [rows][cols] -> Q8_0 tensor, uint8 [rows * cols/32 * 36] (two planes)."""
+    lib = lib or load()
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    rows, cols = w.shape
+    out = np.empty(rows * (cols // QB) * Q80_BYTES, dtype=np.uint8)
+    lib.orc_quantize_q80(_p(w, ctypes.c_float), rows, cols, _p(out, ctypes.c_uint8))
+    return out
+
+
+def quantize(wtype: str, w, lib=None) -> np.ndarray:
+    """Any of the four formats (Q6_K with its plain encoding)."""
+    return {"q4k": quantize_q4k, "q6k": quantize_q6k, "q40": quantize_q40,
+            "q80": quantize_q80}[wtype](w, lib=lib)
+
+
 def quantize_q6k(w, negate_scales: bool = False, lib=None) -> np.ndarray:
     """w float32 [rows][cols] -> Q6_K tensor, uint8 [rows * cols/256 * 210] (four planes)."""
     lib = lib or load()
@@ -264,7 +377,8 @@ def dequantize(wtype: str, wbuf, rows: int, cols: int, lib=None) -> np.ndarray:
     wbuf = np.ascontiguousarray(wbuf, dtype=np.uint8).reshape(-1)
     if wbuf.size != tensor_bytes(wtype, rows, cols):
         raise ValueError("tensor has %d bytes, expected %d" % (wbuf.size, tensor_bytes(wtype, rows, cols)))
-    fn = lib.orc_dequant_q4k if wtype == "q4k" else lib.orc_dequant_q6k
+    fn = {"q4k": lib.orc_dequant_q4k, "q6k": lib.orc_dequant_q6k, "q40": lib.orc_dequant_q40,
+          "q80": lib.orc_dequant_q80}[wtype]
     fn(_p(wbuf, ctypes.c_uint8), rows, cols, _p(out, ctypes.c_double))
     return out
 
@@ -273,8 +387,8 @@ def dequantize(wtype: str, wbuf, rows: int, cols: int, lib=None) -> np.ndarray:
 def gemv(wtype: str, wbuf, rows: int, cols: int, xq, xd, partials: bool = False,
          bound: bool = True, lib=None) -> dict:
     """Integer-formulated GEMV. Returns y [nvec][rows] (float64), bound, and optionally
-    the exact partials P (Q4_K [nvec][rows][cols/32], Q6_K [nvec][rows][cols/16]) and
-    S [nvec][cols/32] (Q4_K only)."""
+    the exact partials P (Q4_K, Q4_0, Q8_0 [nvec][rows][cols/32], Q6_K [nvec][rows][cols/16])
+    and S [nvec][cols/32] (Q4_K only)."""
     lib = lib or load()
     xq = np.ascontiguousarray(np.atleast_2d(xq), dtype=np.int8)
     xd = np.ascontiguousarray(np.atleast_2d(xd), dtype=np.float32)
@@ -300,6 +414,14 @@ def gemv(wtype: str, wbuf, rows: int, cols: int, xq, xd, partials: bool = False,
         lib.orc_gemv_q6k(_p(wbuf, ctypes.c_uint8), rows, cols, nvec, _p(xq, ctypes.c_int8),
                          _p(xd, ctypes.c_float), _p(P, ctypes.c_int32), _p(y, ctypes.c_double),
                          _p(bnd, ctypes.c_double))
+        if partials:
+            out["P"] = P
+    elif wtype in ("q40", "q80"):
+        P = np.empty((nvec, rows, cols // 32), dtype=np.int32) if partials else None
+        fn = lib.orc_gemv_q40 if wtype == "q40" else lib.orc_gemv_q80
+        fn(_p(wbuf, ctypes.c_uint8), rows, cols, nvec, _p(xq, ctypes.c_int8),
+           _p(xd, ctypes.c_float), _p(P, ctypes.c_int32), _p(y, ctypes.c_double),
+           _p(bnd, ctypes.c_double))
         if partials:
             out["P"] = P
     else:
@@ -332,11 +454,11 @@ def bruteforce(what, xq, xd, lib=None) -> np.ndarray:
 
 def planes(wtype: str, wbuf, rows: int, cols: int) -> list:
     """The planes of a tensor as [rows][bytes per row] views (Q4_K: codes, headers; Q6_K: low
-    bits, high bits, scales, d)."""
-    nb = cols // QK
+    bits, high bits, scales, d; Q4_0 and Q8_0: codes, scales)."""
+    nb = cols // (QB if wtype in ("q40", "q80") else QK)
     n = rows * nb
     wbuf = np.ascontiguousarray(wbuf, dtype=np.uint8).reshape(-1)
-    widths = [128, 16] if wtype == "q4k" else [128, 64, 16, 2]
+    widths = {"q4k": [128, 16], "q6k": [128, 64, 16, 2], "q40": [16, 2], "q80": [32, 4]}[wtype]
     out, off = [], 0
     for wdt in widths:
         out.append(wbuf[off:off + n * wdt].reshape(rows, nb * wdt))

@@ -23,6 +23,10 @@
  *    int8 sub-scales, fp16 d, 6-bit codes with offset -32; activations to int8
  *    blocks of 32 with an fp32 scale; exact int32 sub-block dot products, then
  *    scaling and reduction in floating point.
+ *  - oxinfer README, "Build and run": --quant q4 is GGUF-style Q4_0 (blocks of
+ *    32 weights, 4-bit codes, one fp16 scale), --quant q8 is int8 weights in
+ *    blocks of 32 with one f32 scale; "Pre-quantized checkpoints": the codes
+ *    (two nibbles per byte for Q4_0) and the scales are separate tensors.
  *
  * The pages fix neither byte layouts nor rounding rules. The readings taken
  * here (byte layouts, quantizer steps, round-to-nearest-even everywhere) are
@@ -45,6 +49,7 @@
 #define Q4K_BYTES 144     /* bytes per Q4_K super-block */
 #define Q6K_BODY 208      /* bytes per Q6_K super-block body (the fp16 d lives in a separate plane) */
 #define ACT_BLOCK 32      /* activation elements per int8 block */
+#define QB 32             /* weights per Q4_0 / Q8_0 block */
 
 static void die(const char *what) {
     fprintf(stderr, "qgemv oracle: %s\n", what);
@@ -278,6 +283,94 @@ void orc_q6k_put_block(uint8_t *t, int64_t nblocks, int64_t i, const uint8_t *bo
     q6k_put(t, nblocks, i, body, d);
 }
 
+/* ------------------------------------------------ Q4_0 and Q8_0 layouts - */
+/* Q4_0: a block of 32 weights (weight t, t < 32) with one fp16 scale d and
+ * codes q_t in [0, 15]; dequantized weight d * (q_t - 8). Its 18-byte image:
+ *   image [0,2)   d (fp16, little-endian)
+ *   image [2,18)  codes: weight t is nibble (t >= 16 ? high : low) of byte
+ *                 2 + (t mod 16), i.e. weights t and t + 16 share a byte.
+ * A Q4_0 tensor of N = rows * cols/32 blocks (block i = r * cols/32 + b) keeps
+ * the codes of block i at 16 * i and its d at 16 * N + 2 * i.
+ *
+ * Q8_0: a block of 32 weights with one float32 scale d and int8 codes q_t;
+ * dequantized weight d * q_t. Its 36-byte image: d (float32, little-endian) at
+ * [0,4), then weight t's code at byte 4 + t. A Q8_0 tensor of N blocks keeps
+ * the codes of block i at 32 * i and its d at 32 * N + 4 * i.                 */
+#define Q40_BYTES 18
+#define Q80_BYTES 36
+
+static int q40_q(const uint8_t *img, int t) {
+    uint8_t byte = img[2 + t % 16];
+    return t < 16 ? (byte & 15) : (byte >> 4);
+}
+
+void orc_q40_pack_block(uint16_t d, const uint8_t *q, uint8_t *img) {
+    memset(img, 0, Q40_BYTES);
+    wr16(img, d);
+    for (int t = 0; t < QB; t++) {
+        if (q[t] > 15) die("Q4_0 code out of range");
+        img[2 + t % 16] |= (uint8_t)(t < 16 ? q[t] : q[t] << 4);
+    }
+}
+
+void orc_q40_unpack_block(const uint8_t *img, uint16_t *d, uint8_t *q) {
+    *d = rd16(img);
+    for (int t = 0; t < QB; t++) q[t] = (uint8_t)q40_q(img, t);
+}
+
+static float rdf32(const uint8_t *p) {
+    uint32_t u = (uint32_t)p[0] | ((uint32_t)p[1] << 8) | ((uint32_t)p[2] << 16) |
+                 ((uint32_t)p[3] << 24);
+    float f;
+    memcpy(&f, &u, 4);
+    return f;
+}
+
+static void wrf32(uint8_t *p, float f) {
+    uint32_t u = f32_bits(f);
+    for (int k = 0; k < 4; k++) p[k] = (uint8_t)(u >> (8 * k));
+}
+
+void orc_q80_pack_block(float d, const int8_t *q, uint8_t *img) {
+    wrf32(img, d);
+    for (int t = 0; t < QB; t++) img[4 + t] = (uint8_t)q[t];
+}
+
+void orc_q80_unpack_block(const uint8_t *img, float *d, int8_t *q) {
+    *d = rdf32(img);
+    for (int t = 0; t < QB; t++) q[t] = (int8_t)img[4 + t];
+}
+
+static void q40_get(const uint8_t *t, int64_t N, int64_t i, uint8_t *img) {
+    memcpy(img, t + 16 * N + 2 * i, 2);
+    memcpy(img + 2, t + 16 * i, 16);
+}
+static void q40_put(uint8_t *t, int64_t N, int64_t i, const uint8_t *img) {
+    memcpy(t + 16 * N + 2 * i, img, 2);
+    memcpy(t + 16 * i, img + 2, 16);
+}
+static void q80_get(const uint8_t *t, int64_t N, int64_t i, uint8_t *img) {
+    memcpy(img, t + 32 * N + 4 * i, 4);
+    memcpy(img + 4, t + 32 * i, 32);
+}
+static void q80_put(uint8_t *t, int64_t N, int64_t i, const uint8_t *img) {
+    memcpy(t + 32 * N + 4 * i, img, 4);
+    memcpy(t + 32 * i, img + 4, 32);
+}
+
+void orc_q40_get_block(const uint8_t *t, int64_t nblocks, int64_t i, uint8_t *img) {
+    q40_get(t, nblocks, i, img);
+}
+void orc_q40_put_block(uint8_t *t, int64_t nblocks, int64_t i, const uint8_t *img) {
+    q40_put(t, nblocks, i, img);
+}
+void orc_q80_get_block(const uint8_t *t, int64_t nblocks, int64_t i, uint8_t *img) {
+    q80_get(t, nblocks, i, img);
+}
+void orc_q80_put_block(uint8_t *t, int64_t nblocks, int64_t i, const uint8_t *img) {
+    q80_put(t, nblocks, i, img);
+}
+
 /* ------------------------------------------------------ weight quantizers - */
 /* Used to make test data; the GEMV never quantizes weights. Every decision
  * that yields an integer is taken in float32 with round-to-nearest-even.
@@ -382,6 +475,63 @@ void orc_quantize_q6k(const float *w, int64_t rows, int64_t cols, uint8_t *out,
     }
 }
 
+/* Q4_0, per block of 32 weights (GGUF-style: the largest-magnitude weight sets
+ * the scale, mapped to code 0):
+ *   m = the weight of largest |w| (the first one in index order on ties; +0
+ *       for an all-zero block)
+ *   d = fp16(m / -8)  (+0 when m = 0)
+ *   q_t = clamp(rint(w_t / d) + 8, 0, 15) with the stored d in float32
+ *         (8 when d = 0)
+ * so m itself is reproduced up to the rounding of d and the opposite extreme
+ * -m is clipped to 7/8 of its magnitude. */
+void orc_quantize_q40(const float *w, int64_t rows, int64_t cols, uint8_t *out) {
+    if (cols % QB) die("cols must be a multiple of 32");
+    int64_t nb = cols / QB;
+    uint8_t q[QB], img[Q40_BYTES];
+    for (int64_t r = 0; r < rows; r++) {
+        for (int64_t b = 0; b < nb; b++) {
+            const float *wb = w + r * cols + b * QB;
+            float m = 0.0f;
+            for (int t = 0; t < QB; t++) {
+                if (!isfinite(wb[t])) die("non-finite weight");
+                if (fabsf(wb[t]) > fabsf(m)) m = wb[t];
+            }
+            uint16_t dh = m != 0.0f ? orc_f32_to_f16(m / -8.0f) : 0;
+            float d = orc_f16_to_f32(dh);
+            if (!isfinite(d)) die("scale overflows fp16");
+            for (int t = 0; t < QB; t++)
+                q[t] = (uint8_t)(d != 0.0f ? clampf(rintf(wb[t] / d) + 8.0f, 0.0f, 15.0f) : 8.0f);
+            orc_q40_pack_block(dh, q, img);
+            q40_put(out, rows * nb, r * nb + b, img);
+        }
+    }
+}
+
+/* Q8_0, per block of 32 weights: the rule of the activation quantizer,
+ *   amax = max |w|, d = amax / 127, id = 127 / amax (0 when amax = 0),
+ *   q_t = clamp(rint(w_t * id), -127, 127). */
+void orc_quantize_q80(const float *w, int64_t rows, int64_t cols, uint8_t *out) {
+    if (cols % QB) die("cols must be a multiple of 32");
+    int64_t nb = cols / QB;
+    int8_t q[QB];
+    uint8_t img[Q80_BYTES];
+    for (int64_t r = 0; r < rows; r++) {
+        for (int64_t b = 0; b < nb; b++) {
+            const float *wb = w + r * cols + b * QB;
+            float amax = 0.0f;
+            for (int t = 0; t < QB; t++) {
+                if (!isfinite(wb[t])) die("non-finite weight");
+                if (fabsf(wb[t]) > amax) amax = fabsf(wb[t]);
+            }
+            float d = amax / 127.0f;
+            float id = amax > 0.0f ? 127.0f / amax : 0.0f;
+            for (int t = 0; t < QB; t++) q[t] = (int8_t)clampf(rintf(wb[t] * id), -127.0f, 127.0f);
+            orc_q80_pack_block(d, q, img);
+            q80_put(out, rows * nb, r * nb + b, img);
+        }
+    }
+}
+
 /* ------------------------------------------------------------ dequantize -- */
 void orc_dequant_q4k(const uint8_t *w, int64_t rows, int64_t cols, double *out) {
     int64_t nb = cols / QK;
@@ -407,6 +557,28 @@ void orc_dequant_q6k(const uint8_t *w, int64_t rows, int64_t cols, double *out) 
             double d = orc_f16_to_f32(dh);
             for (int i = 0; i < QK; i++)
                 out[r * cols + b * QK + i] = d * q6k_sc(body, i / 16) * (q6k_q(body, i) - 32);
+        }
+}
+
+void orc_dequant_q40(const uint8_t *w, int64_t rows, int64_t cols, double *out) {
+    int64_t nb = cols / QB;
+    uint8_t img[Q40_BYTES];
+    for (int64_t r = 0; r < rows; r++)
+        for (int64_t b = 0; b < nb; b++) {
+            q40_get(w, rows * nb, r * nb + b, img);
+            double d = orc_f16_to_f32(rd16(img));
+            for (int t = 0; t < QB; t++) out[r * cols + b * QB + t] = d * (q40_q(img, t) - 8);
+        }
+}
+
+void orc_dequant_q80(const uint8_t *w, int64_t rows, int64_t cols, double *out) {
+    int64_t nb = cols / QB;
+    uint8_t img[Q80_BYTES];
+    for (int64_t r = 0; r < rows; r++)
+        for (int64_t b = 0; b < nb; b++) {
+            q80_get(w, rows * nb, r * nb + b, img);
+            double d = rdf32(img);
+            for (int t = 0; t < QB; t++) out[r * cols + b * QB + t] = d * (int8_t)img[4 + t];
         }
 }
 
@@ -508,6 +680,58 @@ void orc_gemv_q6k(const uint8_t *w, int64_t rows, int64_t cols, int32_t nvec,
             if (bound) bound[(int64_t)v * rows + r] = bnd;
         }
     }
+}
+
+/* Q4_0 and Q8_0: for vector v, row r and block j (32 columns, the columns of
+ * activation block j):
+ *   P[v][r][j] = sum_t c_t * qx_t       (exact integer; c_t = q_t - 8 for Q4_0,
+ *                                         q_t for Q8_0)
+ *   y[v][r]    = sum_j xd_j * d_j * P   (float64)
+ * P is [nvec][rows][cols/32]; the other arrays as for Q4_K. */
+static void gemv_q32(int is_q8, const uint8_t *w, int64_t rows, int64_t cols, int32_t nvec,
+                     const int8_t *xq, const float *xd, int32_t *P, double *y, double *bound) {
+    if (cols % QB) die("cols must be a multiple of 32");
+    int64_t nb = cols / QB;
+    for (int32_t v = 0; v < nvec; v++) {
+        const int8_t *xv = xq + (int64_t)v * cols;
+        const float *dv = xd + (int64_t)v * nb;
+        for (int64_t r = 0; r < rows; r++) {
+            double acc = 0.0, bnd = 0.0;
+            for (int64_t j = 0; j < nb; j++) {
+                uint8_t img[Q80_BYTES];
+                double d;
+                int c[QB];
+                if (is_q8) {
+                    q80_get(w, rows * nb, r * nb + j, img);
+                    d = rdf32(img);
+                    for (int t = 0; t < QB; t++) c[t] = (int8_t)img[4 + t];
+                } else {
+                    q40_get(w, rows * nb, r * nb + j, img);
+                    d = orc_f16_to_f32(rd16(img));
+                    for (int t = 0; t < QB; t++) c[t] = q40_q(img, t) - 8;
+                }
+                int64_t p = 0;
+                for (int t = 0; t < QB; t++) p += (int64_t)c[t] * xv[QB * j + t];
+                double scale = dv[j];
+                acc += scale * d * (double)checked32(p);
+                if (P) P[((int64_t)v * rows + r) * nb + j] = (int32_t)p;
+                if (bound)
+                    for (int t = 0; t < QB; t++) bnd += fabs(d * c[t]) * fabs(scale * xv[QB * j + t]);
+            }
+            y[(int64_t)v * rows + r] = acc;
+            if (bound) bound[(int64_t)v * rows + r] = bnd;
+        }
+    }
+}
+
+void orc_gemv_q40(const uint8_t *w, int64_t rows, int64_t cols, int32_t nvec,
+                  const int8_t *xq, const float *xd, int32_t *P, double *y, double *bound) {
+    gemv_q32(0, w, rows, cols, nvec, xq, xd, P, y, bound);
+}
+
+void orc_gemv_q80(const uint8_t *w, int64_t rows, int64_t cols, int32_t nvec,
+                  const int8_t *xq, const float *xd, int32_t *P, double *y, double *bound) {
+    gemv_q32(1, w, rows, cols, nvec, xq, xd, P, y, bound);
 }
 
 /* -------------------------------------------------------------- brute force */

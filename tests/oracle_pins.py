@@ -155,20 +155,64 @@ def check_layout_goldens(lib):
 
 def check_layout_probes(lib):
     for fmt, byte, shift, width, name, idx, value in read_probes():
-        size = 144 if fmt == "q4k" else 208
+        size = {"q4k": 144, "q6k": 208, "q40": 18, "q80": 36}[fmt]
         blk = np.zeros(size, np.uint8)
         blk[byte] = ((1 << width) - 1) << shift
         if fmt == "q4k":
             _, _, sc, m, q = oracle.q4k_unpack_block(blk, lib=lib)
             fields = {"sc": sc.astype(int), "m": m.astype(int), "q": q.astype(int)}
-        else:
+        elif fmt == "q6k":
             sc, q = oracle.q6k_unpack_block(blk, lib=lib)
             fields = {"sc": sc.astype(int), "q": q.astype(int)}
+        elif fmt == "q40":
+            _, q = oracle.q40_unpack_block(blk, lib=lib)
+            fields = {"q": q.astype(int)}
+        else:
+            _, q = oracle.q80_unpack_block(blk, lib=lib)
+            fields = {"q": q.astype(int)}
         for fname, arr in fields.items():
             want = np.zeros_like(arr)
             if fname == name:
                 want[idx] = value
             assert np.array_equal(arr, want), (fmt, byte, shift, fname)
+
+
+def check_q32_layout_goldens(lib):
+    """Q4_0 / Q8_0 block images and the planar two-block tensors, against hand-derived bytes."""
+    t = np.arange(32)
+    p, img = read_hex_fixture("q40_block_a.txt")
+    assert img.size == 18
+    q = np.where(t < 16, t, 31 - t).astype(np.uint8)
+    assert np.array_equal(oracle.q40_pack_block(int(p["d16"], 16), q, lib=lib), img)
+    d16, gq = oracle.q40_unpack_block(img, lib=lib)
+    assert d16 == 0xB000 and np.array_equal(gq, q)
+    p80, img80 = read_hex_fixture("q80_block_a.txt")
+    assert img80.size == 36
+    q8 = (4 * t - 64).astype(np.int8)
+    assert np.array_equal(oracle.q80_pack_block(np.float32(0.5), q8, lib=lib), img80)
+    d8, gq8 = oracle.q80_unpack_block(img80, lib=lib)
+    assert d8 == np.float32(0.5) and np.array_equal(gq8, q8)
+    # the planar tensors of two blocks each
+    pt, data = read_hex_fixture("q32_tensors.txt")
+    n40 = int(pt["q40_bytes"])
+    want40, want80 = data[:n40], data[n40:]
+    img1 = oracle.q40_pack_block(0x3C00, np.full(32, 8, np.uint8), lib=lib)
+    t40 = oracle.q32_tensor("q40", [img, img1], lib=lib)
+    assert np.array_equal(t40, want40)
+    img81 = oracle.q80_pack_block(np.float32(2.0), np.ones(32, np.int8), lib=lib)
+    t80 = oracle.q32_tensor("q80", [img80, img81], lib=lib)
+    assert np.array_equal(t80, want80)
+    assert np.array_equal(oracle.q32_get_block("q40", t40, 2, 1, lib=lib), img1)
+    assert np.array_equal(oracle.q32_get_block("q80", t80, 2, 0, lib=lib), img80)
+    # dequantization: the closed forms d * (q - 8) and d * q, block by block
+    w40 = oracle.dequantize("q40", t40, 1, 64, lib=lib)[0]
+    assert np.array_equal(w40[:32], -0.125 * (q.astype(np.float64) - 8))
+    assert np.all(w40[32:] == 0.0)
+    w80 = oracle.dequantize("q80", t80, 1, 64, lib=lib)[0]
+    assert np.array_equal(w80[:32], 0.5 * q8.astype(np.float64))
+    assert np.all(w80[32:] == 2.0)
+    # the same tensors read as two rows of one block each
+    assert np.array_equal(oracle.dequantize("q40", t40, 2, 32, lib=lib).reshape(-1), w40)
 
 
 # -------------------------------------------------------------- activations --
@@ -296,11 +340,66 @@ def check_q6k_quantizer(lib, w, negate=False):
     return buf
 
 
+def check_q40_quantizer(lib, w):
+    """Q4_0: the block's largest-magnitude weight sets d (it lands on code 0 up to the fp16
+    rounding of d), every code is a nearest grid point d * (q - 8), and only weights beyond
+    7.5 |d| on the opposite side are clipped (to code 15)."""
+    rows, cols = w.shape
+    buf = oracle.quantize_q40(w, lib=lib)
+    n = rows * cols // 32
+    imgs = np.stack([oracle.q32_get_block("q40", buf, n, i, lib=lib) for i in range(n)])
+    d = _f16(imgs[:, :2].copy().view(np.uint16)[:, 0])
+    wb = w.astype(np.float64).reshape(n, 32)
+    what = oracle.dequantize("q40", buf, rows, cols, lib=lib).reshape(n, 32)
+    codes = np.stack([oracle.q40_unpack_block(imgs[i], lib=lib)[1] for i in range(n)]).astype(int)
+    # the scale: d * (0 - 8) reproduces the first largest-magnitude weight m
+    idx = np.abs(wb).argmax(axis=1)
+    m = wb[np.arange(n), idx]
+    normal = np.abs(d) >= 2.0 ** -14
+    assert np.all(np.abs(-8 * d - m)[normal] <= 8 * np.abs(d[normal]) * 2.0 ** -11)
+    assert np.all(codes[np.arange(n), idx][normal] == 0)
+    assert np.all(d[m == 0] == 0) and np.all(codes[m == 0] == 8)
+    # nearest grid point among the 16 codes
+    grid = d[:, None, None] * (np.arange(16) - 8)[None, None, :]
+    best = np.abs(wb[:, :, None] - grid).min(axis=2)
+    err = np.abs(wb - what)
+    assert np.all(err <= best + 1e-6 * np.abs(d)[:, None] + 1e-300)
+    # round-trip bound: |d|/2 inside the grid, and at most |w| - 7 |d| for clipped weights
+    inside = np.abs(wb) <= 7.5 * np.abs(d)[:, None] * (1 - 1e-6)
+    assert np.all(err[inside] <= (np.abs(d)[:, None] * (0.5 + 1e-6)).repeat(32, 1)[inside])
+    clipped = ~inside & (np.sign(wb) == -np.sign(m)[:, None])
+    assert np.all(codes[clipped] == 15)
+    return buf
+
+
+def check_q80_quantizer(lib, w):
+    """Q8_0: the activation rule applied to weight blocks (the hand-pinned activation
+    quantizer gives the same codes and scales), so |w - d q| <= d / 2 and the
+    largest-magnitude weight gets +-127."""
+    rows, cols = w.shape
+    buf = oracle.quantize_q80(w, lib=lib)
+    n = rows * cols // 32
+    xq, xd = oracle.quantize_act(w.reshape(1, -1), lib=lib)
+    codes = oracle.planes("q80", buf, rows, cols)[0].reshape(-1).view(np.int8)
+    scales = oracle.planes("q80", buf, rows, cols)[1].reshape(-1).copy().view(np.float32)
+    assert np.array_equal(codes, xq.reshape(-1))
+    assert np.array_equal(scales.view(np.uint32), xd.reshape(-1).view(np.uint32))
+    what = oracle.dequantize("q80", buf, rows, cols, lib=lib).reshape(n, 32)
+    wb = w.astype(np.float64).reshape(n, 32)
+    assert np.all(np.abs(wb - what) <= scales.astype(np.float64)[:, None] * (0.5 + 1e-5))
+    return buf
+
+
 # --------------------------------------------------------------- the GEMV --
+def _quantize_for(lib, wtype, w):
+    if wtype == "q6k":
+        return oracle.quantize_q6k(w, negate_scales=True, lib=lib)
+    return oracle.quantize(wtype, w, lib=lib)
+
+
 def check_gemv_bruteforce(lib, wtype, w, x, tol=1e-12):
     rows, cols = w.shape
-    buf = (oracle.quantize_q4k(w, lib=lib) if wtype == "q4k"
-           else oracle.quantize_q6k(w, negate_scales=True, lib=lib))
+    buf = _quantize_for(lib, wtype, w)
     xq, xd = oracle.quantize_act(x, lib=lib)
     res = oracle.gemv(wtype, buf, rows, cols, xq, xd, partials=True, lib=lib)
     what = oracle.dequantize(wtype, buf, rows, cols, lib=lib)
@@ -317,11 +416,10 @@ def check_gemv_bruteforce(lib, wtype, w, x, tol=1e-12):
 
 def check_gemv_onehot(lib, wtype, w, cols_to_probe=(0, 17, 255, 256 + 130)):
     rows, cols = w.shape
-    buf = (oracle.quantize_q4k(w, lib=lib) if wtype == "q4k"
-           else oracle.quantize_q6k(w, negate_scales=True, lib=lib))
+    buf = _quantize_for(lib, wtype, w)
     what = oracle.dequantize(wtype, buf, rows, cols, lib=lib)
-    ns = cols // 32 if wtype == "q4k" else cols // 16
-    sub = 32 if wtype == "q4k" else 16
+    ns = cols // 16 if wtype == "q6k" else cols // 32
+    sub = 16 if wtype == "q6k" else 32
     for k in cols_to_probe:
         if k >= cols:
             continue
@@ -342,7 +440,14 @@ def check_gemv_onehot(lib, wtype, w, cols_to_probe=(0, 17, 255, 256 + 130)):
             nb = cols // 256
             for r in range(rows):
                 i = r * nb + k // 256
-                if wtype == "q4k":
+                if wtype in ("q40", "q80"):
+                    n32 = rows * cols // 32
+                    img = oracle.q32_get_block(wtype, buf, n32, r * (cols // 32) + k // 32, lib=lib)
+                    if wtype == "q40":
+                        codes.append(int(oracle.q40_unpack_block(img, lib=lib)[1][k % 32]) - 8)
+                    else:
+                        codes.append(int(oracle.q80_unpack_block(img, lib=lib)[1][k % 32]))
+                elif wtype == "q4k":
                     blk = oracle.q4k_get_block(buf, rows * nb, i, lib=lib)
                     codes.append(int(oracle.q4k_unpack_block(blk, lib=lib)[4][k % 256]))
                 else:
@@ -415,3 +520,17 @@ def check_gemv_extremes(lib):
     assert np.all(res["P"] == 65024)
     what = oracle.dequantize("q6k", tensor, 1, cols, lib=lib)
     assert np.all(what == 1.0 * -128 * -32)
+    # Q8_0: every code 127 against every activation code 127: P = 127 * 127 * 32 = 516128
+    img = oracle.q80_pack_block(np.float32(1.0), np.full(32, 127, np.int8), lib=lib)
+    tensor = oracle.q32_tensor("q80", [img] * (cols // 32), lib=lib)
+    xq, xd = oracle.quantize_act(x_pos, lib=lib)
+    res = oracle.gemv("q80", tensor, 1, cols, xq, xd, partials=True, lib=lib)
+    assert np.all(res["P"] == 516128)
+    # Q4_0: every code 0 (value -8) against -127: P = 8 * 127 * 32 = 32512; code 15 gives
+    # 7 * -127 * 32 = -28448
+    img0 = oracle.q40_pack_block(0x3C00, np.zeros(32, np.uint8), lib=lib)
+    img15 = oracle.q40_pack_block(0x3C00, np.full(32, 15, np.uint8), lib=lib)
+    tensor = oracle.q32_tensor("q40", [img0, img15] * (cols // 64), lib=lib)
+    xq, xd = oracle.quantize_act(x_neg, lib=lib)
+    res = oracle.gemv("q40", tensor, 1, cols, xq, xd, partials=True, lib=lib)
+    assert np.all(res["P"][0, 0, 0::2] == 32512) and np.all(res["P"][0, 0, 1::2] == -28448)

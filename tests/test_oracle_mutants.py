@@ -67,6 +67,27 @@ MUTANTS = {
     "q6k_quant_divisor_63": (
         "uint16_t dh = orc_f32_to_f16(smax / 127.0f);\n            float d = orc_f16_to_f32(dh);",
         "uint16_t dh = orc_f32_to_f16(smax / 63.0f);\n            float d = orc_f16_to_f32(dh);"),
+    "q40_offset_7": (
+        "for (int t = 0; t < QB; t++) c[t] = q40_q(img, t) - 8;",
+        "for (int t = 0; t < QB; t++) c[t] = q40_q(img, t) - 7;"),
+    "q40_nibble_order": (
+        "return t < 16 ? (byte & 15) : (byte >> 4);",
+        "return t < 16 ? (byte >> 4) : (byte & 15);"),
+    "q40_scale_plane_offset": (
+        "memcpy(img, t + 16 * N + 2 * i, 2);",
+        "memcpy(img, t + 16 * N + 2 * (i ^ 1), 2);"),
+    "q80_scale_from_codes_plane": (
+        "memcpy(img, t + 32 * N + 4 * i, 4);",
+        "memcpy(img, t + 32 * i, 4);"),
+    "q40_quant_scale_sign": (
+        "uint16_t dh = m != 0.0f ? orc_f32_to_f16(m / -8.0f) : 0;",
+        "uint16_t dh = m != 0.0f ? orc_f32_to_f16(m / 8.0f) : 0;"),
+    "q40_quant_divisor_7": (
+        "uint16_t dh = m != 0.0f ? orc_f32_to_f16(m / -8.0f) : 0;",
+        "uint16_t dh = m != 0.0f ? orc_f32_to_f16(m / -7.0f) : 0;"),
+    "q80_quant_divide": (
+        "for (int t = 0; t < QB; t++) q[t] = (int8_t)clampf(rintf(wb[t] * id), -127.0f, 127.0f);",
+        "for (int t = 0; t < QB; t++) q[t] = (int8_t)clampf(d > 0.0f ? rintf(wb[t] / d) : 0.0f, -127.0f, 127.0f);"),
     "bound_drops_min": (
         "double wh = d * sc * q4k_q(blk, 32 * j + i) - dmin * m;",
         "double wh = d * sc * q4k_q(blk, 32 * j + i);"),
@@ -99,6 +120,16 @@ checks = {{
     "onehot_q6k": lambda: pins.check_gemv_onehot(lib, "q6k", w),
     "special": lambda: pins.check_gemv_special(lib),
     "extremes": lambda: pins.check_gemv_extremes(lib),
+    "q32_layout": lambda: pins.check_q32_layout_goldens(lib),
+    "q40_quantizer": lambda: (pins.check_q40_quantizer(lib, w), pins.check_q40_quantizer(lib, w3)),
+    "q80_quantizer": lambda: (pins.check_q80_quantizer(lib, w), pins.check_q80_quantizer(lib, w3)),
+    "q80_act_cases": lambda: [np.testing.assert_array_equal(
+        oracle.planes("q80", oracle.quantize_q80(xc[None, :], lib=lib), 1, xc.size)[0].reshape(-1).view(np.int8), qc)
+        for xc, qc, _ in pins.read_act_cases()],
+    "bf_q40": lambda: pins.check_gemv_bruteforce(lib, "q40", w, x),
+    "bf_q80": lambda: pins.check_gemv_bruteforce(lib, "q80", w, x),
+    "onehot_q40": lambda: pins.check_gemv_onehot(lib, "q40", w),
+    "onehot_q80": lambda: pins.check_gemv_onehot(lib, "q80", w),
 }}
 failed = []
 for name, fn in checks.items():

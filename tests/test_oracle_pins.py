@@ -17,6 +17,10 @@ def test_layout_hand_derived_blocks(orc):
     pins.check_layout_goldens(orc)
 
 
+def test_layout_q40_q80_hand_derived(orc):
+    pins.check_q32_layout_goldens(orc)
+
+
 def test_layout_single_field_probes(orc):
     pins.check_layout_probes(orc)
 
@@ -57,7 +61,38 @@ def test_q4k_subnormal_super_scale(orc):
     assert np.any(d16 < 0x0400)
 
 
-@pytest.mark.parametrize("wtype", ["q4k", "q6k"])
+@pytest.mark.parametrize("sigma", [0.02, 0.002, 1.0, 1e-6])
+def test_q40_quantizer(orc, sigma):
+    rng = np.random.default_rng(int(sigma * 1e6) % 1000 + 3)
+    w = (rng.standard_normal((12, 1024)) * sigma).astype(np.float32)
+    w[2, :32] = 0.0                          # an all-zero block
+    w[3, 32:64] = np.float32(sigma)          # a constant block (ties for the maximum)
+    w[4, 64:96] = -np.abs(w[4, 64:96])       # one-signed blocks
+    w[5, 96:128] = np.abs(w[5, 96:128])
+    w[6, 0] = np.float32(8 * sigma)          # a block whose opposite side gets clipped
+    w[6, 1:32] = np.float32(-7.9 * sigma)
+    pins.check_q40_quantizer(orc, w)
+
+
+@pytest.mark.parametrize("sigma", [0.02, 1.0, 1e6])
+def test_q80_quantizer(orc, sigma):
+    rng = np.random.default_rng(int(sigma) % 1000 + 5)
+    w = (rng.standard_normal((12, 1024)) * sigma).astype(np.float32)
+    w[2, :32] = 0.0
+    pins.check_q80_quantizer(orc, w)
+
+
+def test_q80_quantizer_hand_worked_blocks(orc):
+    """The activation fixtures (ties, the scale as one division, x * (127 / amax) against
+    x / xd) give the same codes and scales when quantized as Q8_0 weights."""
+    for x, q, xd in pins.read_act_cases():
+        buf = oracle.quantize_q80(x[None, :], lib=orc)
+        codes, scales = oracle.planes("q80", buf, 1, x.size)
+        assert np.array_equal(codes.reshape(-1).view(np.int8), q)
+        assert scales.reshape(-1).copy().view(np.float32)[0].view(np.uint32) == np.float32(xd).view(np.uint32)
+
+
+@pytest.mark.parametrize("wtype", ["q4k", "q6k", "q40", "q80"])
 def test_gemv_equals_bruteforce_on_random(orc, wtype):
     rng = np.random.default_rng(3)
     w = (rng.standard_normal((24, 768)) * 0.02).astype(np.float32)
@@ -77,7 +112,20 @@ def test_gemv_equals_bruteforce_tiny(orc, rows, nb, nvec, seed, wtype, wscale):
     pins.check_gemv_bruteforce(orc, wtype, w, x)
 
 
-@pytest.mark.parametrize("wtype", ["q4k", "q6k"])
+@settings(max_examples=40, deadline=None)
+@given(rows=st.integers(1, 8), nblk=st.integers(1, 12), nvec=st.integers(1, 3),
+       seed=st.integers(0, 2**31 - 1), wtype=st.sampled_from(["q40", "q80"]),
+       wscale=st.sampled_from([0.02, 0.002, 1.0, 30.0]))
+def test_gemv_equals_bruteforce_tiny_q32(orc, rows, nblk, nvec, seed, wtype, wscale):
+    """The 32-weight formats on widths that are not multiples of 256."""
+    rng = np.random.default_rng(seed)
+    w = (rng.standard_normal((rows, 32 * nblk)) * wscale).astype(np.float32)
+    x = (rng.standard_normal((nvec, 32 * nblk)) * rng.choice([1e-3, 1.0, 50.0])).astype(np.float32)
+    x[:, rng.integers(0, 32 * nblk, size=10)] = 0.0
+    pins.check_gemv_bruteforce(orc, wtype, w, x)
+
+
+@pytest.mark.parametrize("wtype", ["q4k", "q6k", "q40", "q80"])
 def test_gemv_one_hot_column_extraction(orc, wtype):
     w = synth.normal_f32(42, 0, 5 * 512, 0.02).reshape(5, 512)
     pins.check_gemv_onehot(orc, wtype, w)
