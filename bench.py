@@ -40,6 +40,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+FORMAT_NAMES = {"q4k": "Q4_K", "q6k": "Q6_K", "q40": "Q4_0", "q80": "Q8_0"}
 CALIB_COPY_BYTES = 256 << 20
 COLD_BYTES = 640 * 10**6
 PROFILES = os.path.join(ROOT, "profiles")
@@ -104,8 +105,10 @@ def roofline_kernel(wtype: str, plan: dict, nvec: int, launches: int) -> str:
     """The step's dominant kernel, as its template instance appears in kernel traces: the
     one-launch fused kernel (form 2) when qgemv_fused makes one launch for this shape, else the
     GEMV kernel of the two-launch route (form 0, codes read from memory)."""
-    return "gemv_%s_kernel<%d, %d, %d, %d>" % (wtype, nvec, plan["lanes_per_row"],
-                                               plan["chunks_per_lane"], 2 if launches == 1 else 0)
+    tag = {"q4k": "Q4K", "q6k": "Q6K", "q40": "Q40", "q80": "Q80"}[wtype]
+    return "gemv_kernel<qgemv::%s, %d, %d, %d, %d>" % (tag, nvec, plan["lanes_per_row"],
+                                                       plan["chunks_per_lane"],
+                                                       2 if launches == 1 else 0)
 
 
 def cpu_baseline(wl, seconds: float, y_gpu: np.ndarray) -> dict:
@@ -116,7 +119,7 @@ def cpu_baseline(wl, seconds: float, y_gpu: np.ndarray) -> dict:
     rows = min(wl.rows, 32768)
     sample = np.linspace(0, wl.rows - 1, rows).astype(np.int64)
     w = wl.weight_rows(sample)
-    wbuf = oracle.quantize_q4k(w) if wl.wtype == "q4k" else oracle.quantize_q6k(w)
+    wbuf = oracle.quantize(wl.wtype, w)
     xq, xd = oracle.quantize_act(wl.activations())
     ref = oracle.gemv(wl.wtype, wbuf, rows, wl.cols, xq, xd)
     err = np.abs(y_gpu[:, sample].astype(np.float64) - ref["y"])
@@ -399,7 +402,7 @@ def bench_group(args) -> dict:
         "data": "synthetic",
         "config": {"workload": "%d matrices sharing one activation, %s, cols %d, batch %d, cold "
                                "weights (%d rotating copies)" % (
-                                   len(grp.parts), " + ".join("%s %d" % (p.wtype.upper(), p.rows)
+                                   len(grp.parts), " + ".join("%s %d" % (FORMAT_NAMES[p.wtype], p.rows)
                                                               for p in grp.parts),
                                    cols, nvec, copies),
                    "name": grp.name, "cols": cols, "nvec": nvec, "weight_bytes": wbytes,
@@ -436,7 +439,7 @@ def cpu_baseline_group(grp, seconds: float, y_gpu: list) -> dict:
     bufs, ratio = [], 0.0
     for p, yg in zip(grp.parts, y_gpu):
         w = p.weight_block(0, p.rows)
-        buf = oracle.quantize_q4k(w) if p.wtype == "q4k" else oracle.quantize_q6k(w)
+        buf = oracle.quantize(p.wtype, w)
         ref = oracle.gemv(p.wtype, buf, p.rows, grp.cols, xq, xd)
         err = np.abs(yg.astype(np.float64) - ref["y"])
         ratio = max(ratio, float(np.max(err / np.maximum(ref["bound"], np.finfo(np.float64).tiny))))
@@ -578,11 +581,10 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int8xq4k" if wl.wtype == "q4k" else "int8xq6k",
+        "dtype": "int8x" + wl.wtype,
         "data": "synthetic",
         "config": {"workload": "%s GEMV W %dx%d, batch %d, cold weights (%d rotating copies)"
-                               % (wl.wtype.upper().replace("Q4K", "Q4_K").replace("Q6K", "Q6_K"),
-                                  wl.rows, wl.cols, wl.nvec, copies),
+                               % (FORMAT_NAMES[wl.wtype], wl.rows, wl.cols, wl.nvec, copies),
                    "name": wl.name, "rows": wl.rows, "cols": wl.cols, "nvec": wl.nvec,
                    "weight_bytes": wbytes, "plan": plan},
         "us_per_step": round(ms_step * 1e3, 3),

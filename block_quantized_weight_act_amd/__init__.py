@@ -28,7 +28,9 @@ __all__ = [
 
 QGEMV_Q4K = 1
 QGEMV_Q6K = 2
-WTYPES = {"q4k": QGEMV_Q4K, "q6k": QGEMV_Q6K}
+QGEMV_Q4_0 = 3
+QGEMV_Q8_0 = 4
+WTYPES = {"q4k": QGEMV_Q4K, "q6k": QGEMV_Q6K, "q40": QGEMV_Q4_0, "q80": QGEMV_Q8_0}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_HERE, "_lib", "libqgemv.so")

@@ -30,17 +30,45 @@ bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
     return a0 < b0 + nb && b0 < a0 + na;
 }
 
-size_t weight_bytes(int wtype, int64_t rows, int64_t cols) {
-    const int64_t nblocks = rows * (cols / kQK);
-    if (wtype == QGEMV_Q4K) return static_cast<size_t>(nblocks) * kQ4KBytes;
-    if (wtype == QGEMV_Q6K) return static_cast<size_t>(nblocks) * (kQ6KBody + 2);
-    return 0;
+bool type_ok(int wtype) {
+    return wtype == QGEMV_Q4K || wtype == QGEMV_Q6K || wtype == QGEMV_Q4_0 || wtype == QGEMV_Q8_0;
 }
 
+// Weights per block of a format: 256 for the super-block formats, 32 for Q4_0 and Q8_0.
+int64_t block_cols(int wtype) { return wtype == QGEMV_Q4_0 || wtype == QGEMV_Q8_0 ? 32 : kQK; }
+
+size_t weight_bytes(int wtype, int64_t rows, int64_t cols) {
+    const int64_t nblocks = rows * (cols / block_cols(wtype));
+    switch (wtype) {
+        case QGEMV_Q4K: return static_cast<size_t>(nblocks) * kQ4KBytes;
+        case QGEMV_Q6K: return static_cast<size_t>(nblocks) * (kQ6KBody + 2);
+        case QGEMV_Q4_0: return static_cast<size_t>(nblocks) * 18;
+        case QGEMV_Q8_0: return static_cast<size_t>(nblocks) * 36;
+        default: return 0;
+    }
+}
+
+// Shape limits common to every format: cols a positive multiple of 32 (the activation block).
 bool shape_ok(int64_t rows, int64_t cols, int32_t nvec) {
-    if (rows < 1 || cols < kQK || cols % kQK != 0 || nvec < 1 || nvec > kMaxVec) return false;
+    if (rows < 1 || cols < 32 || cols % 32 != 0 || nvec < 1 || nvec > kMaxVec) return false;
     if (rows > (int64_t{1} << 30) || cols > (int64_t{1} << 30)) return false;
-    return rows * (cols / kQK) < (int64_t{1} << 31);
+    return rows * (cols / 32) < (int64_t{1} << 31);
+}
+
+// ... and of one format: a valid type and whole weight blocks per row.
+bool shape_ok_t(int wtype, int64_t rows, int64_t cols, int32_t nvec) {
+    return type_ok(wtype) && shape_ok(rows, cols, nvec) && cols % block_cols(wtype) == 0;
+}
+
+hipError_t launch_gemv(int wtype, const GemvArgs &a, const LaunchShape &s, int nvec, bool debug,
+                       hipStream_t stream) {
+    switch (wtype) {
+        case QGEMV_Q4K: return launch_gemv_q4k(a, s, nvec, debug, stream);
+        case QGEMV_Q6K: return launch_gemv_q6k(a, s, nvec, debug, stream);
+        case QGEMV_Q4_0: return launch_gemv_q40(a, s, nvec, debug, stream);
+        case QGEMV_Q8_0: return launch_gemv_q80(a, s, nvec, debug, stream);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 bool variant_exists(int lanes, int chunks, int nvec) {
@@ -135,9 +163,8 @@ size_t plan_ws_bytes(const qgemv_plan &p, int64_t rows, int64_t cols, int32_t nv
 
 int check_gemv_args(int wtype, const void *w, const int8_t *xq, const float *xd, const void *out,
                     size_t out_bytes, int64_t rows, int64_t cols, int32_t nvec) {
-    if (wtype != QGEMV_Q4K && wtype != QGEMV_Q6K) return QGEMV_EINVAL;
     if (!w || !xq || !xd || !out) return QGEMV_EINVAL;
-    if (!shape_ok(rows, cols, nvec)) return QGEMV_EINVAL;
+    if (!shape_ok_t(wtype, rows, cols, nvec)) return QGEMV_EINVAL;
     if (!aligned(w, 16) || !aligned(xq, 16) || !aligned(xd, 4) || !aligned(out, 4))
         return QGEMV_EALIGN;
     const size_t wb = weight_bytes(wtype, rows, cols);
@@ -186,8 +213,7 @@ int run_gemv(int wtype, const void *w, const Activation &act, float *y, int64_t 
     int st;
     if (act.x) {
         // check the weights and y as for the unfused form (the codes' places are unused)
-        if (wtype != QGEMV_Q4K && wtype != QGEMV_Q6K) return QGEMV_EINVAL;
-        if (!w || !y || !shape_ok(rows, cols, nvec)) return QGEMV_EINVAL;
+        if (!w || !y || !shape_ok_t(wtype, rows, cols, nvec)) return QGEMV_EINVAL;
         if (!aligned(w, 16) || !aligned(y, 4)) return QGEMV_EALIGN;
         if (overlaps(y, ybytes, w, weight_bytes(wtype, rows, cols))) return QGEMV_EINVAL;
         st = check_fused_act(act, w, weight_bytes(wtype, rows, cols), y, ybytes, cols, nvec);
@@ -220,12 +246,11 @@ int run_gemv(int wtype, const void *w, const Activation &act, float *y, int64_t 
     a.xd_out = act.xd_out;
     a.out = need > 0 ? static_cast<float *>(ws) : y;
     a.rows = static_cast<int32_t>(rows);
-    a.nb = static_cast<int32_t>(cols / kQK);
+    a.nb = static_cast<int32_t>(cols / block_cols(wtype));
     a.nchunks = static_cast<int32_t>(cols / 32);
     LaunchShape s{plan.lanes_per_row, plan.chunks_per_lane, plan.waves_per_block, plan.blocks,
                   plan.splits};
-    hipError_t e = wtype == QGEMV_Q4K ? launch_gemv_q4k(a, s, nvec, false, stream)
-                                      : launch_gemv_q6k(a, s, nvec, false, stream);
+    hipError_t e = launch_gemv(wtype, a, s, nvec, false, stream);
     if (e != hipSuccess) return hip_fail(e);
     if (need > 0) {
         e = launch_splitk_reduce(static_cast<const float *>(ws), y, static_cast<int64_t>(nvec) * rows,
@@ -272,8 +297,7 @@ int prepare_multi(const qgemv_matrix *mats, int32_t nmats, const Activation &act
     }
     for (int i = 0; i < nmats; i++) {
         const qgemv_matrix &m = mats[i];
-        if ((m.wtype != QGEMV_Q4K && m.wtype != QGEMV_Q6K) || m.reserved != 0 || !m.w || !m.y ||
-            !shape_ok(m.rows, cols, nvec))
+        if (m.reserved != 0 || !m.w || !m.y || !shape_ok_t(m.wtype, m.rows, cols, nvec))
             return QGEMV_EINVAL;
         if (!aligned(m.w, 16) || !aligned(m.y, 4)) return QGEMV_EALIGN;
     }
@@ -304,7 +328,7 @@ int prepare_multi(const qgemv_matrix *mats, int32_t nmats, const Activation &act
     a.act.x = act.x;
     a.act.xq_out = act.xq_out;
     a.act.xd_out = act.xd_out;
-    a.act.nb = static_cast<int32_t>(cols / kQK);
+    a.act.nb = 0;                            // unused: each matrix has its own
     a.act.nchunks = static_cast<int32_t>(cols / 32);
     int64_t steps = 0;
     for (int i = 0; i < nmats; i++) {
@@ -312,7 +336,7 @@ int prepare_multi(const qgemv_matrix *mats, int32_t nmats, const Activation &act
         d.w = static_cast<const uint8_t *>(mats[i].w);
         d.out = mats[i].y;
         d.rows = static_cast<int32_t>(mats[i].rows);
-        d.nb = static_cast<int32_t>(cols / kQK);
+        d.nb = static_cast<int32_t>(cols / block_cols(mats[i].wtype));
         d.wtype = mats[i].wtype;
         d.step0 = static_cast<int32_t>(steps);
         steps += ((mats[i].rows + rpw - 1) / rpw + g - 1) / g;
@@ -351,7 +375,7 @@ const char *qgemv_status_string(int status) {
 const char *qgemv_last_error(void) { return g_last_error; }
 
 size_t qgemv_weight_bytes(int wtype, int64_t rows, int64_t cols) {
-    if (!shape_ok(rows, cols, 1)) return 0;
+    if (!shape_ok_t(wtype, rows, cols, 1)) return 0;
     return weight_bytes(wtype, rows, cols);
 }
 
@@ -368,12 +392,12 @@ int qgemv_quantize_act(const float *x, int8_t *xq, float *xd, int64_t cols, int3
 }
 
 size_t qgemv_workspace_bytes(int wtype, int64_t rows, int64_t cols, int32_t nvec) {
-    if ((wtype != QGEMV_Q4K && wtype != QGEMV_Q6K) || !shape_ok(rows, cols, nvec)) return 0;
+    if (!shape_ok_t(wtype, rows, cols, nvec)) return 0;
     return plan_ws_bytes(make_plan(wtype, rows, cols, nvec), rows, cols, nvec);
 }
 
 int qgemv_plan_for(int wtype, int64_t rows, int64_t cols, int32_t nvec, qgemv_plan *plan) {
-    if (!plan || (wtype != QGEMV_Q4K && wtype != QGEMV_Q6K) || !shape_ok(rows, cols, nvec))
+    if (!plan || !shape_ok_t(wtype, rows, cols, nvec))
         return QGEMV_EINVAL;
     *plan = make_plan(wtype, rows, cols, nvec);
     return QGEMV_OK;
@@ -398,7 +422,7 @@ int qgemv_batch_plan(int wtype, const void *w, const int8_t *xq, const float *xd
 int qgemv_batch(int wtype, const void *w, const int8_t *xq, const float *xd, float *y,
                 int64_t rows, int64_t cols, int32_t nvec, void *workspace,
                 size_t workspace_bytes, hipStream_t stream) {
-    if ((wtype != QGEMV_Q4K && wtype != QGEMV_Q6K) || !shape_ok(rows, cols, nvec))
+    if (!shape_ok_t(wtype, rows, cols, nvec))
         return QGEMV_EINVAL;
     Activation act;
     act.xq = xq;
@@ -408,7 +432,7 @@ int qgemv_batch(int wtype, const void *w, const int8_t *xq, const float *xd, flo
 }
 
 int qgemv_fused_launches(int wtype, int64_t rows, int64_t cols, int32_t nvec, int with_outputs) {
-    if ((wtype != QGEMV_Q4K && wtype != QGEMV_Q6K) || !shape_ok(rows, cols, nvec)) return 0;
+    if (!shape_ok_t(wtype, rows, cols, nvec)) return 0;
     if (!with_outputs) return 1;
     // Every workgroup of the fused kernel quantizes the whole activation slice its lanes read.
     // When that slice is large next to the workgroup's share of the weights (wide rows, many
@@ -425,7 +449,7 @@ int qgemv_fused_launches(int wtype, int64_t rows, int64_t cols, int32_t nvec, in
 int qgemv_fused(int wtype, const void *w, const float *x, int8_t *xq_out, float *xd_out, float *y,
                 int64_t rows, int64_t cols, int32_t nvec, void *workspace, size_t workspace_bytes,
                 hipStream_t stream) {
-    if ((wtype != QGEMV_Q4K && wtype != QGEMV_Q6K) || !shape_ok(rows, cols, nvec))
+    if (!shape_ok_t(wtype, rows, cols, nvec))
         return QGEMV_EINVAL;
     const qgemv_plan plan = make_plan(wtype, rows, cols, nvec);
     Activation act;
@@ -531,27 +555,31 @@ int qgemv_debug_partials(int wtype, const void *w, const int8_t *xq, const float
     a.P = P;
     a.S = S;
     a.rows = static_cast<int32_t>(rows);
-    a.nb = static_cast<int32_t>(cols / kQK);
+    a.nb = static_cast<int32_t>(cols / block_cols(wtype));
     a.nchunks = static_cast<int32_t>(cols / 32);
     LaunchShape s{plan.lanes_per_row, plan.chunks_per_lane, plan.waves_per_block, plan.blocks,
                   splits_for(plan.lanes_per_row, plan.chunks_per_lane, cols)};
-    const hipError_t e = wtype == QGEMV_Q4K ? launch_gemv_q4k(a, s, nvec, true, stream)
-                                            : launch_gemv_q6k(a, s, nvec, true, stream);
+    const hipError_t e = launch_gemv(wtype, a, s, nvec, true, stream);
     return e == hipSuccess ? QGEMV_OK : hip_fail(e);
 }
 
 int qgemv_quantize_weights_rows(int wtype, const float *w, void *out, int64_t rows,
                                 int64_t cols, int64_t row0, int64_t nrows, hipStream_t stream) {
-    if ((wtype != QGEMV_Q4K && wtype != QGEMV_Q6K) || !w || !out || !shape_ok(rows, cols, 1) ||
-        row0 < 0 || nrows < 1 || row0 > rows - nrows)
+    if (!w || !out || !shape_ok_t(wtype, rows, cols, 1) || row0 < 0 || nrows < 1 ||
+        row0 > rows - nrows)
         return QGEMV_EINVAL;
     if (!aligned(w, 16) || !aligned(out, 16)) return QGEMV_EALIGN;
     const size_t ob = weight_bytes(wtype, rows, cols);
     if (overlaps(out, ob, w, static_cast<size_t>(nrows) * cols * sizeof(float))) return QGEMV_EINVAL;
-    const hipError_t e =
-        wtype == QGEMV_Q4K
-            ? launch_quantize_q4k(w, static_cast<uint8_t *>(out), rows, cols, row0, nrows, stream)
-            : launch_quantize_q6k(w, static_cast<uint8_t *>(out), rows, cols, row0, nrows, stream);
+    uint8_t *o = static_cast<uint8_t *>(out);
+    hipError_t e = hipErrorInvalidValue;
+    switch (wtype) {
+        case QGEMV_Q4K: e = launch_quantize_q4k(w, o, rows, cols, row0, nrows, stream); break;
+        case QGEMV_Q6K: e = launch_quantize_q6k(w, o, rows, cols, row0, nrows, stream); break;
+        case QGEMV_Q4_0: e = launch_quantize_q40(w, o, rows, cols, row0, nrows, stream); break;
+        case QGEMV_Q8_0: e = launch_quantize_q80(w, o, rows, cols, row0, nrows, stream); break;
+        default: break;
+    }
     return e == hipSuccess ? QGEMV_OK : hip_fail(e);
 }
 

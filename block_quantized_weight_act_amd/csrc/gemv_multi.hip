@@ -1,11 +1,11 @@
-// Several matrices that multiply the same activation, in one launch (any mix of Q4_K and
-// Q6_K, up to kMaxMats of them, all with the same column count).
+// Several matrices that multiply the same activation, in one launch (any mix of Q4_K, Q6_K,
+// Q4_0 and Q8_0, up to kMaxMats of them, all with the same column count).
 //
 // genie-ai-runtime (jared-hpc.com), "v1.2.0": the attention projections of a decode step share
 // one quantized activation, which is made once and read by all of them instead of once per
 // product. Here they also share one launch: the matrices' row steps are numbered one after
 // the other and waves walk the combined numbering with a grid-wide stride, each step taking the
-// Q4_K or Q6_K tile (tile.h) of the matrix it falls in. A wave's activation slice is loaded (or,
+// tile (tile.h) of the matrix it falls in. A wave's activation slice is loaded (or,
 // in the fused form, quantized by its workgroup) once and serves every matrix, since lane t's
 // columns are the same in all of them. No column split: the shared lane geometry covers a
 // whole row (at most 256 chunks, 8192 columns).
@@ -17,7 +17,9 @@
 namespace qgemv {
 
 // The matrix that step st falls in (the same for the whole wave): the last one whose first
-// step is not after st. Only constant indices into the argument block, so it stays in SGPRs.
+// step is not after st. Only the first steps are scanned; the chosen descriptor is then read with
+// a wave-uniform index, so it comes from the argument block by scalar loads and only one
+// descriptor is held in SGPRs at a time.
 struct StepMat {
     const uint8_t *w;
     float *out;
@@ -25,20 +27,12 @@ struct StepMat {
 };
 
 __device__ __forceinline__ StepMat step_matrix(const MultiArgs &a, int st) {
-    StepMat m{a.m[0].w, a.m[0].out, a.m[0].rows, a.m[0].nb, a.m[0].wtype, 0};
+    int mi = 0;
 #pragma unroll
-    for (int i = 1; i < kMaxMats; i++) {
-        if (i < a.nmats && st >= a.m[i].step0) {
-            m.w = a.m[i].w;
-            m.out = a.m[i].out;
-            m.rows = a.m[i].rows;
-            m.nb = a.m[i].nb;
-            m.wtype = a.m[i].wtype;
-            m.local = a.m[i].step0;
-        }
-    }
-    m.local = st - m.local;
-    return m;
+    for (int i = 1; i < kMaxMats; i++)
+        if (i < a.nmats && st >= a.m[i].step0) mi = i;
+    const MatDesc &d = a.m[mi];
+    return StepMat{d.w, d.out, d.rows, d.nb, d.wtype, st - d.step0};
 }
 
 template <int V, int T, int NC, int MODE>
@@ -46,20 +40,27 @@ __global__ void __launch_bounds__(256) gemv_multi_kernel(MultiArgs a) {
     constexpr bool FUSED = MODE == kModeFused;
     using T4 = Q4kTile<V, T, NC>;
     using T6 = Q6kTile<V, T, NC>;
-    static_assert(T4::G == T6::G && T4::RPW == T6::RPW, "one step geometry for both formats");
+    using T40 = Q40Tile<V, T, NC>;
+    using T80 = Q80Tile<V, T, NC>;
+    static_assert(T4::G == T6::G && T4::G == T40::G && T4::G == T80::G && T4::RPW == T6::RPW,
+                  "one step geometry for every format");
     const LaneGeom<T, NC> L(a.act.nchunks);
     // the wave index is the same in all 64 lanes: keep it (and the step numbers) in SGPRs
     const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
     const int wpb = blockDim.x >> 6;
     const int stride = gridDim.x * wpb;
     const int st0 = blockIdx.x * wpb + wave;
-    typename T4::Regs regs;                  // one register set for either format
+    typename T4::Regs regs;                  // one register set for every format
     auto issue = [&](int st) {
         const StepMat m = step_matrix(a, st);
         if (m.wtype == kTypeQ4K)
             T4::issue(regs, m.w, m.rows, m.nb, m.local, L);
-        else
+        else if (m.wtype == kTypeQ6K)
             T6::issue(regs, m.w, m.rows, m.nb, m.local, L);
+        else if (m.wtype == kTypeQ40)
+            T40::issue(regs, m.w, m.rows, m.nb, m.local, L);
+        else
+            T80::issue(regs, m.w, m.rows, m.nb, m.local, L);
     };
 
     // Unlike the one-matrix kernels, the first step's weights are not loaded ahead of the
@@ -68,24 +69,27 @@ __global__ void __launch_bounds__(256) gemv_multi_kernel(MultiArgs a) {
     // 4.8 against 4.6 us from codes); the walk keeps the plain order, loads then arithmetic.
     uint32_t xw[V][NC][8];
     float xs[V][NC];
-    float xsumf[V][NC];
-    int sums[V][NC], xlo[V][NC], xhi[V][NC];
+    ActTerms<V, NC> at;
     ActPending<V, T, NC, FUSED> pend;
     act_slice_issue<V, T, NC, FUSED>(a.act, L.g, L.cv, xw, xs, pend);
     act_slice_finish<V, T, NC, FUSED>(a.act, L.cv, L.t, xw, xs, pend);
-    q4k_act_sums<V, NC>(xw, xsumf, sums);
-    q6k_act_sums<V, NC>(xw, xlo, xhi);
+    act_terms<V, NC>(xw, at);
 
     for (int st = st0; st < a.steps; st += stride) {
         issue(st);
         __builtin_amdgcn_sched_barrier(0);
         const StepMat m = step_matrix(a, st);
+        const int nsub = a.act.nchunks;
         if (m.wtype == kTypeQ4K)
-            T4::template compute<false>(regs, xw, xs, xsumf, m.out, m.rows, m.local, L, nullptr,
-                                        a.act.nchunks);
+            T4::template compute<false>(regs, xw, xs, at, m.out, m.rows, m.local, L, nullptr, nsub);
+        else if (m.wtype == kTypeQ6K)
+            T6::template compute<false>(regs, xw, xs, at, m.out, m.rows, m.local, L, nullptr, nsub);
+        else if (m.wtype == kTypeQ40)
+            T40::template compute<false>(regs, xw, xs, at, m.out, m.rows, m.local, L, nullptr,
+                                         nsub);
         else
-            T6::template compute<false>(regs, xw, xs, xlo, xhi, m.out, m.rows, m.local, L,
-                                        nullptr, a.act.nchunks);
+            T80::template compute<false>(regs, xw, xs, at, m.out, m.rows, m.local, L, nullptr,
+                                         nsub);
         __builtin_amdgcn_sched_barrier(0);
     }
 }

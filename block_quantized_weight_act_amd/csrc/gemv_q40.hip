@@ -1,0 +1,13 @@
+// The one-matrix GEMV for Q4_0 (32-weight blocks: fp16 d, 4-bit codes with offset -8):
+// the instances of the shared wave walk (gemv_walk.h) with this format's tile (tile.h), one
+// translation unit per format to keep builds parallel.
+#include "gemv_walk.h"
+
+namespace qgemv {
+
+hipError_t launch_gemv_q40(const GemvArgs &a, const LaunchShape &s, int nvec, bool debug,
+                           hipStream_t stream) {
+    return GemvLaunch<Q40>::launch(a, s, nvec, debug, stream);
+}
+
+}  // namespace qgemv

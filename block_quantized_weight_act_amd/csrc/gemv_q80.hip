@@ -1,0 +1,13 @@
+// The one-matrix GEMV for Q8_0 (32-weight blocks: float32 d, int8 codes):
+// the instances of the shared wave walk (gemv_walk.h) with this format's tile (tile.h), one
+// translation unit per format to keep builds parallel.
+#include "gemv_walk.h"
+
+namespace qgemv {
+
+hipError_t launch_gemv_q80(const GemvArgs &a, const LaunchShape &s, int nvec, bool debug,
+                           hipStream_t stream) {
+    return GemvLaunch<Q80>::launch(a, s, nvec, debug, stream);
+}
+
+}  // namespace qgemv

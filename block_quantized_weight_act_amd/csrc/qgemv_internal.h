@@ -32,7 +32,8 @@ struct GemvArgs {
     int8_t *xq_out;        // where the fused kernel also stores the codes (may be nullptr)
     float *xd_out;         // ... and the scales (nullptr exactly when xq_out is)
     int32_t rows;
-    int32_t nb;            // super-blocks per row
+    int32_t nb;            // weight blocks per row (256-weight super-blocks for Q4_K / Q6_K,
+                           // 32-weight blocks for Q4_0 / Q8_0)
     int32_t nchunks;       // 16-byte chunks per row = 8 * nb
 };
 
@@ -46,12 +47,15 @@ enum KernelMode : int { kModePlain = 0, kModeDebug = 1, kModeFused = 2 };
 constexpr int kMaxMats = 8;
 constexpr int kTypeQ4K = 1;        // the ABI's QGEMV_Q4K
 constexpr int kTypeQ6K = 2;        // the ABI's QGEMV_Q6K
+constexpr int kTypeQ40 = 3;        // the ABI's QGEMV_Q4_0
+constexpr int kTypeQ80 = 4;        // the ABI's QGEMV_Q8_0
 struct MatDesc {
     const uint8_t *w;      // planar tensor of rows x cols
     float *out;            // y of this matrix, [nvec][rows]
     int32_t rows;
-    int32_t nb;            // super-blocks per row
-    int32_t wtype;         // kTypeQ4K or kTypeQ6K
+    int32_t nb;            // weight blocks per row (256-weight super-blocks for Q4_K / Q6_K,
+                           // 32-weight blocks for Q4_0 / Q8_0)
+    int32_t wtype;         // kTypeQ4K, kTypeQ6K, kTypeQ40 or kTypeQ80
     int32_t step0;         // the matrix's first step in the launch's step numbering
 };
 struct MultiArgs {
@@ -76,6 +80,10 @@ hipError_t launch_gemv_q4k(const GemvArgs &a, const LaunchShape &s, int nvec, bo
                            hipStream_t stream);
 hipError_t launch_gemv_q6k(const GemvArgs &a, const LaunchShape &s, int nvec, bool debug,
                            hipStream_t stream);
+hipError_t launch_gemv_q40(const GemvArgs &a, const LaunchShape &s, int nvec, bool debug,
+                           hipStream_t stream);
+hipError_t launch_gemv_q80(const GemvArgs &a, const LaunchShape &s, int nvec, bool debug,
+                           hipStream_t stream);
 hipError_t launch_gemv_multi(const MultiArgs &a, const LaunchShape &s, int nvec,
                              hipStream_t stream);
 hipError_t launch_splitk_reduce(const float *part, float *y, int64_t n, int splits,
@@ -85,6 +93,10 @@ hipError_t launch_splitk_reduce(const float *part, float *y, int64_t n, int spli
 hipError_t launch_quantize_q4k(const float *w, uint8_t *out, int64_t rows, int64_t cols,
                                int64_t row0, int64_t nrows, hipStream_t stream);
 hipError_t launch_quantize_q6k(const float *w, uint8_t *out, int64_t rows, int64_t cols,
+                               int64_t row0, int64_t nrows, hipStream_t stream);
+hipError_t launch_quantize_q40(const float *w, uint8_t *out, int64_t rows, int64_t cols,
+                               int64_t row0, int64_t nrows, hipStream_t stream);
+hipError_t launch_quantize_q80(const float *w, uint8_t *out, int64_t rows, int64_t cols,
                                int64_t row0, int64_t nrows, hipStream_t stream);
 
 hipError_t launch_read_probe(const void *buf, int64_t bytes, uint32_t *sink, int blocks,

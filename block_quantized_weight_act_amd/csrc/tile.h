@@ -67,12 +67,44 @@ __device__ __forceinline__ void store_row(float (&acc)[V], float *out, int rows,
     }
 }
 
-// The loaded data of one step: 8 dwords per (row group, chunk) in both formats, so a kernel
-// that mixes formats keeps one set of registers.
+// The loaded data of one step: up to 9 dwords per (row group, chunk) in every format, so a
+// kernel that mixes formats keeps one set of registers. Every format's issue writes all three
+// fields (zeros where it has nothing), so that the branches of a mixed kernel define the same
+// values and the register set is never demoted to scratch memory.
 template <int G, int NC>
 struct StepRegs {
     uint4 a[G][NC], b[G][NC];
+    uint32_t c[G][NC];
 };
+
+// The activation terms the formats need besides the codes, all exact integers computed from
+// the slice: the code sum of each 32-column block and of its two 16-column halves.
+template <int V, int NC>
+struct ActTerms {
+    int sum[V][NC];
+    int lo[V][NC], hi[V][NC];
+    float sumf[V][NC];      // sum as float (exact: |sum| <= 4064)
+};
+
+template <int V, int NC>
+__device__ __forceinline__ void act_terms(const uint32_t (&xw)[V][NC][8], ActTerms<V, NC> &a) {
+#pragma unroll
+    for (int v = 0; v < V; v++) {
+#pragma unroll
+        for (int k = 0; k < NC; k++) {
+            int s0 = 0, s1 = 0;
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                s0 = byte_sum(xw[v][k][i], s0);
+                s1 = byte_sum(xw[v][k][4 + i], s1);
+            }
+            a.lo[v][k] = s0;
+            a.hi[v][k] = s1;
+            a.sum[v][k] = s0 + s1;
+            a.sumf[v][k] = static_cast<float>(s0 + s1);
+        }
+    }
+}
 
 // ---------------------------------------------------------------------------------- Q4_K --
 // Planar tensor: codes plane (128 bytes per super-block), then the header plane (16 bytes:
@@ -108,6 +140,7 @@ struct Q4kTile {
             for (int k = 0; k < NC; k++) {
                 r.a[gg][k] = load16(hrow + L.blk[k] * 16);
                 r.b[gg][k] = load16_stream(qrow + L.blk[k] * 128 + 16 * L.j);
+                r.c[gg][k] = 0u;
             }
         }
     }
@@ -117,7 +150,7 @@ struct Q4kTile {
     template <bool DBG>
     static __device__ __forceinline__ void compute(const Regs &r, const uint32_t (&xw)[V][NC][8],
                                                    const float (&xs)[V][NC],
-                                                   const float (&xsumf)[V][NC], float *out,
+                                                   const ActTerms<V, NC> &at, float *out,
                                                    int rows, int st, const LaneGeom<T, NC> &L,
                                                    int32_t *P, int nsub) {
 #pragma unroll
@@ -156,8 +189,8 @@ struct Q4kTile {
                     // pb is the rounded min product and eb its exact rounding error, so
                     // fmaf(d sc, P, -pb) - eb is the difference up to two roundings of
                     // quantities no larger than the result (plus eps^2 |pb|).
-                    const float pb = dm * xsumf[v][k];
-                    const float eb = fmaf(dm, xsumf[v][k], -pb);
+                    const float pb = dm * at.sumf[v][k];
+                    const float eb = fmaf(dm, at.sumf[v][k], -pb);
                     const float diff = fmaf(dsc, static_cast<float>(p), -pb) - eb;
                     acc[v] = fmaf(xs[v][k], diff, acc[v]);
                     if (DBG && rv && L.cv[k])
@@ -168,23 +201,6 @@ struct Q4kTile {
         }
     }
 };
-
-// Q4_K activation terms: the code sum of each 32-column block, as float (exact: |S| <= 4064).
-template <int V, int NC>
-__device__ __forceinline__ void q4k_act_sums(const uint32_t (&xw)[V][NC][8], float (&xsumf)[V][NC],
-                                             int (&sums)[V][NC]) {
-#pragma unroll
-    for (int v = 0; v < V; v++) {
-#pragma unroll
-        for (int k = 0; k < NC; k++) {
-            int s = 0;
-#pragma unroll
-            for (int i = 0; i < 8; i++) s = byte_sum(xw[v][k][i], s);
-            sums[v][k] = s;
-            xsumf[v][k] = static_cast<float>(s);
-        }
-    }
-}
 
 // ---------------------------------------------------------------------------------- Q6_K --
 // Planar tensor: low-bit plane (128 bytes per super-block), high-bit plane (64), sub-scale
@@ -199,7 +215,7 @@ template <int V, int T, int NC>
 struct Q6kTile {
     static constexpr int G = groups_per_step(NC);
     static constexpr int RPW = 64 / T;
-    // a: 16 low-bit bytes; b: 8 high-bit bytes, the sub-scale word, the fp16 super-scale
+    // a: 16 low-bit bytes; b: 8 high-bit bytes and the sub-scale word; c: the fp16 super-scale
     using Regs = StepRegs<G, NC>;
 
     // Low and high bits are contiguous runs that no other load touches (nontemporal); the
@@ -221,7 +237,8 @@ struct Q6kTile {
                 const uint2 h = load8_stream(hplane + b * 64 + 8 * L.j);
                 const uint32_t sc = *reinterpret_cast<const uint32_t *>(splane + b * 16 +
                                                                         4 * (L.j >> 1));
-                r.b[gg][k] = make_uint4(h.x, h.y, sc, dplane[b]);
+                r.b[gg][k] = make_uint4(h.x, h.y, sc, 0u);
+                r.c[gg][k] = dplane[b];
             }
         }
     }
@@ -230,8 +247,7 @@ struct Q6kTile {
     template <bool DBG>
     static __device__ __forceinline__ void compute(const Regs &r, const uint32_t (&xw)[V][NC][8],
                                                    const float (&xs)[V][NC],
-                                                   const int (&xlo)[V][NC],
-                                                   const int (&xhi)[V][NC], float *out, int rows,
+                                                   const ActTerms<V, NC> &at, float *out, int rows,
                                                    int st, const LaneGeom<T, NC> &L, int32_t *P,
                                                    int nsub) {
 #pragma unroll
@@ -244,7 +260,7 @@ struct Q6kTile {
 #pragma unroll
             for (int k = 0; k < NC; k++) {
                 const uint4 hb = r.b[gg][k];
-                const float d = half_to_float(hb.w);
+                const float d = half_to_float(r.c[gg][k]);
                 const int sh = 16 * (L.j & 1);
                 const int sc_lo = static_cast<int>(static_cast<int8_t>(hb.z >> sh));
                 const int sc_hi = static_cast<int>(static_cast<int8_t>(hb.z >> (sh + 8)));
@@ -265,8 +281,8 @@ struct Q6kTile {
                         plo = dot4(lo[s], xw[v][k][s], plo);
                         phi = dot4(hi[s], xw[v][k][4 + s], phi);
                     }
-                    plo -= 32 * xlo[v][k];
-                    phi -= 32 * xhi[v][k];
+                    plo -= 32 * at.lo[v][k];
+                    phi -= 32 * at.hi[v][k];
                     const int scp = sc_lo * plo + sc_hi * phi;
                     acc[v] = fmaf(xs[v][k] * d, static_cast<float>(scp), acc[v]);
                     if (DBG && rv && L.cv[k]) {
@@ -281,24 +297,140 @@ struct Q6kTile {
     }
 };
 
-// Q6_K activation terms: the code sums of the two 16-column halves of each 32-column block.
-template <int V, int NC>
-__device__ __forceinline__ void q6k_act_sums(const uint32_t (&xw)[V][NC][8], int (&xlo)[V][NC],
-                                             int (&xhi)[V][NC]) {
+// ----------------------------------------------------------------- Q4_0, Q8_0 --
+// oxinfer README, "Build and run": GGUF-style Q4_0 (32 weights, 4-bit codes, one fp16 scale)
+// and int8 weights in blocks of 32 with an f32 scale; "Pre-quantized checkpoints": codes and
+// scales are separate tensors. Here: a codes plane (16 or 32 bytes per block) then a scale plane
+// (fp16 or float32 per block); one 32-weight block is exactly one lane's chunk, so the lane loads
+// its codes (one or two 16-byte loads, streamed) and its own scale. Q4_0 weight t is nibble
+// (t >= 16) of code byte t mod 16, the same arrangement as a Q4_K chunk: the low nibbles meet
+// activation bytes 0..15 and the high nibbles bytes 16..31. Per block the product is
+// xd * d * P with P = sum (q - 8) x = sum q x - 8 S (Q4_0) or sum q x (Q8_0), exact integers
+// below 2^24.
+template <int V, int T, int NC>
+struct Q40Tile {
+    static constexpr int G = groups_per_step(NC);
+    static constexpr int RPW = 64 / T;
+    using Regs = StepRegs<G, NC>;           // a: 16 code bytes, c: fp16 d
+
+    // nb = 32-weight blocks per row
+    static __device__ __forceinline__ void issue(Regs &r, const uint8_t *w, int rows, int nb,
+                                                 int st, const LaneGeom<T, NC> &L) {
+        const uint16_t *dplane = reinterpret_cast<const uint16_t *>(
+            w + static_cast<int64_t>(rows) * nb * 16);
 #pragma unroll
-    for (int v = 0; v < V; v++) {
+        for (int gg = 0; gg < G; gg++) {
+            const int row = (st * G + gg) * RPW + L.rsub;
+            const int64_t brow = static_cast<int64_t>(row < rows ? row : rows - 1) * nb;
 #pragma unroll
-        for (int k = 0; k < NC; k++) {
-            int s0 = 0, s1 = 0;
-#pragma unroll
-            for (int i = 0; i < 4; i++) {
-                s0 = byte_sum(xw[v][k][i], s0);
-                s1 = byte_sum(xw[v][k][4 + i], s1);
+            for (int k = 0; k < NC; k++) {
+                const int64_t b = brow + (L.cv[k] ? L.g[k] : 0);
+                r.a[gg][k] = load16_stream(w + b * 16);
+                r.b[gg][k] = make_uint4(0u, 0u, 0u, 0u);
+                r.c[gg][k] = dplane[b];
             }
-            xlo[v][k] = s0;
-            xhi[v][k] = s1;
         }
     }
-}
+
+    template <bool DBG>
+    static __device__ __forceinline__ void compute(const Regs &r, const uint32_t (&xw)[V][NC][8],
+                                                   const float (&xs)[V][NC],
+                                                   const ActTerms<V, NC> &at, float *out,
+                                                   int rows, int st, const LaneGeom<T, NC> &L,
+                                                   int32_t *P, int nsub) {
+#pragma unroll
+        for (int gg = 0; gg < G; gg++) {
+            const int row = (st * G + gg) * RPW + L.rsub;
+            const bool rv = row < rows;
+            float acc[V];
+#pragma unroll
+            for (int v = 0; v < V; v++) acc[v] = 0.0f;
+#pragma unroll
+            for (int k = 0; k < NC; k++) {
+                const float d = half_to_float(r.c[gg][k]);
+                const uint32_t q[4] = {r.a[gg][k].x, r.a[gg][k].y, r.a[gg][k].z, r.a[gg][k].w};
+                uint32_t lo[4], hi[4];
+#pragma unroll
+                for (int i = 0; i < 4; i++) {
+                    lo[i] = q[i] & 0x0F0F0F0Fu;
+                    hi[i] = (q[i] >> 4) & 0x0F0F0F0Fu;
+                }
+#pragma unroll
+                for (int v = 0; v < V; v++) {
+                    int p = 0;
+#pragma unroll
+                    for (int i = 0; i < 4; i++) {
+                        p = dot4(lo[i], xw[v][k][i], p);
+                        p = dot4(hi[i], xw[v][k][4 + i], p);
+                    }
+                    p -= 8 * at.sum[v][k];
+                    acc[v] = fmaf(xs[v][k] * d, static_cast<float>(p), acc[v]);
+                    if (DBG && rv && L.cv[k])
+                        P[(static_cast<int64_t>(v) * rows + row) * nsub + L.g[k]] = p;
+                }
+            }
+            if (!DBG) store_row<V, T>(acc, out, rows, row, rv, L.t, L.lane, L.split);
+        }
+    }
+};
+
+template <int V, int T, int NC>
+struct Q80Tile {
+    static constexpr int G = groups_per_step(NC);
+    static constexpr int RPW = 64 / T;
+    using Regs = StepRegs<G, NC>;           // a, b: the 32 int8 codes, c: float32 d
+
+    // nb = 32-weight blocks per row
+    static __device__ __forceinline__ void issue(Regs &r, const uint8_t *w, int rows, int nb,
+                                                 int st, const LaneGeom<T, NC> &L) {
+        const uint32_t *dplane = reinterpret_cast<const uint32_t *>(
+            w + static_cast<int64_t>(rows) * nb * 32);
+#pragma unroll
+        for (int gg = 0; gg < G; gg++) {
+            const int row = (st * G + gg) * RPW + L.rsub;
+            const int64_t brow = static_cast<int64_t>(row < rows ? row : rows - 1) * nb;
+#pragma unroll
+            for (int k = 0; k < NC; k++) {
+                const int64_t b = brow + (L.cv[k] ? L.g[k] : 0);
+                r.a[gg][k] = load16_stream(w + b * 32);
+                r.b[gg][k] = load16_stream(w + b * 32 + 16);
+                r.c[gg][k] = dplane[b];
+            }
+        }
+    }
+
+    template <bool DBG>
+    static __device__ __forceinline__ void compute(const Regs &r, const uint32_t (&xw)[V][NC][8],
+                                                   const float (&xs)[V][NC],
+                                                   const ActTerms<V, NC> &at, float *out,
+                                                   int rows, int st, const LaneGeom<T, NC> &L,
+                                                   int32_t *P, int nsub) {
+        (void)at;
+#pragma unroll
+        for (int gg = 0; gg < G; gg++) {
+            const int row = (st * G + gg) * RPW + L.rsub;
+            const bool rv = row < rows;
+            float acc[V];
+#pragma unroll
+            for (int v = 0; v < V; v++) acc[v] = 0.0f;
+#pragma unroll
+            for (int k = 0; k < NC; k++) {
+                const float d = __builtin_bit_cast(float, r.c[gg][k]);
+                const uint32_t q[8] = {r.a[gg][k].x, r.a[gg][k].y, r.a[gg][k].z, r.a[gg][k].w,
+                                       r.b[gg][k].x, r.b[gg][k].y, r.b[gg][k].z, r.b[gg][k].w};
+#pragma unroll
+                for (int v = 0; v < V; v++) {
+                    int p = 0;
+#pragma unroll
+                    for (int i = 0; i < 8; i++) p = dot4(q[i], xw[v][k][i], p);
+                    acc[v] = fmaf(xs[v][k] * d, static_cast<float>(p), acc[v]);
+                    if (DBG && rv && L.cv[k])
+                        P[(static_cast<int64_t>(v) * rows + row) * nsub + L.g[k]] = p;
+                }
+            }
+            if (!DBG) store_row<V, T>(acc, out, rows, row, rv, L.t, L.lane, L.split);
+        }
+    }
+};
 
 }  // namespace qgemv

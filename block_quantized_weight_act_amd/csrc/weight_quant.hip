@@ -156,4 +156,94 @@ hipError_t launch_quantize_q6k(const float *w, uint8_t *out, int64_t rows, int64
     return hipGetLastError();
 }
 
+// The 32-weight formats: 8 lanes per block, 4 consecutive weights per lane (lane l of a block
+// holds weights 4l .. 4l + 3). w holds the rows' floats; block `local` of the launch is weights
+// 32 local .. 32 local + 31 of w and block blk0 + local of the tensor of ntotal blocks.
+
+// Q8_0: the activation rule on each block (quantize_act_quad: the same codes and scale).
+__global__ void __launch_bounds__(256) quantize_q80_kernel(const float4 *__restrict__ w,
+                                                           uint8_t *__restrict__ out,
+                                                           int64_t nblocks, int64_t blk0,
+                                                           int64_t ntotal) {
+    const int64_t gid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    const int64_t local = gid >> 3;
+    const bool valid = local < nblocks;       // the same for the block's 8 lanes
+    const float4 v = valid ? w[gid] : make_float4(0.f, 0.f, 0.f, 0.f);
+    const ActQuad q = quantize_act_quad(v);
+    if (valid) {
+        const int64_t blk = blk0 + local;
+        *reinterpret_cast<uint32_t *>(out + 32 * blk + 4 * (gid & 7)) = q.codes;
+        if ((gid & 7) == 0) *reinterpret_cast<float *>(out + 32 * ntotal + 4 * blk) = q.scale;
+    }
+}
+
+// Q4_0: m = the block's first weight of largest magnitude (a lane keeps the first of its four
+// on ties; across lanes the larger magnitude wins, then the smaller index); d = fp16(m / -8),
+// +0 for an all-zero block; q = clamp(rint(w / d) + 8, 0, 15), 8 when d = 0. Codes of weights
+// t and t + 16 share byte t: lane l < 4 packs its codes with those of lane l + 4.
+__global__ void __launch_bounds__(256) quantize_q40_kernel(const float4 *__restrict__ w,
+                                                           uint8_t *__restrict__ out,
+                                                           int64_t nblocks, int64_t blk0,
+                                                           int64_t ntotal) {
+    const int64_t gid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    const int64_t local = gid >> 3;
+    const int l = static_cast<int>(gid & 7);
+    const bool valid = local < nblocks;
+    const float4 v4 = valid ? w[gid] : make_float4(0.f, 0.f, 0.f, 0.f);
+    const float e[4] = {v4.x, v4.y, v4.z, v4.w};
+    float mag = fabsf(e[0]), val = e[0];
+    int idx = 4 * l;
+#pragma unroll
+    for (int i = 1; i < 4; i++) {
+        if (fabsf(e[i]) > mag) {
+            mag = fabsf(e[i]);
+            val = e[i];
+            idx = 4 * l + i;
+        }
+    }
+#pragma unroll
+    for (int off = 4; off >= 1; off >>= 1) {
+        const float pm = __shfl_xor(mag, off, 64);
+        const float pv = __shfl_xor(val, off, 64);
+        const int pi = __shfl_xor(idx, off, 64);
+        if (pm > mag || (pm == mag && pi < idx)) {
+            mag = pm;
+            val = pv;
+            idx = pi;
+        }
+    }
+    const uint32_t dh = val != 0.0f ? float_to_half(val / -8.0f) : 0u;
+    const float d = half_to_float(dh);
+    uint32_t codes = 0;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        const float q = d != 0.0f ? clampf(rintf(e[i] / d) + 8.0f, 0.0f, 15.0f) : 8.0f;
+        codes |= static_cast<uint32_t>(q) << (8 * i);
+    }
+    const uint32_t partner = __shfl_xor(codes, 4, 64);
+    if (valid) {
+        const int64_t blk = blk0 + local;
+        if (l < 4) *reinterpret_cast<uint32_t *>(out + 16 * blk + 4 * l) = codes | (partner << 4);
+        if (l == 0) reinterpret_cast<uint16_t *>(out + 16 * ntotal)[blk] = static_cast<uint16_t>(dh);
+    }
+}
+
+hipError_t launch_quantize_q40(const float *w, uint8_t *out, int64_t rows, int64_t cols,
+                               int64_t row0, int64_t nrows, hipStream_t stream) {
+    const int64_t nb = cols / 32, nblocks = nrows * nb;
+    const int64_t grid = (nblocks * 8 + 255) / 256;
+    hipLaunchKernelGGL(quantize_q40_kernel, dim3(static_cast<unsigned>(grid)), dim3(256), 0, stream,
+                       reinterpret_cast<const float4 *>(w), out, nblocks, row0 * nb, rows * nb);
+    return hipGetLastError();
+}
+
+hipError_t launch_quantize_q80(const float *w, uint8_t *out, int64_t rows, int64_t cols,
+                               int64_t row0, int64_t nrows, hipStream_t stream) {
+    const int64_t nb = cols / 32, nblocks = nrows * nb;
+    const int64_t grid = (nblocks * 8 + 255) / 256;
+    hipLaunchKernelGGL(quantize_q80_kernel, dim3(static_cast<unsigned>(grid)), dim3(256), 0, stream,
+                       reinterpret_cast<const float4 *>(w), out, nblocks, row0 * nb, rows * nb);
+    return hipGetLastError();
+}
+
 }  // namespace qgemv

@@ -47,6 +47,22 @@
  *    d of block i: fp16 at 208 N + 2 i
  *    weight = d * sc_j * (q - 32), q in [0, 63]
  *
+ *  The 32-weight formats (oxinfer README, "Build and run": --quant q4 is
+ *  GGUF-style Q4_0, --quant q8 int8 blocks of 32 with f32 scales;
+ *  "Pre-quantized checkpoints": codes and scales in separate tensors). Block i
+ *  = block b of row r with i = r * cols/32 + b; N = rows * cols/32.
+ *  Q4_0 tensor (18 bytes per block): codes plane [0, 16 N), scale plane
+ *  [16 N, 18 N).
+ *    codes of block i, at 16 i: weight t (t < 32) is the low (t < 16) or high
+ *      (t >= 16) nibble of byte t mod 16
+ *    d of block i: fp16 at 16 N + 2 i
+ *    weight = d * (q - 8), q in [0, 15]
+ *  Q8_0 tensor (36 bytes per block): codes plane [0, 32 N), scale plane
+ *  [32 N, 36 N).
+ *    codes of block i, at 32 i: weight t is the int8 at byte t
+ *    d of block i: float32 at 32 N + 4 i
+ *    weight = d * q, q in [-127, 127]
+ *
  *  Activations: codes xq int8 [nvec][cols] in [-127, 127] and scales xd
  *  float32 [nvec][cols/32]; element i of vector v stands for
  *  xd[v][i/32] * xq[v][i].
@@ -62,8 +78,8 @@
  *    Launch failures return QGEMV_EHIP with the HIP message available from
  *    qgemv_last_error() (per thread). Faults inside a kernel surface at the
  *    caller's next synchronization.
- *  - Shapes: cols a positive multiple of 256, 1 <= rows <= 2^30, 1 <= nvec <= 8,
- *    rows * cols / 256 < 2^31 super-blocks.
+ *  - Shapes: cols a positive multiple of 256 (Q4_K, Q6_K) or of 32 (Q4_0,
+ *    Q8_0), 1 <= rows <= 2^30, 1 <= nvec <= 8, rows * cols / 32 < 2^31.
  *  - Alignment: w and xq 16 bytes, xd and y 4 bytes.
  *  - Outputs must not overlap inputs.
  *  - The functions are safe to call from several host threads.
@@ -90,7 +106,9 @@ enum qgemv_status {
 
 enum qgemv_wtype {
     QGEMV_Q4K = 1,
-    QGEMV_Q6K = 2
+    QGEMV_Q6K = 2,
+    QGEMV_Q4_0 = 3,
+    QGEMV_Q8_0 = 4
 };
 
 #define QGEMV_MAX_NVEC 8
@@ -154,7 +172,7 @@ int qgemv_q6k(const void *w, const int8_t *xq, const float *xd, float *y, int64_
  * The same product for nvec = 1..8 activation vectors sharing one pass over
  * the weights (several sequences decoded together; oxinfer README, "How it
  * works": multi-token int8 decode variants). xq [nvec][cols],
- * xd [nvec][cols/32], y [nvec][rows]. wtype is QGEMV_Q4K or QGEMV_Q6K.
+ * xd [nvec][cols/32], y [nvec][rows]. wtype is one of enum qgemv_wtype.
  */
 int qgemv_batch(int wtype, const void *w, const int8_t *xq, const float *xd, float *y,
                 int64_t rows, int64_t cols, int32_t nvec, void *workspace,
@@ -198,7 +216,7 @@ int qgemv_fused_launches(int wtype, int64_t rows, int64_t cols, int32_t nvec, in
  * the same bound).
  *
  * mats: HOST array of nmats (1..QGEMV_MAX_MATRICES) descriptors, read during the
- * call only. Each: wtype QGEMV_Q4K or QGEMV_Q6K, reserved = 0, rows >= 1, w the
+ * call only. Each: wtype (any of enum qgemv_wtype), reserved = 0, rows >= 1, w the
  * device planar tensor (16-byte aligned), y device float32 [nvec][rows]
  * (4-byte aligned; no y may overlap any weights, the activation or another y).
  * The row is covered by one pass of lanes, so cols is at most 8192 for 1-2
@@ -247,7 +265,7 @@ int qgemv_debug_partials(int wtype, const void *w, const int8_t *xq, const float
                          hipStream_t stream);
 
 /*
- * Load-time weight quantization, float32 [rows][cols] -> Q4_K or Q6_K tensor
+ * Load-time weight quantization, float32 [rows][cols] -> a tensor of any format
  * (oxinfer README, "How it works", quant.rs: weights are block-quantized when
  * the model is loaded). Not on the per-token path. Every decision is taken in
  * float32 with round-to-nearest-even:
@@ -258,6 +276,10 @@ int qgemv_debug_partials(int wtype, const void *w, const int8_t *xq, const float
  *  Q6_K, per sub-block of 16: s = max |w| / 31; d = fp16(max s / 127);
  *    sc = clamp(rint(s / d), -128, 127); q = clamp(rint(w / (d * sc)), -32, 31) + 32
  *    (32 when sc = 0).
+ *  Q4_0, per block of 32: m = the first weight of largest |w|; d = fp16(m / -8)
+ *    (+0 for an all-zero block); q = clamp(rint(w / d) + 8, 0, 15) (8 when d = 0).
+ *  Q8_0, per block of 32: the activation rule, d = amax / 127,
+ *    q = clamp(rint(w * (127 / amax)), -127, 127) (0 when amax = 0).
  * w 16-byte aligned, out 16-byte aligned with qgemv_weight_bytes() bytes.
  * Inputs must be finite and small enough for the fp16 super-scales.
  */

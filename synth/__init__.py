@@ -165,7 +165,7 @@ class Workload:
                          for v in range(self.nvec)])
 
 
-# The five decode workloads. Index i uses weight seed 1000 + i, activation seed 2000 + 100 i (+ v),
+# The decode workloads. Index i uses weight seed 1000 + i, activation seed 2000 + 100 i (+ v),
 # row seed 3000 + i.
 WORKLOADS = {
     "q4k_512x512": Workload("q4k_512x512", "q4k", 512, 512, 1, 1000, 2000),
@@ -174,6 +174,11 @@ WORKLOADS = {
     "q4k_262144x1536": Workload("q4k_262144x1536", "q4k", 262144, 1536, 1, 1003, 2300,
                                 outlier_frac=0.01, seed_rows=3003),
     "q4k_16384x2048_b8": Workload("q4k_16384x2048_b8", "q4k", 16384, 2048, 8, 1004, 2400),
+    # the 32-weight formats at the vocabulary-projection shape (weight seeds 1005, 1006)
+    "q40_262144x1536": Workload("q40_262144x1536", "q40", 262144, 1536, 1,
+                                1005, 2700, outlier_frac=0.01, seed_rows=3005),
+    "q80_262144x1536": Workload("q80_262144x1536", "q80", 262144, 1536, 1, 1006, 2800,
+                                outlier_frac=0.01, seed_rows=3006),
 }
 
 

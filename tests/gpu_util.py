@@ -56,7 +56,7 @@ def gemv(wtype: str, w, xq, xd, rows: int, cols: int, nvec: int, plan=None) -> n
         qg.qgemv_batch_plan(wtype, wt, xq, xd, y, rows, cols, nvec, plan, workspace=ws)
     elif nvec == 1 and wtype == "q4k":
         qg.qgemv_q4k(wt, xq, xd, y, rows, cols, workspace=ws)
-    elif nvec == 1:
+    elif nvec == 1 and wtype == "q6k":
         qg.qgemv_q6k(wt, xq, xd, y, rows, cols, workspace=ws)
     else:
         qg.qgemv_batch(wtype, wt, xq, xd, y, rows, cols, nvec, workspace=ws)
@@ -67,7 +67,7 @@ def partials(wtype: str, w, xq, xd, rows: int, cols: int, nvec: int):
     wt = w if isinstance(w, torch.Tensor) else dev(w)
     xq = xq if isinstance(xq, torch.Tensor) else dev(xq)
     xd = xd if isinstance(xd, torch.Tensor) else dev(xd)
-    nsub = cols // 32 if wtype == "q4k" else cols // 16
+    nsub = cols // 16 if wtype == "q6k" else cols // 32
     P = torch.full((nvec, rows, nsub), -(2 ** 31), dtype=torch.int32, device=DEV)
     S = torch.full((nvec, cols // 32), -(2 ** 31), dtype=torch.int32, device=DEV)
     qg.qgemv_debug_partials(wtype, wt, xq, xd, P, S, rows, cols, nvec)

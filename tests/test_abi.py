@@ -54,7 +54,7 @@ def _call_batch(wtype=1, w=A, xq=A + (1 << 30), xd=A + (2 << 30), y=A + (3 << 30
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(wtype=3), EINVAL), (dict(w=None), EINVAL), (dict(y=None), EINVAL),
+    (dict(wtype=5), EINVAL), (dict(wtype=0), EINVAL), (dict(w=None), EINVAL), (dict(y=None), EINVAL),
     (dict(cols=1000), EINVAL), (dict(cols=0), EINVAL), (dict(rows=0), EINVAL),
     (dict(nvec=0), EINVAL), (dict(nvec=9), EINVAL), (dict(w=A + 8), EALIGN),
     (dict(xq=A + (1 << 30) + 4), EALIGN), (dict(y=A + (3 << 30) + 2), EALIGN),
@@ -116,7 +116,7 @@ def test_fused_launch_count():
     assert qg.qgemv_fused_launches("q4k", 16384, 2048, 8) == 2
     assert qg.qgemv_fused_launches("q4k", 16384, 2048, 8, with_outputs=False) == 1
     assert qg._load().qgemv_fused_launches(1, 0, 256, 1, 1) == 0
-    assert qg._load().qgemv_fused_launches(3, 8, 256, 1, 1) == 0
+    assert qg._load().qgemv_fused_launches(5, 8, 256, 1, 1) == 0
 
 
 def test_fused_rejects_bad_arguments():
@@ -128,7 +128,7 @@ def test_fused_rejects_bad_arguments():
     assert lib.qgemv_fused(1, A, X, Q + 2, D, Y, 8, 256, 1, None, 0, None) == EALIGN
     assert lib.qgemv_fused(1, A, X, Q, D, X + 64, 8, 256, 1, None, 0, None) == EINVAL  # y over x
     assert lib.qgemv_fused(1, A, X, X + 16, D, Y, 8, 256, 1, None, 0, None) == EINVAL  # codes over x
-    assert lib.qgemv_fused(3, A, X, None, None, Y, 8, 256, 1, None, 0, None) == EINVAL
+    assert lib.qgemv_fused(5, A, X, None, None, Y, 8, 256, 1, None, 0, None) == EINVAL
 
 
 def _mats(*specs):
@@ -152,7 +152,7 @@ def test_multi_rejects_bad_arguments():
     assert call(good, n=0) == EINVAL
     assert call(good * 5, n=9) == EINVAL                            # more than 8 matrices
     assert lib.qgemv_multi(None, 1, XQ, XD, 1536, 1, None) == EINVAL
-    assert call([(3, 64, W1, Y1)]) == EINVAL                        # weight type
+    assert call([(5, 64, W1, Y1)]) == EINVAL                        # weight type
     assert call([(1, 64, W1, Y1, 1)]) == EINVAL                     # reserved field set
     assert call([(1, 0, W1, Y1)]) == EINVAL                         # no rows
     assert call([(1, 64, None, Y1)]) == EINVAL

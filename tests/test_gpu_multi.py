@@ -49,6 +49,9 @@ CASES = [
     (8192, 1, [("q6k", 40), ("q4k", 9)]),
     (256, 1, [("q4k" if i % 2 else "q6k", i + 1) for i in range(8)]),   # eight matrices
     (768, 5, [("q6k", 3)]),                                               # one matrix
+    (1536, 1, [("q4k", 100), ("q40", 65), ("q80", 33), ("q6k", 20)]),    # all four formats
+    (800, 2, [("q40", 50), ("q80", 70)]),                                 # width not /256
+    (96, 8, [("q80", 5), ("q40", 3)]),
 ]
 
 
@@ -68,8 +71,7 @@ def test_multi_parity(case):
     bufs = []
     for wtype, rows in spec:
         w = (rng.standard_normal((rows, cols)) * 0.02).astype(np.float32)
-        buf = oracle.quantize_q4k(w) if wtype == "q4k" else oracle.quantize_q6k(w)
-        bufs.append(buf)
+        bufs.append(oracle.quantize(wtype, w))
     rq, rd = oracle.quantize_act(x)
     xq, xd = gu.quantize_act(x)
     assert np.array_equal(gu.host(xq), rq)

@@ -26,6 +26,16 @@ def _say(*a):
     print("[parity]", *a, flush=True)
 
 
+def _quant(wtype, w, negate=False):
+    """The oracle's tensor of w in any format (Q6_K optionally with negated sub-scales)."""
+    if wtype == "q6k":
+        return oracle.quantize_q6k(w, negate_scales=negate)
+    return oracle.quantize(wtype, w)
+
+
+ALL = ["q4k", "q6k", "q40", "q80"]
+
+
 # --------------------------------------------------------------- activations --
 @pytest.mark.parametrize("nvec,cols", [(1, 32), (1, 96), (2, 1536), (8, 2048), (3, 8192),
                                        (1, 32 * 1001)])
@@ -55,7 +65,7 @@ def test_quantize_act_hand_worked_ties():
 
 
 # ---------------------------------------------------------------- weights --
-@pytest.mark.parametrize("wtype", ["q4k", "q6k"])
+@pytest.mark.parametrize("wtype", ALL)
 @pytest.mark.parametrize("sigma", [0.02, 0.002, 1.0, 40.0])
 def test_quantize_weights_bitexact(wtype, sigma):
     _say("quantize_weights", wtype, sigma)
@@ -67,12 +77,16 @@ def test_quantize_weights_bitexact(wtype, sigma):
     w[4, 32:64] = np.float32(-0.25 * sigma)
     w[5, 0:16] = np.float32(0.0)
     w[5, 16] = np.float32(-0.0)
+    w[6, 0:32] = np.float32(0.5 * sigma)           # equal magnitudes: the first one decides
+    w[6, 40] = np.float32(-3 * sigma)
+    w[6, 41] = np.float32(3 * sigma)
+    w[7, 0] = np.float32(8 * sigma)                # the opposite extreme gets clipped (Q4_0)
+    w[7, 1:32] = np.float32(-7.9 * sigma)
     got = gu.host(gu.quantize_weights(wtype, w))
-    ref = oracle.quantize_q4k(w) if wtype == "q4k" else oracle.quantize_q6k(w)
-    assert np.array_equal(got, ref)
+    assert np.array_equal(got, _quant(wtype, w))
 
 
-@pytest.mark.parametrize("wtype", ["q4k", "q6k"])
+@pytest.mark.parametrize("wtype", ALL)
 def test_quantize_weights_rows_pieces(wtype):
     """Row ranges quantized in pieces, in any order, give the one-call tensor byte for byte,
     and one piece writes only its own rows' bytes in every plane."""
@@ -82,7 +96,7 @@ def test_quantize_weights_rows_pieces(wtype):
     _say("quantize_weights_rows", wtype, rows, cols)
     rng = np.random.default_rng(5)
     w = (rng.standard_normal((rows, cols)) * 0.03).astype(np.float32)
-    ref = oracle.quantize_q4k(w) if wtype == "q4k" else oracle.quantize_q6k(w)
+    ref = _quant(wtype, w)
     out = torch.full((qg.qgemv_weight_bytes(wtype, rows, cols),), 0xAB, dtype=torch.uint8,
                      device=gu.DEV)
     for r0, r1 in [(6, 37), (0, 5), (5, 6)]:
@@ -125,7 +139,7 @@ def test_workload_parity_full_size(name):
     for r0 in range(0, wl.rows, chunk):
         r1 = min(wl.rows, r0 + chunk)
         w = wl.weight_block(r0, r1)
-        ref = oracle.quantize_q4k(w) if wl.wtype == "q4k" else oracle.quantize_q6k(w)
+        ref = _quant(wl.wtype, w)
         got = gu.host(gu.quantize_weights(wl.wtype, w))
         assert np.array_equal(got, ref), "weight bytes differ in rows %d..%d" % (r0, r1)
         parts.append(ref)
@@ -147,6 +161,18 @@ def test_ragged_shapes(wtype, rows, cols, nvec):
     _check_gemv(wtype, wbuf, rows, cols, x)
 
 
+@pytest.mark.parametrize("wtype", ["q40", "q80"])
+@pytest.mark.parametrize("rows,cols,nvec", [(1, 32, 1), (3, 96, 1), (17, 800, 2), (100, 1056, 3),
+                                            (64, 8224, 1), (5, 1504, 8), (999, 224, 5)])
+def test_ragged_shapes_32_weight_blocks(wtype, rows, cols, nvec):
+    """Q4_0 / Q8_0 on widths that are multiples of 32 but not of 256 (8224: split columns)."""
+    _say("ragged32", wtype, rows, cols, nvec)
+    rng = np.random.default_rng(rows * 5 + cols + nvec)
+    w = (rng.standard_normal((rows, cols)) * 0.02).astype(np.float32)
+    x = rng.standard_normal((nvec, cols)).astype(np.float32)
+    _check_gemv(wtype, _quant(wtype, w), rows, cols, x)
+
+
 PLANS = [dict(lanes_per_row=t, chunks_per_lane=nc, waves_per_block=wv, blocks=b)
          for t, nc, wv, b in [(8, 1, 1, 1), (8, 4, 4, 3), (16, 1, 2, 7), (16, 3, 4, 64),
                               (32, 2, 4, 5), (64, 1, 4, 100), (64, 4, 1, 2), (64, 2, 3, 1000)]]
@@ -154,24 +180,24 @@ PLANS = [dict(lanes_per_row=t, chunks_per_lane=nc, waves_per_block=wv, blocks=b)
 
 @pytest.mark.parametrize("plan", PLANS, ids=lambda p: "T%d_NC%d_W%d_B%d" % (
     p["lanes_per_row"], p["chunks_per_lane"], p["waves_per_block"], p["blocks"]))
-@pytest.mark.parametrize("wtype", ["q4k", "q6k"])
+@pytest.mark.parametrize("wtype", ALL)
 def test_explicit_plans_and_splits(wtype, plan):
     """Every lane geometry, including column splits with the two-pass reduce."""
     rows, cols, nvec = 203, 2560, 2
     rng = np.random.default_rng(11)
     w = (rng.standard_normal((rows, cols)) * 0.02).astype(np.float32)
-    wbuf = oracle.quantize_q4k(w) if wtype == "q4k" else oracle.quantize_q6k(w)
+    wbuf = _quant(wtype, w)
     x = rng.standard_normal((nvec, cols)).astype(np.float32)
     nv = nvec if nvec * plan["chunks_per_lane"] <= 8 else 1
     _check_gemv(wtype, wbuf, rows, cols, x[:nv], plan=plan, debug=False)
 
 
-@pytest.mark.parametrize("wtype", ["q4k", "q6k"])
+@pytest.mark.parametrize("wtype", ALL)
 def test_special_inputs(wtype):
     rows, cols = 64, 1024
     rng = np.random.default_rng(3)
     w = (rng.standard_normal((rows, cols)) * 0.02).astype(np.float32)
-    wbuf = oracle.quantize_q4k(w) if wtype == "q4k" else oracle.quantize_q6k(w, negate_scales=True)
+    wbuf = _quant(wtype, w, negate=True)
     what = oracle.dequantize(wtype, wbuf, rows, cols)
     # zero activation: y is exactly zero
     y, _ = _check_gemv(wtype, wbuf, rows, cols, np.zeros((1, cols), np.float32))
@@ -188,19 +214,18 @@ def test_special_inputs(wtype):
     # constant activation
     _check_gemv(wtype, wbuf, rows, cols, np.full((2, cols), 0.7, np.float32))
     # zero weights: y is exactly zero
-    zbuf = oracle.quantize_q4k(np.zeros((rows, cols), np.float32)) if wtype == "q4k" else \
-        oracle.quantize_q6k(np.zeros((rows, cols), np.float32))
+    zbuf = _quant(wtype, np.zeros((rows, cols), np.float32))
     y, _ = _check_gemv(wtype, zbuf, rows, cols, rng.standard_normal((1, cols)).astype(np.float32))
     assert np.all(y == 0)
 
 
 @pytest.mark.parametrize("sigma", [0.002, 30.0])
-@pytest.mark.parametrize("wtype", ["q4k", "q6k"])
+@pytest.mark.parametrize("wtype", ALL)
 def test_scale_extremes(wtype, sigma):
     """Subnormal fp16 super-scales (sigma 0.002) and large ones (sigma 30)."""
     rows, cols = 128, 2048
     w = synth.normal_f32(77, 0, rows * cols, sigma).reshape(rows, cols)
-    wbuf = oracle.quantize_q4k(w) if wtype == "q4k" else oracle.quantize_q6k(w, negate_scales=True)
+    wbuf = _quant(wtype, w, negate=True)
     x = synth.normal_f32(78, 0, 2 * cols, 1.0).reshape(2, cols)
     _check_gemv(wtype, wbuf, rows, cols, x)
 
@@ -214,14 +239,22 @@ def test_integer_extremes():
     body = oracle.q6k_pack_block(np.full(16, -128, np.int8), np.zeros(256, np.uint8))
     t6 = oracle.q6k_tensor([body] * (2 * 5), [0x3C00] * (2 * 5))
     _check_gemv("q6k", t6, 5, cols, np.full((1, cols), -3.0, np.float32))
+    # Q8_0: codes 127 against 127 (P = 516128); Q4_0: codes 0 and 15 against -127
+    img = oracle.q80_pack_block(np.float32(1.0), np.full(32, 127, np.int8))
+    _check_gemv("q80", oracle.q32_tensor("q80", [img] * (16 * 5)), 5, cols,
+                np.full((1, cols), 3.0, np.float32))
+    img0 = oracle.q40_pack_block(0x3C00, np.zeros(32, np.uint8))
+    img15 = oracle.q40_pack_block(0x3C00, np.full(32, 15, np.uint8))
+    _check_gemv("q40", oracle.q32_tensor("q40", [img0, img15] * (8 * 5)), 5, cols,
+                np.full((1, cols), -3.0, np.float32))
 
 
-@pytest.mark.parametrize("wtype", ["q4k", "q6k"])
+@pytest.mark.parametrize("wtype", ALL)
 def test_determinism_permutation_and_batch(wtype):
     rows, cols = 300, 3072
     rng = np.random.default_rng(21)
     w = (rng.standard_normal((rows, cols)) * 0.02).astype(np.float32)
-    wbuf = oracle.quantize_q4k(w) if wtype == "q4k" else oracle.quantize_q6k(w)
+    wbuf = _quant(wtype, w)
     x = rng.standard_normal((1, cols)).astype(np.float32)
     xq, xd = gu.quantize_act(x)
     wt = gu.dev(wbuf)
@@ -229,7 +262,7 @@ def test_determinism_permutation_and_batch(wtype):
     y2 = gu.gemv(wtype, wt, xq, xd, rows, cols, 1)
     assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32))      # run-to-run identical
     perm = rng.permutation(rows)
-    wp = oracle.quantize_q4k(w[perm]) if wtype == "q4k" else oracle.quantize_q6k(w[perm])
+    wp = _quant(wtype, w[perm])
     yp = gu.gemv(wtype, gu.dev(wp), xq, xd, rows, cols, 1)
     assert np.array_equal(yp[0].view(np.uint32), y1[0, perm].view(np.uint32))
     # a batch of identical vectors gives identical rows
@@ -257,6 +290,7 @@ def test_workspace_required_when_split():
 @pytest.mark.parametrize("wtype,rows,cols,nvec", [
     ("q4k", 262144, 1536, 1), ("q4k", 8192, 2048, 1), ("q6k", 2048, 8192, 1),
     ("q4k", 16384, 2048, 8), ("q4k", 512, 512, 1), ("q6k", 333, 8448, 3), ("q4k", 77, 8448, 2),
+    ("q40", 4099, 1504, 1), ("q80", 1000, 2080, 2), ("q40", 300, 8224, 3), ("q80", 64, 96, 8),
 ])
 def test_fused_quantize_and_gemv(wtype, rows, cols, nvec):
     """qgemv_fused: its codes and scales are the oracle's bit for bit, and its y is

@@ -1,4 +1,4 @@
-"""The oracle on the five decode workloads (rows sampled where the full matrix is large):
+"""The oracle on the decode workloads (rows sampled where the full matrix is large):
 integer GEMV against the float64 brute force, and the quantizers' round-trip bounds."""
 
 import numpy as np
@@ -22,17 +22,18 @@ def _rows(wl, n):
 
 @pytest.mark.parametrize("name,n", [("q4k_512x512", 512), ("q4k_8192x2048", 48),
                                     ("q6k_2048x8192", 16), ("q4k_262144x1536", 64),
-                                    ("q4k_16384x2048_b8", 24)])
+                                    ("q4k_16384x2048_b8", 24), ("q40_262144x1536", 64),
+                                    ("q80_262144x1536", 64)])
 def test_workload_gemv_vs_bruteforce(orc, name, n):
     wl = synth.WORKLOADS[name]
     rows = _rows(wl, n)
     w = wl.weight_rows(rows)
     x = wl.activations()
     pins.check_gemv_bruteforce(orc, wl.wtype, w, x)
-    if wl.wtype == "q4k":
-        pins.check_q4k_quantizer(orc, w[:8])
-    else:
-        pins.check_q6k_quantizer(orc, w[:4])
+    {"q4k": lambda: pins.check_q4k_quantizer(orc, w[:8]),
+     "q6k": lambda: pins.check_q6k_quantizer(orc, w[:4]),
+     "q40": lambda: pins.check_q40_quantizer(orc, w[:8]),
+     "q80": lambda: pins.check_q80_quantizer(orc, w[:8])}[wl.wtype]()
 
 
 def test_outlier_rows_have_larger_super_scales(orc):
