@@ -465,6 +465,207 @@ def cpu_baseline_group(grp, seconds: float, y_gpu: list) -> dict:
             "gpu_y_check": {"max_err_over_bound": ratio, "ok": ratio <= 1.0}}
 
 
+def bench_decode(args) -> dict:
+    """A whole decode step's products (every layer, then the vocabulary projection), recorded
+    once with qgemv_graph_begin / qgemv_graph_end and replayed with one qgemv_graph_launch per
+    step. Step = one replay. Beside it: the same calls made directly from Python, and a
+    per-matrix form (quantize, then one product per matrix) replayed as a graph too."""
+    import torch
+
+    import block_quantized_weight_act_amd as qg
+    import synth
+
+    dec = synth.DECODE_STEPS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    t_setup = time.perf_counter()
+    items, wbytes, ws_bytes, codes_bytes, y_bytes, x_bytes = [], 0, 16, 0, 0, 0
+    for kind, item in dec.products():
+        parts = item.parts if kind == "multi" else (item,)
+        cols, nvec = parts[0].cols, parts[0].nvec
+        ws = []
+        for p in parts:
+            w0 = torch.empty(qg.qgemv_weight_bytes(p.wtype, p.rows, cols), dtype=torch.uint8,
+                             device=dev)
+            for r0 in range(0, p.rows, 32768):
+                r1 = min(p.rows, r0 + 32768)
+                wf = torch.from_numpy(p.weight_block(r0, r1)).to(dev)
+                qg.qgemv_quantize_weights_rows(p.wtype, wf, w0, p.rows, cols, r0, r1 - r0)
+                del wf
+            ws.append(w0)
+            wbytes += w0.numel()
+            ws_bytes = max(ws_bytes, qg.qgemv_workspace_bytes(p.wtype, p.rows, cols, nvec))
+        x = torch.from_numpy(parts[0].activations()).to(dev)
+        x_bytes += x.numel() * 4
+        codes_bytes += nvec * cols + nvec * (cols // 32) * 4
+        ys = [torch.empty((nvec, p.rows), dtype=torch.float32, device=dev) for p in parts]
+        y_bytes += sum(y.numel() * 4 for y in ys)
+        xq = torch.empty((nvec, cols), dtype=torch.int8, device=dev)
+        xd = torch.empty((nvec, cols // 32), dtype=torch.float32, device=dev)
+        items.append((kind, parts, ws, x, ys, xq, xd))
+    work = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    setup_s = time.perf_counter() - t_setup
+
+    def step():
+        for kind, parts, ws, x, ys, xq, xd in items:
+            cols, nvec = parts[0].cols, parts[0].nvec
+            if kind == "multi":
+                qg.qgemv_multi_fused([(p.wtype, w, p.rows, y) for p, w, y in zip(parts, ws, ys)],
+                                     x, cols, nvec)
+            else:
+                p = parts[0]
+                qg.qgemv_fused(p.wtype, ws[0], x, ys[0], p.rows, cols, nvec, workspace=work)
+
+    def per_matrix():
+        for kind, parts, ws, x, ys, xq, xd in items:
+            cols, nvec = parts[0].cols, parts[0].nvec
+            qg.qgemv_quantize_act(x, xq, xd, cols, nvec)
+            for p, w, y in zip(parts, ws, ys):
+                qg.qgemv_batch(p.wtype, w, xq, xd, y, p.rows, cols, nvec, workspace=work)
+
+    def record(fn):
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            fn()                                  # once directly on the capture stream
+            qg.qgemv_graph_begin()
+            fn()
+            g = qg.qgemv_graph_end()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        return g
+
+    g_step, g_per = record(step), record(per_matrix)
+    launches, others = g_step.nodes()
+    launches_per, _ = g_per.nodes()
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    sink_mark = torch.zeros(16, dtype=torch.uint8, device=dev)
+    for kind, parts, ws, *_ in items:
+        for w in ws:
+            qg.qgemv_read_probe(w, sink, blocks=1024)
+    for _ in range(args.warmup):
+        g_step.launch()
+    qg.qgemv_read_probe(sink_mark, sink, blocks=1, nbytes=16)
+
+    def events(fn, n):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        w = time.perf_counter()
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n, (time.perf_counter() - w) * 1e3 / n
+
+    ms_step, wall_step = events(g_step.launch, args.steps)
+    dist = spread(lambda i: g_step.launch(), args.steps)
+    for _ in range(20):
+        g_per.launch()
+    ms_per, _ = events(g_per.launch, max(20, args.steps // 4))
+    for _ in range(5):
+        step()
+    ms_direct, wall_direct = events(step, max(10, args.steps // 10))
+    g_step.launch()
+    torch.cuda.synchronize()
+    ys_all = [y for it in items for y in it[4]]
+    if not all(bool(torch.isfinite(y).all()) for y in ys_all):
+        print("bench.py: the decode step gave non-finite outputs", file=sys.stderr)
+        sys.exit(1)
+    step_bytes = wbytes + x_bytes + y_bytes
+    achieved = step_bytes / (ms_step * 1e-3) / 1e9
+    nl = len(dec.layers)
+    out = {
+        "metric": "achieved HBM GB/s and % of roofline, whole decode step of GEMVs replayed as one "
+                  "graph",
+        "value": round(achieved, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8xq4k/q6k",
+        "data": "synthetic",
+        "config": {"workload": "decode step: %d layers x (QKV %d/%d/%d, O %dx%d, gate+up 2x%dx%d, "
+                               "down %dx%d) + head %dx%d, batch 1" % (
+                                   nl, *[p.rows for p in dec.layers[0].qkv.parts],
+                                   dec.layers[0].o.rows, dec.layers[0].o.cols,
+                                   dec.layers[0].gate_up.parts[0].rows, dec.layers[0].gate_up.cols,
+                                   dec.layers[0].down.rows, dec.layers[0].down.cols,
+                                   dec.head.rows, dec.head.cols),
+                   "name": dec.name, "layers": nl, "weight_bytes": wbytes,
+                   "graph_kernel_launches": launches, "graph_other_nodes": others},
+        "us_per_step": round(ms_step * 1e3, 3),
+        "tokens_per_s_gemv_only": round(1e3 / ms_step, 1),
+        "us_per_step_distribution": dist,
+        "host_us_per_graph_launch": round(wall_step * 1e3, 3),
+        "direct_calls": {"us_per_step": round(ms_direct * 1e3, 3),
+                         "host_us_per_step": round(wall_direct * 1e3, 3),
+                         "calls_per_step": len(items)},
+        "per_matrix_graph": {"us_per_step": round(ms_per * 1e3, 3),
+                             "kernel_launches": launches_per,
+                             "gbs": round((wbytes + x_bytes + y_bytes + 2 * codes_bytes)
+                                          / (ms_per * 1e-3) / 1e9, 1)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "decode-step graph (%d kernel launches)" % launches,
+                     "algorithmic_bytes_per_launch": step_bytes,
+                     "us_per_launch": round(ms_step * 1e3, 3)},
+        "setup_s": round(setup_s, 1),
+    }
+    if not args.no_cpu_baseline:
+        l0 = dec.layers[0]
+        grp_like = [(l0.qkv.parts, items[0]), ((l0.o,), items[1]), (l0.gate_up.parts, items[2]),
+                    ((l0.down,), items[3])]
+        out["cpu_baseline"] = cpu_baseline_decode_layer(grp_like, args.cpu_seconds)
+    g_step.close()
+    g_per.close()
+    return out
+
+
+def cpu_baseline_decode_layer(products, seconds: float) -> dict:
+    """The oracle over layer 0's seven matrices (every row, each on its own activation),
+    timed; on the way the GPU's y of those products is checked against the oracle's error bound
+    (untimed)."""
+    import oracle
+    threads = max(1, min(16, os.cpu_count() or 1))
+    work, ratio, nbytes = [], 0.0, 0
+    for parts, (kind, _, _, x, ys, _, _) in products:
+        cols = parts[0].cols
+        xq, xd = oracle.quantize_act(parts[0].activations())
+        nbytes += xq.size + xd.size * 4
+        for p, yg in zip(parts, ys):
+            buf = oracle.quantize(p.wtype, p.weight_block(0, p.rows))
+            ref = oracle.gemv(p.wtype, buf, p.rows, cols, xq, xd)
+            err = np.abs(yg.cpu().numpy().astype(np.float64) - ref["y"])
+            ratio = max(ratio, float(np.max(err / np.maximum(ref["bound"],
+                                                              np.finfo(np.float64).tiny))))
+            work.append((p.wtype, buf, p.rows, cols, xq, xd))
+            nbytes += buf.size + p.nvec * p.rows * 4
+
+    def once():
+        for wtype, buf, rows, cols, xq, xd in work:
+            oracle.gemv_threaded(wtype, buf, rows, cols, xq, xd, threads)
+
+    once()
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        once()
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {"value": round(nbytes / (el / reps) / 1e9, 3), "unit": "GB/s", "cores": threads,
+            "kind": "oracle", "sample": "layer 0's seven matrices, every row, %d reps in %.1f s "
+                                        "on %d threads" % (reps, el, threads),
+            "gpu_y_check": {"max_err_over_bound": ratio, "ok": ratio <= 1.0}}
+
+
 def main():
     args = parse()
     if args.summarize_traffic:
@@ -480,6 +681,9 @@ def main():
     import synth
     if args.workload in synth.GROUPS:
         print(json.dumps(bench_group(args)), flush=True)
+        return
+    if args.workload in synth.DECODE_STEPS:
+        print(json.dumps(bench_decode(args)), flush=True)
         return
     import torch
 

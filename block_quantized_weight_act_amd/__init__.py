@@ -23,7 +23,9 @@ __all__ = [
     "qgemv_workspace_bytes", "qgemv_q4k", "qgemv_q6k", "qgemv_batch", "qgemv_debug_partials",
     "qgemv_quantize_weights", "qgemv_plan_for", "qgemv_plan_workspace_bytes", "qgemv_batch_plan",
     "qgemv_read_probe", "qgemv_fused", "qgemv_quantize_weights_rows", "qgemv_fused_launches",
-    "qgemv_multi", "qgemv_multi_fused", "qgemv_multi_geometry",
+    "qgemv_multi", "qgemv_multi_fused", "qgemv_multi_geometry", "QGEMV_Q4_0", "QGEMV_Q8_0",
+    "Graph", "qgemv_graph_begin", "qgemv_graph_end", "qgemv_graph_launch", "qgemv_graph_nodes",
+    "qgemv_graph_destroy",
 ]
 
 QGEMV_Q4K = 1
@@ -97,6 +99,11 @@ def _load():
                                             ctypes.POINTER(Plan), vp, sz, vp]),
         "qgemv_read_probe": (ctypes.c_int, [vp, sz, vp, i32, vp]),
         "qgemv_fused": (ctypes.c_int, [ctypes.c_int, vp, vp, vp, vp, vp, i64, i64, i32, vp, sz, vp]),
+        "qgemv_graph_begin": (ctypes.c_int, [vp]),
+        "qgemv_graph_end": (ctypes.c_int, [vp, ctypes.POINTER(vp)]),
+        "qgemv_graph_launch": (ctypes.c_int, [vp, vp]),
+        "qgemv_graph_nodes": (ctypes.c_int, [vp, ctypes.POINTER(i64), ctypes.POINTER(i64)]),
+        "qgemv_graph_destroy": (ctypes.c_int, [vp]),
     }
     for name, (res, args) in sigs.items():
         fn = getattr(lib, name)
@@ -312,3 +319,60 @@ def qgemv_read_probe(buf, sink, blocks: int = 2048, nbytes: int | None = None, s
     n = _nbytes(buf) if nbytes is None else nbytes
     _check("qgemv_read_probe", lib.qgemv_read_probe(_ptr(buf, name="buf"), n, _ptr(sink, name="sink"),
                                                     blocks, _stream(stream, buf)))
+
+
+# ---------------------------------------------------------------- graphs --
+class Graph:
+    """A captured sequence of library calls (qgemv_graph_end); launch() replays it."""
+
+    def __init__(self, handle: int):
+        self._h = handle
+
+    def launch(self, stream=None) -> None:
+        if not self._h:
+            raise ValueError("graph is closed")
+        _check("qgemv_graph_launch", _load().qgemv_graph_launch(self._h, _stream(stream)))
+
+    def nodes(self) -> tuple:
+        """(kernel launches, other nodes) recorded in the graph."""
+        k, o = ctypes.c_int64(), ctypes.c_int64()
+        _check("qgemv_graph_nodes", _load().qgemv_graph_nodes(self._h, ctypes.byref(k),
+                                                               ctypes.byref(o)))
+        return k.value, o.value
+
+    def close(self) -> None:
+        """Free the graph; its last launch must have finished."""
+        if self._h:
+            _load().qgemv_graph_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def qgemv_graph_begin(stream=None) -> None:
+    """Start recording this library's calls on `stream` (a created stream, default: the
+    current one)."""
+    _check("qgemv_graph_begin", _load().qgemv_graph_begin(_stream(stream)))
+
+
+def qgemv_graph_end(stream=None) -> Graph:
+    """Stop recording on `stream` and return the recorded calls as a Graph."""
+    h = ctypes.c_void_p()
+    _check("qgemv_graph_end", _load().qgemv_graph_end(_stream(stream), ctypes.byref(h)))
+    return Graph(h.value)
+
+
+def qgemv_graph_launch(graph: Graph, stream=None) -> None:
+    graph.launch(stream)
+
+
+def qgemv_graph_nodes(graph: Graph) -> tuple:
+    return graph.nodes()
+
+
+def qgemv_graph_destroy(graph: Graph) -> None:
+    graph.close()

@@ -11,17 +11,28 @@
 
 #include "qgemv_internal.h"
 
+namespace qgemv {
+
 namespace {
-
-using namespace qgemv;
-
 thread_local char g_last_error[256] = "";
+}
 
 int hip_fail(hipError_t e) {
     std::snprintf(g_last_error, sizeof g_last_error, "%s: %s", hipGetErrorName(e),
                   hipGetErrorString(e));
     return QGEMV_EHIP;
 }
+
+int fail_with(int status, const char *text) {
+    std::snprintf(g_last_error, sizeof g_last_error, "%s", text);
+    return status;
+}
+
+}  // namespace qgemv
+
+namespace {
+
+using namespace qgemv;
 
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 

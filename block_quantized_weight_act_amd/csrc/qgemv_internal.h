@@ -105,4 +105,9 @@ hipError_t launch_read_probe(const void *buf, int64_t bytes, uint32_t *sink, int
 // Whether a (lanes, chunks, nvec) combination has a compiled kernel.
 bool gemv_variant_exists(int lanes, int chunks, int nvec);
 
+// Host: record a HIP error (or a message) as this thread's last error text and return the
+// status the C ABI reports (QGEMV_EHIP, or `status`).
+int hip_fail(hipError_t e);
+int fail_with(int status, const char *text);
+
 }  // namespace qgemv

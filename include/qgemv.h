@@ -119,7 +119,8 @@ int qgemv_version(void);
 /* Static text for a status code. */
 const char *qgemv_status_string(int status);
 
-/* Text of the last HIP error seen by this thread ("" if none). */
+/* Text of the last HIP error seen by this thread, or of the reason of the last
+ * refusal of a qgemv_graph_* call ("" if none). */
 const char *qgemv_last_error(void);
 
 /* Bytes of a weight tensor of the given type and shape (0 on a bad shape). */
@@ -252,6 +253,44 @@ int qgemv_multi(const qgemv_matrix *mats, int32_t nmats, const int8_t *xq, const
  * same results). */
 int qgemv_multi_fused(const qgemv_matrix *mats, int32_t nmats, const float *x, int8_t *xq_out,
                       float *xd_out, int64_t cols, int32_t nvec, hipStream_t stream);
+
+/*
+ * Replay of a decode step (genie-ai-runtime, "v1.2.1": the per-token kernel
+ * launches of a decode step captured once into a graph, then one graph launch
+ * per token). Between qgemv_graph_begin and qgemv_graph_end on a stream, calls
+ * of this library (and any other capturable work the caller enqueues on that
+ * stream) are recorded, not run; qgemv_graph_end turns the record into a
+ * graph that qgemv_graph_launch replays. A replay runs the recorded kernels
+ * with the recorded arguments, in the recorded order, on the same buffers:
+ * the caller writes each step's inputs into the captured buffers first. The
+ * library's calls enqueue only kernels (no allocation, memset or
+ * synchronization), so a recorded call behaves as the same call made
+ * directly and its outputs are the same bit for bit.
+ *
+ * qgemv_graph_begin: stream must be a created stream (QGEMV_EINVAL for the
+ * null stream or one already capturing). The capture is thread-local: on this
+ * thread, a HIP call that cannot be recorded fails (and invalidates the
+ * capture) instead of running outside the graph. A call that fails its
+ * argument checks during the capture records nothing and leaves it valid.
+ * qgemv_graph_end: ends the capture on the same stream and stores a new graph
+ * in *graph (NULL on any error: QGEMV_EINVAL when the stream is not capturing
+ * or the record holds a memset node, which this library refuses to replay;
+ * QGEMV_EHIP when the runtime invalidated the capture or cannot instantiate
+ * the graph). The capture ends in every case where the stream was capturing.
+ * qgemv_graph_launch: enqueue one replay on `stream` (any stream, 0 = null
+ * stream). Replays of one graph run one after another; a graph must not be
+ * destroyed before its last replay has finished.
+ * qgemv_graph_nodes: the recorded kernel launches and other nodes (copies,
+ * event waits) of a graph.
+ * qgemv_graph_destroy: free the graph (host call; NULL is accepted).
+ * Graph creation and destruction allocate; a launch does not.
+ */
+typedef struct qgemv_graph qgemv_graph;
+int qgemv_graph_begin(hipStream_t stream);
+int qgemv_graph_end(hipStream_t stream, qgemv_graph **graph);
+int qgemv_graph_launch(const qgemv_graph *graph, hipStream_t stream);
+int qgemv_graph_nodes(const qgemv_graph *graph, int64_t *kernel_nodes, int64_t *other_nodes);
+int qgemv_graph_destroy(qgemv_graph *graph);
 
 /*
  * Test hook: the exact integer partials of the same kernels.

@@ -217,3 +217,74 @@ GROUPS = {
     "gate_up_1536": _group("gate_up_1536", 1536, 1, 2600, [("gate", "q4k", 6144, 1013),
                                                            ("up", "q4k", 6144, 1014)]),
 }
+
+
+@dataclasses.dataclass(frozen=True)
+class DecodeLayer:
+    """The products of one decoder layer for one token, in the order a decode step makes them:
+    the attention projections (one multi-matrix product on the normalized hidden state), the
+    output projection (on the attention output), the FFN gate and up projections (one
+    multi-matrix product) and the down projection (on the gated FFN activation)."""
+
+    qkv: WorkloadGroup
+    o: Workload
+    gate_up: WorkloadGroup
+    down: Workload
+
+
+@dataclasses.dataclass(frozen=True)
+class DecodeStep:
+    """One generated token's matrix-vector products: the layers in order, then the vocabulary
+    projection. The inputs of the products are independent seeded vectors, standing for the
+    outputs of the operations between them (normalization, attention, gating), which are not
+    part of this library."""
+
+    name: str
+    layers: tuple
+    head: Workload
+
+    def products(self):
+        """[(kind, item)] in step order: kind "multi" (a WorkloadGroup) or "one" (a Workload)."""
+        out = []
+        for layer in self.layers:
+            out += [("multi", layer.qkv), ("one", layer.o), ("multi", layer.gate_up),
+                    ("one", layer.down)]
+        out.append(("one", self.head))
+        return out
+
+
+def decode_step(name, layers, hidden, q, kv, ffn, head, formats=("q4k", "q4k", "q6k", "q4k",
+                                                                  "q4k", "q4k", "q4k"),
+                nvec=1, seed=100000):
+    """A decode step of `layers` identical layers at width `hidden`: Q, K, V projections of q,
+    kv, kv rows, output projection hidden x q, gate and up ffn x hidden, down hidden x ffn.
+    formats: the weight formats of (q, k, v, o, gate, up, down). Layer l's matrix k (in that
+    order) has weight seed seed + 16 l + k; its four inputs have seeds seed + 100000 + 100 l +
+    10 j (+ v)."""
+    fq, fk, fv, fo, fg, fu, fd = formats
+    out = []
+    for l in range(layers):
+        sw = seed + 16 * l
+        sx = seed + 100000 + 100 * l
+        qkv = WorkloadGroup("%s.l%d.qkv" % (name, l), (
+            Workload("%s.l%d.q" % (name, l), fq, q, hidden, nvec, sw + 0, sx),
+            Workload("%s.l%d.k" % (name, l), fk, kv, hidden, nvec, sw + 1, sx),
+            Workload("%s.l%d.v" % (name, l), fv, kv, hidden, nvec, sw + 2, sx)))
+        o = Workload("%s.l%d.o" % (name, l), fo, hidden, q, nvec, sw + 3, sx + 10)
+        gu = WorkloadGroup("%s.l%d.gate_up" % (name, l), (
+            Workload("%s.l%d.gate" % (name, l), fg, ffn, hidden, nvec, sw + 4, sx + 20),
+            Workload("%s.l%d.up" % (name, l), fu, ffn, hidden, nvec, sw + 5, sx + 20)))
+        down = Workload("%s.l%d.down" % (name, l), fd, hidden, ffn, nvec, sw + 6, sx + 30)
+        out.append(DecodeLayer(qkv, o, gu, down))
+    return DecodeStep(name, tuple(out), head)
+
+
+# A decode step shaped like Gemma 4 E2B, the model of the genie-ai-runtime post and of the
+# "Gemma WebGPU Engine" page: 35 layers and the 1536 -> 2048 / 256 / 256 attention projections
+# and 2048 -> 1536 output projection of that page ("Roadmap"), an FFN of width 6144 (4 x 1536;
+# the pages give no FFN width), the 262144 x 1536 vocabulary projection above as the head; V in
+# Q6_K as in the post's triple QKV product ("v1.2.0"), every other matrix Q4_K.
+DECODE_STEPS = {
+    "decode_step_1536x35": decode_step("decode_step_1536x35", 35, 1536, 2048, 256, 6144,
+                                       WORKLOADS["q4k_262144x1536"]),
+}

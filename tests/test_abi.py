@@ -193,3 +193,17 @@ def test_multi_geometry():
     assert lib.qgemv_multi_geometry(8448, 1, ctypes.byref(t), ctypes.byref(nc)) == EINVAL
     assert lib.qgemv_multi_geometry(4096, 5, ctypes.byref(t), ctypes.byref(nc)) == EINVAL
     assert lib.qgemv_multi_geometry(1536, 1, None, ctypes.byref(nc)) == EINVAL
+
+
+def test_graph_entry_points_reject_bad_arguments_on_the_host():
+    """Null graph or stream arguments are refused before any HIP call."""
+    lib = qg._load()
+    h = ctypes.c_void_p(123)
+    assert lib.qgemv_graph_begin(None) == EINVAL                     # the null stream
+    assert lib.qgemv_graph_end(None, ctypes.byref(h)) == EINVAL
+    assert h.value is None                                           # cleared on error
+    assert lib.qgemv_graph_end(A, None) == EINVAL
+    assert lib.qgemv_graph_launch(None, None) == EINVAL
+    k, o = ctypes.c_int64(), ctypes.c_int64()
+    assert lib.qgemv_graph_nodes(None, ctypes.byref(k), ctypes.byref(o)) == EINVAL
+    assert lib.qgemv_graph_destroy(None) == 0
