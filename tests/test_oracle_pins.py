@@ -137,3 +137,24 @@ def test_gemv_special_cases(orc):
 
 def test_gemv_int32_extremes(orc):
     pins.check_gemv_extremes(orc)
+
+
+@pytest.mark.parametrize("wtype", ["q4k", "q6k", "q40", "q80"])
+def test_gemv_many_vectors(orc, wtype):
+    """More than 8 vectors (the matrix-core path's range): every y equals the brute-force
+    product with the dequantized matrix, and each vector's y, P and S are those of that vector
+    alone (vectors never mix)."""
+    rng = np.random.default_rng(77)
+    nvec, rows, cols = 37, 6, 512
+    w = (rng.standard_normal((rows, cols)) * 0.05).astype(np.float32)
+    x = (rng.standard_normal((nvec, cols)) * rng.choice([0.01, 1.0, 40.0], size=(nvec, 1))
+         ).astype(np.float32)
+    x[5] = 0.0
+    buf, xq, xd, res = pins.check_gemv_bruteforce(orc, wtype, w, x)
+    for v in (0, 5, 17, 36):
+        one = oracle.gemv(wtype, buf, rows, cols, xq[v:v + 1], xd[v:v + 1], partials=True, lib=orc)
+        assert np.array_equal(one["y"][0], res["y"][v])
+        assert np.array_equal(one["P"][0], res["P"][v])
+        if wtype == "q4k":
+            assert np.array_equal(one["S"][0], res["S"][v])
+    assert not res["y"][5].any() and not res["P"][5].any()
