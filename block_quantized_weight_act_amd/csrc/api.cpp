@@ -271,6 +271,84 @@ int run_gemv(int wtype, const void *w, const Activation &act, float *y, int64_t 
     return QGEMV_OK;
 }
 
+// More than kMaxVec vectors (Q4_K): the matrix-core kernel. Workgroups of 128 rows x one
+// group of 32 * nt vectors; the super-blocks are split over more workgroups when rows and
+// groups alone give fewer than two workgroups per CU (the splits are added by the ordered
+// reduce, as for the vector kernels).
+struct McPlan {
+    int nt, row_tiles, groups, splits, sbps;
+};
+
+bool mc_shape_ok(int wtype, int64_t rows, int64_t cols, int32_t nvec) {
+    return wtype == QGEMV_Q4K && nvec > kMaxVec && nvec <= kMaxBatch && rows >= 1 &&
+           rows <= (int64_t{1} << 30) && cols >= kQK && cols % kQK == 0 &&
+           cols <= (int64_t{1} << 30) && rows * (cols / 32) < (int64_t{1} << 31);
+}
+
+McPlan make_mc_plan(int64_t rows, int64_t cols, int32_t nvec) {
+    McPlan p{};
+    const int64_t nb = cols / kQK;
+    p.nt = std::min(4, (nvec + 31) / 32);
+    p.groups = (nvec + 32 * p.nt - 1) / (32 * p.nt);
+    p.row_tiles = static_cast<int>((rows + kMcRows - 1) / kMcRows);
+    const int64_t base = static_cast<int64_t>(p.row_tiles) * p.groups;
+    const int64_t want = 2 * 256;
+    int64_t splits = base < want ? std::min<int64_t>(nb, (want + base - 1) / base) : 1;
+    p.sbps = static_cast<int>((nb + splits - 1) / splits);
+    p.splits = static_cast<int>((nb + p.sbps - 1) / p.sbps);
+    return p;
+}
+
+size_t mc_ws_bytes(const McPlan &p, int64_t rows, int32_t nvec) {
+    return p.splits > 1 ? static_cast<size_t>(p.splits) * nvec * rows * sizeof(float) : 0;
+}
+
+int run_mc(const void *w, const int8_t *xq, const float *xd, float *y, int32_t *P, int32_t *S,
+           int64_t rows, int64_t cols, int32_t nvec, void *ws, size_t ws_bytes,
+           hipStream_t stream) {
+    const bool debug = P != nullptr;
+    if (!w || !xq || !xd || (!debug && !y)) return QGEMV_EINVAL;
+    if (!aligned(w, 16) || !aligned(xq, 16) || !aligned(xd, 4) || (y && !aligned(y, 4)))
+        return QGEMV_EALIGN;
+    const size_t wb = weight_bytes(QGEMV_Q4K, rows, cols);
+    const size_t qb = static_cast<size_t>(nvec) * cols;
+    const size_t db = static_cast<size_t>(nvec) * (cols / 32) * sizeof(float);
+    const size_t yb = static_cast<size_t>(nvec) * rows * sizeof(float);
+    if (y && (overlaps(y, yb, w, wb) || overlaps(y, yb, xq, qb) || overlaps(y, yb, xd, db)))
+        return QGEMV_EINVAL;
+    const McPlan p = make_mc_plan(rows, cols, nvec);
+    const size_t need = debug ? 0 : mc_ws_bytes(p, rows, nvec);
+    if (need > 0) {
+        if (!ws || ws_bytes < need) return QGEMV_EWORKSPACE;
+        if (!aligned(ws, 4)) return QGEMV_EALIGN;
+        if (overlaps(ws, need, w, wb) || overlaps(ws, need, y, yb) || overlaps(ws, need, xq, qb) ||
+            overlaps(ws, need, xd, db))
+            return QGEMV_EINVAL;
+    }
+    GemmArgs a{};
+    a.w = static_cast<const uint8_t *>(w);
+    a.xq = xq;
+    a.xd = xd;
+    a.out = need > 0 ? static_cast<float *>(ws) : y;
+    a.P = P;
+    a.S = S;
+    a.rows = static_cast<int32_t>(rows);
+    a.nb = static_cast<int32_t>(cols / kQK);
+    a.nvec = nvec;
+    a.sb_per_split = p.sbps;
+    // the debug form covers every super-block in one split (its stores need no reduction)
+    if (debug) a.sb_per_split = a.nb;
+    hipError_t e = launch_gemm_q4k_mfma(a, p.nt, p.row_tiles, p.groups, debug ? 1 : p.splits,
+                                        debug, stream);
+    if (e != hipSuccess) return hip_fail(e);
+    if (need > 0) {
+        e = launch_splitk_reduce(static_cast<const float *>(ws), y, static_cast<int64_t>(nvec) * rows,
+                                 p.splits, stream);
+        if (e != hipSuccess) return hip_fail(e);
+    }
+    return QGEMV_OK;
+}
+
 // Several matrices with one activation (plain: act.xq / act.xd; fused: act.x and optionally
 // act.xq_out / act.xd_out): every check, then the launch description in a and s.
 int prepare_multi(const qgemv_matrix *mats, int32_t nmats, const Activation &act, int64_t cols,
@@ -403,6 +481,8 @@ int qgemv_quantize_act(const float *x, int8_t *xq, float *xd, int64_t cols, int3
 }
 
 size_t qgemv_workspace_bytes(int wtype, int64_t rows, int64_t cols, int32_t nvec) {
+    if (mc_shape_ok(wtype, rows, cols, nvec))
+        return mc_ws_bytes(make_mc_plan(rows, cols, nvec), rows, nvec);
     if (!shape_ok_t(wtype, rows, cols, nvec)) return 0;
     return plan_ws_bytes(make_plan(wtype, rows, cols, nvec), rows, cols, nvec);
 }
@@ -433,6 +513,9 @@ int qgemv_batch_plan(int wtype, const void *w, const int8_t *xq, const float *xd
 int qgemv_batch(int wtype, const void *w, const int8_t *xq, const float *xd, float *y,
                 int64_t rows, int64_t cols, int32_t nvec, void *workspace,
                 size_t workspace_bytes, hipStream_t stream) {
+    if (mc_shape_ok(wtype, rows, cols, nvec))
+        return run_mc(w, xq, xd, y, nullptr, nullptr, rows, cols, nvec, workspace,
+                      workspace_bytes, stream);
     if (!shape_ok_t(wtype, rows, cols, nvec))
         return QGEMV_EINVAL;
     Activation act;
@@ -547,6 +630,19 @@ int qgemv_debug_partials(int wtype, const void *w, const int8_t *xq, const float
                          int32_t *P, int32_t *S, int64_t rows, int64_t cols, int32_t nvec,
                          hipStream_t stream) {
     if (!P || !S) return QGEMV_EINVAL;
+    if (mc_shape_ok(wtype, rows, cols, nvec)) {
+        const size_t pbytes = static_cast<size_t>(nvec) * rows * (cols / 32) * sizeof(int32_t);
+        const size_t sbytes = static_cast<size_t>(nvec) * (cols / 32) * sizeof(int32_t);
+        if (!aligned(P, 4) || !aligned(S, 4)) return QGEMV_EALIGN;
+        const size_t wb = weight_bytes(wtype, rows, cols);
+        const size_t qb = static_cast<size_t>(nvec) * cols;
+        const size_t db = static_cast<size_t>(nvec) * (cols / 32) * sizeof(float);
+        if (overlaps(P, pbytes, S, sbytes) || overlaps(P, pbytes, w, wb) ||
+            overlaps(P, pbytes, xq, qb) || overlaps(P, pbytes, xd, db) ||
+            overlaps(S, sbytes, w, wb) || overlaps(S, sbytes, xq, qb) || overlaps(S, sbytes, xd, db))
+            return QGEMV_EINVAL;
+        return run_mc(w, xq, xd, nullptr, P, S, rows, cols, nvec, nullptr, 0, stream);
+    }
     const int64_t nsub = wtype == QGEMV_Q6K ? cols / 16 : cols / 32;
     const size_t pbytes = static_cast<size_t>(nvec) * rows * nsub * sizeof(int32_t);
     int st = check_gemv_args(wtype, w, xq, xd, P, pbytes, rows, cols, nvec);

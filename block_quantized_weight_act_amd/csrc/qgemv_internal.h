@@ -105,6 +105,26 @@ hipError_t launch_read_probe(const void *buf, int64_t bytes, uint32_t *sink, int
 // Whether a (lanes, chunks, nvec) combination has a compiled kernel.
 bool gemv_variant_exists(int lanes, int chunks, int nvec);
 
+// Many vectors on the matrix cores (gemm_mfma.hip): a workgroup of 4 waves takes 128 rows
+// (32 per wave) and a group of 32 * nt vectors over the super-blocks of one column split.
+constexpr int kMaxBatch = 256;     // vectors per product on the matrix-core path
+constexpr int kMcRows = 128;       // rows per workgroup
+struct GemmArgs {
+    const uint8_t *w;      // Q4_K tensor
+    const int8_t *xq;      // [nvec][cols]
+    const float *xd;       // [nvec][cols/32]
+    float *out;            // [splits][nvec][rows] (y itself when splits == 1)
+    int32_t *P;            // debug: [nvec][rows][cols/32] integer partials, or nullptr
+    int32_t *S;            // debug: [nvec][cols/32] activation block sums, or nullptr
+    int32_t rows;
+    int32_t nb;            // super-blocks per row
+    int32_t nvec;
+    int32_t sb_per_split;  // super-blocks per column split
+};
+// Grid: (row tiles, vector groups, splits); nt = 1..4 tiles of 32 vectors per group.
+hipError_t launch_gemm_q4k_mfma(const GemmArgs &a, int nt, int row_tiles, int groups, int splits,
+                                bool debug, hipStream_t stream);
+
 // Host: record a HIP error (or a message) as this thread's last error text and return the
 // status the C ABI reports (QGEMV_EHIP, or `status`).
 int hip_fail(hipError_t e);

@@ -79,7 +79,9 @@
  *    qgemv_last_error() (per thread). Faults inside a kernel surface at the
  *    caller's next synchronization.
  *  - Shapes: cols a positive multiple of 256 (Q4_K, Q6_K) or of 32 (Q4_0,
- *    Q8_0), 1 <= rows <= 2^30, 1 <= nvec <= 8, rows * cols / 32 < 2^31.
+ *    Q8_0), 1 <= rows <= 2^30, 1 <= nvec <= 8, rows * cols / 32 < 2^31;
+ *    qgemv_batch, qgemv_workspace_bytes and qgemv_debug_partials also take
+ *    9 <= nvec <= QGEMV_MAX_BATCH vectors for Q4_K (the matrix-core path).
  *  - Alignment: w and xq 16 bytes, xd and y 4 bytes.
  *  - Outputs must not overlap inputs.
  *  - The functions are safe to call from several host threads.
@@ -112,6 +114,7 @@ enum qgemv_wtype {
 };
 
 #define QGEMV_MAX_NVEC 8
+#define QGEMV_MAX_BATCH 256
 
 /* Library version, major * 10000 + minor * 100 + patch. */
 int qgemv_version(void);
@@ -174,6 +177,14 @@ int qgemv_q6k(const void *w, const int8_t *xq, const float *xd, float *y, int64_
  * the weights (several sequences decoded together; oxinfer README, "How it
  * works": multi-token int8 decode variants). xq [nvec][cols],
  * xd [nvec][cols/32], y [nvec][rows]. wtype is one of enum qgemv_wtype.
+ *
+ * Q4_K with 9 <= nvec <= QGEMV_MAX_BATCH (many tokens verified or prefilled
+ * at once; oxinfer README, "Speculative decoding": the many-token int8
+ * variants are instruction-bound at Q4) runs on the matrix cores: the same
+ * exact integer sub-block products P and sums S, then the same float32
+ * scaling, so y lies within the same bound of the exact product. Other types
+ * with nvec > 8: QGEMV_EINVAL. The workspace (qgemv_workspace_bytes) is
+ * needed when the super-blocks are split over workgroups (few rows).
  */
 int qgemv_batch(int wtype, const void *w, const int8_t *xq, const float *xd, float *y,
                 int64_t rows, int64_t cols, int32_t nvec, void *workspace,
@@ -293,7 +304,8 @@ int qgemv_graph_nodes(const qgemv_graph *graph, int64_t *kernel_nodes, int64_t *
 int qgemv_graph_destroy(qgemv_graph *graph);
 
 /*
- * Test hook: the exact integer partials of the same kernels.
+ * Test hook: the exact integer partials of the same kernels (for Q4_K with
+ * more than 8 vectors, of the matrix-core kernel).
  * P int32: Q4_K [nvec][rows][cols/32] (sum of q * xq per 32-column
  * sub-block), Q6_K [nvec][rows][cols/16] (sum of (q - 32) * xq per 16-column
  * sub-block). S int32 [nvec][cols/32]: sum of xq per activation block.
@@ -355,7 +367,8 @@ typedef struct qgemv_plan {
     int32_t splits;           /* derived: column chunks (output of qgemv_plan_for) */
 } qgemv_plan;
 
-/* The plan the library uses for a shape (filled into *plan). */
+/* The plan the library uses for a shape (filled into *plan); nvec <= 8 only
+ * (the matrix-core path for more vectors has no explicit plans). */
 int qgemv_plan_for(int wtype, int64_t rows, int64_t cols, int32_t nvec, qgemv_plan *plan);
 
 /* Workspace bytes for an explicit plan (0 when it does not split). */

@@ -56,7 +56,7 @@ def _call_batch(wtype=1, w=A, xq=A + (1 << 30), xd=A + (2 << 30), y=A + (3 << 30
 @pytest.mark.parametrize("kw,status", [
     (dict(wtype=5), EINVAL), (dict(wtype=0), EINVAL), (dict(w=None), EINVAL), (dict(y=None), EINVAL),
     (dict(cols=1000), EINVAL), (dict(cols=0), EINVAL), (dict(rows=0), EINVAL),
-    (dict(nvec=0), EINVAL), (dict(nvec=9), EINVAL), (dict(w=A + 8), EALIGN),
+    (dict(nvec=0), EINVAL), (dict(nvec=257), EINVAL), (dict(w=A + 8), EALIGN),
     (dict(xq=A + (1 << 30) + 4), EALIGN), (dict(y=A + (3 << 30) + 2), EALIGN),
     (dict(y=A + 64), EINVAL),              # output overlapping the weights
     (dict(rows=1 << 31), EINVAL),
@@ -207,3 +207,20 @@ def test_graph_entry_points_reject_bad_arguments_on_the_host():
     k, o = ctypes.c_int64(), ctypes.c_int64()
     assert lib.qgemv_graph_nodes(None, ctypes.byref(k), ctypes.byref(o)) == EINVAL
     assert lib.qgemv_graph_destroy(None) == 0
+
+
+def test_matrix_core_path_limits_on_the_host():
+    """More than 8 vectors: Q4_K only, at most QGEMV_MAX_BATCH, workspace sized for its split;
+    all refused before any launch."""
+    lib = qg._load()
+    assert qg.qgemv_workspace_bytes("q4k", 256, 2048, 64) > 0          # few rows: split
+    assert qg.qgemv_workspace_bytes("q4k", 1 << 16, 2048, 64) == 0      # enough rows
+    assert qg.qgemv_workspace_bytes("q6k", 256, 2048, 64) == 0          # no such path
+    assert qg.qgemv_workspace_bytes("q4k", 256, 2048, 257) == 0
+    assert _call_batch(nvec=257) == EINVAL
+    assert _call_batch(wtype=2, nvec=9) == EINVAL
+    assert _call_batch(wtype=3, nvec=9) == EINVAL
+    assert _call_batch(nvec=64, rows=256, cols=2048) == EWORKSPACE
+    assert _call_batch(nvec=64, xq=A + (1 << 30) + 4) == EALIGN
+    plan = qg.Plan()
+    assert lib.qgemv_plan_for(1, 64, 1024, 9, ctypes.byref(plan)) == EINVAL
