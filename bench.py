@@ -27,6 +27,7 @@ Prints ONE JSON line (rank 0, N = 1):
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import math
@@ -40,6 +41,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+MFMA_F16_PEAK_TFLOPS = 2500.0     # dense fp16 matrix peak of MI355X
 FORMAT_NAMES = {"q4k": "Q4_K", "q6k": "Q6_K", "q40": "Q4_0", "q80": "Q8_0"}
 CALIB_COPY_BYTES = 256 << 20
 COLD_BYTES = 640 * 10**6
@@ -59,6 +61,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=2000)
     ap.add_argument("--workload", default="q4k_262144x1536")
+    ap.add_argument("--nvec", type=int, default=0,
+                    help="override the workload's vector count (more than 8: matrix cores)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--warm", action="store_true", help="reuse one weight copy (cache-warm)")
@@ -111,12 +115,12 @@ def roofline_kernel(wtype: str, plan: dict, nvec: int, launches: int) -> str:
                                                        2 if launches == 1 else 0)
 
 
-def cpu_baseline(wl, seconds: float, y_gpu: np.ndarray) -> dict:
+def cpu_baseline(wl, seconds: float, y_gpu: np.ndarray, max_rows: int = 32768) -> dict:
     """The oracle's GEMV timed on a bounded sample of rows; on the way it also checks the
     GPU's y on those rows against the oracle's error bound (untimed)."""
     import oracle
     threads = max(1, min(16, os.cpu_count() or 1))
-    rows = min(wl.rows, 32768)
+    rows = min(wl.rows, max_rows)
     sample = np.linspace(0, wl.rows - 1, rows).astype(np.int64)
     w = wl.weight_rows(sample)
     wbuf = oracle.quantize(wl.wtype, w)
@@ -666,6 +670,134 @@ def cpu_baseline_decode_layer(products, seconds: float) -> dict:
             "gpu_y_check": {"max_err_over_bound": ratio, "ok": ratio <= 1.0}}
 
 
+def bench_many(args, wl) -> dict:
+    """More than 8 vectors (the matrix-core kernel). Step = qgemv_quantize_act + qgemv_batch
+    (plus the ordered reduce when the super-blocks are split), replayed as one graph over
+    rotating weight copies. Beside it: the product alone, and the same vectors through the
+    8-vector kernel (ceil(nvec / 8) products, each reading all the weights)."""
+    import torch
+
+    import block_quantized_weight_act_amd as qg
+
+    nvec, rows, cols = wl.nvec, wl.rows, wl.cols
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    t_setup = time.perf_counter()
+    wbytes = qg.qgemv_weight_bytes(wl.wtype, rows, cols)
+    w0 = torch.empty(wbytes, dtype=torch.uint8, device=dev)
+    for r0 in range(0, rows, 32768):
+        r1 = min(rows, r0 + 32768)
+        wf = torch.from_numpy(wl.weight_block(r0, r1)).to(dev)
+        qg.qgemv_quantize_weights_rows(wl.wtype, wf, w0, rows, cols, r0, r1 - r0)
+        del wf
+    copies = 1 if args.warm else max(1, min(64, math.ceil(COLD_BYTES / wbytes)))
+    ws_list = [w0] + [w0.clone() for _ in range(copies - 1)]
+    x = torch.from_numpy(wl.activations()).to(dev)
+    xq = torch.empty((nvec, cols), dtype=torch.int8, device=dev)
+    xd = torch.empty((nvec, cols // 32), dtype=torch.float32, device=dev)
+    y = torch.empty((nvec, rows), dtype=torch.float32, device=dev)
+    wsb = max(qg.qgemv_workspace_bytes(wl.wtype, rows, cols, nvec),
+              qg.qgemv_workspace_bytes(wl.wtype, rows, cols, 8))
+    work = torch.empty(max(wsb, 4), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    setup_s = time.perf_counter() - t_setup
+
+    def gemm(i):
+        qg.qgemv_batch(wl.wtype, ws_list[i % copies], xq, xd, y, rows, cols, nvec, workspace=work)
+
+    def step(i):
+        qg.qgemv_quantize_act(x, xq, xd, cols, nvec)
+        gemm(i)
+
+    def by_eight(i):
+        for v0 in range(0, nvec, 8):
+            n = min(8, nvec - v0)
+            qg.qgemv_batch(wl.wtype, ws_list[i % copies], xq[v0:v0 + n], xd[v0:v0 + n],
+                           y[v0:v0 + n], rows, cols, n, workspace=work)
+
+    n8 = max(4, args.steps // 8)
+    graphs = {"step": capture(step, args.steps), "gemm": capture(gemm, args.steps),
+              "by_eight": capture(by_eight, n8)}
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    sink_mark = torch.zeros(16, dtype=torch.uint8, device=dev)
+    for _ in range(2):
+        for t in ws_list:
+            qg.qgemv_read_probe(t, sink, blocks=4096)
+    for i in range(args.warmup):
+        step(i)
+    qg.qgemv_read_probe(sink_mark, sink, blocks=1, nbytes=16)
+    ms_step = replay_timed(graphs["step"], args.steps)
+    ms_gemm = replay_timed(graphs["gemm"], args.steps)
+    ms_gemm_events, _ = timed(gemm, args.steps)
+    ms_eight = replay_timed(graphs["by_eight"], n8)
+    dist = spread(step, args.steps)
+    step(0)
+    torch.cuda.synchronize()
+    if not bool(torch.isfinite(y).all()):
+        print("bench.py: the product gave non-finite outputs", file=sys.stderr)
+        sys.exit(1)
+
+    codes = nvec * cols + nvec * (cols // 32) * 4
+    ybytes = nvec * rows * 4
+    gemm_bytes = wbytes + codes + ybytes
+    step_bytes = wbytes + nvec * cols * 4 + ybytes
+    flops = 2.0 * rows * cols * nvec
+    achieved = step_bytes / (ms_step * 1e-3) / 1e9
+    gemm_gbs = gemm_bytes / (ms_gemm * 1e-3) / 1e9
+    gemm_tflops = flops / (ms_gemm * 1e-3) / 1e12
+    t_hbm = gemm_bytes / (HBM_PEAK_GBS * 1e9)
+    t_mfma = flops / (MFMA_F16_PEAK_TFLOPS * 1e12)
+    nt = min(4, (nvec + 31) // 32)
+    kernel = "gemm_q4k_mfma_kernel<%d, false>" % nt
+    if t_hbm >= t_mfma:
+        roof = {"bound": "hbm", "achieved": round(gemm_gbs, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(gemm_gbs / HBM_PEAK_GBS, 4)}
+    else:
+        roof = {"bound": "mfma", "achieved": round(gemm_tflops, 1), "peak": MFMA_F16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(gemm_tflops / MFMA_F16_PEAK_TFLOPS, 4)}
+    roof.update({"traffic": None, "kernel": kernel, "algorithmic_bytes_per_launch": gemm_bytes,
+                 "algorithmic_flops_per_launch": flops,
+                 "us_per_launch": round(ms_gemm * 1e3, 3),
+                 "hbm_frac": round(gemm_gbs / HBM_PEAK_GBS, 4),
+                 "mfma_frac": round(gemm_tflops / MFMA_F16_PEAK_TFLOPS, 4)})
+    out = {
+        "metric": "achieved HBM GB/s and % of roofline, block-quantized GEMV with many activation "
+                  "vectors (matrix cores)",
+        "value": round(achieved, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8xq4k",
+        "data": "synthetic",
+        "config": {"workload": "%s W %d x %d, %d vectors, cold weights (%d rotating copies)" % (
+                       FORMAT_NAMES[wl.wtype], rows, cols, nvec, copies),
+                   "name": wl.name, "rows": rows, "cols": cols, "nvec": nvec,
+                   "weight_bytes": wbytes,
+                   "workspace_bytes": qg.qgemv_workspace_bytes(wl.wtype, rows, cols, nvec)},
+        "us_per_step": round(ms_step * 1e3, 3),
+        "us_per_step_distribution": dist,
+        "us_per_gemm": round(ms_gemm * 1e3, 3),
+        "us_per_gemm_host_launched": round(ms_gemm_events * 1e3, 3),
+        "gemm_gbs": round(gemm_gbs, 1),
+        "gemm_tflops": round(gemm_tflops, 2),
+        "roofline_floor_us": {"hbm": round(t_hbm * 1e6, 2), "mfma_f16": round(t_mfma * 1e6, 2)},
+        "eight_vector_kernel": {"us_for_all_vectors": round(ms_eight * 1e3, 3),
+                                "launches": (nvec + 7) // 8,
+                                "speedup_of_matrix_cores": round(ms_eight / ms_gemm, 2)},
+        "roofline": roof,
+        "setup_s": round(setup_s, 1),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds, y.cpu().numpy(),
+                                           max_rows=max(512, 32768 * 8 // nvec))
+    return out
+
+
 def main():
     args = parse()
     if args.summarize_traffic:
@@ -690,6 +822,11 @@ def main():
     import block_quantized_weight_act_amd as qg
 
     wl = synth.WORKLOADS[args.workload]
+    if args.nvec:
+        wl = dataclasses.replace(wl, nvec=args.nvec, name="%s_n%d" % (wl.name, args.nvec))
+    if wl.nvec > 8:
+        print(json.dumps(bench_many(args, wl)), flush=True)
+        return
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     t_setup = time.perf_counter()

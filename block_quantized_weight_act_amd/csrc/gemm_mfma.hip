@@ -14,14 +14,16 @@
 //    float32 result is exactly 2^-24 * sc * P with P = sum of q * xq. The factor 2^24 goes into
 //    the super-scale d, so the only float work per output and block is one fma with the
 //    activation scale; d is applied once per super-block.
-//  * The min term dmin * m * xd * S (S = sum of the block's codes) is one fma per output and
-//    block with T = xd * S prepared per vector.
+//  * The min term dmin * m * xd * S (S = sum of the block's codes) is a contraction over the
+//    blocks of dmin * m (row, block) with -xd * S (block, vector), done on the float32 matrix
+//    cores (v_mfma_f32_32x32x2f32, two blocks per instruction) straight into the accumulator.
 //
 // Work split: a workgroup of 4 waves takes 128 rows; each wave 32 rows (the MFMA's M) and every
 // vector of its group (nt tiles of 32 vectors, the MFMA's N) over one column split. Per
 // super-block the workgroup converts the group's codes for 256 columns to fp16 in LDS once
-// (shared by the four waves) with T = xd * S; each wave loads its rows' codes (64 contiguous
-// bytes per lane) and headers straight from HBM one super-block ahead.
+// (shared by the four waves) with -xd * S; every load of the next super-block (each wave's
+// codes, 64 contiguous bytes per lane, and headers straight from HBM; the activation pieces)
+// goes out before the current one's arithmetic.
 //
 // Lane layout of the 32x32x16 fp16 MFMA (checked on gfx950): lane l holds operand slots
 // k = 8 (l / 32) .. + 7 of row (A) or column (B) l % 32, and result element i of row
@@ -75,7 +77,6 @@ template <int NT, bool DBG>
 __global__ void __launch_bounds__(256) gemm_q4k_mfma_kernel(GemmArgs a) {
     __shared__ __attribute__((aligned(16))) _Float16 act[NT * 32 * kActStride];
     __shared__ __attribute__((aligned(16))) float2 xdt[8 * NT * 32];     // (xd, -xd * S)
-    __shared__ __attribute__((aligned(16))) float cm[4][8 * 32];         // dmin * m per wave
     __shared__ __attribute__((aligned(16))) float dd[4][32];             // d * 2^24 per wave
 
     const int tid = threadIdx.x;
@@ -95,17 +96,40 @@ __global__ void __launch_bounds__(256) gemm_q4k_mfma_kernel(GemmArgs a) {
     const int64_t nblocks = static_cast<int64_t>(rows) * nb;
     const uint8_t *codes = a.w + (static_cast<int64_t>(arow) * nb) * 128 + 64 * h;
     const uint8_t *hdrs = a.w + nblocks * 128 + (static_cast<int64_t>(arow) * nb) * 16;
+    // staging: thread -> (vector tid / 16 + 16 r, 16-byte piece tid % 16) in round r
+    const int sp = tid & 15;
+    const int sv = tid >> 4;
 
-    float acc[NT][16], t1[NT][16];
+    float16v_t acc[NT];
+    float t1[NT][16];
 #pragma unroll
     for (int t = 0; t < NT; t++)
 #pragma unroll
-        for (int i = 0; i < 16; i++) acc[t][i] = t1[t][i] = 0.0f;
+        for (int i = 0; i < 16; i++) {
+            acc[t][i] = 0.0f;
+            t1[t][i] = 0.0f;
+        }
 
-    uint4 c[4], hdr;
+    // loads of one super-block: this lane's codes and header, this thread's activation pieces
+    uint4 c[4], hdr, xqr[2 * NT];
+    float xdr[2 * NT];
+    auto issue = [&](int sb) {
 #pragma unroll
-    for (int k = 0; k < 4; k++) c[k] = load16_stream(codes + static_cast<int64_t>(sb0) * 128 + 16 * k);
-    hdr = load16(hdrs + static_cast<int64_t>(sb0) * 16);
+        for (int k = 0; k < 4; k++)
+            c[k] = load16_stream(codes + static_cast<int64_t>(sb) * 128 + 16 * k);
+        hdr = load16(hdrs + static_cast<int64_t>(sb) * 16);
+#pragma unroll
+        for (int rnd = 0; rnd < 2 * NT; rnd++) {
+            const int tok = tok0 + rnd * 16 + sv;
+            xqr[rnd] = make_uint4(0u, 0u, 0u, 0u);
+            xdr[rnd] = 0.0f;
+            if (tok < nvec) {
+                xqr[rnd] = load16(a.xq + static_cast<int64_t>(tok) * cols + sb * 256 + 16 * sp);
+                if ((sp & 1) == 0) xdr[rnd] = a.xd[static_cast<int64_t>(tok) * nbk + sb * 8 + (sp >> 1)];
+            }
+        }
+    };
+    issue(sb0);
 
     for (int sb = sb0; sb < sb1; sb++) {
         // ---- this super-block's weights: codes to (dword 2h, 2h + 1) of every chunk ----
@@ -121,54 +145,50 @@ __global__ void __launch_bounds__(256) gemm_q4k_mfma_kernel(GemmArgs a) {
             bw[k + 4] = y1;
         }
         uint32_t sc[8];
-        const float d = half_to_float(hdr.x & 0xFFFFu);
-        const float dmin = half_to_float(hdr.x >> 16);
+        float cmin[4];      // dmin * m of blocks h, h + 2, h + 4, h + 6 of this lane's row
+        {
+            const float d = half_to_float(hdr.x & 0xFFFFu);
+            const float dmin = half_to_float(hdr.x >> 16);
 #pragma unroll
-        for (int j = 0; j < 8; j++)
-            sc[j] = ((hdr.y >> (8 * (j / 2) + 4 * (j % 2))) & 0xFu) |
-                    (((hdr.w >> (8 * (j / 4) + 2 * (j % 4))) & 3u) << 4);
+            for (int j = 0; j < 8; j++)
+                sc[j] = ((hdr.y >> (8 * (j / 2) + 4 * (j % 2))) & 0xFu) |
+                        (((hdr.w >> (8 * (j / 4) + 2 * (j % 4))) & 3u) << 4);
 #pragma unroll
-        for (int jj = 0; jj < 4; jj++) {
-            const int j = 4 * h + jj;
-            const uint32_t m = ((hdr.z >> (8 * (j / 2) + 4 * (j % 2))) & 0xFu) |
-                               (((hdr.w >> (16 + 8 * (j / 4) + 2 * (j % 4))) & 3u) << 4);
-            cm[wave][j * 32 + l32] = dmin * static_cast<float>(m);
-        }
-        if (h == 0) dd[wave][l32] = d * 16777216.0f;
-
-        // ---- next super-block's loads go out now, to land during this one's work ----
-        if (sb + 1 < sb1) {
-#pragma unroll
-            for (int k = 0; k < 4; k++)
-                c[k] = load16_stream(codes + static_cast<int64_t>(sb + 1) * 128 + 16 * k);
-            hdr = load16(hdrs + static_cast<int64_t>(sb + 1) * 16);
+            for (int pp = 0; pp < 4; pp++) {
+                // block 2 pp + h: low nibble of byte pp of the m field, high bits of byte
+                // 14 + pp / 2 at bit 4 (pp % 2) + 2 h
+                const uint32_t m = ((hdr.z >> (8 * pp + 4 * h)) & 0xFu) |
+                                   (((hdr.w >> (16 + 8 * (pp / 2) + 4 * (pp % 2) + 2 * h)) & 3u) << 4);
+                cmin[pp] = dmin * static_cast<float>(m);
+            }
+            if (h == 0) dd[wave][l32] = d * 16777216.0f;
         }
 
         // ---- the group's activation codes for these 256 columns, to fp16 in LDS ----
 #pragma unroll
         for (int rnd = 0; rnd < 2 * NT; rnd++) {
-            const int v = rnd * 16 + (tid >> 4);
-            const int p = tid & 15;
-            const int tok = tok0 + v;
-            uint4 q = make_uint4(0u, 0u, 0u, 0u);
-            if (tok < nvec) q = load16(a.xq + static_cast<int64_t>(tok) * cols + sb * 256 + 16 * p);
+            const int v = rnd * 16 + sv;
+            const uint4 q = xqr[rnd];
             int s = byte_sum(q.x, byte_sum(q.y, byte_sum(q.z, byte_sum(q.w, 0))));
             s += __builtin_amdgcn_update_dpp(0, s, kDppXor1, 0xF, 0xF, false);
             const uint32_t fx = q.x ^ 0x80808080u, fy = q.y ^ 0x80808080u;
             const uint32_t fz = q.z ^ 0x80808080u, fw = q.w ^ 0x80808080u;
-            uint4 *dst = reinterpret_cast<uint4 *>(act + v * kActStride + 16 * p);
+            uint4 *dst = reinterpret_cast<uint4 *>(act + v * kActStride + 16 * sp);
             dst[0] = make_uint4(codes_to_half2<0>(fx), codes_to_half2<8>(fx), codes_to_half2<0>(fy),
                                 codes_to_half2<8>(fy));
             dst[1] = make_uint4(codes_to_half2<0>(fz), codes_to_half2<8>(fz), codes_to_half2<0>(fw),
                                 codes_to_half2<8>(fw));
-            if ((p & 1) == 0) {
-                const int j = p >> 1;
-                const float x = tok < nvec ? a.xd[static_cast<int64_t>(tok) * nbk + sb * 8 + j] : 0.0f;
+            if ((sp & 1) == 0) {
+                const int j = sp >> 1;
+                const float x = xdr[rnd];
                 xdt[j * NT * 32 + v] = make_float2(x, -(x * static_cast<float>(s)));
+                const int tok = tok0 + v;
                 if (DBG && blockIdx.x == 0 && tok < nvec)
                     a.S[static_cast<int64_t>(tok) * nbk + sb * 8 + j] = s;
             }
         }
+        // ---- the next super-block's loads go out now, to land during this one's work ----
+        if (sb + 1 < sb1) issue(sb + 1);
         __syncthreads();
 
         // ---- eight 32-column blocks ----
@@ -180,29 +200,17 @@ __global__ void __launch_bounds__(256) gemm_q4k_mfma_kernel(GemmArgs a) {
                                         nib_times<0>(wb, scp), nib_times<8>(wb, scp));
             const half8_t A1 = as_half8(nib_times<4>(wa, scp), nib_times<12>(wa, scp),
                                         nib_times<4>(wb, scp), nib_times<12>(wb, scp));
-            float cmv[16];
-#pragma unroll
-            for (int qq = 0; qq < 4; qq++) {
-                const float4 f = *reinterpret_cast<const float4 *>(&cm[wave][j * 32 + 8 * qq + 4 * h]);
-                cmv[4 * qq] = f.x;
-                cmv[4 * qq + 1] = f.y;
-                cmv[4 * qq + 2] = f.z;
-                cmv[4 * qq + 3] = f.w;
-            }
 #pragma unroll
             for (int t = 0; t < NT; t++) {
                 const _Float16 *brow = act + (t * 32 + l32) * kActStride + 32 * j + 8 * h;
                 const half8_t B0 = *reinterpret_cast<const half8_t *>(brow);
                 const half8_t B1 = *reinterpret_cast<const half8_t *>(brow + 16);
-                const float2 xt = xdt[j * NT * 32 + t * 32 + l32];
+                const float xs = xdt[j * NT * 32 + t * 32 + l32].x;
                 const float16v_t zero = {};
                 float16v_t Q = __builtin_amdgcn_mfma_f32_32x32x16_f16(A0, B0, zero, 0, 0, 0);
                 Q = __builtin_amdgcn_mfma_f32_32x32x16_f16(A1, B1, Q, 0, 0, 0);
 #pragma unroll
-                for (int i = 0; i < 16; i++) {
-                    t1[t][i] = fmaf(xt.x, Q[i], t1[t][i]);
-                    acc[t][i] = fmaf(cmv[i], xt.y, acc[t][i]);
-                }
+                for (int i = 0; i < 16; i++) t1[t][i] = fmaf(xs, Q[i], t1[t][i]);
                 if (DBG) {
                     const half8_t U0 = as_half8(nib<0>(wa), nib<8>(wa), nib<0>(wb), nib<8>(wb));
                     const half8_t U1 = as_half8(nib<4>(wa), nib<12>(wa), nib<4>(wb), nib<12>(wb));
@@ -219,6 +227,15 @@ __global__ void __launch_bounds__(256) gemm_q4k_mfma_kernel(GemmArgs a) {
                 }
             }
         }
+        // ---- the min terms of the eight blocks on the float32 matrix cores: two blocks per
+        //      32x32x2 product, A = dmin * m (row, block), B = -xd * S (block, vector) ----
+#pragma unroll
+        for (int pp = 0; pp < 4; pp++)
+#pragma unroll
+            for (int t = 0; t < NT; t++) {
+                const float tb = xdt[(2 * pp + h) * NT * 32 + t * 32 + l32].y;
+                acc[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(cmin[pp], tb, acc[t], 0, 0, 0);
+            }
         float ddv[16];
 #pragma unroll
         for (int qq = 0; qq < 4; qq++) {

@@ -179,6 +179,11 @@ WORKLOADS = {
                                 1005, 2700, outlier_frac=0.01, seed_rows=3005),
     "q80_262144x1536": Workload("q80_262144x1536", "q80", 262144, 1536, 1, 1006, 2800,
                                 outlier_frac=0.01, seed_rows=3006),
+    # many vectors at once (tokens verified or prefilled together) on the matrices above:
+    # vector v has activation seed 3100 + v (resp. 3400 + v)
+    "q4k_262144x1536_b64": Workload("q4k_262144x1536_b64", "q4k", 262144, 1536, 64, 1003, 3100,
+                                    outlier_frac=0.01, seed_rows=3003),
+    "q4k_16384x2048_b64": Workload("q4k_16384x2048_b64", "q4k", 16384, 2048, 64, 1004, 3400),
 }
 
 
