@@ -85,7 +85,8 @@ def _load():
         "qgemv_q4k": (ctypes.c_int, [vp, vp, vp, vp, i64, i64, vp, sz, vp]),
         "qgemv_q6k": (ctypes.c_int, [vp, vp, vp, vp, i64, i64, vp, sz, vp]),
         "qgemv_batch": (ctypes.c_int, [ctypes.c_int, vp, vp, vp, vp, i64, i64, i32, vp, sz, vp]),
-        "qgemv_debug_partials": (ctypes.c_int, [ctypes.c_int, vp, vp, vp, vp, vp, i64, i64, i32, vp]),
+        "qgemv_debug_partials": (ctypes.c_int, [ctypes.c_int, vp, vp, vp, vp, vp, i64, i64, i32, vp,
+                                                sz, vp]),
         "qgemv_quantize_weights": (ctypes.c_int, [ctypes.c_int, vp, vp, i64, i64, vp]),
         "qgemv_quantize_weights_rows": (ctypes.c_int, [ctypes.c_int, vp, vp, i64, i64, i64, i64, vp]),
         "qgemv_fused_launches": (ctypes.c_int, [ctypes.c_int, i64, i64, i32, ctypes.c_int]),
@@ -279,12 +280,13 @@ def qgemv_multi_fused(mats, x, cols: int, nvec: int = 1, xq_out=None, xd_out=Non
 
 
 def qgemv_debug_partials(wtype, w, xq, xd, P, S, rows: int, cols: int, nvec: int = 1,
-                         stream=None) -> None:
+                         workspace=None, stream=None) -> None:
     lib = _load()
+    wsp, wsb = _ws(workspace)
     _check("qgemv_debug_partials", lib.qgemv_debug_partials(
         _wtype(wtype), _ptr(w, name="w"), _ptr(xq, torch.int8, "xq"),
         _ptr(xd, torch.float32, "xd"), _ptr(P, torch.int32, "P"), _ptr(S, torch.int32, "S"),
-        rows, cols, nvec, _stream(stream, P)))
+        rows, cols, nvec, wsp, wsb, _stream(stream, P)))
 
 
 def qgemv_quantize_weights(wtype, w, out, rows: int, cols: int, stream=None) -> None:

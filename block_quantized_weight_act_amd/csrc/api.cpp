@@ -299,8 +299,14 @@ McPlan make_mc_plan(int64_t rows, int64_t cols, int32_t nvec) {
     return p;
 }
 
-size_t mc_ws_bytes(const McPlan &p, int64_t rows, int32_t nvec) {
-    return p.splits > 1 ? static_cast<size_t>(p.splits) * nvec * rows * sizeof(float) : 0;
+// Workspace of the matrix-core path: the staged tiles, then (when split) the partial outputs.
+size_t mc_tiles_bytes(const McPlan &p, int64_t cols) {
+    return static_cast<size_t>(cols / kQK) * p.groups * mc_tile_bytes(p.nt);
+}
+
+size_t mc_ws_bytes(const McPlan &p, int64_t rows, int64_t cols, int32_t nvec) {
+    const size_t parts = p.splits > 1 ? static_cast<size_t>(p.splits) * nvec * rows * sizeof(float) : 0;
+    return mc_tiles_bytes(p, cols) + parts;
 }
 
 int run_mc(const void *w, const int8_t *xq, const float *xd, float *y, int32_t *P, int32_t *S,
@@ -316,34 +322,40 @@ int run_mc(const void *w, const int8_t *xq, const float *xd, float *y, int32_t *
     const size_t yb = static_cast<size_t>(nvec) * rows * sizeof(float);
     if (y && (overlaps(y, yb, w, wb) || overlaps(y, yb, xq, qb) || overlaps(y, yb, xd, db)))
         return QGEMV_EINVAL;
-    const McPlan p = make_mc_plan(rows, cols, nvec);
-    const size_t need = debug ? 0 : mc_ws_bytes(p, rows, nvec);
-    if (need > 0) {
-        if (!ws || ws_bytes < need) return QGEMV_EWORKSPACE;
-        if (!aligned(ws, 4)) return QGEMV_EALIGN;
-        if (overlaps(ws, need, w, wb) || overlaps(ws, need, y, yb) || overlaps(ws, need, xq, qb) ||
-            overlaps(ws, need, xd, db))
-            return QGEMV_EINVAL;
+    McPlan p = make_mc_plan(rows, cols, nvec);
+    if (debug) p.splits = 1;    // the debug form covers every super-block in one split
+    const size_t tb = mc_tiles_bytes(p, cols);
+    const size_t need = mc_ws_bytes(p, rows, cols, nvec);
+    if (!ws || ws_bytes < need) return QGEMV_EWORKSPACE;
+    if (!aligned(ws, 16)) return QGEMV_EALIGN;
+    if (overlaps(ws, need, w, wb) || (y && overlaps(ws, need, y, yb)) || overlaps(ws, need, xq, qb) ||
+        overlaps(ws, need, xd, db))
+        return QGEMV_EINVAL;
+    if (debug) {
+        const size_t pb = static_cast<size_t>(nvec) * rows * (cols / 32) * sizeof(int32_t);
+        const size_t sbb = static_cast<size_t>(nvec) * (cols / 32) * sizeof(int32_t);
+        if (overlaps(ws, need, P, pb) || overlaps(ws, need, S, sbb)) return QGEMV_EINVAL;
     }
     GemmArgs a{};
     a.w = static_cast<const uint8_t *>(w);
     a.xq = xq;
     a.xd = xd;
-    a.out = need > 0 ? static_cast<float *>(ws) : y;
+    a.tiles = static_cast<uint8_t *>(ws);
+    float *parts = reinterpret_cast<float *>(static_cast<uint8_t *>(ws) + tb);
+    a.out = p.splits > 1 ? parts : y;
     a.P = P;
     a.S = S;
     a.rows = static_cast<int32_t>(rows);
     a.nb = static_cast<int32_t>(cols / kQK);
     a.nvec = nvec;
-    a.sb_per_split = p.sbps;
-    // the debug form covers every super-block in one split (its stores need no reduction)
-    if (debug) a.sb_per_split = a.nb;
-    hipError_t e = launch_gemm_q4k_mfma(a, p.nt, p.row_tiles, p.groups, debug ? 1 : p.splits,
-                                        debug, stream);
+    a.sb_per_split = debug ? a.nb : p.sbps;
+    a.row_tiles = p.row_tiles;
+    a.groups = p.groups;
+    a.splits = p.splits;
+    hipError_t e = launch_gemm_q4k_mfma(a, p.nt, p.row_tiles, p.groups, p.splits, debug, stream);
     if (e != hipSuccess) return hip_fail(e);
-    if (need > 0) {
-        e = launch_splitk_reduce(static_cast<const float *>(ws), y, static_cast<int64_t>(nvec) * rows,
-                                 p.splits, stream);
+    if (!debug && p.splits > 1) {
+        e = launch_splitk_reduce(parts, y, static_cast<int64_t>(nvec) * rows, p.splits, stream);
         if (e != hipSuccess) return hip_fail(e);
     }
     return QGEMV_OK;
@@ -482,7 +494,7 @@ int qgemv_quantize_act(const float *x, int8_t *xq, float *xd, int64_t cols, int3
 
 size_t qgemv_workspace_bytes(int wtype, int64_t rows, int64_t cols, int32_t nvec) {
     if (mc_shape_ok(wtype, rows, cols, nvec))
-        return mc_ws_bytes(make_mc_plan(rows, cols, nvec), rows, nvec);
+        return mc_ws_bytes(make_mc_plan(rows, cols, nvec), rows, cols, nvec);
     if (!shape_ok_t(wtype, rows, cols, nvec)) return 0;
     return plan_ws_bytes(make_plan(wtype, rows, cols, nvec), rows, cols, nvec);
 }
@@ -628,7 +640,7 @@ int qgemv_q6k(const void *w, const int8_t *xq, const float *xd, float *y, int64_
 
 int qgemv_debug_partials(int wtype, const void *w, const int8_t *xq, const float *xd,
                          int32_t *P, int32_t *S, int64_t rows, int64_t cols, int32_t nvec,
-                         hipStream_t stream) {
+                         void *workspace, size_t workspace_bytes, hipStream_t stream) {
     if (!P || !S) return QGEMV_EINVAL;
     if (mc_shape_ok(wtype, rows, cols, nvec)) {
         const size_t pbytes = static_cast<size_t>(nvec) * rows * (cols / 32) * sizeof(int32_t);
@@ -641,7 +653,8 @@ int qgemv_debug_partials(int wtype, const void *w, const int8_t *xq, const float
             overlaps(P, pbytes, xq, qb) || overlaps(P, pbytes, xd, db) ||
             overlaps(S, sbytes, w, wb) || overlaps(S, sbytes, xq, qb) || overlaps(S, sbytes, xd, db))
             return QGEMV_EINVAL;
-        return run_mc(w, xq, xd, nullptr, P, S, rows, cols, nvec, nullptr, 0, stream);
+        return run_mc(w, xq, xd, nullptr, P, S, rows, cols, nvec, workspace, workspace_bytes,
+                      stream);
     }
     const int64_t nsub = wtype == QGEMV_Q6K ? cols / 16 : cols / 32;
     const size_t pbytes = static_cast<size_t>(nvec) * rows * nsub * sizeof(int32_t);

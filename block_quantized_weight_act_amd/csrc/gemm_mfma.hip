@@ -31,6 +31,9 @@
 // each (lane half, slot) stands for, as long as A and B agree; here, within each group of 8
 // columns, slots 0..7 hold columns 0, 2, 1, 3, 4, 6, 5, 7 (the order the nibbles and bytes come
 // out of a 32-bit word with two masks).
+#include <algorithm>
+#include <type_traits>
+
 #include "device_common.h"
 #include "qgemv_internal.h"
 
@@ -42,8 +45,6 @@ typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef float float16v_t __attribute__((ext_vector_type(16)));
 typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
-
-constexpr int kActStride = 264;   // fp16 per staged activation row: 256 columns + 8 (banks)
 
 // Two signed bytes (bytes 0 and 2 of w, or 1 and 3 with shift 8) -> two exact fp16 values:
 // the pattern 0x6600 + xq is the fp16 1536 + xq (ulp 1 in [1024, 2048)); subtracting 1536 in
@@ -69,15 +70,104 @@ __device__ __forceinline__ uint32_t nib(uint32_t w) {
     return (w >> SHIFT) & 0x000F000Fu;
 }
 
+// 16 bytes from global memory straight into LDS (global_load_lds_dwordx4): lane l of the wave
+// writes the 16 bytes at lds + 16 l; lds is the same for the whole wave (it goes in M0). The
+// instruction is issued from inline assembly so that the compiler does not see an LDS write
+// in flight: seeing one, it waits for every outstanding load before each LDS read, which
+// would wait for the next super-block's loads too. The kernel waits for these copies
+// explicitly (vmcnt) before the barrier that publishes them. Loads complete in order, so the
+// compiler's own vmcnt waits, which do not count these copies, stay correct (only more
+// conservative).
+__device__ __forceinline__ void copy16_to_lds(const void *src, const void *lds) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    const uint32_t base =
+        __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds)));
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+                 :
+                 : "s"(base), "v"(src)
+                 : "memory", "m0");
+#endif
+}
+
 __device__ __forceinline__ half8_t as_half8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
     return __builtin_bit_cast(half8_t, make_uint4(a, b, c, d));
 }
 
+// s_waitcnt immediate: no vector-memory load outstanding, the other counters not waited for
+// (vmcnt bits 3:0 and 15:14, expcnt 6:4 at its maximum 7, lgkmcnt 11:8 at its maximum 15).
+constexpr int kWaitVm0 = (7 << 4) | (15 << 8);
+
+// Bytes of one staged tile (one super-block of one vector group): the fp16 codes of 32 * NT
+// vectors x 256 columns (512 bytes per vector), then (xd, -xd * S) for 8 blocks x the vectors.
+template <int NT>
+constexpr int tile_bytes() {
+    return NT * 32 * 512 + 8 * NT * 32 * 8;
+}
+
+// Pre-pass: the activation codes of every (super-block, vector group) converted once to the
+// fp16 image the main kernel copies into LDS. In a vector's 512 bytes, the 16-byte piece p
+// (columns 8p .. 8p + 7 in the slot order above) sits at slot p ^ (vector % 32), so the 32
+// vectors of a matrix-core operand read 32 different bank groups.
+template <int NT, bool DBG>
+__global__ void __launch_bounds__(256) mc_stage_kernel(GemmArgs a) {
+    const int tid = threadIdx.x;
+    const int sp = tid & 15;
+    const int sv = tid >> 4;
+    const int sb = blockIdx.x;
+    const int nb = a.nb, nvec = a.nvec;
+    const int64_t cols = static_cast<int64_t>(nb) * 256;
+    const int nbk = nb * 8;
+    const int tok0 = blockIdx.y * NT * 32;
+    uint8_t *tile = a.tiles + (static_cast<int64_t>(sb) * gridDim.y + blockIdx.y) * tile_bytes<NT>();
+    float2 *xdt = reinterpret_cast<float2 *>(tile + NT * 32 * 512);
+#pragma unroll
+    for (int rnd = 0; rnd < 2 * NT; rnd++) {
+        const int v = rnd * 16 + sv;
+        const int tok = tok0 + v;
+        uint4 q = make_uint4(0u, 0u, 0u, 0u);
+        float x = 0.0f;
+        if (tok < nvec) {
+            q = load16(a.xq + static_cast<int64_t>(tok) * cols + sb * 256 + 16 * sp);
+            x = a.xd[static_cast<int64_t>(tok) * nbk + sb * 8 + (sp >> 1)];
+        }
+        int s = byte_sum(q.x, byte_sum(q.y, byte_sum(q.z, byte_sum(q.w, 0))));
+        s += __builtin_amdgcn_update_dpp(0, s, kDppXor1, 0xF, 0xF, false);
+        const uint32_t fx = q.x ^ 0x80808080u, fy = q.y ^ 0x80808080u;
+        const uint32_t fz = q.z ^ 0x80808080u, fw = q.w ^ 0x80808080u;
+        uint8_t *row = tile + v * 512;
+        const int sw = v & 31;
+        *reinterpret_cast<uint4 *>(row + 16 * ((2 * sp) ^ sw)) =
+            make_uint4(codes_to_half2<0>(fx), codes_to_half2<8>(fx), codes_to_half2<0>(fy),
+                       codes_to_half2<8>(fy));
+        *reinterpret_cast<uint4 *>(row + 16 * ((2 * sp + 1) ^ sw)) =
+            make_uint4(codes_to_half2<0>(fz), codes_to_half2<8>(fz), codes_to_half2<0>(fw),
+                       codes_to_half2<8>(fw));
+        if ((sp & 1) == 0) {
+            const int j = sp >> 1;
+            xdt[j * NT * 32 + v] = make_float2(x, -(x * static_cast<float>(s)));
+            if (DBG && tok < nvec) a.S[static_cast<int64_t>(tok) * nbk + sb * 8 + j] = s;
+        }
+    }
+}
+
+// One work item: a row tile (128 rows), a vector group (32 NT vectors), a column split.
+struct Item {
+    int wrow0;      // first row of this wave
+    int tok0;       // first vector of the group
+    int group;
+    int split;
+    int sb0, sb1;   // super-blocks of the split
+};
+
+// Persistent: the grid holds about as many workgroups as stay resident, and each takes items
+// blockIdx.x, blockIdx.x + gridDim.x, ... (split fastest, then group, then row tile). The load
+// pipeline runs on across items: the next item's first super-block is loaded while the current
+// item's last one is computed.
 template <int NT, bool DBG>
 __global__ void __launch_bounds__(256) gemm_q4k_mfma_kernel(GemmArgs a) {
-    __shared__ __attribute__((aligned(16))) _Float16 act[NT * 32 * kActStride];
-    __shared__ __attribute__((aligned(16))) float2 xdt[8 * NT * 32];     // (xd, -xd * S)
-    __shared__ __attribute__((aligned(16))) float dd[4][32];             // d * 2^24 per wave
+    constexpr int TB = tile_bytes<NT>();
+    __shared__ __attribute__((aligned(16))) uint8_t lds[2][TB];   // staged tiles, two in flight
+    __shared__ __attribute__((aligned(16))) float dd[4][32];      // d * 2^24 per wave
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -85,210 +175,281 @@ __global__ void __launch_bounds__(256) gemm_q4k_mfma_kernel(GemmArgs a) {
     const int l32 = lane & 31;
     const int h = lane >> 5;
     const int rows = a.rows, nb = a.nb, nvec = a.nvec;
-    const int64_t cols = static_cast<int64_t>(nb) * 256;
     const int nbk = nb * 8;                           // 32-column blocks per row
-    const int tok0 = blockIdx.y * NT * 32;
-    const int sb0 = blockIdx.z * a.sb_per_split;
-    const int sb1 = min(nb, sb0 + a.sb_per_split);
-    const int wrow0 = blockIdx.x * kMcRows + wave * 32;
-    // this lane's weight row (A operand), clamped so the last tile's loads stay in bounds
-    const int arow = min(wrow0 + l32, rows - 1);
+    const int groups = a.groups, splits = a.splits;
+    const int items = a.row_tiles * groups * splits;
     const int64_t nblocks = static_cast<int64_t>(rows) * nb;
-    const uint8_t *codes = a.w + (static_cast<int64_t>(arow) * nb) * 128 + 64 * h;
-    const uint8_t *hdrs = a.w + nblocks * 128 + (static_cast<int64_t>(arow) * nb) * 16;
-    // staging: thread -> (vector tid / 16 + 16 r, 16-byte piece tid % 16) in round r
-    const int sp = tid & 15;
-    const int sv = tid >> 4;
+    const int64_t tile_stride = static_cast<int64_t>(groups) * TB;
 
-    float16v_t acc[NT];
-    float t1[NT][16];
-#pragma unroll
-    for (int t = 0; t < NT; t++)
-#pragma unroll
-        for (int i = 0; i < 16; i++) {
-            acc[t][i] = 0.0f;
-            t1[t][i] = 0.0f;
-        }
-
-    // loads of one super-block: this lane's codes and header, this thread's activation pieces
-    uint4 c[4], hdr, xqr[2 * NT];
-    float xdr[2 * NT];
-    auto issue = [&](int sb) {
-#pragma unroll
-        for (int k = 0; k < 4; k++)
-            c[k] = load16_stream(codes + static_cast<int64_t>(sb) * 128 + 16 * k);
-        hdr = load16(hdrs + static_cast<int64_t>(sb) * 16);
-#pragma unroll
-        for (int rnd = 0; rnd < 2 * NT; rnd++) {
-            const int tok = tok0 + rnd * 16 + sv;
-            xqr[rnd] = make_uint4(0u, 0u, 0u, 0u);
-            xdr[rnd] = 0.0f;
-            if (tok < nvec) {
-                xqr[rnd] = load16(a.xq + static_cast<int64_t>(tok) * cols + sb * 256 + 16 * sp);
-                if ((sp & 1) == 0) xdr[rnd] = a.xd[static_cast<int64_t>(tok) * nbk + sb * 8 + (sp >> 1)];
-            }
-        }
+    auto item_of = [&](int it) {
+        Item m;
+        m.split = it % splits;
+        const int rest = it / splits;
+        m.group = rest % groups;
+        m.wrow0 = (rest / groups) * kMcRows + wave * 32;
+        m.tok0 = m.group * NT * 32;
+        m.sb0 = m.split * a.sb_per_split;
+        m.sb1 = min(nb, m.sb0 + a.sb_per_split);
+        return m;
     };
-    issue(sb0);
+    // this lane's weight row (A operand), clamped so the last tile's loads stay in bounds
+    auto codes_of = [&](const Item &m) {
+        const int arow = min(m.wrow0 + l32, rows - 1);
+        return a.w + (static_cast<int64_t>(arow) * nb) * 128 + 64 * h;
+    };
+    auto hdrs_of = [&](const Item &m) {
+        const int arow = min(m.wrow0 + l32, rows - 1);
+        return a.w + nblocks * 128 + (static_cast<int64_t>(arow) * nb) * 16;
+    };
 
-    for (int sb = sb0; sb < sb1; sb++) {
-        // ---- this super-block's weights: codes to (dword 2h, 2h + 1) of every chunk ----
-        uint32_t aw[8], bw[8];
+    // The next super-block's weights (registers) and staged tile (the other LDS buffer) are
+    // loaded while the current one is computed; the tile copies go out first, and the barrier
+    // waits for every load of the current super-block.
+    uint4 c[4], hdr;
+    auto issue_weights = [&](const uint8_t *codes, const uint8_t *hdrs, int sb) {
 #pragma unroll
-        for (int k = 0; k < 4; k++) {
-            const auto rx = __builtin_amdgcn_permlane32_swap(c[k].x, c[k].z, false, false);
-            const auto ry = __builtin_amdgcn_permlane32_swap(c[k].y, c[k].w, false, false);
-            const uint32_t x0 = rx[0], x1 = rx[1], y0 = ry[0], y1 = ry[1];
-            aw[k] = x0;
-            aw[k + 4] = x1;
-            bw[k] = y0;
-            bw[k + 4] = y1;
-        }
-        uint32_t sc[8];
-        float cmin[4];      // dmin * m of blocks h, h + 2, h + 4, h + 6 of this lane's row
-        {
-            const float d = half_to_float(hdr.x & 0xFFFFu);
-            const float dmin = half_to_float(hdr.x >> 16);
+        for (int k = 0; k < 4; k++) c[k] = load16(codes + static_cast<int64_t>(sb) * 128 + 16 * k);
+        hdr = load16(hdrs + static_cast<int64_t>(sb) * 16);
+    };
+    // a super-block's staged tile into LDS buffer `buf` (1 KB per wave instruction)
+    auto issue_tile = [&](const Item &m, int sb, int buf) {
+        const uint8_t *src = a.tiles + static_cast<int64_t>(m.group) * TB + sb * tile_stride;
+        for (int k = wave; k < TB / 1024; k += 4)
+            copy16_to_lds(src + k * 1024 + lane * 16, &lds[buf][k * 1024]);
+    };
+
+    int it = blockIdx.x;
+    if (it >= items) return;
+    Item cur = item_of(it);
+    issue_weights(codes_of(cur), hdrs_of(cur), cur.sb0);
+    issue_tile(cur, cur.sb0, 0);
+    int buf = 0;
+
+    while (true) {
+        float16v_t acc[NT];
+        float t1[NT][16];
 #pragma unroll
-            for (int j = 0; j < 8; j++)
-                sc[j] = ((hdr.y >> (8 * (j / 2) + 4 * (j % 2))) & 0xFu) |
-                        (((hdr.w >> (8 * (j / 4) + 2 * (j % 4))) & 3u) << 4);
+        for (int t = 0; t < NT; t++)
 #pragma unroll
-            for (int pp = 0; pp < 4; pp++) {
-                // block 2 pp + h: low nibble of byte pp of the m field, high bits of byte
-                // 14 + pp / 2 at bit 4 (pp % 2) + 2 h
-                const uint32_t m = ((hdr.z >> (8 * pp + 4 * h)) & 0xFu) |
-                                   (((hdr.w >> (16 + 8 * (pp / 2) + 4 * (pp % 2) + 2 * h)) & 3u) << 4);
-                cmin[pp] = dmin * static_cast<float>(m);
+            for (int i = 0; i < 16; i++) acc[t][i] = 0.0f;
+        const int tok0 = cur.tok0, wrow0 = cur.wrow0;
+
+        for (int sb = cur.sb0; sb < cur.sb1; sb++) {
+            // ---- this super-block's weights: codes to (dword 2h, 2h + 1) of every chunk ----
+            uint32_t aw[8], bw[8];
+#pragma unroll
+            for (int k = 0; k < 4; k++) {
+                const auto rx = __builtin_amdgcn_permlane32_swap(c[k].x, c[k].z, false, false);
+                const auto ry = __builtin_amdgcn_permlane32_swap(c[k].y, c[k].w, false, false);
+                const uint32_t x0 = rx[0], x1 = rx[1], y0 = ry[0], y1 = ry[1];
+                aw[k] = x0;
+                aw[k + 4] = x1;
+                bw[k] = y0;
+                bw[k + 4] = y1;
             }
-            if (h == 0) dd[wave][l32] = d * 16777216.0f;
-        }
-
-        // ---- the group's activation codes for these 256 columns, to fp16 in LDS ----
+            const uint4 hd = hdr;
+            uint32_t sc[8];
+            float cmin[4];      // dmin * m of blocks h, h + 2, h + 4, h + 6 of this lane's row
+            {
+                const float d = half_to_float(hd.x & 0xFFFFu);
+                const float dmin = half_to_float(hd.x >> 16);
 #pragma unroll
-        for (int rnd = 0; rnd < 2 * NT; rnd++) {
-            const int v = rnd * 16 + sv;
-            const uint4 q = xqr[rnd];
-            int s = byte_sum(q.x, byte_sum(q.y, byte_sum(q.z, byte_sum(q.w, 0))));
-            s += __builtin_amdgcn_update_dpp(0, s, kDppXor1, 0xF, 0xF, false);
-            const uint32_t fx = q.x ^ 0x80808080u, fy = q.y ^ 0x80808080u;
-            const uint32_t fz = q.z ^ 0x80808080u, fw = q.w ^ 0x80808080u;
-            uint4 *dst = reinterpret_cast<uint4 *>(act + v * kActStride + 16 * sp);
-            dst[0] = make_uint4(codes_to_half2<0>(fx), codes_to_half2<8>(fx), codes_to_half2<0>(fy),
-                                codes_to_half2<8>(fy));
-            dst[1] = make_uint4(codes_to_half2<0>(fz), codes_to_half2<8>(fz), codes_to_half2<0>(fw),
-                                codes_to_half2<8>(fw));
-            if ((sp & 1) == 0) {
-                const int j = sp >> 1;
-                const float x = xdr[rnd];
-                xdt[j * NT * 32 + v] = make_float2(x, -(x * static_cast<float>(s)));
-                const int tok = tok0 + v;
-                if (DBG && blockIdx.x == 0 && tok < nvec)
-                    a.S[static_cast<int64_t>(tok) * nbk + sb * 8 + j] = s;
+                for (int j = 0; j < 8; j++)
+                    sc[j] = ((hd.y >> (8 * (j / 2) + 4 * (j % 2))) & 0xFu) |
+                            (((hd.w >> (8 * (j / 4) + 2 * (j % 4))) & 3u) << 4);
+#pragma unroll
+                for (int pp = 0; pp < 4; pp++) {
+                    // block 2 pp + h: low nibble of byte pp of the m field, high bits of byte
+                    // 14 + pp / 2 at bit 4 (pp % 2) + 2 h
+                    const uint32_t m = ((hd.z >> (8 * pp + 4 * h)) & 0xFu) |
+                                       (((hd.w >> (16 + 8 * (pp / 2) + 4 * (pp % 2) + 2 * h)) & 3u)
+                                        << 4);
+                    cmin[pp] = dmin * static_cast<float>(m);
+                }
+                if (h == 0) dd[wave][l32] = d * 16777216.0f;
             }
-        }
-        // ---- the next super-block's loads go out now, to land during this one's work ----
-        if (sb + 1 < sb1) issue(sb + 1);
-        __syncthreads();
-
-        // ---- eight 32-column blocks ----
+            // Everything this super-block needs from its loaded registers is computed now (the
+            // empty asm statements keep the compiler from recomputing it from them later), so
+            // the next loads can reuse those registers without copies.
 #pragma unroll
-        for (int j = 0; j < 8; j++) {
-            const uint32_t scp = sc[j] * 0x00010001u;
-            const uint32_t wa = aw[j], wb = bw[j];
-            const half8_t A0 = as_half8(nib_times<0>(wa, scp), nib_times<8>(wa, scp),
-                                        nib_times<0>(wb, scp), nib_times<8>(wb, scp));
-            const half8_t A1 = as_half8(nib_times<4>(wa, scp), nib_times<12>(wa, scp),
-                                        nib_times<4>(wb, scp), nib_times<12>(wb, scp));
+            for (int k = 0; k < 8; k++) asm volatile("" : "+v"(aw[k]), "+v"(bw[k]), "+v"(sc[k]));
+#pragma unroll
+            for (int pp = 0; pp < 4; pp++) asm volatile("" : "+v"(cmin[pp]));
+            // this super-block's tile has landed in every wave's part, and every wave is done
+            // with the buffer the next tile overwrites
+            __builtin_amdgcn_s_waitcnt(kWaitVm0);
+            __syncthreads();
+
+            // ---- the next loads: the next super-block of this item, else the first of the next
+            //      item of this workgroup (the weights unconditionally: without a next one they
+            //      reload the current super-block, unused; a conditional load would make the
+            //      register allocator copy the loaded registers, which waits for them) ----
+            {
+                const bool more = sb + 1 < cur.sb1;
+                const bool next_item = !more && it + static_cast<int>(gridDim.x) < items;
+                const Item nx = more ? cur : item_of(next_item ? it + gridDim.x : it);
+                const int nsb = more ? sb + 1 : (next_item ? nx.sb0 : sb);
+                if (more || next_item) issue_tile(nx, nsb, buf ^ 1);
+                // the fences keep the scheduler from sinking the loads into the arithmetic
+                __builtin_amdgcn_sched_barrier(0);
+                issue_weights(codes_of(nx), hdrs_of(nx), nsb);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+
+            const uint8_t *act = lds[buf];
+            const float2 *xdt = reinterpret_cast<const float2 *>(act + NT * 32 * 512);
+            // ---- eight 32-column blocks ----
+            auto product = [&](int j, float16v_t (&Q)[NT]) {
+                const uint32_t scp = sc[j] * 0x00010001u;
+                const uint32_t wa = aw[j], wb = bw[j];
+                const half8_t A0 = as_half8(nib_times<0>(wa, scp), nib_times<8>(wa, scp),
+                                            nib_times<0>(wb, scp), nib_times<8>(wb, scp));
+                const half8_t A1 = as_half8(nib_times<4>(wa, scp), nib_times<12>(wa, scp),
+                                            nib_times<4>(wb, scp), nib_times<12>(wb, scp));
+#pragma unroll
+                for (int t = 0; t < NT; t++) {
+                    const uint8_t *brow = act + (t * 32 + l32) * 512;
+                    const half8_t B0 =
+                        *reinterpret_cast<const half8_t *>(brow + 16 * ((4 * j + h) ^ l32));
+                    const half8_t B1 =
+                        *reinterpret_cast<const half8_t *>(brow + 16 * ((4 * j + 2 + h) ^ l32));
+                    const float16v_t zero = {};
+                    Q[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A0, B0, zero, 0, 0, 0);
+                    Q[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A1, B1, Q[t], 0, 0, 0);
+                    if (DBG) {
+                        const half8_t U0 = as_half8(nib<0>(wa), nib<8>(wa), nib<0>(wb), nib<8>(wb));
+                        const half8_t U1 =
+                            as_half8(nib<4>(wa), nib<12>(wa), nib<4>(wb), nib<12>(wb));
+                        float16v_t R = __builtin_amdgcn_mfma_f32_32x32x16_f16(U0, B0, zero, 0, 0, 0);
+                        R = __builtin_amdgcn_mfma_f32_32x32x16_f16(U1, B1, R, 0, 0, 0);
+                        const int tok = tok0 + t * 32 + l32;
+#pragma unroll
+                        for (int i = 0; i < 16; i++) {
+                            const int row = wrow0 + 8 * (i / 4) + 4 * h + (i % 4);
+                            if (tok < nvec && row < rows)
+                                a.P[(static_cast<int64_t>(tok) * rows + row) * nbk + sb * 8 + j] =
+                                    static_cast<int>(R[i] * 16777216.0f);
+                        }
+                    }
+                }
+            };
+            auto scale = [&](int j, const float16v_t (&Q)[NT]) {
+#pragma unroll
+                for (int t = 0; t < NT; t++) {
+                    const float xs = xdt[j * NT * 32 + t * 32 + l32].x;
+#pragma unroll
+                    for (int i = 0; i < 16; i++)
+                        t1[t][i] = j == 0 ? xs * Q[t][i] : fmaf(xs, Q[t][i], t1[t][i]);
+                }
+            };
+            if constexpr (NT == 1) {
+                // software-pipelined: block j + 1's products go out before block j's float work
+                float16v_t Qa[NT], Qb[NT];
+                product(0, Qa);
+#pragma unroll
+                for (int j = 0; j < 8; j++) {
+                    float16v_t(&cur_q)[NT] = (j & 1) ? Qb : Qa;
+                    float16v_t(&nxt_q)[NT] = (j & 1) ? Qa : Qb;
+                    if (j + 1 < 8) product(j + 1, nxt_q);
+                    scale(j, cur_q);
+                }
+            } else {
+                // with several vector tiles the later tiles' products overlap the earlier
+                // tiles' float work; a second set of product registers would cost occupancy
+#pragma unroll
+                for (int j = 0; j < 8; j++) {
+                    float16v_t Q[NT];
+                    product(j, Q);
+                    scale(j, Q);
+                }
+            }
+            // ---- the min terms of the eight blocks on the float32 matrix cores: two blocks
+            //      per 32x32x2 product, A = dmin * m (row, block), B = -xd * S (block, vector) ----
+#pragma unroll
+            for (int pp = 0; pp < 4; pp++)
+#pragma unroll
+                for (int t = 0; t < NT; t++) {
+                    const float tb = xdt[(2 * pp + h) * NT * 32 + t * 32 + l32].y;
+                    acc[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(cmin[pp], tb, acc[t], 0, 0, 0);
+                }
+            float ddv[16];
+#pragma unroll
+            for (int qq = 0; qq < 4; qq++) {
+                const float4 f = *reinterpret_cast<const float4 *>(&dd[wave][8 * qq + 4 * h]);
+                ddv[4 * qq] = f.x;
+                ddv[4 * qq + 1] = f.y;
+                ddv[4 * qq + 2] = f.z;
+                ddv[4 * qq + 3] = f.w;
+            }
+#pragma unroll
+            for (int t = 0; t < NT; t++)
+#pragma unroll
+                for (int i = 0; i < 16; i++) acc[t][i] = fmaf(ddv[i], t1[t][i], acc[t][i]);
+            buf ^= 1;
+        }
+
+        if (!DBG) {
+            float *out = a.out + static_cast<int64_t>(cur.split) * nvec * rows;
+            // 16-byte stores when every row group of 4 starts 16-byte aligned
+            const bool vec4 = (rows & 3) == 0 && (reinterpret_cast<uintptr_t>(out) & 15) == 0;
 #pragma unroll
             for (int t = 0; t < NT; t++) {
-                const _Float16 *brow = act + (t * 32 + l32) * kActStride + 32 * j + 8 * h;
-                const half8_t B0 = *reinterpret_cast<const half8_t *>(brow);
-                const half8_t B1 = *reinterpret_cast<const half8_t *>(brow + 16);
-                const float xs = xdt[j * NT * 32 + t * 32 + l32].x;
-                const float16v_t zero = {};
-                float16v_t Q = __builtin_amdgcn_mfma_f32_32x32x16_f16(A0, B0, zero, 0, 0, 0);
-                Q = __builtin_amdgcn_mfma_f32_32x32x16_f16(A1, B1, Q, 0, 0, 0);
+                const int tok = tok0 + t * 32 + l32;
+                if (tok >= nvec) continue;
+                float *yv = out + static_cast<int64_t>(tok) * rows;
 #pragma unroll
-                for (int i = 0; i < 16; i++) t1[t][i] = fmaf(xs, Q[i], t1[t][i]);
-                if (DBG) {
-                    const half8_t U0 = as_half8(nib<0>(wa), nib<8>(wa), nib<0>(wb), nib<8>(wb));
-                    const half8_t U1 = as_half8(nib<4>(wa), nib<12>(wa), nib<4>(wb), nib<12>(wb));
-                    float16v_t R = __builtin_amdgcn_mfma_f32_32x32x16_f16(U0, B0, zero, 0, 0, 0);
-                    R = __builtin_amdgcn_mfma_f32_32x32x16_f16(U1, B1, R, 0, 0, 0);
-                    const int tok = tok0 + t * 32 + l32;
+                for (int qq = 0; qq < 4; qq++) {
+                    const int row = wrow0 + 8 * qq + 4 * h;
+                    if (vec4 && row + 3 < rows) {
+                        *reinterpret_cast<float4 *>(yv + row) =
+                            make_float4(acc[t][4 * qq], acc[t][4 * qq + 1], acc[t][4 * qq + 2],
+                                        acc[t][4 * qq + 3]);
+                    } else {
 #pragma unroll
-                    for (int i = 0; i < 16; i++) {
-                        const int row = wrow0 + 8 * (i / 4) + 4 * h + (i % 4);
-                        if (tok < nvec && row < rows)
-                            a.P[(static_cast<int64_t>(tok) * rows + row) * nbk + sb * 8 + j] =
-                                static_cast<int>(R[i] * 16777216.0f);
+                        for (int i = 0; i < 4; i++)
+                            if (row + i < rows) yv[row + i] = acc[t][4 * qq + i];
                     }
                 }
             }
         }
-        // ---- the min terms of the eight blocks on the float32 matrix cores: two blocks per
-        //      32x32x2 product, A = dmin * m (row, block), B = -xd * S (block, vector) ----
-#pragma unroll
-        for (int pp = 0; pp < 4; pp++)
-#pragma unroll
-            for (int t = 0; t < NT; t++) {
-                const float tb = xdt[(2 * pp + h) * NT * 32 + t * 32 + l32].y;
-                acc[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(cmin[pp], tb, acc[t], 0, 0, 0);
-            }
-        float ddv[16];
-#pragma unroll
-        for (int qq = 0; qq < 4; qq++) {
-            const float4 f = *reinterpret_cast<const float4 *>(&dd[wave][8 * qq + 4 * h]);
-            ddv[4 * qq] = f.x;
-            ddv[4 * qq + 1] = f.y;
-            ddv[4 * qq + 2] = f.z;
-            ddv[4 * qq + 3] = f.w;
-        }
-#pragma unroll
-        for (int t = 0; t < NT; t++)
-#pragma unroll
-            for (int i = 0; i < 16; i++) {
-                acc[t][i] = fmaf(ddv[i], t1[t][i], acc[t][i]);
-                t1[t][i] = 0.0f;
-            }
-        __syncthreads();   // the next super-block overwrites the staged codes and tables
-    }
-
-    if (DBG) return;
-    float *out = a.out + static_cast<int64_t>(blockIdx.z) * nvec * rows;
-    // 16-byte stores when every row group of 4 starts 16-byte aligned
-    const bool vec4 = (rows & 3) == 0 && (reinterpret_cast<uintptr_t>(out) & 15) == 0;
-#pragma unroll
-    for (int t = 0; t < NT; t++) {
-        const int tok = tok0 + t * 32 + l32;
-        if (tok >= nvec) continue;
-        float *yv = out + static_cast<int64_t>(tok) * rows;
-#pragma unroll
-        for (int qq = 0; qq < 4; qq++) {
-            const int row = wrow0 + 8 * qq + 4 * h;
-            if (vec4 && row + 3 < rows) {
-                *reinterpret_cast<float4 *>(yv + row) =
-                    make_float4(acc[t][4 * qq], acc[t][4 * qq + 1], acc[t][4 * qq + 2],
-                                acc[t][4 * qq + 3]);
-            } else {
-#pragma unroll
-                for (int i = 0; i < 4; i++)
-                    if (row + i < rows) yv[row + i] = acc[t][4 * qq + i];
-            }
-        }
+        it += gridDim.x;
+        if (it >= items) break;
+        cur = item_of(it);
     }
 }
 
 template <int NT>
 hipError_t launch_nt(const GemmArgs &a, int row_tiles, int groups, int splits, bool debug,
                      hipStream_t stream) {
-    const dim3 grid(static_cast<unsigned>(row_tiles), static_cast<unsigned>(groups),
-                    static_cast<unsigned>(splits));
-    if (debug)
-        hipLaunchKernelGGL((gemm_q4k_mfma_kernel<NT, true>), grid, dim3(256), 0, stream, a);
-    else
-        hipLaunchKernelGGL((gemm_q4k_mfma_kernel<NT, false>), grid, dim3(256), 0, stream, a);
+    const dim3 sgrid(static_cast<unsigned>(a.nb), static_cast<unsigned>(groups));
+    // workgroups that stay resident at once (per CU, from the kernel's registers and LDS)
+    static int per_cu[2] = {0, 0};
+    static int cus = 0;
+    if (cus == 0) {
+        int dev = 0, n = 0;
+        if (hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess)
+            cus = n > 0 ? n : 256;
+        else
+            cus = 256;
+    }
+    int &resident = per_cu[debug ? 1 : 0];
+    if (resident == 0) {
+        int n = 0;
+        const hipError_t e =
+            debug ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gemm_q4k_mfma_kernel<NT, true>, 256, 0)
+                  : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gemm_q4k_mfma_kernel<NT, false>, 256, 0);
+        resident = (e == hipSuccess && n > 0) ? n : 1;
+    }
+    const int64_t items = static_cast<int64_t>(row_tiles) * groups * splits;
+    const unsigned blocks = static_cast<unsigned>(std::min<int64_t>(items, int64_t{resident} * cus));
+    if (debug) {
+        hipLaunchKernelGGL((mc_stage_kernel<NT, true>), sgrid, dim3(256), 0, stream, a);
+        hipLaunchKernelGGL((gemm_q4k_mfma_kernel<NT, true>), dim3(blocks), dim3(256), 0, stream, a);
+    } else {
+        hipLaunchKernelGGL((mc_stage_kernel<NT, false>), sgrid, dim3(256), 0, stream, a);
+        hipLaunchKernelGGL((gemm_q4k_mfma_kernel<NT, false>), dim3(blocks), dim3(256), 0, stream, a);
+    }
     return hipGetLastError();
 }
 

@@ -116,12 +116,18 @@ struct GemmArgs {
     float *out;            // [splits][nvec][rows] (y itself when splits == 1)
     int32_t *P;            // debug: [nvec][rows][cols/32] integer partials, or nullptr
     int32_t *S;            // debug: [nvec][cols/32] activation block sums, or nullptr
+    uint8_t *tiles;        // workspace: the staged fp16 activation tiles (pre-pass output)
     int32_t rows;
     int32_t nb;            // super-blocks per row
     int32_t nvec;
     int32_t sb_per_split;  // super-blocks per column split
+    int32_t row_tiles;     // work items: row tiles x vector groups x splits
+    int32_t groups;
+    int32_t splits;
 };
-// Grid: (row tiles, vector groups, splits); nt = 1..4 tiles of 32 vectors per group.
+// Two launches: the staging pre-pass (grid super-blocks x groups) writes the tiles, then the
+// product (grid row tiles x groups x splits); nt = 1..4 tiles of 32 vectors per group.
+constexpr int64_t mc_tile_bytes(int nt) { return int64_t{nt} * (32 * 512 + 8 * 32 * 8); }
 hipError_t launch_gemm_q4k_mfma(const GemmArgs &a, int nt, int row_tiles, int groups, int splits,
                                 bool debug, hipStream_t stream);
 

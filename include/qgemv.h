@@ -305,7 +305,8 @@ int qgemv_graph_destroy(qgemv_graph *graph);
 
 /*
  * Test hook: the exact integer partials of the same kernels (for Q4_K with
- * more than 8 vectors, of the matrix-core kernel).
+ * more than 8 vectors, of the matrix-core kernel, which needs the workspace of
+ * qgemv_workspace_bytes(); elsewhere workspace may be NULL).
  * P int32: Q4_K [nvec][rows][cols/32] (sum of q * xq per 32-column
  * sub-block), Q6_K [nvec][rows][cols/16] (sum of (q - 32) * xq per 16-column
  * sub-block). S int32 [nvec][cols/32]: sum of xq per activation block.
@@ -313,7 +314,7 @@ int qgemv_graph_destroy(qgemv_graph *graph);
  */
 int qgemv_debug_partials(int wtype, const void *w, const int8_t *xq, const float *xd,
                          int32_t *P, int32_t *S, int64_t rows, int64_t cols, int32_t nvec,
-                         hipStream_t stream);
+                         void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Load-time weight quantization, float32 [rows][cols] -> a tensor of any format

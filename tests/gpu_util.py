@@ -70,7 +70,9 @@ def partials(wtype: str, w, xq, xd, rows: int, cols: int, nvec: int):
     nsub = cols // 16 if wtype == "q6k" else cols // 32
     P = torch.full((nvec, rows, nsub), -(2 ** 31), dtype=torch.int32, device=DEV)
     S = torch.full((nvec, cols // 32), -(2 ** 31), dtype=torch.int32, device=DEV)
-    qg.qgemv_debug_partials(wtype, wt, xq, xd, P, S, rows, cols, nvec)
+    nbytes = qg.qgemv_workspace_bytes(wtype, rows, cols, nvec)
+    ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=DEV) if nbytes else None
+    qg.qgemv_debug_partials(wtype, wt, xq, xd, P, S, rows, cols, nvec, workspace=ws)
     return host(P), host(S)
 
 

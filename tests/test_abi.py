@@ -93,7 +93,10 @@ def test_other_entry_points_reject_bad_arguments():
     assert lib.qgemv_q6k(A + 2, A + (1 << 30), A + (2 << 30), A + (3 << 30), 8, 256, None, 0,
                          None) == EALIGN
     assert lib.qgemv_debug_partials(1, A, A + (1 << 30), A + (2 << 30), None, A, 8, 256, 1,
-                                    None) == EINVAL
+                                    None, 0, None) == EINVAL
+    # the matrix-core debug form needs the workspace
+    assert lib.qgemv_debug_partials(1, A, A + (1 << 30), A + (2 << 30), A + (3 << 30),
+                                    A + (4 << 30), 8, 256, 9, None, 0, None) == EWORKSPACE
     assert lib.qgemv_quantize_weights(2, A, A + 64, 8, 256, None) == EINVAL   # overlap
     assert lib.qgemv_quantize_weights(2, A + 4, A + (1 << 30), 8, 256, None) == EALIGN
     assert lib.qgemv_quantize_weights(5, A, A + (1 << 30), 8, 256, None) == EINVAL
@@ -214,7 +217,8 @@ def test_matrix_core_path_limits_on_the_host():
     all refused before any launch."""
     lib = qg._load()
     assert qg.qgemv_workspace_bytes("q4k", 256, 2048, 64) > 0          # few rows: split
-    assert qg.qgemv_workspace_bytes("q4k", 1 << 16, 2048, 64) == 0      # enough rows
+    # enough rows: no split, only the staged activation tiles (8 super-blocks x 64 vectors)
+    assert qg.qgemv_workspace_bytes("q4k", 1 << 16, 2048, 64) == 8 * 2 * 18432
     assert qg.qgemv_workspace_bytes("q6k", 256, 2048, 64) == 0          # no such path
     assert qg.qgemv_workspace_bytes("q4k", 256, 2048, 257) == 0
     assert _call_batch(nvec=257) == EINVAL

@@ -111,12 +111,12 @@ def test_workspace_and_limits():
     import block_quantized_weight_act_amd as qg
     rows, cols, nvec = 256, 2048, 64          # few rows: the super-blocks are split
     assert qg.qgemv_workspace_bytes("q4k", rows, cols, nvec) > 0
-    assert qg.qgemv_workspace_bytes("q4k", 65536, cols, nvec) == 0
+    assert qg.qgemv_workspace_bytes("q4k", 65536, cols, nvec) == 8 * 2 * 18432   # tiles only
     w = torch.zeros(qg.qgemv_weight_bytes("q4k", rows, cols), dtype=torch.uint8, device=gu.DEV)
     xq = torch.zeros((257, cols), dtype=torch.int8, device=gu.DEV)
     xd = torch.zeros((257, cols // 32), dtype=torch.float32, device=gu.DEV)
     y = torch.zeros((257, rows), dtype=torch.float32, device=gu.DEV)
-    with pytest.raises(qg.QgemvError):       # split planned, no workspace
+    with pytest.raises(qg.QgemvError):       # no workspace
         qg.qgemv_batch("q4k", w, xq, xd, y, rows, cols, nvec)
     with pytest.raises(qg.QgemvError):       # more vectors than the matrix-core path takes
         qg.qgemv_batch("q4k", w, xq, xd, y, rows, cols, 257,
@@ -156,3 +156,27 @@ def test_full_size_vocabulary_projection_sampled():
     wbuf = oracle.quantize_q4k(wl.weight_rows(sample))
     ref = oracle.gemv("q4k", wbuf, sample.size, cols, rq, rd)
     gu.assert_within_bound(yh[:, sample], ref)
+
+
+@pytest.mark.parametrize("rows,cols,nvec", [
+    (40000, 1536, 25),    # one vector tile, 313 row tiles: 2 splits of 3 super-blocks (odd)
+    (70000, 1280, 17),    # one vector tile, 547 row tiles: no split, 5 super-blocks (odd)
+])
+def test_odd_super_block_counts_sampled(rows, cols, nvec):
+    """Many rows with an odd number of super-blocks per workgroup (the one-tile kernel keeps
+    weights two super-blocks ahead and pads odd counts): sampled rows against the oracle."""
+    import torch
+    import block_quantized_weight_act_amd as qg
+    _say("odd", rows, cols, nvec)
+    rng = np.random.default_rng(rows + nvec)
+    w = (rng.standard_normal((rows, cols)) * 0.02).astype(np.float32)
+    wbuf = oracle.quantize_q4k(w)
+    x = rng.standard_normal((nvec, cols)).astype(np.float32)
+    rq, rd = oracle.quantize_act(x)
+    xq, xd = gu.quantize_act(x)
+    y = gu.gemv("q4k", gu.dev(wbuf), xq, xd, rows, cols, nvec)
+    sample = np.unique(np.concatenate([np.arange(0, rows, 97), np.arange(rows - 300, rows)]))
+    sbuf = oracle.quantize_q4k(w[sample])
+    ref = oracle.gemv("q4k", sbuf, sample.size, cols, rq, rd)
+    gu.assert_within_bound(y[:, sample], ref)
+    torch.cuda.synchronize()
