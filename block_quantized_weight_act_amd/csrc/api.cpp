@@ -279,6 +279,28 @@ struct McPlan {
     int nt, row_tiles, groups, splits, sbps;
 };
 
+// More than kMaxVec vectors for a format without a matrix-core path: groups of kMaxVec.
+bool grouped_shape_ok(int wtype, int64_t rows, int64_t cols, int32_t nvec) {
+    return type_ok(wtype) && wtype != QGEMV_Q4K && nvec > kMaxVec && nvec <= kMaxBatch &&
+           shape_ok_t(wtype, rows, cols, 1) &&
+           static_cast<int64_t>(nvec) * cols < (int64_t{1} << 34);
+}
+
+// check_gemv_args for any vector count (the shape itself checked by the caller)
+int check_gemv_args_n(int wtype, const void *w, const int8_t *xq, const float *xd, const void *out,
+                      size_t out_bytes, int64_t rows, int64_t cols, int32_t nvec) {
+    if (!w || !xq || !xd || !out) return QGEMV_EINVAL;
+    if (!aligned(w, 16) || !aligned(xq, 16) || !aligned(xd, 4) || !aligned(out, 4))
+        return QGEMV_EALIGN;
+    const size_t wb = weight_bytes(wtype, rows, cols);
+    const size_t xqb = static_cast<size_t>(nvec) * cols;
+    const size_t xdb = static_cast<size_t>(nvec) * (cols / 32) * sizeof(float);
+    if (overlaps(out, out_bytes, w, wb) || overlaps(out, out_bytes, xq, xqb) ||
+        overlaps(out, out_bytes, xd, xdb))
+        return QGEMV_EINVAL;
+    return QGEMV_OK;
+}
+
 bool mc_shape_ok(int wtype, int64_t rows, int64_t cols, int32_t nvec) {
     return wtype == QGEMV_Q4K && nvec > kMaxVec && nvec <= kMaxBatch && rows >= 1 &&
            rows <= (int64_t{1} << 30) && cols >= kQK && cols % kQK == 0 &&
@@ -495,6 +517,11 @@ int qgemv_quantize_act(const float *x, int8_t *xq, float *xd, int64_t cols, int3
 size_t qgemv_workspace_bytes(int wtype, int64_t rows, int64_t cols, int32_t nvec) {
     if (mc_shape_ok(wtype, rows, cols, nvec))
         return mc_ws_bytes(make_mc_plan(rows, cols, nvec), rows, cols, nvec);
+    if (grouped_shape_ok(wtype, rows, cols, nvec)) {
+        // groups of up to kMaxVec vectors, one after another on the stream, share the workspace
+        const int32_t g = std::min<int32_t>(nvec, kMaxVec);
+        return plan_ws_bytes(make_plan(wtype, rows, cols, g), rows, cols, g);
+    }
     if (!shape_ok_t(wtype, rows, cols, nvec)) return 0;
     return plan_ws_bytes(make_plan(wtype, rows, cols, nvec), rows, cols, nvec);
 }
@@ -528,6 +555,34 @@ int qgemv_batch(int wtype, const void *w, const int8_t *xq, const float *xd, flo
     if (mc_shape_ok(wtype, rows, cols, nvec))
         return run_mc(w, xq, xd, y, nullptr, nullptr, rows, cols, nvec, workspace,
                       workspace_bytes, stream);
+    if (grouped_shape_ok(wtype, rows, cols, nvec)) {
+        // more than kMaxVec vectors without a matrix-core path: the vector kernel on groups of
+        // up to kMaxVec vectors (each group one pass over the weights); every argument is
+        // checked for the whole product before the first launch
+        const size_t ybytes = static_cast<size_t>(nvec) * rows * sizeof(float);
+        int st = check_gemv_args_n(wtype, w, xq, xd, y, ybytes, rows, cols, nvec);
+        if (st != QGEMV_OK) return st;
+        const size_t need = qgemv_workspace_bytes(wtype, rows, cols, nvec);
+        if (need > 0) {
+            if (!workspace || workspace_bytes < need) return QGEMV_EWORKSPACE;
+            if (!aligned(workspace, 4)) return QGEMV_EALIGN;
+            if (overlaps(workspace, need, w, weight_bytes(wtype, rows, cols)) ||
+                overlaps(workspace, need, y, ybytes) ||
+                overlaps(workspace, need, xq, static_cast<size_t>(nvec) * cols) ||
+                overlaps(workspace, need, xd, static_cast<size_t>(nvec) * (cols / 32) * sizeof(float)))
+                return QGEMV_EINVAL;
+        }
+        for (int32_t v0 = 0; v0 < nvec; v0 += kMaxVec) {
+            const int32_t g = std::min<int32_t>(kMaxVec, nvec - v0);
+            Activation act;
+            act.xq = xq + static_cast<int64_t>(v0) * cols;
+            act.xd = xd + static_cast<int64_t>(v0) * (cols / 32);
+            st = run_gemv(wtype, w, act, y + static_cast<int64_t>(v0) * rows, rows, cols, g,
+                          make_plan(wtype, rows, cols, g), workspace, workspace_bytes, stream);
+            if (st != QGEMV_OK) return st;
+        }
+        return QGEMV_OK;
+    }
     if (!shape_ok_t(wtype, rows, cols, nvec))
         return QGEMV_EINVAL;
     Activation act;

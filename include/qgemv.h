@@ -80,8 +80,9 @@
  *    caller's next synchronization.
  *  - Shapes: cols a positive multiple of 256 (Q4_K, Q6_K) or of 32 (Q4_0,
  *    Q8_0), 1 <= rows <= 2^30, 1 <= nvec <= 8, rows * cols / 32 < 2^31;
- *    qgemv_batch, qgemv_workspace_bytes and qgemv_debug_partials also take
- *    9 <= nvec <= QGEMV_MAX_BATCH vectors for Q4_K (the matrix-core path).
+ *    qgemv_batch and qgemv_workspace_bytes also take 9 <= nvec <=
+ *    QGEMV_MAX_BATCH vectors (Q4_K: the matrix-core path), and so does
+ *    qgemv_debug_partials for Q4_K.
  *  - Alignment: w and xq 16 bytes, xd and y 4 bytes.
  *  - Outputs must not overlap inputs.
  *  - The functions are safe to call from several host threads.
@@ -182,9 +183,12 @@ int qgemv_q6k(const void *w, const int8_t *xq, const float *xd, float *y, int64_
  * at once; oxinfer README, "Speculative decoding": the many-token int8
  * variants are instruction-bound at Q4) runs on the matrix cores: the same
  * exact integer sub-block products P and sums S, then the same float32
- * scaling, so y lies within the same bound of the exact product. Other types
- * with nvec > 8: QGEMV_EINVAL. The workspace (qgemv_workspace_bytes) is
- * needed when the super-blocks are split over workgroups (few rows).
+ * scaling, so y lies within the same bound of the exact product; the
+ * workspace (qgemv_workspace_bytes) then holds the staged activation and, for
+ * matrices with few rows, partial sums. The other types with 9 <= nvec <=
+ * QGEMV_MAX_BATCH run the vector kernels on groups of up to 8 vectors, one
+ * after another on the stream (one pass over the weights per group; the
+ * workspace is that of 8 vectors, shared by the groups).
  */
 int qgemv_batch(int wtype, const void *w, const int8_t *xq, const float *xd, float *y,
                 int64_t rows, int64_t cols, int32_t nvec, void *workspace,

@@ -219,11 +219,13 @@ def test_matrix_core_path_limits_on_the_host():
     assert qg.qgemv_workspace_bytes("q4k", 256, 2048, 64) > 0          # few rows: split
     # enough rows: no split, only the staged activation tiles (8 super-blocks x 64 vectors)
     assert qg.qgemv_workspace_bytes("q4k", 1 << 16, 2048, 64) == 8 * 2 * 18432
-    assert qg.qgemv_workspace_bytes("q6k", 256, 2048, 64) == 0          # no such path
+    # other formats: groups of 8 vectors on the vector kernel, sharing one group's workspace
+    assert qg.qgemv_workspace_bytes("q6k", 256, 2048, 64) == qg.qgemv_workspace_bytes("q6k", 256, 2048, 8)
     assert qg.qgemv_workspace_bytes("q4k", 256, 2048, 257) == 0
     assert _call_batch(nvec=257) == EINVAL
-    assert _call_batch(wtype=2, nvec=9) == EINVAL
-    assert _call_batch(wtype=3, nvec=9) == EINVAL
+    assert _call_batch(wtype=2, nvec=257) == EINVAL
+    assert _call_batch(wtype=3, nvec=9, y=None) == EINVAL
+    assert _call_batch(wtype=4, nvec=40, xq=A + (1 << 30) + 4) == EALIGN
     assert _call_batch(nvec=64, rows=256, cols=2048) == EWORKSPACE
     assert _call_batch(nvec=64, xq=A + (1 << 30) + 4) == EALIGN
     plan = qg.Plan()

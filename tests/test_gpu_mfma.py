@@ -121,11 +121,32 @@ def test_workspace_and_limits():
     with pytest.raises(qg.QgemvError):       # more vectors than the matrix-core path takes
         qg.qgemv_batch("q4k", w, xq, xd, y, rows, cols, 257,
                        workspace=torch.zeros(1 << 24, dtype=torch.uint8, device=gu.DEV))
-    with pytest.raises(qg.QgemvError):       # Q6_K has no matrix-core path
-        w6 = torch.zeros(qg.qgemv_weight_bytes("q6k", rows, cols), dtype=torch.uint8,
-                         device=gu.DEV)
-        qg.qgemv_batch("q6k", w6, xq, xd, y, rows, cols, 9)
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("wtype,rows,cols,nvec", [
+    ("q6k", 300, 1024, 9), ("q6k", 2048, 8192, 20), ("q40", 513, 800, 17), ("q80", 77, 1536, 40),
+    ("q40", 4000, 2048, 64),
+])
+def test_other_formats_many_vectors_grouped(wtype, rows, cols, nvec):
+    """Formats without a matrix-core path take more than 8 vectors as groups of up to 8 on the
+    vector kernel: every y within the bound, and each group's y equals that group's own
+    product bit for bit."""
+    _say("grouped", wtype, rows, cols, nvec)
+    rng = np.random.default_rng(rows + cols + nvec)
+    w = (rng.standard_normal((rows, cols)) * 0.02).astype(np.float32)
+    wbuf = oracle.quantize(wtype, w)
+    x = rng.standard_normal((nvec, cols)).astype(np.float32)
+    rq, rd = oracle.quantize_act(x)
+    xq, xd = gu.quantize_act(x)
+    wt = gu.dev(wbuf)
+    y = gu.gemv(wtype, wt, xq, xd, rows, cols, nvec)
+    gu.assert_within_bound(y, oracle.gemv(wtype, wbuf, rows, cols, rq, rd))
+    for v0 in range(0, nvec, 8):
+        g = min(8, nvec - v0)
+        yg = gu.gemv(wtype, wt, xq[v0:v0 + g].contiguous(), xd[v0:v0 + g].contiguous(), rows,
+                     cols, g)
+        assert np.array_equal(yg.view(np.uint32), y[v0:v0 + g].view(np.uint32))
 
 
 def test_full_size_vocabulary_projection_sampled():
