@@ -105,7 +105,7 @@ constexpr int tile_bytes() {
 }
 
 // Pre-pass: the activation codes of every (super-block, vector group) converted once to the
-// fp16 image the main kernel copies into LDS. In a vector's 512 bytes, the 16-byte piece p
+// fp16 image the main kernel copies into LDS; a workgroup per 16 vectors of a group. In a vector's 512 bytes, the 16-byte piece p
 // (columns 8p .. 8p + 7 in the slot order above) sits at slot p ^ (vector % 32), so the 32
 // vectors of a matrix-core operand read 32 different bank groups.
 template <int NT, bool DBG>
@@ -120,8 +120,8 @@ __global__ void __launch_bounds__(256) mc_stage_kernel(GemmArgs a) {
     const int tok0 = blockIdx.y * NT * 32;
     uint8_t *tile = a.tiles + (static_cast<int64_t>(sb) * gridDim.y + blockIdx.y) * tile_bytes<NT>();
     float2 *xdt = reinterpret_cast<float2 *>(tile + NT * 32 * 512);
-#pragma unroll
-    for (int rnd = 0; rnd < 2 * NT; rnd++) {
+    {
+        const int rnd = blockIdx.z;     // 16 vectors per workgroup
         const int v = rnd * 16 + sv;
         const int tok = tok0 + v;
         uint4 q = make_uint4(0u, 0u, 0u, 0u);
@@ -421,7 +421,7 @@ __global__ void __launch_bounds__(256) gemm_q4k_mfma_kernel(GemmArgs a) {
 template <int NT>
 hipError_t launch_nt(const GemmArgs &a, int row_tiles, int groups, int splits, bool debug,
                      hipStream_t stream) {
-    const dim3 sgrid(static_cast<unsigned>(a.nb), static_cast<unsigned>(groups));
+    const dim3 sgrid(static_cast<unsigned>(a.nb), static_cast<unsigned>(groups), 2 * NT);
     // workgroups that stay resident at once (per CU, from the kernel's registers and LDS)
     static int per_cu[2] = {0, 0};
     static int cus = 0;
