@@ -298,8 +298,24 @@ __global__ void __launch_bounds__(256) gemm_q4k_mfma_kernel(GemmArgs a) {
 
             const uint8_t *act = lds[buf];
             const float2 *xdt = reinterpret_cast<const float2 *>(act + NT * 32 * 512);
-            // ---- eight 32-column blocks ----
-            auto product = [&](int j, float16v_t (&Q)[NT]) {
+            // ---- eight 32-column blocks. The operand reads from LDS go out two blocks ahead
+            //      and the matrix products one block ahead of the float work that uses them,
+            //      so neither waits on the previous step (for up to two vector tiles; with
+            //      more, the registers are not there and each block is done in turn) ----
+            struct BOps {
+                half8_t b0[NT], b1[NT];
+                float xs[NT];
+            };
+            auto read_b = [&](int j, BOps &o) {
+#pragma unroll
+                for (int t = 0; t < NT; t++) {
+                    const uint8_t *brow = act + (t * 32 + l32) * 512;
+                    o.b0[t] = *reinterpret_cast<const half8_t *>(brow + 16 * ((4 * j + h) ^ l32));
+                    o.b1[t] = *reinterpret_cast<const half8_t *>(brow + 16 * ((4 * j + 2 + h) ^ l32));
+                    o.xs[t] = xdt[j * NT * 32 + t * 32 + l32].x;
+                }
+            };
+            auto product = [&](int j, const BOps &o, float16v_t (&Q)[NT]) {
                 const uint32_t scp = sc[j] * 0x00010001u;
                 const uint32_t wa = aw[j], wb = bw[j];
                 const half8_t A0 = as_half8(nib_times<0>(wa, scp), nib_times<8>(wa, scp),
@@ -308,20 +324,16 @@ __global__ void __launch_bounds__(256) gemm_q4k_mfma_kernel(GemmArgs a) {
                                             nib_times<4>(wb, scp), nib_times<12>(wb, scp));
 #pragma unroll
                 for (int t = 0; t < NT; t++) {
-                    const uint8_t *brow = act + (t * 32 + l32) * 512;
-                    const half8_t B0 =
-                        *reinterpret_cast<const half8_t *>(brow + 16 * ((4 * j + h) ^ l32));
-                    const half8_t B1 =
-                        *reinterpret_cast<const half8_t *>(brow + 16 * ((4 * j + 2 + h) ^ l32));
                     const float16v_t zero = {};
-                    Q[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A0, B0, zero, 0, 0, 0);
-                    Q[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A1, B1, Q[t], 0, 0, 0);
+                    Q[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A0, o.b0[t], zero, 0, 0, 0);
+                    Q[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A1, o.b1[t], Q[t], 0, 0, 0);
                     if (DBG) {
                         const half8_t U0 = as_half8(nib<0>(wa), nib<8>(wa), nib<0>(wb), nib<8>(wb));
                         const half8_t U1 =
                             as_half8(nib<4>(wa), nib<12>(wa), nib<4>(wb), nib<12>(wb));
-                        float16v_t R = __builtin_amdgcn_mfma_f32_32x32x16_f16(U0, B0, zero, 0, 0, 0);
-                        R = __builtin_amdgcn_mfma_f32_32x32x16_f16(U1, B1, R, 0, 0, 0);
+                        float16v_t R =
+                            __builtin_amdgcn_mfma_f32_32x32x16_f16(U0, o.b0[t], zero, 0, 0, 0);
+                        R = __builtin_amdgcn_mfma_f32_32x32x16_f16(U1, o.b1[t], R, 0, 0, 0);
                         const int tok = tok0 + t * 32 + l32;
 #pragma unroll
                         for (int i = 0; i < 16; i++) {
@@ -333,34 +345,36 @@ __global__ void __launch_bounds__(256) gemm_q4k_mfma_kernel(GemmArgs a) {
                     }
                 }
             };
-            auto scale = [&](int j, const float16v_t (&Q)[NT]) {
+            auto scale = [&](int j, const BOps &o, const float16v_t (&Q)[NT]) {
 #pragma unroll
-                for (int t = 0; t < NT; t++) {
-                    const float xs = xdt[j * NT * 32 + t * 32 + l32].x;
+                for (int t = 0; t < NT; t++)
 #pragma unroll
                     for (int i = 0; i < 16; i++)
-                        t1[t][i] = j == 0 ? xs * Q[t][i] : fmaf(xs, Q[t][i], t1[t][i]);
-                }
+                        t1[t][i] = j == 0 ? o.xs[t] * Q[t][i] : fmaf(o.xs[t], Q[t][i], t1[t][i]);
             };
-            if constexpr (NT == 1) {
-                // software-pipelined: block j + 1's products go out before block j's float work
+            if constexpr (NT <= 2) {
+                BOps ob[3];
                 float16v_t Qa[NT], Qb[NT];
-                product(0, Qa);
+                read_b(0, ob[0]);
+                read_b(1, ob[1]);
+                product(0, ob[0], Qa);
 #pragma unroll
                 for (int j = 0; j < 8; j++) {
                     float16v_t(&cur_q)[NT] = (j & 1) ? Qb : Qa;
                     float16v_t(&nxt_q)[NT] = (j & 1) ? Qa : Qb;
-                    if (j + 1 < 8) product(j + 1, nxt_q);
-                    scale(j, cur_q);
+                    if (j + 2 < 8) read_b(j + 2, ob[(j + 2) % 3]);
+                    __builtin_amdgcn_sched_barrier(0);
+                    if (j + 1 < 8) product(j + 1, ob[(j + 1) % 3], nxt_q);
+                    scale(j, ob[j % 3], cur_q);
                 }
             } else {
-                // with several vector tiles the later tiles' products overlap the earlier
-                // tiles' float work; a second set of product registers would cost occupancy
 #pragma unroll
                 for (int j = 0; j < 8; j++) {
+                    BOps o;
                     float16v_t Q[NT];
-                    product(j, Q);
-                    scale(j, Q);
+                    read_b(j, o);
+                    product(j, o, Q);
+                    scale(j, o, Q);
                 }
             }
             // ---- the min terms of the eight blocks on the float32 matrix cores: two blocks
