@@ -32,6 +32,7 @@
 // columns, slots 0..7 hold columns 0, 2, 1, 3, 4, 6, 5, 7 (the order the nibbles and bytes come
 // out of a 32-bit word with two masks).
 #include <algorithm>
+#include <atomic>
 #include <type_traits>
 
 #include "device_common.h"
@@ -436,27 +437,31 @@ template <int NT>
 hipError_t launch_nt(const GemmArgs &a, int row_tiles, int groups, int splits, bool debug,
                      hipStream_t stream) {
     const dim3 sgrid(static_cast<unsigned>(a.nb), static_cast<unsigned>(groups), 2 * NT);
-    // workgroups that stay resident at once (per CU, from the kernel's registers and LDS)
-    static int per_cu[2] = {0, 0};
-    static int cus = 0;
-    if (cus == 0) {
+    // Workgroups that stay resident at once: per CU (from the kernel's registers and LDS) times
+    // the CUs. Looked up once; concurrent first calls store the same values. The grid size only
+    // sets how many workgroups share the items, so any value gives the same results.
+    static std::atomic<int> per_cu[2] = {{0}, {0}};
+    static std::atomic<int> cus{0};
+    if (cus.load(std::memory_order_relaxed) == 0) {
         int dev = 0, n = 0;
-        if (hipGetDevice(&dev) == hipSuccess &&
-            hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess)
-            cus = n > 0 ? n : 256;
-        else
-            cus = 256;
+        const bool ok = hipGetDevice(&dev) == hipSuccess &&
+                        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) ==
+                            hipSuccess &&
+                        n > 0;
+        cus.store(ok ? n : 256, std::memory_order_relaxed);
     }
-    int &resident = per_cu[debug ? 1 : 0];
-    if (resident == 0) {
+    std::atomic<int> &res = per_cu[debug ? 1 : 0];
+    if (res.load(std::memory_order_relaxed) == 0) {
         int n = 0;
         const hipError_t e =
             debug ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gemm_q4k_mfma_kernel<NT, true>, 256, 0)
                   : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gemm_q4k_mfma_kernel<NT, false>, 256, 0);
-        resident = (e == hipSuccess && n > 0) ? n : 1;
+        res.store((e == hipSuccess && n > 0) ? n : 1, std::memory_order_relaxed);
     }
+    const int resident = res.load(std::memory_order_relaxed);
     const int64_t items = static_cast<int64_t>(row_tiles) * groups * splits;
-    const unsigned blocks = static_cast<unsigned>(std::min<int64_t>(items, int64_t{resident} * cus));
+    const unsigned blocks = static_cast<unsigned>(
+        std::min<int64_t>(items, int64_t{resident} * cus.load(std::memory_order_relaxed)));
     if (debug) {
         hipLaunchKernelGGL((mc_stage_kernel<NT, true>), sgrid, dim3(256), 0, stream, a);
         hipLaunchKernelGGL((gemm_q4k_mfma_kernel<NT, true>), dim3(blocks), dim3(256), 0, stream, a);
