@@ -25,7 +25,8 @@ __all__ = [
     "qgemv_read_probe", "qgemv_fused", "qgemv_quantize_weights_rows", "qgemv_fused_launches",
     "qgemv_multi", "qgemv_multi_fused", "qgemv_multi_geometry", "QGEMV_Q4_0", "QGEMV_Q8_0",
     "Graph", "qgemv_graph_begin", "qgemv_graph_end", "qgemv_graph_launch", "qgemv_graph_nodes",
-    "qgemv_graph_destroy",
+    "qgemv_graph_destroy", "qgemv_i8mc_workspace_bytes", "qgemv_batch_i8mc",
+    "qgemv_debug_partials_i8mc", "qgemv_fused_i8mc",
 ]
 
 QGEMV_Q4K = 1
@@ -105,6 +106,10 @@ def _load():
         "qgemv_graph_launch": (ctypes.c_int, [vp, vp]),
         "qgemv_graph_nodes": (ctypes.c_int, [vp, ctypes.POINTER(i64), ctypes.POINTER(i64)]),
         "qgemv_graph_destroy": (ctypes.c_int, [vp]),
+        "qgemv_i8mc_workspace_bytes": (sz, [i64, i64, i32]),
+        "qgemv_batch_i8mc": (ctypes.c_int, [vp, vp, vp, vp, i64, i64, i32, vp, sz, vp]),
+        "qgemv_debug_partials_i8mc": (ctypes.c_int, [vp, vp, vp, vp, vp, i64, i64, i32, vp]),
+        "qgemv_fused_i8mc": (ctypes.c_int, [vp, vp, vp, vp, vp, i64, i64, i32, vp, sz, vp]),
     }
     for name, (res, args) in sigs.items():
         fn = getattr(lib, name)
@@ -287,6 +292,39 @@ def qgemv_debug_partials(wtype, w, xq, xd, P, S, rows: int, cols: int, nvec: int
         _wtype(wtype), _ptr(w, name="w"), _ptr(xq, torch.int8, "xq"),
         _ptr(xd, torch.float32, "xd"), _ptr(P, torch.int32, "P"), _ptr(S, torch.int32, "S"),
         rows, cols, nvec, wsp, wsb, _stream(stream, P)))
+
+
+def qgemv_i8mc_workspace_bytes(rows: int, cols: int, nvec: int) -> int:
+    return int(_load().qgemv_i8mc_workspace_bytes(rows, cols, nvec))
+
+
+def qgemv_batch_i8mc(w, xq, xd, y, rows: int, cols: int, nvec: int, workspace=None,
+                     stream=None) -> None:
+    """Q4_K y = W x for 1..8 vectors on the integer matrix cores, whatever the shape."""
+    lib = _load()
+    wsp, wsb = _ws(workspace)
+    _check("qgemv_batch_i8mc", lib.qgemv_batch_i8mc(
+        _ptr(w, name="w"), _ptr(xq, torch.int8, "xq"), _ptr(xd, torch.float32, "xd"),
+        _ptr(y, torch.float32, "y"), rows, cols, nvec, wsp, wsb, _stream(stream, y)))
+
+
+def qgemv_debug_partials_i8mc(w, xq, xd, P, S, rows: int, cols: int, nvec: int,
+                              stream=None) -> None:
+    lib = _load()
+    _check("qgemv_debug_partials_i8mc", lib.qgemv_debug_partials_i8mc(
+        _ptr(w, name="w"), _ptr(xq, torch.int8, "xq"), _ptr(xd, torch.float32, "xd"),
+        _ptr(P, torch.int32, "P"), _ptr(S, torch.int32, "S"), rows, cols, nvec,
+        _stream(stream, P)))
+
+
+def qgemv_fused_i8mc(w, x, y, rows: int, cols: int, nvec: int, xq_out=None, xd_out=None,
+                     workspace=None, stream=None) -> None:
+    lib = _load()
+    wsp, wsb = _ws(workspace)
+    _check("qgemv_fused_i8mc", lib.qgemv_fused_i8mc(
+        _ptr(w, name="w"), _ptr(x, torch.float32, "x"), _ptr(xq_out, torch.int8, "xq_out"),
+        _ptr(xd_out, torch.float32, "xd_out"), _ptr(y, torch.float32, "y"), rows, cols, nvec,
+        wsp, wsb, _stream(stream, y)))
 
 
 def qgemv_quantize_weights(wtype, w, out, rows: int, cols: int, stream=None) -> None:

@@ -24,7 +24,7 @@ OBJ = os.path.join(HERE, "_lib", "obj")
 LIB = os.path.join(HERE, "_lib", "libqgemv.so")
 
 SOURCES = ["gemv_multi.hip", "gemv_q4k.hip", "gemv_q6k.hip", "gemv_q40.hip", "gemv_q80.hip",
-           "api.cpp", "graph.cpp", "gemm_mfma.hip", "act_quant.hip", "reduce.hip", "weight_quant.hip", "read_probe.hip"]
+           "api.cpp", "graph.cpp", "gemm_mfma.hip", "gemm_i8.hip", "act_quant.hip", "reduce.hip", "weight_quant.hip", "read_probe.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",
@@ -32,9 +32,10 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=o
          "-Wall", "-Wno-unused-function", "-I", INCLUDE, "-I", CSRC]
 
 
-# Per-file additions. gemm_mfma.hip: matrix-core results in ordinary VGPRs, so the float
+# Per-file additions. gemm_mfma.hip, gemm_i8.hip: matrix-core results in ordinary VGPRs, so the float
 # work that reads them needs no accumulator-register copies (v_accvgpr_read) first.
-FILE_FLAGS = {"gemm_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+FILE_FLAGS = {"gemm_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+              "gemm_i8.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src: str) -> str:

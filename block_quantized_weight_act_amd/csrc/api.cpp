@@ -385,6 +385,126 @@ int run_mc(const void *w, const int8_t *xq, const float *xd, float *y, int32_t *
 
 // Several matrices with one activation (plain: act.xq / act.xd; fused: act.x and optionally
 // act.xq_out / act.xd_out): every check, then the launch description in a and s.
+// Q4_K with up to kMaxVec vectors on the integer matrix cores (gemm_i8.hip). The kernel takes
+// any 1..kMaxVec vectors (qgemv_batch_i8mc); qgemv_batch routes to it where it was measured
+// faster than the vector kernel: from 3 vectors on tensors of 128 MiB down to 8 vectors on
+// 16 MiB (i8_min_bytes). With few vectors the vector kernel's dot products hide under the
+// weight stream; on small tensors the time is the latency of a few loads per wave, where the
+// vector kernel (no activation staging) is ahead. A split holds at most
+// kI8MaxWaves * kI8SbPerWave super-blocks (the activation a workgroup stages in LDS); wider
+// rows are split into equal parts, added by the ordered reduce.
+int64_t i8_min_bytes(int32_t nvec) {
+    constexpr int64_t MiB = int64_t{1} << 20;
+    switch (nvec) {
+        case 3: return 128 * MiB;
+        case 4: return 96 * MiB;
+        case 5: return 48 * MiB;
+        case 6: return 32 * MiB;
+        case 7: return 24 * MiB;
+        case 8: return 16 * MiB;
+        default: return INT64_MAX;
+    }
+}
+
+bool i8_ok(int64_t rows, int64_t cols, int32_t nvec) {
+    return shape_ok_t(QGEMV_Q4K, rows, cols, nvec);
+}
+
+bool i8_auto(int wtype, int64_t rows, int64_t cols, int32_t nvec) {
+    return wtype == QGEMV_Q4K && i8_ok(rows, cols, nvec) &&
+           static_cast<int64_t>(weight_bytes(QGEMV_Q4K, rows, cols)) >= i8_min_bytes(nvec);
+}
+
+struct I8Plan {
+    int waves, splits, sbps, row_tiles;
+};
+
+I8Plan make_i8_plan(int64_t rows, int64_t cols) {
+    I8Plan p{};
+    const int64_t nb = cols / kQK;
+    const int64_t most = int64_t{kI8MaxWaves} * kI8SbPerWave;
+    const int64_t parts = (nb + most - 1) / most;
+    const int64_t per = (nb + parts - 1) / parts;
+    p.waves = static_cast<int>((per + kI8SbPerWave - 1) / kI8SbPerWave);
+    p.sbps = p.waves * kI8SbPerWave;
+    p.splits = static_cast<int>((nb + p.sbps - 1) / p.sbps);
+    p.row_tiles = static_cast<int>((rows + 15) / 16);
+    return p;
+}
+
+size_t i8_ws_bytes(const I8Plan &p, int64_t rows, int32_t nvec) {
+    return p.splits > 1 ? static_cast<size_t>(p.splits) * nvec * rows * sizeof(float) : 0;
+}
+
+// y (or, with P, the debug partials P and S instead) of a Q4_K product on the integer matrix
+// cores, from codes and scales or (act.x) from the float32 activation; arguments checked as
+// for the vector kernels.
+int run_i8(const void *w, const Activation &act, float *y, int32_t *P, int32_t *S, int64_t rows,
+           int64_t cols, int32_t nvec, void *ws, size_t ws_bytes, hipStream_t stream) {
+    const bool debug = P != nullptr;
+    const size_t ybytes = static_cast<size_t>(nvec) * rows * sizeof(float);
+    const size_t pbytes = static_cast<size_t>(nvec) * rows * (cols / 32) * sizeof(int32_t);
+    const size_t wb = weight_bytes(QGEMV_Q4K, rows, cols);
+    int st;
+    if (act.x) {
+        if (debug || !w || !y || !i8_ok(rows, cols, nvec)) return QGEMV_EINVAL;
+        if (!aligned(w, 16) || !aligned(y, 4)) return QGEMV_EALIGN;
+        if (overlaps(y, ybytes, w, wb)) return QGEMV_EINVAL;
+        st = check_fused_act(act, w, wb, y, ybytes, cols, nvec);
+    } else {
+        st = check_gemv_args(QGEMV_Q4K, w, act.xq, act.xd, debug ? static_cast<const void *>(P) : y,
+                             debug ? pbytes : ybytes, rows, cols, nvec);
+    }
+    if (st != QGEMV_OK) return st;
+    const int8_t *xq = act.xq;
+    const float *xd = act.xd;
+    const I8Plan p = make_i8_plan(rows, cols);
+    const size_t need = debug ? 0 : i8_ws_bytes(p, rows, nvec);
+    const size_t qb = static_cast<size_t>(nvec) * cols;
+    const size_t db = static_cast<size_t>(nvec) * (cols / 32) * sizeof(float);
+    if (debug) {
+        const size_t sbytes = static_cast<size_t>(nvec) * (cols / 32) * sizeof(int32_t);
+        if (!aligned(S, 4)) return QGEMV_EALIGN;
+        if (overlaps(S, sbytes, P, pbytes) || overlaps(S, sbytes, w, wb) ||
+            overlaps(S, sbytes, xq, qb) || overlaps(S, sbytes, xd, db))
+            return QGEMV_EINVAL;
+    }
+    if (need > 0) {
+        if (!ws || ws_bytes < need) return QGEMV_EWORKSPACE;
+        if (!aligned(ws, 4)) return QGEMV_EALIGN;
+        if (overlaps(ws, need, w, wb) || overlaps(ws, need, y, ybytes) ||
+            (xq && overlaps(ws, need, xq, qb)) || (xd && overlaps(ws, need, xd, db)) ||
+            (act.x && overlaps(ws, need, act.x, qb * sizeof(float))) ||
+            (act.xq_out && (overlaps(ws, need, act.xq_out, qb) || overlaps(ws, need, act.xd_out, db))))
+            return QGEMV_EINVAL;
+    }
+    GemmArgs a{};
+    a.w = static_cast<const uint8_t *>(w);
+    a.xq = xq;
+    a.xd = xd;
+    a.x = act.x;
+    a.xq_out = act.xq_out;
+    a.xd_out = act.xd_out;
+    a.out = need > 0 ? static_cast<float *>(ws) : y;
+    a.P = P;
+    a.S = S;
+    a.rows = static_cast<int32_t>(rows);
+    a.nb = static_cast<int32_t>(cols / kQK);
+    a.nvec = nvec;
+    a.sb_per_split = p.sbps;
+    a.row_tiles = p.row_tiles;
+    a.groups = 1;
+    a.splits = p.splits;
+    hipError_t e = launch_gemm_q4k_i8(a, p.waves, debug, stream);
+    if (e != hipSuccess) return hip_fail(e);
+    if (need > 0) {
+        e = launch_splitk_reduce(static_cast<const float *>(ws), y,
+                                 static_cast<int64_t>(nvec) * rows, p.splits, stream);
+        if (e != hipSuccess) return hip_fail(e);
+    }
+    return QGEMV_OK;
+}
+
 int prepare_multi(const qgemv_matrix *mats, int32_t nmats, const Activation &act, int64_t cols,
                   int32_t nvec, MultiArgs &a, LaunchShape &s, double &wbytes) {
     if (!mats || nmats < 1 || nmats > kMaxMats || !shape_ok(1, cols, nvec)) return QGEMV_EINVAL;
@@ -517,6 +637,7 @@ int qgemv_quantize_act(const float *x, int8_t *xq, float *xd, int64_t cols, int3
 size_t qgemv_workspace_bytes(int wtype, int64_t rows, int64_t cols, int32_t nvec) {
     if (mc_shape_ok(wtype, rows, cols, nvec))
         return mc_ws_bytes(make_mc_plan(rows, cols, nvec), rows, cols, nvec);
+    if (i8_auto(wtype, rows, cols, nvec)) return i8_ws_bytes(make_i8_plan(rows, cols), rows, nvec);
     if (grouped_shape_ok(wtype, rows, cols, nvec)) {
         // groups of up to kMaxVec vectors, one after another on the stream, share the workspace
         const int32_t g = std::min<int32_t>(nvec, kMaxVec);
@@ -583,6 +704,13 @@ int qgemv_batch(int wtype, const void *w, const int8_t *xq, const float *xd, flo
         }
         return QGEMV_OK;
     }
+    if (i8_auto(wtype, rows, cols, nvec)) {
+        Activation act;
+        act.xq = xq;
+        act.xd = xd;
+        return run_i8(w, act, y, nullptr, nullptr, rows, cols, nvec, workspace, workspace_bytes,
+                      stream);
+    }
     if (!shape_ok_t(wtype, rows, cols, nvec))
         return QGEMV_EINVAL;
     Activation act;
@@ -595,6 +723,10 @@ int qgemv_batch(int wtype, const void *w, const int8_t *xq, const float *xd, flo
 int qgemv_fused_launches(int wtype, int64_t rows, int64_t cols, int32_t nvec, int with_outputs) {
     if (!shape_ok_t(wtype, rows, cols, nvec)) return 0;
     if (!with_outputs) return 1;
+    // The integer matrix-core kernel: quantizing once (into the caller's code outputs) and
+    // running the product from the codes was measured faster than every workgroup quantizing
+    // the split's activation itself.
+    if (i8_auto(wtype, rows, cols, nvec)) return 2;
     // Every workgroup of the fused kernel quantizes the whole activation slice its lanes read.
     // When that slice is large next to the workgroup's share of the weights (wide rows, many
     // vectors, few rows per workgroup), the repeated quantization costs more than a second
@@ -622,13 +754,22 @@ int qgemv_fused(int wtype, const void *w, const float *x, int8_t *xq_out, float 
         int st = check_fused_act(act, w, weight_bytes(wtype, rows, cols), y,
                                  static_cast<size_t>(nvec) * rows * sizeof(float), cols, nvec);
         if (st != QGEMV_OK) return st;
+        // the product's workspace is checked before the quantization goes out
+        const size_t need = qgemv_workspace_bytes(wtype, rows, cols, nvec);
+        if (need > 0 && (!workspace || workspace_bytes < need)) return QGEMV_EWORKSPACE;
         st = qgemv_quantize_act(x, xq_out, xd_out, cols, nvec, stream);
         if (st != QGEMV_OK) return st;
         Activation q;
         q.xq = xq_out;
         q.xd = xd_out;
+        if (i8_auto(wtype, rows, cols, nvec))
+            return run_i8(w, q, y, nullptr, nullptr, rows, cols, nvec, workspace, workspace_bytes,
+                          stream);
         return run_gemv(wtype, w, q, y, rows, cols, nvec, plan, workspace, workspace_bytes, stream);
     }
+    if (i8_auto(wtype, rows, cols, nvec))
+        return run_i8(w, act, y, nullptr, nullptr, rows, cols, nvec, workspace, workspace_bytes,
+                      stream);
     return run_gemv(wtype, w, act, y, rows, cols, nvec, plan, workspace, workspace_bytes, stream);
 }
 
@@ -683,6 +824,42 @@ int qgemv_multi_fused(const qgemv_matrix *mats, int32_t nmats, const float *x, i
     return launch_multi(a, s, nvec, stream);
 }
 
+size_t qgemv_i8mc_workspace_bytes(int64_t rows, int64_t cols, int32_t nvec) {
+    if (!i8_ok(rows, cols, nvec)) return 0;
+    return i8_ws_bytes(make_i8_plan(rows, cols), rows, nvec);
+}
+
+int qgemv_batch_i8mc(const void *w, const int8_t *xq, const float *xd, float *y, int64_t rows,
+                     int64_t cols, int32_t nvec, void *workspace, size_t workspace_bytes,
+                     hipStream_t stream) {
+    Activation act;
+    act.xq = xq;
+    act.xd = xd;
+    return run_i8(w, act, y, nullptr, nullptr, rows, cols, nvec, workspace, workspace_bytes,
+                  stream);
+}
+
+int qgemv_debug_partials_i8mc(const void *w, const int8_t *xq, const float *xd, int32_t *P,
+                              int32_t *S, int64_t rows, int64_t cols, int32_t nvec,
+                              hipStream_t stream) {
+    if (!P || !S) return QGEMV_EINVAL;
+    Activation act;
+    act.xq = xq;
+    act.xd = xd;
+    return run_i8(w, act, nullptr, P, S, rows, cols, nvec, nullptr, 0, stream);
+}
+
+int qgemv_fused_i8mc(const void *w, const float *x, int8_t *xq_out, float *xd_out, float *y,
+                     int64_t rows, int64_t cols, int32_t nvec, void *workspace,
+                     size_t workspace_bytes, hipStream_t stream) {
+    Activation act;
+    act.x = x;
+    act.xq_out = xq_out;
+    act.xd_out = xd_out;
+    return run_i8(w, act, y, nullptr, nullptr, rows, cols, nvec, workspace, workspace_bytes,
+                  stream);
+}
+
 int qgemv_q4k(const void *w, const int8_t *xq, const float *xd, float *y, int64_t rows,
               int64_t cols, void *workspace, size_t workspace_bytes, hipStream_t stream) {
     return qgemv_batch(QGEMV_Q4K, w, xq, xd, y, rows, cols, 1, workspace, workspace_bytes, stream);
@@ -710,6 +887,12 @@ int qgemv_debug_partials(int wtype, const void *w, const int8_t *xq, const float
             return QGEMV_EINVAL;
         return run_mc(w, xq, xd, nullptr, P, S, rows, cols, nvec, workspace, workspace_bytes,
                       stream);
+    }
+    if (i8_auto(wtype, rows, cols, nvec)) {
+        Activation act;
+        act.xq = xq;
+        act.xd = xd;
+        return run_i8(w, act, nullptr, P, S, rows, cols, nvec, nullptr, 0, stream);
     }
     const int64_t nsub = wtype == QGEMV_Q6K ? cols / 16 : cols / 32;
     const size_t pbytes = static_cast<size_t>(nvec) * rows * nsub * sizeof(int32_t);

@@ -1,0 +1,424 @@
+// Q4_K weights x a few (2..8) int8 activation vectors on the integer matrix cores
+// (v_mfma_i32_16x16x64_i8).
+//
+// With several vectors the vector kernel's int8 4-way dot products, eight per 32-column block
+// and vector, become the bulk of its work (oxinfer README, "Speculative decoding": the
+// multi-token int8 decode variants are instruction-bound at Q4). The same exact integer
+// sub-block products P = sum q * xq are formed here on the matrix cores, where one instruction
+// does 16 rows x 64 columns x 16 outputs:
+//
+//  * The weight operand is the 4-bit codes themselves as int8 (two masks per 8 codes); the
+//    activation operand is the int8 codes as stored. Nothing is scaled inside the product, so
+//    the int32 result is P exactly.
+//  * A product covers two 32-column blocks: the 16 output columns are 8 vectors x the two
+//    blocks, and the activation operand holds zeros where a vector's block does not meet the
+//    weight columns of the other block. Every output is then the P of one (vector, block, row).
+//  * The float work per output and block is the exact integer sc * P, its conversion and one
+//    fma with the activation scale; the super-scale d is applied once per super-block. The min
+//    term dmin * m * xd * S (S = sum of the block's codes) is a contraction over the blocks of
+//    dmin * m (block, row) with -xd * S (vector, block), done on the float32 matrix cores
+//    (v_mfma_f32_16x16x4_f32, four blocks per instruction) straight into the accumulator.
+//
+// Work split: a workgroup of up to 4 waves takes a row tile of 16 rows at a time over one
+// column split of up to 8 super-blocks, each wave two super-blocks; the waves' sums are added
+// in LDS in wave order. The split's activation (codes in the operand order, scales, -xd * S) is
+// staged in LDS once per workgroup and held in registers by each wave for its super-blocks, so
+// the loop over row tiles reads only weights: 4 x 8 code bytes and a 16-byte header per lane
+// and super-block, the next tile's loads issued before the current tile's arithmetic.
+//
+// Lane layouts (16 x 16 products, checked on gfx950): lane l holds operand row / column l % 16,
+// slots of lane group g = l / 16; result element i is row 4 g + i, column l % 16. Which column
+// each (group, slot) stands for is free as long as both operands agree; here the weight lane of
+// group g takes the 8 code bytes 8 (g % 2) .. + 7 of block 2 t + g / 2 of the pair t, slots
+// 0..7 their low nibbles (columns 8 (g % 2) + 0..7) and 8..15 their high nibbles (columns
+// 16 + 8 (g % 2) + 0..7). The staged activation of a block is stored in that order.
+#include <algorithm>
+#include <atomic>
+
+#include "device_common.h"
+#include "qgemv_internal.h"
+
+namespace qgemv {
+
+namespace {
+
+typedef int v4i_t __attribute__((ext_vector_type(4)));
+typedef float v4f_t __attribute__((ext_vector_type(4)));
+
+constexpr int kSbw = kI8SbPerWave;                  // super-blocks per wave
+
+// LDS of a workgroup of `waves` waves (split of kSbw * waves super-blocks): 9 rows of codes
+// (8 vectors, then zeros) of pitch columns + 16 bytes (the 16 spread the rows over the banks),
+// the scales and -xd * S of the split's blocks (8 vectors each), and two slots of the waves'
+// sums of a row tile (16 rows x 8 vectors per wave).
+__host__ __device__ constexpr int code_pitch(int waves) { return waves * kSbw * 256 + 16; }
+__host__ __device__ constexpr int lds_bytes(int waves) {
+    return 9 * code_pitch(waves) + 2 * (waves * kSbw * 8) * 8 * 4 + 2 * waves * 16 * 8 * 4;
+}
+
+// s_waitcnt immediate: no vector-memory load outstanding, the other counters not waited for
+// (vmcnt bits 3:0 and 15:14, expcnt 6:4 at its maximum 7, lgkmcnt 11:8 at its maximum 15).
+constexpr int kWaitVm0 = (7 << 4) | (15 << 8);
+
+// Staging passes of the fused form at most: each group of 8 lanes quantizes one 32-column block
+// per pass; 8 vectors x 8 nsb blocks over 8 waves groups, with nsb <= kSbw waves. The form from
+// codes takes a block per 2 lanes, a quarter of the passes.
+constexpr int kStagePasses = 8 * kSbw;
+
+template <int MODE>
+__global__ void __launch_bounds__(256) gemm_q4k_i8_kernel(GemmArgs a) {
+    constexpr bool DBG = MODE == kModeDebug;
+    constexpr bool FUSED = MODE == kModeFused;
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds_i8[];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int waves = blockDim.x >> 6;
+    const int pitch = code_pitch(waves);
+    const int sblk = waves * kSbw * 8;
+    uint8_t *const xq_s = lds_i8;                   // [9][pitch]: vectors' codes (block-permuted), zeros
+    float *const xd_s = reinterpret_cast<float *>(lds_i8 + 9 * pitch);   // [sblk][8]
+    float *const xs_s = xd_s + sblk * 8;            // [sblk][8]: -xd * S
+    float *const red_s = xs_s + sblk * 8;           // [2][waves][16][8]
+    const int r = lane & 15;        // tile row of this lane's weights and outputs
+    const int g = lane >> 4;        // lane group
+    const int q = g >> 1;           // block of the pair this lane's weights and outputs are in
+    const int rows = a.rows, nb = a.nb, nvec = a.nvec;
+    const int nbk = nb * 8;
+    const int row_tiles = a.row_tiles;
+    const int sb_lo = blockIdx.y * a.sb_per_split;
+    const int sb_hi = min(nb, sb_lo + a.sb_per_split);
+    const int nsb = sb_hi - sb_lo;
+    const int wsb = wave * kSbw;    // this wave's first super-block, relative to sb_lo
+    const uint8_t *hplane = a.w + static_cast<int64_t>(rows) * nb * 128;
+
+    int rt = blockIdx.x;
+    if (rt >= row_tiles) return;    // the whole workgroup (never taken: grid <= row tiles)
+
+    // One row tile's loads per super-block: two 16-byte code chunks and the header. The four
+    // lanes of a row read the 64 bytes of chunks 4 i .. 4 i + 3 together (i = 0, 1): lane group
+    // g takes chunk 4 i + pc, pc = 2 (g % 2) + g / 2, so the lanes of even groups hold the
+    // chunks of pairs t = 0 and 2 and those of odd groups the chunks of pairs 1 and 3 (block
+    // 2 t + g / 2 each); one exchange between the groups (in `products`) then gives every lane
+    // the half it multiplies. A wave with fewer super-blocks than kSbw (the split's end) reloads
+    // the split's last one, unused. Rows past the matrix read its last row (not stored).
+    const int pc = 2 * (g & 1) + (g >> 1);
+    auto issue = [&](int tile, uint4 (&c)[kSbw][2], uint4 (&h)[kSbw]) {
+        const int row = min(tile * 16 + r, rows - 1);
+#pragma unroll
+        for (int k = 0; k < kSbw; k++) {
+            const int sb = sb_lo + min(wsb + k, nsb - 1);
+            const int64_t blk = static_cast<int64_t>(row) * nb + sb;
+            const uint8_t *src = a.w + blk * 128 + 16 * pc;
+            c[k][0] = load16(src);
+            c[k][1] = load16(src + 64);
+            h[k] = load16(hplane + blk * 16);
+        }
+    };
+    uint4 cw[kSbw][2];
+    uint4 hd[kSbw];
+    issue(rt, cw, hd);
+
+    // ---- the split's activation into LDS: codes permuted per block (columns 0-7, 16-23,
+    //      8-15, 24-31), scales and -xd * S; zeros for vectors past nvec. All loads go out
+    //      first. From codes: 2 lanes per block (16 columns each); the fused form quantizes
+    //      the float32 block itself, 8 lanes per block (4 columns each), and the first
+    //      workgroup of the split also stores the codes and scales ----
+    for (int i = tid; i < pitch / 16; i += blockDim.x)
+        *reinterpret_cast<uint4 *>(xq_s + 8 * pitch + 16 * i) = make_uint4(0u, 0u, 0u, 0u);
+    {
+        const int nblk = nsb * 8;
+        const int items = 8 * nblk;                     // (vector, block), vector-major
+        for (int it = nvec * nblk + tid; it < items; it += blockDim.x) {
+            const int v = it / nblk, b = it - v * nblk;
+            xd_s[b * 8 + v] = 0.0f;
+            xs_s[b * 8 + v] = 0.0f;
+        }
+        if constexpr (FUSED) {
+            const int per_pass = static_cast<int>(blockDim.x) >> 3;
+            const int passes = (nvec * nblk + per_pass - 1) / per_pass;   // <= kStagePasses
+            const int j8 = tid & 7;
+            // dword of the permuted block image holding columns 4 j8 .. 4 j8 + 3
+            const int pd = j8 + ((j8 >> 1) == 1 ? 2 : ((j8 >> 1) == 2 ? -2 : 0));
+            float4 xv[kStagePasses];
+#pragma unroll
+            for (int ps = 0; ps < kStagePasses; ps++) {
+                const int item = ps * per_pass + (tid >> 3);
+                const int v = item / nblk;
+                const int64_t gb = static_cast<int64_t>(v) * nbk + sb_lo * 8 + (item - v * nblk);
+                xv[ps] = ps < passes && v < nvec
+                             ? *reinterpret_cast<const float4 *>(a.x + gb * 32 + 4 * j8)
+                             : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            }
+#pragma unroll
+            for (int ps = 0; ps < kStagePasses; ps++) {
+                if (ps < passes) {            // the same in every lane of the workgroup
+                    const int item = ps * per_pass + (tid >> 3);
+                    const int v = item / nblk, b = item - v * nblk;
+                    const int64_t gb = static_cast<int64_t>(v) * nbk + sb_lo * 8 + b;
+                    const ActQuad aq = quantize_act_quad(xv[ps]);   // all lanes: DPP over 8
+                    // the block's code sum: exact in float32 (|S| <= 4064)
+                    const float s = group_sum<8>(static_cast<float>(byte_sum(aq.codes, 0)));
+                    if (v < nvec) {
+                        if (a.xq_out != nullptr && blockIdx.x == 0) {
+                            reinterpret_cast<uint32_t *>(a.xq_out)[gb * 8 + j8] = aq.codes;
+                            if (j8 == 0) a.xd_out[gb] = aq.scale;
+                        }
+                        *reinterpret_cast<uint32_t *>(xq_s + v * pitch + 32 * b + 4 * pd) = aq.codes;
+                        if (j8 == 0) {
+                            xd_s[b * 8 + v] = aq.scale;
+                            xs_s[b * 8 + v] = -(aq.scale * s);
+                        }
+                    }
+                }
+            }
+        } else {
+            const int per_pass = static_cast<int>(blockDim.x) >> 1;
+            const int passes = (nvec * nblk + per_pass - 1) / per_pass;   // <= kStagePasses / 4
+            const int h = tid & 1;
+            uint4 cv[kStagePasses / 4];
+            float sv[kStagePasses / 4];
+#pragma unroll
+            for (int ps = 0; ps < kStagePasses / 4; ps++) {
+                const int item = ps * per_pass + (tid >> 1);
+                const int v = item / nblk;
+                const int64_t gb = static_cast<int64_t>(v) * nbk + sb_lo * 8 + (item - v * nblk);
+                const bool live = ps < passes && v < nvec;
+                cv[ps] = live ? load16(a.xq + gb * 32 + 16 * h) : make_uint4(0u, 0u, 0u, 0u);
+                sv[ps] = live ? a.xd[gb] : 0.0f;
+            }
+#pragma unroll
+            for (int ps = 0; ps < kStagePasses / 4; ps++) {
+                if (ps < passes) {            // the same in every lane of the workgroup
+                    const int item = ps * per_pass + (tid >> 1);
+                    const int v = item / nblk, b = item - v * nblk;
+                    const uint4 c = cv[ps];
+                    // the block's code sum (the two halves added across the lane pair): exact
+                    const int half = byte_sum(c.x, byte_sum(c.y, byte_sum(c.z, byte_sum(c.w, 0))));
+                    const int s = half + __builtin_amdgcn_update_dpp(0, half, kDppXor1, 0xF, 0xF, false);
+                    if (v < nvec) {
+                        // columns 16 h .. + 7 to position 8 h, columns 16 h + 8 .. + 15 to 16 + 8 h
+                        uint8_t *dst = xq_s + v * pitch + 32 * b;
+                        *reinterpret_cast<uint2 *>(dst + 8 * h) = make_uint2(c.x, c.y);
+                        *reinterpret_cast<uint2 *>(dst + 16 + 8 * h) = make_uint2(c.z, c.w);
+                        if (h == 0) {
+                            xd_s[b * 8 + v] = sv[ps];
+                            xs_s[b * 8 + v] = -(sv[ps] * static_cast<float>(s));
+                            if (DBG && blockIdx.x == 0)
+                                a.S[static_cast<int64_t>(v) * nbk + sb_lo * 8 + b] = s;
+                        }
+                    }
+                }
+            }
+        }
+    }
+    // Every load so far has landed (the first tile's weights came before the staging's loads,
+    // which are in use): waiting for all of them here also settles the staging loads of passes
+    // past `passes`, issued but unused, which would otherwise count as in flight at the head of
+    // the loop below and make the compiler wait for every load there on each iteration.
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    __syncthreads();
+
+    // ---- where this lane reads its activation operands in LDS (for every row tile): the
+    //      operand row of vector av, block ap of each pair (the zero row where the vector is
+    //      past nvec or the block does not meet this lane group's weights), the scales of the
+    //      output vectors 4 (g % 2) .. + 3, and the min-term operands ----
+    const int av = lane & 7, ap = (lane >> 3) & 1;
+    const uint8_t *arow = xq_s + (((g >> 1) == ap && av < nvec) ? av : 8) * pitch + ap * 32 + 16 * (g & 1);
+    const float *xrow = xd_s + q * 8 + 4 * (g & 1);
+    float mina[kSbw][2];
+    {
+        const int am = lane & 15;
+#pragma unroll
+        for (int k = 0; k < kSbw; k++) {
+            const int sbl = min(wsb + k, nsb - 1);
+#pragma unroll
+            for (int u = 0; u < 2; u++)
+                mina[k][u] = am < 8 ? xs_s[(sbl * 8 + 4 * u + g) * 8 + am] : 0.0f;
+        }
+    }
+
+    float *out = DBG ? nullptr : a.out + static_cast<int64_t>(blockIdx.y) * nvec * rows;
+    int slot = 0;
+    // Row tile `rt` from the loaded registers (cw, hd): its products, folded to this lane's two
+    // outputs (vectors vv and vv + 2 of row r, vv = 4 (g % 2) + l / 32).
+    auto products = [&](int rt, float (&fold)[2]) {
+        v4f_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int k = 0; k < kSbw; k++) {
+            if (wsb + k < nsb) {            // the same in every lane of the wave
+                const uint4 h = hd[k];
+                const float d = half_to_float(h.x & 0xFFFFu);
+                const float dmin = half_to_float(h.x >> 16);
+                // sub-scale of block 2 t + q: low 4 bits at y bit 4 (2 t + q), high 2 bits at w bit
+                // 2 (2 t + q)
+                const uint32_t ysh = h.y >> (4 * q), wsh = h.w >> (2 * q);
+                // The exchange: the half-chunks an even group sends (the upper halves of its
+                // chunks) swap with those its odd neighbour sends (the lower halves of its
+                // chunks), v_permlane16_swap pairing rows of 16 lanes 0-1 and 2-3. Afterwards
+                // pair t's 8 code bytes are dwords 2 (t % 2), + 1 of chunk register t / 2.
+                uint32_t pw[4][2];
+#pragma unroll
+                for (int i = 0; i < 2; i++) {
+                    const auto s0 = __builtin_amdgcn_permlane16_swap(cw[k][i].x, cw[k][i].z, false, false);
+                    const auto s1 = __builtin_amdgcn_permlane16_swap(cw[k][i].y, cw[k][i].w, false, false);
+                    const uint32_t x = s0[0], z = s0[1], y = s1[0], w = s1[1];
+                    pw[2 * i][0] = x;
+                    pw[2 * i][1] = y;
+                    pw[2 * i + 1][0] = z;
+                    pw[2 * i + 1][1] = w;
+                }
+                v4f_t tt;
+#pragma unroll
+                for (int t = 0; t < 4; t++) {
+                    const uint2 c = make_uint2(pw[t][0], pw[t][1]);
+                    const v4i_t B = {static_cast<int>(c.x & 0x0F0F0F0Fu),
+                                     static_cast<int>(c.y & 0x0F0F0F0Fu),
+                                     static_cast<int>((c.x >> 4) & 0x0F0F0F0Fu),
+                                     static_cast<int>((c.y >> 4) & 0x0F0F0F0Fu)};
+                    const v4i_t zero = {0, 0, 0, 0};
+                    const int blk = (wsb + k) * 8 + 2 * t;      // first block of the pair, in the split
+                    const v4i_t A = *reinterpret_cast<const v4i_t *>(arow + blk * 32);
+                    const v4f_t xdv = *reinterpret_cast<const v4f_t *>(xrow + blk * 8);
+                    const v4i_t P = __builtin_amdgcn_mfma_i32_16x16x64_i8(A, B, zero, 0, 0, 0);
+                    const int sc = static_cast<int>(((ysh >> (8 * t)) & 15u) | (((wsh >> (4 * t)) & 3u) << 4));
+#pragma unroll
+                    for (int i = 0; i < 4; i++) {
+                        const float ps = static_cast<float>(__mul24(sc, P[i]));   // exact: < 2^22
+                        tt[i] = t == 0 ? xdv[i] * ps : fmaf(xdv[i], ps, tt[i]);
+                    }
+                    if (DBG) {
+                        const int row = rt * 16 + r;
+                        const int gblk = sb_lo * 8 + blk + q;
+#pragma unroll
+                        for (int i = 0; i < 4; i++) {
+                            const int v = 4 * (g & 1) + i;
+                            if (v < nvec && row < rows)
+                                a.P[(static_cast<int64_t>(v) * rows + row) * nbk + gblk] = P[i];
+                        }
+                    }
+                }
+#pragma unroll
+                for (int i = 0; i < 4; i++) acc[i] = fmaf(d, tt[i], acc[i]);
+                // min terms of blocks 4 u + g: m low 4 bits at z bit 4 (4 u + g), high 2 bits at w
+                // bit 16 + 2 (4 u + g)
+                const uint32_t zsh = h.z >> (4 * g), wsh2 = h.w >> (16 + 2 * g);
+#pragma unroll
+                for (int u = 0; u < 2; u++) {
+                    const uint32_t m = ((zsh >> (16 * u)) & 15u) | (((wsh2 >> (8 * u)) & 3u) << 4);
+                    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(mina[k][u], dmin * static_cast<float>(m),
+                                                              acc, 0, 0, 0);
+                }
+            }
+        }
+
+        // ---- the two blocks of each pair sit in lane groups g and g + 2 (lanes l, l + 32).
+        //      One swap of the upper half of element 2 e with the lower half of element
+        //      2 e + 1 leaves, after one add, element 2 e's pair sum in lanes 0-31 and element
+        //      2 e + 1's in lanes 32-63: lane l then holds vectors vv and vv + 2 of row r, with
+        //      vv = 4 (g % 2) + l / 32. The waves' sums are then added in LDS, in wave order ----
+        // (The elements are copied to scalars first: __builtin_bit_cast of a vector element
+        // read the vector's first element with this compiler.)
+#pragma unroll
+        for (int e = 0; e < 2; e++) {
+            const float lo = acc[2 * e], hi = acc[2 * e + 1];
+            const auto sw = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, lo),
+                                                             __builtin_bit_cast(uint32_t, hi),
+                                                             false, false);
+            const uint32_t s0 = sw[0], s1 = sw[1];
+            fold[e] = __builtin_bit_cast(float, s0) + __builtin_bit_cast(float, s1);
+        }
+    };
+    // The sums over the workgroup's waves (in wave order) and the stores of row tile rt.
+    auto finish = [&](int rt, const float (&fold)[2]) {
+        if (!DBG) {
+            const int vv = 4 * (g & 1) + (lane >> 5);
+            red_s[((slot * waves + wave) * 16 + r) * 8 + vv] = fold[0];
+            red_s[((slot * waves + wave) * 16 + r) * 8 + vv + 2] = fold[1];
+            __syncthreads();
+            // 128 outputs: one per lane of the first two waves, or two per lane of a lone wave
+            // (a fixed number of stores per lane, so the compiler can count the loads still
+            // in flight past them instead of waiting for all of them)
+#pragma unroll
+            for (int i = 0; i < 2; i++) {
+                const int e = tid + 64 * i;
+                const int v = e >> 4, rr = e & 15;
+                const int row = rt * 16 + rr;
+                if ((i == 0 || waves == 1) && e < 128 && v < nvec && row < rows) {
+                    float y = red_s[((slot * waves) * 16 + rr) * 8 + v];
+#pragma unroll
+                    for (int w = 1; w < kI8MaxWaves; w++)
+                        if (w < waves) y += red_s[((slot * waves + w) * 16 + rr) * 8 + v];
+                    out[static_cast<int64_t>(v) * rows + row] = y;
+                }
+            }
+            slot ^= 1;
+        }
+    };
+    // The next tile's loads go out into the same registers as soon as this tile's arithmetic
+    // has read them, ahead of the sums over the waves and the stores (unconditionally: past the
+    // last tile they reload it, unused).
+    const int stride = static_cast<int>(gridDim.x);
+    while (true) {
+        float fold[2];
+        __builtin_amdgcn_sched_barrier(0);
+        products(rt, fold);
+        __builtin_amdgcn_sched_barrier(0);
+        issue(min(rt + stride, row_tiles - 1), cw, hd);
+        __builtin_amdgcn_sched_barrier(0);
+        finish(rt, fold);
+        rt += stride;
+        if (rt >= row_tiles) break;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_gemm_q4k_i8(const GemmArgs &a, int waves, bool debug, hipStream_t stream) {
+    if (waves < 1 || waves > kI8MaxWaves || a.sb_per_split != kSbw * waves || a.nvec < 1 ||
+        a.nvec > kMaxVec || a.row_tiles < 1 || a.splits < 1)
+        return hipErrorInvalidValue;
+    // Workgroups of this size resident at once (registers and LDS) times the CUs, looked up
+    // once per form and size; each workgroup then takes an equal share of the row tiles (the
+    // staging is per workgroup). Concurrent first calls store the same values.
+    static std::atomic<int> per_cu[3][kI8MaxWaves] = {};
+    static std::atomic<int> cus{0};
+    if (cus.load(std::memory_order_relaxed) == 0) {
+        int dev = 0, n = 0;
+        const bool ok = hipGetDevice(&dev) == hipSuccess &&
+                        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) ==
+                            hipSuccess &&
+                        n > 0;
+        cus.store(ok ? n : 256, std::memory_order_relaxed);
+    }
+    const int mode = debug ? kModeDebug : (a.x != nullptr ? kModeFused : kModePlain);
+    const int threads = 64 * waves;
+    const size_t lds = static_cast<size_t>(lds_bytes(waves));
+    std::atomic<int> &res = per_cu[mode][waves - 1];
+    if (res.load(std::memory_order_relaxed) == 0) {
+        int n = 0;
+        const hipError_t e =
+            mode == kModeDebug
+                ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gemm_q4k_i8_kernel<kModeDebug>, threads, lds)
+                : mode == kModeFused
+                      ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gemm_q4k_i8_kernel<kModeFused>, threads, lds)
+                      : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gemm_q4k_i8_kernel<kModePlain>, threads, lds);
+        res.store((e == hipSuccess && n > 0) ? n : 1, std::memory_order_relaxed);
+    }
+    const int64_t cap = std::max<int64_t>(
+        1, int64_t{res.load(std::memory_order_relaxed)} * cus.load(std::memory_order_relaxed) /
+               a.splits);
+    const int64_t per_wg = (a.row_tiles + cap - 1) / cap;
+    const int64_t blocks = (a.row_tiles + per_wg - 1) / per_wg;
+    const dim3 grid(static_cast<unsigned>(blocks), static_cast<unsigned>(a.splits));
+    const dim3 block(static_cast<unsigned>(threads));
+    if (mode == kModeDebug)
+        hipLaunchKernelGGL(gemm_q4k_i8_kernel<kModeDebug>, grid, block, lds, stream, a);
+    else if (mode == kModeFused)
+        hipLaunchKernelGGL(gemm_q4k_i8_kernel<kModeFused>, grid, block, lds, stream, a);
+    else
+        hipLaunchKernelGGL(gemm_q4k_i8_kernel<kModePlain>, grid, block, lds, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace qgemv

@@ -117,6 +117,10 @@ struct GemmArgs {
     int32_t *P;            // debug: [nvec][rows][cols/32] integer partials, or nullptr
     int32_t *S;            // debug: [nvec][cols/32] activation block sums, or nullptr
     uint8_t *tiles;        // workspace: the staged fp16 activation tiles (pre-pass output)
+    const float *x;        // integer-core path only: float32 activations [nvec][cols] that
+                           // the kernel quantizes itself, or nullptr (then xq, xd are read)
+    int8_t *xq_out;        // ... where it also stores the codes and scales (or nullptr)
+    float *xd_out;
     int32_t rows;
     int32_t nb;            // super-blocks per row
     int32_t nvec;
@@ -130,6 +134,15 @@ struct GemmArgs {
 constexpr int64_t mc_tile_bytes(int nt) { return int64_t{nt} * (32 * 512 + 8 * 32 * 8); }
 hipError_t launch_gemm_q4k_mfma(const GemmArgs &a, int nt, int row_tiles, int groups, int splits,
                                 bool debug, hipStream_t stream);
+
+// 2..8 vectors on the integer matrix cores (gemm_i8.hip): a workgroup of up to kI8MaxWaves
+// waves takes 16 rows at a time over a column split of kI8SbPerWave super-blocks per wave
+// (GemmArgs::sb_per_split == kI8SbPerWave * waves; row_tiles = ceil(rows / 16); splits
+// column splits writing out [splits][nvec][rows]; tiles unused). One launch; with x set, the
+// kernel quantizes the activation itself (the codes of qgemv_quantize_act, bit for bit).
+constexpr int kI8SbPerWave = 2;
+constexpr int kI8MaxWaves = 4;
+hipError_t launch_gemm_q4k_i8(const GemmArgs &a, int waves, bool debug, hipStream_t stream);
 
 // Host: record a HIP error (or a message) as this thread's last error text and return the
 // status the C ABI reports (QGEMV_EHIP, or `status`).

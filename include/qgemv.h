@@ -195,6 +195,42 @@ int qgemv_batch(int wtype, const void *w, const int8_t *xq, const float *xd, flo
                 size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Q4_K with 1 <= nvec <= 8 on the integer matrix cores (v_mfma_i32_16x16x64_i8),
+ * for any shape; qgemv_batch, qgemv_fused and qgemv_debug_partials take this path
+ * by themselves where it was measured faster than the vector kernel: tensors of at
+ * least 128, 96, 48, 32, 24 and 16 MiB for 3, 4, 5, 6, 7 and 8 vectors (there the
+ * vector kernel's 4-way dot products, one per 4 codes and vector, are the
+ * bottleneck; qgemv_fused with code outputs then quantizes once and runs this path
+ * from the codes).
+ * The same exact integer sub-block products P = sum q * xq (the product's int32
+ * results as they are), S = sum xq, then per block the float32 term
+ * xd * (sc * P) (sc * P exact) summed over the super-block and scaled by d, and the
+ * min terms dmin * m * (-xd * S) on the float32 matrix cores: y lies within the
+ * same bound of the exact product as the vector kernel's, with other rounding.
+ * Arguments as for qgemv_batch with wtype QGEMV_Q4K; the workspace
+ * (qgemv_i8mc_workspace_bytes: 0 unless cols > 2048, then partial sums of
+ * column splits of up to 2048 columns) may be NULL when that is 0.
+ */
+size_t qgemv_i8mc_workspace_bytes(int64_t rows, int64_t cols, int32_t nvec);
+int qgemv_batch_i8mc(const void *w, const int8_t *xq, const float *xd, float *y, int64_t rows,
+                     int64_t cols, int32_t nvec, void *workspace, size_t workspace_bytes,
+                     hipStream_t stream);
+
+/* The same from the float32 activation x (16-byte aligned), quantized inside the
+ * launch exactly as qgemv_quantize_act does (bit for bit); xq_out / xd_out (both
+ * NULL or both set, 4-byte aligned) optionally receive the codes and scales. */
+int qgemv_fused_i8mc(const void *w, const float *x, int8_t *xq_out, float *xd_out, float *y,
+                     int64_t rows, int64_t cols, int32_t nvec, void *workspace,
+                     size_t workspace_bytes, hipStream_t stream);
+
+/* Tests only: the integer partials P [nvec][rows][cols/32] and block sums
+ * S [nvec][cols/32] of this path, as qgemv_debug_partials writes them; no y, no
+ * workspace. */
+int qgemv_debug_partials_i8mc(const void *w, const int8_t *xq, const float *xd, int32_t *P,
+                              int32_t *S, int64_t rows, int64_t cols, int32_t nvec,
+                              hipStream_t stream);
+
+/*
  * Activation quantization and the product in one launch: x float32 [nvec][cols]
  * is quantized exactly as qgemv_quantize_act does (the same codes and scales,
  * bit for bit) by each workgroup for the columns it reads, then y = W x as in

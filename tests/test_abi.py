@@ -65,6 +65,50 @@ def test_batch_rejects_bad_arguments(kw, status):
     assert _call_batch(**kw) == status
 
 
+def _call_i8mc(w=A, xq=A + (1 << 30), xd=A + (2 << 30), y=A + (3 << 30), rows=64, cols=1024,
+               nvec=4, ws=None, wsb=0):
+    return qg._load().qgemv_batch_i8mc(w, xq, xd, y, rows, cols, nvec, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(w=None), EINVAL), (dict(y=None), EINVAL), (dict(cols=1000), EINVAL),
+    (dict(cols=0), EINVAL), (dict(rows=0), EINVAL), (dict(nvec=0), EINVAL),
+    (dict(nvec=9), EINVAL), (dict(w=A + 8), EALIGN), (dict(xq=A + (1 << 30) + 4), EALIGN),
+    (dict(y=A + 64), EINVAL), (dict(rows=1 << 31), EINVAL),
+    (dict(cols=4096), EWORKSPACE),                       # two column splits need partial sums
+    (dict(cols=4096, ws=A + (4 << 30), wsb=2 * 4 * 64 * 4 - 4), EWORKSPACE),
+    (dict(cols=4096, ws=A + (4 << 30) + 2, wsb=1 << 20), EALIGN),
+    (dict(cols=4096, ws=A + (3 << 30), wsb=1 << 20), EINVAL),   # workspace over y
+])
+def test_i8mc_rejects_bad_arguments(kw, status):
+    assert _call_i8mc(**kw) == status
+
+
+def test_i8mc_workspace_and_routing():
+    """Partial sums only past one split of 2048 columns; qgemv_batch takes this path (and its
+    workspace) from 4 vectors on tensors of at least 32 MiB."""
+    assert qg.qgemv_i8mc_workspace_bytes(64, 2048, 8) == 0
+    assert qg.qgemv_i8mc_workspace_bytes(64, 4096, 3) == 2 * 3 * 64 * 4
+    assert qg.qgemv_i8mc_workspace_bytes(10, 6144, 8) == 3 * 8 * 10 * 4
+    assert qg.qgemv_i8mc_workspace_bytes(64, 2304, 2) == 2 * 2 * 64 * 4   # 9 super-blocks: 6 + 3
+    assert qg.qgemv_i8mc_workspace_bytes(64, 4096, 9) == 0                 # invalid
+    big = (65536, 4096)                                                    # 144 MiB of Q4_K
+    assert qg.qgemv_workspace_bytes("q4k", *big, 4) == qg.qgemv_i8mc_workspace_bytes(*big, 4)
+    # the routing thresholds: 16 MiB at 8 vectors (16384 x 2048: 18 MiB), 128 MiB at 3
+    assert qg.qgemv_workspace_bytes("q4k", 16384, 4096, 8) == qg.qgemv_i8mc_workspace_bytes(16384, 4096, 8)
+    assert qg.qgemv_workspace_bytes("q4k", 16384, 4096, 3) != qg.qgemv_i8mc_workspace_bytes(16384, 4096, 3)
+    lib = qg._load()
+    # no workspace: refused as the integer path refuses it, before any launch
+    assert lib.qgemv_batch(1, A, A + (1 << 30), A + (2 << 30), A + (3 << 30), *big, 4, None, 0,
+                           None) == EWORKSPACE
+    fused = lib.qgemv_fused_i8mc
+    assert fused(A, A + (1 << 30) + 4, None, None, A + (3 << 30), 64, 1024, 4, None, 0, None) == EALIGN
+    assert fused(A, A + (1 << 30), A + (4 << 30), None, A + (3 << 30), 64, 1024, 4, None, 0,
+                 None) == EINVAL                                           # one output of two
+    assert lib.qgemv_debug_partials_i8mc(A, A + (1 << 30), A + (2 << 30), None, A + (4 << 30), 64,
+                                         1024, 4, None) == EINVAL
+
+
 def test_split_plan_without_workspace_is_rejected():
     lib = qg._load()
     plan = qg.Plan(16, 1, 4, 4, 0)
@@ -112,11 +156,14 @@ def test_other_entry_points_reject_bad_arguments():
 
 def test_fused_launch_count():
     """The one-launch kernel unless code outputs are wanted and the activation slice is large
-    next to a workgroup's share of the weights (then quantize once, then the product)."""
+    next to a workgroup's share of the weights (then quantize once, then the product), and
+    always on the integer matrix-core path (Q4_K, several vectors, a large tensor)."""
     assert qg.qgemv_fused_launches("q4k", 262144, 1536, 1) == 1
     assert qg.qgemv_fused_launches("q4k", 8192, 2048, 1) == 1
     assert qg.qgemv_fused_launches("q6k", 2048, 8192, 1) == 2
     assert qg.qgemv_fused_launches("q4k", 16384, 2048, 8) == 2
+    assert qg.qgemv_fused_launches("q4k", 262144, 1536, 8) == 2      # integer matrix cores
+    assert qg.qgemv_fused_launches("q4k", 262144, 1536, 8, with_outputs=False) == 1
     assert qg.qgemv_fused_launches("q4k", 16384, 2048, 8, with_outputs=False) == 1
     assert qg._load().qgemv_fused_launches(1, 0, 256, 1, 1) == 0
     assert qg._load().qgemv_fused_launches(5, 8, 256, 1, 1) == 0
