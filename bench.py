@@ -105,10 +105,13 @@ def algorithmic_bytes(wl, wbytes: int) -> dict:
     return {"gemv": gemv, "quantize_act": quant, "step": step}
 
 
-def roofline_kernel(wtype: str, plan: dict, nvec: int, launches: int) -> str:
+def roofline_kernel(wtype: str, plan: dict, nvec: int, launches: int, route: str = "vector") -> str:
     """The step's dominant kernel, as its template instance appears in kernel traces: the
     one-launch fused kernel (form 2) when qgemv_fused makes one launch for this shape, else the
-    GEMV kernel of the two-launch route (form 0, codes read from memory)."""
+    GEMV kernel of the two-launch route (form 0, codes read from memory); on the integer
+    matrix-core route the product kernel of that route."""
+    if route == "i8mc":
+        return "gemm_q4k_i8_kernel<%d>" % (2 if launches == 1 else 0)
     tag = {"q4k": "Q4K", "q6k": "Q6K", "q40": "Q40", "q80": "Q80"}[wtype]
     return "gemv_kernel<qgemv::%s, %d, %d, %d, %d>" % (tag, nvec, plan["lanes_per_row"],
                                                        plan["chunks_per_lane"],
@@ -176,7 +179,7 @@ def summarize_traffic(args) -> None:
     wbytes = qg.qgemv_weight_bytes(wl.wtype, wl.rows, wl.cols)
     launches = qg.qgemv_fused_launches(wl.wtype, wl.rows, wl.cols, wl.nvec, True)
     kname = roofline_kernel(wl.wtype, qg.qgemv_plan_for(wl.wtype, wl.rows, wl.cols, wl.nvec),
-                            wl.nvec, launches)
+                            wl.nvec, launches, qg.qgemv_route(wl.wtype, wl.rows, wl.cols, wl.nvec))
     per = {}
     for path, counter in zip(args.summarize_traffic, ("FETCH_SIZE", "WRITE_SIZE")):
         rows = [r for r in _counter_rows(path) if r["Counter_Name"] == counter]
@@ -907,6 +910,7 @@ def main():
     nbytes = algorithmic_bytes(wl, wbytes)
     value = nbytes["step"] / (ms_step * 1e-3) / 1e9
     launches = qg.qgemv_fused_launches(wl.wtype, wl.rows, wl.cols, wl.nvec, True)
+    route = qg.qgemv_route(wl.wtype, wl.rows, wl.cols, wl.nvec)
     # the dominant kernel: the step itself when it is one launch, else its GEMV launch
     rk_bytes, rk_ms = (nbytes["step"], ms_step) if launches == 1 else (nbytes["gemv"], ms_gemv)
     achieved = rk_bytes / (rk_ms * 1e-3) / 1e9
@@ -927,7 +931,8 @@ def main():
         "config": {"workload": "%s GEMV W %dx%d, batch %d, cold weights (%d rotating copies)"
                                % (FORMAT_NAMES[wl.wtype], wl.rows, wl.cols, wl.nvec, copies),
                    "name": wl.name, "rows": wl.rows, "cols": wl.cols, "nvec": wl.nvec,
-                   "weight_bytes": wbytes, "plan": plan},
+                   "weight_bytes": wbytes, "route": route,
+                   "plan": plan if route == "vector" else None},
         "us_per_step": round(ms_step * 1e3, 3),
         "us_per_gemv": round(ms_gemv * 1e3, 3),
         "us_per_quantize_act": round(ms_quant * 1e3, 3),
@@ -941,7 +946,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic,
-                     "kernel": roofline_kernel(wl.wtype, plan, wl.nvec, launches),
+                     "kernel": roofline_kernel(wl.wtype, plan, wl.nvec, launches, route),
                      "algorithmic_bytes_per_launch": rk_bytes, "us_per_launch": round(rk_ms * 1e3, 3)},
         "step_launches": launches,
         "us_per_step_distribution": step_dist,

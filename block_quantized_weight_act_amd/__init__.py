@@ -26,7 +26,7 @@ __all__ = [
     "qgemv_multi", "qgemv_multi_fused", "qgemv_multi_geometry", "QGEMV_Q4_0", "QGEMV_Q8_0",
     "Graph", "qgemv_graph_begin", "qgemv_graph_end", "qgemv_graph_launch", "qgemv_graph_nodes",
     "qgemv_graph_destroy", "qgemv_i8mc_workspace_bytes", "qgemv_batch_i8mc",
-    "qgemv_debug_partials_i8mc", "qgemv_fused_i8mc",
+    "qgemv_debug_partials_i8mc", "qgemv_fused_i8mc", "qgemv_route", "ROUTES",
 ]
 
 QGEMV_Q4K = 1
@@ -107,6 +107,7 @@ def _load():
         "qgemv_graph_nodes": (ctypes.c_int, [vp, ctypes.POINTER(i64), ctypes.POINTER(i64)]),
         "qgemv_graph_destroy": (ctypes.c_int, [vp]),
         "qgemv_i8mc_workspace_bytes": (sz, [i64, i64, i32]),
+        "qgemv_route": (ctypes.c_int, [ctypes.c_int, i64, i64, i32]),
         "qgemv_batch_i8mc": (ctypes.c_int, [vp, vp, vp, vp, i64, i64, i32, vp, sz, vp]),
         "qgemv_debug_partials_i8mc": (ctypes.c_int, [vp, vp, vp, vp, vp, i64, i64, i32, vp]),
         "qgemv_fused_i8mc": (ctypes.c_int, [vp, vp, vp, vp, vp, i64, i64, i32, vp, sz, vp]),
@@ -292,6 +293,19 @@ def qgemv_debug_partials(wtype, w, xq, xd, P, S, rows: int, cols: int, nvec: int
         _wtype(wtype), _ptr(w, name="w"), _ptr(xq, torch.int8, "xq"),
         _ptr(xd, torch.float32, "xd"), _ptr(P, torch.int32, "P"), _ptr(S, torch.int32, "S"),
         rows, cols, nvec, wsp, wsb, _stream(stream, P)))
+
+
+ROUTES = {1: "vector", 2: "i8mc", 3: "mc", 4: "grouped"}
+
+
+def qgemv_route(wtype, rows: int, cols: int, nvec: int = 1) -> str:
+    """Which kernels qgemv_batch runs for this shape: "vector", "i8mc" (integer matrix cores),
+    "mc" (matrix cores, 9+ Q4_K vectors) or "grouped" (vector kernels on groups of 8)."""
+    lib = _load()
+    r = int(lib.qgemv_route(_wtype(wtype), rows, cols, nvec))
+    if r not in ROUTES:
+        raise QgemvError("qgemv_route", 1, lib)
+    return ROUTES[r]
 
 
 def qgemv_i8mc_workspace_bytes(rows: int, cols: int, nvec: int) -> int:

@@ -824,6 +824,14 @@ int qgemv_multi_fused(const qgemv_matrix *mats, int32_t nmats, const float *x, i
     return launch_multi(a, s, nvec, stream);
 }
 
+int qgemv_route(int wtype, int64_t rows, int64_t cols, int32_t nvec) {
+    if (mc_shape_ok(wtype, rows, cols, nvec)) return QGEMV_ROUTE_MC;
+    if (grouped_shape_ok(wtype, rows, cols, nvec)) return QGEMV_ROUTE_GROUPED;
+    if (i8_auto(wtype, rows, cols, nvec)) return QGEMV_ROUTE_I8MC;
+    if (shape_ok_t(wtype, rows, cols, nvec)) return QGEMV_ROUTE_VECTOR;
+    return 0;
+}
+
 size_t qgemv_i8mc_workspace_bytes(int64_t rows, int64_t cols, int32_t nvec) {
     if (!i8_ok(rows, cols, nvec)) return 0;
     return i8_ws_bytes(make_i8_plan(rows, cols), rows, nvec);

@@ -194,6 +194,18 @@ int qgemv_batch(int wtype, const void *w, const int8_t *xq, const float *xd, flo
                 int64_t rows, int64_t cols, int32_t nvec, void *workspace,
                 size_t workspace_bytes, hipStream_t stream);
 
+/* Which kernels qgemv_batch (and qgemv_fused, qgemv_debug_partials) run for a
+ * shape: the vector kernels, the integer matrix cores (qgemv_batch_i8mc), the
+ * float matrix cores for 9..QGEMV_MAX_BATCH Q4_K vectors, or the vector kernels
+ * on groups of 8 vectors; 0 for an invalid type or shape. Host only. */
+enum qgemv_route_kind {
+    QGEMV_ROUTE_VECTOR = 1,
+    QGEMV_ROUTE_I8MC = 2,
+    QGEMV_ROUTE_MC = 3,
+    QGEMV_ROUTE_GROUPED = 4
+};
+int qgemv_route(int wtype, int64_t rows, int64_t cols, int32_t nvec);
+
 /*
  * Q4_K with 1 <= nvec <= 8 on the integer matrix cores (v_mfma_i32_16x16x64_i8),
  * for any shape; qgemv_batch, qgemv_fused and qgemv_debug_partials take this path

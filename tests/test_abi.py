@@ -109,6 +109,18 @@ def test_i8mc_workspace_and_routing():
                                          1024, 4, None) == EINVAL
 
 
+def test_routes():
+    assert qg.qgemv_route("q4k", 262144, 1536, 1) == "vector"
+    assert qg.qgemv_route("q4k", 16384, 2048, 8) == "i8mc"
+    assert qg.qgemv_route("q4k", 16384, 2048, 4) == "vector"
+    assert qg.qgemv_route("q4k", 262144, 1536, 3) == "i8mc"
+    assert qg.qgemv_route("q6k", 262144, 1536, 8) == "vector"
+    assert qg.qgemv_route("q4k", 16384, 2048, 64) == "mc"
+    assert qg.qgemv_route("q40", 16384, 2048, 64) == "grouped"
+    assert qg._load().qgemv_route(1, 8, 500, 1) == 0
+    assert qg._load().qgemv_route(1, 8, 512, 300) == 0
+
+
 def test_split_plan_without_workspace_is_rejected():
     lib = qg._load()
     plan = qg.Plan(16, 1, 4, 4, 0)
