@@ -676,8 +676,9 @@ def cpu_baseline_decode_layer(products, seconds: float) -> dict:
 def bench_many(args, wl) -> dict:
     """More than 8 vectors (the matrix-core kernel). Step = qgemv_quantize_act + qgemv_batch
     (plus the ordered reduce when the super-blocks are split), replayed as one graph over
-    rotating weight copies. Beside it: the product alone, and the same vectors through the
-    8-vector kernel (ceil(nvec / 8) products, each reading all the weights)."""
+    rotating weight copies. Beside it: the product alone, and the same vectors in groups of 8
+    (ceil(nvec / 8) products, each reading all the weights) through the vector kernel and
+    through the integer matrix-core kernel."""
     import torch
 
     import block_quantized_weight_act_amd as qg
@@ -712,15 +713,28 @@ def bench_many(args, wl) -> dict:
         qg.qgemv_quantize_act(x, xq, xd, cols, nvec)
         gemm(i)
 
+    plans = {n: qg.qgemv_plan_for(wl.wtype, rows, cols, n) for n in range(1, 9)}
+    wsb = max(wsb, max(qg.qgemv_plan_workspace_bytes(p, rows, cols, n) for n, p in plans.items()),
+              qg.qgemv_i8mc_workspace_bytes(rows, cols, 8))
+    work = torch.empty(max(wsb, 4), dtype=torch.uint8, device=dev)
+
     def by_eight(i):
+        # the vector kernel (its own plan) on groups of 8 vectors
         for v0 in range(0, nvec, 8):
             n = min(8, nvec - v0)
-            qg.qgemv_batch(wl.wtype, ws_list[i % copies], xq[v0:v0 + n], xd[v0:v0 + n],
-                           y[v0:v0 + n], rows, cols, n, workspace=work)
+            qg.qgemv_batch_plan(wl.wtype, ws_list[i % copies], xq[v0:v0 + n], xd[v0:v0 + n],
+                                y[v0:v0 + n], rows, cols, n, plans[n], workspace=work)
+
+    def by_eight_i8(i):
+        # the integer matrix-core kernel on groups of 8 vectors
+        for v0 in range(0, nvec, 8):
+            n = min(8, nvec - v0)
+            qg.qgemv_batch_i8mc(ws_list[i % copies], xq[v0:v0 + n], xd[v0:v0 + n],
+                                y[v0:v0 + n], rows, cols, n, workspace=work)
 
     n8 = max(4, args.steps // 8)
     graphs = {"step": capture(step, args.steps), "gemm": capture(gemm, args.steps),
-              "by_eight": capture(by_eight, n8)}
+              "by_eight": capture(by_eight, n8), "by_eight_i8": capture(by_eight_i8, n8)}
     sink = torch.zeros(1, dtype=torch.int32, device=dev)
     sink_mark = torch.zeros(16, dtype=torch.uint8, device=dev)
     for _ in range(2):
@@ -733,6 +747,7 @@ def bench_many(args, wl) -> dict:
     ms_gemm = replay_timed(graphs["gemm"], args.steps)
     ms_gemm_events, _ = timed(gemm, args.steps)
     ms_eight = replay_timed(graphs["by_eight"], n8)
+    ms_eight_i8 = replay_timed(graphs["by_eight_i8"], n8)
     dist = spread(step, args.steps)
     step(0)
     torch.cuda.synchronize()
@@ -792,6 +807,9 @@ def bench_many(args, wl) -> dict:
         "eight_vector_kernel": {"us_for_all_vectors": round(ms_eight * 1e3, 3),
                                 "launches": (nvec + 7) // 8,
                                 "speedup_of_matrix_cores": round(ms_eight / ms_gemm, 2)},
+        "eight_vector_integer_matrix_cores": {"us_for_all_vectors": round(ms_eight_i8 * 1e3, 3),
+                                              "launches": (nvec + 7) // 8,
+                                              "speedup_of_matrix_cores": round(ms_eight_i8 / ms_gemm, 2)},
         "roofline": roof,
         "setup_s": round(setup_s, 1),
     }
