@@ -379,8 +379,10 @@ hipError_t launch_gemm_q4k_i8(const GemmArgs &a, int waves, bool debug, hipStrea
         a.nvec > kMaxVec || a.row_tiles < 1 || a.splits < 1)
         return hipErrorInvalidValue;
     // Workgroups of this size resident at once (registers and LDS) times the CUs, looked up
-    // once per form and size; each workgroup then takes an equal share of the row tiles (the
-    // staging is per workgroup). Concurrent first calls store the same values.
+    // once per form and size; each workgroup then takes an equal share of the row tiles, and at
+    // least two (the staging is per workgroup, and a second tile's loads overlap the first
+    // tile's arithmetic: 16384 x 2048 x 8 measured 9.6 us against 10.3 us with one tile per
+    // workgroup). Concurrent first calls store the same values.
     static std::atomic<int> per_cu[3][kI8MaxWaves] = {};
     static std::atomic<int> cus{0};
     if (cus.load(std::memory_order_relaxed) == 0) {
@@ -408,7 +410,7 @@ hipError_t launch_gemm_q4k_i8(const GemmArgs &a, int waves, bool debug, hipStrea
     const int64_t cap = std::max<int64_t>(
         1, int64_t{res.load(std::memory_order_relaxed)} * cus.load(std::memory_order_relaxed) /
                a.splits);
-    const int64_t per_wg = (a.row_tiles + cap - 1) / cap;
+    const int64_t per_wg = std::max<int64_t>(2, (a.row_tiles + cap - 1) / cap);
     const int64_t blocks = (a.row_tiles + per_wg - 1) / per_wg;
     const dim3 grid(static_cast<unsigned>(blocks), static_cast<unsigned>(a.splits));
     const dim3 block(static_cast<unsigned>(threads));
