@@ -29,6 +29,7 @@ from __future__ import annotations
 import argparse
 import dataclasses
 import hashlib
+import re
 import json
 import math
 import os
@@ -72,10 +73,27 @@ def parse():
     return ap.parse_args()
 
 
-def kernel_source_hash() -> str:
+def kernel_sources(unit: str) -> list:
+    """The source files of one kernel translation unit in csrc/: the unit and every file it
+    includes from csrc/ (recursively), sorted."""
+    csrc = os.path.join(ROOT, "block_quantized_weight_act_amd", "csrc")
+    seen, todo = set(), [unit]
+    while todo:
+        name = todo.pop()
+        if name in seen or not os.path.exists(os.path.join(csrc, name)):
+            continue
+        seen.add(name)
+        with open(os.path.join(csrc, name)) as f:
+            todo += re.findall(r'^#include "([^"]+)"', f.read(), flags=re.M)
+    return sorted(seen)
+
+
+def kernel_source_hash(unit: str = "gemv_q4k.hip") -> str:
+    """SHA-256 over the sources the kernel is compiled from (default: the Q4_K GEMV kernels),
+    so counters taken on those kernels stay valid while other files change."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "block_quantized_weight_act_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    for name in kernel_sources(unit):
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()
