@@ -43,6 +43,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 MFMA_F16_PEAK_TFLOPS = 2500.0     # dense fp16 matrix peak of MI355X
+MFMA_I8_PEAK_TOPS = 5000.0        # dense int8 matrix peak of MI355X (POP/s)
 FORMAT_NAMES = {"q4k": "Q4_K", "q6k": "Q6_K", "q40": "Q4_0", "q80": "Q8_0"}
 CALIB_COPY_BYTES = 256 << 20
 COLD_BYTES = 640 * 10**6
@@ -129,7 +130,7 @@ def roofline_kernel(wtype: str, plan: dict, nvec: int, launches: int, route: str
     GEMV kernel of the two-launch route (form 0, codes read from memory); on the integer
     matrix-core route the product kernel of that route."""
     if route == "i8mc":
-        return "gemm_q4k_i8_kernel<%d>" % (2 if launches == 1 else 0)
+        return "gemm_q4k_i8_kernel<%d, %d>" % (2 if launches == 1 else 0, (nvec + 7) // 8)
     tag = {"q4k": "Q4K", "q6k": "Q6K", "q40": "Q40", "q80": "Q80"}[wtype]
     return "gemv_kernel<qgemv::%s, %d, %d, %d, %d>" % (tag, nvec, plan["lanes_per_row"],
                                                        plan["chunks_per_lane"],
@@ -782,20 +783,26 @@ def bench_many(args, wl) -> dict:
     gemm_gbs = gemm_bytes / (ms_gemm * 1e-3) / 1e9
     gemm_tflops = flops / (ms_gemm * 1e-3) / 1e12
     t_hbm = gemm_bytes / (HBM_PEAK_GBS * 1e9)
-    t_mfma = flops / (MFMA_F16_PEAK_TFLOPS * 1e12)
-    nt = min(4, (nvec + 31) // 32)
-    kernel = "gemm_q4k_mfma_kernel<%d, false>" % nt
+    route = qg.qgemv_route(wl.wtype, rows, cols, nvec)
+    if route == "i8mc":
+        # the integer matrix cores (int8 products; 9..16 vectors)
+        kernel = "gemm_q4k_i8_kernel<0, %d>" % ((nvec + 7) // 8)
+        mfma_peak, mfma_unit = MFMA_I8_PEAK_TOPS, "TOP/s"
+    else:
+        kernel = "gemm_q4k_mfma_kernel<%d, false>" % min(4, (nvec + 31) // 32)
+        mfma_peak, mfma_unit = MFMA_F16_PEAK_TFLOPS, "TFLOP/s"
+    t_mfma = flops / (mfma_peak * 1e12)
     if t_hbm >= t_mfma:
         roof = {"bound": "hbm", "achieved": round(gemm_gbs, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(gemm_gbs / HBM_PEAK_GBS, 4)}
     else:
-        roof = {"bound": "mfma", "achieved": round(gemm_tflops, 1), "peak": MFMA_F16_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(gemm_tflops / MFMA_F16_PEAK_TFLOPS, 4)}
+        roof = {"bound": "mfma", "achieved": round(gemm_tflops, 1), "peak": mfma_peak,
+                "unit": mfma_unit, "frac": round(gemm_tflops / mfma_peak, 4)}
     roof.update({"traffic": None, "kernel": kernel, "algorithmic_bytes_per_launch": gemm_bytes,
                  "algorithmic_flops_per_launch": flops,
                  "us_per_launch": round(ms_gemm * 1e3, 3),
                  "hbm_frac": round(gemm_gbs / HBM_PEAK_GBS, 4),
-                 "mfma_frac": round(gemm_tflops / MFMA_F16_PEAK_TFLOPS, 4)})
+                 "mfma_frac": round(gemm_tflops / mfma_peak, 4), "route": route})
     out = {
         "metric": "achieved HBM GB/s and % of roofline, block-quantized GEMV with many activation "
                   "vectors (matrix cores)",
@@ -821,7 +828,8 @@ def bench_many(args, wl) -> dict:
         "us_per_gemm_host_launched": round(ms_gemm_events * 1e3, 3),
         "gemm_gbs": round(gemm_gbs, 1),
         "gemm_tflops": round(gemm_tflops, 2),
-        "roofline_floor_us": {"hbm": round(t_hbm * 1e6, 2), "mfma_f16": round(t_mfma * 1e6, 2)},
+        "roofline_floor_us": {"hbm": round(t_hbm * 1e6, 2),
+                              ("mfma_i8" if route == "i8mc" else "mfma_f16"): round(t_mfma * 1e6, 2)},
         "eight_vector_kernel": {"us_for_all_vectors": round(ms_eight * 1e3, 3),
                                 "launches": (nvec + 7) // 8,
                                 "speedup_of_matrix_cores": round(ms_eight / ms_gemm, 2)},

@@ -386,9 +386,11 @@ int run_mc(const void *w, const int8_t *xq, const float *xd, float *y, int32_t *
 // Several matrices with one activation (plain: act.xq / act.xd; fused: act.x and optionally
 // act.xq_out / act.xd_out): every check, then the launch description in a and s.
 // Q4_K with up to kMaxVec vectors on the integer matrix cores (gemm_i8.hip). The kernel takes
-// any 1..kMaxVec vectors (qgemv_batch_i8mc); qgemv_batch routes to it where it was measured
+// any 1..kI8MaxVec vectors (qgemv_batch_i8mc); qgemv_batch routes to it where it was measured
 // faster than the vector kernel: from 3 vectors on tensors of 128 MiB down to 8 vectors on
-// 16 MiB (i8_min_bytes). With few vectors the vector kernel's dot products hide under the
+// 16 MiB (i8_min_bytes), and always for 9..16 vectors (faster than the float matrix-core
+// kernel on every shape measured: 262144 x 1536 x 16 in 64 against 76 us, 16384 x 2048 x 16
+// in 11 against 17 us). With few vectors the vector kernel's dot products hide under the
 // weight stream; on small tensors the time is the latency of a few loads per wave, where the
 // vector kernel (no activation staging) is ahead. A split holds at most
 // kI8MaxWaves * kI8SbPerWave super-blocks (the activation a workgroup stages in LDS); wider
@@ -402,12 +404,13 @@ int64_t i8_min_bytes(int32_t nvec) {
         case 6: return 32 * MiB;
         case 7: return 24 * MiB;
         case 8: return 16 * MiB;
-        default: return INT64_MAX;
+        default: return nvec > kMaxVec && nvec <= kI8MaxVec ? 0 : INT64_MAX;
     }
 }
 
 bool i8_ok(int64_t rows, int64_t cols, int32_t nvec) {
-    return shape_ok_t(QGEMV_Q4K, rows, cols, nvec);
+    return nvec >= 1 && nvec <= kI8MaxVec && shape_ok_t(QGEMV_Q4K, rows, cols, 1) &&
+           static_cast<int64_t>(nvec) * cols < (int64_t{1} << 34);
 }
 
 bool i8_auto(int wtype, int64_t rows, int64_t cols, int32_t nvec) {
@@ -447,13 +450,15 @@ int run_i8(const void *w, const Activation &act, float *y, int32_t *P, int32_t *
     const size_t wb = weight_bytes(QGEMV_Q4K, rows, cols);
     int st;
     if (act.x) {
-        if (debug || !w || !y || !i8_ok(rows, cols, nvec)) return QGEMV_EINVAL;
+        if (debug || !w || !y || !i8_ok(rows, cols, nvec) || nvec > kMaxVec) return QGEMV_EINVAL;
         if (!aligned(w, 16) || !aligned(y, 4)) return QGEMV_EALIGN;
         if (overlaps(y, ybytes, w, wb)) return QGEMV_EINVAL;
         st = check_fused_act(act, w, wb, y, ybytes, cols, nvec);
     } else {
-        st = check_gemv_args(QGEMV_Q4K, w, act.xq, act.xd, debug ? static_cast<const void *>(P) : y,
-                             debug ? pbytes : ybytes, rows, cols, nvec);
+        if (!i8_ok(rows, cols, nvec)) return QGEMV_EINVAL;
+        st = check_gemv_args_n(QGEMV_Q4K, w, act.xq, act.xd,
+                               debug ? static_cast<const void *>(P) : y, debug ? pbytes : ybytes,
+                               rows, cols, nvec);
     }
     if (st != QGEMV_OK) return st;
     const int8_t *xq = act.xq;
@@ -635,9 +640,9 @@ int qgemv_quantize_act(const float *x, int8_t *xq, float *xd, int64_t cols, int3
 }
 
 size_t qgemv_workspace_bytes(int wtype, int64_t rows, int64_t cols, int32_t nvec) {
+    if (i8_auto(wtype, rows, cols, nvec)) return i8_ws_bytes(make_i8_plan(rows, cols), rows, nvec);
     if (mc_shape_ok(wtype, rows, cols, nvec))
         return mc_ws_bytes(make_mc_plan(rows, cols, nvec), rows, cols, nvec);
-    if (i8_auto(wtype, rows, cols, nvec)) return i8_ws_bytes(make_i8_plan(rows, cols), rows, nvec);
     if (grouped_shape_ok(wtype, rows, cols, nvec)) {
         // groups of up to kMaxVec vectors, one after another on the stream, share the workspace
         const int32_t g = std::min<int32_t>(nvec, kMaxVec);
@@ -673,6 +678,13 @@ int qgemv_batch_plan(int wtype, const void *w, const int8_t *xq, const float *xd
 int qgemv_batch(int wtype, const void *w, const int8_t *xq, const float *xd, float *y,
                 int64_t rows, int64_t cols, int32_t nvec, void *workspace,
                 size_t workspace_bytes, hipStream_t stream) {
+    if (i8_auto(wtype, rows, cols, nvec)) {
+        Activation act;
+        act.xq = xq;
+        act.xd = xd;
+        return run_i8(w, act, y, nullptr, nullptr, rows, cols, nvec, workspace, workspace_bytes,
+                      stream);
+    }
     if (mc_shape_ok(wtype, rows, cols, nvec))
         return run_mc(w, xq, xd, y, nullptr, nullptr, rows, cols, nvec, workspace,
                       workspace_bytes, stream);
@@ -703,13 +715,6 @@ int qgemv_batch(int wtype, const void *w, const int8_t *xq, const float *xd, flo
             if (st != QGEMV_OK) return st;
         }
         return QGEMV_OK;
-    }
-    if (i8_auto(wtype, rows, cols, nvec)) {
-        Activation act;
-        act.xq = xq;
-        act.xd = xd;
-        return run_i8(w, act, y, nullptr, nullptr, rows, cols, nvec, workspace, workspace_bytes,
-                      stream);
     }
     if (!shape_ok_t(wtype, rows, cols, nvec))
         return QGEMV_EINVAL;
@@ -825,9 +830,9 @@ int qgemv_multi_fused(const qgemv_matrix *mats, int32_t nmats, const float *x, i
 }
 
 int qgemv_route(int wtype, int64_t rows, int64_t cols, int32_t nvec) {
+    if (i8_auto(wtype, rows, cols, nvec)) return QGEMV_ROUTE_I8MC;
     if (mc_shape_ok(wtype, rows, cols, nvec)) return QGEMV_ROUTE_MC;
     if (grouped_shape_ok(wtype, rows, cols, nvec)) return QGEMV_ROUTE_GROUPED;
-    if (i8_auto(wtype, rows, cols, nvec)) return QGEMV_ROUTE_I8MC;
     if (shape_ok_t(wtype, rows, cols, nvec)) return QGEMV_ROUTE_VECTOR;
     return 0;
 }
@@ -882,6 +887,12 @@ int qgemv_debug_partials(int wtype, const void *w, const int8_t *xq, const float
                          int32_t *P, int32_t *S, int64_t rows, int64_t cols, int32_t nvec,
                          void *workspace, size_t workspace_bytes, hipStream_t stream) {
     if (!P || !S) return QGEMV_EINVAL;
+    if (i8_auto(wtype, rows, cols, nvec)) {
+        Activation act;
+        act.xq = xq;
+        act.xd = xd;
+        return run_i8(w, act, nullptr, P, S, rows, cols, nvec, nullptr, 0, stream);
+    }
     if (mc_shape_ok(wtype, rows, cols, nvec)) {
         const size_t pbytes = static_cast<size_t>(nvec) * rows * (cols / 32) * sizeof(int32_t);
         const size_t sbytes = static_cast<size_t>(nvec) * (cols / 32) * sizeof(int32_t);
@@ -895,12 +906,6 @@ int qgemv_debug_partials(int wtype, const void *w, const int8_t *xq, const float
             return QGEMV_EINVAL;
         return run_mc(w, xq, xd, nullptr, P, S, rows, cols, nvec, workspace, workspace_bytes,
                       stream);
-    }
-    if (i8_auto(wtype, rows, cols, nvec)) {
-        Activation act;
-        act.xq = xq;
-        act.xd = xd;
-        return run_i8(w, act, nullptr, P, S, rows, cols, nvec, nullptr, 0, stream);
     }
     const int64_t nsub = wtype == QGEMV_Q6K ? cols / 16 : cols / 32;
     const size_t pbytes = static_cast<size_t>(nvec) * rows * nsub * sizeof(int32_t);

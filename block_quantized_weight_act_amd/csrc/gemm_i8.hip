@@ -47,13 +47,14 @@ typedef float v4f_t __attribute__((ext_vector_type(4)));
 
 constexpr int kSbw = kI8SbPerWave;                  // super-blocks per wave
 
-// LDS of a workgroup of `waves` waves (split of kSbw * waves super-blocks): 9 rows of codes
-// (8 vectors, then zeros) of pitch columns + 16 bytes (the 16 spread the rows over the banks),
-// the scales and -xd * S of the split's blocks (8 vectors each), and two slots of the waves'
-// sums of a row tile (16 rows x 8 vectors per wave).
+// LDS of a workgroup of `waves` waves (split of kSbw * waves super-blocks) for vg groups of 8
+// vectors: 8 vg + 1 rows of codes (the vectors, then zeros) of pitch columns + 16 bytes (the 16
+// spread the rows over the banks), the scales and -xd * S of the split's blocks (8 vg vectors
+// each), and two slots of the waves' sums of a row tile (16 rows x 8 vg vectors per wave).
 __host__ __device__ constexpr int code_pitch(int waves) { return waves * kSbw * 256 + 16; }
-__host__ __device__ constexpr int lds_bytes(int waves) {
-    return 9 * code_pitch(waves) + 2 * (waves * kSbw * 8) * 8 * 4 + 2 * waves * 16 * 8 * 4;
+__host__ __device__ constexpr int lds_bytes(int waves, int vg) {
+    return (8 * vg + 1) * code_pitch(waves) + 2 * (waves * kSbw * 8) * (8 * vg) * 4 +
+           2 * waves * 16 * (8 * vg) * 4;
 }
 
 // s_waitcnt immediate: no vector-memory load outstanding, the other counters not waited for
@@ -62,13 +63,17 @@ constexpr int kWaitVm0 = (7 << 4) | (15 << 8);
 
 // Staging passes of the fused form at most: each group of 8 lanes quantizes one 32-column block
 // per pass; 8 vectors x 8 nsb blocks over 8 waves groups, with nsb <= kSbw waves. The form from
-// codes takes a block per 2 lanes, a quarter of the passes.
+// codes takes a block per 2 lanes, a quarter of the passes per group of 8 vectors.
 constexpr int kStagePasses = 8 * kSbw;
 
-template <int MODE>
+// VG groups of 8 vectors per launch (nvec <= 8 VG): every group multiplies the same loaded
+// weights (one product per group and pair of blocks).
+template <int MODE, int VG>
 __global__ void __launch_bounds__(256) gemm_q4k_i8_kernel(GemmArgs a) {
     constexpr bool DBG = MODE == kModeDebug;
     constexpr bool FUSED = MODE == kModeFused;
+    constexpr int NV = 8 * VG;      // vector slots
+    static_assert(!FUSED || VG == 1, "the fused form takes up to 8 vectors");
     extern __shared__ __attribute__((aligned(16))) uint8_t lds_i8[];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -76,10 +81,10 @@ __global__ void __launch_bounds__(256) gemm_q4k_i8_kernel(GemmArgs a) {
     const int waves = blockDim.x >> 6;
     const int pitch = code_pitch(waves);
     const int sblk = waves * kSbw * 8;
-    uint8_t *const xq_s = lds_i8;                   // [9][pitch]: vectors' codes (block-permuted), zeros
-    float *const xd_s = reinterpret_cast<float *>(lds_i8 + 9 * pitch);   // [sblk][8]
-    float *const xs_s = xd_s + sblk * 8;            // [sblk][8]: -xd * S
-    float *const red_s = xs_s + sblk * 8;           // [2][waves][16][8]
+    uint8_t *const xq_s = lds_i8;                   // [NV + 1][pitch]: codes (block-permuted), zeros
+    float *const xd_s = reinterpret_cast<float *>(lds_i8 + (NV + 1) * pitch);   // [sblk][NV]
+    float *const xs_s = xd_s + sblk * NV;           // [sblk][NV]: -xd * S
+    float *const red_s = xs_s + sblk * NV;          // [2][waves][16][NV]
     const int r = lane & 15;        // tile row of this lane's weights and outputs
     const int g = lane >> 4;        // lane group
     const int q = g >> 1;           // block of the pair this lane's weights and outputs are in
@@ -125,14 +130,14 @@ __global__ void __launch_bounds__(256) gemm_q4k_i8_kernel(GemmArgs a) {
     //      the float32 block itself, 8 lanes per block (4 columns each), and the first
     //      workgroup of the split also stores the codes and scales ----
     for (int i = tid; i < pitch / 16; i += blockDim.x)
-        *reinterpret_cast<uint4 *>(xq_s + 8 * pitch + 16 * i) = make_uint4(0u, 0u, 0u, 0u);
+        *reinterpret_cast<uint4 *>(xq_s + NV * pitch + 16 * i) = make_uint4(0u, 0u, 0u, 0u);
     {
         const int nblk = nsb * 8;
-        const int items = 8 * nblk;                     // (vector, block), vector-major
+        const int items = NV * nblk;                    // (vector, block), vector-major
         for (int it = nvec * nblk + tid; it < items; it += blockDim.x) {
             const int v = it / nblk, b = it - v * nblk;
-            xd_s[b * 8 + v] = 0.0f;
-            xs_s[b * 8 + v] = 0.0f;
+            xd_s[b * NV + v] = 0.0f;
+            xs_s[b * NV + v] = 0.0f;
         }
         if constexpr (FUSED) {
             const int per_pass = static_cast<int>(blockDim.x) >> 3;
@@ -166,20 +171,20 @@ __global__ void __launch_bounds__(256) gemm_q4k_i8_kernel(GemmArgs a) {
                         }
                         *reinterpret_cast<uint32_t *>(xq_s + v * pitch + 32 * b + 4 * pd) = aq.codes;
                         if (j8 == 0) {
-                            xd_s[b * 8 + v] = aq.scale;
-                            xs_s[b * 8 + v] = -(aq.scale * s);
+                            xd_s[b * NV + v] = aq.scale;
+                            xs_s[b * NV + v] = -(aq.scale * s);
                         }
                     }
                 }
             }
         } else {
             const int per_pass = static_cast<int>(blockDim.x) >> 1;
-            const int passes = (nvec * nblk + per_pass - 1) / per_pass;   // <= kStagePasses / 4
+            const int passes = (nvec * nblk + per_pass - 1) / per_pass;   // <= VG kStagePasses / 4
             const int h = tid & 1;
-            uint4 cv[kStagePasses / 4];
-            float sv[kStagePasses / 4];
+            uint4 cv[VG * kStagePasses / 4];
+            float sv[VG * kStagePasses / 4];
 #pragma unroll
-            for (int ps = 0; ps < kStagePasses / 4; ps++) {
+            for (int ps = 0; ps < VG * kStagePasses / 4; ps++) {
                 const int item = ps * per_pass + (tid >> 1);
                 const int v = item / nblk;
                 const int64_t gb = static_cast<int64_t>(v) * nbk + sb_lo * 8 + (item - v * nblk);
@@ -188,7 +193,7 @@ __global__ void __launch_bounds__(256) gemm_q4k_i8_kernel(GemmArgs a) {
                 sv[ps] = live ? a.xd[gb] : 0.0f;
             }
 #pragma unroll
-            for (int ps = 0; ps < kStagePasses / 4; ps++) {
+            for (int ps = 0; ps < VG * kStagePasses / 4; ps++) {
                 if (ps < passes) {            // the same in every lane of the workgroup
                     const int item = ps * per_pass + (tid >> 1);
                     const int v = item / nblk, b = item - v * nblk;
@@ -202,8 +207,8 @@ __global__ void __launch_bounds__(256) gemm_q4k_i8_kernel(GemmArgs a) {
                         *reinterpret_cast<uint2 *>(dst + 8 * h) = make_uint2(c.x, c.y);
                         *reinterpret_cast<uint2 *>(dst + 16 + 8 * h) = make_uint2(c.z, c.w);
                         if (h == 0) {
-                            xd_s[b * 8 + v] = sv[ps];
-                            xs_s[b * 8 + v] = -(sv[ps] * static_cast<float>(s));
+                            xd_s[b * NV + v] = sv[ps];
+                            xs_s[b * NV + v] = -(sv[ps] * static_cast<float>(s));
                             if (DBG && blockIdx.x == 0)
                                 a.S[static_cast<int64_t>(v) * nbk + sb_lo * 8 + b] = s;
                         }
@@ -219,31 +224,38 @@ __global__ void __launch_bounds__(256) gemm_q4k_i8_kernel(GemmArgs a) {
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
     __syncthreads();
 
-    // ---- where this lane reads its activation operands in LDS (for every row tile): the
-    //      operand row of vector av, block ap of each pair (the zero row where the vector is
-    //      past nvec or the block does not meet this lane group's weights), the scales of the
-    //      output vectors 4 (g % 2) .. + 3, and the min-term operands ----
+    // ---- where this lane reads its activation operands in LDS (for every row tile), per
+    //      group gi of 8 vectors: the operand row of vector 8 gi + av, block ap of each pair
+    //      (the zero row where the vector is past nvec or the block does not meet this lane
+    //      group's weights), the scales of the output vectors 8 gi + 4 (g % 2) .. + 3, and the
+    //      min-term operands ----
     const int av = lane & 7, ap = (lane >> 3) & 1;
-    const uint8_t *arow = xq_s + (((g >> 1) == ap && av < nvec) ? av : 8) * pitch + ap * 32 + 16 * (g & 1);
-    const float *xrow = xd_s + q * 8 + 4 * (g & 1);
-    float mina[kSbw][2];
-    {
+    const uint8_t *arow[VG];
+    const float *xrow[VG];
+    float mina[VG][kSbw][2];
+#pragma unroll
+    for (int gi = 0; gi < VG; gi++) {
+        const int v = 8 * gi + av;
+        arow[gi] = xq_s + (((g >> 1) == ap && v < nvec) ? v : NV) * pitch + ap * 32 + 16 * (g & 1);
+        xrow[gi] = xd_s + q * NV + 8 * gi + 4 * (g & 1);
         const int am = lane & 15;
 #pragma unroll
         for (int k = 0; k < kSbw; k++) {
             const int sbl = min(wsb + k, nsb - 1);
 #pragma unroll
             for (int u = 0; u < 2; u++)
-                mina[k][u] = am < 8 ? xs_s[(sbl * 8 + 4 * u + g) * 8 + am] : 0.0f;
+                mina[gi][k][u] = am < 8 ? xs_s[(sbl * 8 + 4 * u + g) * NV + 8 * gi + am] : 0.0f;
         }
     }
 
     float *out = DBG ? nullptr : a.out + static_cast<int64_t>(blockIdx.y) * nvec * rows;
     int slot = 0;
     // Row tile `rt` from the loaded registers (cw, hd): its products, folded to this lane's two
-    // outputs (vectors vv and vv + 2 of row r, vv = 4 (g % 2) + l / 32).
-    auto products = [&](int rt, float (&fold)[2]) {
-        v4f_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    // outputs per group gi (vectors 8 gi + vv and 8 gi + vv + 2 of row r, vv = 4 (g % 2) + l / 32).
+    auto products = [&](int rt, float (&fold)[VG][2]) {
+        v4f_t acc[VG];
+#pragma unroll
+        for (int gi = 0; gi < VG; gi++) acc[gi] = v4f_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int k = 0; k < kSbw; k++) {
             if (wsb + k < nsb) {            // the same in every lane of the wave
@@ -268,7 +280,7 @@ __global__ void __launch_bounds__(256) gemm_q4k_i8_kernel(GemmArgs a) {
                     pw[2 * i + 1][0] = z;
                     pw[2 * i + 1][1] = w;
                 }
-                v4f_t tt;
+                v4f_t tt[VG];
 #pragma unroll
                 for (int t = 0; t < 4; t++) {
                     const uint2 c = make_uint2(pw[t][0], pw[t][1]);
@@ -278,36 +290,43 @@ __global__ void __launch_bounds__(256) gemm_q4k_i8_kernel(GemmArgs a) {
                                      static_cast<int>((c.y >> 4) & 0x0F0F0F0Fu)};
                     const v4i_t zero = {0, 0, 0, 0};
                     const int blk = (wsb + k) * 8 + 2 * t;      // first block of the pair, in the split
-                    const v4i_t A = *reinterpret_cast<const v4i_t *>(arow + blk * 32);
-                    const v4f_t xdv = *reinterpret_cast<const v4f_t *>(xrow + blk * 8);
-                    const v4i_t P = __builtin_amdgcn_mfma_i32_16x16x64_i8(A, B, zero, 0, 0, 0);
                     const int sc = static_cast<int>(((ysh >> (8 * t)) & 15u) | (((wsh >> (4 * t)) & 3u) << 4));
 #pragma unroll
-                    for (int i = 0; i < 4; i++) {
-                        const float ps = static_cast<float>(__mul24(sc, P[i]));   // exact: < 2^22
-                        tt[i] = t == 0 ? xdv[i] * ps : fmaf(xdv[i], ps, tt[i]);
-                    }
-                    if (DBG) {
-                        const int row = rt * 16 + r;
-                        const int gblk = sb_lo * 8 + blk + q;
+                    for (int gi = 0; gi < VG; gi++) {
+                        const v4i_t A = *reinterpret_cast<const v4i_t *>(arow[gi] + blk * 32);
+                        const v4f_t xdv = *reinterpret_cast<const v4f_t *>(xrow[gi] + blk * NV);
+                        const v4i_t P = __builtin_amdgcn_mfma_i32_16x16x64_i8(A, B, zero, 0, 0, 0);
 #pragma unroll
                         for (int i = 0; i < 4; i++) {
-                            const int v = 4 * (g & 1) + i;
-                            if (v < nvec && row < rows)
-                                a.P[(static_cast<int64_t>(v) * rows + row) * nbk + gblk] = P[i];
+                            const float ps = static_cast<float>(__mul24(sc, P[i]));   // exact: < 2^22
+                            tt[gi][i] = t == 0 ? xdv[i] * ps : fmaf(xdv[i], ps, tt[gi][i]);
+                        }
+                        if (DBG) {
+                            const int row = rt * 16 + r;
+                            const int gblk = sb_lo * 8 + blk + q;
+#pragma unroll
+                            for (int i = 0; i < 4; i++) {
+                                const int v = 8 * gi + 4 * (g & 1) + i;
+                                if (v < nvec && row < rows)
+                                    a.P[(static_cast<int64_t>(v) * rows + row) * nbk + gblk] = P[i];
+                            }
                         }
                     }
                 }
 #pragma unroll
-                for (int i = 0; i < 4; i++) acc[i] = fmaf(d, tt[i], acc[i]);
+                for (int gi = 0; gi < VG; gi++)
+#pragma unroll
+                    for (int i = 0; i < 4; i++) acc[gi][i] = fmaf(d, tt[gi][i], acc[gi][i]);
                 // min terms of blocks 4 u + g: m low 4 bits at z bit 4 (4 u + g), high 2 bits at w
                 // bit 16 + 2 (4 u + g)
                 const uint32_t zsh = h.z >> (4 * g), wsh2 = h.w >> (16 + 2 * g);
 #pragma unroll
                 for (int u = 0; u < 2; u++) {
                     const uint32_t m = ((zsh >> (16 * u)) & 15u) | (((wsh2 >> (8 * u)) & 3u) << 4);
-                    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(mina[k][u], dmin * static_cast<float>(m),
-                                                              acc, 0, 0, 0);
+                    const float dm = dmin * static_cast<float>(m);
+#pragma unroll
+                    for (int gi = 0; gi < VG; gi++)
+                        acc[gi] = __builtin_amdgcn_mfma_f32_16x16x4f32(mina[gi][k][u], dm, acc[gi], 0, 0, 0);
                 }
             }
         }
@@ -320,35 +339,40 @@ __global__ void __launch_bounds__(256) gemm_q4k_i8_kernel(GemmArgs a) {
         // (The elements are copied to scalars first: __builtin_bit_cast of a vector element
         // read the vector's first element with this compiler.)
 #pragma unroll
-        for (int e = 0; e < 2; e++) {
-            const float lo = acc[2 * e], hi = acc[2 * e + 1];
-            const auto sw = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, lo),
-                                                             __builtin_bit_cast(uint32_t, hi),
-                                                             false, false);
-            const uint32_t s0 = sw[0], s1 = sw[1];
-            fold[e] = __builtin_bit_cast(float, s0) + __builtin_bit_cast(float, s1);
-        }
+        for (int gi = 0; gi < VG; gi++)
+#pragma unroll
+            for (int e = 0; e < 2; e++) {
+                const float lo = acc[gi][2 * e], hi = acc[gi][2 * e + 1];
+                const auto sw = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, lo),
+                                                                 __builtin_bit_cast(uint32_t, hi),
+                                                                 false, false);
+                const uint32_t s0 = sw[0], s1 = sw[1];
+                fold[gi][e] = __builtin_bit_cast(float, s0) + __builtin_bit_cast(float, s1);
+            }
     };
     // The sums over the workgroup's waves (in wave order) and the stores of row tile rt.
-    auto finish = [&](int rt, const float (&fold)[2]) {
+    auto finish = [&](int rt, const float (&fold)[VG][2]) {
         if (!DBG) {
             const int vv = 4 * (g & 1) + (lane >> 5);
-            red_s[((slot * waves + wave) * 16 + r) * 8 + vv] = fold[0];
-            red_s[((slot * waves + wave) * 16 + r) * 8 + vv + 2] = fold[1];
-            __syncthreads();
-            // 128 outputs: one per lane of the first two waves, or two per lane of a lone wave
-            // (a fixed number of stores per lane, so the compiler can count the loads still
-            // in flight past them instead of waiting for all of them)
 #pragma unroll
-            for (int i = 0; i < 2; i++) {
-                const int e = tid + 64 * i;
+            for (int gi = 0; gi < VG; gi++) {
+                red_s[((slot * waves + wave) * 16 + r) * NV + 8 * gi + vv] = fold[gi][0];
+                red_s[((slot * waves + wave) * 16 + r) * NV + 8 * gi + vv + 2] = fold[gi][1];
+            }
+            __syncthreads();
+            // 16 NV outputs, output e by thread e % blockDim (a fixed number of stores per
+            // lane, so the compiler can count the loads still in flight past them instead of
+            // waiting for all of them)
+#pragma unroll
+            for (int i = 0; i < 2 * VG; i++) {
+                const int e = tid + static_cast<int>(blockDim.x) * i;
                 const int v = e >> 4, rr = e & 15;
                 const int row = rt * 16 + rr;
-                if ((i == 0 || waves == 1) && e < 128 && v < nvec && row < rows) {
-                    float y = red_s[((slot * waves) * 16 + rr) * 8 + v];
+                if (e < 16 * NV && v < nvec && row < rows) {
+                    float y = red_s[((slot * waves) * 16 + rr) * NV + v];
 #pragma unroll
                     for (int w = 1; w < kI8MaxWaves; w++)
-                        if (w < waves) y += red_s[((slot * waves + w) * 16 + rr) * 8 + v];
+                        if (w < waves) y += red_s[((slot * waves + w) * 16 + rr) * NV + v];
                     out[static_cast<int64_t>(v) * rows + row] = y;
                 }
             }
@@ -360,7 +384,7 @@ __global__ void __launch_bounds__(256) gemm_q4k_i8_kernel(GemmArgs a) {
     // last tile they reload it, unused).
     const int stride = static_cast<int>(gridDim.x);
     while (true) {
-        float fold[2];
+        float fold[VG][2];
         __builtin_amdgcn_sched_barrier(0);
         products(rt, fold);
         __builtin_amdgcn_sched_barrier(0);
@@ -374,10 +398,10 @@ __global__ void __launch_bounds__(256) gemm_q4k_i8_kernel(GemmArgs a) {
 
 }  // namespace
 
-hipError_t launch_gemm_q4k_i8(const GemmArgs &a, int waves, bool debug, hipStream_t stream) {
-    if (waves < 1 || waves > kI8MaxWaves || a.sb_per_split != kSbw * waves || a.nvec < 1 ||
-        a.nvec > kMaxVec || a.row_tiles < 1 || a.splits < 1)
-        return hipErrorInvalidValue;
+namespace {
+
+template <int VG>
+hipError_t launch_vg(const GemmArgs &a, int waves, bool debug, hipStream_t stream) {
     // Workgroups of this size resident at once (registers and LDS) times the CUs, looked up
     // once per form and size; each workgroup then takes an equal share of the row tiles, and at
     // least two (the staging is per workgroup, and a second tile's loads overlap the first
@@ -394,17 +418,19 @@ hipError_t launch_gemm_q4k_i8(const GemmArgs &a, int waves, bool debug, hipStrea
         cus.store(ok ? n : 256, std::memory_order_relaxed);
     }
     const int mode = debug ? kModeDebug : (a.x != nullptr ? kModeFused : kModePlain);
+    if (mode == kModeFused && VG != 1) return hipErrorInvalidValue;
     const int threads = 64 * waves;
-    const size_t lds = static_cast<size_t>(lds_bytes(waves));
+    const size_t lds = static_cast<size_t>(lds_bytes(waves, VG));
     std::atomic<int> &res = per_cu[mode][waves - 1];
     if (res.load(std::memory_order_relaxed) == 0) {
         int n = 0;
-        const hipError_t e =
-            mode == kModeDebug
-                ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gemm_q4k_i8_kernel<kModeDebug>, threads, lds)
-                : mode == kModeFused
-                      ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gemm_q4k_i8_kernel<kModeFused>, threads, lds)
-                      : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gemm_q4k_i8_kernel<kModePlain>, threads, lds);
+        hipError_t e;
+        if (mode == kModeDebug)
+            e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gemm_q4k_i8_kernel<kModeDebug, VG>, threads, lds);
+        else if (mode == kModeFused)
+            e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gemm_q4k_i8_kernel<kModeFused, 1>, threads, lds);
+        else
+            e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gemm_q4k_i8_kernel<kModePlain, VG>, threads, lds);
         res.store((e == hipSuccess && n > 0) ? n : 1, std::memory_order_relaxed);
     }
     const int64_t cap = std::max<int64_t>(
@@ -415,12 +441,22 @@ hipError_t launch_gemm_q4k_i8(const GemmArgs &a, int waves, bool debug, hipStrea
     const dim3 grid(static_cast<unsigned>(blocks), static_cast<unsigned>(a.splits));
     const dim3 block(static_cast<unsigned>(threads));
     if (mode == kModeDebug)
-        hipLaunchKernelGGL(gemm_q4k_i8_kernel<kModeDebug>, grid, block, lds, stream, a);
+        hipLaunchKernelGGL((gemm_q4k_i8_kernel<kModeDebug, VG>), grid, block, lds, stream, a);
     else if (mode == kModeFused)
-        hipLaunchKernelGGL(gemm_q4k_i8_kernel<kModeFused>, grid, block, lds, stream, a);
+        hipLaunchKernelGGL((gemm_q4k_i8_kernel<kModeFused, 1>), grid, block, lds, stream, a);
     else
-        hipLaunchKernelGGL(gemm_q4k_i8_kernel<kModePlain>, grid, block, lds, stream, a);
+        hipLaunchKernelGGL((gemm_q4k_i8_kernel<kModePlain, VG>), grid, block, lds, stream, a);
     return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gemm_q4k_i8(const GemmArgs &a, int waves, bool debug, hipStream_t stream) {
+    if (waves < 1 || waves > kI8MaxWaves || a.sb_per_split != kSbw * waves || a.nvec < 1 ||
+        a.nvec > kI8MaxVec || a.row_tiles < 1 || a.splits < 1)
+        return hipErrorInvalidValue;
+    if (a.nvec <= 8) return launch_vg<1>(a, waves, debug, stream);
+    return launch_vg<2>(a, waves, debug, stream);
 }
 
 }  // namespace qgemv

@@ -135,13 +135,14 @@ constexpr int64_t mc_tile_bytes(int nt) { return int64_t{nt} * (32 * 512 + 8 * 3
 hipError_t launch_gemm_q4k_mfma(const GemmArgs &a, int nt, int row_tiles, int groups, int splits,
                                 bool debug, hipStream_t stream);
 
-// 2..8 vectors on the integer matrix cores (gemm_i8.hip): a workgroup of up to kI8MaxWaves
+// 1..16 vectors on the integer matrix cores (gemm_i8.hip): a workgroup of up to kI8MaxWaves
 // waves takes 16 rows at a time over a column split of kI8SbPerWave super-blocks per wave
 // (GemmArgs::sb_per_split == kI8SbPerWave * waves; row_tiles = ceil(rows / 16); splits
 // column splits writing out [splits][nvec][rows]; tiles unused). One launch; with x set, the
 // kernel quantizes the activation itself (the codes of qgemv_quantize_act, bit for bit).
 constexpr int kI8SbPerWave = 2;
 constexpr int kI8MaxWaves = 4;
+constexpr int kI8MaxVec = 16;      // vectors per launch (two groups of 8)
 hipError_t launch_gemm_q4k_i8(const GemmArgs &a, int waves, bool debug, hipStream_t stream);
 
 // Host: record a HIP error (or a message) as this thread's last error text and return the

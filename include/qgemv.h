@@ -81,8 +81,9 @@
  *  - Shapes: cols a positive multiple of 256 (Q4_K, Q6_K) or of 32 (Q4_0,
  *    Q8_0), 1 <= rows <= 2^30, 1 <= nvec <= 8, rows * cols / 32 < 2^31;
  *    qgemv_batch and qgemv_workspace_bytes also take 9 <= nvec <=
- *    QGEMV_MAX_BATCH vectors (Q4_K: the matrix-core path), and so does
- *    qgemv_debug_partials for Q4_K.
+ *    QGEMV_MAX_BATCH vectors (Q4_K: the matrix-core paths), and so does
+ *    qgemv_debug_partials for Q4_K; the qgemv_*_i8mc functions take
+ *    1 <= nvec <= 16.
  *  - Alignment: w and xq 16 bytes, xd and y 4 bytes.
  *  - Outputs must not overlap inputs.
  *  - The functions are safe to call from several host threads.
@@ -181,11 +182,13 @@ int qgemv_q6k(const void *w, const int8_t *xq, const float *xd, float *y, int64_
  *
  * Q4_K with 9 <= nvec <= QGEMV_MAX_BATCH (many tokens verified or prefilled
  * at once; oxinfer README, "Speculative decoding": the many-token int8
- * variants are instruction-bound at Q4) runs on the matrix cores: the same
- * exact integer sub-block products P and sums S, then the same float32
- * scaling, so y lies within the same bound of the exact product; the
- * workspace (qgemv_workspace_bytes) then holds the staged activation and, for
- * matrices with few rows, partial sums. The other types with 9 <= nvec <=
+ * variants are instruction-bound at Q4) runs on the matrix cores: 9..16
+ * vectors on the integer matrix cores (qgemv_batch_i8mc below), 17 and more
+ * on the float matrix cores. Both form the same exact integer sub-block
+ * products P and sums S, then the same float32 scaling, so y lies within the
+ * same bound of the exact product; the float path's workspace
+ * (qgemv_workspace_bytes) holds the staged activation and, for matrices with
+ * few rows, partial sums. The other types with 9 <= nvec <=
  * QGEMV_MAX_BATCH run the vector kernels on groups of up to 8 vectors, one
  * after another on the stream (one pass over the weights per group; the
  * workspace is that of 8 vectors, shared by the groups).
@@ -196,7 +199,7 @@ int qgemv_batch(int wtype, const void *w, const int8_t *xq, const float *xd, flo
 
 /* Which kernels qgemv_batch (and qgemv_fused, qgemv_debug_partials) run for a
  * shape: the vector kernels, the integer matrix cores (qgemv_batch_i8mc), the
- * float matrix cores for 9..QGEMV_MAX_BATCH Q4_K vectors, or the vector kernels
+ * float matrix cores for 17..QGEMV_MAX_BATCH Q4_K vectors, or the vector kernels
  * on groups of 8 vectors; 0 for an invalid type or shape. Host only. */
 enum qgemv_route_kind {
     QGEMV_ROUTE_VECTOR = 1,
@@ -207,13 +210,13 @@ enum qgemv_route_kind {
 int qgemv_route(int wtype, int64_t rows, int64_t cols, int32_t nvec);
 
 /*
- * Q4_K with 1 <= nvec <= 8 on the integer matrix cores (v_mfma_i32_16x16x64_i8),
- * for any shape; qgemv_batch, qgemv_fused and qgemv_debug_partials take this path
- * by themselves where it was measured faster than the vector kernel: tensors of at
+ * Q4_K with 1 <= nvec <= 16 on the integer matrix cores (v_mfma_i32_16x16x64_i8;
+ * two groups of 8 vectors share each loaded weight from 9 vectors on), for any shape; qgemv_batch, qgemv_fused and qgemv_debug_partials take this path
+ * by themselves where it was measured faster than the other kernels: tensors of at
  * least 128, 96, 48, 32, 24 and 16 MiB for 3, 4, 5, 6, 7 and 8 vectors (there the
  * vector kernel's 4-way dot products, one per 4 codes and vector, are the
  * bottleneck; qgemv_fused with code outputs then quantizes once and runs this path
- * from the codes).
+ * from the codes), and every Q4_K product with 9..16 vectors.
  * The same exact integer sub-block products P = sum q * xq (the product's int32
  * results as they are), S = sum xq, then per block the float32 term
  * xd * (sc * P) (sc * P exact) summed over the super-block and scaled by d, and the
@@ -228,9 +231,10 @@ int qgemv_batch_i8mc(const void *w, const int8_t *xq, const float *xd, float *y,
                      int64_t cols, int32_t nvec, void *workspace, size_t workspace_bytes,
                      hipStream_t stream);
 
-/* The same from the float32 activation x (16-byte aligned), quantized inside the
- * launch exactly as qgemv_quantize_act does (bit for bit); xq_out / xd_out (both
- * NULL or both set, 4-byte aligned) optionally receive the codes and scales. */
+/* The same from the float32 activation x (16-byte aligned; 1 <= nvec <= 8),
+ * quantized inside the launch exactly as qgemv_quantize_act does (bit for bit);
+ * xq_out / xd_out (both NULL or both set, 4-byte aligned) optionally receive the
+ * codes and scales. */
 int qgemv_fused_i8mc(const void *w, const float *x, int8_t *xq_out, float *xd_out, float *y,
                      int64_t rows, int64_t cols, int32_t nvec, void *workspace,
                      size_t workspace_bytes, hipStream_t stream);

@@ -73,7 +73,7 @@ def _call_i8mc(w=A, xq=A + (1 << 30), xd=A + (2 << 30), y=A + (3 << 30), rows=64
 @pytest.mark.parametrize("kw,status", [
     (dict(w=None), EINVAL), (dict(y=None), EINVAL), (dict(cols=1000), EINVAL),
     (dict(cols=0), EINVAL), (dict(rows=0), EINVAL), (dict(nvec=0), EINVAL),
-    (dict(nvec=9), EINVAL), (dict(w=A + 8), EALIGN), (dict(xq=A + (1 << 30) + 4), EALIGN),
+    (dict(nvec=17), EINVAL), (dict(w=A + 8), EALIGN), (dict(xq=A + (1 << 30) + 4), EALIGN),
     (dict(y=A + 64), EINVAL), (dict(rows=1 << 31), EINVAL),
     (dict(cols=4096), EWORKSPACE),                       # two column splits need partial sums
     (dict(cols=4096, ws=A + (4 << 30), wsb=2 * 4 * 64 * 4 - 4), EWORKSPACE),
@@ -91,7 +91,8 @@ def test_i8mc_workspace_and_routing():
     assert qg.qgemv_i8mc_workspace_bytes(64, 4096, 3) == 2 * 3 * 64 * 4
     assert qg.qgemv_i8mc_workspace_bytes(10, 6144, 8) == 3 * 8 * 10 * 4
     assert qg.qgemv_i8mc_workspace_bytes(64, 2304, 2) == 2 * 2 * 64 * 4   # 9 super-blocks: 6 + 3
-    assert qg.qgemv_i8mc_workspace_bytes(64, 4096, 9) == 0                 # invalid
+    assert qg.qgemv_i8mc_workspace_bytes(64, 4096, 17) == 0                # invalid
+    assert qg.qgemv_i8mc_workspace_bytes(64, 4096, 16) == 2 * 16 * 64 * 4
     big = (65536, 4096)                                                    # 144 MiB of Q4_K
     assert qg.qgemv_workspace_bytes("q4k", *big, 4) == qg.qgemv_i8mc_workspace_bytes(*big, 4)
     # the routing thresholds: 16 MiB at 8 vectors (16384 x 2048: 18 MiB), 128 MiB at 3
@@ -116,6 +117,9 @@ def test_routes():
     assert qg.qgemv_route("q4k", 262144, 1536, 3) == "i8mc"
     assert qg.qgemv_route("q6k", 262144, 1536, 8) == "vector"
     assert qg.qgemv_route("q4k", 16384, 2048, 64) == "mc"
+    assert qg.qgemv_route("q4k", 16384, 2048, 12) == "i8mc"         # 9..16 vectors: always
+    assert qg.qgemv_route("q4k", 512, 512, 16) == "i8mc"
+    assert qg.qgemv_route("q4k", 512, 512, 17) == "mc"
     assert qg.qgemv_route("q40", 16384, 2048, 64) == "grouped"
     assert qg._load().qgemv_route(1, 8, 500, 1) == 0
     assert qg._load().qgemv_route(1, 8, 512, 300) == 0
@@ -150,9 +154,9 @@ def test_other_entry_points_reject_bad_arguments():
                          None) == EALIGN
     assert lib.qgemv_debug_partials(1, A, A + (1 << 30), A + (2 << 30), None, A, 8, 256, 1,
                                     None, 0, None) == EINVAL
-    # the matrix-core debug form needs the workspace
+    # the float matrix-core debug form (17+ vectors) needs the workspace
     assert lib.qgemv_debug_partials(1, A, A + (1 << 30), A + (2 << 30), A + (3 << 30),
-                                    A + (4 << 30), 8, 256, 9, None, 0, None) == EWORKSPACE
+                                    A + (4 << 30), 8, 256, 17, None, 0, None) == EWORKSPACE
     assert lib.qgemv_quantize_weights(2, A, A + 64, 8, 256, None) == EINVAL   # overlap
     assert lib.qgemv_quantize_weights(2, A + 4, A + (1 << 30), 8, 256, None) == EALIGN
     assert lib.qgemv_quantize_weights(5, A, A + (1 << 30), 8, 256, None) == EINVAL

@@ -1,4 +1,4 @@
-"""GPU parity of the integer matrix-core path (Q4_K with 1..8 activation vectors,
+"""GPU parity of the integer matrix-core path (Q4_K with 1..16 activation vectors,
 v_mfma_i32_16x16x64_i8) against the CPU oracle, through the C-ABI: integer partials P and
 activation block sums S bit-exact (debug form), every y within 1e-5 of sum_i |w_i| |x_i| of its
 row and vector. Small shapes call the path directly (qgemv_*_i8mc) and cover every wave count
@@ -69,6 +69,12 @@ SHAPES = [
     (4100, 2048, 8),      # many row tiles per workgroup
     (2000, 1024, 2),
     (777, 1280, 1),       # one vector
+    # two groups of 8 vectors per launch
+    (300, 512, 9),
+    (1000, 1536, 12),
+    (4100, 2048, 16),
+    (513, 2304, 13),      # two splits, a wave with no super-block
+    (37, 6144, 16),
 ]
 
 
@@ -106,12 +112,13 @@ def test_integer_extremes():
     assert np.array_equal(P, ref["P"])
 
 
-def test_deterministic_identical_vectors_and_untouched_outside():
+@pytest.mark.parametrize("nvec", [8, 16])
+def test_deterministic_identical_vectors_and_untouched_outside(nvec):
     """Run-to-run identical bits; identical vectors give identical rows of y (each vector
     sits in different lanes); nothing outside y is written."""
     import torch
     import block_quantized_weight_act_amd as qg
-    rows, cols, nvec = 515, 2048, 8
+    rows, cols = 515, 2048
     rng = np.random.default_rng(5)
     wt = gu.dev(oracle.quantize_q4k((rng.standard_normal((rows, cols)) * 0.02).astype(np.float32)))
     x = rng.standard_normal((1, cols)).astype(np.float32)

@@ -1,4 +1,4 @@
-"""GPU parity of the matrix-core path (Q4_K with 9..256 activation vectors) against the CPU
+"""GPU parity of the matrix-core path (Q4_K with 17..256 activation vectors) against the CPU
 oracle, through the C-ABI: integer partials P and activation block sums S bit-exact (debug
 form), every y within 1e-5 of sum_i |w_i| |x_i| of its row and vector. Shapes cover every
 vector-tile count (1..4 tiles of 32, one and several vector groups), ragged row tiles, column
@@ -42,7 +42,7 @@ def _check(wbuf, rows, cols, x, debug=True):
 
 SHAPES = [
     # (rows, cols, nvec)
-    (300, 512, 9),        # one tile of 32 vectors, 23 idle; ragged last row tile; split
+    (300, 512, 17),       # one tile of 32 vectors, 15 idle; ragged last row tile; split
     (257, 768, 33),       # two tiles
     (128, 2048, 64),      # one row tile, split over 8 super-blocks
     (1000, 1536, 100),    # four tiles (100 of 128)
