@@ -1,4 +1,4 @@
-// Q4_K weights x a few (2..8) int8 activation vectors on the integer matrix cores
+// Q4_K weights x 1..16 int8 activation vectors on the integer matrix cores
 // (v_mfma_i32_16x16x64_i8).
 //
 // With several vectors the vector kernel's int8 4-way dot products, eight per 32-column block
@@ -13,25 +13,29 @@
 //  * A product covers two 32-column blocks: the 16 output columns are 8 vectors x the two
 //    blocks, and the activation operand holds zeros where a vector's block does not meet the
 //    weight columns of the other block. Every output is then the P of one (vector, block, row).
+//    With 9..16 vectors a second product per pair of blocks takes the second group of 8 from
+//    the same weight operand.
 //  * The float work per output and block is the exact integer sc * P, its conversion and one
 //    fma with the activation scale; the super-scale d is applied once per super-block. The min
 //    term dmin * m * xd * S (S = sum of the block's codes) is a contraction over the blocks of
 //    dmin * m (block, row) with -xd * S (vector, block), done on the float32 matrix cores
 //    (v_mfma_f32_16x16x4_f32, four blocks per instruction) straight into the accumulator.
 //
-// Work split: a workgroup of up to 4 waves takes a row tile of 16 rows at a time over one
-// column split of up to 8 super-blocks, each wave two super-blocks; the waves' sums are added
-// in LDS in wave order. The split's activation (codes in the operand order, scales, -xd * S) is
-// staged in LDS once per workgroup and held in registers by each wave for its super-blocks, so
-// the loop over row tiles reads only weights: 4 x 8 code bytes and a 16-byte header per lane
-// and super-block, the next tile's loads issued before the current tile's arithmetic.
+// Work split: a workgroup of up to 4 waves takes row tiles of 16 rows in turn over one column
+// split of up to 8 super-blocks, each wave two super-blocks; the waves' sums are added in LDS
+// in wave order. The split's activation (codes in the operand order, scales, -xd * S) is staged
+// in LDS once per workgroup, so the loop over row tiles reads only weights from memory: per
+// lane and super-block two 16-byte code loads (the four lanes of a row read 64 contiguous
+// bytes; one exchange between lane groups then gives each lane the half-chunks it multiplies)
+// and the 16-byte header. The next tile's loads go out as soon as the current tile's
+// arithmetic has read the registers, ahead of the sums over the waves and the stores.
 //
 // Lane layouts (16 x 16 products, checked on gfx950): lane l holds operand row / column l % 16,
 // slots of lane group g = l / 16; result element i is row 4 g + i, column l % 16. Which column
 // each (group, slot) stands for is free as long as both operands agree; here the weight lane of
-// group g takes the 8 code bytes 8 (g % 2) .. + 7 of block 2 t + g / 2 of the pair t, slots
-// 0..7 their low nibbles (columns 8 (g % 2) + 0..7) and 8..15 their high nibbles (columns
-// 16 + 8 (g % 2) + 0..7). The staged activation of a block is stored in that order.
+// group g multiplies the 8 code bytes 8 (g % 2) .. + 7 of block 2 t + g / 2 of the pair t,
+// slots 0..7 their low nibbles (columns 8 (g % 2) + 0..7) and 8..15 their high nibbles
+// (columns 16 + 8 (g % 2) + 0..7). The staged activation of a block is stored in that order.
 #include <algorithm>
 #include <atomic>
 
