@@ -156,6 +156,12 @@ qgemv_plan make_plan(int wtype, int64_t rows, int64_t cols, int32_t nvec) {
     const int64_t steps = (groups + groups_per_step(best_nc) - 1) / groups_per_step(best_nc);
     const int64_t waves_per_split = std::max<int64_t>(1, target_waves(nvec) / splits);
     const int64_t want = std::min(steps, waves_per_split);
+    // A wide activation slice: every workgroup of the fused form quantizes the whole slice its
+    // lanes read, so 8 waves per workgroup halve that work per lane and the slice's L2 reads
+    // per wave (1536 x 6144, one vector: 3.9 us in one launch against 5.6 us with 4 waves).
+    // Not when it would leave fewer than 128 workgroups (1536 x 2048: 3.4 us against 2.9 us);
+    // the unfused form runs at the same speed either way.
+    if (gemv_max_waves(nvec, best_t, best_nc) == 8 && want >= 8 * 128) p.waves_per_block = 8;
     p.blocks = static_cast<int32_t>(std::max<int64_t>(1, (want + p.waves_per_block - 1) /
                                                              p.waves_per_block));
     return p;
@@ -163,7 +169,8 @@ qgemv_plan make_plan(int wtype, int64_t rows, int64_t cols, int32_t nvec) {
 
 bool plan_ok(const qgemv_plan &p, int32_t nvec) {
     return variant_exists(p.lanes_per_row, p.chunks_per_lane, nvec) && p.waves_per_block >= 1 &&
-           p.waves_per_block <= 4 && p.blocks >= 1 && p.blocks <= 65535 * 64;
+           p.waves_per_block <= gemv_max_waves(nvec, p.lanes_per_row, p.chunks_per_lane) &&
+           p.blocks >= 1 && p.blocks <= 65535 * 64;
 }
 
 size_t plan_ws_bytes(const qgemv_plan &p, int64_t rows, int64_t cols, int32_t nvec) {
@@ -732,16 +739,17 @@ int qgemv_fused_launches(int wtype, int64_t rows, int64_t cols, int32_t nvec, in
     // running the product from the codes was measured faster than every workgroup quantizing
     // the split's activation itself.
     if (i8_auto(wtype, rows, cols, nvec)) return 2;
-    // Every workgroup of the fused kernel quantizes the whole activation slice its lanes read.
-    // When that slice is large next to the workgroup's share of the weights (wide rows, many
-    // vectors, few rows per workgroup), the repeated quantization costs more than a second
-    // launch: then, if the caller gave places for the codes, the library quantizes once into
-    // them and runs the product from them. Both forms give the same codes and the same y.
+    // Every workgroup of the fused kernel quantizes the whole activation slice its lanes read,
+    // groups of 4 elements spread over its lanes. Past 4 groups per lane (wide rows, several
+    // vectors) that costs more than a second launch (~1.9 us): then, if the caller gave places
+    // for the codes, the library quantizes once into them and runs the product from them.
+    // Both forms give the same codes and the same y. Measured on MI355X, one launch against
+    // two: 1536 x 6144 (3 groups per lane) 3.9 / 5.4 us, 8192 x 2048 x 4 vectors (4) 6.6 /
+    // 7.1 us, 2048 x 8192 Q6_K x 2 vectors (8) 8.1 / 7.2 us.
     const qgemv_plan plan = make_plan(wtype, rows, cols, nvec);
-    const double slice = static_cast<double>(nvec) * plan.lanes_per_row * plan.chunks_per_lane * 32;
-    const double share = static_cast<double>(weight_bytes(wtype, rows, cols)) /
-                         (static_cast<double>(plan.blocks) * plan.splits);
-    return slice > 0.15 * share ? 2 : 1;
+    const int64_t quads = static_cast<int64_t>(nvec) * plan.lanes_per_row * plan.chunks_per_lane * 8;
+    const int64_t lanes = 64 * static_cast<int64_t>(plan.waves_per_block);
+    return (quads + lanes - 1) / lanes > 4 ? 2 : 1;
 }
 
 int qgemv_fused(int wtype, const void *w, const float *x, int8_t *xq_out, float *xd_out, float *y,

@@ -13,6 +13,8 @@
 //    (while the weights are in flight) the slice is finished; each later step's loads go out
 //    at the end of the previous step's arithmetic. Loads complete in issue order, so waiting
 //    for the slice never waits for the weights.
+//  * Workgroups have up to 4 waves, or up to 8 where the lanes of a row read a wide activation
+//    slice: the fused form quantizes the slice once per workgroup, so more waves share it.
 //  * Kernel forms (kModePlain / kModeFused / kModeDebug) are a template parameter, so each has
 //    its own name in kernel traces.
 //
@@ -45,7 +47,7 @@ struct Q80 {
 };
 
 template <class F, int V, int T, int NC, int MODE>
-__global__ void __launch_bounds__(256) gemv_kernel(GemvArgs a) {
+__global__ void __launch_bounds__(64 * gemv_max_waves(V, T, NC)) gemv_kernel(GemvArgs a) {
     constexpr bool DBG = MODE == kModeDebug;
     constexpr bool FUSED = MODE == kModeFused;
     using Tile = typename F::template Tile<V, T, NC>;
@@ -98,6 +100,7 @@ struct GemvLaunch {
     template <int V, int T, int NC>
     static hipError_t variant(const GemvArgs &a, const LaunchShape &s, bool debug,
                               hipStream_t stream) {
+        if (s.waves < 1 || s.waves > gemv_max_waves(V, T, NC)) return hipErrorInvalidValue;
         const dim3 grid(static_cast<unsigned>(s.blocks), static_cast<unsigned>(s.splits));
         const dim3 block(static_cast<unsigned>(64 * s.waves));
         const size_t lds = act_slice_lds_bytes<V, T, NC>();

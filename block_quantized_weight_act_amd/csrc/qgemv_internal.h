@@ -20,6 +20,15 @@ constexpr int groups_per_step(int chunks_per_lane) {
     return chunks_per_lane == 1 ? 4 : (chunks_per_lane == 2 ? 2 : 1);
 }
 
+// Largest workgroup of the one-matrix GEMV, in waves: 8 for a wide activation slice (a lane
+// group reading nvec * lanes_per_row * chunks_per_lane >= 128 blocks of 32 columns), whose
+// quantization in the fused form the workgroup's lanes share; 4 otherwise, which keeps the
+// register budget of the narrow-slice kernels at that of 256-thread workgroups.
+constexpr int kWideSliceBlocks = 128;
+constexpr int gemv_max_waves(int nvec, int lanes_per_row, int chunks_per_lane) {
+    return nvec * lanes_per_row * chunks_per_lane >= kWideSliceBlocks ? 8 : 4;
+}
+
 // One GEMV launch: the kernels read everything they need from here.
 struct GemvArgs {
     const uint8_t *w;      // weight tensor (Q4_K blocks, or Q6_K bodies followed by the d plane)

@@ -419,7 +419,8 @@ int qgemv_quantize_weights_rows(int wtype, const float *w, void *out, int64_t ro
 typedef struct qgemv_plan {
     int32_t lanes_per_row;    /* 8, 16, 32 or 64 */
     int32_t chunks_per_lane;  /* 1 .. 4 */
-    int32_t waves_per_block;  /* 1 .. 4 */
+    int32_t waves_per_block;  /* 1 .. 4; 1 .. 8 when nvec * lanes_per_row *
+                                 chunks_per_lane >= 128 */
     int32_t blocks;           /* workgroups per column chunk, >= 1 */
     int32_t splits;           /* derived: column chunks (output of qgemv_plan_for) */
 } qgemv_plan;

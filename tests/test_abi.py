@@ -139,6 +139,10 @@ def test_split_plan_without_workspace_is_rejected():
     bad = qg.Plan(12, 1, 4, 4, 0)
     assert lib.qgemv_batch_plan(1, A, A + (1 << 30), A + (2 << 30), A + (3 << 30), rows, cols, 1,
                                 ctypes.byref(bad), None, 0, None) == EINVAL
+    for wide in (qg.Plan(16, 1, 8, 4, 0),              # a narrow slice: at most 4 waves
+                 qg.Plan(64, 3, 9, 4, 0), qg.Plan(64, 3, 0, 4, 0)):
+        assert lib.qgemv_batch_plan(1, A, A + (1 << 30), A + (2 << 30), A + (3 << 30), rows,
+                                    cols, 1, ctypes.byref(wide), None, 0, None) == EINVAL
     toomany = qg.Plan(16, 4, 4, 4, 0)                  # 3 vectors x 4 chunks: not compiled
     assert lib.qgemv_batch_plan(1, A, A + (1 << 30), A + (2 << 30), A + (3 << 30), rows, cols, 3,
                                 ctypes.byref(toomany), None, 0, None) == EINVAL
@@ -171,12 +175,17 @@ def test_other_entry_points_reject_bad_arguments():
 
 
 def test_fused_launch_count():
-    """The one-launch kernel unless code outputs are wanted and the activation slice is large
-    next to a workgroup's share of the weights (then quantize once, then the product), and
-    always on the integer matrix-core path (Q4_K, several vectors, a large tensor)."""
+    """The one-launch kernel unless code outputs are wanted and the activation slice is more
+    than 4 groups of 4 elements per lane of a workgroup (then quantize once, then the
+    product), and always on the integer matrix-core path (Q4_K, several vectors, a large
+    tensor)."""
     assert qg.qgemv_fused_launches("q4k", 262144, 1536, 1) == 1
     assert qg.qgemv_fused_launches("q4k", 8192, 2048, 1) == 1
-    assert qg.qgemv_fused_launches("q6k", 2048, 8192, 1) == 2
+    assert qg.qgemv_fused_launches("q6k", 2048, 8192, 1) == 1       # 8192 columns, 8 waves: 4
+    assert qg.qgemv_fused_launches("q4k", 1536, 6144, 1) == 1       # 6144 columns, 8 waves: 3
+    assert qg.qgemv_fused_launches("q6k", 2048, 8192, 2) == 2       # two vectors: 8
+    assert qg.qgemv_fused_launches("q4k", 8192, 2048, 8) == 2       # 8 vectors, 8 waves: 8
+    assert qg.qgemv_fused_launches("q4k", 8192, 2048, 4) == 1       # 4 vectors, 8 waves: 4
     assert qg.qgemv_fused_launches("q4k", 16384, 2048, 8) == 2
     assert qg.qgemv_fused_launches("q4k", 262144, 1536, 8) == 2      # integer matrix cores
     assert qg.qgemv_fused_launches("q4k", 262144, 1536, 8, with_outputs=False) == 1

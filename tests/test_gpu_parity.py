@@ -175,7 +175,8 @@ def test_ragged_shapes_32_weight_blocks(wtype, rows, cols, nvec):
 
 PLANS = [dict(lanes_per_row=t, chunks_per_lane=nc, waves_per_block=wv, blocks=b)
          for t, nc, wv, b in [(8, 1, 1, 1), (8, 4, 4, 3), (16, 1, 2, 7), (16, 3, 4, 64),
-                              (32, 2, 4, 5), (64, 1, 4, 100), (64, 4, 1, 2), (64, 2, 3, 1000)]]
+                              (32, 2, 4, 5), (64, 1, 4, 100), (64, 4, 1, 2), (64, 2, 3, 1000),
+                              (32, 2, 8, 3), (64, 3, 8, 9), (64, 1, 6, 40)]]
 
 
 @pytest.mark.parametrize("plan", PLANS, ids=lambda p: "T%d_NC%d_W%d_B%d" % (
@@ -290,6 +291,7 @@ def test_workspace_required_when_split():
 @pytest.mark.parametrize("wtype,rows,cols,nvec", [
     ("q4k", 262144, 1536, 1), ("q4k", 8192, 2048, 1), ("q6k", 2048, 8192, 1),
     ("q4k", 16384, 2048, 8), ("q4k", 512, 512, 1), ("q6k", 333, 8448, 3), ("q4k", 77, 8448, 2),
+    ("q4k", 1536, 6144, 1), ("q4k", 8192, 2048, 2), ("q6k", 2048, 8192, 2),
     ("q40", 4099, 1504, 1), ("q80", 1000, 2080, 2), ("q40", 300, 8224, 3), ("q80", 64, 96, 8),
 ])
 def test_fused_quantize_and_gemv(wtype, rows, cols, nvec):
