@@ -17,7 +17,7 @@ namespace qgemv {
 
 // Shape of the fused form's work: the workgroup's column chunk holds kBlocks activation
 // blocks (all vectors), kQuads groups of 4 elements; each lane takes up to kSlots quads per
-// round (quad base + i * blockDim.x + threadIdx.x of round base). kSlots is sized so that
+// round (quad base + i * a.threads + threadIdx.x of round base). kSlots is sized so that
 // one round of a 256-thread workgroup covers the chunk (at most 4 quads per lane; smaller
 // workgroups and larger chunks take more rounds).
 template <int V, int T, int NC>
@@ -64,7 +64,7 @@ __device__ __forceinline__ void load_round(const GemvArgs &a, int base,
         int64_t elem;
         int v, gc;
         const bool ok = quad_at<V, T, NC>(
-            a, base + i * static_cast<int>(blockDim.x) + static_cast<int>(threadIdx.x), elem, v,
+            a, base + i * a.threads + static_cast<int>(threadIdx.x), elem, v,
             gc);
         xv[i] = ok ? *reinterpret_cast<const float4 *>(a.x + elem)
                    : make_float4(0.f, 0.f, 0.f, 0.f);
@@ -82,7 +82,7 @@ __device__ __forceinline__ void store_round(const GemvArgs &a, int base,
     float *s_scale = reinterpret_cast<float *>(lds + 2 * F::kBlocks);
 #pragma unroll
     for (int i = 0; i < F::kSlots; i++) {
-        const int first = base + i * static_cast<int>(blockDim.x);   // the same for the workgroup
+        const int first = base + i * a.threads;   // the same for the workgroup
         if (first >= F::kQuads) break;
         const int qd = first + static_cast<int>(threadIdx.x);
         int64_t elem;
@@ -140,7 +140,7 @@ __device__ __forceinline__ void act_slice_finish(const GemvArgs &a, const bool (
                                                  ActPending<V, T, NC, FUSED> &pend) {
     if constexpr (FUSED) {
         using F = FusedAct<V, T, NC>;
-        const int round = F::kSlots * static_cast<int>(blockDim.x);
+        const int round = F::kSlots * a.threads;
         fused_detail::store_round<V, T, NC>(a, 0, pend.xv);
         for (int base = round; base < F::kQuads; base += round) {
             fused_detail::load_round<V, T, NC>(a, base, pend.xv);

@@ -8,32 +8,12 @@
 // tile (tile.h) of the matrix it falls in. A wave's activation slice is loaded (or,
 // in the fused form, quantized by its workgroup) once and serves every matrix, since lane t's
 // columns are the same in all of them. No column split: the shared lane geometry covers a
-// whole row (at most 256 chunks, 8192 columns).
-#include "act_slice.h"
-#include "device_common.h"
-#include "qgemv_internal.h"
-#include "tile.h"
+// whole row (at most 256 chunks, 8192 columns). This file holds the kernel for a mix of
+// formats; matrices all of one format take the one-matrix walk over the same step numbering
+// (gemv_multi_fmt_kernel in gemv_walk.h).
+#include "gemv_walk.h"
 
 namespace qgemv {
-
-// The matrix that step st falls in (the same for the whole wave): the last one whose first
-// step is not after st. Only the first steps are scanned; the chosen descriptor is then read with
-// a wave-uniform index, so it comes from the argument block by scalar loads and only one
-// descriptor is held in SGPRs at a time.
-struct StepMat {
-    const uint8_t *w;
-    float *out;
-    int rows, nb, wtype, local;
-};
-
-__device__ __forceinline__ StepMat step_matrix(const MultiArgs &a, int st) {
-    int mi = 0;
-#pragma unroll
-    for (int i = 1; i < kMaxMats; i++)
-        if (i < a.nmats && st >= a.m[i].step0) mi = i;
-    const MatDesc &d = a.m[mi];
-    return StepMat{d.w, d.out, d.rows, d.nb, d.wtype, st - d.step0};
-}
 
 template <int V, int T, int NC, int MODE>
 __global__ void __launch_bounds__(256) gemv_multi_kernel(MultiArgs a) {
@@ -47,12 +27,12 @@ __global__ void __launch_bounds__(256) gemv_multi_kernel(MultiArgs a) {
     const LaneGeom<T, NC> L(a.act.nchunks);
     // the wave index is the same in all 64 lanes: keep it (and the step numbers) in SGPRs
     const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
-    const int wpb = blockDim.x >> 6;
+    const int wpb = a.act.threads >> 6;
     const int stride = gridDim.x * wpb;
     const int st0 = blockIdx.x * wpb + wave;
     typename T4::Regs regs;                  // one register set for every format
     auto issue = [&](int st) {
-        const StepMat m = step_matrix(a, st);
+        const StepMat m = MatrixList{a}.at(st);
         if (m.wtype == kTypeQ4K)
             T4::issue(regs, m.w, m.rows, m.nb, m.local, L);
         else if (m.wtype == kTypeQ6K)
@@ -63,10 +43,11 @@ __global__ void __launch_bounds__(256) gemv_multi_kernel(MultiArgs a) {
             T80::issue(regs, m.w, m.rows, m.nb, m.local, L);
     };
 
-    // Unlike the one-matrix kernels, the first step's weights are not loaded ahead of the
-    // slice: with the decode-layer shapes this kernel serves, each wave takes about one step
-    // and issuing those loads first measured slower (2 x 6144 x 1536: 5.9 against 5.2 us fused,
-    // 4.8 against 4.6 us from codes); the walk keeps the plain order, loads then arithmetic.
+    // Unlike the one-format walk, the first step's weights are not loaded ahead of the slice:
+    // with the load sequence chosen by a branch on the format, the compiler's wait for the
+    // slice at the branches' join waits for every load issued in them, so loading the weights
+    // first only moved their latency in front of the slice's (measured slower); the walk keeps
+    // the plain order, loads then arithmetic.
     uint32_t xw[V][NC][8];
     float xs[V][NC];
     ActTerms<V, NC> at;
@@ -78,7 +59,7 @@ __global__ void __launch_bounds__(256) gemv_multi_kernel(MultiArgs a) {
     for (int st = st0; st < a.steps; st += stride) {
         issue(st);
         __builtin_amdgcn_sched_barrier(0);
-        const StepMat m = step_matrix(a, st);
+        const StepMat m = MatrixList{a}.at(st);
         const int nsub = a.act.nchunks;
         if (m.wtype == kTypeQ4K)
             T4::template compute<false>(regs, xw, xs, at, m.out, m.rows, m.local, L, nullptr, nsub);
@@ -103,10 +84,12 @@ hipError_t launch_multi_variant(const MultiArgs &a, const LaunchShape &s, hipStr
     const dim3 grid(static_cast<unsigned>(s.blocks));
     const dim3 block(static_cast<unsigned>(64 * s.waves));
     const size_t lds = act_slice_lds_bytes<V, T, NC>();
+    MultiArgs b = a;
+    b.act.threads = 64 * s.waves;
     if (a.act.x != nullptr)
-        hipLaunchKernelGGL((gemv_multi_kernel<V, T, NC, kModeFused>), grid, block, lds, stream, a);
+        hipLaunchKernelGGL((gemv_multi_kernel<V, T, NC, kModeFused>), grid, block, lds, stream, b);
     else
-        hipLaunchKernelGGL((gemv_multi_kernel<V, T, NC, kModePlain>), grid, block, 0, stream, a);
+        hipLaunchKernelGGL((gemv_multi_kernel<V, T, NC, kModePlain>), grid, block, 0, stream, b);
     return hipGetLastError();
 }
 

@@ -46,17 +46,49 @@ struct Q80 {
     using Tile = Q80Tile<V, T, NC>;
 };
 
-template <class F, int V, int T, int NC, int MODE>
-__global__ void __launch_bounds__(64 * gemv_max_waves(V, T, NC)) gemv_kernel(GemvArgs a) {
+// Where the weights and the outputs of one step are: the matrix's planes, its y, its rows and
+// blocks per row, and the step's number within the matrix (local).
+struct StepMat {
+    const uint8_t *w;
+    float *out;
+    int rows, nb, wtype, local;
+};
+
+// One matrix: step st is its own step st.
+struct OneMatrix {
+    const GemvArgs &a;
+    __device__ __forceinline__ StepMat at(int st) const {
+        return StepMat{a.w, a.out, a.rows, a.nb, 0, st};
+    }
+};
+
+// Several matrices sharing the activation (MultiArgs): their steps are numbered one after the
+// other, and step st falls in the last matrix whose first step is not after it. Only the first
+// steps are scanned; the chosen descriptor is then read with a wave-uniform index, so it comes
+// from the argument block by scalar loads. A step past the end falls in the last matrix (its
+// rows are clamped like any row past the end).
+struct MatrixList {
+    const MultiArgs &a;
+    __device__ __forceinline__ StepMat at(int st) const {
+        int mi = 0;
+#pragma unroll
+        for (int i = 1; i < kMaxMats; i++)
+            if (i < a.nmats && st >= a.m[i].step0) mi = i;
+        const MatDesc &d = a.m[mi];
+        return StepMat{d.w, d.out, d.rows, d.nb, d.wtype, st - d.step0};
+    }
+};
+
+// The walk of a wave over its steps (steps st0, st0 + stride, ... of `steps`), for one tile
+// type; `src` says where each step's weights and outputs are.
+template <class Tile, int V, int T, int NC, int MODE, class Steps>
+__device__ __forceinline__ void gemv_walk(const GemvArgs &a, const Steps &src, int steps) {
     constexpr bool DBG = MODE == kModeDebug;
     constexpr bool FUSED = MODE == kModeFused;
-    using Tile = typename F::template Tile<V, T, NC>;
     const LaneGeom<T, NC> L(a.nchunks);
     // the wave index is the same in all 64 lanes: keep it (and the step numbers) in SGPRs
     const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
-    const int wpb = blockDim.x >> 6;
-    const int groups = (a.rows + Tile::RPW - 1) / Tile::RPW;
-    const int steps = (groups + Tile::G - 1) / Tile::G;
+    const int wpb = a.threads >> 6;
     const int stride = gridDim.x * wpb;
     const int st0 = blockIdx.x * wpb + wave;
 
@@ -67,7 +99,10 @@ __global__ void __launch_bounds__(64 * gemv_max_waves(V, T, NC)) gemv_kernel(Gem
     ActPending<V, T, NC, FUSED> pend;
     act_slice_issue<V, T, NC, FUSED>(a, L.g, L.cv, xw, xs, pend);
     __builtin_amdgcn_sched_barrier(0);
-    Tile::issue(regs, a.w, a.rows, a.nb, st0, L);   // rows (>= 1) clamped: valid for any st0
+    {
+        const StepMat m = src.at(st0);   // rows (>= 1) clamped: valid for any st0
+        Tile::issue(regs, m.w, m.rows, m.nb, m.local, L);
+    }
     __builtin_amdgcn_sched_barrier(0);
     act_slice_finish<V, T, NC, FUSED>(a, L.cv, L.t, xw, xs, pend);
     act_terms<V, NC>(xw, at);
@@ -83,75 +118,123 @@ __global__ void __launch_bounds__(64 * gemv_max_waves(V, T, NC)) gemv_kernel(Gem
         // Keep every load of the step ahead of the arithmetic: without this fence the
         // scheduler interleaves them to save registers and waits for each load in turn.
         __builtin_amdgcn_sched_barrier(0);
-        Tile::template compute<DBG>(regs, xw, xs, at, a.out, a.rows, st, L, a.P, a.nchunks);
+        const StepMat m = src.at(st);
+        Tile::template compute<DBG>(regs, xw, xs, at, m.out, m.rows, m.local, L, a.P, a.nchunks);
         // The next step's loads go out as soon as this step's arithmetic is done, so the
         // values of one step are never live across the loop's back edge with the next ones.
         __builtin_amdgcn_sched_barrier(0);
-        if (st + stride < steps) Tile::issue(regs, a.w, a.rows, a.nb, st + stride, L);
+        if (st + stride < steps) {
+            const StepMat n = src.at(st + stride);
+            Tile::issue(regs, n.w, n.rows, n.nb, n.local, L);
+        }
     }
 }
 
-// The launch of one format: a table over (vectors, lanes per row, chunks per lane) of the
-// compiled instances (nvec * chunks <= 8, so the activation slice fits in VGPRs).
+template <class F, int V, int T, int NC, int MODE>
+__global__ void __launch_bounds__(64 * gemv_max_waves(V, T, NC)) gemv_kernel(GemvArgs a) {
+    using Tile = typename F::template Tile<V, T, NC>;
+    const int groups = (a.rows + Tile::RPW - 1) / Tile::RPW;
+    const int steps = (groups + Tile::G - 1) / Tile::G;
+    gemv_walk<Tile, V, T, NC, MODE>(a, OneMatrix{a}, steps);
+}
+
+// Several matrices of this one format sharing the activation (qgemv_multi with a single
+// format): the same walk over their combined step numbering, so the first step's weights go
+// out before the activation slice is finished, as for one matrix.
+template <class F, int V, int T, int NC, int MODE>
+__global__ void __launch_bounds__(256) gemv_multi_fmt_kernel(MultiArgs a) {
+    gemv_walk<typename F::template Tile<V, T, NC>, V, T, NC, MODE>(a.act, MatrixList{a}, a.steps);
+}
+
+// The launches of one format: tables over (vectors, lanes per row, chunks per lane) of the
+// compiled instances (nvec * chunks <= 8, so the activation slice fits in VGPRs), one for the
+// one-matrix kernel and one for several matrices of this format.
 template <class F>
 struct GemvLaunch {
-    using Launcher = hipError_t (*)(const GemvArgs &, const LaunchShape &, bool, hipStream_t);
-
-    template <int V, int T, int NC>
-    static hipError_t variant(const GemvArgs &a, const LaunchShape &s, bool debug,
+    struct One {
+        using Args = GemvArgs;
+        template <int V, int T, int NC>
+        static hipError_t run(const GemvArgs &a, const LaunchShape &s, bool debug,
                               hipStream_t stream) {
-        if (s.waves < 1 || s.waves > gemv_max_waves(V, T, NC)) return hipErrorInvalidValue;
-        const dim3 grid(static_cast<unsigned>(s.blocks), static_cast<unsigned>(s.splits));
-        const dim3 block(static_cast<unsigned>(64 * s.waves));
-        const size_t lds = act_slice_lds_bytes<V, T, NC>();
-        if (debug)
-            hipLaunchKernelGGL((gemv_kernel<F, V, T, NC, kModeDebug>), grid, block, 0, stream, a);
-        else if (a.x != nullptr)
-            hipLaunchKernelGGL((gemv_kernel<F, V, T, NC, kModeFused>), grid, block, lds, stream, a);
-        else
-            hipLaunchKernelGGL((gemv_kernel<F, V, T, NC, kModePlain>), grid, block, 0, stream, a);
-        return hipGetLastError();
-    }
+            if (s.waves < 1 || s.waves > gemv_max_waves(V, T, NC)) return hipErrorInvalidValue;
+            const dim3 grid(static_cast<unsigned>(s.blocks), static_cast<unsigned>(s.splits));
+            const dim3 block(static_cast<unsigned>(64 * s.waves));
+            const size_t lds = act_slice_lds_bytes<V, T, NC>();
+            GemvArgs b = a;
+            b.threads = 64 * s.waves;
+            if (debug)
+                hipLaunchKernelGGL((gemv_kernel<F, V, T, NC, kModeDebug>), grid, block, 0, stream,
+                                   b);
+            else if (a.x != nullptr)
+                hipLaunchKernelGGL((gemv_kernel<F, V, T, NC, kModeFused>), grid, block, lds,
+                                   stream, b);
+            else
+                hipLaunchKernelGGL((gemv_kernel<F, V, T, NC, kModePlain>), grid, block, 0, stream,
+                                   b);
+            return hipGetLastError();
+        }
+    };
 
-    template <int V, int T, int NC>
-    static constexpr Launcher pick() {
-        if constexpr (V * NC <= 8)
-            return &variant<V, T, NC>;
-        else
-            return nullptr;
-    }
+    struct Multi {
+        using Args = MultiArgs;
+        template <int V, int T, int NC>
+        static hipError_t run(const MultiArgs &a, const LaunchShape &s, bool debug,
+                              hipStream_t stream) {
+            if (debug || s.waves < 1 || s.waves > 4 || s.splits != 1) return hipErrorInvalidValue;
+            const dim3 grid(static_cast<unsigned>(s.blocks));
+            const dim3 block(static_cast<unsigned>(64 * s.waves));
+            const size_t lds = act_slice_lds_bytes<V, T, NC>();
+            MultiArgs b = a;
+            b.act.threads = 64 * s.waves;
+            if (a.act.x != nullptr)
+                hipLaunchKernelGGL((gemv_multi_fmt_kernel<F, V, T, NC, kModeFused>), grid, block,
+                                   lds, stream, b);
+            else
+                hipLaunchKernelGGL((gemv_multi_fmt_kernel<F, V, T, NC, kModePlain>), grid, block,
+                                   0, stream, b);
+            return hipGetLastError();
+        }
+    };
 
-    template <int V, int T>
-    static constexpr void row(Launcher (&out)[4]) {
-        out[0] = pick<V, T, 1>();
-        out[1] = pick<V, T, 2>();
-        out[2] = pick<V, T, 3>();
-        out[3] = pick<V, T, 4>();
-    }
+    template <class K>
+    struct Table {
+        using Fn = hipError_t (*)(const typename K::Args &, const LaunchShape &, bool,
+                                  hipStream_t);
+        Fn fn[8][4][4] = {};
+        template <int V, int T, int NC>
+        constexpr void put(int ti) {
+            if constexpr (V * NC <= 8) fn[V - 1][ti][NC - 1] = &K::template run<V, T, NC>;
+        }
+        template <int V, int T>
+        constexpr void row(int ti) {
+            put<V, T, 1>(ti);
+            put<V, T, 2>(ti);
+            put<V, T, 3>(ti);
+            put<V, T, 4>(ti);
+        }
+        template <int V>
+        constexpr void vec() {
+            row<V, 8>(0);
+            row<V, 16>(1);
+            row<V, 32>(2);
+            row<V, 64>(3);
+        }
+        constexpr Table() {
+            vec<1>();
+            vec<2>();
+            vec<3>();
+            vec<4>();
+            vec<5>();
+            vec<6>();
+            vec<7>();
+            vec<8>();
+        }
+    };
 
-    template <int V>
-    static constexpr void fill(Launcher (&out)[4][4]) {
-        row<V, 8>(out[0]);
-        row<V, 16>(out[1]);
-        row<V, 32>(out[2]);
-        row<V, 64>(out[3]);
-    }
-
-    static hipError_t launch(const GemvArgs &a, const LaunchShape &s, int nvec, bool debug,
-                             hipStream_t stream) {
-        static Launcher table[8][4][4] = {};
-        static const bool filled = [] {
-            fill<1>(table[0]);
-            fill<2>(table[1]);
-            fill<3>(table[2]);
-            fill<4>(table[3]);
-            fill<5>(table[4]);
-            fill<6>(table[5]);
-            fill<7>(table[6]);
-            fill<8>(table[7]);
-            return true;
-        }();
-        (void)filled;
+    template <class K>
+    static hipError_t dispatch(const typename K::Args &a, const LaunchShape &s, int nvec,
+                               bool debug, hipStream_t stream) {
+        static const Table<K> table;
         int ti = -1;
         switch (s.lanes) {
             case 8: ti = 0; break;
@@ -161,9 +244,18 @@ struct GemvLaunch {
             default: return hipErrorInvalidValue;
         }
         if (nvec < 1 || nvec > 8 || s.chunks < 1 || s.chunks > 4) return hipErrorInvalidValue;
-        const Launcher fn = table[nvec - 1][ti][s.chunks - 1];
+        const auto fn = table.fn[nvec - 1][ti][s.chunks - 1];
         if (!fn) return hipErrorInvalidValue;
         return fn(a, s, debug, stream);
+    }
+
+    static hipError_t launch(const GemvArgs &a, const LaunchShape &s, int nvec, bool debug,
+                             hipStream_t stream) {
+        return dispatch<One>(a, s, nvec, debug, stream);
+    }
+    static hipError_t launch_multi(const MultiArgs &a, const LaunchShape &s, int nvec,
+                                   hipStream_t stream) {
+        return dispatch<Multi>(a, s, nvec, false, stream);
     }
 };
 

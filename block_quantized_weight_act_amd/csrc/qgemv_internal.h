@@ -44,6 +44,9 @@ struct GemvArgs {
     int32_t nb;            // weight blocks per row (256-weight super-blocks for Q4_K / Q6_K,
                            // 32-weight blocks for Q4_0 / Q8_0)
     int32_t nchunks;       // 16-byte chunks per row = 8 * nb
+    int32_t threads;       // threads per workgroup of the launch, set by the launcher (the
+                           // kernels use it instead of blockDim, which the compiler may read
+                           // with a vector load and a wait at the kernel's start)
 };
 
 // Kernel forms, a template parameter so that each has its own name in kernel traces:
@@ -93,8 +96,18 @@ hipError_t launch_gemv_q40(const GemvArgs &a, const LaunchShape &s, int nvec, bo
                            hipStream_t stream);
 hipError_t launch_gemv_q80(const GemvArgs &a, const LaunchShape &s, int nvec, bool debug,
                            hipStream_t stream);
+// Several matrices: any mix of formats (gemv_multi.hip), or all of one format (the per-format
+// files, with the one-matrix walk)
 hipError_t launch_gemv_multi(const MultiArgs &a, const LaunchShape &s, int nvec,
                              hipStream_t stream);
+hipError_t launch_gemv_multi_q4k(const MultiArgs &a, const LaunchShape &s, int nvec,
+                                 hipStream_t stream);
+hipError_t launch_gemv_multi_q6k(const MultiArgs &a, const LaunchShape &s, int nvec,
+                                 hipStream_t stream);
+hipError_t launch_gemv_multi_q40(const MultiArgs &a, const LaunchShape &s, int nvec,
+                                 hipStream_t stream);
+hipError_t launch_gemv_multi_q80(const MultiArgs &a, const LaunchShape &s, int nvec,
+                                 hipStream_t stream);
 hipError_t launch_splitk_reduce(const float *part, float *y, int64_t n, int splits,
                                 hipStream_t stream);
 // Rows [row0, row0 + nrows) of a rows x cols matrix (w points at row row0) into their places
