@@ -585,23 +585,46 @@ int prepare_multi(const qgemv_matrix *mats, int32_t nmats, const Activation &act
     a.act.xd_out = act.xd_out;
     a.act.nb = 0;                            // unused: each matrix has its own
     a.act.nchunks = static_cast<int32_t>(cols / 32);
+    // descriptors ordered by format (stable), so each format's steps are consecutive
     int64_t steps = 0;
-    for (int i = 0; i < nmats; i++) {
-        MatDesc &d = a.m[i];
-        d.w = static_cast<const uint8_t *>(mats[i].w);
-        d.out = mats[i].y;
-        d.rows = static_cast<int32_t>(mats[i].rows);
-        d.nb = static_cast<int32_t>(cols / block_cols(mats[i].wtype));
-        d.wtype = mats[i].wtype;
-        d.step0 = static_cast<int32_t>(steps);
-        steps += ((mats[i].rows + rpw - 1) / rpw + g - 1) / g;
-        if (steps >= (int64_t{1} << 30)) return QGEMV_EINVAL;
+    int k = 0;
+    for (int wt : {QGEMV_Q4K, QGEMV_Q6K, QGEMV_Q4_0, QGEMV_Q8_0}) {
+        const int64_t first = steps;
+        for (int i = 0; i < nmats; i++) {
+            if (mats[i].wtype != wt) continue;
+            MatDesc &d = a.m[k++];
+            d.w = static_cast<const uint8_t *>(mats[i].w);
+            d.out = mats[i].y;
+            d.rows = static_cast<int32_t>(mats[i].rows);
+            d.nb = static_cast<int32_t>(cols / block_cols(wt));
+            d.wtype = wt;
+            d.step0 = static_cast<int32_t>(steps);
+            steps += ((mats[i].rows + rpw - 1) / rpw + g - 1) / g;
+            if (steps >= (int64_t{1} << 30)) return QGEMV_EINVAL;
+        }
+        if (steps > first) {
+            FmtGroup &fg = a.g[a.ngroups++];
+            fg.wtype = wt;
+            fg.step0 = static_cast<int32_t>(first);
+            fg.steps = static_cast<int32_t>(steps - first);
+        }
     }
+    if (k != nmats) return QGEMV_EINVAL;
     a.nmats = nmats;
     a.steps = static_cast<int32_t>(steps);
+    // The grid, then each format's share of it in proportion to its steps (at least one
+    // workgroup each).
     const int waves = 4;
     const int64_t want = std::min<int64_t>(steps, target_waves(nvec));
-    s = LaunchShape{t, nc, waves, static_cast<int>((want + waves - 1) / waves), 1};
+    const int64_t total = (want + waves - 1) / waves;
+    int32_t blocks = 0;
+    for (int i = 0; i < a.ngroups; i++) {
+        FmtGroup &fg = a.g[i];
+        fg.block0 = blocks;
+        fg.blocks = static_cast<int32_t>(std::max<int64_t>(1, (total * fg.steps + steps - 1) / steps));
+        blocks += fg.blocks;
+    }
+    s = LaunchShape{t, nc, waves, blocks, 1};
     return QGEMV_OK;
 }
 

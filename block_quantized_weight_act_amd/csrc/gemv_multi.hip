@@ -4,75 +4,43 @@
 // genie-ai-runtime (jared-hpc.com), "v1.2.0": the attention projections of a decode step share
 // one quantized activation, which is made once and read by all of them instead of once per
 // product. Here they also share one launch: the matrices' row steps are numbered one after
-// the other and waves walk the combined numbering with a grid-wide stride, each step taking the
-// tile (tile.h) of the matrix it falls in. A wave's activation slice is loaded (or,
+// the other (grouped by format) and waves walk the numbering with a grid-wide stride, each step
+// taking the tile (tile.h) of the matrix it falls in. A wave's activation slice is loaded (or,
 // in the fused form, quantized by its workgroup) once and serves every matrix, since lane t's
 // columns are the same in all of them. No column split: the shared lane geometry covers a
 // whole row (at most 256 chunks, 8192 columns). This file holds the kernel for a mix of
-// formats; matrices all of one format take the one-matrix walk over the same step numbering
-// (gemv_multi_fmt_kernel in gemv_walk.h).
+// formats, whose workgroups are split between the formats in proportion to their steps, each
+// range walking its own format's steps; matrices all of one format take the one-matrix walk
+// over the same step numbering (gemv_multi_fmt_kernel in gemv_walk.h).
 #include "gemv_walk.h"
 
 namespace qgemv {
 
 template <int V, int T, int NC, int MODE>
 __global__ void __launch_bounds__(256) gemv_multi_kernel(MultiArgs a) {
-    constexpr bool FUSED = MODE == kModeFused;
-    using T4 = Q4kTile<V, T, NC>;
-    using T6 = Q6kTile<V, T, NC>;
-    using T40 = Q40Tile<V, T, NC>;
-    using T80 = Q80Tile<V, T, NC>;
-    static_assert(T4::G == T6::G && T4::G == T40::G && T4::G == T80::G && T4::RPW == T6::RPW,
+    static_assert(Q4kTile<V, T, NC>::G == Q6kTile<V, T, NC>::G &&
+                      Q4kTile<V, T, NC>::G == Q40Tile<V, T, NC>::G &&
+                      Q4kTile<V, T, NC>::G == Q80Tile<V, T, NC>::G &&
+                      Q4kTile<V, T, NC>::RPW == Q6kTile<V, T, NC>::RPW,
                   "one step geometry for every format");
-    const LaneGeom<T, NC> L(a.act.nchunks);
-    // the wave index is the same in all 64 lanes: keep it (and the step numbers) in SGPRs
-    const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
-    const int wpb = a.act.threads >> 6;
-    const int stride = gridDim.x * wpb;
-    const int st0 = blockIdx.x * wpb + wave;
-    typename T4::Regs regs;                  // one register set for every format
-    auto issue = [&](int st) {
-        const StepMat m = MatrixList{a}.at(st);
-        if (m.wtype == kTypeQ4K)
-            T4::issue(regs, m.w, m.rows, m.nb, m.local, L);
-        else if (m.wtype == kTypeQ6K)
-            T6::issue(regs, m.w, m.rows, m.nb, m.local, L);
-        else if (m.wtype == kTypeQ40)
-            T40::issue(regs, m.w, m.rows, m.nb, m.local, L);
-        else
-            T80::issue(regs, m.w, m.rows, m.nb, m.local, L);
-    };
-
-    // Unlike the one-format walk, the first step's weights are not loaded ahead of the slice:
-    // with the load sequence chosen by a branch on the format, the compiler's wait for the
-    // slice at the branches' join waits for every load issued in them, so loading the weights
-    // first only moved their latency in front of the slice's (measured slower); the walk keeps
-    // the plain order, loads then arithmetic.
-    uint32_t xw[V][NC][8];
-    float xs[V][NC];
-    ActTerms<V, NC> at;
-    ActPending<V, T, NC, FUSED> pend;
-    act_slice_issue<V, T, NC, FUSED>(a.act, L.g, L.cv, xw, xs, pend);
-    act_slice_finish<V, T, NC, FUSED>(a.act, L.cv, L.t, xw, xs, pend);
-    act_terms<V, NC>(xw, at);
-
-    for (int st = st0; st < a.steps; st += stride) {
-        issue(st);
-        __builtin_amdgcn_sched_barrier(0);
-        const StepMat m = MatrixList{a}.at(st);
-        const int nsub = a.act.nchunks;
-        if (m.wtype == kTypeQ4K)
-            T4::template compute<false>(regs, xw, xs, at, m.out, m.rows, m.local, L, nullptr, nsub);
-        else if (m.wtype == kTypeQ6K)
-            T6::template compute<false>(regs, xw, xs, at, m.out, m.rows, m.local, L, nullptr, nsub);
-        else if (m.wtype == kTypeQ40)
-            T40::template compute<false>(regs, xw, xs, at, m.out, m.rows, m.local, L, nullptr,
-                                         nsub);
-        else
-            T80::template compute<false>(regs, xw, xs, at, m.out, m.rows, m.local, L, nullptr,
-                                         nsub);
-        __builtin_amdgcn_sched_barrier(0);
-    }
+    // The workgroup's format group (wave-uniform), then that format's whole walk: each branch
+    // issues its first step's weights ahead of the activation slice and waits for exactly the
+    // loads of its own format, as the one-format walk does.
+    int gi = 0;
+#pragma unroll
+    for (int i = 1; i < kMaxFmtGroups; i++)
+        if (i < a.ngroups && static_cast<int>(blockIdx.x) >= a.g[i].block0) gi = i;
+    const FmtGroup &g = a.g[gi];
+    const GroupSteps src{a, g.step0, g.steps};
+    const int blk = static_cast<int>(blockIdx.x) - g.block0;
+    if (g.wtype == kTypeQ4K)
+        gemv_walk<Q4kTile<V, T, NC>, V, T, NC, MODE>(a.act, src, g.steps, blk, g.blocks);
+    else if (g.wtype == kTypeQ6K)
+        gemv_walk<Q6kTile<V, T, NC>, V, T, NC, MODE>(a.act, src, g.steps, blk, g.blocks);
+    else if (g.wtype == kTypeQ40)
+        gemv_walk<Q40Tile<V, T, NC>, V, T, NC, MODE>(a.act, src, g.steps, blk, g.blocks);
+    else
+        gemv_walk<Q80Tile<V, T, NC>, V, T, NC, MODE>(a.act, src, g.steps, blk, g.blocks);
 }
 
 namespace {

@@ -79,18 +79,30 @@ struct MatrixList {
     }
 };
 
-// The walk of a wave over its steps (steps st0, st0 + stride, ... of `steps`), for one tile
-// type; `src` says where each step's weights and outputs are.
+// The steps of one format group of a mixed launch, in the group's own numbering. A step past
+// the group's end reads its last step's rows, so it stays within matrices of the group's format.
+struct GroupSteps {
+    const MultiArgs &a;
+    int step0, steps;
+    __device__ __forceinline__ StepMat at(int st) const {
+        return MatrixList{a}.at(step0 + (st < steps ? st : steps - 1));
+    }
+};
+
+// The walk of a wave over its steps for one tile type: workgroup blk of the nblk that share
+// the `steps` steps takes steps st0, st0 + stride, ...; `src` says where each step's weights
+// and outputs are.
 template <class Tile, int V, int T, int NC, int MODE, class Steps>
-__device__ __forceinline__ void gemv_walk(const GemvArgs &a, const Steps &src, int steps) {
+__device__ __forceinline__ void gemv_walk(const GemvArgs &a, const Steps &src, int steps, int blk,
+                                          int nblk) {
     constexpr bool DBG = MODE == kModeDebug;
     constexpr bool FUSED = MODE == kModeFused;
     const LaneGeom<T, NC> L(a.nchunks);
     // the wave index is the same in all 64 lanes: keep it (and the step numbers) in SGPRs
     const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
     const int wpb = a.threads >> 6;
-    const int stride = gridDim.x * wpb;
-    const int st0 = blockIdx.x * wpb + wave;
+    const int stride = nblk * wpb;
+    const int st0 = blk * wpb + wave;
 
     typename Tile::Regs regs;
     uint32_t xw[V][NC][8];
@@ -135,7 +147,7 @@ __global__ void __launch_bounds__(64 * gemv_max_waves(V, T, NC)) gemv_kernel(Gem
     using Tile = typename F::template Tile<V, T, NC>;
     const int groups = (a.rows + Tile::RPW - 1) / Tile::RPW;
     const int steps = (groups + Tile::G - 1) / Tile::G;
-    gemv_walk<Tile, V, T, NC, MODE>(a, OneMatrix{a}, steps);
+    gemv_walk<Tile, V, T, NC, MODE>(a, OneMatrix{a}, steps, blockIdx.x, gridDim.x);
 }
 
 // Several matrices of this one format sharing the activation (qgemv_multi with a single
@@ -143,7 +155,8 @@ __global__ void __launch_bounds__(64 * gemv_max_waves(V, T, NC)) gemv_kernel(Gem
 // out before the activation slice is finished, as for one matrix.
 template <class F, int V, int T, int NC, int MODE>
 __global__ void __launch_bounds__(256) gemv_multi_fmt_kernel(MultiArgs a) {
-    gemv_walk<typename F::template Tile<V, T, NC>, V, T, NC, MODE>(a.act, MatrixList{a}, a.steps);
+    gemv_walk<typename F::template Tile<V, T, NC>, V, T, NC, MODE>(a.act, MatrixList{a}, a.steps,
+                                                                   blockIdx.x, gridDim.x);
 }
 
 // The launches of one format: tables over (vectors, lanes per row, chunks per lane) of the

@@ -70,11 +70,23 @@ struct MatDesc {
     int32_t wtype;         // kTypeQ4K, kTypeQ6K, kTypeQ40 or kTypeQ80
     int32_t step0;         // the matrix's first step in the launch's step numbering
 };
+// The matrices of one format in a launch: their steps are consecutive in the launch's
+// numbering, and a range of the grid's workgroups walks them (and only them).
+constexpr int kMaxFmtGroups = 4;
+struct FmtGroup {
+    int32_t wtype;
+    int32_t step0;         // the group's first step
+    int32_t steps;
+    int32_t block0;        // the group's first workgroup
+    int32_t blocks;
+};
 struct MultiArgs {
     GemvArgs act;          // the activation fields (xq, xd or x, xq_out, xd_out, nchunks)
     int32_t nmats;
     int32_t steps;         // steps of all matrices together
-    MatDesc m[kMaxMats];
+    MatDesc m[kMaxMats];   // ordered by format, so each format's steps are consecutive
+    int32_t ngroups;
+    FmtGroup g[kMaxFmtGroups];
 };
 
 struct LaunchShape {
