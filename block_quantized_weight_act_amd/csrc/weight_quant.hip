@@ -160,7 +160,9 @@ hipError_t launch_quantize_q6k(const float *w, uint8_t *out, int64_t rows, int64
 // holds weights 4l .. 4l + 3). w holds the rows' floats; block `local` of the launch is weights
 // 32 local .. 32 local + 31 of w and block blk0 + local of the tensor of ntotal blocks.
 
-// Q8_0: the activation rule on each block (quantize_act_quad: the same codes and scale).
+// Q8_0: the activation rule on each block (quantize_act_quad: the same codes and scale). Lanes
+// 0..3 of a block write its first 16 codes into the first codes plane, lanes 4..7 the other 16
+// into the second.
 __global__ void __launch_bounds__(256) quantize_q80_kernel(const float4 *__restrict__ w,
                                                            uint8_t *__restrict__ out,
                                                            int64_t nblocks, int64_t blk0,
@@ -172,7 +174,9 @@ __global__ void __launch_bounds__(256) quantize_q80_kernel(const float4 *__restr
     const ActQuad q = quantize_act_quad(v);
     if (valid) {
         const int64_t blk = blk0 + local;
-        *reinterpret_cast<uint32_t *>(out + 32 * blk + 4 * (gid & 7)) = q.codes;
+        const int l = static_cast<int>(gid & 7);
+        const int64_t at = l < 4 ? 16 * blk + 4 * l : 16 * ntotal + 16 * blk + 4 * (l - 4);
+        *reinterpret_cast<uint32_t *>(out + at) = q.codes;
         if ((gid & 7) == 0) *reinterpret_cast<float *>(out + 32 * ntotal + 4 * blk) = q.scale;
     }
 }

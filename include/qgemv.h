@@ -57,9 +57,10 @@
  *      (t >= 16) nibble of byte t mod 16
  *    d of block i: fp16 at 16 N + 2 i
  *    weight = d * (q - 8), q in [0, 15]
- *  Q8_0 tensor (36 bytes per block): codes plane [0, 32 N), scale plane
- *  [32 N, 36 N).
- *    codes of block i, at 32 i: weight t is the int8 at byte t
+ *  Q8_0 tensor (36 bytes per block): two codes planes [0, 16 N) and
+ *  [16 N, 32 N), scale plane [32 N, 36 N).
+ *    codes of block i: weight t < 16 is the int8 at byte 16 i + t, weight
+ *      t >= 16 the int8 at byte 16 N + 16 i + (t - 16)
  *    d of block i: float32 at 32 N + 4 i
  *    weight = d * q, q in [-127, 127]
  *

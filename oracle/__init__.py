@@ -15,8 +15,9 @@ Byte layouts (restated in the C file). N = rows * cols/256 super-blocks, block i
                  per block); one block's "body" is its low bits, high bits and scales (208 bytes).
   Q4_0 tensor  = codes plane (16 bytes per 32-weight block) then fp16 scale plane (2 bytes);
                  one block's "image" is its fp16 d followed by its 16 code bytes.
-  Q8_0 tensor  = codes plane (32 int8 per block) then float32 scale plane (4 bytes); the
-                 image is d followed by the 32 codes.
+  Q8_0 tensor  = two codes planes (int8 codes 0..15, then codes 16..31 of each block, 16
+                 bytes per block each) then float32 scale plane (4 bytes); the image is d
+                 followed by the 32 codes.
   activations  = int8 codes [nvec][cols] and float32 scales [nvec][cols/32].
 """
 
@@ -454,16 +455,30 @@ def bruteforce(what, xq, xd, lib=None) -> np.ndarray:
 
 def planes(wtype: str, wbuf, rows: int, cols: int) -> list:
     """The planes of a tensor as [rows][bytes per row] views (Q4_K: codes, headers; Q6_K: low
-    bits, high bits, scales, d; Q4_0 and Q8_0: codes, scales)."""
+    bits, high bits, scales, d; Q4_0: codes, scales; Q8_0: codes 0..15 of each block, codes
+    16..31, scales)."""
     nb = cols // (QB if wtype in ("q40", "q80") else QK)
     n = rows * nb
     wbuf = np.ascontiguousarray(wbuf, dtype=np.uint8).reshape(-1)
-    widths = {"q4k": [128, 16], "q6k": [128, 64, 16, 2], "q40": [16, 2], "q80": [32, 4]}[wtype]
+    widths = {"q4k": [128, 16], "q6k": [128, 64, 16, 2], "q40": [16, 2], "q80": [16, 16, 4]}[wtype]
     out, off = [], 0
     for wdt in widths:
         out.append(wbuf[off:off + n * wdt].reshape(rows, nb * wdt))
         off += n * wdt
     return out
+
+
+def q80_codes(wbuf, rows: int, cols: int) -> np.ndarray:
+    """The int8 codes of a Q8_0 tensor as [rows][cols], from its two codes planes."""
+    lo, hi, _ = planes("q80", wbuf, rows, cols)
+    n = rows * (cols // QB)
+    return np.concatenate([lo.reshape(n, 16), hi.reshape(n, 16)], axis=1).reshape(
+        rows, cols).view(np.int8)
+
+
+def q80_scales(wbuf, rows: int, cols: int) -> np.ndarray:
+    """The float32 scales of a Q8_0 tensor as [rows][cols/32]."""
+    return planes("q80", wbuf, rows, cols)[2].copy().view(np.float32)
 
 
 def from_planes(parts) -> np.ndarray:

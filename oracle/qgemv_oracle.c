@@ -295,7 +295,8 @@ void orc_q6k_put_block(uint8_t *t, int64_t nblocks, int64_t i, const uint8_t *bo
  * Q8_0: a block of 32 weights with one float32 scale d and int8 codes q_t;
  * dequantized weight d * q_t. Its 36-byte image: d (float32, little-endian) at
  * [0,4), then weight t's code at byte 4 + t. A Q8_0 tensor of N blocks keeps
- * the codes of block i at 32 * i and its d at 32 * N + 4 * i.                 */
+ * the codes of weights 0..15 of block i at 16 * i, those of weights 16..31 at
+ * 16 * N + 16 * i, and its d at 32 * N + 4 * i.                                */
 #define Q40_BYTES 18
 #define Q80_BYTES 36
 
@@ -351,11 +352,13 @@ static void q40_put(uint8_t *t, int64_t N, int64_t i, const uint8_t *img) {
 }
 static void q80_get(const uint8_t *t, int64_t N, int64_t i, uint8_t *img) {
     memcpy(img, t + 32 * N + 4 * i, 4);
-    memcpy(img + 4, t + 32 * i, 32);
+    memcpy(img + 4, t + 16 * i, 16);
+    memcpy(img + 20, t + 16 * N + 16 * i, 16);
 }
 static void q80_put(uint8_t *t, int64_t N, int64_t i, const uint8_t *img) {
     memcpy(t + 32 * N + 4 * i, img, 4);
-    memcpy(t + 32 * i, img + 4, 32);
+    memcpy(t + 16 * i, img + 4, 16);
+    memcpy(t + 16 * N + 16 * i, img + 20, 16);
 }
 
 void orc_q40_get_block(const uint8_t *t, int64_t nblocks, int64_t i, uint8_t *img) {

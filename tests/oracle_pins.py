@@ -380,8 +380,8 @@ def check_q80_quantizer(lib, w):
     buf = oracle.quantize_q80(w, lib=lib)
     n = rows * cols // 32
     xq, xd = oracle.quantize_act(w.reshape(1, -1), lib=lib)
-    codes = oracle.planes("q80", buf, rows, cols)[0].reshape(-1).view(np.int8)
-    scales = oracle.planes("q80", buf, rows, cols)[1].reshape(-1).copy().view(np.float32)
+    codes = oracle.q80_codes(buf, rows, cols).reshape(-1)
+    scales = oracle.q80_scales(buf, rows, cols).reshape(-1)
     assert np.array_equal(codes, xq.reshape(-1))
     assert np.array_equal(scales.view(np.uint32), xd.reshape(-1).view(np.uint32))
     what = oracle.dequantize("q80", buf, rows, cols, lib=lib).reshape(n, 32)

@@ -124,7 +124,7 @@ checks = {{
     "q40_quantizer": lambda: (pins.check_q40_quantizer(lib, w), pins.check_q40_quantizer(lib, w3)),
     "q80_quantizer": lambda: (pins.check_q80_quantizer(lib, w), pins.check_q80_quantizer(lib, w3)),
     "q80_act_cases": lambda: [np.testing.assert_array_equal(
-        oracle.planes("q80", oracle.quantize_q80(xc[None, :], lib=lib), 1, xc.size)[0].reshape(-1).view(np.int8), qc)
+        oracle.q80_codes(oracle.quantize_q80(xc[None, :], lib=lib), 1, xc.size).reshape(-1), qc)
         for xc, qc, _ in pins.read_act_cases()],
     "bf_q40": lambda: pins.check_gemv_bruteforce(lib, "q40", w, x),
     "bf_q80": lambda: pins.check_gemv_bruteforce(lib, "q80", w, x),

@@ -87,9 +87,9 @@ def test_q80_quantizer_hand_worked_blocks(orc):
     x / xd) give the same codes and scales when quantized as Q8_0 weights."""
     for x, q, xd in pins.read_act_cases():
         buf = oracle.quantize_q80(x[None, :], lib=orc)
-        codes, scales = oracle.planes("q80", buf, 1, x.size)
-        assert np.array_equal(codes.reshape(-1).view(np.int8), q)
-        assert scales.reshape(-1).copy().view(np.float32)[0].view(np.uint32) == np.float32(xd).view(np.uint32)
+        codes, scales = oracle.q80_codes(buf, 1, x.size), oracle.q80_scales(buf, 1, x.size)
+        assert np.array_equal(codes.reshape(-1), q)
+        assert scales.reshape(-1)[0].view(np.uint32) == np.float32(xd).view(np.uint32)
 
 
 @pytest.mark.parametrize("wtype", ["q4k", "q6k", "q40", "q80"])
