@@ -778,16 +778,23 @@ int qgemv_fused_launches(int wtype, int64_t rows, int64_t cols, int32_t nvec, in
     // the split's activation itself.
     if (i8_auto(wtype, rows, cols, nvec)) return 2;
     // Every workgroup of the fused kernel quantizes the whole activation slice its lanes read,
-    // groups of 4 elements spread over its lanes. Past 4 groups per lane (wide rows, several
-    // vectors) that costs more than a second launch (~1.9 us): then, if the caller gave places
-    // for the codes, the library quantizes once into them and runs the product from them.
-    // Both forms give the same codes and the same y. Measured on MI355X, one launch against
-    // two: 1536 x 6144 (3 groups per lane) 3.9 / 5.4 us, 8192 x 2048 x 4 vectors (4) 6.6 /
-    // 7.1 us, 2048 x 8192 Q6_K x 2 vectors (8) 8.1 / 7.2 us.
+    // groups of 4 elements spread over its lanes. That costs more than a second launch (~1.9
+    // us) past 4 groups per lane (wide rows, several vectors), or when the workgroups together
+    // repeat it for more than 12K elements per CU while the slice is over a tenth of a
+    // workgroup's share of the weight bytes (many workgroups on a wide row that is not long
+    // enough to hide it): then, if the caller gave places for the codes, the library quantizes
+    // once into them and runs the product from them. Both forms give the same codes and the
+    // same y. Measured on MI355X, one launch against two: 1536 x 6144 (3 groups per lane, 4.6K
+    // elements per CU) 3.9 / 5.4 us; 8192 x 2048 x 4 vectors (4, 8.2K) 6.6 / 7.1 us;
+    // 2048 x 8192 Q6_K x 2 vectors (8) 8.1 / 7.2 us; 4096 x 16384 (4, 33K, slice 0.22 of the
+    // share) 13.9 / 13.0 us; 262144 x 1536 (1.5, 25K, slice 0.03 of the share) 34.7 / 36.7 us.
     const qgemv_plan plan = make_plan(wtype, rows, cols, nvec);
-    const int64_t quads = static_cast<int64_t>(nvec) * plan.lanes_per_row * plan.chunks_per_lane * 8;
+    const int64_t slice = static_cast<int64_t>(nvec) * plan.lanes_per_row * plan.chunks_per_lane * 32;
     const int64_t lanes = 64 * static_cast<int64_t>(plan.waves_per_block);
-    return (quads + lanes - 1) / lanes > 4 ? 2 : 1;
+    if ((slice / 4 + lanes - 1) / lanes > 4) return 2;
+    const double wgs = static_cast<double>(plan.blocks) * plan.splits;
+    const double share = static_cast<double>(weight_bytes(wtype, rows, cols)) / wgs;
+    return wgs * static_cast<double>(slice) / 256.0 > 12288.0 && slice > 0.1 * share ? 2 : 1;
 }
 
 int qgemv_fused(int wtype, const void *w, const float *x, int8_t *xq_out, float *xd_out, float *y,

@@ -184,6 +184,9 @@ WORKLOADS = {
     "q4k_262144x1536_b64": Workload("q4k_262144x1536_b64", "q4k", 262144, 1536, 64, 1003, 3100,
                                     outlier_frac=0.01, seed_rows=3003),
     "q4k_16384x2048_b64": Workload("q4k_16384x2048_b64", "q4k", 16384, 2048, 64, 1004, 3400),
+    # a row wider than one pass of 256 chunks (16384 columns = 512 chunks): the column split
+    # with its ordered second pass (weight seed 1007)
+    "q4k_4096x16384": Workload("q4k_4096x16384", "q4k", 4096, 16384, 1, 1007, 2900),
 }
 
 

@@ -23,7 +23,7 @@ def _rows(wl, n):
 @pytest.mark.parametrize("name,n", [("q4k_512x512", 512), ("q4k_8192x2048", 48),
                                     ("q6k_2048x8192", 16), ("q4k_262144x1536", 64),
                                     ("q4k_16384x2048_b8", 24), ("q40_262144x1536", 64),
-                                    ("q80_262144x1536", 64)])
+                                    ("q80_262144x1536", 64), ("q4k_4096x16384", 16)])
 def test_workload_gemv_vs_bruteforce(orc, name, n):
     wl = synth.WORKLOADS[name]
     rows = _rows(wl, n)
