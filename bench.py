@@ -127,11 +127,16 @@ def algorithmic_bytes(wl, wbytes: int) -> dict:
 def roofline_kernel(wtype: str, plan: dict, nvec: int, launches: int, route: str = "vector") -> str:
     """The step's dominant kernel, as its template instance appears in kernel traces: the
     one-launch fused kernel (form 2) when qgemv_fused makes one launch for this shape, else the
-    GEMV kernel of the two-launch route (form 0, codes read from memory); on the integer
-    matrix-core route the product kernel of that route."""
+    GEMV kernel of the two-launch route (form 0, codes read from memory; for a plan with
+    column splits the kernel that splits inside the workgroup); on the integer matrix-core
+    route the product kernel of that route."""
     if route == "i8mc":
         return "gemm_q4k_i8_kernel<%d, %d>" % (2 if launches == 1 else 0, (nvec + 7) // 8)
     tag = {"q4k": "Q4K", "q6k": "Q6K", "q40": "Q40", "q80": "Q80"}[wtype]
+    if launches != 1 and plan["splits"] > 1:
+        # the unfused product of a split plan: the column split inside the workgroup
+        return "gemv_split_kernel<qgemv::%s, %d, %d, %d>" % (tag, nvec, plan["lanes_per_row"],
+                                                           plan["chunks_per_lane"])
     return "gemv_kernel<qgemv::%s, %d, %d, %d, %d>" % (tag, nvec, plan["lanes_per_row"],
                                                        plan["chunks_per_lane"],
                                                        2 if launches == 1 else 0)

@@ -71,6 +71,17 @@ bool shape_ok_t(int wtype, int64_t rows, int64_t cols, int32_t nvec) {
     return type_ok(wtype) && shape_ok(rows, cols, nvec) && cols % block_cols(wtype) == 0;
 }
 
+hipError_t launch_gemv_split(int wtype, const GemvArgs &a, const LaunchShape &s, int nvec,
+                             hipStream_t stream) {
+    switch (wtype) {
+        case QGEMV_Q4K: return launch_gemv_split_q4k(a, s, nvec, stream);
+        case QGEMV_Q6K: return launch_gemv_split_q6k(a, s, nvec, stream);
+        case QGEMV_Q4_0: return launch_gemv_split_q40(a, s, nvec, stream);
+        case QGEMV_Q8_0: return launch_gemv_split_q80(a, s, nvec, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
 hipError_t launch_gemv(int wtype, const GemvArgs &a, const LaunchShape &s, int nvec, bool debug,
                        hipStream_t stream) {
     switch (wtype) {
@@ -262,10 +273,27 @@ int run_gemv(int wtype, const void *w, const Activation &act, float *y, int64_t 
     a.x = act.x;
     a.xq_out = act.xq_out;
     a.xd_out = act.xd_out;
-    a.out = need > 0 ? static_cast<float *>(ws) : y;
     a.rows = static_cast<int32_t>(rows);
     a.nb = static_cast<int32_t>(cols / block_cols(wtype));
     a.nchunks = static_cast<int32_t>(cols / 32);
+    // The unfused form with column splits: the splits inside the workgroup (its waves in sets
+    // of `splits`, their row sums added in LDS in chunk order), one launch and the same y bit
+    // for bit as the split-K reduce, with as many waves in all as the plan's two-pass form.
+    // The workspace is still required (the ABI's contract is per shape), though not touched.
+    const int maxw = gemv_max_waves(nvec, plan.lanes_per_row, plan.chunks_per_lane);
+    if (need > 0 && !act.x && plan.splits <= maxw) {
+        const int wpb = plan.waves_per_block % plan.splits == 0
+                            ? plan.waves_per_block
+                            : plan.splits * (maxw / plan.splits);
+        const int64_t waves = static_cast<int64_t>(plan.blocks) * plan.splits * plan.waves_per_block;
+        const int64_t blocks = std::min<int64_t>((waves + wpb - 1) / wpb, int64_t{65535} * 64);
+        a.out = y;
+        const LaunchShape s{plan.lanes_per_row, plan.chunks_per_lane, wpb,
+                            static_cast<int>(blocks), plan.splits};
+        const hipError_t e = launch_gemv_split(wtype, a, s, nvec, stream);
+        return e == hipSuccess ? QGEMV_OK : hip_fail(e);
+    }
+    a.out = need > 0 ? static_cast<float *>(ws) : y;
     LaunchShape s{plan.lanes_per_row, plan.chunks_per_lane, plan.waves_per_block, plan.blocks,
                   plan.splits};
     hipError_t e = launch_gemv(wtype, a, s, nvec, false, stream);

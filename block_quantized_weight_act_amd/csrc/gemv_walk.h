@@ -159,6 +159,61 @@ __global__ void __launch_bounds__(256) gemv_multi_fmt_kernel(MultiArgs a) {
                                                                    blockIdx.x, gridDim.x);
 }
 
+// The column split inside the workgroup (the unfused form of a plan with splits > 1): the
+// workgroup's waves come in sets of `ws` = the plan's column chunks, wave w taking chunk w % ws
+// of row step `slot` = w / ws of each workgroup step. After a step the row sums of the chunks
+// (stored by the tiles as for the split-K workspace, here into LDS) are added in chunk order,
+// the order of the split-K reduce, so y is bit-identical to the two-launch split in one launch.
+// Every wave of a workgroup runs the same number of workgroup steps (the barriers), and the
+// next step's loads go out before the sums over the chunks.
+template <class F, int V, int T, int NC>
+__global__ void __launch_bounds__(64 * gemv_max_waves(V, T, NC)) gemv_split_kernel(GemvArgs a) {
+    using Tile = typename F::template Tile<V, T, NC>;
+    constexpr int kStepRows = Tile::G * Tile::RPW;
+    extern __shared__ float part[];                  // [ws][V][rows_local]
+    const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+    const int ws = a.wg_splits;
+    const int slots = (a.threads >> 6) / ws;
+    const int split = wave % ws, slot = wave / ws;
+    const LaneGeom<T, NC> L(a.nchunks, split);
+    const int groups = (a.rows + Tile::RPW - 1) / Tile::RPW;
+    const int steps = (groups + Tile::G - 1) / Tile::G;
+    const int wg_steps = (steps + slots - 1) / slots;
+    const int rows_local = slots * kStepRows;
+
+    typename Tile::Regs regs;
+    uint32_t xw[V][NC][8];
+    float xs[V][NC];
+    ActTerms<V, NC> at;
+    ActPending<V, T, NC, false> pend;
+    act_slice_issue<V, T, NC, false>(a, L.g, L.cv, xw, xs, pend);
+    int wst = static_cast<int>(blockIdx.x);
+    __builtin_amdgcn_sched_barrier(0);
+    Tile::issue(regs, a.w, a.rows, a.nb, wst * slots + slot, L);   // rows clamped
+    __builtin_amdgcn_sched_barrier(0);
+    act_terms<V, NC>(xw, at);
+    const int stride = static_cast<int>(gridDim.x);
+    for (; wst < wg_steps; wst += stride) {
+        __builtin_amdgcn_sched_barrier(0);
+        // the workgroup-local rows: every local row is stored (rows past the matrix are
+        // dropped below)
+        Tile::template compute<false>(regs, xw, xs, at, part, rows_local, slot, L, nullptr,
+                                      a.nchunks);
+        __builtin_amdgcn_sched_barrier(0);
+        if (wst + stride < wg_steps)
+            Tile::issue(regs, a.w, a.rows, a.nb, (wst + stride) * slots + slot, L);
+        __syncthreads();
+        for (int i = static_cast<int>(threadIdx.x); i < V * rows_local; i += a.threads) {
+            const int v = i / rows_local, rl = i - v * rows_local;
+            const int row = wst * rows_local + rl;
+            float acc = part[v * rows_local + rl];
+            for (int s = 1; s < ws; s++) acc += part[(s * V + v) * rows_local + rl];
+            if (row < a.rows) a.out[static_cast<int64_t>(v) * a.rows + row] = acc;
+        }
+        __syncthreads();
+    }
+}
+
 // The launches of one format: tables over (vectors, lanes per row, chunks per lane) of the
 // compiled instances (nvec * chunks <= 8, so the activation slice fits in VGPRs), one for the
 // one-matrix kernel and one for several matrices of this format.
@@ -205,6 +260,25 @@ struct GemvLaunch {
             else
                 hipLaunchKernelGGL((gemv_multi_fmt_kernel<F, V, T, NC, kModePlain>), grid, block,
                                    0, stream, b);
+            return hipGetLastError();
+        }
+    };
+
+    struct Split {
+        using Args = GemvArgs;
+        template <int V, int T, int NC>
+        static hipError_t run(const GemvArgs &a, const LaunchShape &s, bool debug,
+                              hipStream_t stream) {
+            using Tile = typename F::template Tile<V, T, NC>;
+            if (debug || a.x != nullptr || s.splits < 2 || s.waves % s.splits != 0 ||
+                s.waves > gemv_max_waves(V, T, NC))
+                return hipErrorInvalidValue;
+            const size_t lds = sizeof(float) * static_cast<size_t>(V) * s.waves * Tile::G * Tile::RPW;
+            GemvArgs b = a;
+            b.threads = 64 * s.waves;
+            b.wg_splits = s.splits;
+            hipLaunchKernelGGL((gemv_split_kernel<F, V, T, NC>), dim3(static_cast<unsigned>(s.blocks)),
+                               dim3(static_cast<unsigned>(64 * s.waves)), lds, stream, b);
             return hipGetLastError();
         }
     };
@@ -269,6 +343,11 @@ struct GemvLaunch {
     static hipError_t launch_multi(const MultiArgs &a, const LaunchShape &s, int nvec,
                                    hipStream_t stream) {
         return dispatch<Multi>(a, s, nvec, false, stream);
+    }
+    // s.splits = column chunks (the waves' sets), s.waves a multiple of it, s.blocks workgroups
+    static hipError_t launch_split(const GemvArgs &a, const LaunchShape &s, int nvec,
+                                   hipStream_t stream) {
+        return dispatch<Split>(a, s, nvec, false, stream);
     }
 };
 

@@ -47,6 +47,7 @@ struct GemvArgs {
     int32_t threads;       // threads per workgroup of the launch, set by the launcher (the
                            // kernels use it instead of blockDim, which the compiler may read
                            // with a vector load and a wait at the kernel's start)
+    int32_t wg_splits;     // column chunks split inside the workgroup (gemv_split_kernel)
 };
 
 // Kernel forms, a template parameter so that each has its own name in kernel traces:
@@ -119,6 +120,16 @@ hipError_t launch_gemv_multi_q6k(const MultiArgs &a, const LaunchShape &s, int n
 hipError_t launch_gemv_multi_q40(const MultiArgs &a, const LaunchShape &s, int nvec,
                                  hipStream_t stream);
 hipError_t launch_gemv_multi_q80(const MultiArgs &a, const LaunchShape &s, int nvec,
+                                 hipStream_t stream);
+// The unfused product of a plan with column splits, the splits inside the workgroup
+// (gemv_split_kernel in gemv_walk.h): s.splits chunks, s.waves a multiple of it
+hipError_t launch_gemv_split_q4k(const GemvArgs &a, const LaunchShape &s, int nvec,
+                                 hipStream_t stream);
+hipError_t launch_gemv_split_q6k(const GemvArgs &a, const LaunchShape &s, int nvec,
+                                 hipStream_t stream);
+hipError_t launch_gemv_split_q40(const GemvArgs &a, const LaunchShape &s, int nvec,
+                                 hipStream_t stream);
+hipError_t launch_gemv_split_q80(const GemvArgs &a, const LaunchShape &s, int nvec,
                                  hipStream_t stream);
 hipError_t launch_splitk_reduce(const float *part, float *y, int64_t n, int splits,
                                 hipStream_t stream);

@@ -28,11 +28,13 @@ struct LaneGeom {
     bool cv[NC];
     uint32_t blk[NC];
 
-    __device__ __forceinline__ explicit LaneGeom(int nsub) {
+    // the lane's column chunk `split` (blockIdx.y unless given)
+    __device__ __forceinline__ explicit LaneGeom(int nsub) : LaneGeom(nsub, blockIdx.y) {}
+    __device__ __forceinline__ LaneGeom(int nsub, int split_) {
         lane = threadIdx.x & 63;
         t = lane & (T - 1);
         rsub = lane / T;
-        split = blockIdx.y;
+        split = split_;
         j = t & 7;                           // chunk inside the super-block
 #pragma unroll
         for (int k = 0; k < NC; k++) {

@@ -148,10 +148,14 @@ int qgemv_quantize_act(const float *x, int8_t *xq, float *xd, int64_t cols, int3
 /*
  * Workspace needed by qgemv_q4k / qgemv_q6k / qgemv_batch for this shape, in
  * bytes; 0 when the chosen plan does not split the columns. The planner splits
- * the columns into S chunks of whole super-blocks when rows alone cannot fill
- * the GPU; the workspace then holds S partial results per output, summed in
- * a second pass in ascending chunk order (no atomics; genie-ai-runtime
- * "v1.3.0": split-K with a separate reduce, chosen per shape).
+ * the columns into S chunks of whole blocks when a row is wider than one pass
+ * or rows alone cannot fill the GPU (genie-ai-runtime "v1.3.0": split-K, chosen
+ * per shape). The S partial results per output are always added in ascending
+ * chunk order, without atomics: from codes (S no larger than a workgroup's
+ * waves) by the waves of one workgroup, through LDS, in the same launch;
+ * otherwise (the one-launch fused form, larger S) through the workspace and a
+ * second launch. The two give the same y bit for bit; the workspace is
+ * required whenever this returns more than 0.
  */
 size_t qgemv_workspace_bytes(int wtype, int64_t rows, int64_t cols, int32_t nvec);
 
@@ -413,7 +417,7 @@ int qgemv_quantize_weights_rows(int wtype, const float *w, void *out, int64_t ro
  * lanes_per_row lanes of a 64-lane wavefront shares a row, each lane taking
  * chunks_per_lane chunks, so one pass covers lanes_per_row * chunks_per_lane
  * chunks and the row is split into ceil(cols/32 / that) column chunks
- * ("splits"; > 1 needs a workspace and a second pass). waves_per_block
+ * ("splits"; > 1 needs a workspace, see qgemv_workspace_bytes). waves_per_block
  * wavefronts form a workgroup; blocks is the number of workgroups per column
  * chunk, each looping over row groups.
  */

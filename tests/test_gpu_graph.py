@@ -38,8 +38,9 @@ SMALL = synth.decode_step(
 
 class Step:
     """Device buffers of one decode step and the library calls that make it. The down
-    projections run from codes with a forced column split (quantization, product, reduction:
-    three launches over a shared workspace); the head is fused with code outputs."""
+    projections run from codes with a forced three-way column split (quantization, then the
+    product with the split inside the workgroup: two launches, the workspace shared); the head
+    is fused with code outputs."""
 
     def __init__(self, step):
         import torch
@@ -69,7 +70,7 @@ class Step:
                 need = qg.qgemv_plan_workspace_bytes(plan, p.rows, cols, nvec)
                 assert need > 0
                 ws_bytes = max(ws_bytes, need)
-                self.launches += 3
+                self.launches += 2
             else:
                 outs = p is step.head
                 if outs:
