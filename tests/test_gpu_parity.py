@@ -323,3 +323,35 @@ def test_fused_quantize_and_gemv(wtype, rows, cols, nvec):
     y2 = torch.full_like(y, float("nan"))
     qg.qgemv_fused(wtype, w, xt, y2, rows, cols, nvec, workspace=ws)      # without code outputs
     assert np.array_equal(gu.host(y2).view(np.uint32), y_two.view(np.uint32))
+
+
+@pytest.mark.parametrize("wtype", ALL)
+@pytest.mark.parametrize("rows,cols,nvec", [(37, 16384, 1), (200, 12288, 2), (91, 8192, 3),
+                                            (64, 4096, 5), (19, 4096, 8)])
+def test_split_inside_workgroup_matches_two_pass(wtype, rows, cols, nvec):
+    """Rows wider than one pass: from codes the column split runs inside the workgroup (the
+    chunks' sums added in LDS), while the one-launch fused form without code outputs writes
+    them to the workspace and adds them in a second launch. Both add the chunks in ascending
+    order, so y must agree bit for bit, and lie within the oracle's bound."""
+    import torch
+    import block_quantized_weight_act_amd as qg
+    _say("split-in-workgroup", wtype, rows, cols, nvec)
+    plan = qg.qgemv_plan_for(wtype, rows, cols, nvec)
+    assert plan["lanes_per_row"] == 64 and plan["splits"] == 2, plan   # 3+ vectors: reduce-scatter
+    assert qg.qgemv_route(wtype, rows, cols, nvec) == "vector"
+    rng = np.random.default_rng(rows + cols + nvec)
+    w = (rng.standard_normal((rows, cols)) * 0.02).astype(np.float32)
+    x = rng.standard_normal((nvec, cols)).astype(np.float32)
+    wbuf = _quant(wtype, w)
+    wd = gu.dev(wbuf)
+    xq, xd = gu.quantize_act(x)
+    nbytes = qg.qgemv_workspace_bytes(wtype, rows, cols, nvec)
+    ws = torch.full((nbytes,), 0xFF, dtype=torch.uint8, device=gu.DEV)
+    y_in = torch.full((nvec, rows), float("nan"), dtype=torch.float32, device=gu.DEV)
+    qg.qgemv_batch(wtype, wd, xq, xd, y_in, rows, cols, nvec, workspace=ws)
+    y_two = torch.full_like(y_in, float("nan"))
+    qg.qgemv_fused(wtype, wd, gu.dev(x), y_two, rows, cols, nvec, workspace=ws)
+    a, b = gu.host(y_in), gu.host(y_two)
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    rq, rd = oracle.quantize_act(x)
+    gu.assert_within_bound(a, oracle.gemv(wtype, wbuf, rows, cols, rq, rd))
