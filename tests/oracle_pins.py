@@ -153,6 +153,63 @@ def check_layout_goldens(lib):
     assert np.array_equal(oracle.dequantize("q6k", tensor, 1, 256, lib=lib)[0], want)
 
 
+def check_qk_tensor_goldens(lib):
+    """Q4_K and Q6_K planar tensors of two blocks, against hand-derived bytes.
+
+    The writer (block images -> tensor) must produce the fixture's bytes, the reader
+    (tensor -> block image) must recover each block from them, and the dequantizer must
+    read the fixture tensor, as one row of two blocks and as two rows of one block, into
+    the closed-form weights. This pins the order and offsets of every plane.
+    """
+    pt, data = read_hex_fixture("qk_tensors.txt")
+    n4 = int(pt["q4k_bytes"])
+    want4, want6 = data[:n4], data[n4:]
+    assert want4.size == 2 * 144 and want6.size == 2 * 210
+    i = np.arange(256)
+    j32 = i // 32
+
+    # Q4_K: block 0 = fixture A, block 1 as stated in the fixture's header comment
+    _, img0 = read_hex_fixture("q4k_block_a.txt")
+    img1 = np.array([0x00, 0x40, 0x00, 0x34, 0x11, 0x11, 0x11, 0x11, 0x22, 0x22, 0x22, 0x22,
+                     0xAA, 0xAA, 0x00, 0x00] + [0xC3] * 128, np.uint8)
+    q1 = np.where(i % 32 < 16, 3, 12).astype(np.uint8)
+    assert np.array_equal(
+        oracle.q4k_pack_block(0x4000, 0x3400, np.full(8, 33, np.uint8), np.full(8, 2, np.uint8),
+                              q1, lib=lib), img1)
+    t4 = oracle.q4k_tensor([img0, img1], lib=lib)
+    assert np.array_equal(t4, want4)
+    assert np.array_equal(oracle.q4k_get_block(want4, 2, 0, lib=lib), img0)
+    assert np.array_equal(oracle.q4k_get_block(want4, 2, 1, lib=lib), img1)
+    p0 = read_hex_fixture("q4k_block_a.txt")[0]
+    _, _, sc0, m0, qa = _q4k_params(p0)
+    w0 = 1.0 * sc0[j32].astype(np.float64) * qa - 0.5 * m0[j32].astype(np.float64)
+    w1 = np.where(i % 32 < 16, 197.5, 791.5)
+    got = oracle.dequantize("q4k", want4, 1, 512, lib=lib)[0]
+    assert np.array_equal(got, np.concatenate([w0, w1]))
+    got2 = oracle.dequantize("q4k", want4, 2, 256, lib=lib)
+    assert np.array_equal(got2[0], w0) and np.array_equal(got2[1], w1)
+
+    # Q6_K: block 0 = fixture A with d = 0.25, block 1 as stated in the fixture's comment
+    _, body0 = read_hex_fixture("q6k_block_a.txt")
+    sc1 = (np.arange(16) - 4).astype(np.int8)
+    body1 = np.concatenate([np.full(128, 0xDD, np.uint8), np.full(64, 0xAA, np.uint8),
+                            sc1.view(np.uint8)])
+    assert np.array_equal(oracle.q6k_pack_block(sc1, np.full(256, 45, np.uint8), lib=lib), body1)
+    t6 = oracle.q6k_tensor([body0, body1], [0x3400, 0x3800], lib=lib)
+    assert np.array_equal(t6, want6)
+    b0, d0 = oracle.q6k_get_block(want6, 2, 0, lib=lib)
+    b1, d1 = oracle.q6k_get_block(want6, 2, 1, lib=lib)
+    assert np.array_equal(b0, body0) and d0 == 0x3400
+    assert np.array_equal(b1, body1) and d1 == 0x3800
+    sc0 = np.array([3 * (j - 8) for j in range(16)], np.float64)
+    v0 = 0.25 * sc0[i // 16] * ((i % 64) - 32.0)
+    v1 = 6.5 * (i // 16 - 4.0)
+    got = oracle.dequantize("q6k", want6, 1, 512, lib=lib)[0]
+    assert np.array_equal(got, np.concatenate([v0, v1]))
+    got2 = oracle.dequantize("q6k", want6, 2, 256, lib=lib)
+    assert np.array_equal(got2[0], v0) and np.array_equal(got2[1], v1)
+
+
 def check_layout_probes(lib):
     for fmt, byte, shift, width, name, idx, value in read_probes():
         size = {"q4k": 144, "q6k": 208, "q40": 18, "q80": 36}[fmt]

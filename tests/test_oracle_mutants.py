@@ -88,6 +88,35 @@ MUTANTS = {
     "q80_quant_divide": (
         "for (int t = 0; t < QB; t++) q[t] = (int8_t)clampf(rintf(wb[t] * id), -127.0f, 127.0f);",
         "for (int t = 0; t < QB; t++) q[t] = (int8_t)clampf(d > 0.0f ? rintf(wb[t] / d) : 0.0f, -127.0f, 127.0f);"),
+    # plane order and plane offsets of the Q4_K / Q6_K tensors: a mutant that moves a plane
+    # in both the reader and the writer stays self-consistent, so only fixed bytes catch it
+    "q4k_header_plane_first": [
+        ("memcpy(img, t + 128 * N + 16 * i, 16);\n    memcpy(img + 16, t + 128 * i, 128);",
+         "memcpy(img, t + 16 * i, 16);\n    memcpy(img + 16, t + 16 * N + 128 * i, 128);"),
+        ("memcpy(t + 128 * N + 16 * i, img, 16);\n    memcpy(t + 128 * i, img + 16, 128);",
+         "memcpy(t + 16 * i, img, 16);\n    memcpy(t + 16 * N + 128 * i, img + 16, 128);")],
+    "q4k_header_index_read": (
+        "memcpy(img, t + 128 * N + 16 * i, 16);",
+        "memcpy(img, t + 128 * N + 16 * (N - 1 - i), 16);"),
+    "q4k_header_index_both": [
+        ("memcpy(img, t + 128 * N + 16 * i, 16);", "memcpy(img, t + 128 * N + 16 * (N - 1 - i), 16);"),
+        ("memcpy(t + 128 * N + 16 * i, img, 16);", "memcpy(t + 128 * N + 16 * (N - 1 - i), img, 16);")],
+    "q6k_high_and_scale_planes_swapped": [
+        ("memcpy(body + 128, t + 128 * N + 64 * i, 64);\n    memcpy(body + 192, t + 192 * N + 16 * i, 16);",
+         "memcpy(body + 128, t + 144 * N + 64 * i, 64);\n    memcpy(body + 192, t + 128 * N + 16 * i, 16);"),
+        ("memcpy(t + 128 * N + 64 * i, body + 128, 64);\n    memcpy(t + 192 * N + 16 * i, body + 192, 16);",
+         "memcpy(t + 144 * N + 64 * i, body + 128, 64);\n    memcpy(t + 128 * N + 16 * i, body + 192, 16);")],
+    "q6k_d_plane_index_both": [
+        ("*d = rd16(t + 208 * N + 2 * i);", "*d = rd16(t + 208 * N + 2 * (N - 1 - i));"),
+        ("wr16(t + 208 * N + 2 * i, d);", "wr16(t + 208 * N + 2 * (N - 1 - i), d);")],
+    "q6k_high_plane_index_both": [
+        ("memcpy(body + 128, t + 128 * N + 64 * i, 64);", "memcpy(body + 128, t + 128 * N + 64 * (N - 1 - i), 64);"),
+        ("memcpy(t + 128 * N + 64 * i, body + 128, 64);", "memcpy(t + 128 * N + 64 * (N - 1 - i), body + 128, 64);")],
+    "q6k_d_before_scales": [
+        ("memcpy(body + 192, t + 192 * N + 16 * i, 16);\n    *d = rd16(t + 208 * N + 2 * i);",
+         "memcpy(body + 192, t + 194 * N + 16 * i, 16);\n    *d = rd16(t + 192 * N + 2 * i);"),
+        ("memcpy(t + 192 * N + 16 * i, body + 192, 16);\n    wr16(t + 208 * N + 2 * i, d);",
+         "memcpy(t + 194 * N + 16 * i, body + 192, 16);\n    wr16(t + 192 * N + 2 * i, d);")],
     "bound_drops_min": (
         "double wh = d * sc * q4k_q(blk, 32 * j + i) - dmin * m;",
         "double wh = d * sc * q4k_q(blk, 32 * j + i);"),
@@ -121,6 +150,7 @@ checks = {{
     "special": lambda: pins.check_gemv_special(lib),
     "extremes": lambda: pins.check_gemv_extremes(lib),
     "q32_layout": lambda: pins.check_q32_layout_goldens(lib),
+    "qk_tensors": lambda: pins.check_qk_tensor_goldens(lib),
     "q40_quantizer": lambda: (pins.check_q40_quantizer(lib, w), pins.check_q40_quantizer(lib, w3)),
     "q80_quantizer": lambda: (pins.check_q80_quantizer(lib, w), pins.check_q80_quantizer(lib, w3)),
     "q80_act_cases": lambda: [np.testing.assert_array_equal(
@@ -164,7 +194,9 @@ def test_unmutated_oracle_passes_every_pin(tmp_path):
 def test_mutant_is_caught(tmp_path, name):
     with open(SRC) as f:
         text = f.read()
-    old, new = MUTANTS[name]
-    assert text.count(old) == 1, "mutation anchor not found once: %s" % name
-    failed = _run(tmp_path, name, text.replace(old, new))
+    edits = MUTANTS[name]
+    for old, new in (edits if isinstance(edits, list) else [edits]):
+        assert text.count(old) == 1, "mutation anchor not found once: %s" % name
+        text = text.replace(old, new)
+    failed = _run(tmp_path, name, text)
     assert failed, "no pin caught mutant %s" % name

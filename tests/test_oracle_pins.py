@@ -21,6 +21,10 @@ def test_layout_q40_q80_hand_derived(orc):
     pins.check_q32_layout_goldens(orc)
 
 
+def test_layout_q4k_q6k_two_block_tensors(orc):
+    pins.check_qk_tensor_goldens(orc)
+
+
 def test_layout_single_field_probes(orc):
     pins.check_layout_probes(orc)
 
