@@ -25,7 +25,7 @@ __all__ = [
     "qgemv_read_probe", "qgemv_fused", "qgemv_quantize_weights_rows", "qgemv_fused_launches",
     "qgemv_multi", "qgemv_multi_fused", "qgemv_multi_geometry", "QGEMV_Q4_0", "QGEMV_Q8_0",
     "Graph", "qgemv_graph_begin", "qgemv_graph_end", "qgemv_graph_launch", "qgemv_graph_nodes",
-    "qgemv_graph_destroy", "qgemv_i8mc_workspace_bytes", "qgemv_batch_i8mc",
+    "qgemv_graph_destroy", "qgemv_graph_classify", "qgemv_i8mc_workspace_bytes", "qgemv_batch_i8mc",
     "qgemv_debug_partials_i8mc", "qgemv_fused_i8mc", "qgemv_route", "ROUTES",
 ]
 
@@ -106,6 +106,8 @@ def _load():
         "qgemv_graph_launch": (ctypes.c_int, [vp, vp]),
         "qgemv_graph_nodes": (ctypes.c_int, [vp, ctypes.POINTER(i64), ctypes.POINTER(i64)]),
         "qgemv_graph_destroy": (ctypes.c_int, [vp]),
+        "qgemv_graph_classify": (ctypes.c_int, [ctypes.POINTER(i32), i64, ctypes.POINTER(i64),
+                                                ctypes.POINTER(i64)]),
         "qgemv_i8mc_workspace_bytes": (sz, [i64, i64, i32]),
         "qgemv_route": (ctypes.c_int, [ctypes.c_int, i64, i64, i32]),
         "qgemv_batch_i8mc": (ctypes.c_int, [vp, vp, vp, vp, i64, i64, i32, vp, sz, vp]),
@@ -430,3 +432,13 @@ def qgemv_graph_nodes(graph: Graph) -> tuple:
 
 def qgemv_graph_destroy(graph: Graph) -> None:
     graph.close()
+
+
+def qgemv_graph_classify(types) -> tuple:
+    """(kernel nodes, other nodes) of a record with these HIP graph node types, as
+    qgemv_graph_end counts them; QgemvError when one of them is a memset node. Host only."""
+    arr = (ctypes.c_int32 * max(1, len(types)))(*[int(t) for t in types])
+    k, o = ctypes.c_int64(), ctypes.c_int64()
+    _check("qgemv_graph_classify",
+           _load().qgemv_graph_classify(arr, len(types), ctypes.byref(k), ctypes.byref(o)))
+    return int(k.value), int(o.value)

@@ -359,6 +359,12 @@ int qgemv_multi_fused(const qgemv_matrix *mats, int32_t nmats, const float *x, i
  */
 typedef struct qgemv_graph qgemv_graph;
 int qgemv_graph_begin(hipStream_t stream);
+/* The check qgemv_graph_end makes of a record, on its node types alone (values of HIP's
+ * hipGraphNodeType): QGEMV_EINVAL when one is a memset node (or on a null pointer), else
+ * QGEMV_OK with the kernel nodes and the other nodes counted. Host only; no HIP call, so it
+ * can be checked without a GPU and without ever recording a memset. */
+int qgemv_graph_classify(const int32_t *types, int64_t n, int64_t *kernel_nodes,
+                         int64_t *other_nodes);
 int qgemv_graph_end(hipStream_t stream, qgemv_graph **graph);
 int qgemv_graph_launch(const qgemv_graph *graph, hipStream_t stream);
 int qgemv_graph_nodes(const qgemv_graph *graph, int64_t *kernel_nodes, int64_t *other_nodes);

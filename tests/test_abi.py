@@ -1,39 +1,22 @@
-"""The C-ABI library on the CPU: it loads, exports every entry point include/qgemv.h declares,
-and rejects bad arguments on the host before anything reaches the GPU. No call here passes
-validation, so nothing is ever launched (these tests need no GPU)."""
+"""The C-ABI library's argument checks on the CPU: bad arguments are rejected on the host
+before anything reaches the GPU. The calls pass fake device addresses, and no call here
+passes validation, so nothing is ever launched. Because a future validation slip would turn
+such a call into a launch at a wild address, the module does not run in a process that sees
+a GPU (the exports and host-only helpers are checked in test_abi_exports.py)."""
 
 import ctypes
-import os
-import re
 
 import pytest
+import torch
 
 import block_quantized_weight_act_amd as qg
 
-ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "qgemv.h")
+# device_count() does not initialise the GPU runtime
+pytestmark = pytest.mark.skipif(torch.cuda.device_count() > 0,
+                                reason="fake device addresses are only passed where no GPU is visible")
 
 EINVAL, EALIGN, EWORKSPACE = 1, 2, 3
 A = 1 << 40          # a fake, 256-byte aligned "device address" (never dereferenced)
-
-
-def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(qgemv_\w+)\s*\(", text)))
-
-
-def test_library_exports_every_declared_function():
-    lib = ctypes.CDLL(qg.library_path)
-    names = declared_functions()
-    assert len(names) >= 14
-    missing = [n for n in names if not hasattr(lib, n)]
-    assert not missing, missing
-
-
-def test_binding_covers_every_declared_function():
-    names = set(declared_functions()) - {"qgemv_last_error"}
-    assert names <= set(qg.__all__), names - set(qg.__all__)
 
 
 def test_status_strings_and_sizes():
