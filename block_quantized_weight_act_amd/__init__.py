@@ -22,7 +22,7 @@ __all__ = [
     "qgemv_status_string", "qgemv_weight_bytes", "qgemv_quantize_act",
     "qgemv_workspace_bytes", "qgemv_q4k", "qgemv_q6k", "qgemv_batch", "qgemv_debug_partials",
     "qgemv_quantize_weights", "qgemv_plan_for", "qgemv_plan_workspace_bytes", "qgemv_batch_plan",
-    "qgemv_read_probe", "qgemv_fused", "qgemv_quantize_weights_rows", "qgemv_fused_launches",
+    "qgemv_read_probe", "qgemv_fused", "qgemv_fused_plan", "qgemv_quantize_weights_rows", "qgemv_fused_launches",
     "qgemv_multi", "qgemv_multi_fused", "qgemv_multi_geometry", "QGEMV_Q4_0", "QGEMV_Q8_0",
     "Graph", "qgemv_graph_begin", "qgemv_graph_end", "qgemv_graph_launch", "qgemv_graph_nodes",
     "qgemv_graph_destroy", "qgemv_graph_classify", "qgemv_i8mc_workspace_bytes", "qgemv_batch_i8mc",
@@ -100,6 +100,8 @@ def _load():
         "qgemv_batch_plan": (ctypes.c_int, [ctypes.c_int, vp, vp, vp, vp, i64, i64, i32,
                                             ctypes.POINTER(Plan), vp, sz, vp]),
         "qgemv_read_probe": (ctypes.c_int, [vp, sz, vp, i32, vp]),
+        "qgemv_fused_plan": (ctypes.c_int, [ctypes.c_int, vp, vp, vp, vp, vp, i64, i64, i32,
+                                            ctypes.POINTER(Plan), vp, sz, vp]),
         "qgemv_fused": (ctypes.c_int, [ctypes.c_int, vp, vp, vp, vp, vp, i64, i64, i32, vp, sz, vp]),
         "qgemv_graph_begin": (ctypes.c_int, [vp]),
         "qgemv_graph_end": (ctypes.c_int, [vp, ctypes.POINTER(vp)]),
@@ -251,6 +253,20 @@ def qgemv_fused(wtype, w, x, y, rows: int, cols: int, nvec: int, xq_out=None, xd
         _wtype(wtype), _ptr(w, name="w"), _ptr(x, torch.float32, "x"),
         _ptr(xq_out, torch.int8, "xq_out"), _ptr(xd_out, torch.float32, "xd_out"),
         _ptr(y, torch.float32, "y"), rows, cols, nvec, wsp, wsb, _stream(stream, y)))
+
+
+def qgemv_fused_plan(wtype, w, x, y, rows: int, cols: int, nvec: int, plan: dict, xq_out=None,
+                     xd_out=None, workspace=None, stream=None) -> None:
+    """qgemv_fused with an explicit plan: always the one-launch fused kernel (plus the
+    ordered reduce when the plan splits the columns)."""
+    lib = _load()
+    wsp, wsb = _ws(workspace)
+    p = Plan(**{k: v for k, v in plan.items() if k in dict(Plan._fields_)})
+    _check("qgemv_fused_plan", lib.qgemv_fused_plan(
+        _wtype(wtype), _ptr(w, name="w"), _ptr(x, torch.float32, "x"),
+        _ptr(xq_out, torch.int8, "xq_out"), _ptr(xd_out, torch.float32, "xd_out"),
+        _ptr(y, torch.float32, "y"), rows, cols, nvec, ctypes.byref(p), wsp, wsb,
+        _stream(stream, y)))
 
 
 def _matrices(mats):

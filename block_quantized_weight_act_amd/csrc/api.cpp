@@ -752,6 +752,17 @@ int qgemv_batch_plan(int wtype, const void *w, const int8_t *xq, const float *xd
     return run_gemv(wtype, w, act, y, rows, cols, nvec, *plan, workspace, workspace_bytes, stream);
 }
 
+int qgemv_fused_plan(int wtype, const void *w, const float *x, int8_t *xq_out, float *xd_out,
+                     float *y, int64_t rows, int64_t cols, int32_t nvec, const qgemv_plan *plan,
+                     void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (!plan) return QGEMV_EINVAL;
+    Activation act;
+    act.x = x;
+    act.xq_out = xq_out;
+    act.xd_out = xd_out;
+    return run_gemv(wtype, w, act, y, rows, cols, nvec, *plan, workspace, workspace_bytes, stream);
+}
+
 int qgemv_batch(int wtype, const void *w, const int8_t *xq, const float *xd, float *y,
                 int64_t rows, int64_t cols, int32_t nvec, void *workspace,
                 size_t workspace_bytes, hipStream_t stream) {

@@ -449,6 +449,16 @@ int qgemv_batch_plan(int wtype, const void *w, const int8_t *xq, const float *xd
                      int64_t rows, int64_t cols, int32_t nvec, const qgemv_plan *plan,
                      void *workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* qgemv_fused with an explicit plan (for tuning and tests): always the one-launch
+ * kernel, each workgroup quantizing the columns it reads (xq_out / xd_out, both NULL or
+ * both set, receive the codes and scales); a plan that splits the columns writes the
+ * partial sums to the workspace (qgemv_plan_workspace_bytes) and adds them in a second
+ * launch, in ascending chunk order, so y is bit-identical to qgemv_batch_plan with the
+ * same plan on the codes of qgemv_quantize_act. */
+int qgemv_fused_plan(int wtype, const void *w, const float *x, int8_t *xq_out, float *xd_out,
+                     float *y, int64_t rows, int64_t cols, int32_t nvec, const qgemv_plan *plan,
+                     void *workspace, size_t workspace_bytes, hipStream_t stream);
+
 /*
  * Measurement: read `bytes` (a multiple of 16) of device memory once with 16-byte loads
  * and nothing else, on `blocks` workgroups of 256 threads (a grid-stride loop). Its rate

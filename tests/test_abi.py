@@ -287,3 +287,20 @@ def test_matrix_core_path_limits_on_the_host():
     assert _call_batch(nvec=64, xq=A + (1 << 30) + 4) == EALIGN
     plan = qg.Plan()
     assert lib.qgemv_plan_for(1, 64, 1024, 9, ctypes.byref(plan)) == EINVAL
+
+
+def test_fused_plan_rejects_bad_arguments():
+    """qgemv_fused_plan refuses what qgemv_fused and qgemv_batch_plan refuse."""
+    lib = qg._load()
+    X, Y = A + (1 << 30), A + (3 << 30)
+    fp = lib.qgemv_fused_plan
+    plan = qg.Plan(64, 2, 4, 4, 0)
+    assert fp(1, A, X, None, None, Y, 64, 8192, 1, None, None, 0, None) == EINVAL      # no plan
+    assert fp(1, A, X, None, None, Y, 64, 8192, 1, ctypes.byref(plan), None, 0,
+              None) == EWORKSPACE                                   # two column chunks
+    assert fp(1, A, X + 4, None, None, Y, 64, 8192, 1, ctypes.byref(plan), None, 0,
+              None) == EALIGN
+    assert fp(1, A, X, A + (4 << 30), None, Y, 64, 8192, 1, ctypes.byref(plan), None, 0,
+              None) == EINVAL                                       # one code output of two
+    bad = qg.Plan(12, 1, 4, 4, 0)
+    assert fp(1, A, X, None, None, Y, 64, 8192, 1, ctypes.byref(bad), None, 0, None) == EINVAL

@@ -295,17 +295,28 @@ def test_workspace_required_when_split():
     ("q40", 4099, 1504, 1), ("q80", 1000, 2080, 2), ("q40", 300, 8224, 3), ("q80", 64, 96, 8),
 ])
 def test_fused_quantize_and_gemv(wtype, rows, cols, nvec):
-    """qgemv_fused: its codes and scales are the oracle's bit for bit, and its y is
-    bit-identical to quantize-then-GEMV with the same plan, including shapes whose plan splits
-    the columns. With code outputs the library may take the two-launch route; without them it
-    always runs the one-launch kernel (each workgroup quantizing its own slice)."""
+    """qgemv_fused: its codes and scales are the oracle's bit for bit, its y lies within the
+    oracle's bound, and its y is bit-identical to quantize-then-GEMV with the same plan,
+    including shapes whose plan splits the columns. With code outputs the library may take
+    the two-launch route; without them it always runs the one-launch kernel (each workgroup
+    quantizing its own slice). Past 16384 rows the weights repeat a 16384-row block of the
+    oracle's tensor, so the oracle's y for that block, repeated, is the reference for every
+    row."""
     import torch
     import block_quantized_weight_act_amd as qg
     _say("fused", wtype, rows, cols, nvec)
     rng = np.random.default_rng(rows + cols + nvec)
     x = (rng.standard_normal((nvec, cols)) * rng.choice([1e-3, 1.0, 40.0], size=(nvec, 1))).astype(np.float32)
     x[0, 32:64] = 0.0
-    w = gu.quantize_weights(wtype, (rng.standard_normal((rows, cols)) * 0.02).astype(np.float32))
+    unique = min(rows, 16384)
+    assert rows % unique == 0
+    wbuf_u = _quant(wtype, (rng.standard_normal((unique, cols)) * 0.02).astype(np.float32))
+    wbuf = wbuf_u if unique == rows else oracle.concat_rows(
+        wtype, [(wbuf_u, unique)] * (rows // unique), cols)
+    rq, rd = oracle.quantize_act(x)
+    ref_u = oracle.gemv(wtype, wbuf_u, unique, cols, rq, rd)
+    ref = {k: np.tile(ref_u[k], (1, rows // unique)) for k in ("y", "bound")}
+    w = gu.dev(wbuf)
     xt = gu.dev(x)
     xq, xd = gu.quantize_act(x)
     y_two = gu.gemv(wtype, w, xq, xd, rows, cols, nvec)
@@ -316,13 +327,15 @@ def test_fused_quantize_and_gemv(wtype, rows, cols, nvec):
     ws = torch.empty(max(nbytes, 4), dtype=torch.uint8, device=gu.DEV) if nbytes else None
     qg.qgemv_fused(wtype, w, xt, y, rows, cols, nvec, xq_out=xq_out, xd_out=xd_out, workspace=ws)
     y_fused = gu.host(y)
+    gu.assert_within_bound(y_fused, ref)
     assert np.array_equal(y_fused.view(np.uint32), y_two.view(np.uint32))
-    rq, rd = oracle.quantize_act(x)
     assert np.array_equal(gu.host(xq_out), rq)
     assert np.array_equal(gu.host(xd_out).view(np.uint32), rd.view(np.uint32))
     y2 = torch.full_like(y, float("nan"))
     qg.qgemv_fused(wtype, w, xt, y2, rows, cols, nvec, workspace=ws)      # without code outputs
-    assert np.array_equal(gu.host(y2).view(np.uint32), y_two.view(np.uint32))
+    y_one = gu.host(y2)
+    gu.assert_within_bound(y_one, ref)
+    assert np.array_equal(y_one.view(np.uint32), y_two.view(np.uint32))
 
 
 @pytest.mark.parametrize("wtype", ALL)
