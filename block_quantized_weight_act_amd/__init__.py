@@ -20,7 +20,7 @@ import torch
 __all__ = [
     "QGEMV_Q4K", "QGEMV_Q6K", "QgemvError", "library_path", "qgemv_version",
     "qgemv_status_string", "qgemv_weight_bytes", "qgemv_quantize_act",
-    "qgemv_workspace_bytes", "qgemv_q4k", "qgemv_q6k", "qgemv_batch", "qgemv_debug_partials",
+    "qgemv_workspace_bytes", "qgemv_q4k", "qgemv_q6k", "qgemv_batch", "qgemv_batch_scratch", "qgemv_debug_partials",
     "qgemv_quantize_weights", "qgemv_plan_for", "qgemv_plan_workspace_bytes", "qgemv_batch_plan",
     "qgemv_read_probe", "qgemv_fused", "qgemv_fused_plan", "qgemv_quantize_weights_rows", "qgemv_fused_launches",
     "qgemv_multi", "qgemv_multi_fused", "qgemv_multi_geometry", "QGEMV_Q4_0", "QGEMV_Q8_0",
@@ -86,6 +86,7 @@ def _load():
         "qgemv_q4k": (ctypes.c_int, [vp, vp, vp, vp, i64, i64, vp, sz, vp]),
         "qgemv_q6k": (ctypes.c_int, [vp, vp, vp, vp, i64, i64, vp, sz, vp]),
         "qgemv_batch": (ctypes.c_int, [ctypes.c_int, vp, vp, vp, vp, i64, i64, i32, vp, sz, vp]),
+        "qgemv_batch_scratch": (ctypes.c_int, [ctypes.c_int, vp, vp, vp, vp, i64, i64, i32, vp]),
         "qgemv_debug_partials": (ctypes.c_int, [ctypes.c_int, vp, vp, vp, vp, vp, i64, i64, i32, vp,
                                                 sz, vp]),
         "qgemv_quantize_weights": (ctypes.c_int, [ctypes.c_int, vp, vp, i64, i64, vp]),
@@ -230,6 +231,19 @@ def qgemv_batch(wtype, w, xq, xd, y, rows: int, cols: int, nvec: int, workspace=
         _wtype(wtype), _ptr(w, name="w"), _ptr(xq, torch.int8, "xq"),
         _ptr(xd, torch.float32, "xd"), _ptr(y, torch.float32, "y"), rows, cols, nvec, wsp, wsb,
         _stream(stream, y)))
+
+
+def qgemv_batch_scratch(wtype, w, xq, xd, y, rows: int, cols: int, nvec: int,
+                        stream=None) -> None:
+    """qgemv_batch with the library's static device scratch as its workspace (no workspace
+    argument; nothing allocated)."""
+    _check("qgemv_batch_scratch", _load().qgemv_batch_scratch(
+        _wtype(wtype), _ptr(w, name="w"), _ptr(xq, torch.int8, "xq"),
+        _ptr(xd, torch.float32, "xd"), _ptr(y, torch.float32, "y"), rows, cols, nvec,
+        _stream(stream, y)))
+
+
+SCRATCH_BYTES = 32 << 20       # the header's QGEMV_SCRATCH_BYTES
 
 
 def qgemv_batch_plan(wtype, w, xq, xd, y, rows: int, cols: int, nvec: int, plan: dict,

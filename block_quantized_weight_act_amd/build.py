@@ -24,7 +24,8 @@ OBJ = os.path.join(HERE, "_lib", "obj")
 LIB = os.path.join(HERE, "_lib", "libqgemv.so")
 
 SOURCES = ["gemv_multi.hip", "gemv_q4k.hip", "gemv_q6k.hip", "gemv_q40.hip", "gemv_q80.hip",
-           "api.cpp", "graph.cpp", "gemm_mfma.hip", "gemm_i8.hip", "act_quant.hip", "reduce.hip", "weight_quant.hip", "read_probe.hip"]
+           "api.cpp", "graph.cpp", "gemm_mfma.hip", "gemm_i8.hip", "act_quant.hip", "reduce.hip", "weight_quant.hip", "read_probe.hip",
+           "scratch.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",

@@ -813,6 +813,18 @@ int qgemv_batch(int wtype, const void *w, const int8_t *xq, const float *xd, flo
                     workspace, workspace_bytes, stream);
 }
 
+int qgemv_batch_scratch(int wtype, const void *w, const int8_t *xq, const float *xd, float *y,
+                        int64_t rows, int64_t cols, int32_t nvec, hipStream_t stream) {
+    if (qgemv_route(wtype, rows, cols, nvec) == 0 || !w || !xq || !xd || !y) return QGEMV_EINVAL;
+    const size_t need = qgemv_workspace_bytes(wtype, rows, cols, nvec);
+    if (need > kScratchBytes)
+        return fail_with(QGEMV_EWORKSPACE, "the shape needs more workspace than the static scratch");
+    void *ws = nullptr;
+    const int st = scratch_address(&ws);
+    if (st != QGEMV_OK) return st;
+    return qgemv_batch(wtype, w, xq, xd, y, rows, cols, nvec, ws, kScratchBytes, stream);
+}
+
 int qgemv_fused_launches(int wtype, int64_t rows, int64_t cols, int32_t nvec, int with_outputs) {
     if (!shape_ok_t(wtype, rows, cols, nvec)) return 0;
     if (!with_outputs) return 1;

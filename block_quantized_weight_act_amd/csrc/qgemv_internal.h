@@ -190,6 +190,11 @@ constexpr int kI8MaxWaves = 4;
 constexpr int kI8MaxVec = 16;      // vectors per launch (two groups of 8)
 hipError_t launch_gemm_q4k_i8(const GemmArgs &a, int waves, bool debug, hipStream_t stream);
 
+// The static device scratch buffer (scratch.hip): its size, and its device address on the
+// current device (looked up once per device; QGEMV_OK, or the failure status).
+constexpr size_t kScratchBytes = size_t{32} << 20;
+int scratch_address(void **ptr);
+
 // Host: record a HIP error (or a message) as this thread's last error text and return the
 // status the C ABI reports (QGEMV_EHIP, or `status`).
 int hip_fail(hipError_t e);

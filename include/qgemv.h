@@ -202,6 +202,25 @@ int qgemv_batch(int wtype, const void *w, const int8_t *xq, const float *xd, flo
                 int64_t rows, int64_t cols, int32_t nvec, void *workspace,
                 size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * qgemv_batch for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same kernels
+ * with the same results, bit for bit, but the workspace is the library's static
+ * device scratch buffer of QGEMV_SCRATCH_BYTES, so the caller passes only inputs and
+ * outputs. Shapes whose qgemv_workspace_bytes() exceeds QGEMV_SCRATCH_BYTES are
+ * refused with QGEMV_EWORKSPACE before anything is enqueued. The call allocates and
+ * frees nothing. Each GPU holds its own copy of the buffer from the library's first
+ * launch on it until the process ends; the first call on a device looks up its
+ * address there (once, host only), so under graph capture make one call on each
+ * device before capturing. stream must belong to the current device. Every call on
+ * one GPU shares that GPU's buffer and it keeps the last call's contents (nothing in
+ * it needs to start at zero): calls that can overlap on one GPU (several streams,
+ * several host threads) race and must be ordered by the caller.
+ */
+#define QGEMV_SCRATCH_BYTES (32u << 20)
+int qgemv_batch_scratch(int wtype, const void *w, const int8_t *xq, const float *xd, float *y,
+                        int64_t rows, int64_t cols, int32_t nvec, hipStream_t stream);
+
 /* Which kernels qgemv_batch (and qgemv_fused, qgemv_debug_partials) run for a
  * shape: the vector kernels, the integer matrix cores (qgemv_batch_i8mc), the
  * float matrix cores for 17..QGEMV_MAX_BATCH Q4_K vectors, or the vector kernels

@@ -289,6 +289,22 @@ def test_matrix_core_path_limits_on_the_host():
     assert lib.qgemv_plan_for(1, 64, 1024, 9, ctypes.byref(plan)) == EINVAL
 
 
+def test_scratch_entry_point_rejects_bad_arguments():
+    """qgemv_batch_scratch refuses a bad type or shape, null pointers and shapes whose
+    workspace exceeds the static scratch before it looks up anything."""
+    lib = qg._load()
+    X, Y = A + (1 << 30), A + (3 << 30)
+    sc = lib.qgemv_batch_scratch
+    assert sc(5, A, X, A + (2 << 30), Y, 64, 1024, 1, None) == EINVAL
+    assert sc(1, A, X, A + (2 << 30), Y, 64, 1000, 1, None) == EINVAL
+    assert sc(1, None, X, A + (2 << 30), Y, 64, 1024, 1, None) == EINVAL
+    assert sc(1, A, X, A + (2 << 30), None, 64, 1024, 1, None) == EINVAL
+    # 128 rows x 65536 columns x 256 vectors on the float matrix cores: 256 column splits of
+    # partial sums (32 MiB) plus the staged tiles, beyond the 32 MiB scratch
+    assert qg.qgemv_workspace_bytes("q4k", 128, 65536, 256) > qg.SCRATCH_BYTES
+    assert sc(1, A, X, A + (2 << 30), Y, 128, 65536, 256, None) == EWORKSPACE
+
+
 def test_fused_plan_rejects_bad_arguments():
     """qgemv_fused_plan refuses what qgemv_fused and qgemv_batch_plan refuse."""
     lib = qg._load()
