@@ -29,6 +29,7 @@ from __future__ import annotations
 import argparse
 import dataclasses
 import hashlib
+import itertools
 import re
 import json
 import math
@@ -68,6 +69,10 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--warm", action="store_true", help="reuse one weight copy (cache-warm)")
+    ap.add_argument("--counters", action="store_true",
+                    help="for hardware-counter runs: skip the graph-replay phases (their "
+                         "launches are the direct ones again) so each counter pass profiles "
+                         "fewer dispatches")
     ap.add_argument("--traffic-calibration", action="store_true",
                     help="also run the read probe over one weight copy and a plain 256 MiB "
                          "device copy, the known-size kernels the HBM counters are scaled by")
@@ -100,17 +105,72 @@ def kernel_source_hash(unit: str = "gemv_q4k.hip") -> str:
     return h.hexdigest()
 
 
-def load_traffic(workload: str, per_launch_bytes: int):
-    """HBM bytes per GEMV launch from the committed rocprofv3 counter summary, or None when
-    the summary is missing or was taken on other kernel sources."""
+def kernel_unit(kname: str) -> str:
+    """The translation unit in csrc/ a kernel (as named in traces) is compiled from."""
+    if kname.startswith("gemm_q4k_i8_kernel"):
+        return "gemm_i8.hip"
+    if kname.startswith("gemm_q4k_mfma_kernel") or kname.startswith("mc_stage_kernel"):
+        return "gemm_mfma.hip"
+    for tag, unit in (("Q4K", "gemv_q4k.hip"), ("Q6K", "gemv_q6k.hip"), ("Q40", "gemv_q40.hip"),
+                      ("Q80", "gemv_q80.hip")):
+        if "qgemv::%s," % tag in kname:
+            return unit
+    raise ValueError("no translation unit known for kernel %r" % kname)
+
+
+def load_traffic(workload: str, kname: str):
+    """HBM bytes per launch of kernel `kname` from the committed rocprofv3 counter summary of
+    the workload, or None when the summary is missing, covers another kernel, or was taken on
+    other sources of that kernel."""
     path = os.path.join(PROFILES, "gemv_%s_traffic.json" % workload)
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("kernel_source_sha256") != kernel_source_hash():
+    if rec.get("kernel") != kname:
+        return None
+    if rec.get("kernel_source_sha256") != kernel_source_hash(kernel_unit(kname)):
         return None
     return rec.get("hbm_bytes_per_launch")
+
+
+def weight_copies(w0, wbytes: int, warm: bool):
+    """The rotating weight copies: (list of copies, count, keep-alive). Enough copies to total
+    at least COLD_BYTES, so the 256 MB memory-side cache cannot hold the weights between uses.
+    Up to 128 copies are separate tensors; more (small matrices) are 256-byte aligned slots of
+    one buffer, passed as device pointers."""
+    import torch
+    if warm:
+        return [w0], 1, None
+    copies = max(1, math.ceil(COLD_BYTES / wbytes))
+    if copies <= 128:
+        return [w0] + [w0.clone() for _ in range(copies - 1)], copies, None
+    stride = (wbytes + 255) // 256 * 256
+    big = torch.empty(copies * stride, dtype=torch.uint8, device=w0.device)
+    big[:wbytes].copy_(w0)
+    filled = 1
+    while filled < copies:
+        n = min(filled, copies - filled)
+        big[filled * stride:(filled + n) * stride].copy_(big[:n * stride])
+        filled += n
+    base = big.data_ptr()
+    return [base + k * stride for k in range(copies)], copies, big
+
+
+class Marks:
+    """One-workgroup 16-byte read probes that cut the kernel trace into named windows, so a
+    trace summary can average each kernel over exactly the dispatches of one measured phase."""
+
+    def __init__(self, qg, dev):
+        import torch
+        self.qg = qg
+        self.buf = torch.zeros(16, dtype=torch.uint8, device=dev)
+        self.sink = torch.zeros(1, dtype=torch.int32, device=dev)
+        self.names = []
+
+    def mark(self, name_of_next_window: str):
+        self.qg.qgemv_read_probe(self.buf, self.sink, blocks=1, nbytes=16)
+        self.names.append(name_of_next_window)
 
 
 def algorithmic_bytes(wl, wbytes: int) -> dict:
@@ -223,7 +283,7 @@ def summarize_traffic(args) -> None:
     alg = algorithmic_bytes(wl, wbytes)["step" if launches == 1 else "gemv"]
     rec = {
         "workload": wl.name, "kernel": kname,
-        "kernel_source_sha256": kernel_source_hash(),
+        "kernel_source_sha256": kernel_source_hash(kernel_unit(kname)),
         "fetch_size_kib_per_dispatch": round(f["gemv_kib"], 3),
         "write_size_kib_per_dispatch": round(w["gemv_kib"], 3),
         "fetch_factor": round(fetch_factor, 6),
@@ -242,6 +302,10 @@ def summarize_traffic(args) -> None:
 
 
 def summarize_trace(paths: list) -> None:
+    """rocprofv3's per-kernel summary, then per-dispatch averages in each measured window. The
+    bench cuts the trace into windows with one-workgroup read probes (Marks); the warmup before
+    the first mark is left out. A third path, a file holding the bench's JSON line, names the
+    windows (its trace_windows)."""
     rows = _counter_rows(paths[0])
     print("| kernel | calls | average us | min us | max us | stddev us | % of GPU time |")
     print("|---|---|---|---|---|---|---|")
@@ -251,23 +315,31 @@ def summarize_trace(paths: list) -> None:
             float(r["MaxNs"]) / 1e3, float(r["StdDev"]) / 1e3, r["Percentage"]))
     if len(paths) < 2:
         return
-    # per-dispatch durations after the end of the warmup (first touch of buffers, clocks
-    # settling), which the run marks with a one-workgroup read probe
+    names = []
+    if len(paths) > 2:
+        with open(paths[2]) as f:
+            line = next(ln for ln in f if ln.lstrip().startswith("{"))
+        names = json.loads(line).get("trace_windows", [])
     trace = sorted(_counter_rows(paths[1]), key=lambda r: int(r["Start_Timestamp"]))
-    marks = [int(r["Start_Timestamp"]) for r in trace if "read_probe_kernel" in r["Kernel_Name"]
-             and r["Grid_Size_X"] == r["Workgroup_Size_X"]]
-    start = marks[-1] if marks else 0
-    per = {}
+    windows, cur = [], None
     for r in trace:
-        if int(r["Start_Timestamp"]) > start:
-            d = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
-            per.setdefault(r["Kernel_Name"], []).append(d)
+        if "read_probe_kernel" in r["Kernel_Name"] and r["Grid_Size_X"] == r["Workgroup_Size_X"]:
+            cur = {}
+            windows.append(cur)
+            continue
+        if cur is None:
+            continue                              # the warmup
+        d = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        cur.setdefault(r["Kernel_Name"], []).append(d)
     print()
-    print("| kernel (dispatches after the warmup) | dispatches | average us | median us |")
-    print("|---|---|---|---|")
-    for name, ds in sorted(per.items(), key=lambda kv: -sum(kv[1])):
-        ds = sorted(ds)
-        print("| `%s` | %d | %.3f | %.3f |" % (name, len(ds), sum(ds) / len(ds), ds[len(ds) // 2]))
+    print("| window (between the bench's marks) | kernel | dispatches | average us | median us |")
+    print("|---|---|---|---|---|")
+    for k, per in enumerate(windows):
+        label = names[k] if k < len(names) else "window %d" % (k + 1)
+        for name, ds in sorted(per.items(), key=lambda kv: -sum(kv[1])):
+            ds = sorted(ds)
+            print("| %s | `%s` | %d | %.3f | %.3f |" % (label, name, len(ds), sum(ds) / len(ds),
+                                                       ds[len(ds) // 2]))
 
 
 def timed(fn, n):
@@ -892,8 +964,8 @@ def main():
         wf = torch.from_numpy(wl.weight_block(r0, r1)).to(dev)
         qg.qgemv_quantize_weights_rows(wl.wtype, wf, w0, wl.rows, wl.cols, r0, r1 - r0)
         del wf
-    copies = 1 if args.warm else max(1, min(64, math.ceil(COLD_BYTES / wbytes)))
-    ws_list = [w0] + [w0.clone() for _ in range(copies - 1)]
+    ws_list, copies, _keep = weight_copies(w0, wbytes, args.warm)
+    rot = itertools.count()           # each launch takes the next copy, in every phase
 
     x = torch.from_numpy(wl.activations()).to(dev)
     xq = torch.empty((wl.nvec, wl.cols), dtype=torch.int8, device=dev)
@@ -909,11 +981,11 @@ def main():
         qg.qgemv_quantize_act(x, xq, xd, wl.cols, wl.nvec)
 
     def gemv(i):
-        qg.qgemv_batch(wl.wtype, ws_list[i % copies], xq, xd, y, wl.rows, wl.cols, wl.nvec,
-                       workspace=work)
+        qg.qgemv_batch(wl.wtype, ws_list[next(rot) % copies], xq, xd, y, wl.rows, wl.cols,
+                       wl.nvec, workspace=work)
 
     def step(i):
-        qg.qgemv_fused(wl.wtype, ws_list[i % copies], x, y, wl.rows, wl.cols, wl.nvec,
+        qg.qgemv_fused(wl.wtype, ws_list[next(rot) % copies], x, y, wl.rows, wl.cols, wl.nvec,
                        xq_out=xq, xd_out=xd, workspace=work)
 
     def two_launch(i):
@@ -924,29 +996,52 @@ def main():
     # few ms (launch durations rise by up to 20% and recover), so every host-side preparation
     # (graph capture) is done first and the measured phases then run back to back after the
     # warmup steps.
-    graphs = {name: capture(fn, args.steps)
-              for name, fn in (("step", step), ("gemv", gemv), ("two", two_launch))}
-    # first touch of every weight copy (page mappings) before any measured kernel runs
+    # a graph holds its launches' weight pointers: enough launches to cover every copy once
+    # (at most 5000), so a replay reads cold weights too
+    n_graph = max(args.steps, min(copies, 5000))
     sink = torch.zeros(1, dtype=torch.int32, device=dev)
-    sink_mark = torch.zeros(16, dtype=torch.uint8, device=dev)
+
+    def probe(i):
+        qg.qgemv_read_probe(ws_list[next(rot) % copies], sink, blocks=4096, nbytes=wbytes)
+
+    graphs = {} if args.counters else {
+        name: capture(fn, n_graph) for name, fn in (("step", step), ("gemv", gemv),
+                                                    ("two", two_launch), ("probe", probe))}
+    # first touch of every weight copy (page mappings) before any measured kernel runs
     for _ in range(2):
         for wc in ws_list:
-            qg.qgemv_read_probe(wc, sink, blocks=4096)
+            qg.qgemv_read_probe(wc, sink, blocks=4096, nbytes=wbytes)
     for i in range(args.warmup):
         step(i)
-    # a one-workgroup read of 16 bytes marks the end of the warmup in kernel traces
-    qg.qgemv_read_probe(sink_mark, sink, blocks=1, nbytes=16)
+    marks = Marks(qg, dev)
+    marks.mark("step, direct launches (HIP events)")
     ms_step, wall_step = timed(step, args.steps)
+    marks.mark("gemv, direct launches")
     ms_gemv, _ = timed(gemv, args.steps)
+    marks.mark("quantize_act, direct launches")
     ms_quant, _ = timed(lambda i: quantize(), args.steps)
+    marks.mark("quantize + gemv, direct launches")
     ms_two, _ = timed(two_launch, args.steps)
-    ms_step_graph = replay_timed(graphs["step"], args.steps)
-    ms_gemv_graph = replay_timed(graphs["gemv"], args.steps)
-    ms_two_graph = replay_timed(graphs["two"], args.steps)
+    if args.counters:
+        ms_step_graph, ms_gemv_graph, ms_two_graph = ms_step, ms_gemv, ms_two
+    else:
+        marks.mark("step, graph replay (the roofline's launches)")
+        ms_step_graph = replay_timed(graphs["step"], n_graph)
+        marks.mark("gemv, graph replay")
+        ms_gemv_graph = replay_timed(graphs["gemv"], n_graph)
+        marks.mark("quantize + gemv, graph replay")
+        ms_two_graph = replay_timed(graphs["two"], n_graph)
+    marks.mark("step, batches for the distribution")
     step_dist = spread(step, args.steps)
     # the practical read ceiling: a plain streaming read of the same (cold, rotating) copies
-    ms_probe, _ = timed(lambda i: qg.qgemv_read_probe(ws_list[i % copies], sink, blocks=4096),
-                        args.steps)
+    marks.mark("read probe over the weight copies, direct launches")
+    ms_probe_direct, _ = timed(probe, args.steps)
+    if args.counters:
+        ms_probe = ms_probe_direct
+    else:
+        marks.mark("read probe over the weight copies, graph replay")
+        ms_probe = replay_timed(graphs["probe"], n_graph)
+    marks.mark("after the measured phases")
     probe_gbs = wbytes / (ms_probe * 1e-3) / 1e9
 
     # the step's result must be usable: every output finite
@@ -960,10 +1055,15 @@ def main():
     value = nbytes["step"] / (ms_step * 1e-3) / 1e9
     launches = qg.qgemv_fused_launches(wl.wtype, wl.rows, wl.cols, wl.nvec, True)
     route = qg.qgemv_route(wl.wtype, wl.rows, wl.cols, wl.nvec)
-    # the dominant kernel: the step itself when it is one launch, else its GEMV launch
-    rk_bytes, rk_ms = (nbytes["step"], ms_step) if launches == 1 else (nbytes["gemv"], ms_gemv)
+    # the dominant kernel: the step itself when it is one launch, else its GEMV launch; its
+    # duration is the mean over a graph replay of back-to-back launches (HIP events around the
+    # replay on its stream), which for short kernels excludes the host's per-call time that
+    # direct launches from Python add between kernels
+    rk_bytes, rk_ms = ((nbytes["step"], ms_step_graph) if launches == 1
+                       else (nbytes["gemv"], ms_gemv_graph))
     achieved = rk_bytes / (rk_ms * 1e-3) / 1e9
-    traffic = load_traffic(args.workload, rk_bytes)
+    kname = roofline_kernel(wl.wtype, plan, wl.nvec, launches, route)
+    traffic = load_traffic(args.workload, kname)
     out = {
         "metric": "achieved HBM GB/s and % of roofline, Q4_K GEMV batch-1 (us per GEMV)",
         "value": round(value, 1),
@@ -977,8 +1077,9 @@ def main():
         "vs_baseline": None,
         "dtype": "int8x" + wl.wtype,
         "data": "synthetic",
-        "config": {"workload": "%s GEMV W %dx%d, batch %d, cold weights (%d rotating copies)"
-                               % (FORMAT_NAMES[wl.wtype], wl.rows, wl.cols, wl.nvec, copies),
+        "config": {"workload": "%s GEMV W %dx%d, batch %d, cold weights (%d rotating copies, "
+                               "%.0f MB)" % (FORMAT_NAMES[wl.wtype], wl.rows, wl.cols, wl.nvec,
+                                             copies, copies * wbytes / 1e6),
                    "name": wl.name, "rows": wl.rows, "cols": wl.cols, "nvec": wl.nvec,
                    "weight_bytes": wbytes, "route": route,
                    "plan": plan if route == "vector" else None},
@@ -995,18 +1096,26 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic,
-                     "kernel": roofline_kernel(wl.wtype, plan, wl.nvec, launches, route),
-                     "algorithmic_bytes_per_launch": rk_bytes, "us_per_launch": round(rk_ms * 1e3, 3)},
+                     "kernel": kname,
+                     "algorithmic_bytes_per_launch": rk_bytes, "us_per_launch": round(rk_ms * 1e3, 3),
+                     "statistic": "mean launch time over a graph replay of %d back-to-back "
+                                  "launches (HIP events on the replay stream); the trace "
+                                  "window '%s' holds the same launches" % (
+                                      n_graph, "step, graph replay (the roofline's launches)"
+                                      if launches == 1 else "gemv, graph replay")},
         "step_launches": launches,
         "us_per_step_distribution": step_dist,
         "read_probe": {"gbs": round(probe_gbs, 1), "us": round(ms_probe * 1e3, 3),
+                       "statistic": "graph replay, as for the roofline",
+                       "us_direct_launches": round(ms_probe_direct * 1e3, 3),
                        "roofline_achieved_pct_of_probe": round(100 * achieved / probe_gbs, 2)},
         "setup_s": round(setup_s, 1),
+        "trace_windows": marks.names,
     }
     if args.traffic_calibration:
         sink = torch.zeros(1, dtype=torch.int32, device=dev)
         for i in range(10):
-            qg.qgemv_read_probe(ws_list[i % copies], sink, blocks=4096)
+            qg.qgemv_read_probe(ws_list[i % copies], sink, blocks=4096, nbytes=wbytes)
         src = torch.empty(CALIB_COPY_BYTES, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
         for _ in range(10):
