@@ -61,10 +61,6 @@ __host__ __device__ constexpr int lds_bytes(int waves, int vg) {
            2 * waves * 16 * (8 * vg) * 4;
 }
 
-// s_waitcnt immediate: no vector-memory load outstanding, the other counters not waited for
-// (vmcnt bits 3:0 and 15:14, expcnt 6:4 at its maximum 7, lgkmcnt 11:8 at its maximum 15).
-constexpr int kWaitVm0 = (7 << 4) | (15 << 8);
-
 // Staging passes of the fused form at most: each group of 8 lanes quantizes one 32-column block
 // per pass; 8 vectors x 8 nsb blocks over 8 waves groups, with nsb <= kSbw waves. The form from
 // codes takes a block per 2 lanes, a quarter of the passes per group of 8 vectors.
@@ -72,7 +68,11 @@ constexpr int kStagePasses = 8 * kSbw;
 
 // VG groups of 8 vectors per launch (nvec <= 8 VG): every group multiplies the same loaded
 // weights (one product per group and pair of blocks).
-template <int MODE, int VG>
+// KEEP: the wave's activation operands stay in registers for the whole kernel (one group of 8
+// vectors, a launch of at most two row tiles per workgroup); otherwise every product reads its
+// operands from LDS as it goes, which leaves registers for more resident waves when each
+// workgroup walks many tiles.
+template <int MODE, int VG, int KEEP>
 __global__ void __launch_bounds__(256) gemm_q4k_i8_kernel(GemmArgs a) {
     constexpr bool DBG = MODE == kModeDebug;
     constexpr bool FUSED = MODE == kModeFused;
@@ -124,9 +124,20 @@ __global__ void __launch_bounds__(256) gemm_q4k_i8_kernel(GemmArgs a) {
             h[k] = load16(hplane + blk * 16);
         }
     };
-    uint4 cw[kSbw][2];
-    uint4 hd[kSbw];
-    issue(rt, cw, hd);
+    // Two row tiles' weights go out before anything waits: this workgroup's tiles rt and
+    // rt + stride (the second clamped to the last tile when the workgroup has only one), after
+    // the staging's loads and before the staging's arithmetic, so the wait for the staged
+    // activation never waits for the weights, and both tiles are in flight from the start.
+    const int stride = static_cast<int>(gridDim.x);
+    const int ntiles = (row_tiles - rt + stride - 1) / stride;      // this workgroup's tiles
+    uint4 cwA[kSbw][2], cwB[kSbw][2];
+    uint4 hdA[kSbw], hdB[kSbw];
+    auto issue_first_two = [&]() {
+        __builtin_amdgcn_sched_barrier(0);
+        issue(rt, cwA, hdA);
+        issue(min(rt + stride, row_tiles - 1), cwB, hdB);
+        __builtin_amdgcn_sched_barrier(0);
+    };
 
     // ---- the split's activation into LDS: codes permuted per block (columns 0-7, 16-23,
     //      8-15, 24-31), scales and -xd * S; zeros for vectors past nvec. All loads go out
@@ -159,6 +170,7 @@ __global__ void __launch_bounds__(256) gemm_q4k_i8_kernel(GemmArgs a) {
                              ? *reinterpret_cast<const float4 *>(a.x + gb * 32 + 4 * j8)
                              : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
             }
+            issue_first_two();
 #pragma unroll
             for (int ps = 0; ps < kStagePasses; ps++) {
                 if (ps < passes) {            // the same in every lane of the workgroup
@@ -196,6 +208,7 @@ __global__ void __launch_bounds__(256) gemm_q4k_i8_kernel(GemmArgs a) {
                 cv[ps] = live ? load16(a.xq + gb * 32 + 16 * h) : make_uint4(0u, 0u, 0u, 0u);
                 sv[ps] = live ? a.xd[gb] : 0.0f;
             }
+            issue_first_two();
 #pragma unroll
             for (int ps = 0; ps < VG * kStagePasses / 4; ps++) {
                 if (ps < passes) {            // the same in every lane of the workgroup
@@ -221,11 +234,8 @@ __global__ void __launch_bounds__(256) gemm_q4k_i8_kernel(GemmArgs a) {
             }
         }
     }
-    // Every load so far has landed (the first tile's weights came before the staging's loads,
-    // which are in use): waiting for all of them here also settles the staging loads of passes
-    // past `passes`, issued but unused, which would otherwise count as in flight at the head of
-    // the loop below and make the compiler wait for every load there on each iteration.
-    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    // (the staging's loads, used or not, were issued before the weights, so every wait for
+    // the weights below also covers them)
     __syncthreads();
 
     // ---- where this lane reads its activation operands in LDS (for every row tile), per
@@ -252,11 +262,34 @@ __global__ void __launch_bounds__(256) gemm_q4k_i8_kernel(GemmArgs a) {
         }
     }
 
+    // This wave's activation operands (codes and scales of every pair of blocks it multiplies)
+    // are the same for every row tile. With KEEP they are read from LDS once, all together (one
+    // wait for the lot instead of one LDS round trip ahead of each product), into 64 registers
+    // kept for the whole kernel (16384 x 2048 x 8: 8.1 against 8.7 us); that halves the resident
+    // waves, so launches whose workgroups walk many tiles read them per product instead
+    // (262144 x 1536 x 8: 50 against 57 us).
+    struct ActOps {
+        v4i_t A[kSbw][4];
+        v4f_t X[kSbw][4];
+    };
+    ActOps ops;
+    if constexpr (KEEP) {
+#pragma unroll
+        for (int k = 0; k < kSbw; k++)
+#pragma unroll
+            for (int t = 0; t < 4; t++) {
+                const int blk = (wsb + k) * 8 + 2 * t;    // within the split's staged blocks
+                ops.A[k][t] = *reinterpret_cast<const v4i_t *>(arow[0] + blk * 32);
+                ops.X[k][t] = *reinterpret_cast<const v4f_t *>(xrow[0] + blk * NV);
+            }
+    }
+
     float *out = DBG ? nullptr : a.out + static_cast<int64_t>(blockIdx.y) * nvec * rows;
     int slot = 0;
     // Row tile `rt` from the loaded registers (cw, hd): its products, folded to this lane's two
     // outputs per group gi (vectors 8 gi + vv and 8 gi + vv + 2 of row r, vv = 4 (g % 2) + l / 32).
-    auto products = [&](int rt, float (&fold)[VG][2]) {
+    auto products = [&](int rt, const uint4 (&cw)[kSbw][2], const uint4 (&hd)[kSbw],
+                        float (&fold)[VG][2]) {
         v4f_t acc[VG];
 #pragma unroll
         for (int gi = 0; gi < VG; gi++) acc[gi] = v4f_t{0.0f, 0.0f, 0.0f, 0.0f};
@@ -284,25 +317,44 @@ __global__ void __launch_bounds__(256) gemm_q4k_i8_kernel(GemmArgs a) {
                     pw[2 * i + 1][0] = z;
                     pw[2 * i + 1][1] = w;
                 }
-                v4f_t tt[VG];
+                // The four pairs' weight operands and sub-scales first, then their products
+                // back to back into separate registers, then the float work on the results:
+                // no product waits for the previous one's float work, and no float work waits
+                // on the product just issued.
+                v4i_t B[4];
+                int sc[4];
 #pragma unroll
                 for (int t = 0; t < 4; t++) {
                     const uint2 c = make_uint2(pw[t][0], pw[t][1]);
-                    const v4i_t B = {static_cast<int>(c.x & 0x0F0F0F0Fu),
-                                     static_cast<int>(c.y & 0x0F0F0F0Fu),
-                                     static_cast<int>((c.x >> 4) & 0x0F0F0F0Fu),
-                                     static_cast<int>((c.y >> 4) & 0x0F0F0F0Fu)};
-                    const v4i_t zero = {0, 0, 0, 0};
+                    B[t] = v4i_t{static_cast<int>(c.x & 0x0F0F0F0Fu),
+                                 static_cast<int>(c.y & 0x0F0F0F0Fu),
+                                 static_cast<int>((c.x >> 4) & 0x0F0F0F0Fu),
+                                 static_cast<int>((c.y >> 4) & 0x0F0F0F0Fu)};
+                    sc[t] = static_cast<int>(((ysh >> (8 * t)) & 15u) | (((wsh >> (4 * t)) & 3u) << 4));
+                }
+                v4i_t P[VG][4];
+#pragma unroll
+                for (int t = 0; t < 4; t++) {
                     const int blk = (wsb + k) * 8 + 2 * t;      // first block of the pair, in the split
-                    const int sc = static_cast<int>(((ysh >> (8 * t)) & 15u) | (((wsh >> (4 * t)) & 3u) << 4));
 #pragma unroll
                     for (int gi = 0; gi < VG; gi++) {
-                        const v4i_t A = *reinterpret_cast<const v4i_t *>(arow[gi] + blk * 32);
-                        const v4f_t xdv = *reinterpret_cast<const v4f_t *>(xrow[gi] + blk * NV);
-                        const v4i_t P = __builtin_amdgcn_mfma_i32_16x16x64_i8(A, B, zero, 0, 0, 0);
+                        const v4i_t A = KEEP ? ops.A[k][t]
+                                                : *reinterpret_cast<const v4i_t *>(arow[gi] + blk * 32);
+                        const v4i_t zero = {0, 0, 0, 0};
+                        P[gi][t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A, B[t], zero, 0, 0, 0);
+                    }
+                }
+                v4f_t tt[VG];
+#pragma unroll
+                for (int t = 0; t < 4; t++) {
+                    const int blk = (wsb + k) * 8 + 2 * t;
+#pragma unroll
+                    for (int gi = 0; gi < VG; gi++) {
+                        const v4f_t xdv = KEEP ? ops.X[k][t]
+                                                  : *reinterpret_cast<const v4f_t *>(xrow[gi] + blk * NV);
 #pragma unroll
                         for (int i = 0; i < 4; i++) {
-                            const float ps = static_cast<float>(__mul24(sc, P[i]));   // exact: < 2^22
+                            const float ps = static_cast<float>(__mul24(sc[t], P[gi][t][i]));   // exact: < 2^22
                             tt[gi][i] = t == 0 ? xdv[i] * ps : fmaf(xdv[i], ps, tt[gi][i]);
                         }
                         if (DBG) {
@@ -312,7 +364,7 @@ __global__ void __launch_bounds__(256) gemm_q4k_i8_kernel(GemmArgs a) {
                             for (int i = 0; i < 4; i++) {
                                 const int v = 8 * gi + 4 * (g & 1) + i;
                                 if (v < nvec && row < rows)
-                                    a.P[(static_cast<int64_t>(v) * rows + row) * nbk + gblk] = P[i];
+                                    a.P[(static_cast<int64_t>(v) * rows + row) * nbk + gblk] = P[gi][t][i];
                             }
                         }
                     }
@@ -383,16 +435,42 @@ __global__ void __launch_bounds__(256) gemm_q4k_i8_kernel(GemmArgs a) {
             slot ^= 1;
         }
     };
-    // The next tile's loads go out into the same registers as soon as this tile's arithmetic
-    // has read them, ahead of the sums over the waves and the stores (unconditionally: past the
-    // last tile they reload it, unused).
-    const int stride = static_cast<int>(gridDim.x);
+    // One or two tiles: both are in flight already. More: tile 3 goes into the first set as
+    // soon as tile 1's arithmetic has read it, and from then on each tile's successor goes out
+    // into the same registers right after the tile's arithmetic, ahead of the sums over the
+    // waves and the stores (past the last tile it reloads the last one, unused). The branches
+    // are uniform over the workgroup and every wait in them counts only loads issued on the
+    // same path.
+    float fold[VG][2];
+    if (ntiles <= 2) {
+        __builtin_amdgcn_sched_barrier(0);
+        products(rt, cwA, hdA, fold);
+        __builtin_amdgcn_sched_barrier(0);
+        finish(rt, fold);
+        if (ntiles == 2) {
+            __builtin_amdgcn_sched_barrier(0);
+            products(rt + stride, cwB, hdB, fold);
+            __builtin_amdgcn_sched_barrier(0);
+            finish(rt + stride, fold);
+        }
+        return;
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    products(rt, cwA, hdA, fold);
+    __builtin_amdgcn_sched_barrier(0);
+    issue(rt + 2 * stride, cwA, hdA);
+    __builtin_amdgcn_sched_barrier(0);
+    finish(rt, fold);
+    __builtin_amdgcn_sched_barrier(0);
+    products(rt + stride, cwB, hdB, fold);
+    __builtin_amdgcn_sched_barrier(0);
+    finish(rt + stride, fold);
+    rt += 2 * stride;
     while (true) {
-        float fold[VG][2];
         __builtin_amdgcn_sched_barrier(0);
-        products(rt, fold);
+        products(rt, cwA, hdA, fold);
         __builtin_amdgcn_sched_barrier(0);
-        issue(min(rt + stride, row_tiles - 1), cw, hd);
+        issue(min(rt + stride, row_tiles - 1), cwA, hdA);
         __builtin_amdgcn_sched_barrier(0);
         finish(rt, fold);
         rt += stride;
@@ -410,8 +488,13 @@ hipError_t launch_vg(const GemmArgs &a, int waves, bool debug, hipStream_t strea
     // once per form and size; each workgroup then takes an equal share of the row tiles, and at
     // least two (the staging is per workgroup, and a second tile's loads overlap the first
     // tile's arithmetic: 16384 x 2048 x 8 measured 9.6 us against 10.3 us with one tile per
-    // workgroup). Concurrent first calls store the same values.
+    // workgroup). Concurrent first calls store the same values. The residency is that of the
+    // form that walks many tiles (KEEP = 0). With one group of 8 vectors, at most two tiles per
+    // workgroup and every workgroup resident at once in the form that keeps its operands in
+    // registers (KEEP = 1, fewer resident workgroups), that form runs (32768 x 2048 x 8: two
+    // rounds of it, 14.3 us, against one of the other, 13.7 us).
     static std::atomic<int> per_cu[3][kI8MaxWaves] = {};
+    static std::atomic<int> per_cu_keep[3][kI8MaxWaves] = {};
     static std::atomic<int> cus{0};
     if (cus.load(std::memory_order_relaxed) == 0) {
         int dev = 0, n = 0;
@@ -430,26 +513,42 @@ hipError_t launch_vg(const GemmArgs &a, int waves, bool debug, hipStream_t strea
         int n = 0;
         hipError_t e;
         if (mode == kModeDebug)
-            e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gemm_q4k_i8_kernel<kModeDebug, VG>, threads, lds);
+            e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gemm_q4k_i8_kernel<kModeDebug, VG, 0>, threads, lds);
         else if (mode == kModeFused)
-            e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gemm_q4k_i8_kernel<kModeFused, 1>, threads, lds);
+            e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gemm_q4k_i8_kernel<kModeFused, 1, 0>, threads, lds);
         else
-            e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gemm_q4k_i8_kernel<kModePlain, VG>, threads, lds);
+            e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gemm_q4k_i8_kernel<kModePlain, VG, 0>, threads, lds);
         res.store((e == hipSuccess && n > 0) ? n : 1, std::memory_order_relaxed);
+    }
+    std::atomic<int> &res_keep = per_cu_keep[mode][waves - 1];
+    if (VG == 1 && mode != kModeDebug && res_keep.load(std::memory_order_relaxed) == 0) {
+        int n = 0;
+        const hipError_t e =
+            mode == kModeFused
+                ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gemm_q4k_i8_kernel<kModeFused, 1, 1>, threads, lds)
+                : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gemm_q4k_i8_kernel<kModePlain, 1, 1>, threads, lds);
+        res_keep.store((e == hipSuccess && n > 0) ? n : 1, std::memory_order_relaxed);
     }
     const int64_t cap = std::max<int64_t>(
         1, int64_t{res.load(std::memory_order_relaxed)} * cus.load(std::memory_order_relaxed) /
                a.splits);
     const int64_t per_wg = std::max<int64_t>(2, (a.row_tiles + cap - 1) / cap);
     const int64_t blocks = (a.row_tiles + per_wg - 1) / per_wg;
+    const bool keep = VG == 1 && mode != kModeDebug && per_wg <= 2 &&
+                      blocks * a.splits <= int64_t{res_keep.load(std::memory_order_relaxed)} *
+                                               cus.load(std::memory_order_relaxed);
     const dim3 grid(static_cast<unsigned>(blocks), static_cast<unsigned>(a.splits));
     const dim3 block(static_cast<unsigned>(threads));
     if (mode == kModeDebug)
-        hipLaunchKernelGGL((gemm_q4k_i8_kernel<kModeDebug, VG>), grid, block, lds, stream, a);
+        hipLaunchKernelGGL((gemm_q4k_i8_kernel<kModeDebug, VG, 0>), grid, block, lds, stream, a);
+    else if (mode == kModeFused && keep)
+        hipLaunchKernelGGL((gemm_q4k_i8_kernel<kModeFused, 1, 1>), grid, block, lds, stream, a);
     else if (mode == kModeFused)
-        hipLaunchKernelGGL((gemm_q4k_i8_kernel<kModeFused, 1>), grid, block, lds, stream, a);
+        hipLaunchKernelGGL((gemm_q4k_i8_kernel<kModeFused, 1, 0>), grid, block, lds, stream, a);
+    else if (keep)
+        hipLaunchKernelGGL((gemm_q4k_i8_kernel<kModePlain, 1, 1>), grid, block, lds, stream, a);
     else
-        hipLaunchKernelGGL((gemm_q4k_i8_kernel<kModePlain, VG>), grid, block, lds, stream, a);
+        hipLaunchKernelGGL((gemm_q4k_i8_kernel<kModePlain, VG, 0>), grid, block, lds, stream, a);
     return hipGetLastError();
 }
 
