@@ -229,6 +229,20 @@ def cpu_baseline(wl, seconds: float, y_gpu: np.ndarray, max_rows: int = 32768) -
 
     per, reps, el = rate(threads, seconds)
     per1, reps1, el1 = rate(1, seconds / 2)
+    # the oracle's activation quantizer on the workload's activation, timed on its own (one
+    # thread; it is a few microseconds per call, so many calls are timed together)
+    x_act = wl.activations()
+    oracle.quantize_act(x_act)
+    qreps, q0 = 0, time.perf_counter()
+    while True:
+        for _ in range(100):
+            oracle.quantize_act(x_act)
+        qreps += 100
+        qel = time.perf_counter() - q0
+        if qel >= min(2.0, seconds / 4):
+            break
+    q_per = qel / qreps
+    q_bytes = x_act.size * 4 + x_act.size + (x_act.size // 32) * 4
     model = ""
     try:
         with open("/proc/cpuinfo") as f:
@@ -244,6 +258,12 @@ def cpu_baseline(wl, seconds: float, y_gpu: np.ndarray, max_rows: int = 32768) -
             "one_core": {"value": round(nbytes / per1 / 1e9, 3), "unit": "GB/s", "reps": reps1,
                          "seconds": round(el1, 1)},
             "cpu_model": model,
+            "quantize_act": {"us_per_call": round(q_per * 1e6, 3),
+                             "gbs": round(q_bytes / q_per / 1e9, 3), "cores": 1,
+                             "calls": qreps, "seconds": round(qel, 2),
+                             "sample": "the workload's whole activation (%d vectors x %d "
+                                       "columns) per call, including the Python binding's "
+                                       "copies" % (wl.nvec, wl.cols)},
             "gpu_y_check": {"rows": rows, "max_err_over_bound": ratio, "ok": ratio <= 1.0}}
 
 
