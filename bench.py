@@ -191,7 +191,9 @@ def roofline_kernel(wtype: str, plan: dict, nvec: int, launches: int, route: str
     column splits the kernel that splits inside the workgroup); on the integer matrix-core
     route the product kernel of that route."""
     if route == "i8mc":
-        return "gemm_q4k_i8_kernel<%d, %d>" % (2 if launches == 1 else 0, (nvec + 7) // 8)
+        # the third template argument (operands kept in registers or not) is chosen at launch
+        # from the GPU's occupancy, so the name is given up to it (a prefix of the trace name)
+        return "gemm_q4k_i8_kernel<%d, %d, " % (2 if launches == 1 else 0, (nvec + 7) // 8)
     tag = {"q4k": "Q4K", "q6k": "Q6K", "q40": "Q40", "q80": "Q80"}[wtype]
     if launches != 1 and plan["splits"] > 1:
         # the unfused product of a split plan: the column split inside the workgroup
@@ -850,7 +852,9 @@ def bench_many(args, wl) -> dict:
 
     n8 = max(4, args.steps // 8)
     graphs = {"step": capture(step, args.steps), "gemm": capture(gemm, args.steps),
-              "by_eight": capture(by_eight, n8), "by_eight_i8": capture(by_eight_i8, n8)}
+              "by_eight": capture(by_eight, n8)}
+    if wl.wtype == "q4k":                 # the integer matrix-core kernel of groups takes Q4_K
+        graphs["by_eight_i8"] = capture(by_eight_i8, n8)
     sink = torch.zeros(1, dtype=torch.int32, device=dev)
     sink_mark = torch.zeros(16, dtype=torch.uint8, device=dev)
     for _ in range(2):
@@ -863,7 +867,7 @@ def bench_many(args, wl) -> dict:
     ms_gemm = replay_timed(graphs["gemm"], args.steps)
     ms_gemm_events, _ = timed(gemm, args.steps)
     ms_eight = replay_timed(graphs["by_eight"], n8)
-    ms_eight_i8 = replay_timed(graphs["by_eight_i8"], n8)
+    ms_eight_i8 = replay_timed(graphs["by_eight_i8"], n8) if "by_eight_i8" in graphs else None
     dist = spread(step, args.steps)
     step(0)
     torch.cuda.synchronize()
@@ -881,13 +885,19 @@ def bench_many(args, wl) -> dict:
     gemm_tflops = flops / (ms_gemm * 1e-3) / 1e12
     t_hbm = gemm_bytes / (HBM_PEAK_GBS * 1e9)
     route = qg.qgemv_route(wl.wtype, rows, cols, nvec)
+    # The contraction is int8 codes x int8 (Q8_0) or 4-bit (Q4_K, Q4_0) codes, so every route
+    # is set against the int8 matrix peak; the float route (fp16 products of exact integers)
+    # is also given against its own fp16 peak.
+    mfma_peak, mfma_unit = MFMA_I8_PEAK_TOPS, "TOP/s"
     if route == "i8mc":
         # the integer matrix cores (int8 products; 9..16 vectors)
-        kernel = "gemm_q4k_i8_kernel<0, %d>" % ((nvec + 7) // 8)
-        mfma_peak, mfma_unit = MFMA_I8_PEAK_TOPS, "TOP/s"
+        kernel = "gemm_q4k_i8_kernel<0, %d, " % ((nvec + 7) // 8)
+    elif route == "mc32":
+        vtiles = (nvec + 31) // 32
+        vw = 4 if vtiles >= 3 else vtiles
+        kernel = "gemm_q32_mc_kernel<%d, %d, %d, false>" % (4 if wl.wtype == "q80" else 3, 4 // vw, vw)
     else:
         kernel = "gemm_q4k_mfma_kernel<%d, false>" % min(4, (nvec + 31) // 32)
-        mfma_peak, mfma_unit = MFMA_F16_PEAK_TFLOPS, "TFLOP/s"
     t_mfma = flops / (mfma_peak * 1e12)
     if t_hbm >= t_mfma:
         roof = {"bound": "hbm", "achieved": round(gemm_gbs, 1), "peak": HBM_PEAK_GBS,
@@ -900,6 +910,8 @@ def bench_many(args, wl) -> dict:
                  "us_per_launch": round(ms_gemm * 1e3, 3),
                  "hbm_frac": round(gemm_gbs / HBM_PEAK_GBS, 4),
                  "mfma_frac": round(gemm_tflops / mfma_peak, 4), "route": route})
+    if route == "mc":
+        roof["mfma_f16_frac"] = round(gemm_tflops / MFMA_F16_PEAK_TFLOPS, 4)
     out = {
         "metric": "achieved HBM GB/s and % of roofline, block-quantized GEMV with many activation "
                   "vectors (matrix cores)",
@@ -912,7 +924,7 @@ def bench_many(args, wl) -> dict:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int8xq4k",
+        "dtype": "int8x" + wl.wtype,
         "data": "synthetic",
         "config": {"workload": "%s W %d x %d, %d vectors, cold weights (%d rotating copies)" % (
                        FORMAT_NAMES[wl.wtype], rows, cols, nvec, copies),
@@ -925,14 +937,13 @@ def bench_many(args, wl) -> dict:
         "us_per_gemm_host_launched": round(ms_gemm_events * 1e3, 3),
         "gemm_gbs": round(gemm_gbs, 1),
         "gemm_tflops": round(gemm_tflops, 2),
-        "roofline_floor_us": {"hbm": round(t_hbm * 1e6, 2),
-                              ("mfma_i8" if route == "i8mc" else "mfma_f16"): round(t_mfma * 1e6, 2)},
+        "roofline_floor_us": {"hbm": round(t_hbm * 1e6, 2), "mfma_i8": round(t_mfma * 1e6, 2)},
         "eight_vector_kernel": {"us_for_all_vectors": round(ms_eight * 1e3, 3),
                                 "launches": (nvec + 7) // 8,
                                 "speedup_of_matrix_cores": round(ms_eight / ms_gemm, 2)},
-        "eight_vector_integer_matrix_cores": {"us_for_all_vectors": round(ms_eight_i8 * 1e3, 3),
-                                              "launches": (nvec + 7) // 8,
-                                              "speedup_of_matrix_cores": round(ms_eight_i8 / ms_gemm, 2)},
+        "eight_vector_integer_matrix_cores": None if ms_eight_i8 is None else {
+            "us_for_all_vectors": round(ms_eight_i8 * 1e3, 3), "launches": (nvec + 7) // 8,
+            "speedup_of_matrix_cores": round(ms_eight_i8 / ms_gemm, 2)},
         "roofline": roof,
         "setup_s": round(setup_s, 1),
     }

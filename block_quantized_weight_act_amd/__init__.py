@@ -327,7 +327,7 @@ def qgemv_debug_partials(wtype, w, xq, xd, P, S, rows: int, cols: int, nvec: int
         rows, cols, nvec, wsp, wsb, _stream(stream, P)))
 
 
-ROUTES = {1: "vector", 2: "i8mc", 3: "mc", 4: "grouped"}
+ROUTES = {1: "vector", 2: "i8mc", 3: "mc", 4: "grouped", 5: "mc32"}
 
 
 def qgemv_route(wtype, rows: int, cols: int, nvec: int = 1) -> str:

@@ -318,9 +318,9 @@ struct McPlan {
     int nt, row_tiles, groups, splits, sbps;
 };
 
-// More than kMaxVec vectors for a format without a matrix-core path: groups of kMaxVec.
+// More than kMaxVec vectors for a format without a matrix-core path (Q6_K): groups of kMaxVec.
 bool grouped_shape_ok(int wtype, int64_t rows, int64_t cols, int32_t nvec) {
-    return type_ok(wtype) && wtype != QGEMV_Q4K && nvec > kMaxVec && nvec <= kMaxBatch &&
+    return wtype == QGEMV_Q6K && nvec > kMaxVec && nvec <= kMaxBatch &&
            shape_ok_t(wtype, rows, cols, 1) &&
            static_cast<int64_t>(nvec) * cols < (int64_t{1} << 34);
 }
@@ -417,6 +417,97 @@ int run_mc(const void *w, const int8_t *xq, const float *xd, float *y, int32_t *
     if (e != hipSuccess) return hip_fail(e);
     if (!debug && p.splits > 1) {
         e = launch_splitk_reduce(parts, y, static_cast<int64_t>(nvec) * rows, p.splits, stream);
+        if (e != hipSuccess) return hip_fail(e);
+    }
+    return QGEMV_OK;
+}
+
+// Q8_0 and Q4_0 with more than kMaxVec vectors: the integer matrix cores (gemm_q32.hip), one
+// pass over the weights for up to 256 vectors. Workgroups of 32 x 32 tiles: vw tiles of 32
+// vectors (1, 2 or 4 for 1, 2, 3+ tiles) by 4 / vw tiles of 32 rows; the columns are split
+// when the row tiles and vector groups alone give fewer than two workgroups per CU (the
+// splits added by the ordered reduce).
+bool q32mc_shape_ok(int wtype, int64_t rows, int64_t cols, int32_t nvec) {
+    return (wtype == QGEMV_Q8_0 || wtype == QGEMV_Q4_0) && nvec > kMaxVec && nvec <= kMaxBatch &&
+           shape_ok_t(wtype, rows, cols, 1) &&
+           static_cast<int64_t>(nvec) * cols < (int64_t{1} << 34);
+}
+
+struct Q32McPlan {
+    int vw, groups, row_tiles, splits, bps;
+};
+
+Q32McPlan make_q32mc_plan(int64_t rows, int64_t cols, int32_t nvec) {
+    Q32McPlan p{};
+    const int vtiles = (nvec + 31) / 32;
+    p.vw = vtiles >= 3 ? 4 : vtiles;
+    const int rw = 4 / p.vw;
+    p.groups = (vtiles + p.vw - 1) / p.vw;
+    p.row_tiles = static_cast<int>((rows + 32 * rw - 1) / (32 * rw));
+    const int64_t nb = cols / 32;
+    const int64_t steps = (nb + 3) / 4;
+    const int64_t base = static_cast<int64_t>(p.row_tiles) * p.groups;
+    const int64_t want = 2 * 256;
+    const int64_t splits = base < want ? std::min<int64_t>(steps, (want + base - 1) / base) : 1;
+    p.bps = static_cast<int>(4 * ((steps + splits - 1) / splits));
+    p.splits = static_cast<int>((nb + p.bps - 1) / p.bps);
+    return p;
+}
+
+size_t q32mc_ws_bytes(const Q32McPlan &p, int64_t rows, int32_t nvec) {
+    return p.splits > 1 ? static_cast<size_t>(p.splits) * nvec * rows * sizeof(float) : 0;
+}
+
+// y (or, with P, the debug partials P and S) of a Q8_0 / Q4_0 product with many vectors.
+int run_q32mc(int wtype, const void *w, const int8_t *xq, const float *xd, float *y, int32_t *P,
+              int32_t *S, int64_t rows, int64_t cols, int32_t nvec, void *ws, size_t ws_bytes,
+              hipStream_t stream) {
+    const bool debug = P != nullptr;
+    if (!q32mc_shape_ok(wtype, rows, cols, nvec)) return QGEMV_EINVAL;
+    const size_t ybytes = static_cast<size_t>(nvec) * rows * sizeof(float);
+    const size_t pbytes = static_cast<size_t>(nvec) * rows * (cols / 32) * sizeof(int32_t);
+    int st = check_gemv_args_n(wtype, w, xq, xd, debug ? static_cast<const void *>(P) : y,
+                               debug ? pbytes : ybytes, rows, cols, nvec);
+    if (st != QGEMV_OK) return st;
+    const size_t wb = weight_bytes(wtype, rows, cols);
+    const size_t qb = static_cast<size_t>(nvec) * cols;
+    const size_t db = static_cast<size_t>(nvec) * (cols / 32) * sizeof(float);
+    if (debug) {
+        const size_t sbytes = static_cast<size_t>(nvec) * (cols / 32) * sizeof(int32_t);
+        if (!S) return QGEMV_EINVAL;
+        if (!aligned(S, 4)) return QGEMV_EALIGN;
+        if (overlaps(S, sbytes, P, pbytes) || overlaps(S, sbytes, w, wb) ||
+            overlaps(S, sbytes, xq, qb) || overlaps(S, sbytes, xd, db))
+            return QGEMV_EINVAL;
+    }
+    const Q32McPlan p = make_q32mc_plan(rows, cols, nvec);
+    const size_t need = debug ? 0 : q32mc_ws_bytes(p, rows, nvec);
+    if (need > 0) {
+        if (!ws || ws_bytes < need) return QGEMV_EWORKSPACE;
+        if (!aligned(ws, 4)) return QGEMV_EALIGN;
+        if (overlaps(ws, need, w, wb) || overlaps(ws, need, y, ybytes) || overlaps(ws, need, xq, qb) ||
+            overlaps(ws, need, xd, db))
+            return QGEMV_EINVAL;
+    }
+    GemmArgs a{};
+    a.w = static_cast<const uint8_t *>(w);
+    a.xq = xq;
+    a.xd = xd;
+    a.out = debug ? nullptr : (need > 0 ? static_cast<float *>(ws) : y);
+    a.P = P;
+    a.S = S;
+    a.rows = static_cast<int32_t>(rows);
+    a.nb = static_cast<int32_t>(cols / 32);
+    a.nvec = nvec;
+    a.sb_per_split = p.bps;
+    a.row_tiles = p.row_tiles;
+    a.groups = p.groups;
+    a.splits = p.splits;
+    hipError_t e = launch_gemm_q32_mc(wtype, a, p.vw, debug, stream);
+    if (e != hipSuccess) return hip_fail(e);
+    if (need > 0) {
+        e = launch_splitk_reduce(static_cast<const float *>(ws), y,
+                                 static_cast<int64_t>(nvec) * rows, p.splits, stream);
         if (e != hipSuccess) return hip_fail(e);
     }
     return QGEMV_OK;
@@ -718,6 +809,8 @@ int qgemv_quantize_act(const float *x, int8_t *xq, float *xd, int64_t cols, int3
 
 size_t qgemv_workspace_bytes(int wtype, int64_t rows, int64_t cols, int32_t nvec) {
     if (i8_auto(wtype, rows, cols, nvec)) return i8_ws_bytes(make_i8_plan(rows, cols), rows, nvec);
+    if (q32mc_shape_ok(wtype, rows, cols, nvec))
+        return q32mc_ws_bytes(make_q32mc_plan(rows, cols, nvec), rows, nvec);
     if (mc_shape_ok(wtype, rows, cols, nvec))
         return mc_ws_bytes(make_mc_plan(rows, cols, nvec), rows, cols, nvec);
     if (grouped_shape_ok(wtype, rows, cols, nvec)) {
@@ -776,6 +869,9 @@ int qgemv_batch(int wtype, const void *w, const int8_t *xq, const float *xd, flo
     if (mc_shape_ok(wtype, rows, cols, nvec))
         return run_mc(w, xq, xd, y, nullptr, nullptr, rows, cols, nvec, workspace,
                       workspace_bytes, stream);
+    if (q32mc_shape_ok(wtype, rows, cols, nvec))
+        return run_q32mc(wtype, w, xq, xd, y, nullptr, nullptr, rows, cols, nvec, workspace,
+                         workspace_bytes, stream);
     if (grouped_shape_ok(wtype, rows, cols, nvec)) {
         // more than kMaxVec vectors without a matrix-core path: the vector kernel on groups of
         // up to kMaxVec vectors (each group one pass over the weights); every argument is
@@ -940,6 +1036,7 @@ int qgemv_multi_fused(const qgemv_matrix *mats, int32_t nmats, const float *x, i
 int qgemv_route(int wtype, int64_t rows, int64_t cols, int32_t nvec) {
     if (i8_auto(wtype, rows, cols, nvec)) return QGEMV_ROUTE_I8MC;
     if (mc_shape_ok(wtype, rows, cols, nvec)) return QGEMV_ROUTE_MC;
+    if (q32mc_shape_ok(wtype, rows, cols, nvec)) return QGEMV_ROUTE_MC32;
     if (grouped_shape_ok(wtype, rows, cols, nvec)) return QGEMV_ROUTE_GROUPED;
     if (shape_ok_t(wtype, rows, cols, nvec)) return QGEMV_ROUTE_VECTOR;
     return 0;
@@ -1015,6 +1112,8 @@ int qgemv_debug_partials(int wtype, const void *w, const int8_t *xq, const float
         return run_mc(w, xq, xd, nullptr, P, S, rows, cols, nvec, workspace, workspace_bytes,
                       stream);
     }
+    if (q32mc_shape_ok(wtype, rows, cols, nvec))
+        return run_q32mc(wtype, w, xq, xd, nullptr, P, S, rows, cols, nvec, nullptr, 0, stream);
     const int64_t nsub = wtype == QGEMV_Q6K ? cols / 16 : cols / 32;
     const size_t pbytes = static_cast<size_t>(nvec) * rows * nsub * sizeof(int32_t);
     int st = check_gemv_args(wtype, w, xq, xd, P, pbytes, rows, cols, nvec);

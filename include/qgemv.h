@@ -193,8 +193,12 @@ int qgemv_q6k(const void *w, const int8_t *xq, const float *xd, float *y, int64_
  * products P and sums S, then the same float32 scaling, so y lies within the
  * same bound of the exact product; the float path's workspace
  * (qgemv_workspace_bytes) holds the staged activation and, for matrices with
- * few rows, partial sums. The other types with 9 <= nvec <=
- * QGEMV_MAX_BATCH run the vector kernels on groups of up to 8 vectors, one
+ * few rows, partial sums. Q8_0 and Q4_0 with 9 <= nvec <= QGEMV_MAX_BATCH run
+ * on the integer matrix cores too (v_mfma_i32_32x32x32_i8: one 32-weight block
+ * of 32 rows against 32 vectors per product, P exact; Q4_0 subtracts 8 S in
+ * integer), one pass over the weights; their workspace holds partial sums of
+ * column splits when the matrix has few rows. Q6_K with 9 <= nvec <=
+ * QGEMV_MAX_BATCH runs the vector kernels on groups of up to 8 vectors, one
  * after another on the stream (one pass over the weights per group; the
  * workspace is that of 8 vectors, shared by the groups).
  */
@@ -223,13 +227,16 @@ int qgemv_batch_scratch(int wtype, const void *w, const int8_t *xq, const float 
 
 /* Which kernels qgemv_batch (and qgemv_fused, qgemv_debug_partials) run for a
  * shape: the vector kernels, the integer matrix cores (qgemv_batch_i8mc), the
- * float matrix cores for 17..QGEMV_MAX_BATCH Q4_K vectors, or the vector kernels
- * on groups of 8 vectors; 0 for an invalid type or shape. Host only. */
+ * float matrix cores for 17..QGEMV_MAX_BATCH Q4_K vectors, the integer matrix
+ * cores for 9..QGEMV_MAX_BATCH Q8_0 or Q4_0 vectors (QGEMV_ROUTE_MC32), or the
+ * vector kernels on groups of 8 vectors (Q6_K); 0 for an invalid type or shape.
+ * Host only. */
 enum qgemv_route_kind {
     QGEMV_ROUTE_VECTOR = 1,
     QGEMV_ROUTE_I8MC = 2,
     QGEMV_ROUTE_MC = 3,
-    QGEMV_ROUTE_GROUPED = 4
+    QGEMV_ROUTE_GROUPED = 4,
+    QGEMV_ROUTE_MC32 = 5
 };
 int qgemv_route(int wtype, int64_t rows, int64_t cols, int32_t nvec);
 
@@ -392,7 +399,9 @@ int qgemv_graph_destroy(qgemv_graph *graph);
 /*
  * Test hook: the exact integer partials of the same kernels (for Q4_K with
  * more than 8 vectors, of the matrix-core kernel, which needs the workspace of
- * qgemv_workspace_bytes(); elsewhere workspace may be NULL).
+ * qgemv_workspace_bytes(); elsewhere workspace may be NULL; Q8_0 and Q4_0 take
+ * 9..QGEMV_MAX_BATCH vectors here too). For Q4_0 and Q8_0, P [nvec][rows][cols/32]
+ * is the block's sum of (q - 8) * xq or q * xq.
  * P int32: Q4_K [nvec][rows][cols/32] (sum of q * xq per 32-column
  * sub-block), Q6_K [nvec][rows][cols/16] (sum of (q - 32) * xq per 16-column
  * sub-block). S int32 [nvec][cols/32]: sum of xq per activation block.

@@ -103,7 +103,10 @@ def test_routes():
     assert qg.qgemv_route("q4k", 16384, 2048, 12) == "i8mc"         # 9..16 vectors: always
     assert qg.qgemv_route("q4k", 512, 512, 16) == "i8mc"
     assert qg.qgemv_route("q4k", 512, 512, 17) == "mc"
-    assert qg.qgemv_route("q40", 16384, 2048, 64) == "grouped"
+    assert qg.qgemv_route("q40", 16384, 2048, 64) == "mc32"
+    assert qg.qgemv_route("q80", 262144, 1536, 9) == "mc32"
+    assert qg.qgemv_route("q80", 262144, 1536, 8) == "vector"
+    assert qg.qgemv_route("q6k", 16384, 2048, 64) == "grouped"
     assert qg._load().qgemv_route(1, 8, 500, 1) == 0
     assert qg._load().qgemv_route(1, 8, 512, 300) == 0
 
@@ -287,6 +290,19 @@ def test_matrix_core_path_limits_on_the_host():
     assert _call_batch(nvec=64, xq=A + (1 << 30) + 4) == EALIGN
     plan = qg.Plan()
     assert lib.qgemv_plan_for(1, 64, 1024, 9, ctypes.byref(plan)) == EINVAL
+
+
+def test_mc32_workspace_and_limits():
+    """Q8_0 / Q4_0 with many vectors: partial sums only when the columns are split (few rows),
+    refused before any launch without them; more than 256 vectors refused."""
+    assert qg.qgemv_workspace_bytes("q80", 262144, 1536, 64) == 0
+    assert qg.qgemv_workspace_bytes("q40", 16384, 2048, 64) == 2 * 64 * 16384 * 4
+    assert _call_batch(wtype=3, rows=16384, cols=2048, nvec=64) == EWORKSPACE
+    assert _call_batch(wtype=4, nvec=257) == EINVAL
+    assert _call_batch(wtype=4, cols=1000, nvec=20) == EINVAL
+    lib = qg._load()
+    assert lib.qgemv_debug_partials(4, A, A + (1 << 30), A + (2 << 30), A + (3 << 30), None, 64,
+                                    1024, 20, None, 0, None) == EINVAL          # no S
 
 
 def test_scratch_entry_point_rejects_bad_arguments():

@@ -1,0 +1,116 @@
+"""GPU parity of the integer matrix-core path for the 32-weight formats (Q8_0 and Q4_0 with
+9..256 activation vectors) against the CPU oracle, through the C ABI: integer partials P and
+activation block sums S bit-exact (debug form), every y within 1e-5 of sum_i |w_i| |x_i| of
+its row and vector. Shapes cover 1, 2 and 4 vector tiles of 32 per workgroup, one and two
+vector groups, ragged row tiles, widths that are not a whole number of 4-block steps, column
+splits (few rows) and one pass (many rows), the int32 extremes of both formats, and the
+262144 x 1536 vocabulary projection with 64 vectors (sampled rows)."""
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+gu = pytest.importorskip("gpu_util")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    gu.require_gpu()
+
+
+def _say(*a):
+    print("[mc32]", *a, flush=True)
+
+
+def _check(wtype, wbuf, rows, cols, x, debug=True):
+    import block_quantized_weight_act_amd as qg
+    nvec = x.shape[0]
+    assert qg.qgemv_route(wtype, rows, cols, nvec) == "mc32"
+    rq, rd = oracle.quantize_act(x)
+    xq, xd = gu.quantize_act(x)
+    assert np.array_equal(gu.host(xq), rq)
+    ref = oracle.gemv(wtype, wbuf, rows, cols, rq, rd, partials=debug)
+    wt = gu.dev(wbuf)
+    y = gu.gemv(wtype, wt, xq, xd, rows, cols, nvec)
+    gu.assert_within_bound(y, ref)
+    if debug:
+        P, S = gu.partials(wtype, wt, xq, xd, rows, cols, nvec)
+        assert np.array_equal(S, oracle.block_sums(rq))
+        assert np.array_equal(P, ref["P"])
+    return y
+
+
+SHAPES = [
+    # (rows, cols, nvec)
+    (300, 1056, 9),       # one tile of 32 vectors (23 idle), 33 blocks (a ragged step), split
+    (257, 768, 33),       # two tiles
+    (128, 2048, 64),      # one row tile, split
+    (1000, 1536, 100),    # four tiles (100 of 128)
+    (131, 32, 128),       # one block: no split possible
+    (64, 4096, 129),      # two vector groups (128 + 1)
+    (513, 1024, 256),     # two full groups of 128
+    (4100, 1536, 40),     # enough rows for one pass (no split)
+    (37, 2592, 77),       # three tiles, ragged everything
+]
+
+
+@pytest.mark.parametrize("rows,cols,nvec", SHAPES)
+@pytest.mark.parametrize("wtype", ["q80", "q40"])
+def test_parity(wtype, rows, cols, nvec):
+    _say(wtype, rows, cols, nvec)
+    rng = np.random.default_rng(rows * 31 + cols + nvec + (wtype == "q40"))
+    w = (rng.standard_normal((rows, cols)) * 0.02).astype(np.float32)
+    w[0, :64] = 0.0                                     # zero weight blocks: exactly 0
+    x = (rng.standard_normal((nvec, cols)) * rng.choice([1e-3, 1.0, 40.0], size=(nvec, 1))).astype(np.float32)
+    x[0, 32:64] = 0.0
+    _check(wtype, oracle.quantize(wtype, w), rows, cols, x)
+
+
+def test_integer_extremes():
+    rows, cols, nvec = 70, 256, 12
+    img = oracle.q80_pack_block(np.float32(1.0), np.full(32, 127, np.int8))
+    t80 = oracle.q32_tensor("q80", [img] * (rows * cols // 32))
+    _check("q80", t80, rows, cols, np.full((nvec, cols), 3.0, np.float32))     # P = 516128
+    img0 = oracle.q40_pack_block(0x3C00, np.zeros(32, np.uint8))
+    img15 = oracle.q40_pack_block(0x3C00, np.full(32, 15, np.uint8))
+    t40 = oracle.q32_tensor("q40", [img0, img15] * (rows * cols // 64))
+    _check("q40", t40, rows, cols, np.full((nvec, cols), -3.0, np.float32))    # P = +-32512
+
+
+def test_zero_weights_give_exact_zero():
+    rows, cols, nvec = 96, 512, 20
+    x = np.random.default_rng(3).standard_normal((nvec, cols)).astype(np.float32)
+    for wtype in ("q80", "q40"):
+        y = _check(wtype, oracle.quantize(wtype, np.zeros((rows, cols), np.float32)), rows, cols, x,
+                   debug=False)
+        assert np.all(y == 0)
+
+
+def test_vocabulary_projection_64_vectors_sampled():
+    """Q8_0 262144 x 1536 with 64 vectors, the workload the many-vector bench times: the
+    weights are the oracle's tensor (built in row pieces), the product runs whole on the GPU,
+    and 4096 evenly spaced rows are checked against the oracle."""
+    import torch
+    import block_quantized_weight_act_amd as qg
+    wl = synth.WORKLOADS["q80_262144x1536"]
+    rows, cols, nvec = wl.rows, wl.cols, 64
+    _say("vocabulary projection", rows, cols, nvec)
+    chunk = 32768
+    parts = [(oracle.quantize("q80", wl.weight_block(r0, min(rows, r0 + chunk))),
+              min(chunk, rows - r0)) for r0 in range(0, rows, chunk)]
+    wbuf = oracle.concat_rows("q80", parts, cols)
+    x = np.stack([synth.normal_f32(wl.seed_x + v, 0, cols, 1.0) for v in range(nvec)])
+    rq, rd = oracle.quantize_act(x)
+    xq, xd = gu.dev(rq), gu.dev(rd)
+    y = torch.full((nvec, rows), float("nan"), dtype=torch.float32, device=gu.DEV)
+    nbytes = qg.qgemv_workspace_bytes("q80", rows, cols, nvec)
+    ws = torch.empty(max(nbytes, 4), dtype=torch.uint8, device=gu.DEV) if nbytes else None
+    qg.qgemv_batch("q80", gu.dev(wbuf), xq, xd, y, rows, cols, nvec, workspace=ws)
+    sample = np.linspace(0, rows - 1, 4096).astype(np.int64)
+    sampled = oracle.from_planes([p[sample] for p in oracle.planes("q80", wbuf, rows, cols)])
+    ref = oracle.gemv("q80", sampled, sample.size, cols, rq, rd)
+    gu.assert_within_bound(gu.host(y)[:, sample], ref)

@@ -125,13 +125,15 @@ def test_workspace_and_limits():
 
 
 @pytest.mark.parametrize("wtype,rows,cols,nvec", [
-    ("q6k", 300, 1024, 9), ("q6k", 2048, 8192, 20), ("q40", 513, 800, 17), ("q80", 77, 1536, 40),
-    ("q40", 4000, 2048, 64),
+    ("q6k", 300, 1024, 9), ("q6k", 2048, 8192, 20), ("q6k", 513, 768, 17), ("q6k", 77, 1536, 40),
+    ("q6k", 4000, 2048, 64),
 ])
 def test_other_formats_many_vectors_grouped(wtype, rows, cols, nvec):
-    """Formats without a matrix-core path take more than 8 vectors as groups of up to 8 on the
-    vector kernel: every y within the bound, and each group's y equals that group's own
-    product bit for bit."""
+    """Q6_K (no matrix-core path) takes more than 8 vectors as groups of up to 8 on the vector
+    kernel: every y within the bound, and each group's y equals that group's own product bit
+    for bit."""
+    import block_quantized_weight_act_amd as qg
+    assert qg.qgemv_route(wtype, rows, cols, nvec) == "grouped"
     _say("grouped", wtype, rows, cols, nvec)
     rng = np.random.default_rng(rows + cols + nvec)
     w = (rng.standard_normal((rows, cols)) * 0.02).astype(np.float32)
