@@ -8,6 +8,11 @@
 // the halves: act_slice_issue starts the slice's global loads, act_slice_finish consumes
 // them. Loads complete in issue order, so the slice is waited for without waiting for the
 // weight loads issued after it, and the weights' HBM latency overlaps the slice's work.
+//
+// In the fused form a workgroup quantizes a span of column chunks: `nch` consecutive chunks
+// from chunk `ch0` (one chunk, blockIdx.y, for a workgroup that works on one column chunk; all
+// of the row's chunks for a workgroup that splits the columns among its waves), and each wave
+// then reads its own chunk `rel` of the span.
 #pragma once
 
 #include "device_common.h"
@@ -27,11 +32,17 @@ struct FusedAct {
     static constexpr int kSlots = kQuads >= 4 * 256 ? 4 : (kQuads + 255) / 256;
 };
 
-// LDS bytes the fused form needs: 32 code bytes and one float32 scale per block of the slice.
+// LDS bytes the fused form needs: 32 code bytes and one float32 scale per block of the slice
+// (of one column chunk; a span of nch chunks takes nch times as much).
 template <int V, int T, int NC>
 constexpr int act_slice_lds_bytes() {
     return FusedAct<V, T, NC>::kBlocks * (32 + 4);
 }
+
+// The column chunks a workgroup's fused form quantizes, and this wave's chunk among them.
+struct ChunkSpan {
+    int ch0, nch, rel;
+};
 
 // What act_slice_issue leaves in flight for act_slice_finish: the fused form's first round of
 // float32 quads (the plain form loads straight into the slice registers).
@@ -42,54 +53,55 @@ struct ActPending {
 
 namespace fused_detail {
 
-// Quad qd of the chunk: block blk = qd / 8 is vector blk / (T NC) and column block
-// chunk0 + blk % (T NC); elem is the offset of its 4 floats in x (and of its codes in
+// Quad qd of the span: block blk = qd / 8 is vector blk / (nch T NC) and column block
+// ch0 T NC + blk % (nch T NC); elem is the offset of its 4 floats in x (and of its codes in
 // xq_out). True when the quad exists.
 template <int V, int T, int NC>
-__device__ __forceinline__ bool quad_at(const GemvArgs &a, int qd, int64_t &elem, int &v,
-                                        int &gc) {
+__device__ __forceinline__ bool quad_at(const GemvArgs &a, const ChunkSpan &sp, int qd,
+                                        int64_t &elem, int &v, int &gc) {
     const int blk = qd >> 3;
-    v = blk / (T * NC);
-    gc = static_cast<int>(blockIdx.y) * T * NC + blk % (T * NC);
+    const int span = sp.nch * T * NC;
+    v = blk / span;
+    gc = sp.ch0 * T * NC + (blk - v * span);
     elem = v * (static_cast<int64_t>(a.nchunks) * 32) + 32 * static_cast<int64_t>(gc) +
            4 * (qd & 7);
-    return qd < FusedAct<V, T, NC>::kQuads && gc < a.nchunks;
+    return qd < FusedAct<V, T, NC>::kQuads * sp.nch && gc < a.nchunks;
 }
 
 template <int V, int T, int NC>
-__device__ __forceinline__ void load_round(const GemvArgs &a, int base,
+__device__ __forceinline__ void load_round(const GemvArgs &a, const ChunkSpan &sp, int base,
                                            float4 (&xv)[FusedAct<V, T, NC>::kSlots]) {
 #pragma unroll
     for (int i = 0; i < FusedAct<V, T, NC>::kSlots; i++) {
         int64_t elem;
         int v, gc;
         const bool ok = quad_at<V, T, NC>(
-            a, base + i * a.threads + static_cast<int>(threadIdx.x), elem, v,
-            gc);
+            a, sp, base + i * a.threads + static_cast<int>(threadIdx.x), elem, v, gc);
         xv[i] = ok ? *reinterpret_cast<const float4 *>(a.x + elem)
                    : make_float4(0.f, 0.f, 0.f, 0.f);
     }
 }
 
 // Quantize one round into LDS (codes word qd, then the scale of block qd / 8 after all the
-// codes); the first workgroup of the column chunk also stores them to xq_out / xd_out.
+// span's codes); the first workgroup of the span also stores them to xq_out / xd_out.
 template <int V, int T, int NC>
-__device__ __forceinline__ void store_round(const GemvArgs &a, int base,
+__device__ __forceinline__ void store_round(const GemvArgs &a, const ChunkSpan &sp, int base,
                                             const float4 (&xv)[FusedAct<V, T, NC>::kSlots]) {
     using F = FusedAct<V, T, NC>;
     extern __shared__ uint4 lds[];
+    const int quads = F::kQuads * sp.nch;
     uint32_t *s_codes = reinterpret_cast<uint32_t *>(lds);
-    float *s_scale = reinterpret_cast<float *>(lds + 2 * F::kBlocks);
+    float *s_scale = reinterpret_cast<float *>(lds + 2 * F::kBlocks * sp.nch);
 #pragma unroll
     for (int i = 0; i < F::kSlots; i++) {
         const int first = base + i * a.threads;   // the same for the workgroup
-        if (first >= F::kQuads) break;
+        if (first >= quads) break;
         const int qd = first + static_cast<int>(threadIdx.x);
         int64_t elem;
         int v, gc;
-        const bool ok = quad_at<V, T, NC>(a, qd, elem, v, gc);
+        const bool ok = quad_at<V, T, NC>(a, sp, qd, elem, v, gc);
         const ActQuad q = quantize_act_quad(xv[i]);   // every lane: the block max is cross-lane
-        if (qd < F::kQuads) {
+        if (qd < quads) {
             s_codes[qd] = q.codes;
             if ((qd & 7) == 0) s_scale[qd >> 3] = q.scale;
         }
@@ -103,15 +115,15 @@ __device__ __forceinline__ void store_round(const GemvArgs &a, int base,
 }  // namespace fused_detail
 
 template <int V, int T, int NC, bool FUSED>
-__device__ __forceinline__ void act_slice_issue(const GemvArgs &a, const int (&g)[NC],
-                                                const bool (&cv)[NC], uint32_t (&xw)[V][NC][8],
-                                                float (&xs)[V][NC],
+__device__ __forceinline__ void act_slice_issue(const GemvArgs &a, const ChunkSpan &sp,
+                                                const int (&g)[NC], const bool (&cv)[NC],
+                                                uint32_t (&xw)[V][NC][8], float (&xs)[V][NC],
                                                 ActPending<V, T, NC, FUSED> &pend) {
     if constexpr (FUSED) {
         (void)g; (void)cv; (void)xw; (void)xs;
-        fused_detail::load_round<V, T, NC>(a, 0, pend.xv);
+        fused_detail::load_round<V, T, NC>(a, sp, 0, pend.xv);
     } else {
-        (void)pend;
+        (void)pend; (void)sp;
         const int nsub = a.nchunks;
         const int64_t cols = static_cast<int64_t>(nsub) * 32;
 #pragma unroll
@@ -135,25 +147,27 @@ __device__ __forceinline__ void act_slice_issue(const GemvArgs &a, const int (&g
 }
 
 template <int V, int T, int NC, bool FUSED>
-__device__ __forceinline__ void act_slice_finish(const GemvArgs &a, const bool (&cv)[NC], int t,
+__device__ __forceinline__ void act_slice_finish(const GemvArgs &a, const ChunkSpan &sp,
+                                                 const bool (&cv)[NC], int t,
                                                  uint32_t (&xw)[V][NC][8], float (&xs)[V][NC],
                                                  ActPending<V, T, NC, FUSED> &pend) {
     if constexpr (FUSED) {
         using F = FusedAct<V, T, NC>;
         const int round = F::kSlots * a.threads;
-        fused_detail::store_round<V, T, NC>(a, 0, pend.xv);
-        for (int base = round; base < F::kQuads; base += round) {
-            fused_detail::load_round<V, T, NC>(a, base, pend.xv);
-            fused_detail::store_round<V, T, NC>(a, base, pend.xv);
+        const int quads = F::kQuads * sp.nch;
+        fused_detail::store_round<V, T, NC>(a, sp, 0, pend.xv);
+        for (int base = round; base < quads; base += round) {
+            fused_detail::load_round<V, T, NC>(a, sp, base, pend.xv);
+            fused_detail::store_round<V, T, NC>(a, sp, base, pend.xv);
         }
         __syncthreads();
         extern __shared__ uint4 lds[];
-        const float *s_scale = reinterpret_cast<const float *>(lds + 2 * F::kBlocks);
+        const float *s_scale = reinterpret_cast<const float *>(lds + 2 * F::kBlocks * sp.nch);
 #pragma unroll
         for (int v = 0; v < V; v++) {
 #pragma unroll
             for (int k = 0; k < NC; k++) {
-                const int blk = v * T * NC + t + T * k;
+                const int blk = (v * sp.nch + sp.rel) * T * NC + t + T * k;
                 const uint4 lo = cv[k] ? lds[2 * blk] : make_uint4(0, 0, 0, 0);
                 const uint4 hi = cv[k] ? lds[2 * blk + 1] : make_uint4(0, 0, 0, 0);
                 xw[v][k][0] = lo.x; xw[v][k][1] = lo.y; xw[v][k][2] = lo.z; xw[v][k][3] = lo.w;
@@ -162,7 +176,7 @@ __device__ __forceinline__ void act_slice_finish(const GemvArgs &a, const bool (
             }
         }
     } else {
-        (void)a; (void)cv; (void)t; (void)xw; (void)xs; (void)pend;
+        (void)a; (void)sp; (void)cv; (void)t; (void)xw; (void)xs; (void)pend;
     }
 }
 

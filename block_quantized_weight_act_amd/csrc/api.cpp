@@ -117,8 +117,11 @@ int64_t target_waves(int32_t nvec) { return nvec <= 2 ? 256 * 64 : 256 * 16; }
 // (nvec * NC <= 8). When a row has more than 256 chunks (cols > 8192) or rows alone are too
 // few to give every CU work, the columns are split.
 // Lanes per row and chunks per lane for a row of `cols` columns (see make_plan). With
-// one_pass set, only geometries that cover the whole row in one pass; false if there is none.
-bool choose_geometry(int64_t cols, int32_t nvec, bool one_pass, int &best_t, int &best_nc) {
+// one_pass set, only geometries that cover the whole row in one pass; with fit_waves, only
+// those whose passes (column chunks) a workgroup can split among its waves; false if there is
+// none.
+bool choose_geometry(int64_t cols, int32_t nvec, bool one_pass, int &best_t, int &best_nc,
+                     bool fit_waves = false) {
     const int64_t nchunks = cols / 32;
     bool found = false;
     double best_cost = 1e30;
@@ -128,6 +131,7 @@ bool choose_geometry(int64_t cols, int32_t nvec, bool one_pass, int &best_t, int
             const int64_t per = static_cast<int64_t>(t) * nc;
             const int64_t passes = (nchunks + per - 1) / per;
             if (one_pass && passes > 1) continue;
+            if (fit_waves && passes > gemv_max_waves(nvec, t, nc)) continue;
             const double waste = 1.0 - static_cast<double>(nchunks) / (passes * per);
             // idle lanes cost bandwidth in flight; split passes cost a workspace round trip
             const double cost = waste + 0.02 * (passes - 1) - 0.01 * nc;
@@ -276,18 +280,22 @@ int run_gemv(int wtype, const void *w, const Activation &act, float *y, int64_t 
     a.rows = static_cast<int32_t>(rows);
     a.nb = static_cast<int32_t>(cols / block_cols(wtype));
     a.nchunks = static_cast<int32_t>(cols / 32);
-    // The unfused form with column splits: the splits inside the workgroup (its waves in sets
-    // of `splits`, their row sums added in LDS in chunk order), one launch and the same y bit
-    // for bit as the split-K reduce, with as many waves in all as the plan's two-pass form but
-    // at most 4096 (one resident round at 16 waves per CU, so every workgroup loops over its
-    // steps with the next loads in flight: 4096 x 16384 from codes 8.7 us against 10.4 us with
-    // 8192 waves on MI355X). The workspace is still required (the ABI's contract is per
-    // shape), though not touched.
+    // Column splits: the splits inside the workgroup (its waves in sets of `splits`, their row
+    // sums added in LDS in chunk order), one launch and the same y bit for bit as the split-K
+    // reduce, with as many waves in all as the plan's two-pass form but at most 4096 (one
+    // resident round at 16 waves per CU, so every workgroup loops over its steps with the next
+    // loads in flight: 4096 x 16384 from codes 8.7 us against 10.4 us with 8192 waves on
+    // MI355X). In the fused form the workgroup quantizes every chunk of the row, so the slices
+    // of all chunks must fit in LDS. The workspace is still required (the ABI's contract is
+    // per shape), though not touched.
     const int maxw = gemv_max_waves(nvec, plan.lanes_per_row, plan.chunks_per_lane);
-    if (need > 0 && !act.x && plan.splits <= maxw) {
-        const int wpb = plan.waves_per_block % plan.splits == 0
-                            ? plan.waves_per_block
-                            : plan.splits * (maxw / plan.splits);
+    const int wpb = plan.splits <= maxw && plan.waves_per_block % plan.splits == 0
+                        ? plan.waves_per_block
+                        : plan.splits * std::max(1, maxw / plan.splits);
+    const bool in_wg = need > 0 && plan.splits <= maxw &&
+                       (!act.x || gemv_split_lds_bytes(nvec, plan.lanes_per_row, plan.chunks_per_lane,
+                                                       true, plan.splits, wpb) <= kMaxSplitLds);
+    if (in_wg) {
         const int64_t waves = std::min<int64_t>(
             static_cast<int64_t>(plan.blocks) * plan.splits * plan.waves_per_block, 4096);
         const int64_t blocks = std::min<int64_t>((waves + wpb - 1) / wpb, int64_t{65535} * 64);
@@ -640,11 +648,22 @@ int run_i8(const void *w, const Activation &act, float *y, int32_t *P, int32_t *
     return QGEMV_OK;
 }
 
+// The lane geometry of a multi-matrix launch: one that covers the row in one pass if any
+// (the fewest idle lanes), else by the one-matrix planner's rule among the geometries whose
+// column chunks a workgroup can split among its waves (one wave per chunk).
+bool multi_geometry(int64_t cols, int32_t nvec, int &t, int &nc, int &splits) {
+    splits = 1;
+    if (choose_geometry(cols, nvec, true, t, nc)) return true;
+    if (!choose_geometry(cols, nvec, false, t, nc, true)) return false;
+    splits = splits_for(t, nc, cols);
+    return true;
+}
+
 int prepare_multi(const qgemv_matrix *mats, int32_t nmats, const Activation &act, int64_t cols,
                   int32_t nvec, MultiArgs &a, LaunchShape &s, double &wbytes) {
     if (!mats || nmats < 1 || nmats > kMaxMats || !shape_ok(1, cols, nvec)) return QGEMV_EINVAL;
-    int t = 0, nc = 0;
-    if (!choose_geometry(cols, nvec, true, t, nc)) return QGEMV_EINVAL;
+    int t = 0, nc = 0, splits = 1;
+    if (!multi_geometry(cols, nvec, t, nc, splits)) return QGEMV_EINVAL;
     const size_t qb = static_cast<size_t>(nvec) * cols;
     const size_t db = static_cast<size_t>(nvec) * (cols / 32) * sizeof(float);
     const size_t xb = qb * sizeof(float);
@@ -736,9 +755,12 @@ int prepare_multi(const qgemv_matrix *mats, int32_t nmats, const Activation &act
     a.nmats = nmats;
     a.steps = static_cast<int32_t>(steps);
     // The grid, then each format's share of it in proportion to its steps (at least one
-    // workgroup each).
-    const int waves = 4;
-    const int64_t want = std::min<int64_t>(steps, target_waves(nvec));
+    // workgroup each). A split row takes the one-matrix split's grid: workgroups of sets of
+    // `splits` waves, at most 4096 waves in all.
+    const int maxw = gemv_max_waves(nvec, t, nc);
+    const int waves = splits > 1 ? splits * (maxw / splits) : 4;
+    const int64_t want = splits > 1 ? std::min<int64_t>(steps * splits, 4096)
+                                    : std::min<int64_t>(steps, target_waves(nvec));
     const int64_t total = (want + waves - 1) / waves;
     int32_t blocks = 0;
     for (int i = 0; i < a.ngroups; i++) {
@@ -747,7 +769,7 @@ int prepare_multi(const qgemv_matrix *mats, int32_t nmats, const Activation &act
         fg.blocks = static_cast<int32_t>(std::max<int64_t>(1, (total * fg.steps + steps - 1) / steps));
         blocks += fg.blocks;
     }
-    s = LaunchShape{t, nc, waves, blocks, 1};
+    s = LaunchShape{t, nc, waves, blocks, splits};
     return QGEMV_OK;
 }
 
@@ -758,7 +780,18 @@ int launch_multi(const MultiArgs &a, const LaunchShape &s, int32_t nvec, hipStre
     bool one_format = true;
     for (int i = 1; i < a.nmats; i++) one_format = one_format && a.m[i].wtype == a.m[0].wtype;
     hipError_t e = hipErrorInvalidValue;
-    if (!one_format)
+    if (s.splits > 1) {
+        if (!one_format)
+            e = launch_gemv_multi_split(a, s, nvec, stream);
+        else if (a.m[0].wtype == QGEMV_Q4K)
+            e = launch_gemv_multi_split_q4k(a, s, nvec, stream);
+        else if (a.m[0].wtype == QGEMV_Q6K)
+            e = launch_gemv_multi_split_q6k(a, s, nvec, stream);
+        else if (a.m[0].wtype == QGEMV_Q4_0)
+            e = launch_gemv_multi_split_q40(a, s, nvec, stream);
+        else if (a.m[0].wtype == QGEMV_Q8_0)
+            e = launch_gemv_multi_split_q80(a, s, nvec, stream);
+    } else if (!one_format)
         e = launch_gemv_multi(a, s, nvec, stream);
     else if (a.m[0].wtype == QGEMV_Q4K)
         e = launch_gemv_multi_q4k(a, s, nvec, stream);
@@ -984,9 +1017,9 @@ int qgemv_fused(int wtype, const void *w, const float *x, int8_t *xq_out, float 
 
 int qgemv_multi_geometry(int64_t cols, int32_t nvec, int32_t *lanes_per_row,
                          int32_t *chunks_per_lane) {
-    int t = 0, nc = 0;
+    int t = 0, nc = 0, splits = 1;
     if (!lanes_per_row || !chunks_per_lane || !shape_ok(1, cols, nvec) ||
-        !choose_geometry(cols, nvec, true, t, nc))
+        !multi_geometry(cols, nvec, t, nc, splits))
         return QGEMV_EINVAL;
     *lanes_per_row = t;
     *chunks_per_lane = nc;
@@ -1019,9 +1052,15 @@ int qgemv_multi_fused(const qgemv_matrix *mats, int32_t nmats, const float *x, i
     if (st != QGEMV_OK) return st;
     // As for one matrix: with code outputs (16-byte aligned, as the product reads them) and a
     // slice that is large next to a workgroup's share of the weights, quantize once and run
-    // the product from the codes.
-    const double slice = static_cast<double>(nvec) * s.lanes * s.chunks * 32;
-    if (xq_out && aligned(xq_out, 16) && slice > 0.15 * wbytes / s.blocks) {
+    // the product from the codes. A split row whose chunks' slices do not all fit in LDS
+    // needs the codes.
+    const double slice = static_cast<double>(nvec) * s.lanes * s.chunks * 32 * s.splits;
+    const bool fits = s.splits == 1 || gemv_split_lds_bytes(nvec, s.lanes, s.chunks, true, s.splits,
+                                                            s.waves) <= kMaxSplitLds;
+    if (!fits && !(xq_out && aligned(xq_out, 16)))
+        return fail_with(QGEMV_EINVAL, "the row's activation slices do not fit in LDS: pass 16-byte "
+                                       "aligned code outputs");
+    if (!fits || (xq_out && aligned(xq_out, 16) && slice > 0.15 * wbytes / s.blocks)) {
         st = qgemv_quantize_act(x, xq_out, xd_out, cols, nvec, stream);
         if (st != QGEMV_OK) return st;
         a.act.x = nullptr;

@@ -22,4 +22,9 @@ hipError_t launch_gemv_split_q4k(const GemvArgs &a, const LaunchShape &s, int nv
     return GemvLaunch<Q4K>::launch_split(a, s, nvec, stream);
 }
 
+hipError_t launch_gemv_multi_split_q4k(const MultiArgs &a, const LaunchShape &s, int nvec,
+                                       hipStream_t stream) {
+    return GemvLaunch<Q4K>::launch_multi_split(a, s, nvec, stream);
+}
+
 }  // namespace qgemv

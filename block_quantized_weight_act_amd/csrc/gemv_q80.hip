@@ -21,4 +21,9 @@ hipError_t launch_gemv_split_q80(const GemvArgs &a, const LaunchShape &s, int nv
     return GemvLaunch<Q80>::launch_split(a, s, nvec, stream);
 }
 
+hipError_t launch_gemv_multi_split_q80(const MultiArgs &a, const LaunchShape &s, int nvec,
+                                       hipStream_t stream) {
+    return GemvLaunch<Q80>::launch_multi_split(a, s, nvec, stream);
+}
+
 }  // namespace qgemv

@@ -109,14 +109,15 @@ __device__ __forceinline__ void gemv_walk(const GemvArgs &a, const Steps &src, i
     float xs[V][NC];
     ActTerms<V, NC> at;
     ActPending<V, T, NC, FUSED> pend;
-    act_slice_issue<V, T, NC, FUSED>(a, L.g, L.cv, xw, xs, pend);
+    const ChunkSpan sp{static_cast<int>(blockIdx.y), 1, 0};
+    act_slice_issue<V, T, NC, FUSED>(a, sp, L.g, L.cv, xw, xs, pend);
     __builtin_amdgcn_sched_barrier(0);
     {
         const StepMat m = src.at(st0);   // rows (>= 1) clamped: valid for any st0
         Tile::issue(regs, m.w, m.rows, m.nb, m.local, L);
     }
     __builtin_amdgcn_sched_barrier(0);
-    act_slice_finish<V, T, NC, FUSED>(a, L.cv, L.t, xw, xs, pend);
+    act_slice_finish<V, T, NC, FUSED>(a, sp, L.cv, L.t, xw, xs, pend);
     act_terms<V, NC>(xw, at);
     if (DBG && blockIdx.x == 0 && wave == 0 && L.rsub == 0) {
 #pragma unroll
@@ -159,60 +160,101 @@ __global__ void __launch_bounds__(256) gemv_multi_fmt_kernel(MultiArgs a) {
                                                                    blockIdx.x, gridDim.x);
 }
 
-// The column split inside the workgroup (the unfused form of a plan with splits > 1): the
-// workgroup's waves come in sets of `ws` = the plan's column chunks, wave w taking chunk w % ws
-// of row step `slot` = w / ws of each workgroup step. After a step the row sums of the chunks
-// (stored by the tiles as for the split-K workspace, here into LDS) are added in chunk order,
-// the order of the split-K reduce, so y is bit-identical to the two-launch split in one launch.
-// Every wave of a workgroup runs the same number of workgroup steps (the barriers), and the
-// next step's loads go out before the sums over the chunks.
-template <class F, int V, int T, int NC>
-__global__ void __launch_bounds__(64 * gemv_max_waves(V, T, NC)) gemv_split_kernel(GemvArgs a) {
-    using Tile = typename F::template Tile<V, T, NC>;
+// The column split inside the workgroup (a plan with splits > 1): the workgroup's waves come in
+// sets of `ws` = the plan's column chunks, wave w taking chunk w % ws of row step `slot` =
+// w / ws of each workgroup step. After a step the row sums of the chunks (stored by the tiles
+// as for the split-K workspace, here into LDS) are added in chunk order, the order of the
+// split-K reduce, and written to the matrix each row step falls in, so y is bit-identical to
+// the two-launch split in one launch. In the fused form the workgroup first quantizes every
+// chunk of the row into LDS (its waves read all of them) and each wave takes its own chunk's
+// slice from there. Every wave of a workgroup runs the same number of workgroup steps (the
+// barriers), and the next step's loads go out before the sums over the chunks. `src` numbers
+// the row steps (one matrix, several matrices, or one format's matrices of a mixed launch).
+template <int V, int T, int NC, bool FUSED>
+__host__ __device__ constexpr int split_slice_lds_bytes(int ws) {
+    return FUSED ? act_slice_lds_bytes<V, T, NC>() * ws : 0;
+}
+
+template <class Tile, int V, int T, int NC, bool FUSED, class Steps>
+__device__ __forceinline__ void gemv_split_walk(const GemvArgs &a, const Steps &src, int steps,
+                                                int blk, int nblk) {
     constexpr int kStepRows = Tile::G * Tile::RPW;
-    extern __shared__ float part[];                  // [ws][V][rows_local]
+    extern __shared__ float lds_split[];
     const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
     const int ws = a.wg_splits;
     const int slots = (a.threads >> 6) / ws;
     const int split = wave % ws, slot = wave / ws;
     const LaneGeom<T, NC> L(a.nchunks, split);
-    const int groups = (a.rows + Tile::RPW - 1) / Tile::RPW;
-    const int steps = (groups + Tile::G - 1) / Tile::G;
     const int wg_steps = (steps + slots - 1) / slots;
     const int rows_local = slots * kStepRows;
+    float *part = lds_split + split_slice_lds_bytes<V, T, NC, FUSED>(ws) / 4;   // [ws][V][rows_local]
 
     typename Tile::Regs regs;
     uint32_t xw[V][NC][8];
     float xs[V][NC];
     ActTerms<V, NC> at;
-    ActPending<V, T, NC, false> pend;
-    act_slice_issue<V, T, NC, false>(a, L.g, L.cv, xw, xs, pend);
-    int wst = static_cast<int>(blockIdx.x);
+    ActPending<V, T, NC, FUSED> pend;
+    const ChunkSpan sp{0, ws, split};
+    act_slice_issue<V, T, NC, FUSED>(a, sp, L.g, L.cv, xw, xs, pend);
+    int wst = blk;
     __builtin_amdgcn_sched_barrier(0);
-    Tile::issue(regs, a.w, a.rows, a.nb, wst * slots + slot, L);   // rows clamped
+    {
+        const StepMat m = src.at(wst * slots + slot);   // rows clamped: valid for any step
+        Tile::issue(regs, m.w, m.rows, m.nb, m.local, L);
+    }
     __builtin_amdgcn_sched_barrier(0);
+    act_slice_finish<V, T, NC, FUSED>(a, sp, L.cv, L.t, xw, xs, pend);
     act_terms<V, NC>(xw, at);
-    const int stride = static_cast<int>(gridDim.x);
-    for (; wst < wg_steps; wst += stride) {
+    for (; wst < wg_steps; wst += nblk) {
         __builtin_amdgcn_sched_barrier(0);
-        // the workgroup-local rows: every local row is stored (rows past the matrix are
-        // dropped below)
+        // the workgroup-local rows: every local row is stored (rows past a matrix are dropped
+        // below)
         Tile::template compute<false>(regs, xw, xs, at, part, rows_local, slot, L, nullptr,
                                       a.nchunks);
         __builtin_amdgcn_sched_barrier(0);
-        if (wst + stride < wg_steps)
-            Tile::issue(regs, a.w, a.rows, a.nb, (wst + stride) * slots + slot, L);
+        if (wst + nblk < wg_steps) {
+            const StepMat n = src.at((wst + nblk) * slots + slot);
+            Tile::issue(regs, n.w, n.rows, n.nb, n.local, L);
+        }
         __syncthreads();
         for (int i = static_cast<int>(threadIdx.x); i < V * rows_local; i += a.threads) {
             const int v = i / rows_local, rl = i - v * rows_local;
-            const int row = wst * rows_local + rl;
-            float acc = part[v * rows_local + rl];
-            for (int s = 1; s < ws; s++) acc += part[(s * V + v) * rows_local + rl];
-            if (row < a.rows) a.out[static_cast<int64_t>(v) * a.rows + row] = acc;
+            const int st = wst * slots + rl / kStepRows;
+            if (st < steps) {
+                const StepMat m = src.at(st);
+                const int row = m.local * kStepRows + (rl % kStepRows);
+                float acc = part[v * rows_local + rl];
+                for (int s = 1; s < ws; s++) acc += part[(s * V + v) * rows_local + rl];
+                if (row < m.rows) m.out[static_cast<int64_t>(v) * m.rows + row] = acc;
+            }
         }
         __syncthreads();
     }
 }
+
+template <class F, int V, int T, int NC, int MODE>
+__global__ void __launch_bounds__(64 * gemv_max_waves(V, T, NC)) gemv_split_kernel(GemvArgs a) {
+    using Tile = typename F::template Tile<V, T, NC>;
+    const int groups = (a.rows + Tile::RPW - 1) / Tile::RPW;
+    const int steps = (groups + Tile::G - 1) / Tile::G;
+    gemv_split_walk<Tile, V, T, NC, MODE == kModeFused>(a, OneMatrix{a}, steps, blockIdx.x,
+                                                        gridDim.x);
+}
+
+// Several matrices of one format whose rows are wider than one pass: the same split walk over
+// their combined step numbering.
+template <class F, int V, int T, int NC, int MODE>
+__global__ void __launch_bounds__(64 * gemv_max_waves(V, T, NC))
+    gemv_multi_split_fmt_kernel(MultiArgs a) {
+    gemv_split_walk<typename F::template Tile<V, T, NC>, V, T, NC, MODE == kModeFused>(
+        a.act, MatrixList{a}, a.steps, blockIdx.x, gridDim.x);
+}
+
+// The LDS layout above, as the host computes it.
+static_assert(gemv_split_lds_bytes(3, 32, 2, true, 4, 8) ==
+                  4 * act_slice_lds_bytes<3, 32, 2>() +
+                      sizeof(float) * 3 * 8 * Q4kTile<3, 32, 2>::G * Q4kTile<3, 32, 2>::RPW,
+              "split LDS layout");
 
 // The launches of one format: tables over (vectors, lanes per row, chunks per lane) of the
 // compiled instances (nvec * chunks <= 8, so the activation slice fits in VGPRs), one for the
@@ -269,16 +311,47 @@ struct GemvLaunch {
         template <int V, int T, int NC>
         static hipError_t run(const GemvArgs &a, const LaunchShape &s, bool debug,
                               hipStream_t stream) {
-            using Tile = typename F::template Tile<V, T, NC>;
-            if (debug || a.x != nullptr || s.splits < 2 || s.waves % s.splits != 0 ||
+            if (debug || s.splits < 2 || s.waves % s.splits != 0 ||
                 s.waves > gemv_max_waves(V, T, NC))
                 return hipErrorInvalidValue;
-            const size_t lds = sizeof(float) * static_cast<size_t>(V) * s.waves * Tile::G * Tile::RPW;
+            const bool fused = a.x != nullptr;
+            const size_t lds = gemv_split_lds_bytes(V, T, NC, fused, s.splits, s.waves);
+            if (lds > kMaxSplitLds) return hipErrorInvalidValue;
             GemvArgs b = a;
             b.threads = 64 * s.waves;
             b.wg_splits = s.splits;
-            hipLaunchKernelGGL((gemv_split_kernel<F, V, T, NC>), dim3(static_cast<unsigned>(s.blocks)),
-                               dim3(static_cast<unsigned>(64 * s.waves)), lds, stream, b);
+            const dim3 grid(static_cast<unsigned>(s.blocks)), block(static_cast<unsigned>(64 * s.waves));
+            if (fused)
+                hipLaunchKernelGGL((gemv_split_kernel<F, V, T, NC, kModeFused>), grid, block, lds,
+                                   stream, b);
+            else
+                hipLaunchKernelGGL((gemv_split_kernel<F, V, T, NC, kModePlain>), grid, block, lds,
+                                   stream, b);
+            return hipGetLastError();
+        }
+    };
+
+    struct MultiSplit {
+        using Args = MultiArgs;
+        template <int V, int T, int NC>
+        static hipError_t run(const MultiArgs &a, const LaunchShape &s, bool debug,
+                              hipStream_t stream) {
+            if (debug || s.splits < 2 || s.waves % s.splits != 0 ||
+                s.waves > gemv_max_waves(V, T, NC))
+                return hipErrorInvalidValue;
+            const bool fused = a.act.x != nullptr;
+            const size_t lds = gemv_split_lds_bytes(V, T, NC, fused, s.splits, s.waves);
+            if (lds > kMaxSplitLds) return hipErrorInvalidValue;
+            MultiArgs b = a;
+            b.act.threads = 64 * s.waves;
+            b.act.wg_splits = s.splits;
+            const dim3 grid(static_cast<unsigned>(s.blocks)), block(static_cast<unsigned>(64 * s.waves));
+            if (fused)
+                hipLaunchKernelGGL((gemv_multi_split_fmt_kernel<F, V, T, NC, kModeFused>), grid, block,
+                                   lds, stream, b);
+            else
+                hipLaunchKernelGGL((gemv_multi_split_fmt_kernel<F, V, T, NC, kModePlain>), grid, block,
+                                   lds, stream, b);
             return hipGetLastError();
         }
     };
@@ -348,6 +421,10 @@ struct GemvLaunch {
     static hipError_t launch_split(const GemvArgs &a, const LaunchShape &s, int nvec,
                                    hipStream_t stream) {
         return dispatch<Split>(a, s, nvec, false, stream);
+    }
+    static hipError_t launch_multi_split(const MultiArgs &a, const LaunchShape &s, int nvec,
+                                         hipStream_t stream) {
+        return dispatch<MultiSplit>(a, s, nvec, false, stream);
     }
 };
 

@@ -29,6 +29,10 @@ constexpr int gemv_max_waves(int nvec, int lanes_per_row, int chunks_per_lane) {
     return nvec * lanes_per_row * chunks_per_lane >= kWideSliceBlocks ? 8 : 4;
 }
 
+// LDS a launch that splits the columns inside the workgroup may take (the fused form's slice of
+// every chunk plus the chunks' row sums); wider fused splits take the workspace instead.
+constexpr size_t kMaxSplitLds = 64 * 1024;
+
 // One GEMV launch: the kernels read everything they need from here.
 struct GemvArgs {
     const uint8_t *w;      // weight tensor (Q4_K blocks, or Q6_K bodies followed by the d plane)
@@ -131,6 +135,28 @@ hipError_t launch_gemv_split_q40(const GemvArgs &a, const LaunchShape &s, int nv
                                  hipStream_t stream);
 hipError_t launch_gemv_split_q80(const GemvArgs &a, const LaunchShape &s, int nvec,
                                  hipStream_t stream);
+// Several matrices of one format with rows wider than one pass, the split inside the
+// workgroup as above (plain or fused)
+hipError_t launch_gemv_multi_split_q4k(const MultiArgs &a, const LaunchShape &s, int nvec,
+                                       hipStream_t stream);
+hipError_t launch_gemv_multi_split_q6k(const MultiArgs &a, const LaunchShape &s, int nvec,
+                                       hipStream_t stream);
+hipError_t launch_gemv_multi_split_q40(const MultiArgs &a, const LaunchShape &s, int nvec,
+                                       hipStream_t stream);
+hipError_t launch_gemv_multi_split_q80(const MultiArgs &a, const LaunchShape &s, int nvec,
+                                       hipStream_t stream);
+// ... and a mix of formats (gemv_multi.hip)
+hipError_t launch_gemv_multi_split(const MultiArgs &a, const LaunchShape &s, int nvec,
+                                   hipStream_t stream);
+// LDS bytes of a launch that splits the columns inside the workgroup: in the fused form the
+// quantized slice of every chunk (32 code bytes and a float32 scale per activation block),
+// then the chunks' row sums, float32 [splits][nvec][rows of the workgroup's step].
+constexpr size_t gemv_split_lds_bytes(int nvec, int lanes, int chunks, bool fused, int splits,
+                                      int waves) {
+    return (fused ? size_t{36} * nvec * lanes * chunks * splits : 0) +
+           sizeof(float) * static_cast<size_t>(nvec) * waves * groups_per_step(chunks) *
+               (64 / lanes);
+}
 hipError_t launch_splitk_reduce(const float *part, float *y, int64_t n, int splits,
                                 hipStream_t stream);
 // Rows [row0, row0 + nrows) of a rows x cols matrix (w points at row row0) into their places

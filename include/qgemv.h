@@ -318,8 +318,12 @@ int qgemv_fused_launches(int wtype, int64_t rows, int64_t cols, int32_t nvec, in
  * call only. Each: wtype (any of enum qgemv_wtype), reserved = 0, rows >= 1, w the
  * device planar tensor (16-byte aligned), y device float32 [nvec][rows]
  * (4-byte aligned; no y may overlap any weights, the activation or another y).
- * The row is covered by one pass of lanes, so cols is at most 8192 for 1-2
- * vectors, 4096 for 3-4 and 2048 for 5-8 (QGEMV_EINVAL beyond). No workspace.
+ * A row wider than one pass of lanes (8192 columns for 1-2 vectors, 4096 for
+ * 3-4, 2048 for 5-8) is split into column chunks inside each workgroup, one
+ * wave per chunk and the chunks' row sums added in LDS in ascending chunk
+ * order (bit-identical to qgemv_batch_plan's split with the same geometry); at
+ * most 8 chunks, so cols is at most 65536, 32768 and 16384 for those vector
+ * counts (QGEMV_EINVAL beyond). No workspace.
  */
 #define QGEMV_MAX_MATRICES 8
 typedef struct qgemv_matrix {
@@ -332,8 +336,12 @@ typedef struct qgemv_matrix {
 
 /* The lanes per row and chunks per lane a multi-matrix launch uses for this
  * row width: the fewest idle lanes among the geometries that cover a row in one
- * pass, more chunks per lane preferred. QGEMV_EINVAL when no geometry covers
- * the row (cols too wide for nvec). Host only. */
+ * pass, more chunks per lane preferred; for a wider row, the one-matrix
+ * planner's rule (fewest idle lanes with each further pass priced as 2% of the
+ * lanes idle) among the geometries whose ceil(cols/32 / (lanes_per_row *
+ * chunks_per_lane)) chunks are at most a workgroup's waves (8 when nvec *
+ * lanes_per_row * chunks_per_lane >= 128, else 4). QGEMV_EINVAL when there is
+ * none. Host only. */
 int qgemv_multi_geometry(int64_t cols, int32_t nvec, int32_t *lanes_per_row,
                          int32_t *chunks_per_lane);
 
@@ -348,7 +356,11 @@ int qgemv_multi(const qgemv_matrix *mats, int32_t nmats, const int8_t *xq, const
  * and scales. With code outputs that are 16-byte aligned and an activation
  * slice that is large next to a workgroup's share of the weights, the library
  * quantizes once and runs qgemv_multi's kernel from them (two launches, the
- * same results). */
+ * same results). A split row's workgroup quantizes all of its chunks into LDS;
+ * where those slices take more than 64 KiB (36 bytes per activation block per
+ * chunk, e.g. 65536 columns x 1 vector, 16384 x 8) the code outputs are
+ * required, 16-byte aligned, and the product runs from them (QGEMV_EINVAL
+ * without them). */
 int qgemv_multi_fused(const qgemv_matrix *mats, int32_t nmats, const float *x, int8_t *xq_out,
                       float *xd_out, int64_t cols, int32_t nvec, hipStream_t stream);
 
@@ -477,12 +489,16 @@ int qgemv_batch_plan(int wtype, const void *w, const int8_t *xq, const float *xd
                      int64_t rows, int64_t cols, int32_t nvec, const qgemv_plan *plan,
                      void *workspace, size_t workspace_bytes, hipStream_t stream);
 
-/* qgemv_fused with an explicit plan (for tuning and tests): always the one-launch
- * kernel, each workgroup quantizing the columns it reads (xq_out / xd_out, both NULL or
- * both set, receive the codes and scales); a plan that splits the columns writes the
- * partial sums to the workspace (qgemv_plan_workspace_bytes) and adds them in a second
- * launch, in ascending chunk order, so y is bit-identical to qgemv_batch_plan with the
- * same plan on the codes of qgemv_quantize_act. */
+/* qgemv_fused with an explicit plan (for tuning and tests): always the fused kernel,
+ * each workgroup quantizing the columns it reads (xq_out / xd_out, both NULL or both
+ * set, receive the codes and scales). A plan that splits the columns into at most a
+ * workgroup's waves of chunks runs in one launch, the workgroup quantizing every chunk
+ * into LDS and its waves' chunk sums added there, when those slices take at most
+ * 64 KiB (36 bytes per activation block per chunk); otherwise each workgroup quantizes
+ * its chunk, the partial sums go to the workspace (qgemv_plan_workspace_bytes, required
+ * whenever the plan splits) and a second launch adds them. Either way the chunks are
+ * added in ascending order, so y is bit-identical to qgemv_batch_plan with the same
+ * plan on the codes of qgemv_quantize_act. */
 int qgemv_fused_plan(int wtype, const void *w, const float *x, int8_t *xq_out, float *xd_out,
                      float *y, int64_t rows, int64_t cols, int32_t nvec, const qgemv_plan *plan,
                      void *workspace, size_t workspace_bytes, hipStream_t stream);

@@ -221,9 +221,10 @@ def test_multi_rejects_bad_arguments():
     assert call([(1, 64, None, Y1)]) == EINVAL
     assert call([(1, 64, W1, None)]) == EINVAL
     assert call(good, cols=1000) == EINVAL
-    assert call(good, cols=8448) == EINVAL                          # wider than one pass
-    assert call(good, cols=8192, nvec=3) == EINVAL                  # 3-4 vectors: <= 4096
-    assert call(good, cols=4096, nvec=5) == EINVAL                  # 5-8 vectors: <= 2048
+    # a row wider than one pass is split into at most a workgroup's waves (8) of chunks
+    assert call(good, cols=65536 + 256) == EINVAL                   # 1 vector: 8 x 256 chunks
+    assert call(good, cols=32768 + 256, nvec=3) == EINVAL           # 3-4 vectors: 8 x 128
+    assert call(good, cols=16384 + 256, nvec=5) == EINVAL           # 5-8 vectors: 8 x 64
     assert call(good, xq=None) == EINVAL
     assert call(good, xq=XQ + 4) == EALIGN
     assert call([(1, 64, W1 + 8, Y1)]) == EALIGN
@@ -242,19 +243,31 @@ def test_multi_rejects_bad_arguments():
     assert f(_mats(*good), 2, X, X + 16, D, 1536, 1, None) == EINVAL    # codes over x
     assert f(_mats(*good), 2, X, W1 + 16, D, 1536, 1, None) == EINVAL   # codes over weights
     assert f(_mats((1, 64, W1, X + 64)), 1, X, None, None, 1536, 1, None) == EINVAL  # y over x
+    # 65536 columns, 8 chunks: their slices (73728 bytes) exceed the LDS limit, so the fused
+    # form needs code outputs to quantize into (16-byte aligned ones)
+    assert f(_mats(*good), 2, X, None, None, 65536, 1, None) == EINVAL
+    assert f(_mats(*good), 2, X, Q + 4, D, 65536, 1, None) == EINVAL
 
 
 def test_multi_geometry():
-    """One pass over the row, fewest idle lanes, more chunks per lane preferred."""
+    """One pass over the row, fewest idle lanes, more chunks per lane preferred; a wider row
+    takes the one-matrix planner's geometry (each further pass priced as 2% idle lanes), its
+    chunks split inside the workgroup."""
     assert qg.qgemv_multi_geometry(1536, 1) == (16, 3)
     assert qg.qgemv_multi_geometry(8192, 1) == (64, 4)
     assert qg.qgemv_multi_geometry(2048, 8) == (64, 1)
     assert qg.qgemv_multi_geometry(256, 1) == (8, 1)
     assert qg.qgemv_multi_geometry(4096, 3) == (64, 2)
+    assert qg.qgemv_multi_geometry(8448, 1) == (32, 3)      # 264 chunks: 3 passes of 96
+    assert qg.qgemv_multi_geometry(16384, 1) == (64, 4)     # 2 passes
+    assert qg.qgemv_multi_geometry(4096, 5) == (64, 1)      # 2 passes
+    assert qg.qgemv_multi_geometry(16384, 8) == (64, 1)     # 8 passes: 8 waves
+    assert qg.qgemv_multi_geometry(14336, 1) == (64, 4)     # not 7 passes of 16 x 4: 4 waves
+    assert qg.qgemv_multi_geometry(14336, 2) == (16, 4)     # 7 passes, 8 waves
     lib = qg._load()
     t, nc = ctypes.c_int32(), ctypes.c_int32()
-    assert lib.qgemv_multi_geometry(8448, 1, ctypes.byref(t), ctypes.byref(nc)) == EINVAL
-    assert lib.qgemv_multi_geometry(4096, 5, ctypes.byref(t), ctypes.byref(nc)) == EINVAL
+    assert lib.qgemv_multi_geometry(65536 + 256, 1, ctypes.byref(t), ctypes.byref(nc)) == EINVAL
+    assert lib.qgemv_multi_geometry(16384 + 256, 5, ctypes.byref(t), ctypes.byref(nc)) == EINVAL
     assert lib.qgemv_multi_geometry(1536, 1, None, ctypes.byref(nc)) == EINVAL
 
 

@@ -4,12 +4,12 @@ when rows alone under-fill the GPU, then add the partial results in a separate p
 
 The library's own plan for this shape covers each 8192-column row in one pass (measured
 faster), so the split forms are forced through explicit plans, at the full shape:
-  - from codes with S <= a workgroup's waves: the split inside the workgroup (one launch, the
-    chunks' row sums added in LDS in ascending chunk order);
-  - from codes with more chunks: partial sums in the workspace and the ordered reduce launch;
-  - fused (each workgroup quantizing its columns) with any S: partial sums in the workspace
-    and the ordered reduce launch (the atomic-free two-pass form).
-Every y lies within the oracle's bound |y - y_ref| <= 1e-5 sum |w||x|; the fused two-pass y is
+  - with S <= a workgroup's waves: the split inside the workgroup (one launch, the chunks' row
+    sums added in LDS in ascending chunk order), from codes and fused (the workgroup quantizing
+    every chunk of the row into LDS first);
+  - with more chunks: partial sums in the workspace and the ordered reduce launch (the
+    atomic-free two-pass form), from codes and fused (each workgroup quantizing its chunk).
+Every y lies within the oracle's bound |y - y_ref| <= 1e-5 sum |w||x|; the fused y is
 bit-identical to the from-codes y of the same plan (the same chunks, added in the same order);
 the fused codes, and the integer partials P and S, are the oracle's bit for bit."""
 
@@ -57,7 +57,7 @@ def _splits(p):
 
 
 def _both_forms(c2, plan):
-    """y from codes (qgemv_batch_plan) and y of the fused two-pass form (qgemv_fused_plan),
+    """y from codes (qgemv_batch_plan) and y of the fused form (qgemv_fused_plan),
     each through a workspace filled with 0xFF (NaN) first; and the fused form's codes."""
     import torch
     import block_quantized_weight_act_amd as qg

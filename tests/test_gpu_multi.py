@@ -1,7 +1,11 @@
 """GPU parity of the multi-matrix product (several matrices sharing one activation, one launch)
 against the CPU oracle, matrix by matrix, and against the one-matrix product with the same lane
 geometry (bit for bit). Bars as in test_gpu_parity: codes and scales bit-exact, each y within
-1e-5 of sum_i |w_i| |x_i| of its row."""
+1e-5 of sum_i |w_i| |x_i| of its row. Rows wider than one pass of lanes (up to 65536 columns)
+are split into column chunks inside the workgroup; their y is bit-identical to the one-matrix
+product's split with the same geometry, from codes and fused (the fused form quantizes every
+chunk of the row into LDS, or, where those slices do not fit, needs code outputs and runs
+from them)."""
 
 import numpy as np
 import pytest
@@ -22,22 +26,41 @@ def _say(*a):
     print("[multi]", *a, flush=True)
 
 
-def one_pass_geometry(cols, nvec):
-    """Lanes per row and chunks per lane the library uses for a multi-matrix launch: the
-    least idle lanes among the geometries that cover a row in one pass, more chunks per lane
-    preferred (the documented planner rule, restated here for the bit-identity check)."""
+def multi_geometry(cols, nvec):
+    """Lanes per row, chunks per lane and column chunks the library uses for a multi-matrix
+    launch: the least idle lanes among the geometries that cover a row in one pass, more
+    chunks per lane preferred; for a wider row the least idle lanes with each further pass
+    priced as 2% of them, among the geometries with at most a workgroup's waves of passes
+    (the documented planner rules, restated here for the bit-identity check)."""
     nchunks = cols // 32
-    best, best_cost = None, 1e30
-    for nc in range(1, 5):
-        if nvec * nc > 8:
-            break
-        for t in (8, 16, 32, 64):
-            if t * nc < nchunks:
-                continue
-            cost = 1.0 - nchunks / (t * nc) - 0.01 * nc
-            if cost < best_cost - 1e-12:
-                best, best_cost = (t, nc), cost
-    return best
+    for one_pass in (True, False):
+        best, best_cost = None, 1e30
+        for nc in range(1, 5):
+            if nvec * nc > 8:
+                break
+            for t in (8, 16, 32, 64):
+                passes = -(-nchunks // (t * nc))
+                if one_pass and passes > 1:
+                    continue
+                if passes > (8 if nvec * t * nc >= 128 else 4):
+                    continue
+                cost = 1.0 - nchunks / (passes * t * nc) + 0.02 * (passes - 1) - 0.01 * nc
+                if cost < best_cost - 1e-12:
+                    best, best_cost = (t, nc, passes), cost
+        if best is not None:
+            return best
+
+
+def fused_slices_fit(nvec, t, nc, splits):
+    """Whether a split row's fused form quantizes in LDS: the slices of every chunk (36 bytes
+    per 32-column block) and the chunks' row sums within 64 KiB, with the launch's waves per
+    workgroup (8 for a slice of >= 128 blocks, else 4, in sets of `splits`)."""
+    if splits == 1:
+        return True
+    maxw = 8 if nvec * t * nc >= 128 else 4
+    waves = splits * (maxw // splits)
+    g = {1: 4, 2: 2}.get(nc, 1)
+    return 36 * nvec * t * nc * splits + 4 * nvec * waves * g * (64 // t) <= 65536
 
 
 CASES = [
@@ -52,6 +75,15 @@ CASES = [
     (1536, 1, [("q4k", 100), ("q40", 65), ("q80", 33), ("q6k", 20)]),    # all four formats
     (800, 2, [("q40", 50), ("q80", 70)]),                                 # width not /256
     (96, 8, [("q80", 5), ("q40", 3)]),
+    # rows wider than one pass: the column split inside the workgroup
+    (16384, 1, [("q4k", 300), ("q6k", 65)]),                              # 2 chunks, one format each
+    (8448, 1, [("q4k", 37), ("q40", 50), ("q80", 20), ("q6k", 5)]),       # 3 chunks of 96 blocks
+    (6144, 5, [("q6k", 70), ("q4k", 33)]),                                # 3 chunks, 6 waves
+    (12288, 3, [("q80", 100), ("q6k", 9)]),
+    (16384, 8, [("q4k", 40), ("q4k", 3)]),                                # 8 chunks: codes needed
+    (65536, 1, [("q6k", 20), ("q80", 3)]),                                # 8 chunks of 256 blocks
+    (14336, 2, [("q4k", 1000)]),                                          # one matrix, 7 chunks
+    (14336, 1, [("q6k", 2048), ("q4k", 64)]),     # the planner's 7 chunks of 64 exceed 4 waves
 ]
 
 
@@ -82,7 +114,8 @@ def test_multi_parity(case):
     qg.qgemv_multi(mats, xq, xd, cols, nvec)
     got = [gu.host(y) for y in ys]
     t, nc = qg.qgemv_multi_geometry(cols, nvec)
-    assert (t, nc) == one_pass_geometry(cols, nvec)
+    t0, nc0, splits = multi_geometry(cols, nvec)
+    assert (t, nc) == (t0, nc0)
     plan = dict(lanes_per_row=t, chunks_per_lane=nc, waves_per_block=4, blocks=7)
     for (wtype, rows), buf, w, y in zip(spec, bufs, ws, got):
         ref = oracle.gemv(wtype, buf, rows, cols, rq, rd)
@@ -92,9 +125,15 @@ def test_multi_parity(case):
 
     # the fused form: the same y bit for bit, with and without code outputs
     xt = gu.dev(x)
+    fits = fused_slices_fit(nvec, t, nc, splits)
     for outs in (False, True):
         for y in ys:
             y.fill_(float("nan"))
+        if not outs and not fits:
+            with pytest.raises(qg.QgemvError):
+                qg.qgemv_multi_fused(mats, xt, cols, nvec)
+            assert all(torch.isnan(y).all() for y in ys)
+            continue
         if outs:
             xq_out = torch.zeros((nvec, cols), dtype=torch.int8, device=gu.DEV)
             xd_out = torch.zeros((nvec, cols // 32), dtype=torch.float32, device=gu.DEV)
