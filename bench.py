@@ -111,6 +111,10 @@ def kernel_unit(kname: str) -> str:
         return "gemm_i8.hip"
     if kname.startswith("gemm_q4k_mfma_kernel") or kname.startswith("mc_stage_kernel"):
         return "gemm_mfma.hip"
+    if kname.startswith("gemm_q32_mc_kernel"):
+        return "gemm_q32.hip"
+    if kname.startswith("gemm_q6k_mc_kernel"):
+        return "gemm_q6k_mc.hip"
     for tag, unit in (("Q4K", "gemv_q4k.hip"), ("Q6K", "gemv_q6k.hip"), ("Q40", "gemv_q40.hip"),
                       ("Q80", "gemv_q80.hip")):
         if "qgemv::%s," % tag in kname:
@@ -885,7 +889,7 @@ def bench_many(args, wl) -> dict:
     gemm_tflops = flops / (ms_gemm * 1e-3) / 1e12
     t_hbm = gemm_bytes / (HBM_PEAK_GBS * 1e9)
     route = qg.qgemv_route(wl.wtype, rows, cols, nvec)
-    # The contraction is int8 codes x int8 (Q8_0) or 4-bit (Q4_K, Q4_0) codes, so every route
+    # The contraction is int8 codes x int8 (Q8_0), 6-bit (Q6_K) or 4-bit (Q4_K, Q4_0) codes, so every route
     # is set against the int8 matrix peak; the float route (fp16 products of exact integers)
     # is also given against its own fp16 peak.
     mfma_peak, mfma_unit = MFMA_I8_PEAK_TOPS, "TOP/s"
@@ -895,7 +899,11 @@ def bench_many(args, wl) -> dict:
     elif route == "mc32":
         vtiles = (nvec + 31) // 32
         vw = 4 if vtiles >= 3 else vtiles
-        kernel = "gemm_q32_mc_kernel<%d, %d, %d, false>" % (4 if wl.wtype == "q80" else 3, 4 // vw, vw)
+        if wl.wtype == "q6k":
+            kernel = "gemm_q6k_mc_kernel<%d, %d, false>" % (4 // vw, vw)
+        else:
+            kernel = "gemm_q32_mc_kernel<%d, %d, %d, false>" % (4 if wl.wtype == "q80" else 3,
+                                                                4 // vw, vw)
     else:
         kernel = "gemm_q4k_mfma_kernel<%d, false>" % min(4, (nvec + 31) // 32)
     t_mfma = flops / (mfma_peak * 1e12)

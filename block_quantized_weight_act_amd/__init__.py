@@ -26,6 +26,7 @@ __all__ = [
     "qgemv_multi", "qgemv_multi_fused", "qgemv_multi_geometry", "QGEMV_Q4_0", "QGEMV_Q8_0",
     "Graph", "qgemv_graph_begin", "qgemv_graph_end", "qgemv_graph_launch", "qgemv_graph_nodes",
     "qgemv_graph_destroy", "qgemv_graph_classify", "qgemv_i8mc_workspace_bytes", "qgemv_batch_i8mc",
+    "qgemv_mc32_workspace_bytes", "qgemv_batch_mc32",
     "qgemv_debug_partials_i8mc", "qgemv_fused_i8mc", "qgemv_route", "ROUTES",
 ]
 
@@ -114,6 +115,8 @@ def _load():
         "qgemv_i8mc_workspace_bytes": (sz, [i64, i64, i32]),
         "qgemv_route": (ctypes.c_int, [ctypes.c_int, i64, i64, i32]),
         "qgemv_batch_i8mc": (ctypes.c_int, [vp, vp, vp, vp, i64, i64, i32, vp, sz, vp]),
+        "qgemv_mc32_workspace_bytes": (sz, [i32, i64, i64, i32]),
+        "qgemv_batch_mc32": (ctypes.c_int, [i32, vp, vp, vp, vp, i64, i64, i32, vp, sz, vp]),
         "qgemv_debug_partials_i8mc": (ctypes.c_int, [vp, vp, vp, vp, vp, i64, i64, i32, vp]),
         "qgemv_fused_i8mc": (ctypes.c_int, [vp, vp, vp, vp, vp, i64, i64, i32, vp, sz, vp]),
     }
@@ -332,7 +335,8 @@ ROUTES = {1: "vector", 2: "i8mc", 3: "mc", 4: "grouped", 5: "mc32"}
 
 def qgemv_route(wtype, rows: int, cols: int, nvec: int = 1) -> str:
     """Which kernels qgemv_batch runs for this shape: "vector", "i8mc" (integer matrix cores),
-    "mc" (matrix cores, 9+ Q4_K vectors) or "grouped" (vector kernels on groups of 8)."""
+    "mc" (float matrix cores, 17+ Q4_K vectors), "mc32" (integer matrix cores, 9+ Q8_0 / Q4_0 /
+    Q6_K vectors) or "grouped" (vector kernels on groups of 8)."""
     lib = _load()
     r = int(lib.qgemv_route(_wtype(wtype), rows, cols, nvec))
     if r not in ROUTES:
@@ -352,6 +356,22 @@ def qgemv_batch_i8mc(w, xq, xd, y, rows: int, cols: int, nvec: int, workspace=No
     _check("qgemv_batch_i8mc", lib.qgemv_batch_i8mc(
         _ptr(w, name="w"), _ptr(xq, torch.int8, "xq"), _ptr(xd, torch.float32, "xd"),
         _ptr(y, torch.float32, "y"), rows, cols, nvec, wsp, wsb, _stream(stream, y)))
+
+
+def qgemv_mc32_workspace_bytes(wtype, rows: int, cols: int, nvec: int) -> int:
+    return int(_load().qgemv_mc32_workspace_bytes(_wtype(wtype), rows, cols, nvec))
+
+
+def qgemv_batch_mc32(wtype, w, xq, xd, y, rows: int, cols: int, nvec: int, workspace=None,
+                     stream=None) -> None:
+    """Q8_0 / Q4_0 / Q6_K y = W x for 9..256 vectors on the integer matrix cores, whatever the
+    shape."""
+    lib = _load()
+    wsp, wsb = _ws(workspace)
+    _check("qgemv_batch_mc32", lib.qgemv_batch_mc32(
+        _wtype(wtype), _ptr(w, name="w"), _ptr(xq, torch.int8, "xq"),
+        _ptr(xd, torch.float32, "xd"), _ptr(y, torch.float32, "y"), rows, cols, nvec, wsp, wsb,
+        _stream(stream, y)))
 
 
 def qgemv_debug_partials_i8mc(w, xq, xd, P, S, rows: int, cols: int, nvec: int,

@@ -9,6 +9,7 @@
 #include <cstdlib>
 #include <cstring>
 
+#include "gemm_mc.h"
 #include "qgemv_internal.h"
 
 namespace qgemv {
@@ -326,13 +327,6 @@ struct McPlan {
     int nt, row_tiles, groups, splits, sbps;
 };
 
-// More than kMaxVec vectors for a format without a matrix-core path (Q6_K): groups of kMaxVec.
-bool grouped_shape_ok(int wtype, int64_t rows, int64_t cols, int32_t nvec) {
-    return wtype == QGEMV_Q6K && nvec > kMaxVec && nvec <= kMaxBatch &&
-           shape_ok_t(wtype, rows, cols, 1) &&
-           static_cast<int64_t>(nvec) * cols < (int64_t{1} << 34);
-}
-
 // check_gemv_args for any vector count (the shape itself checked by the caller)
 int check_gemv_args_n(int wtype, const void *w, const int8_t *xq, const float *xd, const void *out,
                       size_t out_bytes, int64_t rows, int64_t cols, int32_t nvec) {
@@ -435,18 +429,42 @@ int run_mc(const void *w, const int8_t *xq, const float *xd, float *y, int32_t *
 // vectors (1, 2 or 4 for 1, 2, 3+ tiles) by 4 / vw tiles of 32 rows; the columns are split
 // when the row tiles and vector groups alone give fewer than two workgroups per CU (the
 // splits added by the ordered reduce).
-bool q32mc_shape_ok(int wtype, int64_t rows, int64_t cols, int32_t nvec) {
-    return (wtype == QGEMV_Q8_0 || wtype == QGEMV_Q4_0) && nvec > kMaxVec && nvec <= kMaxBatch &&
+bool mc32_ok(int wtype, int64_t rows, int64_t cols, int32_t nvec) {
+    return (wtype == QGEMV_Q8_0 || wtype == QGEMV_Q4_0 || wtype == QGEMV_Q6K) && nvec > kMaxVec &&
+           nvec <= kMaxBatch &&
            shape_ok_t(wtype, rows, cols, 1) &&
            static_cast<int64_t>(nvec) * cols < (int64_t{1} << 34);
 }
 
-struct Q32McPlan {
+// Where qgemv_batch takes that path. On a small tensor its staging, split and reduce cost a
+// floor of 16-20 us, where the vector kernel on groups of 8 vectors (each group reading every
+// weight) is ahead until the groups are many. Measured on MI355X (graph replay, cold weights;
+// matrix cores against groups of 8): 2048 x 8192 Q6_K / Q8_0 / Q4_0 with 9 vectors 20.0 / 19.4
+// / 18.9 us against 12.4 / 12.0 / 10.4, with 24 vectors 22.2 / 23.5 / 23.1 against 22.3 / 19.5
+// / 19.1, with 32 vectors 22.9 / 25.0 / 24.6 against 29.3 / 25.7 / 25.2; 16384 x 2048 with 16
+// vectors 19.2 / 17.9 / 18.3 against 21.2 / 20.2 / 16.9, with 24 vectors 20.0 / 19.3 / 20.2
+// against 31.5 / 29.7 / 24.9; 65536 x 1536 with 9 vectors 38.4 / 30.7 / 30.2 against 55.4 /
+// 48.4 / 38.5. The weight count (not the bytes) separates the formats: from 32 vectors
+// always, from 16 vectors from 24 Mi weights, from 9 vectors from 48 Mi weights.
+bool mc32_auto(int wtype, int64_t rows, int64_t cols, int32_t nvec) {
+    if (!mc32_ok(wtype, rows, cols, nvec)) return false;
+    const int64_t weights = rows * cols;
+    constexpr int64_t Mi = int64_t{1} << 20;
+    return nvec >= 32 || (nvec >= 16 && weights >= 24 * Mi) || weights >= 48 * Mi;
+}
+
+// More than kMaxVec vectors where the matrix-core path is not taken: the vector kernel on
+// groups of up to kMaxVec vectors, one after another on the stream.
+bool grouped_shape_ok(int wtype, int64_t rows, int64_t cols, int32_t nvec) {
+    return mc32_ok(wtype, rows, cols, nvec) && !mc32_auto(wtype, rows, cols, nvec);
+}
+
+struct Mc32Plan {
     int vw, groups, row_tiles, splits, bps;
 };
 
-Q32McPlan make_q32mc_plan(int64_t rows, int64_t cols, int32_t nvec) {
-    Q32McPlan p{};
+Mc32Plan make_mc32_plan(int64_t rows, int64_t cols, int32_t nvec) {
+    Mc32Plan p{};
     const int vtiles = (nvec + 31) / 32;
     p.vw = vtiles >= 3 ? 4 : vtiles;
     const int rw = 4 / p.vw;
@@ -462,18 +480,19 @@ Q32McPlan make_q32mc_plan(int64_t rows, int64_t cols, int32_t nvec) {
     return p;
 }
 
-size_t q32mc_ws_bytes(const Q32McPlan &p, int64_t rows, int32_t nvec) {
+size_t mc32_ws_bytes(const Mc32Plan &p, int64_t rows, int32_t nvec) {
     return p.splits > 1 ? static_cast<size_t>(p.splits) * nvec * rows * sizeof(float) : 0;
 }
 
-// y (or, with P, the debug partials P and S) of a Q8_0 / Q4_0 product with many vectors.
-int run_q32mc(int wtype, const void *w, const int8_t *xq, const float *xd, float *y, int32_t *P,
+// y (or, with P, the debug partials P and S) of a Q8_0, Q4_0 or Q6_K product with many vectors.
+int run_mc32(int wtype, const void *w, const int8_t *xq, const float *xd, float *y, int32_t *P,
               int32_t *S, int64_t rows, int64_t cols, int32_t nvec, void *ws, size_t ws_bytes,
               hipStream_t stream) {
     const bool debug = P != nullptr;
-    if (!q32mc_shape_ok(wtype, rows, cols, nvec)) return QGEMV_EINVAL;
+    if (!mc32_ok(wtype, rows, cols, nvec)) return QGEMV_EINVAL;
     const size_t ybytes = static_cast<size_t>(nvec) * rows * sizeof(float);
-    const size_t pbytes = static_cast<size_t>(nvec) * rows * (cols / 32) * sizeof(int32_t);
+    const int64_t nsub = wtype == QGEMV_Q6K ? cols / 16 : cols / 32;
+    const size_t pbytes = static_cast<size_t>(nvec) * rows * nsub * sizeof(int32_t);
     int st = check_gemv_args_n(wtype, w, xq, xd, debug ? static_cast<const void *>(P) : y,
                                debug ? pbytes : ybytes, rows, cols, nvec);
     if (st != QGEMV_OK) return st;
@@ -488,8 +507,8 @@ int run_q32mc(int wtype, const void *w, const int8_t *xq, const float *xd, float
             overlaps(S, sbytes, xq, qb) || overlaps(S, sbytes, xd, db))
             return QGEMV_EINVAL;
     }
-    const Q32McPlan p = make_q32mc_plan(rows, cols, nvec);
-    const size_t need = debug ? 0 : q32mc_ws_bytes(p, rows, nvec);
+    const Mc32Plan p = make_mc32_plan(rows, cols, nvec);
+    const size_t need = debug ? 0 : mc32_ws_bytes(p, rows, nvec);
     if (need > 0) {
         if (!ws || ws_bytes < need) return QGEMV_EWORKSPACE;
         if (!aligned(ws, 4)) return QGEMV_EALIGN;
@@ -511,7 +530,8 @@ int run_q32mc(int wtype, const void *w, const int8_t *xq, const float *xd, float
     a.row_tiles = p.row_tiles;
     a.groups = p.groups;
     a.splits = p.splits;
-    hipError_t e = launch_gemm_q32_mc(wtype, a, p.vw, debug, stream);
+    hipError_t e = wtype == QGEMV_Q6K ? launch_gemm_q6k_mc(a, p.vw, debug, stream)
+                                      : launch_gemm_q32_mc(wtype, a, p.vw, debug, stream);
     if (e != hipSuccess) return hip_fail(e);
     if (need > 0) {
         e = launch_splitk_reduce(static_cast<const float *>(ws), y,
@@ -842,8 +862,8 @@ int qgemv_quantize_act(const float *x, int8_t *xq, float *xd, int64_t cols, int3
 
 size_t qgemv_workspace_bytes(int wtype, int64_t rows, int64_t cols, int32_t nvec) {
     if (i8_auto(wtype, rows, cols, nvec)) return i8_ws_bytes(make_i8_plan(rows, cols), rows, nvec);
-    if (q32mc_shape_ok(wtype, rows, cols, nvec))
-        return q32mc_ws_bytes(make_q32mc_plan(rows, cols, nvec), rows, nvec);
+    if (mc32_auto(wtype, rows, cols, nvec))
+        return mc32_ws_bytes(make_mc32_plan(rows, cols, nvec), rows, nvec);
     if (mc_shape_ok(wtype, rows, cols, nvec))
         return mc_ws_bytes(make_mc_plan(rows, cols, nvec), rows, cols, nvec);
     if (grouped_shape_ok(wtype, rows, cols, nvec)) {
@@ -902,13 +922,12 @@ int qgemv_batch(int wtype, const void *w, const int8_t *xq, const float *xd, flo
     if (mc_shape_ok(wtype, rows, cols, nvec))
         return run_mc(w, xq, xd, y, nullptr, nullptr, rows, cols, nvec, workspace,
                       workspace_bytes, stream);
-    if (q32mc_shape_ok(wtype, rows, cols, nvec))
-        return run_q32mc(wtype, w, xq, xd, y, nullptr, nullptr, rows, cols, nvec, workspace,
+    if (mc32_auto(wtype, rows, cols, nvec))
+        return run_mc32(wtype, w, xq, xd, y, nullptr, nullptr, rows, cols, nvec, workspace,
                          workspace_bytes, stream);
     if (grouped_shape_ok(wtype, rows, cols, nvec)) {
-        // more than kMaxVec vectors without a matrix-core path: the vector kernel on groups of
-        // up to kMaxVec vectors (each group one pass over the weights); every argument is
-        // checked for the whole product before the first launch
+        // the vector kernel on groups of up to kMaxVec vectors (each group one pass over the
+        // weights); every argument is checked for the whole product before the first launch
         const size_t ybytes = static_cast<size_t>(nvec) * rows * sizeof(float);
         int st = check_gemv_args_n(wtype, w, xq, xd, y, ybytes, rows, cols, nvec);
         if (st != QGEMV_OK) return st;
@@ -1075,7 +1094,7 @@ int qgemv_multi_fused(const qgemv_matrix *mats, int32_t nmats, const float *x, i
 int qgemv_route(int wtype, int64_t rows, int64_t cols, int32_t nvec) {
     if (i8_auto(wtype, rows, cols, nvec)) return QGEMV_ROUTE_I8MC;
     if (mc_shape_ok(wtype, rows, cols, nvec)) return QGEMV_ROUTE_MC;
-    if (q32mc_shape_ok(wtype, rows, cols, nvec)) return QGEMV_ROUTE_MC32;
+    if (mc32_auto(wtype, rows, cols, nvec)) return QGEMV_ROUTE_MC32;
     if (grouped_shape_ok(wtype, rows, cols, nvec)) return QGEMV_ROUTE_GROUPED;
     if (shape_ok_t(wtype, rows, cols, nvec)) return QGEMV_ROUTE_VECTOR;
     return 0;
@@ -1094,6 +1113,18 @@ int qgemv_batch_i8mc(const void *w, const int8_t *xq, const float *xd, float *y,
     act.xd = xd;
     return run_i8(w, act, y, nullptr, nullptr, rows, cols, nvec, workspace, workspace_bytes,
                   stream);
+}
+
+size_t qgemv_mc32_workspace_bytes(int wtype, int64_t rows, int64_t cols, int32_t nvec) {
+    if (!mc32_ok(wtype, rows, cols, nvec)) return 0;
+    return mc32_ws_bytes(make_mc32_plan(rows, cols, nvec), rows, nvec);
+}
+
+int qgemv_batch_mc32(int wtype, const void *w, const int8_t *xq, const float *xd, float *y,
+                     int64_t rows, int64_t cols, int32_t nvec, void *workspace,
+                     size_t workspace_bytes, hipStream_t stream) {
+    return run_mc32(wtype, w, xq, xd, y, nullptr, nullptr, rows, cols, nvec, workspace,
+                    workspace_bytes, stream);
 }
 
 int qgemv_debug_partials_i8mc(const void *w, const int8_t *xq, const float *xd, int32_t *P,
@@ -1151,8 +1182,8 @@ int qgemv_debug_partials(int wtype, const void *w, const int8_t *xq, const float
         return run_mc(w, xq, xd, nullptr, P, S, rows, cols, nvec, workspace, workspace_bytes,
                       stream);
     }
-    if (q32mc_shape_ok(wtype, rows, cols, nvec))
-        return run_q32mc(wtype, w, xq, xd, nullptr, P, S, rows, cols, nvec, nullptr, 0, stream);
+    if (mc32_ok(wtype, rows, cols, nvec))
+        return run_mc32(wtype, w, xq, xd, nullptr, P, S, rows, cols, nvec, nullptr, 0, stream);
     const int64_t nsub = wtype == QGEMV_Q6K ? cols / 16 : cols / 32;
     const size_t pbytes = static_cast<size_t>(nvec) * rows * nsub * sizeof(int32_t);
     int st = check_gemv_args(wtype, w, xq, xd, P, pbytes, rows, cols, nvec);

@@ -228,9 +228,12 @@ int qgemv_batch_scratch(int wtype, const void *w, const int8_t *xq, const float 
 /* Which kernels qgemv_batch (and qgemv_fused, qgemv_debug_partials) run for a
  * shape: the vector kernels, the integer matrix cores (qgemv_batch_i8mc), the
  * float matrix cores for 17..QGEMV_MAX_BATCH Q4_K vectors, the integer matrix
- * cores for 9..QGEMV_MAX_BATCH Q8_0 or Q4_0 vectors (QGEMV_ROUTE_MC32), or the
- * vector kernels on groups of 8 vectors (Q6_K); 0 for an invalid type or shape.
- * Host only. */
+ * cores for 9..QGEMV_MAX_BATCH Q8_0, Q4_0 or Q6_K vectors (qgemv_batch_mc32;
+ * QGEMV_ROUTE_MC32) from 32 vectors, from 16 vectors on tensors of at least
+ * 24 Mi weights and from 9 vectors on at least 48 Mi weights, or else for those
+ * formats the vector kernels on groups of 8 vectors (QGEMV_ROUTE_GROUPED: on a
+ * small tensor they stay ahead of the matrix-core path's 16-20 us floor until
+ * the groups are many); 0 for an invalid type or shape. Host only. */
 enum qgemv_route_kind {
     QGEMV_ROUTE_VECTOR = 1,
     QGEMV_ROUTE_I8MC = 2,
@@ -239,6 +242,26 @@ enum qgemv_route_kind {
     QGEMV_ROUTE_MC32 = 5
 };
 int qgemv_route(int wtype, int64_t rows, int64_t cols, int32_t nvec);
+
+/*
+ * Q8_0, Q4_0 or Q6_K with 9 <= nvec <= QGEMV_MAX_BATCH on the integer matrix
+ * cores, for any shape (qgemv_batch takes it where QGEMV_ROUTE_MC32 says; oxinfer
+ * README, "Speculative decoding": the multi-token int8 variants). One product is
+ * 32 weight rows x 32 vectors over one 32-weight block (Q8_0: the stored codes;
+ * Q4_0: the codes 0..15, then P = sum q * xq - 8 S in integer) or over one
+ * 16-weight Q6_K sub-block (the operand q - 32), so its int32 result is the exact
+ * integer partial P of qgemv_debug_partials for every (row, vector); then y is
+ * sum over blocks of (d * xd) * P (Q6_K: xd * (sc0 * P0 + sc1 * P1) per block,
+ * the integer combination exact, times d per half super-block) in float32,
+ * within the same bound as the vector kernels' y. Arguments as for qgemv_batch;
+ * the workspace (qgemv_mc32_workspace_bytes: partial sums when the columns are
+ * split because row tiles and vector groups give fewer than 512 workgroups) may
+ * be NULL when that is 0.
+ */
+size_t qgemv_mc32_workspace_bytes(int wtype, int64_t rows, int64_t cols, int32_t nvec);
+int qgemv_batch_mc32(int wtype, const void *w, const int8_t *xq, const float *xd, float *y,
+                     int64_t rows, int64_t cols, int32_t nvec, void *workspace,
+                     size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Q4_K with 1 <= nvec <= 16 on the integer matrix cores (v_mfma_i32_16x16x64_i8;
@@ -411,9 +434,11 @@ int qgemv_graph_destroy(qgemv_graph *graph);
 /*
  * Test hook: the exact integer partials of the same kernels (for Q4_K with
  * more than 8 vectors, of the matrix-core kernel, which needs the workspace of
- * qgemv_workspace_bytes(); elsewhere workspace may be NULL; Q8_0 and Q4_0 take
- * 9..QGEMV_MAX_BATCH vectors here too). For Q4_0 and Q8_0, P [nvec][rows][cols/32]
- * is the block's sum of (q - 8) * xq or q * xq.
+ * qgemv_workspace_bytes(); elsewhere workspace may be NULL; Q8_0, Q4_0 and Q6_K
+ * take 9..QGEMV_MAX_BATCH vectors here too, on the kernel of qgemv_batch_mc32,
+ * whichever route qgemv_batch takes: every route forms the same exact integers).
+ * For Q4_0 and Q8_0, P [nvec][rows][cols/32] is the block's sum of (q - 8) * xq
+ * or q * xq.
  * P int32: Q4_K [nvec][rows][cols/32] (sum of q * xq per 32-column
  * sub-block), Q6_K [nvec][rows][cols/16] (sum of (q - 32) * xq per 16-column
  * sub-block). S int32 [nvec][cols/32]: sum of xq per activation block.

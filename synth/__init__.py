@@ -179,6 +179,9 @@ WORKLOADS = {
                                 1005, 2700, outlier_frac=0.01, seed_rows=3005),
     "q80_262144x1536": Workload("q80_262144x1536", "q80", 262144, 1536, 1, 1006, 2800,
                                 outlier_frac=0.01, seed_rows=3006),
+    # ... and Q6_K there (the format a vocabulary projection is often kept in; weight seed 1009)
+    "q6k_262144x1536": Workload("q6k_262144x1536", "q6k", 262144, 1536, 1, 1009, 3700,
+                                outlier_frac=0.01, seed_rows=3009),
     # many vectors at once (tokens verified or prefilled together) on the matrices above:
     # vector v has activation seed 3100 + v (resp. 3400 + v)
     "q4k_262144x1536_b64": Workload("q4k_262144x1536_b64", "q4k", 262144, 1536, 64, 1003, 3100,

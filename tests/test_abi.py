@@ -106,7 +106,16 @@ def test_routes():
     assert qg.qgemv_route("q40", 16384, 2048, 64) == "mc32"
     assert qg.qgemv_route("q80", 262144, 1536, 9) == "mc32"
     assert qg.qgemv_route("q80", 262144, 1536, 8) == "vector"
-    assert qg.qgemv_route("q6k", 16384, 2048, 64) == "grouped"
+    assert qg.qgemv_route("q6k", 16384, 2048, 64) == "mc32"
+    # Q8_0, Q4_0, Q6_K: the matrix cores from 32 vectors, from 16 on >= 24 Mi weights, from 9
+    # on >= 48 Mi weights; groups of 8 on the vector kernel below
+    assert qg.qgemv_route("q80", 2048, 8192, 9) == "grouped"
+    assert qg.qgemv_route("q80", 2048, 8192, 24) == "grouped"
+    assert qg.qgemv_route("q80", 2048, 8192, 32) == "mc32"
+    assert qg.qgemv_route("q6k", 16384, 2048, 9) == "grouped"
+    assert qg.qgemv_route("q6k", 16384, 2048, 16) == "mc32"
+    assert qg.qgemv_route("q40", 65536, 1536, 9) == "mc32"
+    assert qg.qgemv_route("q40", 16384, 1536, 15) == "grouped"
     assert qg._load().qgemv_route(1, 8, 500, 1) == 0
     assert qg._load().qgemv_route(1, 8, 512, 300) == 0
 
@@ -292,8 +301,10 @@ def test_matrix_core_path_limits_on_the_host():
     assert qg.qgemv_workspace_bytes("q4k", 256, 2048, 64) > 0          # few rows: split
     # enough rows: no split, only the staged activation tiles (8 super-blocks x 64 vectors)
     assert qg.qgemv_workspace_bytes("q4k", 1 << 16, 2048, 64) == 8 * 2 * 18432
-    # other formats: groups of 8 vectors on the vector kernel, sharing one group's workspace
-    assert qg.qgemv_workspace_bytes("q6k", 256, 2048, 64) == qg.qgemv_workspace_bytes("q6k", 256, 2048, 8)
+    # Q6_K takes the plan of the 32-weight formats' matrix-core path: 4 row tiles of 64 rows,
+    # 16 splits of 4 blocks
+    assert qg.qgemv_workspace_bytes("q6k", 256, 2048, 64) == 16 * 64 * 256 * 4
+    assert qg.qgemv_workspace_bytes("q6k", 256, 2048, 64) == qg.qgemv_workspace_bytes("q80", 256, 2048, 64)
     assert qg.qgemv_workspace_bytes("q4k", 256, 2048, 257) == 0
     assert _call_batch(nvec=257) == EINVAL
     assert _call_batch(wtype=2, nvec=257) == EINVAL
@@ -316,6 +327,17 @@ def test_mc32_workspace_and_limits():
     lib = qg._load()
     assert lib.qgemv_debug_partials(4, A, A + (1 << 30), A + (2 << 30), A + (3 << 30), None, 64,
                                     1024, 20, None, 0, None) == EINVAL          # no S
+    # the explicit entry point takes any shape of its formats with 9..256 vectors
+    X, D, Y = A + (1 << 30), A + (2 << 30), A + (3 << 30)
+    mc = lib.qgemv_batch_mc32
+    assert qg.qgemv_mc32_workspace_bytes("q80", 2048, 8192, 9) == 32 * 9 * 2048 * 4
+    assert qg.qgemv_mc32_workspace_bytes("q80", 2048, 8192, 8) == 0
+    assert qg.qgemv_mc32_workspace_bytes("q4k", 2048, 8192, 64) == 0
+    assert mc(4, A, X, D, Y, 2048, 8192, 8, None, 0, None) == EINVAL         # too few vectors
+    assert mc(1, A, X, D, Y, 2048, 8192, 64, None, 0, None) == EINVAL        # Q4_K
+    assert mc(2, A, X, D, Y, 2048, 1024 + 32, 64, None, 0, None) == EINVAL   # Q6_K: whole 256s
+    assert mc(4, A, X, D, Y, 2048, 8192, 9, None, 0, None) == EWORKSPACE     # its split
+    assert mc(4, A, X + 4, D, Y, 2048, 8192, 9, None, 0, None) == EALIGN
 
 
 def test_scratch_entry_point_rejects_bad_arguments():

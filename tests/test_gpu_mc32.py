@@ -1,9 +1,11 @@
-"""GPU parity of the integer matrix-core path for the 32-weight formats (Q8_0 and Q4_0 with
-9..256 activation vectors) against the CPU oracle, through the C ABI: integer partials P and
-activation block sums S bit-exact (debug form), every y within 1e-5 of sum_i |w_i| |x_i| of
-its row and vector. Shapes cover 1, 2 and 4 vector tiles of 32 per workgroup, one and two
-vector groups, ragged row tiles, widths that are not a whole number of 4-block steps, column
-splits (few rows) and one pass (many rows), the int32 extremes of both formats, and the
+"""GPU parity of the integer matrix-core path for 9..256 activation vectors (Q8_0 and Q4_0: one
+32 x 32 x 32 product per 32-weight block; Q6_K: one 32 x 32 x 16 product per 16-weight
+sub-block) against the CPU oracle, through the C ABI: integer partials P (per block, or per
+Q6_K sub-block) and activation block sums S bit-exact (debug form), every y within 1e-5 of
+sum_i |w_i| |x_i| of its row and vector. Shapes cover 1, 2 and 4 vector tiles of 32 per
+workgroup, one and two vector groups, ragged row tiles, widths that are not a whole number of
+4-block steps, column splits (few rows; for Q6_K splits that start in the middle of a
+super-block) and one pass (many rows), the int32 extremes of every format, and the
 262144 x 1536 vocabulary projection with 64 vectors (sampled rows)."""
 
 import numpy as np
@@ -26,17 +28,37 @@ def _say(*a):
     print("[mc32]", *a, flush=True)
 
 
+def _mc32(wtype, wt, xq, xd, rows, cols, nvec):
+    """y of the matrix-core kernel itself (qgemv_batch_mc32), whichever route qgemv_batch
+    takes for the shape."""
+    import torch
+    import block_quantized_weight_act_amd as qg
+    y = torch.full((nvec, rows), float("nan"), dtype=torch.float32, device=gu.DEV)
+    nbytes = qg.qgemv_mc32_workspace_bytes(wtype, rows, cols, nvec)
+    ws = torch.empty(max(nbytes, 4), dtype=torch.uint8, device=gu.DEV) if nbytes else None
+    qg.qgemv_batch_mc32(wtype, wt, xq, xd, y, rows, cols, nvec, workspace=ws)
+    return gu.host(y)
+
+
 def _check(wtype, wbuf, rows, cols, x, debug=True):
     import block_quantized_weight_act_amd as qg
     nvec = x.shape[0]
-    assert qg.qgemv_route(wtype, rows, cols, nvec) == "mc32"
     rq, rd = oracle.quantize_act(x)
     xq, xd = gu.quantize_act(x)
     assert np.array_equal(gu.host(xq), rq)
     ref = oracle.gemv(wtype, wbuf, rows, cols, rq, rd, partials=debug)
     wt = gu.dev(wbuf)
-    y = gu.gemv(wtype, wt, xq, xd, rows, cols, nvec)
+    y = _mc32(wtype, wt, xq, xd, rows, cols, nvec)
     gu.assert_within_bound(y, ref)
+    # qgemv_batch: the same kernel (bit for bit) where it routes there, else groups of 8 on
+    # the vector kernel, within the same bound
+    route = qg.qgemv_route(wtype, rows, cols, nvec)
+    assert route in ("mc32", "grouped")
+    yb = gu.gemv(wtype, wt, xq, xd, rows, cols, nvec)
+    if route == "mc32":
+        assert np.array_equal(yb.view(np.uint32), y.view(np.uint32))
+    else:
+        gu.assert_within_bound(yb, ref)
     if debug:
         P, S = gu.partials(wtype, wt, xq, xd, rows, cols, nvec)
         assert np.array_equal(S, oracle.block_sums(rq))
@@ -58,11 +80,27 @@ SHAPES = [
 ]
 
 
-@pytest.mark.parametrize("rows,cols,nvec", SHAPES)
-@pytest.mark.parametrize("wtype", ["q80", "q40"])
+SHAPES_Q6K = [
+    # (rows, cols, nvec): Q6_K rows are whole super-blocks of 256 columns
+    (300, 1280, 9),       # 40 blocks over 10 splits of half a super-block each
+    (257, 768, 33),
+    (128, 2048, 64),
+    (1000, 1536, 100),
+    (131, 256, 128),      # one super-block: two steps
+    (64, 4096, 129),
+    (513, 1024, 256),
+    (4100, 1536, 40),
+    (37, 2560, 77),
+    (2048, 8192, 64),     # the short, wide matrix with 64 vectors
+]
+
+CASES = [(w, *s) for w in ("q80", "q40") for s in SHAPES] + [("q6k", *s) for s in SHAPES_Q6K]
+
+
+@pytest.mark.parametrize("wtype,rows,cols,nvec", CASES)
 def test_parity(wtype, rows, cols, nvec):
     _say(wtype, rows, cols, nvec)
-    rng = np.random.default_rng(rows * 31 + cols + nvec + (wtype == "q40"))
+    rng = np.random.default_rng(rows * 31 + cols + nvec + ("q80", "q40", "q6k").index(wtype))
     w = (rng.standard_normal((rows, cols)) * 0.02).astype(np.float32)
     w[0, :64] = 0.0                                     # zero weight blocks: exactly 0
     x = (rng.standard_normal((nvec, cols)) * rng.choice([1e-3, 1.0, 40.0], size=(nvec, 1))).astype(np.float32)
@@ -79,38 +117,47 @@ def test_integer_extremes():
     img15 = oracle.q40_pack_block(0x3C00, np.full(32, 15, np.uint8))
     t40 = oracle.q32_tensor("q40", [img0, img15] * (rows * cols // 64))
     _check("q40", t40, rows, cols, np.full((nvec, cols), -3.0, np.float32))    # P = +-32512
+    # Q6_K: codes 0 and 63 (q - 32 = -32, 31) with sub-scales -128 and 127 against codes -127:
+    # P = 65024 and -62992, sc0 P0 + sc1 P1 = -16646144 (just under 2^24 in magnitude)
+    lo = oracle.q6k_pack_block(np.full(16, -128, np.int8), np.zeros(256, np.uint8))
+    hi = oracle.q6k_pack_block(np.array([127, -128] * 8, np.int8),
+                               np.array(([63] * 16 + [0] * 16) * 8, np.uint8))
+    nsb = rows * cols // 256
+    t6 = oracle.q6k_tensor([lo, hi] * (nsb // 2), [0x3C00, 0x0400] * (nsb // 2))
+    _check("q6k", t6, rows, cols, np.full((nvec, cols), -3.0, np.float32))
 
 
 def test_zero_weights_give_exact_zero():
     rows, cols, nvec = 96, 512, 20
     x = np.random.default_rng(3).standard_normal((nvec, cols)).astype(np.float32)
-    for wtype in ("q80", "q40"):
+    for wtype in ("q80", "q40", "q6k"):
         y = _check(wtype, oracle.quantize(wtype, np.zeros((rows, cols), np.float32)), rows, cols, x,
                    debug=False)
         assert np.all(y == 0)
 
 
-def test_vocabulary_projection_64_vectors_sampled():
-    """Q8_0 262144 x 1536 with 64 vectors, the workload the many-vector bench times: the
-    weights are the oracle's tensor (built in row pieces), the product runs whole on the GPU,
-    and 4096 evenly spaced rows are checked against the oracle."""
+@pytest.mark.parametrize("wtype", ["q80", "q6k"])
+def test_vocabulary_projection_64_vectors_sampled(wtype):
+    """262144 x 1536 with 64 vectors, the workloads the many-vector bench times: the weights
+    are the oracle's tensor (built in row pieces), the product runs whole on the GPU, and 4096
+    evenly spaced rows are checked against the oracle."""
     import torch
     import block_quantized_weight_act_amd as qg
-    wl = synth.WORKLOADS["q80_262144x1536"]
+    wl = synth.WORKLOADS["%s_262144x1536" % wtype]
     rows, cols, nvec = wl.rows, wl.cols, 64
-    _say("vocabulary projection", rows, cols, nvec)
+    _say("vocabulary projection", wtype, rows, cols, nvec)
     chunk = 32768
-    parts = [(oracle.quantize("q80", wl.weight_block(r0, min(rows, r0 + chunk))),
+    parts = [(oracle.quantize(wtype, wl.weight_block(r0, min(rows, r0 + chunk))),
               min(chunk, rows - r0)) for r0 in range(0, rows, chunk)]
-    wbuf = oracle.concat_rows("q80", parts, cols)
+    wbuf = oracle.concat_rows(wtype, parts, cols)
     x = np.stack([synth.normal_f32(wl.seed_x + v, 0, cols, 1.0) for v in range(nvec)])
     rq, rd = oracle.quantize_act(x)
     xq, xd = gu.dev(rq), gu.dev(rd)
     y = torch.full((nvec, rows), float("nan"), dtype=torch.float32, device=gu.DEV)
-    nbytes = qg.qgemv_workspace_bytes("q80", rows, cols, nvec)
+    nbytes = qg.qgemv_workspace_bytes(wtype, rows, cols, nvec)
     ws = torch.empty(max(nbytes, 4), dtype=torch.uint8, device=gu.DEV) if nbytes else None
-    qg.qgemv_batch("q80", gu.dev(wbuf), xq, xd, y, rows, cols, nvec, workspace=ws)
+    qg.qgemv_batch(wtype, gu.dev(wbuf), xq, xd, y, rows, cols, nvec, workspace=ws)
     sample = np.linspace(0, rows - 1, 4096).astype(np.int64)
-    sampled = oracle.from_planes([p[sample] for p in oracle.planes("q80", wbuf, rows, cols)])
-    ref = oracle.gemv("q80", sampled, sample.size, cols, rq, rd)
+    sampled = oracle.from_planes([p[sample] for p in oracle.planes(wtype, wbuf, rows, cols)])
+    ref = oracle.gemv(wtype, sampled, sample.size, cols, rq, rd)
     gu.assert_within_bound(gu.host(y)[:, sample], ref)

@@ -124,33 +124,6 @@ def test_workspace_and_limits():
     torch.cuda.synchronize()
 
 
-@pytest.mark.parametrize("wtype,rows,cols,nvec", [
-    ("q6k", 300, 1024, 9), ("q6k", 2048, 8192, 20), ("q6k", 513, 768, 17), ("q6k", 77, 1536, 40),
-    ("q6k", 4000, 2048, 64),
-])
-def test_other_formats_many_vectors_grouped(wtype, rows, cols, nvec):
-    """Q6_K (no matrix-core path) takes more than 8 vectors as groups of up to 8 on the vector
-    kernel: every y within the bound, and each group's y equals that group's own product bit
-    for bit."""
-    import block_quantized_weight_act_amd as qg
-    assert qg.qgemv_route(wtype, rows, cols, nvec) == "grouped"
-    _say("grouped", wtype, rows, cols, nvec)
-    rng = np.random.default_rng(rows + cols + nvec)
-    w = (rng.standard_normal((rows, cols)) * 0.02).astype(np.float32)
-    wbuf = oracle.quantize(wtype, w)
-    x = rng.standard_normal((nvec, cols)).astype(np.float32)
-    rq, rd = oracle.quantize_act(x)
-    xq, xd = gu.quantize_act(x)
-    wt = gu.dev(wbuf)
-    y = gu.gemv(wtype, wt, xq, xd, rows, cols, nvec)
-    gu.assert_within_bound(y, oracle.gemv(wtype, wbuf, rows, cols, rq, rd))
-    for v0 in range(0, nvec, 8):
-        g = min(8, nvec - v0)
-        yg = gu.gemv(wtype, wt, xq[v0:v0 + g].contiguous(), xd[v0:v0 + g].contiguous(), rows,
-                     cols, g)
-        assert np.array_equal(yg.view(np.uint32), y[v0:v0 + g].view(np.uint32))
-
-
 def test_full_size_vocabulary_projection_sampled():
     """The 262144 x 1536 projection with 64 vectors (the launch the bench times): every output
     finite, sampled rows against the oracle's bound, integer partials of sampled rows exact."""
