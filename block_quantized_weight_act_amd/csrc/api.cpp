@@ -424,11 +424,11 @@ int run_mc(const void *w, const int8_t *xq, const float *xd, float *y, int32_t *
     return QGEMV_OK;
 }
 
-// Q8_0 and Q4_0 with more than kMaxVec vectors: the integer matrix cores (gemm_q32.hip), one
-// pass over the weights for up to 256 vectors. Workgroups of 32 x 32 tiles: vw tiles of 32
-// vectors (1, 2 or 4 for 1, 2, 3+ tiles) by 4 / vw tiles of 32 rows; the columns are split
-// when the row tiles and vector groups alone give fewer than two workgroups per CU (the
-// splits added by the ordered reduce).
+// Q8_0, Q4_0 and Q6_K with more than kMaxVec vectors: the integer matrix cores (gemm_q32.hip,
+// gemm_q6k_mc.hip), one pass over the weights for up to 256 vectors. A workgroup covers vw
+// tiles of 32 vectors (1, 2 or 4 for 1, 2, 3+ tiles) by mc32_rows_per_wg(vw) rows; the
+// columns are split when the row tiles and vector groups alone give fewer than two workgroups
+// per CU (the splits added by the ordered reduce).
 bool mc32_ok(int wtype, int64_t rows, int64_t cols, int32_t nvec) {
     return (wtype == QGEMV_Q8_0 || wtype == QGEMV_Q4_0 || wtype == QGEMV_Q6K) && nvec > kMaxVec &&
            nvec <= kMaxBatch &&
@@ -467,15 +467,15 @@ Mc32Plan make_mc32_plan(int64_t rows, int64_t cols, int32_t nvec) {
     Mc32Plan p{};
     const int vtiles = (nvec + 31) / 32;
     p.vw = vtiles >= 3 ? 4 : vtiles;
-    const int rw = 4 / p.vw;
+    const int wg_rows = mc32_rows_per_wg(p.vw);
     p.groups = (vtiles + p.vw - 1) / p.vw;
-    p.row_tiles = static_cast<int>((rows + 32 * rw - 1) / (32 * rw));
+    p.row_tiles = static_cast<int>((rows + wg_rows - 1) / wg_rows);
     const int64_t nb = cols / 32;
-    const int64_t steps = (nb + 3) / 4;
+    const int64_t steps = (nb + 7) / 8;               // the kernels' steps of 8 blocks
     const int64_t base = static_cast<int64_t>(p.row_tiles) * p.groups;
     const int64_t want = 2 * 256;
     const int64_t splits = base < want ? std::min<int64_t>(steps, (want + base - 1) / base) : 1;
-    p.bps = static_cast<int>(4 * ((steps + splits - 1) / splits));
+    p.bps = static_cast<int>(8 * ((steps + splits - 1) / splits));
     p.splits = static_cast<int>((nb + p.bps - 1) / p.bps);
     return p;
 }

@@ -15,13 +15,14 @@
 //    weight block's scale, xd the activation block's scale): y = sum over blocks of
 //    (d * xd) * P in float32.
 //
-// Work split: a workgroup of 4 waves computes 32 RW rows x 32 VW vectors (RW * VW = 4; each
-// wave one 32 x 32 tile) over one column split, in steps of 4 blocks (128 columns; two such
-// workgroups fit a CU's LDS, double buffered). Each step's
-// weights (codes and scales of the workgroup's rows) and activation (codes, scales, block
-// sums of its vectors) are loaded with coalesced 16-byte loads, 4 lanes per 64-byte run,
-// into LDS tiles padded against bank conflicts, double buffered: the next step's loads go out
-// before the current step's products, which read only LDS. A ragged last split reads valid
+// Work split: a workgroup of 4 waves computes 32 RW rows x 32 VG TV vectors (RW * VG = 4; each
+// wave 32 rows x TV tiles of 32 vectors, so the weight operand and the 16 row scales a lane
+// reads from LDS per block serve TV products: those scale reads are most of the LDS traffic)
+// over one column split, in steps of 8 blocks (256 columns). Each step's weights (codes and
+// scales of the workgroup's rows) and activation (codes, scales, block sums of its vectors) are
+// loaded with coalesced 16-byte loads, 8 lanes per 128-byte line, into LDS tiles padded
+// against bank conflicts; the next step's loads go out into registers before the current
+// step's products, which read only LDS (one LDS buffer: two or three workgroups fit a CU). A ragged last split reads valid
 // blocks against zero activation codes, so the extra blocks add exactly 0; rows past the
 // matrix read its last row and are not stored.
 //
@@ -34,7 +35,7 @@
 #include <atomic>
 
 #include "device_common.h"
-#include "qgemv_internal.h"
+#include "gemm_mc.h"
 
 namespace qgemv {
 
@@ -43,25 +44,31 @@ namespace {
 typedef int v4i_t __attribute__((ext_vector_type(4)));
 typedef int v16i_t __attribute__((ext_vector_type(16)));
 
-constexpr int kStep = 4;                              // 32-weight blocks per step
-// LDS row pitches, padded by 16 bytes so that the 32 rows a read touches fall in distinct banks
-// (16-lane groups)
-template <int FMT>
-__host__ __device__ constexpr int wpitch() { return (FMT == kTypeQ80 ? 32 : 16) * kStep + 16; }
-constexpr int kXPitch = 32 * kStep + 16;
+// LDS row pitches for steps of KS blocks, padded by 16 bytes so that the 32 rows a read
+// touches fall in distinct banks (16-lane groups)
+template <int FMT, int KS>
+__host__ __device__ constexpr int wpitch() { return (FMT == kTypeQ80 ? 32 : 16) * KS + 16; }
+template <int KS>
+__host__ __device__ constexpr int xpitch() { return 32 * KS + 16; }
 
-// LDS of one buffer: weight codes [32 RW rows][pitch], weight scales [8 blocks][32 RW] float,
-// activation codes [32 VW vectors][pitch], activation scales and block sums [8][32 VW] each.
-template <int FMT, int RW, int VW>
+// LDS of one step's buffer: weight codes [32 RW rows][pitch], weight scales [KS blocks][32 RW]
+// float, activation codes [32 VW vectors][pitch], activation scales and block sums [KS][32 VW]
+// each (VW = VG TV vector tiles).
+template <int FMT, int RW, int VW, int KS>
 __host__ __device__ constexpr int q32_buf_bytes() {
-    return 32 * RW * wpitch<FMT>() + kStep * 32 * RW * 4 + 32 * VW * kXPitch +
-           2 * kStep * 32 * VW * 4;
+    return 32 * RW * wpitch<FMT, KS>() + KS * 32 * RW * 4 + 32 * VW * xpitch<KS>() +
+           2 * KS * 32 * VW * 4;
 }
 
-template <int FMT, int RW, int VW, bool DBG>
+template <int FMT, int RW, int VG, int TV, int KS, bool DBG>
 __global__ void __launch_bounds__(256) gemm_q32_mc_kernel(GemmArgs a) {
-    constexpr int WP = wpitch<FMT>();
-    constexpr int BUF = q32_buf_bytes<FMT, RW, VW>();
+    static_assert(RW * VG == 4, "four waves");
+    static_assert(KS == 4 || KS == 8, "steps of 4 blocks (two buffers) or 8 (one buffer)");
+    constexpr int kStep = KS;
+    constexpr int VW = VG * TV;                       // vector tiles of the workgroup
+    constexpr int WP = wpitch<FMT, KS>();
+    constexpr int kXPitch = xpitch<KS>();
+    constexpr int BUF = q32_buf_bytes<FMT, RW, VW, KS>();
     // codes chunks (16 bytes) of the weight tile and of the activation tile per step
     constexpr int kWChunks = 32 * RW * kStep * (FMT == kTypeQ80 ? 2 : 1);
     constexpr int kXChunks = 32 * VW * kStep * 2;
@@ -74,7 +81,7 @@ __global__ void __launch_bounds__(256) gemm_q32_mc_kernel(GemmArgs a) {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int rw = wave / VW, vw = wave % VW;
+    const int rw = wave / VG, vg = wave % VG;
     const int rows = a.rows, nb = a.nb, nvec = a.nvec;
     const int64_t cols = static_cast<int64_t>(nb) * 32;
     // work item: (row tile, vector group, column split)
@@ -192,16 +199,20 @@ __global__ void __launch_bounds__(256) gemm_q32_mc_kernel(GemmArgs a) {
         }
     };
 
-    // ---- this lane's place in its wave's 32 x 32 tile ----
+    // ---- this lane's place in its wave's tiles: vector l % 32 of each, 16 rows ----
     const int l32 = lane & 31, h = lane >> 5;
-    const int my_vec = v0 + vw * 32 + l32;            // the output vector of this lane
-    float acc[16];
+    float acc[TV][16];
 #pragma unroll
-    for (int i = 0; i < 16; i++) acc[i] = 0.0f;
+    for (int t = 0; t < TV; t++)
+#pragma unroll
+        for (int i = 0; i < 16; i++) acc[t][i] = 0.0f;
 
     issue(0);
     for (int step = 0; step < steps; step++) {
-        const int buf = step & 1;
+        // two buffers: the step's buffer was last read two steps ago, before the barrier of
+        // the last step; one buffer: wait until every wave is done with the last step
+        const int buf = KS == 4 ? (step & 1) : 0;
+        if (KS == 8 && step > 0) __syncthreads();
         store(buf, step);
         __syncthreads();
         if (step + 1 < steps) issue(step + 1);
@@ -212,7 +223,6 @@ __global__ void __launch_bounds__(256) gemm_q32_mc_kernel(GemmArgs a) {
         const uint8_t *xq = base + 32 * RW * WP + kStep * 32 * RW * 4;
         const float *xs = reinterpret_cast<const float *>(xq + 32 * VW * kXPitch);
         const int *xsum = reinterpret_cast<const int *>(xs + kStep * 32 * VW);
-        const uint8_t *xrow = xq + (vw * 32 + l32) * kXPitch;
         const int nblk = min(kStep, b_hi - (b_lo + step * kStep));
 #pragma unroll
         for (int k = 0; k < kStep; k++) {
@@ -228,11 +238,14 @@ __global__ void __launch_bounds__(256) gemm_q32_mc_kernel(GemmArgs a) {
                               static_cast<int>((raw.z >> (4 * h)) & 0x0F0F0F0Fu),
                               static_cast<int>((raw.w >> (4 * h)) & 0x0F0F0F0Fu)};
                 }
-                const v4i_t B = *reinterpret_cast<const v4i_t *>(xrow + k * 32 + 16 * h);
-                const v16i_t zero = {};
-                const v16i_t P = __builtin_amdgcn_mfma_i32_32x32x32_i8(A, B, zero, 0, 0, 0);
-                const float xdv = xs[k * 32 * VW + vw * 32 + l32];
-                const int s8 = FMT == kTypeQ40 ? 8 * xsum[k * 32 * VW + vw * 32 + l32] : 0;
+                v16i_t P[TV];
+#pragma unroll
+                for (int t = 0; t < TV; t++) {
+                    const uint8_t *xrow = xq + ((vg * TV + t) * 32 + l32) * kXPitch;
+                    const v4i_t B = *reinterpret_cast<const v4i_t *>(xrow + k * 32 + 16 * h);
+                    const v16i_t zero = {};
+                    P[t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(A, B, zero, 0, 0, 0);
+                }
                 float dv[16];
 #pragma unroll
                 for (int qq = 0; qq < 4; qq++) {
@@ -244,15 +257,22 @@ __global__ void __launch_bounds__(256) gemm_q32_mc_kernel(GemmArgs a) {
                     dv[4 * qq + 3] = f.w;
                 }
 #pragma unroll
-                for (int i = 0; i < 16; i++) {
-                    const int p = FMT == kTypeQ40 ? P[i] - s8 : P[i];   // exact integer
-                    if constexpr (DBG) {
-                        const int row = row0 + rw * 32 + 8 * (i / 4) + 4 * h + i % 4;
-                        const int gb = b_lo + step * kStep + k;
-                        if (row < rows && my_vec < nvec)
-                            a.P[(static_cast<int64_t>(my_vec) * rows + row) * nb + gb] = p;
-                    } else {
-                        acc[i] = fmaf(dv[i] * xdv, static_cast<float>(p), acc[i]);
+                for (int t = 0; t < TV; t++) {
+                    const int vl = (vg * TV + t) * 32 + l32;
+                    const float xdv = xs[k * 32 * VW + vl];
+                    const int s8 = FMT == kTypeQ40 ? 8 * xsum[k * 32 * VW + vl] : 0;
+#pragma unroll
+                    for (int i = 0; i < 16; i++) {
+                        const int p = FMT == kTypeQ40 ? P[t][i] - s8 : P[t][i];   // exact integer
+                        if constexpr (DBG) {
+                            const int row = row0 + rw * 32 + 8 * (i / 4) + 4 * h + i % 4;
+                            const int gb = b_lo + step * kStep + k;
+                            const int v = v0 + vl;
+                            if (row < rows && v < nvec)
+                                a.P[(static_cast<int64_t>(v) * rows + row) * nb + gb] = p;
+                        } else {
+                            acc[t][i] = fmaf(dv[i] * xdv, static_cast<float>(p), acc[t][i]);
+                        }
                     }
                 }
             }
@@ -260,50 +280,57 @@ __global__ void __launch_bounds__(256) gemm_q32_mc_kernel(GemmArgs a) {
         __builtin_amdgcn_sched_barrier(0);
     }
 
-    if (!DBG && my_vec < nvec) {
-        float *yv = a.out + (static_cast<int64_t>(sp) * nvec + my_vec) * rows;
+    if constexpr (!DBG) {
 #pragma unroll
-        for (int qq = 0; qq < 4; qq++) {
-            const int row = row0 + rw * 32 + 8 * qq + 4 * h;
+        for (int t = 0; t < TV; t++) {
+            const int v = v0 + (vg * TV + t) * 32 + l32;
+            if (v < nvec) {
+                float *yv = a.out + (static_cast<int64_t>(sp) * nvec + v) * rows;
 #pragma unroll
-            for (int i = 0; i < 4; i++)
-                if (row + i < rows) yv[row + i] = acc[4 * qq + i];
+                for (int qq = 0; qq < 4; qq++) {
+                    const int row = row0 + rw * 32 + 8 * qq + 4 * h;
+#pragma unroll
+                    for (int i = 0; i < 4; i++)
+                        if (row + i < rows) yv[row + i] = acc[t][4 * qq + i];
+                }
+            }
         }
     }
 }
 
-template <int FMT, int RW, int VW>
+template <int FMT, int RW, int VG, int TV, int KS>
 hipError_t launch_rv(const GemmArgs &a, bool debug, hipStream_t stream) {
-    const size_t lds = 2 * static_cast<size_t>(q32_buf_bytes<FMT, RW, VW>());
+    const size_t lds = static_cast<size_t>(q32_buf_bytes<FMT, RW, VG * TV, KS>()) * (KS == 4 ? 2 : 1);
     const int64_t items = static_cast<int64_t>(a.row_tiles) * a.groups * a.splits;
     if (items < 1 || items > 0x7FFFFFFF) return hipErrorInvalidValue;
     const dim3 grid(static_cast<unsigned>(items));
     if (debug)
-        hipLaunchKernelGGL((gemm_q32_mc_kernel<FMT, RW, VW, true>), grid, dim3(256), lds, stream, a);
+        hipLaunchKernelGGL((gemm_q32_mc_kernel<FMT, RW, VG, TV, KS, true>), grid, dim3(256), lds, stream, a);
     else
-        hipLaunchKernelGGL((gemm_q32_mc_kernel<FMT, RW, VW, false>), grid, dim3(256), lds, stream, a);
+        hipLaunchKernelGGL((gemm_q32_mc_kernel<FMT, RW, VG, TV, KS, false>), grid, dim3(256), lds, stream, a);
     return hipGetLastError();
 }
 
+// The workgroup shapes (mc32_rows_per_wg): 128 rows x 32 vectors, 128 x 64, 64 x 128.
 template <int FMT>
-hipError_t launch_fmt(const GemmArgs &a, int vw, bool debug, hipStream_t stream) {
-    switch (vw) {
-        case 1: return launch_rv<FMT, 4, 1>(a, debug, stream);
-        case 2: return launch_rv<FMT, 2, 2>(a, debug, stream);
-        case 4: return launch_rv<FMT, 1, 4>(a, debug, stream);
+hipError_t launch_fmt(const GemmArgs &a, int vt, bool debug, hipStream_t stream) {
+    switch (vt) {
+        case 1: return launch_rv<FMT, 4, 1, 1, mc32_step_blocks(FMT, 1)>(a, debug, stream);
+        case 2: return launch_rv<FMT, 4, 1, 2, mc32_step_blocks(FMT, 2)>(a, debug, stream);
+        case 4: return launch_rv<FMT, 2, 2, 2, mc32_step_blocks(FMT, 4)>(a, debug, stream);
         default: return hipErrorInvalidValue;
     }
 }
 
 }  // namespace
 
-hipError_t launch_gemm_q32_mc(int wtype, const GemmArgs &a, int vw, bool debug,
+hipError_t launch_gemm_q32_mc(int wtype, const GemmArgs &a, int vt, bool debug,
                               hipStream_t stream) {
-    if (a.sb_per_split < 1 || a.sb_per_split % kStep != 0 || a.row_tiles < 1 || a.groups < 1 ||
+    if (a.sb_per_split < 1 || a.sb_per_split % 8 != 0 || a.row_tiles < 1 || a.groups < 1 ||
         a.splits < 1 || a.nvec < 1 || a.nvec > kMaxBatch)
         return hipErrorInvalidValue;
-    if (wtype == kTypeQ80) return launch_fmt<kTypeQ80>(a, vw, debug, stream);
-    if (wtype == kTypeQ40) return launch_fmt<kTypeQ40>(a, vw, debug, stream);
+    if (wtype == kTypeQ80) return launch_fmt<kTypeQ80>(a, vt, debug, stream);
+    if (wtype == kTypeQ40) return launch_fmt<kTypeQ40>(a, vt, debug, stream);
     return hipErrorInvalidValue;
 }
 

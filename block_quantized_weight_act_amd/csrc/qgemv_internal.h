@@ -221,12 +221,6 @@ hipError_t launch_gemm_q4k_i8(const GemmArgs &a, int waves, bool debug, hipStrea
 constexpr size_t kScratchBytes = size_t{32} << 20;
 int scratch_address(void **ptr);
 
-// Q8_0 / Q4_0 with 9..kMaxBatch vectors on the integer matrix cores (gemm_q32.hip): workgroups
-// of 32 (4 / vw) rows x 32 vw vectors (vw = 1, 2, 4) over column splits of sb_per_split
-// 32-weight blocks (a multiple of 4); row_tiles of 32 (4 / vw) rows, groups of 32 vw vectors;
-// out [splits][nvec][rows]; with debug, P [nvec][rows][cols/32] and S [nvec][cols/32] instead.
-hipError_t launch_gemm_q32_mc(int wtype, const GemmArgs &a, int vw, bool debug,
-                              hipStream_t stream);
 
 // Host: record a HIP error (or a message) as this thread's last error text and return the
 // status the C ABI reports (QGEMV_EHIP, or `status`).

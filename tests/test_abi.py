@@ -301,9 +301,9 @@ def test_matrix_core_path_limits_on_the_host():
     assert qg.qgemv_workspace_bytes("q4k", 256, 2048, 64) > 0          # few rows: split
     # enough rows: no split, only the staged activation tiles (8 super-blocks x 64 vectors)
     assert qg.qgemv_workspace_bytes("q4k", 1 << 16, 2048, 64) == 8 * 2 * 18432
-    # Q6_K takes the plan of the 32-weight formats' matrix-core path: 4 row tiles of 64 rows,
-    # 16 splits of 4 blocks
-    assert qg.qgemv_workspace_bytes("q6k", 256, 2048, 64) == 16 * 64 * 256 * 4
+    # Q6_K takes the plan of the 32-weight formats' matrix-core path: 2 row tiles of 128 rows,
+    # 8 splits of one 8-block step
+    assert qg.qgemv_workspace_bytes("q6k", 256, 2048, 64) == 8 * 64 * 256 * 4
     assert qg.qgemv_workspace_bytes("q6k", 256, 2048, 64) == qg.qgemv_workspace_bytes("q80", 256, 2048, 64)
     assert qg.qgemv_workspace_bytes("q4k", 256, 2048, 257) == 0
     assert _call_batch(nvec=257) == EINVAL
@@ -320,7 +320,8 @@ def test_mc32_workspace_and_limits():
     """Q8_0 / Q4_0 with many vectors: partial sums only when the columns are split (few rows),
     refused before any launch without them; more than 256 vectors refused."""
     assert qg.qgemv_workspace_bytes("q80", 262144, 1536, 64) == 0
-    assert qg.qgemv_workspace_bytes("q40", 16384, 2048, 64) == 2 * 64 * 16384 * 4
+    # 128-row workgroups (64 vectors): 128 row tiles, so the columns are split in 4
+    assert qg.qgemv_workspace_bytes("q40", 16384, 2048, 64) == 4 * 64 * 16384 * 4
     assert _call_batch(wtype=3, rows=16384, cols=2048, nvec=64) == EWORKSPACE
     assert _call_batch(wtype=4, nvec=257) == EINVAL
     assert _call_batch(wtype=4, cols=1000, nvec=20) == EINVAL
