@@ -516,6 +516,14 @@ def bench_group(args) -> dict:
     multi_bytes = wbytes + codes + ybytes
     t, nc = qg.qgemv_multi_geometry(cols, nvec)
     achieved = step_bytes / (ms["step"] * 1e-3) / 1e9
+    roof_gbs = step_bytes / (ms_graph["step"] * 1e-3) / 1e9
+    # one format: the one-format walk; several: the kernel that splits its grid between them
+    formats = sorted({p.wtype for p in grp.parts})
+    if len(formats) == 1:
+        multi_kernel = "gemv_multi_fmt_kernel<qgemv::%s, %d, %d, %d, 2>" % (
+            {"q4k": "Q4K", "q6k": "Q6K", "q40": "Q40", "q80": "Q80"}[formats[0]], nvec, t, nc)
+    else:
+        multi_kernel = "gemv_multi_kernel<%d, %d, %d, 2>" % (nvec, t, nc)
     out = {
         "metric": "achieved HBM GB/s and % of roofline, multi-matrix GEMV sharing one activation",
         "value": round(achieved, 1),
@@ -545,11 +553,13 @@ def bench_group(args) -> dict:
                          "us_per_fused_each": round(ms_graph["fused_each"] * 1e3, 3),
                          "us_per_separate": round(ms_graph["separate"] * 1e3, 3)},
         "us_per_step_distribution": step_dist,
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "gemv_multi_kernel<%d, %d, %d, 2>" % (nvec, t, nc),
+        "roofline": {"bound": "hbm", "achieved": round(roof_gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(roof_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": multi_kernel,
                      "algorithmic_bytes_per_launch": step_bytes,
-                     "us_per_launch": round(ms["step"] * 1e3, 3)},
+                     "us_per_launch": round(ms_graph["step"] * 1e3, 3),
+                     "statistic": "mean launch time over a graph replay of back-to-back steps "
+                                  "(HIP events on the replay stream)"},
         "multi_from_codes_gbs": round(multi_bytes / (ms["multi"] * 1e-3) / 1e9, 1),
         "setup_s": round(setup_s, 1),
     }
@@ -897,13 +907,17 @@ def bench_many(args, wl) -> dict:
         # the integer matrix cores (int8 products; 9..16 vectors)
         kernel = "gemm_q4k_i8_kernel<0, %d, " % ((nvec + 7) // 8)
     elif route == "mc32":
+        # the workgroup shape by vector tiles (1, 2, 4): Q8_0 / Q4_0 rows, vector groups, tiles
+        # per wave; Q6_K row groups, vector tiles, row tiles per wave; then blocks per step
         vtiles = (nvec + 31) // 32
-        vw = 4 if vtiles >= 3 else vtiles
+        vt = 4 if vtiles >= 3 else vtiles
         if wl.wtype == "q6k":
-            kernel = "gemm_q6k_mc_kernel<%d, %d, false>" % (4 // vw, vw)
+            kernel = "gemm_q6k_mc_kernel<%d, %d, %d, 8, false>" % {1: (4, 1, 1), 2: (2, 2, 2),
+                                                                  4: (1, 4, 2)}[vt]
         else:
-            kernel = "gemm_q32_mc_kernel<%d, %d, %d, false>" % (4 if wl.wtype == "q80" else 3,
-                                                                4 // vw, vw)
+            ks = 4 if wl.wtype == "q40" and vt == 2 else 8
+            kernel = "gemm_q32_mc_kernel<%d, %d, %d, %d, %d, false>" % (
+                (4 if wl.wtype == "q80" else 3,) + {1: (4, 1, 1), 2: (4, 1, 2), 4: (2, 2, 2)}[vt] + (ks,))
     else:
         kernel = "gemm_q4k_mfma_kernel<%d, false>" % min(4, (nvec + 31) // 32)
     t_mfma = flops / (mfma_peak * 1e12)
