@@ -342,10 +342,11 @@ def test_fused_quantize_and_gemv(wtype, rows, cols, nvec):
 @pytest.mark.parametrize("rows,cols,nvec", [(37, 16384, 1), (200, 12288, 2), (91, 8192, 3),
                                             (64, 4096, 5), (19, 4096, 8)])
 def test_split_inside_workgroup_matches_two_pass(wtype, rows, cols, nvec):
-    """Rows wider than one pass: from codes the column split runs inside the workgroup (the
-    chunks' sums added in LDS), while the one-launch fused form without code outputs writes
-    them to the workspace and adds them in a second launch. Both add the chunks in ascending
-    order, so y must agree bit for bit, and lie within the oracle's bound."""
+    """Rows wider than one pass (two column chunks): from codes the column split runs inside
+    the workgroup (the chunks' sums added in LDS); the one-launch fused form without code
+    outputs does the same after its workgroup quantized both chunks into LDS. Both add the
+    chunks in ascending order, so y must agree bit for bit, and lie within the oracle's
+    bound."""
     import torch
     import block_quantized_weight_act_amd as qg
     _say("split-in-workgroup", wtype, rows, cols, nvec)
@@ -365,6 +366,42 @@ def test_split_inside_workgroup_matches_two_pass(wtype, rows, cols, nvec):
     y_two = torch.full_like(y_in, float("nan"))
     qg.qgemv_fused(wtype, wd, gu.dev(x), y_two, rows, cols, nvec, workspace=ws)
     a, b = gu.host(y_in), gu.host(y_two)
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    rq, rd = oracle.quantize_act(x)
+    gu.assert_within_bound(a, oracle.gemv(wtype, wbuf, rows, cols, rq, rd))
+
+
+@pytest.mark.parametrize("wtype", ALL)
+@pytest.mark.parametrize("rows,cols,nvec", [(19, 16384, 8), (40, 65536, 1)])
+def test_fused_split_beyond_lds_takes_two_passes(wtype, rows, cols, nvec):
+    """Eight column chunks whose quantized slices (36 bytes per activation block per chunk:
+    147 KB and 74 KB) do not fit in a workgroup's 64 KiB of LDS: the fused form without code
+    outputs quantizes each chunk in its own workgroups, writes the chunks' sums to the
+    workspace (filled with NaN first) and adds them in a second launch, in ascending order.
+    From codes the eight chunks are split inside the workgroup. y agrees bit for bit and lies
+    within the oracle's bound."""
+    import torch
+    import block_quantized_weight_act_amd as qg
+    _say("fused split beyond LDS", wtype, rows, cols, nvec)
+    plan = qg.qgemv_plan_for(wtype, rows, cols, nvec)
+    assert plan["lanes_per_row"] == 64 and plan["splits"] == 8, plan
+    assert qg.qgemv_route(wtype, rows, cols, nvec) == "vector"
+    assert qg.qgemv_fused_launches(wtype, rows, cols, nvec, 0) == 1
+    rng = np.random.default_rng(rows * 3 + cols + nvec)
+    w = (rng.standard_normal((rows, cols)) * 0.02).astype(np.float32)
+    x = rng.standard_normal((nvec, cols)).astype(np.float32)
+    wbuf = _quant(wtype, w)
+    wd = gu.dev(wbuf)
+    xq, xd = gu.quantize_act(x)
+    nbytes = qg.qgemv_workspace_bytes(wtype, rows, cols, nvec)
+    assert nbytes == 8 * nvec * rows * 4
+    ws = torch.full((nbytes,), 0xFF, dtype=torch.uint8, device=gu.DEV)
+    y_codes = torch.full((nvec, rows), float("nan"), dtype=torch.float32, device=gu.DEV)
+    qg.qgemv_batch(wtype, wd, xq, xd, y_codes, rows, cols, nvec, workspace=ws)
+    ws.fill_(0xFF)
+    y_fused = torch.full_like(y_codes, float("nan"))
+    qg.qgemv_fused(wtype, wd, gu.dev(x), y_fused, rows, cols, nvec, workspace=ws)
+    a, b = gu.host(y_codes), gu.host(y_fused)
     assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
     rq, rd = oracle.quantize_act(x)
     gu.assert_within_bound(a, oracle.gemv(wtype, wbuf, rows, cols, rq, rd))
