@@ -18,22 +18,20 @@
 // Work split: a workgroup of 4 waves computes 32 RW rows x 32 VG TV vectors (RW * VG = 4; each
 // wave 32 rows x TV tiles of 32 vectors, so the weight operand and the 16 row scales a lane
 // reads from LDS per block serve TV products: those scale reads are most of the LDS traffic)
-// over one column split, in steps of 8 blocks (256 columns). Each step's weights (codes and
-// scales of the workgroup's rows) and activation (codes, scales, block sums of its vectors) are
-// loaded with coalesced 16-byte loads, 8 lanes per 128-byte line, into LDS tiles padded
-// against bank conflicts; the next step's loads go out into registers before the current
-// step's products, which read only LDS (one LDS buffer: two or three workgroups fit a CU). A ragged last split reads valid
-// blocks against zero activation codes, so the extra blocks add exactly 0; rows past the
-// matrix read its last row and are not stored.
+// over one column split, in steps of KS blocks. Each step's weights (codes and scales of the
+// workgroup's rows) and activation (codes, scales, block sums of its vectors) are loaded with
+// coalesced 16-byte loads into LDS tiles padded against bank conflicts; the next step's loads
+// go out into registers before the current step's products, which read only LDS. KS = 8: 8
+// lanes per 128-byte line of each codes plane, one LDS buffer (two or three workgroups per CU);
+// KS = 4: half lines, two LDS buffers (mc32_step_blocks picks by format and shape). A ragged
+// last step reads valid blocks against zero activation codes, so the extra blocks add exactly
+// 0; rows past the matrix read its last row and are not stored.
 //
 // Lane layout of the 32 x 32 x 32 product (checked on gfx950): operand lane l holds row (or
 // column) l % 32 and K slots 16 (l / 32) .. + 15; result element i is row 8 (i / 4) +
 // 4 (l / 32) + i % 4, column l % 32. Here the weights are the row operand (32 weight rows),
 // the activation the column operand (32 vectors): lane l of a wave owns vector l % 32 and
 // 16 rows of its tile.
-#include <algorithm>
-#include <atomic>
-
 #include "device_common.h"
 #include "gemm_mc.h"
 
