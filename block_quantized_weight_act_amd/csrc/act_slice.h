@@ -2,7 +2,7 @@
 // vector, the 32 int8 codes (8 words) and the float32 scale of that 32-column activation
 // block. Either read from memory (codes and scales made by qgemv_quantize_act) or, in the
 // fused form, quantized by the workgroup itself into LDS with the same arithmetic
-// (quantize_act_quad), so one launch does both steps of the product.
+// (quantize_act_oct), so one launch does both steps of the product.
 //
 // Getting the slice is split in two so that a kernel can put its first weight loads between
 // the halves: act_slice_issue starts the slice's global loads, act_slice_finish consumes
@@ -21,15 +21,15 @@
 namespace qgemv {
 
 // Shape of the fused form's work: the workgroup's column chunk holds kBlocks activation
-// blocks (all vectors), kQuads groups of 4 elements; each lane takes up to kSlots quads per
-// round (quad base + i * a.threads + threadIdx.x of round base). kSlots is sized so that
-// one round of a 256-thread workgroup covers the chunk (at most 4 quads per lane; smaller
-// workgroups and larger chunks take more rounds).
+// blocks (all vectors), kOcts groups of 8 elements, a block per 4 lanes (a DPP quad); each lane
+// takes up to kSlots octs per round (oct base + i * a.threads + threadIdx.x of round base).
+// kSlots is sized so that one round of a 256-thread workgroup covers the chunk (at most 2
+// octs per lane; smaller workgroups and larger chunks take more rounds).
 template <int V, int T, int NC>
 struct FusedAct {
     static constexpr int kBlocks = V * T * NC;
-    static constexpr int kQuads = kBlocks * 8;
-    static constexpr int kSlots = kQuads >= 4 * 256 ? 4 : (kQuads + 255) / 256;
+    static constexpr int kOcts = kBlocks * 4;
+    static constexpr int kSlots = kOcts >= 2 * 256 ? 2 : (kOcts + 255) / 256;
 };
 
 // LDS bytes the fused form needs: 32 code bytes and one float32 scale per block of the slice
@@ -45,69 +45,73 @@ struct ChunkSpan {
 };
 
 // What act_slice_issue leaves in flight for act_slice_finish: the fused form's first round of
-// float32 quads (the plain form loads straight into the slice registers).
+// float32 octs (the plain form loads straight into the slice registers).
 template <int V, int T, int NC, bool FUSED>
 struct ActPending {
-    float4 xv[FUSED ? FusedAct<V, T, NC>::kSlots : 1];
+    float4 xv[FUSED ? FusedAct<V, T, NC>::kSlots : 1][2];
 };
 
 namespace fused_detail {
 
-// Quad qd of the span: block blk = qd / 8 is vector blk / (nch T NC) and column block
-// ch0 T NC + blk % (nch T NC); elem is the offset of its 4 floats in x (and of its codes in
-// xq_out). True when the quad exists.
+// Oct od of the span: block blk = od / 4 is vector blk / (nch T NC) and column block
+// ch0 T NC + blk % (nch T NC); elem is the offset of its 8 floats in x (and of its codes in
+// xq_out). True when the oct exists (the same for the 4 octs of a block).
 template <int V, int T, int NC>
-__device__ __forceinline__ bool quad_at(const GemvArgs &a, const ChunkSpan &sp, int qd,
-                                        int64_t &elem, int &v, int &gc) {
-    const int blk = qd >> 3;
+__device__ __forceinline__ bool oct_at(const GemvArgs &a, const ChunkSpan &sp, int od,
+                                       int64_t &elem, int &v, int &gc) {
+    const int blk = od >> 2;
     const int span = sp.nch * T * NC;
     v = blk / span;
     gc = sp.ch0 * T * NC + (blk - v * span);
     elem = v * (static_cast<int64_t>(a.nchunks) * 32) + 32 * static_cast<int64_t>(gc) +
-           4 * (qd & 7);
-    return qd < FusedAct<V, T, NC>::kQuads * sp.nch && gc < a.nchunks;
+           8 * (od & 3);
+    return od < FusedAct<V, T, NC>::kOcts * sp.nch && gc < a.nchunks;
 }
 
 template <int V, int T, int NC>
 __device__ __forceinline__ void load_round(const GemvArgs &a, const ChunkSpan &sp, int base,
-                                           float4 (&xv)[FusedAct<V, T, NC>::kSlots]) {
+                                           float4 (&xv)[FusedAct<V, T, NC>::kSlots][2]) {
 #pragma unroll
     for (int i = 0; i < FusedAct<V, T, NC>::kSlots; i++) {
         int64_t elem;
         int v, gc;
-        const bool ok = quad_at<V, T, NC>(
+        const bool ok = oct_at<V, T, NC>(
             a, sp, base + i * a.threads + static_cast<int>(threadIdx.x), elem, v, gc);
-        xv[i] = ok ? *reinterpret_cast<const float4 *>(a.x + elem)
-                   : make_float4(0.f, 0.f, 0.f, 0.f);
+        const float4 *p = reinterpret_cast<const float4 *>(a.x + elem);
+        xv[i][0] = ok ? p[0] : make_float4(0.f, 0.f, 0.f, 0.f);
+        xv[i][1] = ok ? p[1] : make_float4(0.f, 0.f, 0.f, 0.f);
     }
 }
 
-// Quantize one round into LDS (codes word qd, then the scale of block qd / 8 after all the
-// span's codes); the first workgroup of the span also stores them to xq_out / xd_out.
+// Quantize one round into LDS (codes words 2 od, 2 od + 1, then the scale of block od / 4
+// after all the span's codes); the first workgroup of the span also stores them to xq_out /
+// xd_out (4-byte stores: xq_out need only be 4-byte aligned).
 template <int V, int T, int NC>
 __device__ __forceinline__ void store_round(const GemvArgs &a, const ChunkSpan &sp, int base,
-                                            const float4 (&xv)[FusedAct<V, T, NC>::kSlots]) {
+                                            const float4 (&xv)[FusedAct<V, T, NC>::kSlots][2]) {
     using F = FusedAct<V, T, NC>;
     extern __shared__ uint4 lds[];
-    const int quads = F::kQuads * sp.nch;
-    uint32_t *s_codes = reinterpret_cast<uint32_t *>(lds);
+    const int octs = F::kOcts * sp.nch;
+    uint2 *s_codes = reinterpret_cast<uint2 *>(lds);
     float *s_scale = reinterpret_cast<float *>(lds + 2 * F::kBlocks * sp.nch);
 #pragma unroll
     for (int i = 0; i < F::kSlots; i++) {
         const int first = base + i * a.threads;   // the same for the workgroup
-        if (first >= quads) break;
-        const int qd = first + static_cast<int>(threadIdx.x);
+        if (first >= octs) break;
+        const int od = first + static_cast<int>(threadIdx.x);
         int64_t elem;
         int v, gc;
-        const bool ok = quad_at<V, T, NC>(a, sp, qd, elem, v, gc);
-        const ActQuad q = quantize_act_quad(xv[i]);   // every lane: the block max is cross-lane
-        if (qd < quads) {
-            s_codes[qd] = q.codes;
-            if ((qd & 7) == 0) s_scale[qd >> 3] = q.scale;
+        const bool ok = oct_at<V, T, NC>(a, sp, od, elem, v, gc);
+        const ActOct q = quantize_act_oct(xv[i][0], xv[i][1]);   // every lane: DPP over 4
+        if (od < octs) {
+            s_codes[od] = make_uint2(q.lo, q.hi);
+            if ((od & 3) == 0) s_scale[od >> 2] = q.scale;
         }
         if (ok && blockIdx.x == 0 && a.xq_out != nullptr) {
-            *reinterpret_cast<uint32_t *>(a.xq_out + elem) = q.codes;
-            if ((qd & 7) == 0) a.xd_out[static_cast<int64_t>(v) * a.nchunks + gc] = q.scale;
+            uint32_t *dst = reinterpret_cast<uint32_t *>(a.xq_out + elem);
+            dst[0] = q.lo;
+            dst[1] = q.hi;
+            if ((od & 3) == 0) a.xd_out[static_cast<int64_t>(v) * a.nchunks + gc] = q.scale;
         }
     }
 }
@@ -154,9 +158,9 @@ __device__ __forceinline__ void act_slice_finish(const GemvArgs &a, const ChunkS
     if constexpr (FUSED) {
         using F = FusedAct<V, T, NC>;
         const int round = F::kSlots * a.threads;
-        const int quads = F::kQuads * sp.nch;
+        const int octs = F::kOcts * sp.nch;
         fused_detail::store_round<V, T, NC>(a, sp, 0, pend.xv);
-        for (int base = round; base < quads; base += round) {
+        for (int base = round; base < octs; base += round) {
             fused_detail::load_round<V, T, NC>(a, sp, base, pend.xv);
             fused_detail::store_round<V, T, NC>(a, sp, base, pend.xv);
         }

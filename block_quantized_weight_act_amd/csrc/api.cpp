@@ -240,6 +240,14 @@ int check_fused_act(const Activation &act, const void *w, size_t wbytes, const v
     return QGEMV_OK;
 }
 
+// Waves per workgroup of the column split inside the workgroup: the plan's, when its sets of
+// `splits` waves divide it, else as many whole sets as the kernel's wave limit allows.
+int split_waves_per_block(const qgemv_plan &plan, int maxw) {
+    return plan.splits <= maxw && plan.waves_per_block % plan.splits == 0
+               ? plan.waves_per_block
+               : plan.splits * std::max(1, maxw / plan.splits);
+}
+
 int run_gemv(int wtype, const void *w, const Activation &act, float *y, int64_t rows,
              int64_t cols, int32_t nvec, const qgemv_plan &plan_in, void *ws, size_t ws_bytes,
              hipStream_t stream) {
@@ -290,9 +298,7 @@ int run_gemv(int wtype, const void *w, const Activation &act, float *y, int64_t 
     // of all chunks must fit in LDS. The workspace is still required (the ABI's contract is
     // per shape), though not touched.
     const int maxw = gemv_max_waves(nvec, plan.lanes_per_row, plan.chunks_per_lane);
-    const int wpb = plan.splits <= maxw && plan.waves_per_block % plan.splits == 0
-                        ? plan.waves_per_block
-                        : plan.splits * std::max(1, maxw / plan.splits);
+    const int wpb = split_waves_per_block(plan, maxw);
     const bool in_wg = need > 0 && plan.splits <= maxw &&
                        (!act.x || gemv_split_lds_bytes(nvec, plan.lanes_per_row, plan.chunks_per_lane,
                                                        true, plan.splits, wpb) <= kMaxSplitLds);
@@ -980,24 +986,42 @@ int qgemv_fused_launches(int wtype, int64_t rows, int64_t cols, int32_t nvec, in
     // running the product from the codes was measured faster than every workgroup quantizing
     // the split's activation itself.
     if (i8_auto(wtype, rows, cols, nvec)) return 2;
-    // Every workgroup of the fused kernel quantizes the whole activation slice its lanes read,
-    // groups of 4 elements spread over its lanes. That costs more than a second launch (~1.9
-    // us) past 4 groups per lane (wide rows, several vectors), or when the workgroups together
-    // repeat it for more than 12K elements per CU while the slice is over a tenth of a
-    // workgroup's share of the weight bytes (many workgroups on a wide row that is not long
-    // enough to hide it): then, if the caller gave places for the codes, the library quantizes
-    // once into them and runs the product from them. Both forms give the same codes and the
-    // same y. Measured on MI355X, one launch against two: 1536 x 6144 (3 groups per lane, 4.6K
-    // elements per CU) 3.9 / 5.4 us; 8192 x 2048 x 4 vectors (4, 8.2K) 6.6 / 7.1 us;
-    // 2048 x 8192 Q6_K x 2 vectors (8) 8.1 / 7.2 us; 4096 x 16384 (4, 33K, slice 0.22 of the
-    // share) 13.9 / 13.0 us; 262144 x 1536 (1.5, 25K, slice 0.03 of the share) 34.7 / 36.7 us.
+    // Every workgroup of the fused kernel quantizes the whole activation slice its lanes read
+    // (with the column split inside the workgroup: the whole row), blocks of 32 elements over
+    // 4 lanes each. That costs more than a second launch (~1.9 us) past 32 elements per lane
+    // (wide rows, several vectors), or when the workgroups together repeat it for more than 16K
+    // elements per CU while the slice is over a tenth of a workgroup's share of the weight
+    // bytes (many workgroups on a wide row that is not long enough to hide it): then, if the
+    // caller gave places for the codes, the library quantizes once into them and runs the
+    // product from them. Both forms give the same codes and the same y. Measured on MI355X, one
+    // launch against two (elements per lane, per CU, slice over the share): 1536 x 6144 (12,
+    // 4.6K, 0.22) 3.4 / 5.3 us; 8192 x 2048 x 8 vectors (32, 16K, 0.44) 7.6 / 8.2 us; 2048 x
+    // 8192 x 2 vectors (32, 16K, 0.44) 6.0 / 6.5 us, Q6_K 7.2 / 7.1 us; 4096 x 8192 x 3 vectors,
+    // split in two (48, 49K, 0.67) 11.7 / 9.2 us; 1536 x 6144 x 4 vectors, split in three (64)
+    // 8.7 / 7.2 us; 16384 x 4096 x 2 vectors (16, 33K, 0.22) 14.7 / 14.2 us; 4096 x 16384, split
+    // in two (32, 33K, 0.22) 10.6 / 10.6 us; 262144 x 1536 (6, 25K, 0.03) 34.7 / 36.3 us.
     const qgemv_plan plan = make_plan(wtype, rows, cols, nvec);
-    const int64_t slice = static_cast<int64_t>(nvec) * plan.lanes_per_row * plan.chunks_per_lane * 32;
-    const int64_t lanes = 64 * static_cast<int64_t>(plan.waves_per_block);
-    if ((slice / 4 + lanes - 1) / lanes > 4) return 2;
-    const double wgs = static_cast<double>(plan.blocks) * plan.splits;
+    // what each workgroup of the one-launch form quantizes, how many workgroups, how many lanes
+    // (with the column split inside the workgroup, every workgroup quantizes the whole row)
+    int64_t slice = static_cast<int64_t>(nvec) * plan.lanes_per_row * plan.chunks_per_lane * 32;
+    int64_t lanes = 64 * static_cast<int64_t>(plan.waves_per_block);
+    double wgs = static_cast<double>(plan.blocks) * plan.splits;
+    if (plan.splits > 1) {
+        const int maxw = gemv_max_waves(nvec, plan.lanes_per_row, plan.chunks_per_lane);
+        const int wpb = split_waves_per_block(plan, maxw);
+        if (plan.splits <= maxw &&
+            gemv_split_lds_bytes(nvec, plan.lanes_per_row, plan.chunks_per_lane, true, plan.splits,
+                                 wpb) <= kMaxSplitLds) {
+            const int64_t waves = std::min<int64_t>(
+                static_cast<int64_t>(plan.blocks) * plan.splits * plan.waves_per_block, 4096);
+            slice = static_cast<int64_t>(nvec) * cols;
+            lanes = 64 * static_cast<int64_t>(wpb);
+            wgs = static_cast<double>((waves + wpb - 1) / wpb);
+        }
+    }
+    if ((slice + lanes - 1) / lanes > 32) return 2;
     const double share = static_cast<double>(weight_bytes(wtype, rows, cols)) / wgs;
-    return wgs * static_cast<double>(slice) / 256.0 > 12288.0 && slice > 0.1 * share ? 2 : 1;
+    return wgs * static_cast<double>(slice) / 256.0 > 16384.0 && slice > 0.1 * share ? 2 : 1;
 }
 
 int qgemv_fused(int wtype, const void *w, const float *x, int8_t *xq_out, float *xd_out, float *y,

@@ -132,12 +132,33 @@ __device__ __forceinline__ uint32_t group_or(uint32_t v) {
 
 __device__ __forceinline__ uint4 load16(const void *p) { return *reinterpret_cast<const uint4 *>(p); }
 
-// Activation quantization of one block of 32 elements held by 8 consecutive lanes, 4 elements
-// each (oxinfer README, "How it works": per-matmul activation quantization; "Build and run":
-// blocks of 32 with an f32 scale): amax over the block, scale = amax / 127, inverse
-// 127 / amax (0 when amax = 0), code = clamp(rint(x * inverse), -127, 127). Both divisions
-// are IEEE float32 divisions, the product one float32 multiply, rint rounds to nearest even:
-// the codes are the same on every IEEE machine. All 64 lanes of the wave must call it.
+// Activation quantization (oxinfer README, "How it works": per-matmul activation quantization;
+// "Build and run": blocks of 32 with an f32 scale): amax over the block, scale = amax / 127,
+// inverse 127 / amax (0 when amax = 0), code = clamp(rint(x * inverse), -127, 127). Both
+// divisions are IEEE float32 divisions, the product one float32 multiply, rint rounds to nearest
+// even: the codes are the same on every IEEE machine, whichever lanes hold the block.
+//
+// act_code_bits returns a float32 whose low byte is the code: the product is clamped first (the
+// same as clamping after rounding, since +-127 are integers; a NaN product, 0 times an infinite
+// inverse, clamps to -127 either way), then 1.5 * 2^23 is added, which rounds it to the nearest
+// integer, ties to even, into the low mantissa bits (|value| <= 127 < 2^22) in two's complement.
+__device__ __forceinline__ uint32_t act_code_bits(float e, float inv) {
+    const float c = fminf(fmaxf(e * inv, -127.0f), 127.0f);
+    return __builtin_bit_cast(uint32_t, c + 12582912.0f);
+}
+
+// The low bytes of four words, element a in the low byte of the result.
+__device__ __forceinline__ uint32_t pack_low_bytes(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+    // v_perm_b32 picks bytes of {src0 : src1}: selector 0-3 = src1's bytes, 4-7 = src0's, 12 = 0
+    return __builtin_amdgcn_perm(b, a, 0x0C0C0400u) | __builtin_amdgcn_perm(d, c, 0x04000C0Cu);
+}
+
+__device__ __forceinline__ uint32_t act_codes4(const float4 v, float inv) {
+    return pack_low_bytes(act_code_bits(v.x, inv), act_code_bits(v.y, inv),
+                          act_code_bits(v.z, inv), act_code_bits(v.w, inv));
+}
+
+// One block held by 8 consecutive lanes, 4 elements each. All 64 lanes of the wave must call it.
 struct ActQuad {
     uint32_t codes;   // 4 int8 codes, element 0 in the low byte
     float scale;      // the block's scale (the same in all 8 lanes)
@@ -152,14 +173,25 @@ __device__ __forceinline__ ActQuad quantize_act_quad(const float4 v) {
     amax = fmaxf(amax, dpp<kDppHalfMirror>(amax));
     const float scale = amax / 127.0f;
     const float inv = amax > 0.0f ? 127.0f / amax : 0.0f;
-    const float e[4] = {v.x, v.y, v.z, v.w};
-    uint32_t packed = 0;
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-        const float code = fminf(fmaxf(rintf(e[i] * inv), -127.0f), 127.0f);
-        packed |= (static_cast<uint32_t>(static_cast<int>(code)) & 0xFFu) << (8 * i);
-    }
-    return {packed, scale};
+    return {act_codes4(v, inv), scale};
+}
+
+// One block held by the 4 lanes of a DPP quad, 8 consecutive elements each (a then b): the
+// divisions and the cross-lane maximum are shared by twice the elements of the form above.
+// All 64 lanes of the wave must call it.
+struct ActOct {
+    uint32_t lo, hi;  // 8 int8 codes, element 0 in the low byte of lo
+    float scale;      // the block's scale (the same in all 4 lanes)
+};
+
+__device__ __forceinline__ ActOct quantize_act_oct(const float4 a, const float4 b) {
+    float amax = fmaxf(fmaxf(fmaxf(fabsf(a.x), fabsf(a.y)), fmaxf(fabsf(a.z), fabsf(a.w))),
+                       fmaxf(fmaxf(fabsf(b.x), fabsf(b.y)), fmaxf(fabsf(b.z), fabsf(b.w))));
+    amax = fmaxf(amax, dpp<kDppXor1>(amax));
+    amax = fmaxf(amax, dpp<kDppXor2>(amax));
+    const float scale = amax / 127.0f;
+    const float inv = amax > 0.0f ? 127.0f / amax : 0.0f;
+    return {act_codes4(a, inv), act_codes4(b, inv), scale};
 }
 
 // 16-byte load marked nontemporal: the weights are read once per product, so they are

@@ -170,19 +170,23 @@ def test_other_entry_points_reject_bad_arguments():
 
 
 def test_fused_launch_count():
-    """The one-launch kernel unless code outputs are wanted and the activation slice is more
-    than 4 groups of 4 elements per lane of a workgroup, or the workgroups together repeat
-    its quantization for over 12K elements per CU with the slice over a tenth of a
-    workgroup's weight bytes (then quantize once, then the product), and always on the
-    integer matrix-core path (Q4_K, several vectors, a large tensor)."""
-    assert qg.qgemv_fused_launches("q4k", 262144, 1536, 1) == 1
+    """The one-launch kernel unless code outputs are wanted and the slice each workgroup
+    quantizes (the whole row where the column split runs inside the workgroup) is more than
+    32 elements per lane, or the workgroups together repeat its quantization for over 16K
+    elements per CU with the slice over a tenth of a workgroup's weight bytes (then quantize
+    once, then the product), and always on the integer matrix-core path (Q4_K, several
+    vectors, a large tensor)."""
+    assert qg.qgemv_fused_launches("q4k", 262144, 1536, 1) == 1      # 25K per CU, slice 0.03
     assert qg.qgemv_fused_launches("q4k", 8192, 2048, 1) == 1
-    assert qg.qgemv_fused_launches("q6k", 2048, 8192, 1) == 1       # 8192 columns, 8 waves: 4
-    assert qg.qgemv_fused_launches("q4k", 1536, 6144, 1) == 1       # 6144 columns, 8 waves: 3
-    assert qg.qgemv_fused_launches("q6k", 2048, 8192, 2) == 2       # two vectors: 8
-    assert qg.qgemv_fused_launches("q4k", 8192, 2048, 8) == 2       # 8 vectors, 8 waves: 8
-    assert qg.qgemv_fused_launches("q4k", 8192, 2048, 4) == 1       # 4 vectors, 8 waves: 4
-    assert qg.qgemv_fused_launches("q4k", 4096, 16384, 1) == 2      # 1024 workgroups x 8192
+    assert qg.qgemv_fused_launches("q6k", 2048, 8192, 1) == 1       # 8192 columns, 8 waves: 16
+    assert qg.qgemv_fused_launches("q4k", 1536, 6144, 1) == 1       # 6144 columns, 8 waves: 12
+    assert qg.qgemv_fused_launches("q6k", 2048, 8192, 2) == 1       # two vectors: 32, 16K
+    assert qg.qgemv_fused_launches("q4k", 8192, 2048, 8) == 1       # 8 vectors, 8 waves: 32, 16K
+    assert qg.qgemv_fused_launches("q4k", 8192, 2048, 4) == 1       # 4 vectors, 8 waves: 16
+    assert qg.qgemv_fused_launches("q4k", 2048, 8192, 3) == 2       # split in two: the row, 48
+    assert qg.qgemv_fused_launches("q4k", 1536, 6144, 4) == 2       # split in three: the row, 64
+    assert qg.qgemv_fused_launches("q4k", 16384, 4096, 2) == 2      # 16 per lane, 33K per CU
+    assert qg.qgemv_fused_launches("q4k", 4096, 16384, 1) == 2      # 512 workgroups x 16384
     assert qg.qgemv_fused_launches("q4k", 16384, 2048, 8) == 2
     assert qg.qgemv_fused_launches("q4k", 262144, 1536, 8) == 2      # integer matrix cores
     assert qg.qgemv_fused_launches("q4k", 262144, 1536, 8, with_outputs=False) == 1
