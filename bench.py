@@ -919,7 +919,8 @@ def bench_many(args, wl) -> dict:
             kernel = "gemm_q32_mc_kernel<%d, %d, %d, %d, %d, false>" % (
                 (4 if wl.wtype == "q80" else 3,) + {1: (4, 1, 1), 2: (4, 1, 2), 4: (2, 2, 2)}[vt] + (ks,))
     else:
-        kernel = "gemm_q4k_mfma_kernel<%d, false>" % min(4, (nvec + 31) // 32)
+        # the library's tile rule: one group of ceil(nvec / 32) tiles up to 96 vectors, else 2
+        kernel = "gemm_q4k_mfma_kernel<%d, false>" % ((nvec + 31) // 32 if nvec <= 96 else 2)
     t_mfma = flops / (mfma_peak * 1e12)
     if t_hbm >= t_mfma:
         roof = {"bound": "hbm", "achieved": round(gemm_gbs, 1), "peak": HBM_PEAK_GBS,

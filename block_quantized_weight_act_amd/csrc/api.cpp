@@ -357,7 +357,12 @@ bool mc_shape_ok(int wtype, int64_t rows, int64_t cols, int32_t nvec) {
 McPlan make_mc_plan(int64_t rows, int64_t cols, int32_t nvec) {
     McPlan p{};
     const int64_t nb = cols / kQK;
-    p.nt = std::min(4, (nvec + 31) / 32);
+    // Up to 96 vectors one group of ceil(nvec / 32) tiles; beyond, groups of 2 tiles (64
+    // vectors): the 2-tile kernel keeps two waves per SIMD and pipelines its blocks, where 3 or 4
+    // tiles leave one, and smaller groups pad less (262144 x 1536, graph replay on MI355X,
+    // 2 / 3 / 4 tiles per group: 96 vectors 192 / 169 / 170 us; 128: 213 / 328 / 221; 160:
+    // 287 / 327 / 427; 192: 298 / 327 / 427; 256: 400 / 478 / 430).
+    p.nt = nvec <= 96 ? (nvec + 31) / 32 : 2;
     p.groups = (nvec + 32 * p.nt - 1) / (32 * p.nt);
     p.row_tiles = static_cast<int>((rows + kMcRows - 1) / kMcRows);
     const int64_t base = static_cast<int64_t>(p.row_tiles) * p.groups;

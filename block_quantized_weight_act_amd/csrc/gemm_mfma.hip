@@ -480,7 +480,6 @@ hipError_t launch_gemm_q4k_mfma(const GemmArgs &a, int nt, int row_tiles, int gr
         case 1: return launch_nt<1>(a, row_tiles, groups, splits, debug, stream);
         case 2: return launch_nt<2>(a, row_tiles, groups, splits, debug, stream);
         case 3: return launch_nt<3>(a, row_tiles, groups, splits, debug, stream);
-        case 4: return launch_nt<4>(a, row_tiles, groups, splits, debug, stream);
         default: return hipErrorInvalidValue;
     }
 }

@@ -201,7 +201,7 @@ struct GemmArgs {
     int32_t splits;
 };
 // Two launches: the staging pre-pass (grid super-blocks x groups) writes the tiles, then the
-// product (grid row tiles x groups x splits); nt = 1..4 tiles of 32 vectors per group.
+// product (grid row tiles x groups x splits); nt = 1..3 tiles of 32 vectors per group.
 constexpr int64_t mc_tile_bytes(int nt) { return int64_t{nt} * (32 * 512 + 8 * 32 * 8); }
 hipError_t launch_gemm_q4k_mfma(const GemmArgs &a, int nt, int row_tiles, int groups, int splits,
                                 bool debug, hipStream_t stream);

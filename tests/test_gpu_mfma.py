@@ -1,7 +1,7 @@
 """GPU parity of the matrix-core path (Q4_K with 17..256 activation vectors) against the CPU
 oracle, through the C-ABI: integer partials P and activation block sums S bit-exact (debug
 form), every y within 1e-5 of sum_i |w_i| |x_i| of its row and vector. Shapes cover every
-vector-tile count (1..4 tiles of 32, one and several vector groups), ragged row tiles, column
+vector-tile count (1..3 tiles of 32 in one group; groups of 2 tiles beyond 96 vectors), ragged row tiles, column
 splits (few rows) and one pass (many rows)."""
 
 import numpy as np
@@ -45,12 +45,13 @@ SHAPES = [
     (300, 512, 17),       # one tile of 32 vectors, 15 idle; ragged last row tile; split
     (257, 768, 33),       # two tiles
     (128, 2048, 64),      # one row tile, split over 8 super-blocks
-    (1000, 1536, 100),    # four tiles (100 of 128)
-    (131, 256, 128),      # one super-block: no split possible
-    (64, 4096, 129),      # two vector groups (128 + 1)
-    (513, 1024, 256),     # two full groups of 128
+    (1000, 1536, 100),    # two groups of two tiles (100 of 128)
+    (131, 256, 128),      # one super-block: no split possible; two groups
+    (64, 4096, 129),      # three vector groups (64 + 64 + 1)
+    (513, 1024, 256),     # four full groups of 64
     (4100, 1536, 40),     # enough rows for one pass (no split)
-    (37, 2560, 77),       # three tiles, ragged everything
+    (37, 2560, 77),       # three tiles in one group, ragged everything
+    (200, 1024, 96),      # three full tiles in one group
 ]
 
 
