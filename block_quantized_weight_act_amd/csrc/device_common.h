@@ -134,14 +134,21 @@ __device__ __forceinline__ uint4 load16(const void *p) { return *reinterpret_cas
 
 // Activation quantization (oxinfer README, "How it works": per-matmul activation quantization;
 // "Build and run": blocks of 32 with an f32 scale): amax over the block, scale = amax / 127,
-// inverse 127 / amax (0 when amax = 0), code = clamp(rint(x * inverse), -127, 127). Both
+// inverse 127 / amax (0 when that is not a finite float32: amax = 0, or amax below 127 / FLT_MAX,
+// whose block's codes are then all 0), code = clamp(rint(x * inverse), -127, 127). Both
 // divisions are IEEE float32 divisions, the product one float32 multiply, rint rounds to nearest
 // even: the codes are the same on every IEEE machine, whichever lanes hold the block.
 //
+// The inverse scale, or 0 where 127 / amax is not finite (amax = 0 included).
+__device__ __forceinline__ float act_inverse(float amax) {
+    const float r = 127.0f / amax;
+    return r <= 3.40282347e38f ? r : 0.0f;
+}
+
 // act_code_bits returns a float32 whose low byte is the code: the product is clamped first (the
-// same as clamping after rounding, since +-127 are integers; a NaN product, 0 times an infinite
-// inverse, clamps to -127 either way), then 1.5 * 2^23 is added, which rounds it to the nearest
-// integer, ties to even, into the low mantissa bits (|value| <= 127 < 2^22) in two's complement.
+// same as clamping after rounding, since +-127 are integers), then 1.5 * 2^23 is added, which
+// rounds it to the nearest integer, ties to even, into the low mantissa bits (|value| <= 127 <
+// 2^22) in two's complement.
 __device__ __forceinline__ uint32_t act_code_bits(float e, float inv) {
     const float c = fminf(fmaxf(e * inv, -127.0f), 127.0f);
     return __builtin_bit_cast(uint32_t, c + 12582912.0f);
@@ -172,7 +179,7 @@ __device__ __forceinline__ ActQuad quantize_act_quad(const float4 v) {
     amax = fmaxf(amax, dpp<kDppXor2>(amax));
     amax = fmaxf(amax, dpp<kDppHalfMirror>(amax));
     const float scale = amax / 127.0f;
-    const float inv = amax > 0.0f ? 127.0f / amax : 0.0f;
+    const float inv = act_inverse(amax);
     return {act_codes4(v, inv), scale};
 }
 
@@ -190,7 +197,7 @@ __device__ __forceinline__ ActOct quantize_act_oct(const float4 a, const float4 
     amax = fmaxf(amax, dpp<kDppXor1>(amax));
     amax = fmaxf(amax, dpp<kDppXor2>(amax));
     const float scale = amax / 127.0f;
-    const float inv = amax > 0.0f ? 127.0f / amax : 0.0f;
+    const float inv = act_inverse(amax);
     return {act_codes4(a, inv), act_codes4(b, inv), scale};
 }
 

@@ -137,7 +137,8 @@ size_t qgemv_weight_bytes(int wtype, int64_t rows, int64_t cols);
  * activation quantization; "Build and run": blocks of 32, f32 scales).
  * x float32 [nvec][cols] -> xq int8 [nvec][cols], xd float32 [nvec][cols/32].
  * Per block of 32: amax = max |x|, xd = amax / 127 (IEEE float32 division),
- * inverse 127 / amax (0 when amax = 0), code = rint(x * inverse) with one
+ * inverse 127 / amax (0 when that is not a finite float32: amax = 0, or amax
+ * below 127 / FLT_MAX, about 3.7e-37), code = rint(x * inverse) with one
  * float32 multiply and round-to-nearest-even, clamped to [-127, 127].
  * Here cols only needs to be a positive multiple of 32. x 16-byte aligned,
  * xq 4-byte aligned, xd 4-byte aligned. Inputs must be finite.
@@ -463,7 +464,7 @@ int qgemv_debug_partials(int wtype, const void *w, const int8_t *xq, const float
  *  Q4_0, per block of 32: m = the first weight of largest |w|; d = fp16(m / -8)
  *    (+0 for an all-zero block); q = clamp(rint(w / d) + 8, 0, 15) (8 when d = 0).
  *  Q8_0, per block of 32: the activation rule, d = amax / 127,
- *    q = clamp(rint(w * (127 / amax)), -127, 127) (0 when amax = 0).
+ *    q = clamp(rint(w * (127 / amax)), -127, 127) (0 when 127 / amax is not finite).
  * w 16-byte aligned, out 16-byte aligned with qgemv_weight_bytes() bytes.
  * Inputs must be finite and small enough for the fp16 super-scales.
  */

@@ -39,6 +39,7 @@
  * float64 brute force over dequantized weights; one-hot / constant / zero
  * inputs; extreme codes at the int32 bounds. Every function below is pinned.
  */
+#include <float.h>
 #include <math.h>
 #include <stdint.h>
 #include <stdio.h>
@@ -117,9 +118,10 @@ static float clampf(float v, float lo, float hi) { return v < lo ? lo : (v > hi 
 
 /* ------------------------------------------------------- activations ---- */
 /* Per block of 32 elements: amax = max |x|; scale xd = amax / 127 (float32
- * division); inverse id = 127 / amax, or 0 when amax = 0; code
- * qx = clamp(rint(x * id), -127, 127) with one float32 multiply and
- * round-to-nearest-even. The codes never take -128. */
+ * division); inverse id = 127 / amax, or 0 when that is not a finite float32
+ * (amax = 0, or amax below 127 / FLT_MAX, about 3.7e-37: such a block's codes
+ * are all 0); code qx = clamp(rint(x * id), -127, 127) with one float32
+ * multiply and round-to-nearest-even. The codes never take -128. */
 void orc_quantize_act(const float *x, int64_t cols, int32_t nvec, int8_t *xq, float *xd) {
     if (cols % ACT_BLOCK) die("cols must be a multiple of 32");
     for (int32_t v = 0; v < nvec; v++) {
@@ -133,6 +135,7 @@ void orc_quantize_act(const float *x, int64_t cols, int32_t nvec, int8_t *xq, fl
             }
             float scale = amax / 127.0f;
             float inv = amax > 0.0f ? 127.0f / amax : 0.0f;
+            if (!(inv <= FLT_MAX)) inv = 0.0f;
             for (int i = 0; i < ACT_BLOCK; i++) {
                 float prod = xb[i] * inv;
                 float code = clampf(rintf(prod), -127.0f, 127.0f);
@@ -511,8 +514,8 @@ void orc_quantize_q40(const float *w, int64_t rows, int64_t cols, uint8_t *out) 
 }
 
 /* Q8_0, per block of 32 weights: the rule of the activation quantizer,
- *   amax = max |w|, d = amax / 127, id = 127 / amax (0 when amax = 0),
- *   q_t = clamp(rint(w_t * id), -127, 127). */
+ *   amax = max |w|, d = amax / 127, id = 127 / amax (0 when that is not a
+ *   finite float32), q_t = clamp(rint(w_t * id), -127, 127). */
 void orc_quantize_q80(const float *w, int64_t rows, int64_t cols, uint8_t *out) {
     if (cols % QB) die("cols must be a multiple of 32");
     int64_t nb = cols / QB;
@@ -528,6 +531,7 @@ void orc_quantize_q80(const float *w, int64_t rows, int64_t cols, uint8_t *out) 
             }
             float d = amax / 127.0f;
             float id = amax > 0.0f ? 127.0f / amax : 0.0f;
+            if (!(id <= FLT_MAX)) id = 0.0f;
             for (int t = 0; t < QB; t++) q[t] = (int8_t)clampf(rintf(wb[t] * id), -127.0f, 127.0f);
             orc_q80_pack_block(d, q, img);
             q80_put(out, rows * nb, r * nb + b, img);

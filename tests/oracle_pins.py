@@ -307,6 +307,38 @@ def check_act_bounds(lib, seed=11):
     assert np.array_equal(xq2, xq) and np.array_equal(xd2, xd * np.float32(8.0))
 
 
+def check_act_overflowing_inverse(lib):
+    """127 / amax overflows float32 below amax = 127 / FLT_MAX (about 3.73e-37): such a block has
+    no finite inverse, and its codes are all 0 (the amax = 0 rule) with xd = amax / 127. A block
+    just above the threshold has a finite inverse and the usual codes (+-127 at its maximum). A
+    zero element gets the code 0 in every block."""
+    f32max = np.finfo(np.float32).max
+    limit = np.float32(127.0) / np.float32(f32max)
+    rng = np.random.default_rng(5)
+    x = np.zeros((1, 32 * 6), np.float32)
+    for b, amax in enumerate([1e-37, 3.7e-37, 3.8e-37, 1e-30, 1.5e-45, 2e-38]):
+        blk = (rng.uniform(-1.0, 1.0, 32) * amax).astype(np.float32)
+        blk[3] = np.float32(amax)
+        blk[7] = 0.0
+        x[0, 32 * b:32 * b + 32] = blk
+    xq, xd = oracle.quantize_act(x, lib=lib)
+    codes = xq.reshape(-1, 32)
+    am = np.abs(x.reshape(-1, 32)).max(axis=1)
+    assert np.array_equal(xd[0], am / np.float32(127.0))
+    assert np.all(codes[:, 7] == 0)
+    for b in range(6):
+        with np.errstate(over="ignore", divide="ignore"):
+            finite = np.isfinite(np.float32(127.0) / am[b])
+        assert finite == (am[b] >= limit), b
+        if finite:
+            assert abs(int(codes[b, 3])) == 127, b
+        else:
+            assert not codes[b].any(), b
+    # Q8_0 weights follow the same rule, block by block
+    wq = oracle.q80_codes(oracle.quantize_q80(x, lib=lib), 1, x.shape[1]).reshape(-1, 32)
+    assert np.array_equal(wq, codes)
+
+
 # ------------------------------------------------------------- quantizers --
 def _f16(h):
     return np.asarray(h, np.uint16).view(np.float16).astype(np.float64)

@@ -64,6 +64,62 @@ def test_quantize_act_hand_worked_ties():
     assert np.array_equal(gu.host(xd)[0], np.array([c[2] for c in cases], np.float32))
 
 
+def _tiny_blocks(nvec, cols, seed):
+    """Activations with blocks whose maximum lies below, at and above 127 / FLT_MAX (about
+    3.73e-37), where 127 / amax stops being a finite float32, each with a zero element."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((nvec, cols)).astype(np.float32)
+    for b, amax in enumerate([1e-37, 3.7e-37, 3.8e-37, 2e-38, 1.5e-45, 1e-30]):
+        blk = (rng.uniform(-1.0, 1.0, 32) * amax).astype(np.float32)
+        blk[5] = np.float32(-amax)
+        blk[9] = 0.0
+        x[b % nvec, 32 * (2 * b + 1):32 * (2 * b + 2)] = blk
+    return x
+
+
+def test_quantize_act_overflowing_inverse():
+    """Blocks whose 127 / amax overflows float32 get the codes 0 (the amax = 0 rule) on every
+    GPU quantizer: qgemv_quantize_act, the fused one-launch kernels of all four formats, the
+    integer matrix-core kernel's own quantization, and the Q8_0 weight quantizer; codes and
+    scales bit for bit the oracle's, y within its bound."""
+    import torch
+    import block_quantized_weight_act_amd as qg
+    nvec, cols = 2, 2048
+    x = _tiny_blocks(nvec, cols, 3)
+    rq, rd = oracle.quantize_act(x)
+    assert not rq[0, 32:64].any() and not rq[1, 96:128].any()       # 1e-37 and 3.7e-37 blocks
+    xq, xd = gu.quantize_act(x)
+    assert np.array_equal(gu.host(xq), rq)
+    assert np.array_equal(gu.host(xd).view(np.uint32), rd.view(np.uint32))
+    xt = gu.dev(x)
+    rng = np.random.default_rng(4)
+    rows = 300
+    for wtype in ALL:
+        _say("overflowing inverse, fused", wtype)
+        wbuf = _quant(wtype, (rng.standard_normal((rows, cols)) * 0.02).astype(np.float32))
+        ref = oracle.gemv(wtype, wbuf, rows, cols, rq, rd)
+        w = gu.dev(wbuf)
+        assert qg.qgemv_fused_launches(wtype, rows, cols, nvec) == 1
+        y = torch.full((nvec, rows), float("nan"), dtype=torch.float32, device=gu.DEV)
+        xq_out = torch.zeros((nvec, cols), dtype=torch.int8, device=gu.DEV)
+        xd_out = torch.zeros((nvec, cols // 32), dtype=torch.float32, device=gu.DEV)
+        qg.qgemv_fused(wtype, w, xt, y, rows, cols, nvec, xq_out=xq_out, xd_out=xd_out)
+        gu.assert_within_bound(gu.host(y), ref)
+        assert np.array_equal(gu.host(xq_out), rq)
+        assert np.array_equal(gu.host(xd_out).view(np.uint32), rd.view(np.uint32))
+        if wtype == "q4k":
+            y.fill_(float("nan"))
+            xq_out.zero_()
+            xd_out.zero_()
+            qg.qgemv_fused_i8mc(w, xt, y, rows, cols, nvec, xq_out=xq_out, xd_out=xd_out)
+            gu.assert_within_bound(gu.host(y), ref)
+            assert np.array_equal(gu.host(xq_out), rq)
+            assert np.array_equal(gu.host(xd_out).view(np.uint32), rd.view(np.uint32))
+    # the Q8_0 weight quantizer applies the same rule to each block of 32 weights
+    wq = gu.host(gu.quantize_weights("q80", x))
+    assert np.array_equal(wq, oracle.quantize_q80(x))
+
+
 # ---------------------------------------------------------------- weights --
 @pytest.mark.parametrize("wtype", ALL)
 @pytest.mark.parametrize("sigma", [0.02, 0.002, 1.0, 40.0])

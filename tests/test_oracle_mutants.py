@@ -52,6 +52,12 @@ MUTANTS = {
     "act_divide_instead": (
         "float prod = xb[i] * inv;",
         "float prod = amax > 0.0f ? xb[i] / scale : 0.0f;"),
+    "act_inverse_unguarded": (
+        "            if (!(inv <= FLT_MAX)) inv = 0.0f;\n",
+        ""),
+    "q80_inverse_unguarded": (
+        "            if (!(id <= FLT_MAX)) id = 0.0f;\n",
+        ""),
     "act_allow_minus_128": (
         "float code = clampf(rintf(prod), -127.0f, 127.0f);",
         "float code = clampf(rintf(prod * 1.004f), -128.0f, 127.0f);"),
@@ -139,6 +145,7 @@ checks = {{
     "layout_probes": lambda: pins.check_layout_probes(lib),
     "act_cases": lambda: pins.check_act_cases(lib),
     "act_bounds": lambda: pins.check_act_bounds(lib),
+    "act_overflow": lambda: pins.check_act_overflowing_inverse(lib),
     "q4k_quantizer": lambda: (pins.check_q4k_quantizer(lib, w), pins.check_q4k_quantizer(lib, w3),
                               pins.check_q4k_quantizer(lib, w2)),
     "q6k_quantizer": lambda: (pins.check_q6k_quantizer(lib, w), pins.check_q6k_quantizer(lib, w3),

@@ -37,6 +37,10 @@ def test_activation_rounding_bound_and_invariants(orc):
     pins.check_act_bounds(orc)
 
 
+def test_activation_overflowing_inverse(orc):
+    pins.check_act_overflowing_inverse(orc)
+
+
 @pytest.mark.parametrize("sigma", [0.02, 0.002, 1.0])
 def test_q4k_quantizer_roundtrip(orc, sigma):
     rng = np.random.default_rng(int(sigma * 1000) + 1)
