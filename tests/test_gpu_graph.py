@@ -191,6 +191,88 @@ def test_graph_replays_match_direct_calls_and_oracle():
     graph.close()
 
 
+MC_CASES = [("q4k", 16384, 2048, 8, "i8mc"), ("q4k", 16384, 2048, 12, "i8mc"),
+            ("q4k", 4096, 1536, 40, "mc"), ("q80", 16384, 2048, 16, "mc32"),
+            ("q6k", 16384, 2048, 32, "mc32")]
+
+
+def test_graph_replays_the_matrix_core_routes():
+    """The routes qgemv_batch takes for several vectors (the integer matrix cores for Q4_K with
+    8 and 12 vectors, the fp16 matrix cores with their staging pre-pass for 40, the 32-weight and
+    Q6_K integer kernels with their splits and ordered reduce) recorded with the activation
+    quantization into one graph: every replay, with new inputs and direct work between, gives
+    the direct calls' outputs bit for bit, and those lie within the oracle's bound on sampled
+    rows."""
+    import torch
+    import block_quantized_weight_act_amd as qg
+    rng = np.random.default_rng(77)
+    cases = []
+    for wtype, rows, cols, nvec, route in MC_CASES:
+        assert qg.qgemv_route(wtype, rows, cols, nvec) == route
+        w = gu.quantize_weights(wtype, (rng.standard_normal((rows, cols)) * 0.02).astype(np.float32))
+        x = torch.zeros((nvec, cols), dtype=torch.float32, device=gu.DEV)
+        xq = torch.zeros((nvec, cols), dtype=torch.int8, device=gu.DEV)
+        xd = torch.zeros((nvec, cols // 32), dtype=torch.float32, device=gu.DEV)
+        y = torch.zeros((nvec, rows), dtype=torch.float32, device=gu.DEV)
+        nbytes = qg.qgemv_workspace_bytes(wtype, rows, cols, nvec)
+        ws = torch.zeros(max(nbytes, 16), dtype=torch.uint8, device=gu.DEV) if nbytes else None
+        cases.append((wtype, rows, cols, nvec, w, x, xq, xd, y, ws))
+
+    def run():
+        for wtype, rows, cols, nvec, w, x, xq, xd, y, ws in cases:
+            qg.qgemv_quantize_act(x, xq, xd, cols, nvec)
+            qg.qgemv_batch(wtype, w, xq, xd, y, rows, cols, nvec, workspace=ws)
+
+    def set_inputs(seed):
+        r = np.random.default_rng(seed)
+        xs = []
+        for c in cases:
+            xv = (r.standard_normal(tuple(c[5].shape)) * 2.0).astype(np.float32)
+            c[5].copy_(torch.from_numpy(xv).to(gu.DEV))
+            xs.append(xv)
+        return xs
+
+    def outputs():
+        return [gu.host(c[8]).copy() for c in cases]
+
+    def clear():
+        for c in cases:
+            c[8].fill_(float("nan"))
+
+    set_inputs(0)
+    run()
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        qg.qgemv_graph_begin()
+        run()
+        graph = qg.qgemv_graph_end()
+    torch.cuda.synchronize()
+    kernels, others = graph.nodes()
+    assert others == 0 and kernels >= 2 * len(cases)
+    for rep in range(1, 4):
+        _say("matrix-core routes, replay", rep)
+        xs = set_inputs(rep)
+        clear()
+        graph.launch()
+        torch.cuda.synchronize()
+        replayed = outputs()
+        clear()
+        run()
+        torch.cuda.synchronize()
+        _same_bits(replayed, outputs())
+    # the last replay's outputs against the oracle, on the first and last 128 rows
+    for (wtype, rows, cols, nvec, w, *_), xv, yv in zip(cases, xs, replayed):
+        wbuf = gu.host(w)
+        rq, rd = oracle.quantize_act(xv)
+        for lo, hi in ((0, 128), (rows - 128, rows)):
+            ref = oracle.gemv(wtype, oracle.row_slice(wtype, wbuf, rows, cols, lo, hi), hi - lo,
+                              cols, rq, rd)
+            gu.assert_within_bound(yv[:, lo:hi], ref)
+    graph.close()
+
+
 def test_graph_capture_errors():
     import torch
     import block_quantized_weight_act_amd as qg
