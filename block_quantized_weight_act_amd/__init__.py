@@ -26,7 +26,7 @@ __all__ = [
     "qgemv_multi", "qgemv_multi_fused", "qgemv_multi_geometry", "QGEMV_Q4_0", "QGEMV_Q8_0",
     "Graph", "qgemv_graph_begin", "qgemv_graph_end", "qgemv_graph_launch", "qgemv_graph_nodes",
     "qgemv_graph_destroy", "qgemv_graph_classify", "qgemv_i8mc_workspace_bytes", "qgemv_batch_i8mc",
-    "qgemv_mc32_workspace_bytes", "qgemv_batch_mc32",
+    "qgemv_mc32_workspace_bytes", "qgemv_batch_mc32", "qgemv_debug_partials_mc32",
     "qgemv_debug_partials_i8mc", "qgemv_fused_i8mc", "qgemv_route", "ROUTES",
 ]
 
@@ -118,6 +118,7 @@ def _load():
         "qgemv_mc32_workspace_bytes": (sz, [i32, i64, i64, i32]),
         "qgemv_batch_mc32": (ctypes.c_int, [i32, vp, vp, vp, vp, i64, i64, i32, vp, sz, vp]),
         "qgemv_debug_partials_i8mc": (ctypes.c_int, [vp, vp, vp, vp, vp, i64, i64, i32, vp]),
+        "qgemv_debug_partials_mc32": (ctypes.c_int, [i32, vp, vp, vp, vp, vp, i64, i64, i32, vp]),
         "qgemv_fused_i8mc": (ctypes.c_int, [vp, vp, vp, vp, vp, i64, i64, i32, vp, sz, vp]),
     }
     for name, (res, args) in sigs.items():
@@ -364,14 +365,23 @@ def qgemv_mc32_workspace_bytes(wtype, rows: int, cols: int, nvec: int) -> int:
 
 def qgemv_batch_mc32(wtype, w, xq, xd, y, rows: int, cols: int, nvec: int, workspace=None,
                      stream=None) -> None:
-    """Q8_0 / Q4_0 / Q6_K y = W x for 9..256 vectors on the integer matrix cores, whatever the
-    shape."""
+    """Q8_0 / Q4_0 / Q6_K y = W x for 9..256 vectors (Q8_0 / Q4_0 also 1..8) on the integer
+    matrix cores, whatever the shape."""
     lib = _load()
     wsp, wsb = _ws(workspace)
     _check("qgemv_batch_mc32", lib.qgemv_batch_mc32(
         _wtype(wtype), _ptr(w, name="w"), _ptr(xq, torch.int8, "xq"),
         _ptr(xd, torch.float32, "xd"), _ptr(y, torch.float32, "y"), rows, cols, nvec, wsp, wsb,
         _stream(stream, y)))
+
+
+def qgemv_debug_partials_mc32(wtype, w, xq, xd, P, S, rows: int, cols: int, nvec: int,
+                              stream=None) -> None:
+    lib = _load()
+    _check("qgemv_debug_partials_mc32", lib.qgemv_debug_partials_mc32(
+        _wtype(wtype), _ptr(w, name="w"), _ptr(xq, torch.int8, "xq"),
+        _ptr(xd, torch.float32, "xd"), _ptr(P, torch.int32, "P"), _ptr(S, torch.int32, "S"),
+        rows, cols, nvec, _stream(stream, P)))
 
 
 def qgemv_debug_partials_i8mc(w, xq, xd, P, S, rows: int, cols: int, nvec: int,

@@ -25,7 +25,7 @@ LIB = os.path.join(HERE, "_lib", "libqgemv.so")
 
 SOURCES = ["gemv_multi.hip", "gemv_q4k.hip", "gemv_q6k.hip", "gemv_q40.hip", "gemv_q80.hip",
            "api.cpp", "graph.cpp", "gemm_mfma.hip", "gemm_i8.hip", "act_quant.hip", "reduce.hip", "weight_quant.hip", "read_probe.hip",
-           "scratch.hip", "gemm_q32.hip", "gemm_q6k_mc.hip"]
+           "scratch.hip", "gemm_q32.hip", "gemm_q6k_mc.hip", "gemm_q32_i8.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",
@@ -38,7 +38,8 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=o
 FILE_FLAGS = {"gemm_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
               "gemm_i8.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
               "gemm_q32.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
-              "gemm_q6k_mc.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+              "gemm_q6k_mc.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+              "gemm_q32_i8.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src: str) -> str:

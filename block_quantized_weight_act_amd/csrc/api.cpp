@@ -441,9 +441,10 @@ int run_mc(const void *w, const int8_t *xq, const float *xd, float *y, int32_t *
 // columns are split when the row tiles and vector groups alone give fewer than two workgroups
 // per CU (the splits added by the ordered reduce).
 bool mc32_ok(int wtype, int64_t rows, int64_t cols, int32_t nvec) {
-    return (wtype == QGEMV_Q8_0 || wtype == QGEMV_Q4_0 || wtype == QGEMV_Q6K) && nvec > kMaxVec &&
-           nvec <= kMaxBatch &&
-           shape_ok_t(wtype, rows, cols, 1) &&
+    const bool q32 = wtype == QGEMV_Q8_0 || wtype == QGEMV_Q4_0;
+    const bool few = q32 && nvec >= 1 && nvec <= kQ32I8MaxVec;
+    const bool many = (q32 || wtype == QGEMV_Q6K) && nvec > kMaxVec && nvec <= kMaxBatch;
+    return (few || many) && shape_ok_t(wtype, rows, cols, 1) &&
            static_cast<int64_t>(nvec) * cols < (int64_t{1} << 34);
 }
 
@@ -457,17 +458,58 @@ bool mc32_ok(int wtype, int64_t rows, int64_t cols, int32_t nvec) {
 // against 31.5 / 29.7 / 24.9; 65536 x 1536 with 9 vectors 38.4 / 30.7 / 30.2 against 55.4 /
 // 48.4 / 38.5. The weight count (not the bytes) separates the formats: from 32 vectors
 // always, from 16 vectors from 24 Mi weights, from 9 vectors from 48 Mi weights.
+// Where qgemv_batch takes the few-vector kernel for Q8_0 and Q4_0 (gemm_q32_i8.hip) instead of
+// the vector kernel. It moves the same HBM bytes (FETCH_SIZE per dispatch equal) at about 85% of
+// the vector kernel's rate, but its work per weight does not grow with the vector count, so it
+// wins where the vector kernel's dot products bind: Q4_0 from 4 vectors on tensors of at least
+// 32 Mi weights with rows of one split (up to 2048 columns; with a second split and its reduce
+// from 8 vectors), Q8_0 (twice the bytes per weight) with 8 vectors from 256 Mi weights.
+// Measured on MI355X (graph replay, cold; this kernel against the vector kernel, us): Q4_0
+// 262144 x 1536 x 1 / 4 / 8: 40.5 / 35.2, 42.8 / 47.9, 54.0 / 97.2; 65536 x 2048 x 2 / 4 / 8:
+// 17.0 / 18.1, 17.6 / 17.5, 18.5 / 23.8; 16384 x 2048 x 2 / 4 / 8: 6.63 / 6.37, 6.64 / 7.29,
+// 7.25 / 8.34; 16384 x 4096 x 6 / 8: 13.2 / 12.5, 13.4 / 14.1; 4096 x 4096 x 8: 7.69 / 6.32;
+// Q8_0 262144 x 1536 x 6 / 8: 86.0 / 84.2, 86.4 / 103.6; 65536 x 2048 x 8: 29.8 / 29.1.
+bool q32i8_auto(int wtype, int64_t rows, int64_t cols, int32_t nvec) {
+    constexpr int64_t Mi = int64_t{1} << 20;
+    const int64_t weights = rows * cols;
+    const bool one_split = cols <= int64_t{kQ32I8MaxWaves} * kQ32I8BlocksPerWave * 32;
+    if (wtype == QGEMV_Q4_0) return weights >= 32 * Mi && nvec >= (one_split ? 4 : 8);
+    return wtype == QGEMV_Q8_0 && nvec >= 8 && weights >= 256 * Mi && one_split;
+}
+
 bool mc32_auto(int wtype, int64_t rows, int64_t cols, int32_t nvec) {
     if (!mc32_ok(wtype, rows, cols, nvec)) return false;
     const int64_t weights = rows * cols;
     constexpr int64_t Mi = int64_t{1} << 20;
+    if (nvec <= kQ32I8MaxVec) return q32i8_auto(wtype, rows, cols, nvec);
     return nvec >= 32 || (nvec >= 16 && weights >= 24 * Mi) || weights >= 48 * Mi;
 }
 
 // More than kMaxVec vectors where the matrix-core path is not taken: the vector kernel on
 // groups of up to kMaxVec vectors, one after another on the stream.
 bool grouped_shape_ok(int wtype, int64_t rows, int64_t cols, int32_t nvec) {
-    return mc32_ok(wtype, rows, cols, nvec) && !mc32_auto(wtype, rows, cols, nvec);
+    return nvec > kMaxVec && mc32_ok(wtype, rows, cols, nvec) &&
+           !mc32_auto(wtype, rows, cols, nvec);
+}
+
+// The plan of the few-vector kernel (gemm_q32_i8.hip): a split holds at most kQ32I8MaxWaves *
+// kQ32I8BlocksPerWave blocks of 32 columns (the activation a workgroup stages in LDS); wider
+// rows are split into equal parts of whole waves, added by the ordered reduce.
+struct Q32I8Plan {
+    int waves, splits, bps, row_tiles;
+};
+
+Q32I8Plan make_q32i8_plan(int64_t rows, int64_t cols) {
+    Q32I8Plan p{};
+    const int64_t nb = cols / 32;
+    const int64_t most = int64_t{kQ32I8MaxWaves} * kQ32I8BlocksPerWave;
+    const int64_t parts = (nb + most - 1) / most;
+    const int64_t per = (nb + parts - 1) / parts;
+    p.waves = static_cast<int>((per + kQ32I8BlocksPerWave - 1) / kQ32I8BlocksPerWave);
+    p.bps = p.waves * kQ32I8BlocksPerWave;
+    p.splits = static_cast<int>((nb + p.bps - 1) / p.bps);
+    p.row_tiles = static_cast<int>((rows + 15) / 16);
+    return p;
 }
 
 struct Mc32Plan {
@@ -491,8 +533,11 @@ Mc32Plan make_mc32_plan(int64_t rows, int64_t cols, int32_t nvec) {
     return p;
 }
 
-size_t mc32_ws_bytes(const Mc32Plan &p, int64_t rows, int32_t nvec) {
-    return p.splits > 1 ? static_cast<size_t>(p.splits) * nvec * rows * sizeof(float) : 0;
+// The workspace of run_mc32 for a shape mc32_ok accepts: partial sums of column splits.
+size_t mc32_route_ws_bytes(int64_t rows, int64_t cols, int32_t nvec) {
+    const int splits = nvec <= kQ32I8MaxVec ? make_q32i8_plan(rows, cols).splits
+                                            : make_mc32_plan(rows, cols, nvec).splits;
+    return splits > 1 ? static_cast<size_t>(splits) * nvec * rows * sizeof(float) : 0;
 }
 
 // y (or, with P, the debug partials P and S) of a Q8_0, Q4_0 or Q6_K product with many vectors.
@@ -518,8 +563,7 @@ int run_mc32(int wtype, const void *w, const int8_t *xq, const float *xd, float 
             overlaps(S, sbytes, xq, qb) || overlaps(S, sbytes, xd, db))
             return QGEMV_EINVAL;
     }
-    const Mc32Plan p = make_mc32_plan(rows, cols, nvec);
-    const size_t need = debug ? 0 : mc32_ws_bytes(p, rows, nvec);
+    const size_t need = debug ? 0 : mc32_route_ws_bytes(rows, cols, nvec);
     if (need > 0) {
         if (!ws || ws_bytes < need) return QGEMV_EWORKSPACE;
         if (!aligned(ws, 4)) return QGEMV_EALIGN;
@@ -537,16 +581,27 @@ int run_mc32(int wtype, const void *w, const int8_t *xq, const float *xd, float 
     a.rows = static_cast<int32_t>(rows);
     a.nb = static_cast<int32_t>(cols / 32);
     a.nvec = nvec;
-    a.sb_per_split = p.bps;
-    a.row_tiles = p.row_tiles;
-    a.groups = p.groups;
-    a.splits = p.splits;
-    hipError_t e = wtype == QGEMV_Q6K ? launch_gemm_q6k_mc(a, p.vw, debug, stream)
-                                      : launch_gemm_q32_mc(wtype, a, p.vw, debug, stream);
+    hipError_t e;
+    if (nvec <= kQ32I8MaxVec) {
+        const Q32I8Plan p = make_q32i8_plan(rows, cols);
+        a.sb_per_split = p.bps;
+        a.row_tiles = p.row_tiles;
+        a.groups = 1;
+        a.splits = p.splits;
+        e = launch_gemm_q32_i8(wtype, a, p.waves, debug, stream);
+    } else {
+        const Mc32Plan p = make_mc32_plan(rows, cols, nvec);
+        a.sb_per_split = p.bps;
+        a.row_tiles = p.row_tiles;
+        a.groups = p.groups;
+        a.splits = p.splits;
+        e = wtype == QGEMV_Q6K ? launch_gemm_q6k_mc(a, p.vw, debug, stream)
+                               : launch_gemm_q32_mc(wtype, a, p.vw, debug, stream);
+    }
     if (e != hipSuccess) return hip_fail(e);
     if (need > 0) {
         e = launch_splitk_reduce(static_cast<const float *>(ws), y,
-                                 static_cast<int64_t>(nvec) * rows, p.splits, stream);
+                                 static_cast<int64_t>(nvec) * rows, a.splits, stream);
         if (e != hipSuccess) return hip_fail(e);
     }
     return QGEMV_OK;
@@ -873,8 +928,7 @@ int qgemv_quantize_act(const float *x, int8_t *xq, float *xd, int64_t cols, int3
 
 size_t qgemv_workspace_bytes(int wtype, int64_t rows, int64_t cols, int32_t nvec) {
     if (i8_auto(wtype, rows, cols, nvec)) return i8_ws_bytes(make_i8_plan(rows, cols), rows, nvec);
-    if (mc32_auto(wtype, rows, cols, nvec))
-        return mc32_ws_bytes(make_mc32_plan(rows, cols, nvec), rows, nvec);
+    if (mc32_auto(wtype, rows, cols, nvec)) return mc32_route_ws_bytes(rows, cols, nvec);
     if (mc_shape_ok(wtype, rows, cols, nvec))
         return mc_ws_bytes(make_mc_plan(rows, cols, nvec), rows, cols, nvec);
     if (grouped_shape_ok(wtype, rows, cols, nvec)) {
@@ -987,10 +1041,10 @@ int qgemv_batch_scratch(int wtype, const void *w, const int8_t *xq, const float 
 int qgemv_fused_launches(int wtype, int64_t rows, int64_t cols, int32_t nvec, int with_outputs) {
     if (!shape_ok_t(wtype, rows, cols, nvec)) return 0;
     if (!with_outputs) return 1;
-    // The integer matrix-core kernel: quantizing once (into the caller's code outputs) and
-    // running the product from the codes was measured faster than every workgroup quantizing
-    // the split's activation itself.
-    if (i8_auto(wtype, rows, cols, nvec)) return 2;
+    // The integer matrix-core kernels: for Q4_K quantizing once (into the caller's code outputs)
+    // and running the product from the codes was measured faster than every workgroup quantizing
+    // the split's activation itself; the Q8_0 / Q4_0 few-vector kernel runs from codes only.
+    if (i8_auto(wtype, rows, cols, nvec) || mc32_auto(wtype, rows, cols, nvec)) return 2;
     // Every workgroup of the fused kernel quantizes the whole activation slice its lanes read
     // (with the column split inside the workgroup: the whole row), blocks of 32 elements over
     // 4 lanes each. That costs more than a second launch (~1.9 us) past 32 elements per lane
@@ -1055,6 +1109,9 @@ int qgemv_fused(int wtype, const void *w, const float *x, int8_t *xq_out, float 
         if (i8_auto(wtype, rows, cols, nvec))
             return run_i8(w, q, y, nullptr, nullptr, rows, cols, nvec, workspace, workspace_bytes,
                           stream);
+        if (mc32_auto(wtype, rows, cols, nvec))
+            return run_mc32(wtype, w, xq_out, xd_out, y, nullptr, nullptr, rows, cols, nvec,
+                            workspace, workspace_bytes, stream);
         return run_gemv(wtype, w, q, y, rows, cols, nvec, plan, workspace, workspace_bytes, stream);
     }
     if (i8_auto(wtype, rows, cols, nvec))
@@ -1146,7 +1203,7 @@ int qgemv_batch_i8mc(const void *w, const int8_t *xq, const float *xd, float *y,
 
 size_t qgemv_mc32_workspace_bytes(int wtype, int64_t rows, int64_t cols, int32_t nvec) {
     if (!mc32_ok(wtype, rows, cols, nvec)) return 0;
-    return mc32_ws_bytes(make_mc32_plan(rows, cols, nvec), rows, nvec);
+    return mc32_route_ws_bytes(rows, cols, nvec);
 }
 
 int qgemv_batch_mc32(int wtype, const void *w, const int8_t *xq, const float *xd, float *y,
@@ -1164,6 +1221,13 @@ int qgemv_debug_partials_i8mc(const void *w, const int8_t *xq, const float *xd, 
     act.xq = xq;
     act.xd = xd;
     return run_i8(w, act, nullptr, P, S, rows, cols, nvec, nullptr, 0, stream);
+}
+
+int qgemv_debug_partials_mc32(int wtype, const void *w, const int8_t *xq, const float *xd,
+                              int32_t *P, int32_t *S, int64_t rows, int64_t cols, int32_t nvec,
+                              hipStream_t stream) {
+    if (!P || !S) return QGEMV_EINVAL;
+    return run_mc32(wtype, w, xq, xd, nullptr, P, S, rows, cols, nvec, nullptr, 0, stream);
 }
 
 int qgemv_fused_i8mc(const void *w, const float *x, int8_t *xq_out, float *xd_out, float *y,
@@ -1211,7 +1275,7 @@ int qgemv_debug_partials(int wtype, const void *w, const int8_t *xq, const float
         return run_mc(w, xq, xd, nullptr, P, S, rows, cols, nvec, workspace, workspace_bytes,
                       stream);
     }
-    if (mc32_ok(wtype, rows, cols, nvec))
+    if (nvec > kMaxVec ? mc32_ok(wtype, rows, cols, nvec) : mc32_auto(wtype, rows, cols, nvec))
         return run_mc32(wtype, w, xq, xd, nullptr, P, S, rows, cols, nvec, nullptr, 0, stream);
     const int64_t nsub = wtype == QGEMV_Q6K ? cols / 16 : cols / 32;
     const size_t pbytes = static_cast<size_t>(nvec) * rows * nsub * sizeof(int32_t);

@@ -1,0 +1,447 @@
+// Q8_0 and Q4_0 weights x 1..8 int8 activation vectors on the integer matrix cores
+// (v_mfma_i32_16x16x64_i8).
+//
+// With a few vectors the vector kernel's int8 4-way dot products, eight per 32-weight block and
+// vector, bound it (oxinfer README, "Speculative decoding": the multi-token int8 variants are
+// instruction-bound at Q4). Here the same exact block partials P are formed on the matrix
+// cores:
+//
+//  * One product covers 16 rows x 64 columns x 16 output slots. Its 64 columns are four 16-code
+//    halves, one per lane group g: the halves of blocks 4 i + g (g = 0..3) of the wave's 16
+//    blocks, so a lane's weight operand is exactly the 16 bytes it loaded (Q8_0: one 16-byte
+//    plane chunk; Q4_0: the low or the high nibbles of its block's 16 bytes, which hold weights
+//    0..15 and 16..31). The 16 output slots are 4 blocks x 4 vectors: the activation operand
+//    of slot (block g', vector v) holds the vector's codes at lane group g' and zeros in the
+//    other three, so every output is one (row, vector, block) partial. Two products (the two
+//    halves of the blocks) accumulate into one P; with 5..8 vectors a second pair takes
+//    vectors 4..7 with the same weight operands.
+//  * Q4_0 stores codes 0..15 for weights q - 8: the products' accumulator input is -8 S (S the
+//    activation block's code sum), so P = sum (q - 8) xq comes out exact, as the vector kernel
+//    and the oracle define it.
+//  * Float work per output and block: (d * xd) and one fma with P converted, as in the vector
+//    kernel, so y stays within the same bound.
+//
+// Work split: a workgroup of up to 4 waves stages the activation of one column split (16
+// blocks per wave) in LDS once, then takes row tiles of 16 rows in turn; each wave multiplies
+// its 16 blocks of the tile and the waves' sums are added in LDS in wave order. A lane (row r,
+// lane group g) loads per tile and i = 0..3 the code chunk(s) of block 4 i + g of its row (the
+// four lanes of a row read 64 contiguous bytes per plane) and that block's scale; the lane
+// then holds the outputs of those blocks, so the scale is the one it loaded. Two tiles' loads
+// are in flight from the start and each tile's successor goes out right after its arithmetic.
+//
+// Lane layouts of both 16 x 16 products (checked on gfx950 for the Q4_K kernel): operand lane
+// l holds row (or column) l % 16, slots of lane group l / 16; result element e is row
+// 4 (l / 16) + e, column l % 16. Here the activation is the row operand (slots) and the weights
+// the column operand (rows of the tile).
+#include <algorithm>
+#include <atomic>
+
+#include "device_common.h"
+#include "gemm_mc.h"
+
+namespace qgemv {
+
+namespace {
+
+typedef int v4i_t __attribute__((ext_vector_type(4)));
+typedef float v4f_t __attribute__((ext_vector_type(4)));
+
+constexpr int kBw = kQ32I8BlocksPerWave;
+
+// LDS of a workgroup of `waves` waves and NV vector slots: NV rows of codes (the split's blocks)
+// and a row of zeros, each of pitch bytes (the 16 spread the rows over the banks); the scales
+// and -8 S of the split's blocks [block][NV]; two slots of the waves' sums of a row tile.
+__host__ __device__ constexpr int q32i8_pitch(int waves) { return waves * kBw * 32 + 16; }
+__host__ __device__ constexpr int q32i8_lds_bytes(int waves, int nv) {
+    return (nv + 1) * q32i8_pitch(waves) + 2 * waves * kBw * nv * 4 + 2 * waves * 16 * nv * 4;
+}
+
+// H halves of 4 vectors (nvec <= 4 H). VS: rows of whole groups of 4 blocks (cols a multiple of
+// 128), so a lane's 4 scales are one aligned load (otherwise one load per block).
+template <int FMT, int MODE, int H, bool VS>
+__global__ void __launch_bounds__(256) gemm_q32_i8_kernel(GemmArgs a) {
+    constexpr bool DBG = MODE == kModeDebug;
+    constexpr bool Q40 = FMT == kTypeQ40;
+    constexpr int NV = 4 * H;
+    constexpr int NP = Q40 ? 1 : 2;            // 16-byte code chunks per block and lane
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds_q32i8[];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int threads = static_cast<int>(blockDim.x);
+    const int waves = threads >> 6;
+    const int pitch = q32i8_pitch(waves);
+    const int nblk = waves * kBw;              // staged blocks of the split
+    uint8_t *const xq_s = lds_q32i8;           // [NV + 1][pitch]: codes, then zeros
+    float *const xd_s = reinterpret_cast<float *>(lds_q32i8 + (NV + 1) * pitch);   // [nblk][NV]
+    int *const s8_s = reinterpret_cast<int *>(xd_s + nblk * NV);                   // [nblk][NV]: -8 S
+    float *const red_s = reinterpret_cast<float *>(s8_s + nblk * NV);             // [2][waves][16][NV]
+    const int r = lane & 15;                   // tile row of this lane's weights and outputs
+    const int g = lane >> 4;                   // lane group: block 4 i + g of the wave's 16
+    const int rows = a.rows, nb = a.nb, nvec = a.nvec;
+    const int row_tiles = a.row_tiles;
+    const int b_lo = blockIdx.y * a.sb_per_split;
+    const int nsb = min(nb, b_lo + a.sb_per_split) - b_lo;   // blocks of this split
+    const int wb0 = wave * kBw;                // this wave's first block, relative to b_lo
+    const int64_t nblocks = static_cast<int64_t>(rows) * nb;
+    const uint8_t *const hi_plane = a.w + nblocks * 16;        // Q8_0: codes 16..31
+    const uint8_t *const d_plane = a.w + nblocks * (Q40 ? 16 : 32);
+
+    int rt = blockIdx.x;
+    if (rt >= row_tiles) return;               // the whole workgroup (never taken: grid <= tiles)
+
+    // One row tile's loads: per i the chunk(s) of block wb0 + 4 i + g of row r (the split's last
+    // block where that is past the split: loaded, never used), and the scales: with VS those of
+    // blocks wb0 + 4 g .. + 3 in one load (a group past the split reads the split's last group,
+    // unused; splits hold whole groups), exchanged between the lane groups in `products`, else
+    // that of block wb0 + 4 i + g per i. Rows past the matrix read its last row (not stored).
+    // (One load of a lane's four scales instead of four 2- or 4-byte loads: 262144 x 1536 Q4_0
+    // with one vector took 50 us with the four loads, 36 us without any.)
+    struct WTile {
+        uint4 c[4][NP];
+        uint32_t d[4];
+    };
+    auto issue = [&](int tile, WTile &t) {
+        const int64_t row = std::min<int64_t>(int64_t{tile} * 16 + r, rows - 1);
+        const int64_t rb = row * nb + b_lo;
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const int64_t blk = rb + min(wb0 + 4 * i + g, nsb - 1);
+            t.c[i][0] = load16(a.w + blk * 16);
+            if constexpr (!Q40) t.c[i][1] = load16(hi_plane + blk * 16);
+            if constexpr (!VS) {
+                if constexpr (Q40)
+                    t.d[i] = reinterpret_cast<const uint16_t *>(d_plane)[blk];
+                else
+                    t.d[i] = reinterpret_cast<const uint32_t *>(d_plane)[blk];
+            }
+        }
+        if constexpr (VS) {
+            const int64_t b4 = rb + min(wb0 + 4 * g, nsb - 4);
+            if constexpr (Q40) {
+                const uint2 v = *reinterpret_cast<const uint2 *>(d_plane + b4 * 2);
+                t.d[0] = v.x;
+                t.d[1] = v.y;
+            } else {
+                const uint4 v = load16(d_plane + b4 * 4);
+                t.d[0] = v.x;
+                t.d[1] = v.y;
+                t.d[2] = v.z;
+                t.d[3] = v.w;
+            }
+        }
+    };
+    const int stride = static_cast<int>(gridDim.x);
+    WTile tA, tB;
+
+    // ---- the split's activation into LDS: codes as stored (one (vector, block) item of 32
+    //      bytes per thread and pass), scales and -8 S; zeros for vectors past nvec and blocks
+    //      past the split. The staging's loads go out first, then both tiles' weights, then the
+    //      staging's stores ----
+    for (int i = tid; i < pitch / 16; i += threads)
+        *reinterpret_cast<uint4 *>(xq_s + NV * pitch + 16 * i) = make_uint4(0u, 0u, 0u, 0u);
+    {
+        uint4 cv[H][2];
+        float sv[H];
+#pragma unroll
+        for (int p = 0; p < H; p++) {
+            const int it = p * threads + tid;  // < NV * nblk = H * threads
+            const int v = it / nblk, b = it - v * nblk;
+            const bool live = v < nvec && b < nsb;
+            const int64_t gb = static_cast<int64_t>(v) * nb + b_lo + b;
+            cv[p][0] = live ? load16(a.xq + gb * 32) : make_uint4(0u, 0u, 0u, 0u);
+            cv[p][1] = live ? load16(a.xq + gb * 32 + 16) : make_uint4(0u, 0u, 0u, 0u);
+            sv[p] = live ? a.xd[gb] : 0.0f;
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        issue(rt, tA);
+        issue(min(rt + stride, row_tiles - 1), tB);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int p = 0; p < H; p++) {
+            const int it = p * threads + tid;
+            const int v = it / nblk, b = it - v * nblk;
+            const uint4 c0 = cv[p][0], c1 = cv[p][1];
+            const int s = byte_sum(c0.x, byte_sum(c0.y, byte_sum(c0.z, byte_sum(c0.w,
+                          byte_sum(c1.x, byte_sum(c1.y, byte_sum(c1.z, byte_sum(c1.w, 0))))))));
+            *reinterpret_cast<uint4 *>(xq_s + v * pitch + 32 * b) = c0;
+            *reinterpret_cast<uint4 *>(xq_s + v * pitch + 32 * b + 16) = c1;
+            xd_s[b * NV + v] = sv[p];
+            s8_s[b * NV + v] = -8 * s;
+            if (DBG && blockIdx.x == 0 && v < nvec && b < nsb)
+                a.S[static_cast<int64_t>(v) * nb + b_lo + b] = s;
+        }
+    }
+    __syncthreads();
+
+    // ---- this lane's operands from LDS, the same for every row tile: the activation rows it
+    //      reads (slot r: block r / 4 of each group of 4, vector 4 h + r % 4; the zero row
+    //      where r / 4 is not this lane group), and for its outputs (vectors 4 h .. 4 h + 3 of
+    //      block wb0 + 4 i + g) the scales and -8 S ----
+    const bool live = (r >> 2) == g;
+    const uint8_t *abase[H];
+#pragma unroll
+    for (int h = 0; h < H; h++)
+        abase[h] = xq_s + (live ? 4 * h + (r & 3) : NV) * pitch + (wb0 + g) * 32;
+    v4f_t xdk[4][H];
+    v4i_t c8k[4][H];
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+        for (int h = 0; h < H; h++) {
+            const int o = (wb0 + 4 * i + g) * NV + 4 * h;
+            xdk[i][h] = *reinterpret_cast<const v4f_t *>(xd_s + o);
+            c8k[i][h] = Q40 ? *reinterpret_cast<const v4i_t *>(s8_s + o) : v4i_t{0, 0, 0, 0};
+        }
+
+    float *out = DBG ? nullptr : a.out + static_cast<int64_t>(blockIdx.y) * nvec * rows;
+    int slot = 0;
+    // Row tile `tile` from the loaded registers: its products, then the sums over the four
+    // lane groups, leaving vectors 4 n + j0 (n < H) of row r in this lane, j0 = 2 (g % 2) + g / 2.
+    auto products = [&](int tile, const WTile &t, float (&z)[H]) {
+        v4f_t acc[H];
+#pragma unroll
+        for (int h = 0; h < H; h++) acc[h] = v4f_t{0.0f, 0.0f, 0.0f, 0.0f};
+        // dl[i]: the scale of block wb0 + 4 i + g
+        float dl[4];
+        if constexpr (VS) {
+            // m[j] (lane group g) = scale of block wb0 + 4 g + j; dl[i] (lane group g) = m[g] of
+            // lane group i: a 4 x 4 transpose over the lane groups of each row r, one swap of
+            // halves (lanes l, l + 32) and one of rows of 16 (0-1, 2-3) per pair of registers
+            float m[4];
+            if constexpr (Q40) {
+                m[0] = half_to_float(t.d[0] & 0xFFFFu);
+                m[1] = half_to_float(t.d[0] >> 16);
+                m[2] = half_to_float(t.d[1] & 0xFFFFu);
+                m[3] = half_to_float(t.d[1] >> 16);
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; j++) m[j] = __builtin_bit_cast(float, t.d[j]);
+            }
+            uint32_t x[4];
+#pragma unroll
+            for (int j = 0; j < 2; j++) {
+                const auto sw = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, m[j]),
+                                                                 __builtin_bit_cast(uint32_t, m[j + 2]),
+                                                                 false, false);
+                x[j] = sw[0];
+                x[j + 2] = sw[1];
+            }
+#pragma unroll
+            for (int j = 0; j < 2; j++) {
+                const auto sw = __builtin_amdgcn_permlane16_swap(x[2 * j], x[2 * j + 1], false, false);
+                const uint32_t lo = sw[0], hi = sw[1];
+                dl[2 * j] = __builtin_bit_cast(float, lo);
+                dl[2 * j + 1] = __builtin_bit_cast(float, hi);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; i++)
+                dl[i] = Q40 ? half_to_float(t.d[i]) : __builtin_bit_cast(float, t.d[i]);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            v4i_t B0, B1;
+            if constexpr (Q40) {
+                const uint4 c = t.c[i][0];
+                B0 = v4i_t{static_cast<int>(c.x & 0x0F0F0F0Fu), static_cast<int>(c.y & 0x0F0F0F0Fu),
+                           static_cast<int>(c.z & 0x0F0F0F0Fu), static_cast<int>(c.w & 0x0F0F0F0Fu)};
+                B1 = v4i_t{static_cast<int>((c.x >> 4) & 0x0F0F0F0Fu),
+                           static_cast<int>((c.y >> 4) & 0x0F0F0F0Fu),
+                           static_cast<int>((c.z >> 4) & 0x0F0F0F0Fu),
+                           static_cast<int>((c.w >> 4) & 0x0F0F0F0Fu)};
+            } else {
+                B0 = __builtin_bit_cast(v4i_t, t.c[i][0]);
+                B1 = __builtin_bit_cast(v4i_t, t.c[i][1]);
+            }
+            v4i_t P[H];
+#pragma unroll
+            for (int h = 0; h < H; h++) {
+                const v4i_t A0 = *reinterpret_cast<const v4i_t *>(abase[h] + 128 * i);
+                const v4i_t A1 = *reinterpret_cast<const v4i_t *>(abase[h] + 128 * i + 16);
+                P[h] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A0, B0, c8k[i][h], 0, 0, 0);
+                P[h] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A1, B1, P[h], 0, 0, 0);
+            }
+            // blocks past the split: P is 0 there, and so is d (whatever the loaded bits)
+            const bool bv = wb0 + 4 * i + g < nsb;
+            const float d = bv ? dl[i] : 0.0f;
+#pragma unroll
+            for (int h = 0; h < H; h++) {
+#pragma unroll
+                for (int e = 0; e < 4; e++)
+                    acc[h][e] = fmaf(xdk[i][h][e] * d, static_cast<float>(P[h][e]), acc[h][e]);
+                if (DBG) {
+                    const int64_t row = int64_t{tile} * 16 + r;
+                    const int blk = b_lo + wb0 + 4 * i + g;
+#pragma unroll
+                    for (int e = 0; e < 4; e++) {
+                        const int v = 4 * h + e;
+                        if (v < nvec && row < rows && bv)
+                            a.P[(int64_t{v} * rows + row) * nb + blk] = P[h][e];
+                    }
+                }
+            }
+        }
+        // ---- sums over the lane groups: the vectors' values u[j] = acc[j / 4][j % 4]. Lanes
+        //      l and l + 32 first: one swap of the upper half of u[2 m] with the lower half of
+        //      u[2 m + 1], one add, leaves u[2 m] in lanes 0-31 and u[2 m + 1] in lanes 32-63;
+        //      then rows of 16 lanes 0-1 and 2-3 the same way ----
+        // (The elements are copied to scalars first: __builtin_bit_cast of a vector element
+        // read the vector's first element with this compiler.)
+        float w1[2 * H];
+#pragma unroll
+        for (int m = 0; m < 2 * H; m++) {
+            const float lo = acc[m >> 1][2 * (m & 1)], hi = acc[m >> 1][2 * (m & 1) + 1];
+            const auto sw = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, lo),
+                                                             __builtin_bit_cast(uint32_t, hi),
+                                                             false, false);
+            const uint32_t s0 = sw[0], s1 = sw[1];
+            w1[m] = __builtin_bit_cast(float, s0) + __builtin_bit_cast(float, s1);
+        }
+#pragma unroll
+        for (int n = 0; n < H; n++) {
+            const auto sw = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, w1[2 * n]),
+                                                             __builtin_bit_cast(uint32_t, w1[2 * n + 1]),
+                                                             false, false);
+            const uint32_t s0 = sw[0], s1 = sw[1];
+            z[n] = __builtin_bit_cast(float, s0) + __builtin_bit_cast(float, s1);
+        }
+    };
+    // The sums over the workgroup's waves (in wave order) and the stores of row tile `tile`.
+    const int j0 = 2 * (g & 1) + (g >> 1);
+    auto finish = [&](int tile, const float (&z)[H]) {
+        if (!DBG) {
+#pragma unroll
+            for (int n = 0; n < H; n++)
+                red_s[((slot * waves + wave) * 16 + r) * NV + 4 * n + j0] = z[n];
+            __syncthreads();
+            // 16 NV outputs, output e by thread e % threads (a fixed number of stores per lane)
+#pragma unroll
+            for (int k = 0; k < (16 * NV + 63) / 64; k++) {
+                const int e = tid + threads * k;
+                const int v = e >> 4, rr = e & 15;
+                const int64_t row = int64_t{tile} * 16 + rr;
+                if (e < 16 * NV && v < nvec && row < rows) {
+                    float y = red_s[((slot * waves) * 16 + rr) * NV + v];
+#pragma unroll
+                    for (int w = 1; w < kQ32I8MaxWaves; w++)
+                        if (w < waves) y += red_s[((slot * waves + w) * 16 + rr) * NV + v];
+                    out[static_cast<int64_t>(v) * rows + row] = y;
+                }
+            }
+            slot ^= 1;
+        }
+    };
+    const int ntiles = (row_tiles - rt + stride - 1) / stride;
+    float z[H];
+    if (ntiles <= 2) {
+        __builtin_amdgcn_sched_barrier(0);
+        products(rt, tA, z);
+        __builtin_amdgcn_sched_barrier(0);
+        finish(rt, z);
+        if (ntiles == 2) {
+            __builtin_amdgcn_sched_barrier(0);
+            products(rt + stride, tB, z);
+            __builtin_amdgcn_sched_barrier(0);
+            finish(rt + stride, z);
+        }
+        return;
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    products(rt, tA, z);
+    __builtin_amdgcn_sched_barrier(0);
+    issue(rt + 2 * stride, tA);
+    __builtin_amdgcn_sched_barrier(0);
+    finish(rt, z);
+    __builtin_amdgcn_sched_barrier(0);
+    products(rt + stride, tB, z);
+    __builtin_amdgcn_sched_barrier(0);
+    finish(rt + stride, z);
+    rt += 2 * stride;
+    while (true) {
+        __builtin_amdgcn_sched_barrier(0);
+        products(rt, tA, z);
+        __builtin_amdgcn_sched_barrier(0);
+        issue(min(rt + stride, row_tiles - 1), tA);
+        __builtin_amdgcn_sched_barrier(0);
+        finish(rt, z);
+        rt += stride;
+        if (rt >= row_tiles) break;
+    }
+}
+
+}  // namespace
+
+namespace {
+
+template <int FMT, int H, bool VS>
+hipError_t launch_fh(const GemmArgs &a, int waves, bool debug, hipStream_t stream) {
+    // Workgroups of this size resident at once (registers and LDS) times the CUs, looked up
+    // once per form and size; each workgroup then takes an equal share of the row tiles, and at
+    // least two (the staging is per workgroup, and the second tile's loads overlap the first
+    // tile's arithmetic). Concurrent first calls store the same values.
+    static std::atomic<int> per_cu[2][kQ32I8MaxWaves] = {};      // per instance (FMT, H, VS)
+    static std::atomic<int> cus{0};
+    if (cus.load(std::memory_order_relaxed) == 0) {
+        int dev = 0, n = 0;
+        const bool ok = hipGetDevice(&dev) == hipSuccess &&
+                        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) ==
+                            hipSuccess &&
+                        n > 0;
+        cus.store(ok ? n : 256, std::memory_order_relaxed);
+    }
+    const int threads = 64 * waves;
+    const size_t lds = static_cast<size_t>(q32i8_lds_bytes(waves, 4 * H));
+    std::atomic<int> &res = per_cu[debug ? 1 : 0][waves - 1];
+    if (res.load(std::memory_order_relaxed) == 0) {
+        int n = 0;
+        const hipError_t e =
+            debug ? hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                        &n, gemm_q32_i8_kernel<FMT, kModeDebug, H, VS>, threads, lds)
+                  : hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                        &n, gemm_q32_i8_kernel<FMT, kModePlain, H, VS>, threads, lds);
+        res.store((e == hipSuccess && n > 0) ? n : 1, std::memory_order_relaxed);
+    }
+    const int64_t cap = std::max<int64_t>(
+        1, int64_t{res.load(std::memory_order_relaxed)} * cus.load(std::memory_order_relaxed) /
+               a.splits);
+    const int64_t per_wg = std::max<int64_t>(2, (a.row_tiles + cap - 1) / cap);
+    const int64_t blocks = (a.row_tiles + per_wg - 1) / per_wg;
+    const dim3 grid(static_cast<unsigned>(blocks), static_cast<unsigned>(a.splits));
+    const dim3 block(static_cast<unsigned>(threads));
+    if (debug)
+        hipLaunchKernelGGL((gemm_q32_i8_kernel<FMT, kModeDebug, H, VS>), grid, block, lds, stream, a);
+    else
+        hipLaunchKernelGGL((gemm_q32_i8_kernel<FMT, kModePlain, H, VS>), grid, block, lds, stream, a);
+    return hipGetLastError();
+}
+
+template <int FMT>
+hipError_t launch_f(const GemmArgs &a, int waves, bool debug, hipStream_t stream) {
+    const bool vs = a.nb % 4 == 0;
+    if (a.nvec <= 4)
+        return vs ? launch_fh<FMT, 1, true>(a, waves, debug, stream)
+                  : launch_fh<FMT, 1, false>(a, waves, debug, stream);
+    return vs ? launch_fh<FMT, 2, true>(a, waves, debug, stream)
+              : launch_fh<FMT, 2, false>(a, waves, debug, stream);
+}
+
+}  // namespace
+
+hipError_t launch_gemm_q32_i8(int wtype, const GemmArgs &a, int waves, bool debug,
+                              hipStream_t stream) {
+    if (waves < 1 || waves > kQ32I8MaxWaves || a.sb_per_split != kBw * waves || a.nvec < 1 ||
+        a.nvec > kQ32I8MaxVec || a.row_tiles < 1 || a.splits < 1 || a.nb < 1 ||
+        static_cast<int64_t>(a.splits - 1) * a.sb_per_split >= a.nb ||
+        static_cast<int64_t>(a.splits) * a.sb_per_split < a.nb ||
+        static_cast<int64_t>(a.row_tiles) * 16 < a.rows ||
+        static_cast<int64_t>(a.row_tiles - 1) * 16 >= a.rows || a.splits > 65535)
+        return hipErrorInvalidValue;
+    switch (wtype) {
+        case kTypeQ80: return launch_f<kTypeQ80>(a, waves, debug, stream);
+        case kTypeQ40: return launch_f<kTypeQ40>(a, waves, debug, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace qgemv

@@ -194,14 +194,15 @@ int qgemv_q6k(const void *w, const int8_t *xq, const float *xd, float *y, int64_
  * products P and sums S, then the same float32 scaling, so y lies within the
  * same bound of the exact product; the float path's workspace
  * (qgemv_workspace_bytes) holds the staged activation and, for matrices with
- * few rows, partial sums. Q8_0 and Q4_0 with 9 <= nvec <= QGEMV_MAX_BATCH run
- * on the integer matrix cores too (v_mfma_i32_32x32x32_i8: one 32-weight block
- * of 32 rows against 32 vectors per product, P exact; Q4_0 subtracts 8 S in
- * integer), one pass over the weights; their workspace holds partial sums of
- * column splits when the matrix has few rows. Q6_K with 9 <= nvec <=
- * QGEMV_MAX_BATCH runs the vector kernels on groups of up to 8 vectors, one
- * after another on the stream (one pass over the weights per group; the
- * workspace is that of 8 vectors, shared by the groups).
+ * few rows, partial sums. Q8_0, Q4_0 and Q6_K with 9 <= nvec <= QGEMV_MAX_BATCH
+ * run on the integer matrix cores too where qgemv_route says QGEMV_ROUTE_MC32
+ * (qgemv_batch_mc32 below), one pass over the weights; their workspace holds
+ * partial sums of column splits when the matrix has few rows. Elsewhere
+ * (QGEMV_ROUTE_GROUPED) they run the vector kernels on groups of up to 8
+ * vectors, one after another on the stream (one pass over the weights per
+ * group; the workspace is that of 8 vectors, shared by the groups). Q4_0 and
+ * Q8_0 with 4..8 vectors on large tensors also take the integer matrix cores
+ * (QGEMV_ROUTE_MC32; qgemv_route gives the sizes).
  */
 int qgemv_batch(int wtype, const void *w, const int8_t *xq, const float *xd, float *y,
                 int64_t rows, int64_t cols, int32_t nvec, void *workspace,
@@ -234,7 +235,12 @@ int qgemv_batch_scratch(int wtype, const void *w, const int8_t *xq, const float 
  * 24 Mi weights and from 9 vectors on at least 48 Mi weights, or else for those
  * formats the vector kernels on groups of 8 vectors (QGEMV_ROUTE_GROUPED: on a
  * small tensor they stay ahead of the matrix-core path's 16-20 us floor until
- * the groups are many); 0 for an invalid type or shape. Host only. */
+ * the groups are many); with 1..8 vectors the integer matrix cores
+ * (QGEMV_ROUTE_MC32) for Q4_0 from 4 vectors on tensors of at least 32 Mi
+ * weights with rows of up to 2048 columns (from 8 vectors on wider rows) and for
+ * Q8_0 with 8 vectors on rows of up to 2048 columns from 256 Mi weights, where
+ * the vector kernel's dot products bind; 0 for an invalid type or shape. Host
+ * only. */
 enum qgemv_route_kind {
     QGEMV_ROUTE_VECTOR = 1,
     QGEMV_ROUTE_I8MC = 2,
@@ -245,24 +251,36 @@ enum qgemv_route_kind {
 int qgemv_route(int wtype, int64_t rows, int64_t cols, int32_t nvec);
 
 /*
- * Q8_0, Q4_0 or Q6_K with 9 <= nvec <= QGEMV_MAX_BATCH on the integer matrix
- * cores, for any shape (qgemv_batch takes it where QGEMV_ROUTE_MC32 says; oxinfer
- * README, "Speculative decoding": the multi-token int8 variants). One product is
- * 32 weight rows x 32 vectors over one 32-weight block (Q8_0: the stored codes;
- * Q4_0: the codes 0..15, then P = sum q * xq - 8 S in integer) or over one
- * 16-weight Q6_K sub-block (the operand q - 32), so its int32 result is the exact
- * integer partial P of qgemv_debug_partials for every (row, vector); then y is
- * sum over blocks of (d * xd) * P (Q6_K: xd * (sc0 * P0 + sc1 * P1) per block,
- * the integer combination exact, times d per half super-block) in float32,
- * within the same bound as the vector kernels' y. Arguments as for qgemv_batch;
- * the workspace (qgemv_mc32_workspace_bytes: partial sums when the columns are
- * split because row tiles and vector groups give fewer than 512 workgroups) may
- * be NULL when that is 0.
+ * Q8_0, Q4_0 or Q6_K with 9 <= nvec <= QGEMV_MAX_BATCH, and Q8_0 or Q4_0 with
+ * 1 <= nvec <= 8, on the integer matrix cores, for any shape (qgemv_batch takes it
+ * where QGEMV_ROUTE_MC32 says; oxinfer README, "Speculative decoding": the
+ * multi-token int8 variants). With 9 or more vectors one product is 32 weight rows
+ * x 32 vectors over one 32-weight block (Q8_0: the stored codes; Q4_0: the codes
+ * 0..15, then P = sum q * xq - 8 S in integer) or over one 16-weight Q6_K
+ * sub-block (the operand q - 32); with 1..8 vectors one product is 16 weight rows
+ * x 4 blocks x 4 vectors over one 16-weight half of each block
+ * (v_mfma_i32_16x16x64_i8; two accumulate into a block's P, Q4_0's starting from
+ * -8 S). Either way the int32 result is the exact integer partial P of
+ * qgemv_debug_partials for every (row, vector); then y is sum over blocks of
+ * (d * xd) * P (Q6_K: xd * (sc0 * P0 + sc1 * P1) per block, the integer
+ * combination exact, times d per half super-block) in float32, within the same
+ * bound as the vector kernels' y. Arguments as for qgemv_batch; the workspace
+ * (qgemv_mc32_workspace_bytes: partial sums when the columns are split, with 9 or
+ * more vectors because row tiles and vector groups give fewer than 512
+ * workgroups, with 1..8 vectors for rows wider than 2048 columns) may be NULL
+ * when that is 0.
  */
 size_t qgemv_mc32_workspace_bytes(int wtype, int64_t rows, int64_t cols, int32_t nvec);
 int qgemv_batch_mc32(int wtype, const void *w, const int8_t *xq, const float *xd, float *y,
                      int64_t rows, int64_t cols, int32_t nvec, void *workspace,
                      size_t workspace_bytes, hipStream_t stream);
+
+/* Tests only: the integer partials P [nvec][rows][cols/32] (Q6_K: [cols/16]) and
+ * block sums S [nvec][cols/32] of qgemv_batch_mc32's kernels for any shape it
+ * takes, as qgemv_debug_partials writes them; no y, no workspace. */
+int qgemv_debug_partials_mc32(int wtype, const void *w, const int8_t *xq, const float *xd,
+                              int32_t *P, int32_t *S, int64_t rows, int64_t cols, int32_t nvec,
+                              hipStream_t stream);
 
 /*
  * Q4_K with 1 <= nvec <= 16 on the integer matrix cores (v_mfma_i32_16x16x64_i8;
@@ -314,7 +332,10 @@ int qgemv_debug_partials_i8mc(const void *w, const int8_t *xq, const float *xd, 
  * is large next to its share of the weights (wide rows, several vectors) and
  * xq_out / xd_out are given (xq_out 16-byte aligned), the library instead
  * quantizes once into them and runs the product from them (two launches,
- * identical results).
+ * identical results). So it does too for the shapes qgemv_batch runs on the
+ * integer matrix cores (QGEMV_ROUTE_I8MC, QGEMV_ROUTE_MC32), whose y is then
+ * qgemv_batch's; without code outputs those shapes run the one-launch vector
+ * kernel (y within the same bound).
  */
 int qgemv_fused(int wtype, const void *w, const float *x, int8_t *xq_out, float *xd_out, float *y,
                 int64_t rows, int64_t cols, int32_t nvec, void *workspace,

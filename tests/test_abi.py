@@ -105,7 +105,15 @@ def test_routes():
     assert qg.qgemv_route("q4k", 512, 512, 17) == "mc"
     assert qg.qgemv_route("q40", 16384, 2048, 64) == "mc32"
     assert qg.qgemv_route("q80", 262144, 1536, 9) == "mc32"
-    assert qg.qgemv_route("q80", 262144, 1536, 8) == "vector"
+    assert qg.qgemv_route("q80", 262144, 1536, 8) == "mc32"         # few vectors: 8 on >= 256 Mi
+    assert qg.qgemv_route("q80", 262144, 1536, 7) == "vector"
+    assert qg.qgemv_route("q80", 65536, 2048, 8) == "vector"
+    assert qg.qgemv_route("q40", 262144, 1536, 3) == "vector"       # Q4_0: from 4 on >= 32 Mi
+    assert qg.qgemv_route("q40", 262144, 1536, 4) == "mc32"
+    assert qg.qgemv_route("q40", 16384, 2048, 4) == "mc32"
+    assert qg.qgemv_route("q40", 16000, 2048, 8) == "vector"
+    assert qg.qgemv_route("q40", 16384, 4096, 7) == "vector"        # two splits: from 8
+    assert qg.qgemv_route("q40", 16384, 4096, 8) == "mc32"
     assert qg.qgemv_route("q6k", 16384, 2048, 64) == "mc32"
     # Q8_0, Q4_0, Q6_K: the matrix cores from 32 vectors, from 16 on >= 24 Mi weights, from 9
     # on >= 48 Mi weights; groups of 8 on the vector kernel below
@@ -332,13 +340,22 @@ def test_mc32_workspace_and_limits():
     lib = qg._load()
     assert lib.qgemv_debug_partials(4, A, A + (1 << 30), A + (2 << 30), A + (3 << 30), None, 64,
                                     1024, 20, None, 0, None) == EINVAL          # no S
-    # the explicit entry point takes any shape of its formats with 9..256 vectors
+    for nvec in (4, 20):
+        assert lib.qgemv_debug_partials_mc32(4, A, A + (1 << 30), A + (2 << 30), A + (3 << 30),
+                                             None, 64, 1024, nvec, None) == EINVAL
+    # the explicit entry point takes any shape of its formats with 9..256 vectors, and of Q8_0
+    # and Q4_0 with 1..8 (splits of up to 64 blocks of 32 columns)
     X, D, Y = A + (1 << 30), A + (2 << 30), A + (3 << 30)
     mc = lib.qgemv_batch_mc32
     assert qg.qgemv_mc32_workspace_bytes("q80", 2048, 8192, 9) == 32 * 9 * 2048 * 4
-    assert qg.qgemv_mc32_workspace_bytes("q80", 2048, 8192, 8) == 0
+    assert qg.qgemv_mc32_workspace_bytes("q80", 2048, 8192, 8) == 4 * 8 * 2048 * 4
+    assert qg.qgemv_mc32_workspace_bytes("q40", 2048, 2048, 8) == 0
+    assert qg.qgemv_mc32_workspace_bytes("q40", 2048, 8224, 3) == 5 * 3 * 2048 * 4
+    assert qg.qgemv_mc32_workspace_bytes("q6k", 2048, 8192, 8) == 0
     assert qg.qgemv_mc32_workspace_bytes("q4k", 2048, 8192, 64) == 0
-    assert mc(4, A, X, D, Y, 2048, 8192, 8, None, 0, None) == EINVAL         # too few vectors
+    assert mc(2, A, X, D, Y, 2048, 8192, 8, None, 0, None) == EINVAL         # Q6_K: 9..256
+    assert mc(4, A, X, D, Y, 2048, 8192, 8, None, 0, None) == EWORKSPACE     # its split
+    assert mc(3, A, X, D, Y, 2048, 8192, 0, None, 0, None) == EINVAL
     assert mc(1, A, X, D, Y, 2048, 8192, 64, None, 0, None) == EINVAL        # Q4_K
     assert mc(2, A, X, D, Y, 2048, 1024 + 32, 64, None, 0, None) == EINVAL   # Q6_K: whole 256s
     assert mc(4, A, X, D, Y, 2048, 8192, 9, None, 0, None) == EWORKSPACE     # its split

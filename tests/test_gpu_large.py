@@ -52,7 +52,7 @@ def _big_tensor(wtype, small):
 
 
 CASES = [("q4k", 1), ("q4k", 8), ("q4k", 16), ("q4k", 64), ("q6k", 1), ("q6k", 16),
-         ("q40", 1), ("q40", 16), ("q80", 1), ("q80", 16)]
+         ("q40", 1), ("q40", 8), ("q40", 16), ("q80", 1), ("q80", 8), ("q80", 16)]
 
 
 @pytest.mark.parametrize("wtype", ["q4k", "q6k", "q40", "q80"])
@@ -81,7 +81,7 @@ def test_beyond_4gib(wtype):
             ws = torch.empty(max(nbytes, 4), dtype=torch.uint8, device=gu.DEV) if nbytes else None
             qg.qgemv_fused(wtype, big, gu.dev(x), y, ROWS, COLS, 1, workspace=ws)
             gu.assert_within_bound(gu.host(y), ref)
-        if nvec in (1, 16):
+        if nvec in (1, 16) or (nvec == 8 and wtype in ("q40", "q80")):
             # integer partials on rows sampled over the whole tensor (the last rows included),
             # gathered on the GPU (the whole array is up to 43 GB)
             nsub = COLS // 16 if wtype == "q6k" else COLS // 32

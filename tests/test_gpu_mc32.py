@@ -1,12 +1,15 @@
 """GPU parity of the integer matrix-core path for 9..256 activation vectors (Q8_0 and Q4_0: one
 32 x 32 x 32 product per 32-weight block; Q6_K: one 32 x 32 x 16 product per 16-weight
-sub-block) against the CPU oracle, through the C ABI: integer partials P (per block, or per
+sub-block) and for 1..8 Q8_0 and Q4_0 vectors (16 x 16 x 64 products over the halves of 4
+blocks) against the CPU oracle, through the C ABI: integer partials P (per block, or per
 Q6_K sub-block) and activation block sums S bit-exact (debug form), every y within 1e-5 of
 sum_i |w_i| |x_i| of its row and vector. Shapes cover 1, 2 and 4 vector tiles of 32 per
 workgroup, one and two vector groups, ragged row tiles, widths that are not a whole number of
 4-block steps, column splits (few rows; for Q6_K splits that start in the middle of a
 super-block) and one pass (many rows), the int32 extremes of every format, and the
-262144 x 1536 vocabulary projection with 64 vectors (sampled rows)."""
+262144 x 1536 vocabulary projection with 64 vectors (sampled rows); with 1..8 vectors, one to
+four waves per workgroup, waves and splits that end inside their 16 blocks, the last split of
+one block, one and two halves of 4 vectors, and workgroups that walk more than two row tiles."""
 
 import numpy as np
 import pytest
@@ -50,20 +53,34 @@ def _check(wtype, wbuf, rows, cols, x, debug=True):
     wt = gu.dev(wbuf)
     y = _mc32(wtype, wt, xq, xd, rows, cols, nvec)
     gu.assert_within_bound(y, ref)
-    # qgemv_batch: the same kernel (bit for bit) where it routes there, else groups of 8 on
-    # the vector kernel, within the same bound
+    # qgemv_batch: the same kernel (bit for bit) where it routes there, else the vector kernel
+    # (on groups of 8 with more than 8 vectors), within the same bound
     route = qg.qgemv_route(wtype, rows, cols, nvec)
-    assert route in ("mc32", "grouped")
+    assert route in (("mc32", "vector") if nvec <= 8 else ("mc32", "grouped"))
     yb = gu.gemv(wtype, wt, xq, xd, rows, cols, nvec)
     if route == "mc32":
         assert np.array_equal(yb.view(np.uint32), y.view(np.uint32))
     else:
         gu.assert_within_bound(yb, ref)
     if debug:
+        # the kernel's own partials, and those of the route qgemv_debug_partials takes
+        P, S = _mc32_partials(wtype, wt, xq, xd, rows, cols, nvec)
+        assert np.array_equal(S, oracle.block_sums(rq))
+        assert np.array_equal(P, ref["P"])
         P, S = gu.partials(wtype, wt, xq, xd, rows, cols, nvec)
         assert np.array_equal(S, oracle.block_sums(rq))
         assert np.array_equal(P, ref["P"])
     return y
+
+
+def _mc32_partials(wtype, wt, xq, xd, rows, cols, nvec):
+    import torch
+    import block_quantized_weight_act_amd as qg
+    nsub = cols // 16 if wtype == "q6k" else cols // 32
+    P = torch.full((nvec, rows, nsub), -(2 ** 31), dtype=torch.int32, device=gu.DEV)
+    S = torch.full((nvec, cols // 32), -(2 ** 31), dtype=torch.int32, device=gu.DEV)
+    qg.qgemv_debug_partials_mc32(wtype, wt, xq, xd, P, S, rows, cols, nvec)
+    return gu.host(P), gu.host(S)
 
 
 SHAPES = [
@@ -94,7 +111,23 @@ SHAPES_Q6K = [
     (2048, 8192, 64),     # the short, wide matrix with 64 vectors
 ]
 
-CASES = [(w, *s) for w in ("q80", "q40") for s in SHAPES] + [("q6k", *s) for s in SHAPES_Q6K]
+SHAPES_FEW = [
+    # (rows, cols, nvec): 1..8 Q8_0 / Q4_0 vectors
+    (300, 1056, 3),       # 33 blocks: three waves, the third with one block; ragged row tiles
+    (257, 768, 8),        # two waves, two halves of 4 vectors
+    (128, 2048, 5),       # four full waves, one row tile pair
+    (1000, 4096, 7),      # two splits of 64 blocks
+    (131, 32, 1),         # one block, one wave
+    (64, 8224, 4),        # 257 blocks: five splits of four waves, the last of one block
+    (4100, 1536, 6),      # three waves, 257 row tiles
+    (37, 2592, 2),        # 81 blocks: two splits of three waves, ragged
+    (20000, 2048, 3),     # 1250 row tiles: workgroups walk more than two
+    (20000, 1600, 8),     # 50 blocks over four waves, more than two tiles per workgroup
+    (16384, 2048, 5),     # where qgemv_batch takes this kernel for Q4_0
+]
+
+CASES = ([(w, *s) for w in ("q80", "q40") for s in SHAPES] + [("q6k", *s) for s in SHAPES_Q6K] +
+         [(w, *s) for w in ("q80", "q40") for s in SHAPES_FEW])
 
 
 @pytest.mark.parametrize("wtype,rows,cols,nvec", CASES)
@@ -127,12 +160,54 @@ def test_integer_extremes():
     _check("q6k", t6, rows, cols, np.full((nvec, cols), -3.0, np.float32))
 
 
+def test_fused_with_code_outputs_takes_the_matrix_cores():
+    """qgemv_fused with code outputs on a shape qgemv_batch runs on the few-vector matrix-core
+    kernel: two launches, the oracle's codes and scales, and qgemv_batch's y bit for bit."""
+    import torch
+    import block_quantized_weight_act_amd as qg
+    rows, cols, nvec = 16384, 2048, 6
+    assert qg.qgemv_route("q40", rows, cols, nvec) == "mc32"
+    assert qg.qgemv_fused_launches("q40", rows, cols, nvec, True) == 2
+    rng = np.random.default_rng(17)
+    w = (rng.standard_normal((rows, cols)) * 0.02).astype(np.float32)
+    x = (rng.standard_normal((nvec, cols)) * 2.0).astype(np.float32)
+    wbuf = oracle.quantize("q40", w)
+    rq, rd = oracle.quantize_act(x)
+    wt = gu.dev(wbuf)
+    xq = torch.empty((nvec, cols), dtype=torch.int8, device=gu.DEV)
+    xd = torch.empty((nvec, cols // 32), dtype=torch.float32, device=gu.DEV)
+    y = torch.full((nvec, rows), float("nan"), dtype=torch.float32, device=gu.DEV)
+    nbytes = qg.qgemv_workspace_bytes("q40", rows, cols, nvec)
+    ws = torch.empty(max(nbytes, 4), dtype=torch.uint8, device=gu.DEV) if nbytes else None
+    qg.qgemv_fused("q40", wt, gu.dev(x), y, rows, cols, nvec, xq_out=xq, xd_out=xd, workspace=ws)
+    assert np.array_equal(gu.host(xq), rq)
+    assert np.array_equal(gu.host(xd).view(np.uint32), rd.view(np.uint32))
+    yb = gu.gemv("q40", wt, xq, xd, rows, cols, nvec)
+    assert np.array_equal(gu.host(y).view(np.uint32), yb.view(np.uint32))
+    gu.assert_within_bound(gu.host(y), oracle.gemv("q40", wbuf, rows, cols, rq, rd))
+
+
+def test_integer_extremes_few_vectors():
+    rows, cols, nvec = 70, 256, 8
+    img = oracle.q80_pack_block(np.float32(1.0), np.full(32, -127, np.int8))
+    t80 = oracle.q32_tensor("q80", [img] * (rows * cols // 32))
+    _check("q80", t80, rows, cols, np.full((nvec, cols), 3.0, np.float32))     # P = -516128
+    img0 = oracle.q40_pack_block(0x3C00, np.zeros(32, np.uint8))
+    img15 = oracle.q40_pack_block(0x3C00, np.full(32, 15, np.uint8))
+    t40 = oracle.q32_tensor("q40", [img15, img0] * (rows * cols // 64))
+    _check("q40", t40, rows, cols, np.full((nvec, cols), -3.0, np.float32))    # P = -28448, 32512
+
+
 def test_zero_weights_give_exact_zero():
     rows, cols, nvec = 96, 512, 20
     x = np.random.default_rng(3).standard_normal((nvec, cols)).astype(np.float32)
     for wtype in ("q80", "q40", "q6k"):
         y = _check(wtype, oracle.quantize(wtype, np.zeros((rows, cols), np.float32)), rows, cols, x,
                    debug=False)
+        assert np.all(y == 0)
+    for wtype in ("q80", "q40"):
+        y = _check(wtype, oracle.quantize(wtype, np.zeros((rows, cols), np.float32)), rows, cols,
+                   x[:6], debug=False)
         assert np.all(y == 0)
 
 
