@@ -441,9 +441,9 @@ int run_mc(const void *w, const int8_t *xq, const float *xd, float *y, int32_t *
 // columns are split when the row tiles and vector groups alone give fewer than two workgroups
 // per CU (the splits added by the ordered reduce).
 bool mc32_ok(int wtype, int64_t rows, int64_t cols, int32_t nvec) {
-    const bool q32 = wtype == QGEMV_Q8_0 || wtype == QGEMV_Q4_0;
-    const bool few = q32 && nvec >= 1 && nvec <= kQ32I8MaxVec;
-    const bool many = (q32 || wtype == QGEMV_Q6K) && nvec > kMaxVec && nvec <= kMaxBatch;
+    const bool fmt = wtype == QGEMV_Q8_0 || wtype == QGEMV_Q4_0 || wtype == QGEMV_Q6K;
+    const bool few = fmt && nvec >= 1 && nvec <= kQ32I8MaxVec;
+    const bool many = fmt && nvec > kMaxVec && nvec <= kMaxBatch;
     return (few || many) && shape_ok_t(wtype, rows, cols, 1) &&
            static_cast<int64_t>(nvec) * cols < (int64_t{1} << 34);
 }
@@ -458,23 +458,37 @@ bool mc32_ok(int wtype, int64_t rows, int64_t cols, int32_t nvec) {
 // against 31.5 / 29.7 / 24.9; 65536 x 1536 with 9 vectors 38.4 / 30.7 / 30.2 against 55.4 /
 // 48.4 / 38.5. The weight count (not the bytes) separates the formats: from 32 vectors
 // always, from 16 vectors from 24 Mi weights, from 9 vectors from 48 Mi weights.
-// Where qgemv_batch takes the few-vector kernel for Q8_0 and Q4_0 (gemm_q32_i8.hip) instead of
-// the vector kernel. It moves the same HBM bytes (FETCH_SIZE per dispatch equal) at about 85% of
-// the vector kernel's rate, but its work per weight does not grow with the vector count, so it
-// wins where the vector kernel's dot products bind: Q4_0 from 4 vectors on tensors of at least
-// 32 Mi weights with rows of one split (up to 2048 columns; with a second split and its reduce
-// from 8 vectors), Q8_0 (twice the bytes per weight) with 8 vectors from 256 Mi weights.
-// Measured on MI355X (graph replay, cold; this kernel against the vector kernel, us): Q4_0
-// 262144 x 1536 x 1 / 4 / 8: 40.5 / 35.2, 42.8 / 47.9, 54.0 / 97.2; 65536 x 2048 x 2 / 4 / 8:
-// 17.0 / 18.1, 17.6 / 17.5, 18.5 / 23.8; 16384 x 2048 x 2 / 4 / 8: 6.63 / 6.37, 6.64 / 7.29,
-// 7.25 / 8.34; 16384 x 4096 x 6 / 8: 13.2 / 12.5, 13.4 / 14.1; 4096 x 4096 x 8: 7.69 / 6.32;
-// Q8_0 262144 x 1536 x 6 / 8: 86.0 / 84.2, 86.4 / 103.6; 65536 x 2048 x 8: 29.8 / 29.1.
+// Where qgemv_batch takes the few-vector kernel for Q8_0, Q4_0 and Q6_K (gemm_q32_i8.hip)
+// instead of the vector kernel. It moves the same HBM bytes (FETCH_SIZE per dispatch equal) at
+// about 85% of the vector kernel's rate, but its work per weight does not grow with the vector
+// count, so it wins where the vector kernel's dot products bind, on rows of one split (up to
+// 2048 columns; a second split and its reduce cost more than they save below 8 vectors):
+// Q4_0 from 4 vectors on tensors of at least 32 Mi weights (3 from 256 Mi; with two splits 8);
+// Q6_K from 4 vectors on 256 Mi weights, with 8 from 64 Mi; Q8_0 (twice the bytes per weight)
+// with 8 vectors from 256 Mi weights. Measured on MI355X (graph replay, cold; this kernel
+// against the vector kernel, us):
+//   Q4_0 262144 x 1536 x 2 / 3 / 4 / 8: 40.9 / 36.5, 40.6 / 44.8, 40.7 / 47.7, 43.8 / 97.8;
+//        65536 x 2048 x 3 / 4 / 5 / 8: 17.1 / 15.2, 17.4 / 17.0, 17.7 / 19.5, 17.8 / 23.5;
+//        16384 x 2048 x 3 / 4 / 8: 6.63 / 6.29, 6.63 / 7.07, 6.90 / 8.32;
+//        16384 x 4096 x 6 / 8: 12.9 / 12.3, 13.1 / 13.8; 4096 x 4096 x 8: 8.0 / 6.4;
+//   Q6_K 262144 x 1536 x 3 / 4 / 8: 66.2 / 64.6, 66.4 / 71.0, 73.4 / 140.8;
+//        65536 x 2048 x 4 / 6 / 8: 26.9 / 25.1, 31.3 / 27.1, 31.2 / 32.1;
+//        16384 x 2048 x 8: 10.6 / 10.7; 16384 x 4096 x 8: 23.3 / 20.1;
+//   Q8_0 262144 x 1536 x 6 / 8: 86.0 / 84.2, 84.2 / 103.6; 65536 x 2048 x 8: 29.7 / 29.1.
 bool q32i8_auto(int wtype, int64_t rows, int64_t cols, int32_t nvec) {
     constexpr int64_t Mi = int64_t{1} << 20;
     const int64_t weights = rows * cols;
     const bool one_split = cols <= int64_t{kQ32I8MaxWaves} * kQ32I8BlocksPerWave * 32;
-    if (wtype == QGEMV_Q4_0) return weights >= 32 * Mi && nvec >= (one_split ? 4 : 8);
-    return wtype == QGEMV_Q8_0 && nvec >= 8 && weights >= 256 * Mi && one_split;
+    switch (wtype) {
+        case QGEMV_Q4_0:
+            if (!one_split) return weights >= 32 * Mi && nvec >= 8;
+            return weights >= 32 * Mi && nvec >= (weights >= 256 * Mi ? 3 : 4);
+        case QGEMV_Q6K:
+            return one_split && ((weights >= 256 * Mi && nvec >= 4) ||
+                                 (weights >= 64 * Mi && nvec >= 8));
+        case QGEMV_Q8_0: return one_split && weights >= 256 * Mi && nvec >= 8;
+        default: return false;
+    }
 }
 
 bool mc32_auto(int wtype, int64_t rows, int64_t cols, int32_t nvec) {

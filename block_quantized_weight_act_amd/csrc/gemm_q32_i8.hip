@@ -50,7 +50,8 @@ constexpr int kBw = kQ32I8BlocksPerWave;
 
 // LDS of a workgroup of `waves` waves and NV vector slots: NV rows of codes (the split's blocks)
 // and a row of zeros, each of pitch bytes (the 16 spread the rows over the banks); the scales
-// and -8 S of the split's blocks [block][NV]; two slots of the waves' sums of a row tile.
+// and Q4_0's -8 S of the split's blocks [block][NV]; two slots of the waves' sums of a row
+// tile.
 __host__ __device__ constexpr int q32i8_pitch(int waves) { return waves * kBw * 32 + 16; }
 __host__ __device__ constexpr int q32i8_lds_bytes(int waves, int nv) {
     return (nv + 1) * q32i8_pitch(waves) + 2 * waves * kBw * nv * 4 + 2 * waves * 16 * nv * 4;
@@ -62,8 +63,15 @@ template <int FMT, int MODE, int H, bool VS>
 __global__ void __launch_bounds__(256) gemm_q32_i8_kernel(GemmArgs a) {
     constexpr bool DBG = MODE == kModeDebug;
     constexpr bool Q40 = FMT == kTypeQ40;
+    constexpr bool Q6 = FMT == kTypeQ6K;
     constexpr int NV = 4 * H;
-    constexpr int NP = Q40 ? 1 : 2;            // 16-byte code chunks per block and lane
+    constexpr int NP = Q40 || Q6 ? 1 : 2;      // 16-byte code chunks per block and lane
+    // One tile in flight per wave from the start (SINGLE), or two (the first two tiles) with the
+    // registers of a second set: with 5..8 Q6_K or Q4_0 vectors the second set costs more
+    // resident waves than it gains (262144 x 1536 x 8: Q6_K 72.4 against 113.1 us, Q4_0 44.1
+    // against 54.5 us); with 1..4 vectors, and for Q8_0, it gains (Q6_K x 4: 66.3 against 74.0,
+    // Q8_0 x 8: 84.2 against 91.3 us).
+    constexpr bool SINGLE = H == 2 && FMT != kTypeQ80;
     extern __shared__ __attribute__((aligned(16))) uint8_t lds_q32i8[];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -74,8 +82,8 @@ __global__ void __launch_bounds__(256) gemm_q32_i8_kernel(GemmArgs a) {
     const int nblk = waves * kBw;              // staged blocks of the split
     uint8_t *const xq_s = lds_q32i8;           // [NV + 1][pitch]: codes, then zeros
     float *const xd_s = reinterpret_cast<float *>(lds_q32i8 + (NV + 1) * pitch);   // [nblk][NV]
-    int *const s8_s = reinterpret_cast<int *>(xd_s + nblk * NV);                   // [nblk][NV]: -8 S
-    float *const red_s = reinterpret_cast<float *>(s8_s + nblk * NV);             // [2][waves][16][NV]
+    int *const s8_s = reinterpret_cast<int *>(xd_s + nblk * NV);     // [nblk][NV]: Q4_0: -8 S
+    float *const red_s = reinterpret_cast<float *>(s8_s + nblk * NV);  // [2][waves][16][NV]
     const int r = lane & 15;                   // tile row of this lane's weights and outputs
     const int g = lane >> 4;                   // lane group: block 4 i + g of the wave's 16
     const int rows = a.rows, nb = a.nb, nvec = a.nvec;
@@ -84,8 +92,9 @@ __global__ void __launch_bounds__(256) gemm_q32_i8_kernel(GemmArgs a) {
     const int nsb = min(nb, b_lo + a.sb_per_split) - b_lo;   // blocks of this split
     const int wb0 = wave * kBw;                // this wave's first block, relative to b_lo
     const int64_t nblocks = static_cast<int64_t>(rows) * nb;
-    const uint8_t *const hi_plane = a.w + nblocks * 16;        // Q8_0: codes 16..31
-    const uint8_t *const d_plane = a.w + nblocks * (Q40 ? 16 : 32);
+    const uint8_t *const hi_plane = a.w + nblocks * 16;        // Q8_0: codes 16..31; Q6_K: high bits
+    const uint8_t *const d_plane = a.w + nblocks * (Q40 ? 16 : (Q6 ? 26 : 32));
+    const uint8_t *const sc_plane = a.w + nblocks * 24;        // Q6_K: sub-scales
 
     int rt = blockIdx.x;
     if (rt >= row_tiles) return;               // the whole workgroup (never taken: grid <= tiles)
@@ -97,9 +106,14 @@ __global__ void __launch_bounds__(256) gemm_q32_i8_kernel(GemmArgs a) {
     // that of block wb0 + 4 i + g per i. Rows past the matrix read its last row (not stored).
     // (One load of a lane's four scales instead of four 2- or 4-byte loads: 262144 x 1536 Q4_0
     // with one vector took 50 us with the four loads, 36 us without any.)
+    // Q6_K: per i also the 8 high-bit bytes of the block, and per tile the 16 sub-scales and
+    // the super-scale of the wave's two super-blocks (a super-block past the split reads the
+    // split's last one, unused).
     struct WTile {
         uint4 c[4][NP];
         uint32_t d[4];
+        uint2 hb[Q6 ? 4 : 1];
+        uint4 sc[Q6 ? 2 : 1];
     };
     auto issue = [&](int tile, WTile &t) {
         const int64_t row = std::min<int64_t>(int64_t{tile} * 16 + r, rows - 1);
@@ -108,15 +122,24 @@ __global__ void __launch_bounds__(256) gemm_q32_i8_kernel(GemmArgs a) {
         for (int i = 0; i < 4; i++) {
             const int64_t blk = rb + min(wb0 + 4 * i + g, nsb - 1);
             t.c[i][0] = load16(a.w + blk * 16);
-            if constexpr (!Q40) t.c[i][1] = load16(hi_plane + blk * 16);
-            if constexpr (!VS) {
+            if constexpr (Q6) t.hb[i] = *reinterpret_cast<const uint2 *>(hi_plane + blk * 8);
+            if constexpr (!Q40 && !Q6) t.c[i][1] = load16(hi_plane + blk * 16);
+            if constexpr (!VS && !Q6) {
                 if constexpr (Q40)
                     t.d[i] = reinterpret_cast<const uint16_t *>(d_plane)[blk];
                 else
                     t.d[i] = reinterpret_cast<const uint32_t *>(d_plane)[blk];
             }
         }
-        if constexpr (VS) {
+        if constexpr (Q6) {
+#pragma unroll
+            for (int q = 0; q < 2; q++) {
+                const int64_t sbk = (rb + min(wb0 + 8 * q, nsb - 8)) >> 3;
+                t.sc[q] = load16(sc_plane + sbk * 16);
+                t.d[q] = reinterpret_cast<const uint16_t *>(d_plane)[sbk];
+            }
+        }
+        if constexpr (VS && !Q6) {
             const int64_t b4 = rb + min(wb0 + 4 * g, nsb - 4);
             if constexpr (Q40) {
                 const uint2 v = *reinterpret_cast<const uint2 *>(d_plane + b4 * 2);
@@ -132,7 +155,7 @@ __global__ void __launch_bounds__(256) gemm_q32_i8_kernel(GemmArgs a) {
         }
     };
     const int stride = static_cast<int>(gridDim.x);
-    WTile tA, tB;
+    WTile tA, tB;     // tB: the second tile of the first two (not with SINGLE)
 
     // ---- the split's activation into LDS: codes as stored (one (vector, block) item of 32
     //      bytes per thread and pass), scales and -8 S; zeros for vectors past nvec and blocks
@@ -155,7 +178,7 @@ __global__ void __launch_bounds__(256) gemm_q32_i8_kernel(GemmArgs a) {
         }
         __builtin_amdgcn_sched_barrier(0);
         issue(rt, tA);
-        issue(min(rt + stride, row_tiles - 1), tB);
+        if constexpr (!SINGLE) issue(min(rt + stride, row_tiles - 1), tB);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int p = 0; p < H; p++) {
@@ -190,8 +213,10 @@ __global__ void __launch_bounds__(256) gemm_q32_i8_kernel(GemmArgs a) {
 #pragma unroll
         for (int h = 0; h < H; h++) {
             const int o = (wb0 + 4 * i + g) * NV + 4 * h;
-            xdk[i][h] = *reinterpret_cast<const v4f_t *>(xd_s + o);
+            xdk[i][h] = Q6 ? v4f_t{0.0f, 0.0f, 0.0f, 0.0f} : *reinterpret_cast<const v4f_t *>(xd_s + o);
             c8k[i][h] = Q40 ? *reinterpret_cast<const v4i_t *>(s8_s + o) : v4i_t{0, 0, 0, 0};
+            // (Q6_K reads its activation scales per product instead: its weight operands take
+            // more registers)
         }
 
     float *out = DBG ? nullptr : a.out + static_cast<int64_t>(blockIdx.y) * nvec * rows;
@@ -202,82 +227,152 @@ __global__ void __launch_bounds__(256) gemm_q32_i8_kernel(GemmArgs a) {
         v4f_t acc[H];
 #pragma unroll
         for (int h = 0; h < H; h++) acc[h] = v4f_t{0.0f, 0.0f, 0.0f, 0.0f};
-        // dl[i]: the scale of block wb0 + 4 i + g
-        float dl[4];
-        if constexpr (VS) {
-            // m[j] (lane group g) = scale of block wb0 + 4 g + j; dl[i] (lane group g) = m[g] of
-            // lane group i: a 4 x 4 transpose over the lane groups of each row r, one swap of
-            // halves (lanes l, l + 32) and one of rows of 16 (0-1, 2-3) per pair of registers
-            float m[4];
-            if constexpr (Q40) {
-                m[0] = half_to_float(t.d[0] & 0xFFFFu);
-                m[1] = half_to_float(t.d[0] >> 16);
-                m[2] = half_to_float(t.d[1] & 0xFFFFu);
-                m[3] = half_to_float(t.d[1] >> 16);
-            } else {
+        if constexpr (Q6) {
 #pragma unroll
-                for (int j = 0; j < 4; j++) m[j] = __builtin_bit_cast(float, t.d[j]);
-            }
-            uint32_t x[4];
-#pragma unroll
-            for (int j = 0; j < 2; j++) {
-                const auto sw = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, m[j]),
-                                                                 __builtin_bit_cast(uint32_t, m[j + 2]),
-                                                                 false, false);
-                x[j] = sw[0];
-                x[j + 2] = sw[1];
-            }
-#pragma unroll
-            for (int j = 0; j < 2; j++) {
-                const auto sw = __builtin_amdgcn_permlane16_swap(x[2 * j], x[2 * j + 1], false, false);
-                const uint32_t lo = sw[0], hi = sw[1];
-                dl[2 * j] = __builtin_bit_cast(float, lo);
-                dl[2 * j + 1] = __builtin_bit_cast(float, hi);
-            }
-        } else {
-#pragma unroll
-            for (int i = 0; i < 4; i++)
-                dl[i] = Q40 ? half_to_float(t.d[i]) : __builtin_bit_cast(float, t.d[i]);
-        }
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-            v4i_t B0, B1;
-            if constexpr (Q40) {
+            for (int i = 0; i < 4; i++) {
+                // (one block at a time: hoisting every block's LDS operands ahead took all 256
+                // registers with 5..8 vectors)
+                __builtin_amdgcn_sched_barrier(0);
+                // the two sub-blocks' weight operands q - 32 as int8: the low nibbles (columns
+                // 0-15) or high nibbles (16-31) of the low-bit chunk, OR the two high bits h
+                // (word s of the high-bit bytes shifted by 2 s) mapped by one byte permute to
+                // the upper nibble of q - 32, (h - 2) * 16: 0xE0, 0xF0, 0x00, 0x10
                 const uint4 c = t.c[i][0];
-                B0 = v4i_t{static_cast<int>(c.x & 0x0F0F0F0Fu), static_cast<int>(c.y & 0x0F0F0F0Fu),
-                           static_cast<int>(c.z & 0x0F0F0F0Fu), static_cast<int>(c.w & 0x0F0F0F0Fu)};
-                B1 = v4i_t{static_cast<int>((c.x >> 4) & 0x0F0F0F0Fu),
-                           static_cast<int>((c.y >> 4) & 0x0F0F0F0Fu),
-                           static_cast<int>((c.z >> 4) & 0x0F0F0F0Fu),
-                           static_cast<int>((c.w >> 4) & 0x0F0F0F0Fu)};
-            } else {
-                B0 = __builtin_bit_cast(v4i_t, t.c[i][0]);
-                B1 = __builtin_bit_cast(v4i_t, t.c[i][1]);
-            }
-            v4i_t P[H];
+                const uint2 hb = t.hb[i];
+                const uint32_t cw[4] = {c.x, c.y, c.z, c.w};
+                int b0[4], b1[4];
 #pragma unroll
-            for (int h = 0; h < H; h++) {
-                const v4i_t A0 = *reinterpret_cast<const v4i_t *>(abase[h] + 128 * i);
-                const v4i_t A1 = *reinterpret_cast<const v4i_t *>(abase[h] + 128 * i + 16);
-                P[h] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A0, B0, c8k[i][h], 0, 0, 0);
-                P[h] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A1, B1, P[h], 0, 0, 0);
-            }
-            // blocks past the split: P is 0 there, and so is d (whatever the loaded bits)
-            const bool bv = wb0 + 4 * i + g < nsb;
-            const float d = bv ? dl[i] : 0.0f;
+                for (int w = 0; w < 4; w++) {
+                    const uint32_t u0 = __builtin_amdgcn_perm(0u, 0x1000F0E0u, (hb.x >> (2 * w)) & 0x03030303u);
+                    const uint32_t u1 = __builtin_amdgcn_perm(0u, 0x1000F0E0u, (hb.y >> (2 * w)) & 0x03030303u);
+                    b0[w] = static_cast<int>((cw[w] & 0x0F0F0F0Fu) | u0);
+                    b1[w] = static_cast<int>(((cw[w] >> 4) & 0x0F0F0F0Fu) | u1);
+                }
+                const v4i_t B0 = v4i_t{b0[0], b0[1], b0[2], b0[3]};
+                const v4i_t B1 = v4i_t{b1[0], b1[1], b1[2], b1[3]};
+                // P0, P1 = sum (q - 32) xq of the block's two sub-blocks
+                v4i_t P0[H], P1[H];
+                v4f_t X[H];
+                const v4i_t zero = {0, 0, 0, 0};
 #pragma unroll
-            for (int h = 0; h < H; h++) {
+                for (int h = 0; h < H; h++) {
+                    const int o = (wb0 + 4 * i + g) * NV + 4 * h;
+                    const v4i_t A0 = *reinterpret_cast<const v4i_t *>(abase[h] + 128 * i);
+                    const v4i_t A1 = *reinterpret_cast<const v4i_t *>(abase[h] + 128 * i + 16);
+                    P0[h] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A0, B0, zero, 0, 0, 0);
+                    P1[h] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A1, B1, zero, 0, 0, 0);
+                    X[h] = *reinterpret_cast<const v4f_t *>(xd_s + o);
+                }
+                // the sub-scales of block wb0 + 4 i + g: bytes 2 (g % 2), + 1 of dword
+                // 2 (i % 2) + g / 2 of super-block i / 2's 16
+                const uint4 sw = t.sc[i >> 1];
+                const uint32_t word = (i & 1) ? ((g & 2) ? sw.w : sw.z) : ((g & 2) ? sw.y : sw.x);
+                const int sh = 16 * (g & 1);
+                const int sc0 = static_cast<int>(static_cast<int8_t>(word >> sh));
+                const int sc1 = static_cast<int>(static_cast<int8_t>(word >> (sh + 8)));
+                const bool bv = wb0 + 4 * i + g < nsb;
+                const float d = bv ? half_to_float(t.d[i >> 1]) : 0.0f;
 #pragma unroll
-                for (int e = 0; e < 4; e++)
-                    acc[h][e] = fmaf(xdk[i][h][e] * d, static_cast<float>(P[h][e]), acc[h][e]);
-                if (DBG) {
-                    const int64_t row = int64_t{tile} * 16 + r;
-                    const int blk = b_lo + wb0 + 4 * i + g;
+                for (int h = 0; h < H; h++) {
 #pragma unroll
                     for (int e = 0; e < 4; e++) {
-                        const int v = 4 * h + e;
-                        if (v < nvec && row < rows && bv)
-                            a.P[(int64_t{v} * rows + row) * nb + blk] = P[h][e];
+                        // exact: |sc P| < 2^23 for each sub-block, the sum below 2^24
+                        const int T = __mul24(sc0, P0[h][e]) + __mul24(sc1, P1[h][e]);
+                        acc[h][e] = fmaf(X[h][e] * d, static_cast<float>(T), acc[h][e]);
+                    }
+                    if (DBG) {
+                        const int64_t row = int64_t{tile} * 16 + r;
+                        const int blk = b_lo + wb0 + 4 * i + g;
+#pragma unroll
+                        for (int e = 0; e < 4; e++) {
+                            const int v = 4 * h + e;
+                            if (v < nvec && row < rows && bv) {
+                                int32_t *pp = a.P + (int64_t{v} * rows + row) * (2 * int64_t{nb}) + 2 * blk;
+                                pp[0] = P0[h][e];
+                                pp[1] = P1[h][e];
+                            }
+                        }
+                    }
+                }
+            }
+        } else {
+            // dl[i]: the scale of block wb0 + 4 i + g
+            float dl[4];
+            if constexpr (VS) {
+                // m[j] (lane group g) = scale of block wb0 + 4 g + j; dl[i] (lane group g) = m[g] of
+                // lane group i: a 4 x 4 transpose over the lane groups of each row r, one swap of
+                // halves (lanes l, l + 32) and one of rows of 16 (0-1, 2-3) per pair of registers
+                float m[4];
+                if constexpr (Q40) {
+                    m[0] = half_to_float(t.d[0] & 0xFFFFu);
+                    m[1] = half_to_float(t.d[0] >> 16);
+                    m[2] = half_to_float(t.d[1] & 0xFFFFu);
+                    m[3] = half_to_float(t.d[1] >> 16);
+                } else {
+    #pragma unroll
+                    for (int j = 0; j < 4; j++) m[j] = __builtin_bit_cast(float, t.d[j]);
+                }
+                uint32_t x[4];
+    #pragma unroll
+                for (int j = 0; j < 2; j++) {
+                    const auto sw = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, m[j]),
+                                                                     __builtin_bit_cast(uint32_t, m[j + 2]),
+                                                                     false, false);
+                    x[j] = sw[0];
+                    x[j + 2] = sw[1];
+                }
+    #pragma unroll
+                for (int j = 0; j < 2; j++) {
+                    const auto sw = __builtin_amdgcn_permlane16_swap(x[2 * j], x[2 * j + 1], false, false);
+                    const uint32_t lo = sw[0], hi = sw[1];
+                    dl[2 * j] = __builtin_bit_cast(float, lo);
+                    dl[2 * j + 1] = __builtin_bit_cast(float, hi);
+                }
+            } else {
+    #pragma unroll
+                for (int i = 0; i < 4; i++)
+                    dl[i] = Q40 ? half_to_float(t.d[i]) : __builtin_bit_cast(float, t.d[i]);
+            }
+    #pragma unroll
+            for (int i = 0; i < 4; i++) {
+                v4i_t B0, B1;
+                if constexpr (Q40) {
+                    const uint4 c = t.c[i][0];
+                    B0 = v4i_t{static_cast<int>(c.x & 0x0F0F0F0Fu), static_cast<int>(c.y & 0x0F0F0F0Fu),
+                               static_cast<int>(c.z & 0x0F0F0F0Fu), static_cast<int>(c.w & 0x0F0F0F0Fu)};
+                    B1 = v4i_t{static_cast<int>((c.x >> 4) & 0x0F0F0F0Fu),
+                               static_cast<int>((c.y >> 4) & 0x0F0F0F0Fu),
+                               static_cast<int>((c.z >> 4) & 0x0F0F0F0Fu),
+                               static_cast<int>((c.w >> 4) & 0x0F0F0F0Fu)};
+                } else {
+                    B0 = __builtin_bit_cast(v4i_t, t.c[i][0]);
+                    B1 = __builtin_bit_cast(v4i_t, t.c[i][1]);
+                }
+                v4i_t P[H];
+    #pragma unroll
+                for (int h = 0; h < H; h++) {
+                    const v4i_t A0 = *reinterpret_cast<const v4i_t *>(abase[h] + 128 * i);
+                    const v4i_t A1 = *reinterpret_cast<const v4i_t *>(abase[h] + 128 * i + 16);
+                    P[h] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A0, B0, c8k[i][h], 0, 0, 0);
+                    P[h] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A1, B1, P[h], 0, 0, 0);
+                }
+                // blocks past the split: P is 0 there, and so is d (whatever the loaded bits)
+                const bool bv = wb0 + 4 * i + g < nsb;
+                const float d = bv ? dl[i] : 0.0f;
+    #pragma unroll
+                for (int h = 0; h < H; h++) {
+    #pragma unroll
+                    for (int e = 0; e < 4; e++)
+                        acc[h][e] = fmaf(xdk[i][h][e] * d, static_cast<float>(P[h][e]), acc[h][e]);
+                    if (DBG) {
+                        const int64_t row = int64_t{tile} * 16 + r;
+                        const int blk = b_lo + wb0 + 4 * i + g;
+    #pragma unroll
+                        for (int e = 0; e < 4; e++) {
+                            const int v = 4 * h + e;
+                            if (v < nvec && row < rows && bv)
+                                a.P[(int64_t{v} * rows + row) * nb + blk] = P[h][e];
+                        }
                     }
                 }
             }
@@ -332,8 +427,28 @@ __global__ void __launch_bounds__(256) gemm_q32_i8_kernel(GemmArgs a) {
             slot ^= 1;
         }
     };
-    const int ntiles = (row_tiles - rt + stride - 1) / stride;
+    // One or two tiles: both are in flight already. More: the third goes into the first set as
+    // soon as the first tile's arithmetic has read it, and from then on each tile's successor
+    // goes out into the same registers right after the tile's arithmetic, ahead of the sums over
+    // the waves and the stores (past the last tile it reloads the last one, unused). The
+    // branches are uniform over the workgroup. (Two sets alternating in the loop kept two tiles
+    // in flight per wave but ran slower with 1-4 vectors: 262144 x 1536 Q8_0 x 1 in 87 against
+    // 77 us.)
     float z[H];
+    if constexpr (SINGLE) {
+        while (true) {
+            __builtin_amdgcn_sched_barrier(0);
+            products(rt, tA, z);
+            __builtin_amdgcn_sched_barrier(0);
+            issue(min(rt + stride, row_tiles - 1), tA);
+            __builtin_amdgcn_sched_barrier(0);
+            finish(rt, z);
+            rt += stride;
+            if (rt >= row_tiles) break;
+        }
+        return;
+    }
+    const int ntiles = (row_tiles - rt + stride - 1) / stride;     // this workgroup's tiles
     if (ntiles <= 2) {
         __builtin_amdgcn_sched_barrier(0);
         products(rt, tA, z);
@@ -418,12 +533,18 @@ hipError_t launch_fh(const GemmArgs &a, int waves, bool debug, hipStream_t strea
 
 template <int FMT>
 hipError_t launch_f(const GemmArgs &a, int waves, bool debug, hipStream_t stream) {
-    const bool vs = a.nb % 4 == 0;
-    if (a.nvec <= 4)
-        return vs ? launch_fh<FMT, 1, true>(a, waves, debug, stream)
-                  : launch_fh<FMT, 1, false>(a, waves, debug, stream);
-    return vs ? launch_fh<FMT, 2, true>(a, waves, debug, stream)
-              : launch_fh<FMT, 2, false>(a, waves, debug, stream);
+    // (Q6_K's super-block scales have loads of their own)
+    if constexpr (FMT == kTypeQ6K) {
+        return a.nvec <= 4 ? launch_fh<FMT, 1, false>(a, waves, debug, stream)
+                           : launch_fh<FMT, 2, false>(a, waves, debug, stream);
+    } else {
+        const bool vs = a.nb % 4 == 0;
+        if (a.nvec <= 4)
+            return vs ? launch_fh<FMT, 1, true>(a, waves, debug, stream)
+                      : launch_fh<FMT, 1, false>(a, waves, debug, stream);
+        return vs ? launch_fh<FMT, 2, true>(a, waves, debug, stream)
+                  : launch_fh<FMT, 2, false>(a, waves, debug, stream);
+    }
 }
 
 }  // namespace
@@ -440,6 +561,9 @@ hipError_t launch_gemm_q32_i8(int wtype, const GemmArgs &a, int waves, bool debu
     switch (wtype) {
         case kTypeQ80: return launch_f<kTypeQ80>(a, waves, debug, stream);
         case kTypeQ40: return launch_f<kTypeQ40>(a, waves, debug, stream);
+        case kTypeQ6K:
+            if (a.nb % 8 != 0) return hipErrorInvalidValue;
+            return launch_f<kTypeQ6K>(a, waves, debug, stream);
         default: return hipErrorInvalidValue;
     }
 }

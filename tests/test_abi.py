@@ -98,7 +98,12 @@ def test_routes():
     assert qg.qgemv_route("q4k", 16384, 2048, 8) == "i8mc"
     assert qg.qgemv_route("q4k", 16384, 2048, 4) == "vector"
     assert qg.qgemv_route("q4k", 262144, 1536, 3) == "i8mc"
-    assert qg.qgemv_route("q6k", 262144, 1536, 8) == "vector"
+    assert qg.qgemv_route("q6k", 262144, 1536, 8) == "mc32"         # few Q6_K vectors
+    assert qg.qgemv_route("q6k", 262144, 1536, 4) == "mc32"
+    assert qg.qgemv_route("q6k", 262144, 1536, 3) == "vector"
+    assert qg.qgemv_route("q6k", 65536, 2048, 8) == "mc32"
+    assert qg.qgemv_route("q6k", 65536, 2048, 7) == "vector"
+    assert qg.qgemv_route("q6k", 16384, 4096, 8) == "vector"
     assert qg.qgemv_route("q4k", 16384, 2048, 64) == "mc"
     assert qg.qgemv_route("q4k", 16384, 2048, 12) == "i8mc"         # 9..16 vectors: always
     assert qg.qgemv_route("q4k", 512, 512, 16) == "i8mc"
@@ -108,7 +113,9 @@ def test_routes():
     assert qg.qgemv_route("q80", 262144, 1536, 8) == "mc32"         # few vectors: 8 on >= 256 Mi
     assert qg.qgemv_route("q80", 262144, 1536, 7) == "vector"
     assert qg.qgemv_route("q80", 65536, 2048, 8) == "vector"
-    assert qg.qgemv_route("q40", 262144, 1536, 3) == "vector"       # Q4_0: from 4 on >= 32 Mi
+    assert qg.qgemv_route("q40", 262144, 1536, 2) == "vector"       # Q4_0: from 4 on >= 32 Mi
+    assert qg.qgemv_route("q40", 262144, 1536, 3) == "mc32"         # (3 on >= 256 Mi)
+    assert qg.qgemv_route("q40", 65536, 2048, 3) == "vector"
     assert qg.qgemv_route("q40", 262144, 1536, 4) == "mc32"
     assert qg.qgemv_route("q40", 16384, 2048, 4) == "mc32"
     assert qg.qgemv_route("q40", 16000, 2048, 8) == "vector"
@@ -351,9 +358,10 @@ def test_mc32_workspace_and_limits():
     assert qg.qgemv_mc32_workspace_bytes("q80", 2048, 8192, 8) == 4 * 8 * 2048 * 4
     assert qg.qgemv_mc32_workspace_bytes("q40", 2048, 2048, 8) == 0
     assert qg.qgemv_mc32_workspace_bytes("q40", 2048, 8224, 3) == 5 * 3 * 2048 * 4
-    assert qg.qgemv_mc32_workspace_bytes("q6k", 2048, 8192, 8) == 0
+    assert qg.qgemv_mc32_workspace_bytes("q6k", 2048, 8192, 8) == 4 * 8 * 2048 * 4
     assert qg.qgemv_mc32_workspace_bytes("q4k", 2048, 8192, 64) == 0
-    assert mc(2, A, X, D, Y, 2048, 8192, 8, None, 0, None) == EINVAL         # Q6_K: 9..256
+    assert mc(2, A, X, D, Y, 2048, 8192, 8, None, 0, None) == EWORKSPACE     # Q6_K: its split
+    assert mc(2, A, X, D, Y, 2048, 8192 + 32, 8, None, 0, None) == EINVAL    # Q6_K: whole 256s
     assert mc(4, A, X, D, Y, 2048, 8192, 8, None, 0, None) == EWORKSPACE     # its split
     assert mc(3, A, X, D, Y, 2048, 8192, 0, None, 0, None) == EINVAL
     assert mc(1, A, X, D, Y, 2048, 8192, 64, None, 0, None) == EINVAL        # Q4_K

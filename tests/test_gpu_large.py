@@ -51,7 +51,7 @@ def _big_tensor(wtype, small):
     return big
 
 
-CASES = [("q4k", 1), ("q4k", 8), ("q4k", 16), ("q4k", 64), ("q6k", 1), ("q6k", 16),
+CASES = [("q4k", 1), ("q4k", 8), ("q4k", 16), ("q4k", 64), ("q6k", 1), ("q6k", 8), ("q6k", 16),
          ("q40", 1), ("q40", 8), ("q40", 16), ("q80", 1), ("q80", 8), ("q80", 16)]
 
 
@@ -74,6 +74,14 @@ def test_beyond_4gib(wtype):
         ref = {k: np.tile(ref_u[k], (1, ROWS // U)) for k in ("y", "bound")}
         xq, xd = gu.quantize_act(x)
         gu.assert_within_bound(gu.gemv(wtype, big, xq, xd, ROWS, COLS, nvec), ref)
+        if nvec == 8 and wtype != "q4k":
+            # the few-vector matrix-core kernel itself, whatever the route
+            y = torch.full((nvec, ROWS), float("nan"), dtype=torch.float32, device=gu.DEV)
+            nbytes = qg.qgemv_mc32_workspace_bytes(wtype, ROWS, COLS, nvec)
+            ws = torch.empty(max(nbytes, 4), dtype=torch.uint8, device=gu.DEV) if nbytes else None
+            qg.qgemv_batch_mc32(wtype, big, xq, xd, y, ROWS, COLS, nvec, workspace=ws)
+            gu.assert_within_bound(gu.host(y), ref)
+            del y, ws
         if nvec == 1:
             # the fused one-launch kernel (no code outputs)
             y = torch.full((1, ROWS), float("nan"), dtype=torch.float32, device=gu.DEV)
@@ -81,15 +89,19 @@ def test_beyond_4gib(wtype):
             ws = torch.empty(max(nbytes, 4), dtype=torch.uint8, device=gu.DEV) if nbytes else None
             qg.qgemv_fused(wtype, big, gu.dev(x), y, ROWS, COLS, 1, workspace=ws)
             gu.assert_within_bound(gu.host(y), ref)
-        if nvec in (1, 16) or (nvec == 8 and wtype in ("q40", "q80")):
+        if nvec in (1, 8, 16):
             # integer partials on rows sampled over the whole tensor (the last rows included),
-            # gathered on the GPU (the whole array is up to 43 GB)
+            # gathered on the GPU (the whole array is up to 43 GB); with 8 vectors those of the
+            # few-vector matrix-core kernel whatever the route
             nsub = COLS // 16 if wtype == "q6k" else COLS // 32
             P = torch.full((nvec, ROWS, nsub), -(2 ** 31), dtype=torch.int32, device=gu.DEV)
             S = torch.empty((nvec, COLS // 32), dtype=torch.int32, device=gu.DEV)
             nbytes = qg.qgemv_workspace_bytes(wtype, ROWS, COLS, nvec)
             ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=gu.DEV) if nbytes else None
-            qg.qgemv_debug_partials(wtype, big, xq, xd, P, S, ROWS, COLS, nvec, workspace=ws)
+            if nvec == 8 and wtype != "q4k":
+                qg.qgemv_debug_partials_mc32(wtype, big, xq, xd, P, S, ROWS, COLS, nvec)
+            else:
+                qg.qgemv_debug_partials(wtype, big, xq, xd, P, S, ROWS, COLS, nvec, workspace=ws)
             rows = np.concatenate([np.arange(0, ROWS, 4099), np.arange(ROWS - U, ROWS)])
             got = gu.host(P[:, torch.from_numpy(rows).to(gu.DEV)])
             del P, S, ws

@@ -126,8 +126,22 @@ SHAPES_FEW = [
     (16384, 2048, 5),     # where qgemv_batch takes this kernel for Q4_0
 ]
 
+SHAPES_FEW_Q6K = [
+    # (rows, cols, nvec): 1..8 Q6_K vectors (rows of whole super-blocks)
+    (300, 1280, 3),       # 40 blocks: three waves, the third with one super-block
+    (257, 768, 8),        # two waves, the second with one super-block; two halves of 4 vectors
+    (128, 2048, 5),       # four full waves
+    (1000, 4096, 7),      # two splits
+    (131, 256, 1),        # one super-block, one wave
+    (64, 8448, 4),        # 264 blocks: five splits of four waves, the last of one super-block
+    (4100, 1536, 6),      # three waves, 257 row tiles
+    (20000, 2048, 3),     # workgroups walk more than two row tiles
+    (20000, 1536, 8),
+]
+
 CASES = ([(w, *s) for w in ("q80", "q40") for s in SHAPES] + [("q6k", *s) for s in SHAPES_Q6K] +
-         [(w, *s) for w in ("q80", "q40") for s in SHAPES_FEW])
+         [(w, *s) for w in ("q80", "q40") for s in SHAPES_FEW] +
+         [("q6k", *s) for s in SHAPES_FEW_Q6K])
 
 
 @pytest.mark.parametrize("wtype,rows,cols,nvec", CASES)
