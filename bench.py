@@ -113,6 +113,8 @@ def kernel_unit(kname: str) -> str:
         return "gemm_mfma.hip"
     if kname.startswith("gemm_q32_mc_kernel"):
         return "gemm_q32.hip"
+    if kname.startswith("gemm_q32_i8_kernel"):
+        return "gemm_q32_i8.hip"
     if kname.startswith("gemm_q6k_mc_kernel"):
         return "gemm_q6k_mc.hip"
     for tag, unit in (("Q4K", "gemv_q4k.hip"), ("Q6K", "gemv_q6k.hip"), ("Q40", "gemv_q40.hip"),
@@ -198,6 +200,11 @@ def roofline_kernel(wtype: str, plan: dict, nvec: int, launches: int, route: str
         # the third template argument (operands kept in registers or not) is chosen at launch
         # from the GPU's occupancy, so the name is given up to it (a prefix of the trace name)
         return "gemm_q4k_i8_kernel<%d, %d, " % (2 if launches == 1 else 0, (nvec + 7) // 8)
+    if route == "mc32" and nvec <= 8:
+        # the few-vector integer matrix-core kernel (format, form from codes, halves of 4
+        # vectors; the last argument, one scale load per lane, follows the row width)
+        return "gemm_q32_i8_kernel<%d, 0, %d, " % ({"q6k": 2, "q40": 3, "q80": 4}[wtype],
+                                                   (nvec + 3) // 4)
     tag = {"q4k": "Q4K", "q6k": "Q6K", "q40": "Q40", "q80": "Q80"}[wtype]
     if launches != 1 and plan["splits"] > 1:
         # the unfused product of a split plan: the column split inside the workgroup

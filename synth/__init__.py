@@ -182,6 +182,12 @@ WORKLOADS = {
     # ... and Q6_K there (the format a vocabulary projection is often kept in; weight seed 1009)
     "q6k_262144x1536": Workload("q6k_262144x1536", "q6k", 262144, 1536, 1, 1009, 3700,
                                 outlier_frac=0.01, seed_rows=3009),
+    # a few vectors at once (several sequences decoded together) on the Q4_0 and Q6_K
+    # projections above (their weights; vector v has activation seed 3800 + v, resp. 3900 + v)
+    "q40_262144x1536_b8": Workload("q40_262144x1536_b8", "q40", 262144, 1536, 8, 1005, 3800,
+                                   outlier_frac=0.01, seed_rows=3005),
+    "q6k_262144x1536_b8": Workload("q6k_262144x1536_b8", "q6k", 262144, 1536, 8, 1009, 3900,
+                                   outlier_frac=0.01, seed_rows=3009),
     # many vectors at once (tokens verified or prefilled together) on the matrices above:
     # vector v has activation seed 3100 + v (resp. 3400 + v)
     "q4k_262144x1536_b64": Workload("q4k_262144x1536_b64", "q4k", 262144, 1536, 64, 1003, 3100,
