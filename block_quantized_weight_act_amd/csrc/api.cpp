@@ -120,14 +120,25 @@ int64_t target_waves(int32_t nvec) { return nvec <= 2 ? 256 * 64 : 256 * 16; }
 // Lanes per row and chunks per lane for a row of `cols` columns (see make_plan). With
 // one_pass set, only geometries that cover the whole row in one pass; with fit_waves, only
 // those whose passes (column chunks) a workgroup can split among its waves; false if there is
-// none.
+// none. With several_rule (the one-matrix planner), two corrections measured with several
+// vectors apply (explicit plans against the planner's, graph replay, cold, MI355X; the best
+// of the T x NC plans within 3% on average, against 8% before):
+//  * 2 vectors take at most 3 chunks per lane: 4 chunks (64 activation registers) ran
+//    24-50% slower than 1-2 (16384 / 65536 x 2048 x 2: 7.2 / 22.7 us with T 16, NC 4, against
+//    5.8 / 15.8 with T 32, NC 2; 16384 x 4096 x 2: 12.3 against 9.3 with T 64, NC 2);
+//  * 5 or more vectors (one chunk per lane) weigh a split pass like 15% idle lanes, so a row
+//    of 48 chunks takes one pass of 64 lanes with a quarter idle rather than three of 16
+//    (262144 x 1536 x 8: 92.9 against 125.4 us; x 6: 78.2 against 84.4; 65536 x 1536 x 8:
+//    26.9 against 36.2).
 bool choose_geometry(int64_t cols, int32_t nvec, bool one_pass, int &best_t, int &best_nc,
-                     bool fit_waves = false) {
+                     bool fit_waves = false, bool several_rule = false) {
     const int64_t nchunks = cols / 32;
     bool found = false;
     double best_cost = 1e30;
+    const double split_cost = several_rule && nvec >= 5 ? 0.15 : 0.02;
     for (int nc = 1; nc <= 4; nc++) {
         if (nvec * nc > 8) break;
+        if (several_rule && nvec == 2 && nc > 3) break;
         for (int t : {8, 16, 32, 64}) {
             const int64_t per = static_cast<int64_t>(t) * nc;
             const int64_t passes = (nchunks + per - 1) / per;
@@ -135,7 +146,7 @@ bool choose_geometry(int64_t cols, int32_t nvec, bool one_pass, int &best_t, int
             if (fit_waves && passes > gemv_max_waves(nvec, t, nc)) continue;
             const double waste = 1.0 - static_cast<double>(nchunks) / (passes * per);
             // idle lanes cost bandwidth in flight; split passes cost a workspace round trip
-            const double cost = waste + 0.02 * (passes - 1) - 0.01 * nc;
+            const double cost = waste + split_cost * (passes - 1) - 0.01 * nc;
             if (cost < best_cost - 1e-12) {
                 best_cost = cost;
                 best_t = t;
@@ -149,7 +160,7 @@ bool choose_geometry(int64_t cols, int32_t nvec, bool one_pass, int &best_t, int
 
 qgemv_plan make_plan(int wtype, int64_t rows, int64_t cols, int32_t nvec) {
     int best_t = 64, best_nc = 1;
-    choose_geometry(cols, nvec, false, best_t, best_nc);
+    choose_geometry(cols, nvec, false, best_t, best_nc, false, true);
     qgemv_plan p{};
     p.lanes_per_row = best_t;
     p.chunks_per_lane = best_nc;
@@ -442,7 +453,7 @@ int run_mc(const void *w, const int8_t *xq, const float *xd, float *y, int32_t *
 // per CU (the splits added by the ordered reduce).
 bool mc32_ok(int wtype, int64_t rows, int64_t cols, int32_t nvec) {
     const bool fmt = wtype == QGEMV_Q8_0 || wtype == QGEMV_Q4_0 || wtype == QGEMV_Q6K;
-    const bool few = fmt && nvec >= 1 && nvec <= kQ32I8MaxVec;
+    const bool few = (fmt || wtype == QGEMV_Q4K) && nvec >= 1 && nvec <= kQ32I8MaxVec;
     const bool many = fmt && nvec > kMaxVec && nvec <= kMaxBatch;
     return (few || many) && shape_ok_t(wtype, rows, cols, 1) &&
            static_cast<int64_t>(nvec) * cols < (int64_t{1} << 34);
@@ -946,9 +957,14 @@ size_t qgemv_workspace_bytes(int wtype, int64_t rows, int64_t cols, int32_t nvec
     if (mc_shape_ok(wtype, rows, cols, nvec))
         return mc_ws_bytes(make_mc_plan(rows, cols, nvec), rows, cols, nvec);
     if (grouped_shape_ok(wtype, rows, cols, nvec)) {
-        // groups of up to kMaxVec vectors, one after another on the stream, share the workspace
-        const int32_t g = std::min<int32_t>(nvec, kMaxVec);
-        return plan_ws_bytes(make_plan(wtype, rows, cols, g), rows, cols, g);
+        // groups of up to kMaxVec vectors, one after another on the stream, share the
+        // workspace: the largest of the full groups' and the last, smaller group's (whose plan
+        // may split the columns where the full groups' does not)
+        const int32_t rest = nvec % kMaxVec;
+        size_t need = plan_ws_bytes(make_plan(wtype, rows, cols, kMaxVec), rows, cols, kMaxVec);
+        if (rest > 0)
+            need = std::max(need, plan_ws_bytes(make_plan(wtype, rows, cols, rest), rows, cols, rest));
+        return need;
     }
     if (!shape_ok_t(wtype, rows, cols, nvec)) return 0;
     return plan_ws_bytes(make_plan(wtype, rows, cols, nvec), rows, cols, nvec);

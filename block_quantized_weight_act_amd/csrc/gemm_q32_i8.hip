@@ -64,8 +64,9 @@ __global__ void __launch_bounds__(256) gemm_q32_i8_kernel(GemmArgs a) {
     constexpr bool DBG = MODE == kModeDebug;
     constexpr bool Q40 = FMT == kTypeQ40;
     constexpr bool Q6 = FMT == kTypeQ6K;
+    constexpr bool QK = FMT == kTypeQ4K;
     constexpr int NV = 4 * H;
-    constexpr int NP = Q40 || Q6 ? 1 : 2;      // 16-byte code chunks per block and lane
+    constexpr int NP = FMT == kTypeQ80 ? 2 : 1;    // 16-byte code chunks per block and lane
     // One tile in flight per wave from the start (SINGLE), or two (the first two tiles) with the
     // registers of a second set: with 5..8 Q6_K or Q4_0 vectors the second set costs more
     // resident waves than it gains (262144 x 1536 x 8: Q6_K 72.4 against 113.1 us, Q4_0 44.1
@@ -94,7 +95,7 @@ __global__ void __launch_bounds__(256) gemm_q32_i8_kernel(GemmArgs a) {
     const int64_t nblocks = static_cast<int64_t>(rows) * nb;
     const uint8_t *const hi_plane = a.w + nblocks * 16;        // Q8_0: codes 16..31; Q6_K: high bits
     const uint8_t *const d_plane = a.w + nblocks * (Q40 ? 16 : (Q6 ? 26 : 32));
-    const uint8_t *const sc_plane = a.w + nblocks * 24;        // Q6_K: sub-scales
+    const uint8_t *const sc_plane = a.w + nblocks * (QK ? 16 : 24);  // Q6_K sub-scales; Q4_K headers
 
     int rt = blockIdx.x;
     if (rt >= row_tiles) return;               // the whole workgroup (never taken: grid <= tiles)
@@ -113,7 +114,7 @@ __global__ void __launch_bounds__(256) gemm_q32_i8_kernel(GemmArgs a) {
         uint4 c[4][NP];
         uint32_t d[4];
         uint2 hb[Q6 ? 4 : 1];
-        uint4 sc[Q6 ? 2 : 1];
+        uint4 sc[Q6 || QK ? 2 : 1];
     };
     auto issue = [&](int tile, WTile &t) {
         const int64_t row = std::min<int64_t>(int64_t{tile} * 16 + r, rows - 1);
@@ -124,22 +125,22 @@ __global__ void __launch_bounds__(256) gemm_q32_i8_kernel(GemmArgs a) {
             t.c[i][0] = load16(a.w + blk * 16);
             if constexpr (Q6) t.hb[i] = *reinterpret_cast<const uint2 *>(hi_plane + blk * 8);
             if constexpr (!Q40 && !Q6) t.c[i][1] = load16(hi_plane + blk * 16);
-            if constexpr (!VS && !Q6) {
+            if constexpr (!VS && !Q6 && !QK) {
                 if constexpr (Q40)
                     t.d[i] = reinterpret_cast<const uint16_t *>(d_plane)[blk];
                 else
                     t.d[i] = reinterpret_cast<const uint32_t *>(d_plane)[blk];
             }
         }
-        if constexpr (Q6) {
+        if constexpr (Q6 || QK) {
 #pragma unroll
             for (int q = 0; q < 2; q++) {
                 const int64_t sbk = (rb + min(wb0 + 8 * q, nsb - 8)) >> 3;
                 t.sc[q] = load16(sc_plane + sbk * 16);
-                t.d[q] = reinterpret_cast<const uint16_t *>(d_plane)[sbk];
+                if constexpr (Q6) t.d[q] = reinterpret_cast<const uint16_t *>(d_plane)[sbk];
             }
         }
-        if constexpr (VS && !Q6) {
+        if constexpr (VS && !Q6 && !QK) {
             const int64_t b4 = rb + min(wb0 + 4 * g, nsb - 4);
             if constexpr (Q40) {
                 const uint2 v = *reinterpret_cast<const uint2 *>(d_plane + b4 * 2);
@@ -190,7 +191,10 @@ __global__ void __launch_bounds__(256) gemm_q32_i8_kernel(GemmArgs a) {
             *reinterpret_cast<uint4 *>(xq_s + v * pitch + 32 * b) = c0;
             *reinterpret_cast<uint4 *>(xq_s + v * pitch + 32 * b + 16) = c1;
             xd_s[b * NV + v] = sv[p];
-            s8_s[b * NV + v] = -8 * s;
+            if constexpr (QK)
+                reinterpret_cast<float *>(s8_s)[b * NV + v] = -(sv[p] * static_cast<float>(s));
+            else
+                s8_s[b * NV + v] = -8 * s;
             if (DBG && blockIdx.x == 0 && v < nvec && b < nsb)
                 a.S[static_cast<int64_t>(v) * nb + b_lo + b] = s;
         }
@@ -208,6 +212,8 @@ __global__ void __launch_bounds__(256) gemm_q32_i8_kernel(GemmArgs a) {
         abase[h] = xq_s + (live ? 4 * h + (r & 3) : NV) * pitch + (wb0 + g) * 32;
     v4f_t xdk[4][H];
     v4i_t c8k[4][H];
+    float mink[4][H];   // Q4_K: the min-term product's row operand (slot r < 4: -xd S of vector
+                        // 4 h + r, block wb0 + 4 i + g; 0 in the other slots)
 #pragma unroll
     for (int i = 0; i < 4; i++)
 #pragma unroll
@@ -215,6 +221,9 @@ __global__ void __launch_bounds__(256) gemm_q32_i8_kernel(GemmArgs a) {
             const int o = (wb0 + 4 * i + g) * NV + 4 * h;
             xdk[i][h] = Q6 ? v4f_t{0.0f, 0.0f, 0.0f, 0.0f} : *reinterpret_cast<const v4f_t *>(xd_s + o);
             c8k[i][h] = Q40 ? *reinterpret_cast<const v4i_t *>(s8_s + o) : v4i_t{0, 0, 0, 0};
+            mink[i][h] = QK && r < 4
+                             ? reinterpret_cast<const float *>(s8_s)[(wb0 + 4 * i + g) * NV + 4 * h + r]
+                             : 0.0f;
             // (Q6_K reads its activation scales per product instead: its weight operands take
             // more registers)
         }
@@ -227,7 +236,66 @@ __global__ void __launch_bounds__(256) gemm_q32_i8_kernel(GemmArgs a) {
         v4f_t acc[H];
 #pragma unroll
         for (int h = 0; h < H; h++) acc[h] = v4f_t{0.0f, 0.0f, 0.0f, 0.0f};
-        if constexpr (Q6) {
+        if constexpr (QK) {
+            // Q4_K: the super-scales of the wave's two super-blocks (d, dmin in the header's
+            // first word), then per block the exact integer sc * P, one fma with d * xd, and the
+            // min term -dmin * m * xd * S as a contraction over the four blocks of the product
+            // (lane group g: dmin * m of block 4 i + g; slots 0-3: -xd * S) on the float32
+            // matrix cores, straight into the accumulator
+            float dq[2], dmq[2];
+#pragma unroll
+            for (int q = 0; q < 2; q++) {
+                dq[q] = half_to_float(t.sc[q].x & 0xFFFFu);
+                dmq[q] = half_to_float(t.sc[q].x >> 16);
+            }
+            const v4i_t zero = {0, 0, 0, 0};
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const uint4 c = t.c[i][0];
+                const v4i_t B0 = v4i_t{static_cast<int>(c.x & 0x0F0F0F0Fu), static_cast<int>(c.y & 0x0F0F0F0Fu),
+                                       static_cast<int>(c.z & 0x0F0F0F0Fu), static_cast<int>(c.w & 0x0F0F0F0Fu)};
+                const v4i_t B1 = v4i_t{static_cast<int>((c.x >> 4) & 0x0F0F0F0Fu),
+                                       static_cast<int>((c.y >> 4) & 0x0F0F0F0Fu),
+                                       static_cast<int>((c.z >> 4) & 0x0F0F0F0Fu),
+                                       static_cast<int>((c.w >> 4) & 0x0F0F0F0Fu)};
+                v4i_t P[H];
+#pragma unroll
+                for (int h = 0; h < H; h++) {
+                    const v4i_t A0 = *reinterpret_cast<const v4i_t *>(abase[h] + 128 * i);
+                    const v4i_t A1 = *reinterpret_cast<const v4i_t *>(abase[h] + 128 * i + 16);
+                    P[h] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A0, B0, zero, 0, 0, 0);
+                    P[h] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A1, B1, P[h], 0, 0, 0);
+                }
+                // sub-scale and min of block bs = 4 (i % 2) + g of super-block i / 2: low 4 bits
+                // at bit 4 bs of the second (scales) and third (mins) words, high 2 bits at bit
+                // 2 bs (scales) and 16 + 2 bs (mins) of the fourth
+                const uint4 hd = t.sc[i >> 1];
+                const int bs = 4 * (i & 1) + g;
+                const int sc = static_cast<int>(((hd.y >> (4 * bs)) & 15u) | (((hd.w >> (2 * bs)) & 3u) << 4));
+                const uint32_t m = ((hd.z >> (4 * bs)) & 15u) | (((hd.w >> (16 + 2 * bs)) & 3u) << 4);
+                const bool bv = wb0 + 4 * i + g < nsb;
+                const float d = bv ? dq[i >> 1] : 0.0f;
+                const float dm = bv ? dmq[i >> 1] * static_cast<float>(m) : 0.0f;
+#pragma unroll
+                for (int h = 0; h < H; h++) {
+#pragma unroll
+                    for (int e = 0; e < 4; e++)     // sc * P exact: below 2^22
+                        acc[h][e] = fmaf(xdk[i][h][e] * d, static_cast<float>(__mul24(sc, P[h][e])),
+                                         acc[h][e]);
+                    acc[h] = __builtin_amdgcn_mfma_f32_16x16x4f32(mink[i][h], dm, acc[h], 0, 0, 0);
+                    if (DBG) {
+                        const int64_t row = int64_t{tile} * 16 + r;
+                        const int blk = b_lo + wb0 + 4 * i + g;
+#pragma unroll
+                        for (int e = 0; e < 4; e++) {
+                            const int v = 4 * h + e;
+                            if (v < nvec && row < rows && bv)
+                                a.P[(int64_t{v} * rows + row) * nb + blk] = P[h][e];
+                        }
+                    }
+                }
+            }
+        } else if constexpr (Q6) {
 #pragma unroll
             for (int i = 0; i < 4; i++) {
                 // (one block at a time: hoisting every block's LDS operands ahead took all 256
@@ -534,7 +602,7 @@ hipError_t launch_fh(const GemmArgs &a, int waves, bool debug, hipStream_t strea
 template <int FMT>
 hipError_t launch_f(const GemmArgs &a, int waves, bool debug, hipStream_t stream) {
     // (Q6_K's super-block scales have loads of their own)
-    if constexpr (FMT == kTypeQ6K) {
+    if constexpr (FMT == kTypeQ6K || FMT == kTypeQ4K) {
         return a.nvec <= 4 ? launch_fh<FMT, 1, false>(a, waves, debug, stream)
                            : launch_fh<FMT, 2, false>(a, waves, debug, stream);
     } else {
@@ -564,6 +632,9 @@ hipError_t launch_gemm_q32_i8(int wtype, const GemmArgs &a, int waves, bool debu
         case kTypeQ6K:
             if (a.nb % 8 != 0) return hipErrorInvalidValue;
             return launch_f<kTypeQ6K>(a, waves, debug, stream);
+        case kTypeQ4K:
+            if (a.nb % 8 != 0) return hipErrorInvalidValue;
+            return launch_f<kTypeQ4K>(a, waves, debug, stream);
         default: return hipErrorInvalidValue;
     }
 }

@@ -135,6 +135,26 @@ def test_routes():
     assert qg._load().qgemv_route(1, 8, 512, 300) == 0
 
 
+def test_grouped_workspace_covers_the_last_group():
+    """Groups of 8 vectors share one workspace: it must hold the last, smaller group's partial
+    sums too when that group's plan splits the columns and the full groups' does not."""
+    rows, cols = 300, 1056
+    assert qg.qgemv_route("q80", rows, cols, 9) == "grouped"
+    p8, p1 = qg.qgemv_plan_for("q80", rows, cols, 8), qg.qgemv_plan_for("q80", rows, cols, 1)
+    need1 = qg.qgemv_plan_workspace_bytes(p1, rows, cols, 1)
+    need8 = qg.qgemv_plan_workspace_bytes(p8, rows, cols, 8)
+    assert need1 > 0
+    assert qg.qgemv_workspace_bytes("q80", rows, cols, 9) == max(need1, need8)
+    for nvec in (9, 12, 17, 24, 33):
+        rest = nvec % 8
+        want = qg.qgemv_plan_workspace_bytes(qg.qgemv_plan_for("q40", 16384, 1536, 8), 16384, 1536, 8)
+        if rest:
+            want = max(want, qg.qgemv_plan_workspace_bytes(
+                qg.qgemv_plan_for("q40", 16384, 1536, rest), 16384, 1536, rest))
+        if qg.qgemv_route("q40", 16384, 1536, nvec) == "grouped":
+            assert qg.qgemv_workspace_bytes("q40", 16384, 1536, nvec) == want
+
+
 def test_split_plan_without_workspace_is_rejected():
     lib = qg._load()
     plan = qg.Plan(16, 1, 4, 4, 0)

@@ -56,7 +56,7 @@ def _check(wtype, wbuf, rows, cols, x, debug=True):
     # qgemv_batch: the same kernel (bit for bit) where it routes there, else the vector kernel
     # (on groups of 8 with more than 8 vectors), within the same bound
     route = qg.qgemv_route(wtype, rows, cols, nvec)
-    assert route in (("mc32", "vector") if nvec <= 8 else ("mc32", "grouped"))
+    assert route in (("mc32", "vector", "i8mc") if nvec <= 8 else ("mc32", "grouped"))
     yb = gu.gemv(wtype, wt, xq, xd, rows, cols, nvec)
     if route == "mc32":
         assert np.array_equal(yb.view(np.uint32), y.view(np.uint32))
@@ -141,13 +141,13 @@ SHAPES_FEW_Q6K = [
 
 CASES = ([(w, *s) for w in ("q80", "q40") for s in SHAPES] + [("q6k", *s) for s in SHAPES_Q6K] +
          [(w, *s) for w in ("q80", "q40") for s in SHAPES_FEW] +
-         [("q6k", *s) for s in SHAPES_FEW_Q6K])
+         [(w, *s) for w in ("q6k", "q4k") for s in SHAPES_FEW_Q6K])
 
 
 @pytest.mark.parametrize("wtype,rows,cols,nvec", CASES)
 def test_parity(wtype, rows, cols, nvec):
     _say(wtype, rows, cols, nvec)
-    rng = np.random.default_rng(rows * 31 + cols + nvec + ("q80", "q40", "q6k").index(wtype))
+    rng = np.random.default_rng(rows * 31 + cols + nvec + ("q80", "q40", "q6k", "q4k").index(wtype))
     w = (rng.standard_normal((rows, cols)) * 0.02).astype(np.float32)
     w[0, :64] = 0.0                                     # zero weight blocks: exactly 0
     x = (rng.standard_normal((nvec, cols)) * rng.choice([1e-3, 1.0, 40.0], size=(nvec, 1))).astype(np.float32)
