@@ -476,7 +476,8 @@ bool mc32_ok(int wtype, int64_t rows, int64_t cols, int32_t nvec) {
 // 2048 columns; a second split and its reduce cost more than they save below 8 vectors):
 // Q4_0 from 4 vectors on tensors of at least 32 Mi weights (3 from 256 Mi; with two splits 8);
 // Q6_K from 4 vectors on 256 Mi weights, with 8 from 64 Mi; Q8_0 (twice the bytes per weight)
-// with 8 vectors from 256 Mi weights. Measured on MI355X (graph replay, cold; this kernel
+// with 8 vectors from 256 Mi weights; Q4_K with 4 vectors where its own integer kernel is not
+// taken (below). Measured on MI355X (graph replay, cold; this kernel
 // against the vector kernel, us):
 //   Q4_0 262144 x 1536 x 2 / 3 / 4 / 8: 40.9 / 36.5, 40.6 / 44.8, 40.7 / 47.7, 43.8 / 97.8;
 //        65536 x 2048 x 3 / 4 / 5 / 8: 17.1 / 15.2, 17.4 / 17.0, 17.7 / 19.5, 17.8 / 23.5;
@@ -486,6 +487,8 @@ bool mc32_ok(int wtype, int64_t rows, int64_t cols, int32_t nvec) {
 //        65536 x 2048 x 4 / 6 / 8: 26.9 / 25.1, 31.3 / 27.1, 31.2 / 32.1;
 //        16384 x 2048 x 8: 10.6 / 10.7; 16384 x 4096 x 8: 23.3 / 20.1;
 //   Q8_0 262144 x 1536 x 6 / 8: 86.0 / 84.2, 84.2 / 103.6; 65536 x 2048 x 8: 29.7 / 29.1.
+int64_t i8_min_bytes(int32_t nvec);
+
 bool q32i8_auto(int wtype, int64_t rows, int64_t cols, int32_t nvec) {
     constexpr int64_t Mi = int64_t{1} << 20;
     const int64_t weights = rows * cols;
@@ -498,6 +501,15 @@ bool q32i8_auto(int wtype, int64_t rows, int64_t cols, int32_t nvec) {
             return one_split && ((weights >= 256 * Mi && nvec >= 4) ||
                                  (weights >= 64 * Mi && nvec >= 8));
         case QGEMV_Q8_0: return one_split && weights >= 256 * Mi && nvec >= 8;
+        case QGEMV_Q4K: {
+            // 4 vectors on tensors of 16-96 MiB, below the Q4_K integer kernel's threshold
+            // (i8_min_bytes); measured against the vector kernel (planner's plan): 16384 /
+            // 32768 / 65536 x 2048 x 4 in 7.09 / 10.7 / 17.7 against 8.15 / 12.3 / 20.9 us;
+            // with 3, 5 or 6 vectors it was within a few % either way
+            const int64_t bytes = static_cast<int64_t>(weight_bytes(wtype, rows, cols));
+            return one_split && nvec == 4 && bytes >= (int64_t{16} << 20) &&
+                   bytes < i8_min_bytes(4);
+        }
         default: return false;
     }
 }

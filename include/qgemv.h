@@ -239,8 +239,9 @@ int qgemv_batch_scratch(int wtype, const void *w, const int8_t *xq, const float 
  * (QGEMV_ROUTE_MC32) where the vector kernel's dot products bind, on rows of up
  * to 2048 columns: Q4_0 from 4 vectors on tensors of at least 32 Mi weights (3
  * from 256 Mi; 8 on wider rows), Q6_K from 4 vectors on 256 Mi weights and with
- * 8 from 64 Mi, Q8_0 with 8 vectors from 256 Mi; 0 for an invalid type or shape.
- * Host only. */
+ * 8 from 64 Mi, Q8_0 with 8 vectors from 256 Mi, and Q4_K with 4 vectors on
+ * tensors of 16 to 96 MiB (below QGEMV_ROUTE_I8MC's sizes); 0 for an invalid
+ * type or shape. Host only. */
 enum qgemv_route_kind {
     QGEMV_ROUTE_VECTOR = 1,
     QGEMV_ROUTE_I8MC = 2,
@@ -251,20 +252,21 @@ enum qgemv_route_kind {
 int qgemv_route(int wtype, int64_t rows, int64_t cols, int32_t nvec);
 
 /*
- * Q8_0, Q4_0 or Q6_K with 1 <= nvec <= QGEMV_MAX_BATCH on the integer matrix
- * cores, for any shape (qgemv_batch takes it
+ * Q8_0, Q4_0 or Q6_K with 1 <= nvec <= QGEMV_MAX_BATCH, and Q4_K with
+ * 1 <= nvec <= 8, on the integer matrix cores, for any shape (qgemv_batch takes it
  * where QGEMV_ROUTE_MC32 says; oxinfer README, "Speculative decoding": the
  * multi-token int8 variants). With 9 or more vectors one product is 32 weight rows
  * x 32 vectors over one 32-weight block (Q8_0: the stored codes; Q4_0: the codes
  * 0..15, then P = sum q * xq - 8 S in integer) or over one 16-weight Q6_K
  * sub-block (the operand q - 32); with 1..8 vectors one product is 16 weight rows
  * x 4 blocks x 4 vectors over one 16-weight half of each block
- * (v_mfma_i32_16x16x64_i8; for Q8_0 and Q4_0 two accumulate into a block's P,
- * Q4_0's starting from -8 S; for Q6_K each half is a sub-block, the operand
+ * (v_mfma_i32_16x16x64_i8; for Q8_0, Q4_0 and Q4_K two accumulate into a block's
+ * P, Q4_0's starting from -8 S; for Q6_K each half is a sub-block, the operand
  * q - 32). Either way the int32 result is the exact integer partial P of
  * qgemv_debug_partials for every (row, vector); then y is sum over blocks of
  * (d * xd) * P (Q6_K: xd * (sc0 * P0 + sc1 * P1) per block, the integer
- * combination exact, times d per half super-block) in float32, within the same
+ * combination exact, times d per half super-block; Q4_K: d * xd * (sc * P) and
+ * the min term -dmin * m * xd * S) in float32, within the same
  * bound as the vector kernels' y. Arguments as for qgemv_batch; the workspace
  * (qgemv_mc32_workspace_bytes: partial sums when the columns are split, with 9 or
  * more vectors because row tiles and vector groups give fewer than 512

@@ -96,7 +96,10 @@ def test_i8mc_workspace_and_routing():
 def test_routes():
     assert qg.qgemv_route("q4k", 262144, 1536, 1) == "vector"
     assert qg.qgemv_route("q4k", 16384, 2048, 8) == "i8mc"
-    assert qg.qgemv_route("q4k", 16384, 2048, 4) == "vector"
+    assert qg.qgemv_route("q4k", 16384, 2048, 4) == "mc32"      # 4 vectors on 16-96 MiB
+    assert qg.qgemv_route("q4k", 16384, 2048, 3) == "vector"
+    assert qg.qgemv_route("q4k", 16384, 4096, 4) == "vector"    # two splits
+    assert qg.qgemv_route("q4k", 8192, 2048, 4) == "vector"     # under 16 MiB
     assert qg.qgemv_route("q4k", 262144, 1536, 3) == "i8mc"
     assert qg.qgemv_route("q6k", 262144, 1536, 8) == "mc32"         # few Q6_K vectors
     assert qg.qgemv_route("q6k", 262144, 1536, 4) == "mc32"

@@ -137,6 +137,7 @@ SHAPES_FEW_Q6K = [
     (4100, 1536, 6),      # three waves, 257 row tiles
     (20000, 2048, 3),     # workgroups walk more than two row tiles
     (20000, 1536, 8),
+    (16384, 2048, 4),     # where qgemv_batch takes this kernel for Q4_K
 ]
 
 CASES = ([(w, *s) for w in ("q80", "q40") for s in SHAPES] + [("q6k", *s) for s in SHAPES_Q6K] +
