@@ -120,8 +120,8 @@ int64_t target_waves(int32_t nvec) { return nvec <= 2 ? 256 * 64 : 256 * 16; }
 // Lanes per row and chunks per lane for a row of `cols` columns (see make_plan). With
 // one_pass set, only geometries that cover the whole row in one pass; with fit_waves, only
 // those whose passes (column chunks) a workgroup can split among its waves; false if there is
-// none. With several_rule (the one-matrix planner), two corrections measured with several
-// vectors apply (explicit plans against the planner's, graph replay, cold, MI355X; the best
+// none. With several_rule (the planners of one and of several matrices), two corrections
+// measured with several vectors apply (explicit plans against the planner's, graph replay, cold, MI355X; the best
 // of the T x NC plans within 3% on average, against 8% before):
 //  * 2 vectors take at most 3 chunks per lane: 4 chunks (64 activation registers) ran
 //    24-50% slower than 1-2 (16384 / 65536 x 2048 x 2: 7.2 / 22.7 us with T 16, NC 4, against
@@ -130,6 +130,8 @@ int64_t target_waves(int32_t nvec) { return nvec <= 2 ? 256 * 64 : 256 * 16; }
 //    of 48 chunks takes one pass of 64 lanes with a quarter idle rather than three of 16
 //    (262144 x 1536 x 8: 92.9 against 125.4 us; x 6: 78.2 against 84.4; 65536 x 1536 x 8:
 //    26.9 against 36.2).
+// In one multi-matrix launch the first gains alike (two 8192 x 2048 Q4_K matrices x 2: 6.02
+// against 6.97 us; three 16384 x 2048: 13.2 against 15.9).
 bool choose_geometry(int64_t cols, int32_t nvec, bool one_pass, int &best_t, int &best_nc,
                      bool fit_waves = false, bool several_rule = false) {
     const int64_t nchunks = cols / 32;
@@ -776,8 +778,8 @@ int run_i8(const void *w, const Activation &act, float *y, int32_t *P, int32_t *
 // column chunks a workgroup can split among its waves (one wave per chunk).
 bool multi_geometry(int64_t cols, int32_t nvec, int &t, int &nc, int &splits) {
     splits = 1;
-    if (choose_geometry(cols, nvec, true, t, nc)) return true;
-    if (!choose_geometry(cols, nvec, false, t, nc, true)) return false;
+    if (choose_geometry(cols, nvec, true, t, nc, false, true)) return true;
+    if (!choose_geometry(cols, nvec, false, t, nc, true, true)) return false;
     splits = splits_for(t, nc, cols);
     return true;
 }

@@ -301,9 +301,9 @@ def test_multi_rejects_bad_arguments():
 
 
 def test_multi_geometry():
-    """One pass over the row, fewest idle lanes, more chunks per lane preferred; a wider row
-    takes the one-matrix planner's geometry (each further pass priced as 2% idle lanes), its
-    chunks split inside the workgroup."""
+    """One pass over the row, fewest idle lanes, more chunks per lane preferred (at most 3 with
+    2 vectors); a wider row takes the one-matrix planner's geometry (each further pass priced
+    as 2% idle lanes, 15% from 5 vectors), its chunks split inside the workgroup."""
     assert qg.qgemv_multi_geometry(1536, 1) == (16, 3)
     assert qg.qgemv_multi_geometry(8192, 1) == (64, 4)
     assert qg.qgemv_multi_geometry(2048, 8) == (64, 1)
@@ -314,7 +314,9 @@ def test_multi_geometry():
     assert qg.qgemv_multi_geometry(4096, 5) == (64, 1)      # 2 passes
     assert qg.qgemv_multi_geometry(16384, 8) == (64, 1)     # 8 passes: 8 waves
     assert qg.qgemv_multi_geometry(14336, 1) == (64, 4)     # not 7 passes of 16 x 4: 4 waves
-    assert qg.qgemv_multi_geometry(14336, 2) == (16, 4)     # 7 passes, 8 waves
+    assert qg.qgemv_multi_geometry(14336, 2) == (32, 2)     # 7 passes, 8 waves (2 vectors:
+    assert qg.qgemv_multi_geometry(2048, 2) == (32, 2)      # at most 3 chunks per lane)
+    assert qg.qgemv_multi_geometry(2048, 1) == (16, 4)
     lib = qg._load()
     t, nc = ctypes.c_int32(), ctypes.c_int32()
     assert lib.qgemv_multi_geometry(65536 + 256, 1, ctypes.byref(t), ctypes.byref(nc)) == EINVAL

@@ -29,14 +29,16 @@ def _say(*a):
 def multi_geometry(cols, nvec):
     """Lanes per row, chunks per lane and column chunks the library uses for a multi-matrix
     launch: the least idle lanes among the geometries that cover a row in one pass, more
-    chunks per lane preferred; for a wider row the least idle lanes with each further pass
-    priced as 2% of them, among the geometries with at most a workgroup's waves of passes
-    (the documented planner rules, restated here for the bit-identity check)."""
+    chunks per lane preferred (at most 3 with 2 vectors); for a wider row the least idle lanes
+    with each further pass priced as 2% of them (15% from 5 vectors), among the geometries with
+    at most a workgroup's waves of passes (the documented planner rules, restated here for the
+    bit-identity check)."""
     nchunks = cols // 32
+    split_cost = 0.15 if nvec >= 5 else 0.02
     for one_pass in (True, False):
         best, best_cost = None, 1e30
         for nc in range(1, 5):
-            if nvec * nc > 8:
+            if nvec * nc > 8 or (nvec == 2 and nc > 3):
                 break
             for t in (8, 16, 32, 64):
                 passes = -(-nchunks // (t * nc))
@@ -44,7 +46,7 @@ def multi_geometry(cols, nvec):
                     continue
                 if passes > (8 if nvec * t * nc >= 128 else 4):
                     continue
-                cost = 1.0 - nchunks / (passes * t * nc) + 0.02 * (passes - 1) - 0.01 * nc
+                cost = 1.0 - nchunks / (passes * t * nc) + split_cost * (passes - 1) - 0.01 * nc
                 if cost < best_cost - 1e-12:
                     best, best_cost = (t, nc, passes), cost
         if best is not None:

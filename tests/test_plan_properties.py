@@ -81,14 +81,16 @@ def test_route_follows_the_documented_rule(shape):
 
 def multi_rule(cols, nvec):
     """Lanes per row and chunks per lane of a multi-matrix launch: the fewest idle lanes among
-    the geometries covering a row in one pass (more chunks per lane preferred); else the
-    one-matrix rule (each further pass priced as 2% of the lanes idle) among the geometries with
-    at most a workgroup's waves of passes (8 when nvec * lanes * chunks >= 128, else 4)."""
+    the geometries covering a row in one pass (more chunks per lane preferred, at most 3 with 2
+    vectors); else the one-matrix rule (each further pass priced as 2% of the lanes idle, 15%
+    from 5 vectors) among the geometries with at most a workgroup's waves of passes (8 when
+    nvec * lanes * chunks >= 128, else 4)."""
     nchunks = cols // 32
+    split_cost = 0.15 if nvec >= 5 else 0.02
     for one_pass in (True, False):
         best, best_cost = None, 1e30
         for nc in range(1, 5):
-            if nvec * nc > 8:
+            if nvec * nc > 8 or (nvec == 2 and nc > 3):
                 break
             for t in (8, 16, 32, 64):
                 passes = -(-nchunks // (t * nc))
@@ -96,7 +98,7 @@ def multi_rule(cols, nvec):
                     continue
                 if passes > (8 if nvec * t * nc >= 128 else 4):
                     continue
-                cost = 1.0 - nchunks / (passes * t * nc) + 0.02 * (passes - 1) - 0.01 * nc
+                cost = 1.0 - nchunks / (passes * t * nc) + split_cost * (passes - 1) - 0.01 * nc
                 if cost < best_cost - 1e-12:
                     best, best_cost = (t, nc), cost
         if best is not None:
