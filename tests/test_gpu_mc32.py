@@ -175,6 +175,32 @@ def test_integer_extremes():
     _check("q6k", t6, rows, cols, np.full((nvec, cols), -3.0, np.float32))
 
 
+def _random_few_cases(n=24, seed=20261202):
+    """Seeded random shapes for the few-vector kernel: every format, 1..8 vectors, rows 1..3000,
+    widths from one block to a few splits (whole super-blocks for Q4_K and Q6_K)."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for k in range(n):
+        wtype = ("q80", "q40", "q6k", "q4k")[k % 4]
+        unit = 256 if wtype in ("q4k", "q6k") else 32
+        cols = unit * int(rng.integers(1, 9000 // unit + 1))
+        rows = int(rng.integers(1, 3001))
+        nvec = int(rng.integers(1, 9))
+        cases.append((wtype, rows, cols, nvec))
+    return cases
+
+
+@pytest.mark.parametrize("wtype,rows,cols,nvec", _random_few_cases())
+def test_few_vectors_random_shapes(wtype, rows, cols, nvec):
+    """The few-vector kernel itself (qgemv_batch_mc32 / qgemv_debug_partials_mc32) on seeded
+    random shapes: P and S bit-exact, y within the bound."""
+    _say("random", wtype, rows, cols, nvec)
+    rng = np.random.default_rng(rows * 13 + cols * 7 + nvec)
+    w = (rng.standard_normal((rows, cols)) * rng.choice([0.002, 0.02, 0.5])).astype(np.float32)
+    x = (rng.standard_normal((nvec, cols)) * rng.choice([1e-3, 1.0, 40.0], size=(nvec, 1))).astype(np.float32)
+    _check(wtype, oracle.quantize(wtype, w), rows, cols, x)
+
+
 def test_fused_with_code_outputs_takes_the_matrix_cores():
     """qgemv_fused with code outputs on a shape qgemv_batch runs on the few-vector matrix-core
     kernel: two launches, the oracle's codes and scales, and qgemv_batch's y bit for bit."""
