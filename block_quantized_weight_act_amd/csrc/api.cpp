@@ -361,10 +361,14 @@ int check_gemv_args_n(int wtype, const void *w, const int8_t *xq, const float *x
     return QGEMV_OK;
 }
 
+bool q32i8_many(int wtype, int64_t rows, int64_t cols, int32_t nvec);
+
+// (Q4_K products with 9..16 vectors that the few-vector kernel takes are not this path's.)
 bool mc_shape_ok(int wtype, int64_t rows, int64_t cols, int32_t nvec) {
     return wtype == QGEMV_Q4K && nvec > kMaxVec && nvec <= kMaxBatch && rows >= 1 &&
            rows <= (int64_t{1} << 30) && cols >= kQK && cols % kQK == 0 &&
-           cols <= (int64_t{1} << 30) && rows * (cols / 32) < (int64_t{1} << 31);
+           cols <= (int64_t{1} << 30) && rows * (cols / 32) < (int64_t{1} << 31) &&
+           !q32i8_many(wtype, rows, cols, nvec);
 }
 
 McPlan make_mc_plan(int64_t rows, int64_t cols, int32_t nvec) {
@@ -516,18 +520,56 @@ bool q32i8_auto(int wtype, int64_t rows, int64_t cols, int32_t nvec) {
     }
 }
 
+// Whether 9..16 vectors run on the few-vector kernel (gemm_q32_i8.hip, 3 or 4 halves of 4
+// vectors) rather than the 32 x 32 x 32 kernels, the vector kernel on groups of 8, or (Q4_K) the
+// Q4_K integer kernel. Measured on MI355X (graph replay, cold; this kernel against what was
+// taken before, us):
+//   Q4_0 262144 x 1536 x 12 / 16: 52.2 / 81.1, 63.0 / 83.6; 65536 x 2048 x 12: 20.7 / 37.4;
+//        16384 x 2048 x 12: 7.85 / 15.2 (groups of 8); 2048 x 8192 x 10: 9.42 / 10.8;
+//   Q6_K 262144 x 1536 x 12: 86.2 / 99.8; 65536 x 2048 x 12: 30.2 / 42.0; 16384 x 2048 x 12:
+//        11.5 / 19.6; 4096 x 4096 x 10: 11.4 / 11.5;
+//   Q8_0 262144 x 1536 x 16: 90.9 / 107.2; 65536 x 2048 x 10 / 12 / 16: 35.8 / 33.4,
+//        36.0 / 33.8, 32.9 / 34.4; 16384 x 2048 x 12: 11.4 / 18.9;
+//   Q4_K 65536 x 2048 x 10 / 12 / 16: 23.9 / 25.2, 24.7 / 25.5, 31.0 / 26.3; 16384 x 2048 x
+//        12: 9.11 / 10.0; 262144 x 1536 x 12: 62.9 / 61.0.
+// Smaller tensors than 16 Mi weights were not measured and keep the earlier routes.
+bool q32i8_many(int wtype, int64_t rows, int64_t cols, int32_t nvec) {
+    if (nvec <= kMaxVec || nvec > kQ32I8MaxVec) return false;
+    constexpr int64_t Mi = int64_t{1} << 20;
+    const int64_t weights = rows * cols;
+    if (weights < 16 * Mi) return false;
+    switch (wtype) {
+        case QGEMV_Q4_0:
+        case QGEMV_Q6K: return true;
+        case QGEMV_Q8_0: return nvec >= 16 || weights < 48 * Mi || weights >= 256 * Mi;
+        case QGEMV_Q4K:
+            return nvec <= 12 && static_cast<int64_t>(weight_bytes(wtype, rows, cols)) <
+                                     (int64_t{128} << 20);
+        default: return false;
+    }
+}
+
 bool mc32_auto(int wtype, int64_t rows, int64_t cols, int32_t nvec) {
     if (!mc32_ok(wtype, rows, cols, nvec)) return false;
     const int64_t weights = rows * cols;
     constexpr int64_t Mi = int64_t{1} << 20;
-    if (nvec <= kQ32I8MaxVec) return q32i8_auto(wtype, rows, cols, nvec);
+    if (nvec <= kMaxVec) return q32i8_auto(wtype, rows, cols, nvec);
+    if (q32i8_many(wtype, rows, cols, nvec)) return true;
+    if (wtype == QGEMV_Q4K) return false;
     return nvec >= 32 || (nvec >= 16 && weights >= 24 * Mi) || weights >= 48 * Mi;
 }
 
+// Which kernel run_mc32 takes: the few-vector kernel for 1..8 vectors, for Q4_K, and for 9..16
+// where q32i8_many says so; else the 32 x 32 x 32 kernels.
+bool mc32_few_kernel(int wtype, int64_t rows, int64_t cols, int32_t nvec) {
+    return nvec <= kMaxVec || wtype == QGEMV_Q4K || q32i8_many(wtype, rows, cols, nvec);
+}
+
 // More than kMaxVec vectors where the matrix-core path is not taken: the vector kernel on
-// groups of up to kMaxVec vectors, one after another on the stream.
+// groups of up to kMaxVec vectors, one after another on the stream (not Q4_K, whose 9..16
+// vectors take its integer kernel).
 bool grouped_shape_ok(int wtype, int64_t rows, int64_t cols, int32_t nvec) {
-    return nvec > kMaxVec && mc32_ok(wtype, rows, cols, nvec) &&
+    return wtype != QGEMV_Q4K && nvec > kMaxVec && mc32_ok(wtype, rows, cols, nvec) &&
            !mc32_auto(wtype, rows, cols, nvec);
 }
 
@@ -573,9 +615,10 @@ Mc32Plan make_mc32_plan(int64_t rows, int64_t cols, int32_t nvec) {
 }
 
 // The workspace of run_mc32 for a shape mc32_ok accepts: partial sums of column splits.
-size_t mc32_route_ws_bytes(int64_t rows, int64_t cols, int32_t nvec) {
-    const int splits = nvec <= kQ32I8MaxVec ? make_q32i8_plan(rows, cols).splits
-                                            : make_mc32_plan(rows, cols, nvec).splits;
+size_t mc32_route_ws_bytes(int wtype, int64_t rows, int64_t cols, int32_t nvec) {
+    const int splits = mc32_few_kernel(wtype, rows, cols, nvec)
+                           ? make_q32i8_plan(rows, cols).splits
+                           : make_mc32_plan(rows, cols, nvec).splits;
     return splits > 1 ? static_cast<size_t>(splits) * nvec * rows * sizeof(float) : 0;
 }
 
@@ -602,7 +645,7 @@ int run_mc32(int wtype, const void *w, const int8_t *xq, const float *xd, float 
             overlaps(S, sbytes, xq, qb) || overlaps(S, sbytes, xd, db))
             return QGEMV_EINVAL;
     }
-    const size_t need = debug ? 0 : mc32_route_ws_bytes(rows, cols, nvec);
+    const size_t need = debug ? 0 : mc32_route_ws_bytes(wtype, rows, cols, nvec);
     if (need > 0) {
         if (!ws || ws_bytes < need) return QGEMV_EWORKSPACE;
         if (!aligned(ws, 4)) return QGEMV_EALIGN;
@@ -621,7 +664,7 @@ int run_mc32(int wtype, const void *w, const int8_t *xq, const float *xd, float 
     a.nb = static_cast<int32_t>(cols / 32);
     a.nvec = nvec;
     hipError_t e;
-    if (nvec <= kQ32I8MaxVec) {
+    if (mc32_few_kernel(wtype, rows, cols, nvec)) {
         const Q32I8Plan p = make_q32i8_plan(rows, cols);
         a.sb_per_split = p.bps;
         a.row_tiles = p.row_tiles;
@@ -678,7 +721,8 @@ bool i8_ok(int64_t rows, int64_t cols, int32_t nvec) {
 
 bool i8_auto(int wtype, int64_t rows, int64_t cols, int32_t nvec) {
     return wtype == QGEMV_Q4K && i8_ok(rows, cols, nvec) &&
-           static_cast<int64_t>(weight_bytes(QGEMV_Q4K, rows, cols)) >= i8_min_bytes(nvec);
+           static_cast<int64_t>(weight_bytes(QGEMV_Q4K, rows, cols)) >= i8_min_bytes(nvec) &&
+           !q32i8_many(wtype, rows, cols, nvec);
 }
 
 struct I8Plan {
@@ -967,7 +1011,7 @@ int qgemv_quantize_act(const float *x, int8_t *xq, float *xd, int64_t cols, int3
 
 size_t qgemv_workspace_bytes(int wtype, int64_t rows, int64_t cols, int32_t nvec) {
     if (i8_auto(wtype, rows, cols, nvec)) return i8_ws_bytes(make_i8_plan(rows, cols), rows, nvec);
-    if (mc32_auto(wtype, rows, cols, nvec)) return mc32_route_ws_bytes(rows, cols, nvec);
+    if (mc32_auto(wtype, rows, cols, nvec)) return mc32_route_ws_bytes(wtype, rows, cols, nvec);
     if (mc_shape_ok(wtype, rows, cols, nvec))
         return mc_ws_bytes(make_mc_plan(rows, cols, nvec), rows, cols, nvec);
     if (grouped_shape_ok(wtype, rows, cols, nvec)) {
@@ -1247,7 +1291,7 @@ int qgemv_batch_i8mc(const void *w, const int8_t *xq, const float *xd, float *y,
 
 size_t qgemv_mc32_workspace_bytes(int wtype, int64_t rows, int64_t cols, int32_t nvec) {
     if (!mc32_ok(wtype, rows, cols, nvec)) return 0;
-    return mc32_route_ws_bytes(rows, cols, nvec);
+    return mc32_route_ws_bytes(wtype, rows, cols, nvec);
 }
 
 int qgemv_batch_mc32(int wtype, const void *w, const int8_t *xq, const float *xd, float *y,

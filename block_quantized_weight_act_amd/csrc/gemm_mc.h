@@ -33,7 +33,7 @@ hipError_t launch_gemm_q32_mc(int wtype, const GemmArgs &a, int vt, bool debug,
 // instead.
 constexpr int kQ32I8BlocksPerWave = 16;
 constexpr int kQ32I8MaxWaves = 4;
-constexpr int kQ32I8MaxVec = 8;
+constexpr int kQ32I8MaxVec = 16;
 hipError_t launch_gemm_q32_i8(int wtype, const GemmArgs &a, int waves, bool debug,
                               hipStream_t stream);
 hipError_t launch_gemm_q6k_mc(const GemmArgs &a, int vt, bool debug, hipStream_t stream);

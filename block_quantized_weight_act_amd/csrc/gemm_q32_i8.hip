@@ -72,7 +72,10 @@ __global__ void __launch_bounds__(256) gemm_q32_i8_kernel(GemmArgs a) {
     // resident waves than it gains (262144 x 1536 x 8: Q6_K 72.4 against 113.1 us, Q4_0 44.1
     // against 54.5 us); with 1..4 vectors, and for Q8_0, it gains (Q6_K x 4: 66.3 against 74.0,
     // Q8_0 x 8: 84.2 against 91.3 us).
-    constexpr bool SINGLE = H == 2 && FMT != kTypeQ80;
+    constexpr bool SINGLE = (H == 2 && FMT != kTypeQ80) || H >= 3;
+    // With up to 8 vectors the activation scales (and Q4_0's -8 S) of the lane's outputs stay in
+    // registers for the whole kernel; with more they are read from LDS per product.
+    constexpr bool KEEP = H <= 2;
     extern __shared__ __attribute__((aligned(16))) uint8_t lds_q32i8[];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -210,8 +213,8 @@ __global__ void __launch_bounds__(256) gemm_q32_i8_kernel(GemmArgs a) {
 #pragma unroll
     for (int h = 0; h < H; h++)
         abase[h] = xq_s + (live ? 4 * h + (r & 3) : NV) * pitch + (wb0 + g) * 32;
-    v4f_t xdk[4][H];
-    v4i_t c8k[4][H];
+    v4f_t xdk[4][KEEP ? H : 1];
+    v4i_t c8k[4][KEEP ? H : 1];
     float mink[4][H];   // Q4_K: the min-term product's row operand (slot r < 4: -xd S of vector
                         // 4 h + r, block wb0 + 4 i + g; 0 in the other slots)
 #pragma unroll
@@ -219,14 +222,26 @@ __global__ void __launch_bounds__(256) gemm_q32_i8_kernel(GemmArgs a) {
 #pragma unroll
         for (int h = 0; h < H; h++) {
             const int o = (wb0 + 4 * i + g) * NV + 4 * h;
-            xdk[i][h] = Q6 ? v4f_t{0.0f, 0.0f, 0.0f, 0.0f} : *reinterpret_cast<const v4f_t *>(xd_s + o);
-            c8k[i][h] = Q40 ? *reinterpret_cast<const v4i_t *>(s8_s + o) : v4i_t{0, 0, 0, 0};
+            if constexpr (KEEP) {
+                xdk[i][h] = Q6 ? v4f_t{0.0f, 0.0f, 0.0f, 0.0f} : *reinterpret_cast<const v4f_t *>(xd_s + o);
+                c8k[i][h] = Q40 ? *reinterpret_cast<const v4i_t *>(s8_s + o) : v4i_t{0, 0, 0, 0};
+            }
             mink[i][h] = QK && r < 4
                              ? reinterpret_cast<const float *>(s8_s)[(wb0 + 4 * i + g) * NV + 4 * h + r]
                              : 0.0f;
             // (Q6_K reads its activation scales per product instead: its weight operands take
             // more registers)
         }
+
+    auto xd_of = [&](int i, int h) -> v4f_t {
+        if constexpr (KEEP) return xdk[i][h];
+        else return *reinterpret_cast<const v4f_t *>(xd_s + (wb0 + 4 * i + g) * NV + 4 * h);
+    };
+    auto c8_of = [&](int i, int h) -> v4i_t {
+        if constexpr (KEEP) return c8k[i][h];
+        else if constexpr (Q40) return *reinterpret_cast<const v4i_t *>(s8_s + (wb0 + 4 * i + g) * NV + 4 * h);
+        else return v4i_t{0, 0, 0, 0};
+    };
 
     float *out = DBG ? nullptr : a.out + static_cast<int64_t>(blockIdx.y) * nvec * rows;
     int slot = 0;
@@ -259,12 +274,14 @@ __global__ void __launch_bounds__(256) gemm_q32_i8_kernel(GemmArgs a) {
                                        static_cast<int>((c.z >> 4) & 0x0F0F0F0Fu),
                                        static_cast<int>((c.w >> 4) & 0x0F0F0F0Fu)};
                 v4i_t P[H];
+                v4f_t X[H];
 #pragma unroll
                 for (int h = 0; h < H; h++) {
                     const v4i_t A0 = *reinterpret_cast<const v4i_t *>(abase[h] + 128 * i);
                     const v4i_t A1 = *reinterpret_cast<const v4i_t *>(abase[h] + 128 * i + 16);
                     P[h] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A0, B0, zero, 0, 0, 0);
                     P[h] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A1, B1, P[h], 0, 0, 0);
+                    X[h] = xd_of(i, h);
                 }
                 // sub-scale and min of block bs = 4 (i % 2) + g of super-block i / 2: low 4 bits
                 // at bit 4 bs of the second (scales) and third (mins) words, high 2 bits at bit
@@ -280,7 +297,7 @@ __global__ void __launch_bounds__(256) gemm_q32_i8_kernel(GemmArgs a) {
                 for (int h = 0; h < H; h++) {
 #pragma unroll
                     for (int e = 0; e < 4; e++)     // sc * P exact: below 2^22
-                        acc[h][e] = fmaf(xdk[i][h][e] * d, static_cast<float>(__mul24(sc, P[h][e])),
+                        acc[h][e] = fmaf(X[h][e] * d, static_cast<float>(__mul24(sc, P[h][e])),
                                          acc[h][e]);
                     acc[h] = __builtin_amdgcn_mfma_f32_16x16x4f32(mink[i][h], dm, acc[h], 0, 0, 0);
                     if (DBG) {
@@ -377,11 +394,11 @@ __global__ void __launch_bounds__(256) gemm_q32_i8_kernel(GemmArgs a) {
                     m[2] = half_to_float(t.d[1] & 0xFFFFu);
                     m[3] = half_to_float(t.d[1] >> 16);
                 } else {
-    #pragma unroll
+#pragma unroll
                     for (int j = 0; j < 4; j++) m[j] = __builtin_bit_cast(float, t.d[j]);
                 }
                 uint32_t x[4];
-    #pragma unroll
+#pragma unroll
                 for (int j = 0; j < 2; j++) {
                     const auto sw = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, m[j]),
                                                                      __builtin_bit_cast(uint32_t, m[j + 2]),
@@ -389,7 +406,7 @@ __global__ void __launch_bounds__(256) gemm_q32_i8_kernel(GemmArgs a) {
                     x[j] = sw[0];
                     x[j + 2] = sw[1];
                 }
-    #pragma unroll
+#pragma unroll
                 for (int j = 0; j < 2; j++) {
                     const auto sw = __builtin_amdgcn_permlane16_swap(x[2 * j], x[2 * j + 1], false, false);
                     const uint32_t lo = sw[0], hi = sw[1];
@@ -397,11 +414,11 @@ __global__ void __launch_bounds__(256) gemm_q32_i8_kernel(GemmArgs a) {
                     dl[2 * j + 1] = __builtin_bit_cast(float, hi);
                 }
             } else {
-    #pragma unroll
+#pragma unroll
                 for (int i = 0; i < 4; i++)
                     dl[i] = Q40 ? half_to_float(t.d[i]) : __builtin_bit_cast(float, t.d[i]);
             }
-    #pragma unroll
+#pragma unroll
             for (int i = 0; i < 4; i++) {
                 v4i_t B0, B1;
                 if constexpr (Q40) {
@@ -417,25 +434,27 @@ __global__ void __launch_bounds__(256) gemm_q32_i8_kernel(GemmArgs a) {
                     B1 = __builtin_bit_cast(v4i_t, t.c[i][1]);
                 }
                 v4i_t P[H];
-    #pragma unroll
+                v4f_t X[H];
+#pragma unroll
                 for (int h = 0; h < H; h++) {
                     const v4i_t A0 = *reinterpret_cast<const v4i_t *>(abase[h] + 128 * i);
                     const v4i_t A1 = *reinterpret_cast<const v4i_t *>(abase[h] + 128 * i + 16);
-                    P[h] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A0, B0, c8k[i][h], 0, 0, 0);
+                    P[h] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A0, B0, c8_of(i, h), 0, 0, 0);
                     P[h] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A1, B1, P[h], 0, 0, 0);
+                    X[h] = xd_of(i, h);
                 }
                 // blocks past the split: P is 0 there, and so is d (whatever the loaded bits)
                 const bool bv = wb0 + 4 * i + g < nsb;
                 const float d = bv ? dl[i] : 0.0f;
-    #pragma unroll
+#pragma unroll
                 for (int h = 0; h < H; h++) {
-    #pragma unroll
+#pragma unroll
                     for (int e = 0; e < 4; e++)
-                        acc[h][e] = fmaf(xdk[i][h][e] * d, static_cast<float>(P[h][e]), acc[h][e]);
+                        acc[h][e] = fmaf(X[h][e] * d, static_cast<float>(P[h][e]), acc[h][e]);
                     if (DBG) {
                         const int64_t row = int64_t{tile} * 16 + r;
                         const int blk = b_lo + wb0 + 4 * i + g;
-    #pragma unroll
+#pragma unroll
                         for (int e = 0; e < 4; e++) {
                             const int v = 4 * h + e;
                             if (v < nvec && row < rows && bv)
@@ -602,16 +621,26 @@ hipError_t launch_fh(const GemmArgs &a, int waves, bool debug, hipStream_t strea
 template <int FMT>
 hipError_t launch_f(const GemmArgs &a, int waves, bool debug, hipStream_t stream) {
     // (Q6_K's super-block scales have loads of their own)
+    const int h = (a.nvec + 3) / 4;     // halves of 4 vectors
     if constexpr (FMT == kTypeQ6K || FMT == kTypeQ4K) {
-        return a.nvec <= 4 ? launch_fh<FMT, 1, false>(a, waves, debug, stream)
-                           : launch_fh<FMT, 2, false>(a, waves, debug, stream);
+        switch (h) {
+            case 1: return launch_fh<FMT, 1, false>(a, waves, debug, stream);
+            case 2: return launch_fh<FMT, 2, false>(a, waves, debug, stream);
+            case 3: return launch_fh<FMT, 3, false>(a, waves, debug, stream);
+            default: return launch_fh<FMT, 4, false>(a, waves, debug, stream);
+        }
     } else {
         const bool vs = a.nb % 4 == 0;
-        if (a.nvec <= 4)
-            return vs ? launch_fh<FMT, 1, true>(a, waves, debug, stream)
-                      : launch_fh<FMT, 1, false>(a, waves, debug, stream);
-        return vs ? launch_fh<FMT, 2, true>(a, waves, debug, stream)
-                  : launch_fh<FMT, 2, false>(a, waves, debug, stream);
+        switch (h) {
+            case 1: return vs ? launch_fh<FMT, 1, true>(a, waves, debug, stream)
+                              : launch_fh<FMT, 1, false>(a, waves, debug, stream);
+            case 2: return vs ? launch_fh<FMT, 2, true>(a, waves, debug, stream)
+                              : launch_fh<FMT, 2, false>(a, waves, debug, stream);
+            case 3: return vs ? launch_fh<FMT, 3, true>(a, waves, debug, stream)
+                              : launch_fh<FMT, 3, false>(a, waves, debug, stream);
+            default: return vs ? launch_fh<FMT, 4, true>(a, waves, debug, stream)
+                               : launch_fh<FMT, 4, false>(a, waves, debug, stream);
+        }
     }
 }
 

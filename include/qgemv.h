@@ -231,11 +231,14 @@ int qgemv_batch_scratch(int wtype, const void *w, const int8_t *xq, const float 
  * shape: the vector kernels, the integer matrix cores (qgemv_batch_i8mc), the
  * float matrix cores for 17..QGEMV_MAX_BATCH Q4_K vectors, the integer matrix
  * cores for 9..QGEMV_MAX_BATCH Q8_0, Q4_0 or Q6_K vectors (qgemv_batch_mc32;
- * QGEMV_ROUTE_MC32) from 32 vectors, from 16 vectors on tensors of at least
- * 24 Mi weights and from 9 vectors on at least 48 Mi weights, or else for those
- * formats the vector kernels on groups of 8 vectors (QGEMV_ROUTE_GROUPED: on a
- * small tensor they stay ahead of the matrix-core path's 16-20 us floor until
- * the groups are many); with 1..8 vectors the integer matrix cores
+ * QGEMV_ROUTE_MC32) with 9..16 vectors on tensors of at least 16 Mi weights, from
+ * 32 vectors, from 16 vectors on tensors of at least 24 Mi weights and from 9
+ * vectors on at least 48 Mi weights, or else for those formats the vector
+ * kernels on groups of 8 vectors (QGEMV_ROUTE_GROUPED: on a small tensor they
+ * stay ahead of the matrix-core path's 16-20 us floor until the groups are
+ * many); Q4_K with 9..12 vectors on tensors of 16 Mi weights to 128 MiB there
+ * too (QGEMV_ROUTE_MC32), else with 9..16 on its own integer kernel
+ * (QGEMV_ROUTE_I8MC); with 1..8 vectors the integer matrix cores
  * (QGEMV_ROUTE_MC32) where the vector kernel's dot products bind, on rows of up
  * to 2048 columns: Q4_0 from 4 vectors on tensors of at least 32 Mi weights (3
  * from 256 Mi; 8 on wider rows), Q6_K from 4 vectors on 256 Mi weights and with
@@ -253,13 +256,15 @@ int qgemv_route(int wtype, int64_t rows, int64_t cols, int32_t nvec);
 
 /*
  * Q8_0, Q4_0 or Q6_K with 1 <= nvec <= QGEMV_MAX_BATCH, and Q4_K with
- * 1 <= nvec <= 8, on the integer matrix cores, for any shape (qgemv_batch takes it
+ * 1 <= nvec <= 16, on the integer matrix cores, for any shape (qgemv_batch takes it
  * where QGEMV_ROUTE_MC32 says; oxinfer README, "Speculative decoding": the
- * multi-token int8 variants). With 9 or more vectors one product is 32 weight rows
- * x 32 vectors over one 32-weight block (Q8_0: the stored codes; Q4_0: the codes
- * 0..15, then P = sum q * xq - 8 S in integer) or over one 16-weight Q6_K
- * sub-block (the operand q - 32); with 1..8 vectors one product is 16 weight rows
- * x 4 blocks x 4 vectors over one 16-weight half of each block
+ * multi-token int8 variants). With 17 or more vectors, and with 9..16 on tensors
+ * of fewer than 16 Mi weights (and Q8_0 with 9..15 vectors on 48 to 256 Mi), one
+ * product is 32 weight rows x 32 vectors over one 32-weight block (Q8_0: the
+ * stored codes; Q4_0: the codes 0..15, then P = sum q * xq - 8 S in integer) or
+ * over one 16-weight Q6_K sub-block (the operand q - 32); otherwise (1..16
+ * vectors) one product is 16 weight rows x 4 blocks x 4 vectors over one
+ * 16-weight half of each block
  * (v_mfma_i32_16x16x64_i8; for Q8_0, Q4_0 and Q4_K two accumulate into a block's
  * P, Q4_0's starting from -8 S; for Q6_K each half is a sub-block, the operand
  * q - 32). Either way the int32 result is the exact integer partial P of
@@ -268,10 +273,10 @@ int qgemv_route(int wtype, int64_t rows, int64_t cols, int32_t nvec);
  * combination exact, times d per half super-block; Q4_K: d * xd * (sc * P) and
  * the min term -dmin * m * xd * S) in float32, within the same
  * bound as the vector kernels' y. Arguments as for qgemv_batch; the workspace
- * (qgemv_mc32_workspace_bytes: partial sums when the columns are split, with 9 or
- * more vectors because row tiles and vector groups give fewer than 512
- * workgroups, with 1..8 vectors for rows wider than 2048 columns) may be NULL
- * when that is 0.
+ * (qgemv_mc32_workspace_bytes: partial sums when the columns are split: by the
+ * 32 x 32 x 32 kernels because row tiles and vector groups give fewer than 512
+ * workgroups, by the 16 x 16 x 64 kernel for rows wider than 2048 columns) may
+ * be NULL when that is 0.
  */
 size_t qgemv_mc32_workspace_bytes(int wtype, int64_t rows, int64_t cols, int32_t nvec);
 int qgemv_batch_mc32(int wtype, const void *w, const int8_t *xq, const float *xd, float *y,

@@ -108,7 +108,9 @@ def test_routes():
     assert qg.qgemv_route("q6k", 65536, 2048, 7) == "vector"
     assert qg.qgemv_route("q6k", 16384, 4096, 8) == "vector"
     assert qg.qgemv_route("q4k", 16384, 2048, 64) == "mc"
-    assert qg.qgemv_route("q4k", 16384, 2048, 12) == "i8mc"         # 9..16 vectors: always
+    assert qg.qgemv_route("q4k", 16384, 2048, 12) == "mc32"         # 9..12 on < 128 MiB: the
+    assert qg.qgemv_route("q4k", 16384, 2048, 13) == "i8mc"         # few-vector kernel; else
+    assert qg.qgemv_route("q4k", 262144, 1536, 12) == "i8mc"        # the Q4_K integer kernel
     assert qg.qgemv_route("q4k", 512, 512, 16) == "i8mc"
     assert qg.qgemv_route("q4k", 512, 512, 17) == "mc"
     assert qg.qgemv_route("q40", 16384, 2048, 64) == "mc32"
@@ -127,13 +129,16 @@ def test_routes():
     assert qg.qgemv_route("q6k", 16384, 2048, 64) == "mc32"
     # Q8_0, Q4_0, Q6_K: the matrix cores from 32 vectors, from 16 on >= 24 Mi weights, from 9
     # on >= 48 Mi weights; groups of 8 on the vector kernel below
-    assert qg.qgemv_route("q80", 2048, 8192, 9) == "grouped"
+    assert qg.qgemv_route("q80", 2048, 8192, 9) == "mc32"           # 9..16: from 16 Mi weights
+    assert qg.qgemv_route("q80", 2048, 4096, 9) == "grouped"
     assert qg.qgemv_route("q80", 2048, 8192, 24) == "grouped"
     assert qg.qgemv_route("q80", 2048, 8192, 32) == "mc32"
-    assert qg.qgemv_route("q6k", 16384, 2048, 9) == "grouped"
+    assert qg.qgemv_route("q6k", 16384, 2048, 9) == "mc32"
+    assert qg.qgemv_route("q80", 65536, 2048, 12) == "mc32"         # (the 32 x 32 x 32 kernel)
     assert qg.qgemv_route("q6k", 16384, 2048, 16) == "mc32"
     assert qg.qgemv_route("q40", 65536, 1536, 9) == "mc32"
-    assert qg.qgemv_route("q40", 16384, 1536, 15) == "grouped"
+    assert qg.qgemv_route("q40", 16384, 1536, 15) == "mc32"
+    assert qg.qgemv_route("q40", 4096, 1536, 15) == "grouped"
     assert qg._load().qgemv_route(1, 8, 500, 1) == 0
     assert qg._load().qgemv_route(1, 8, 512, 300) == 0
 
@@ -379,7 +384,8 @@ def test_mc32_workspace_and_limits():
     # and Q4_0 with 1..8 (splits of up to 64 blocks of 32 columns)
     X, D, Y = A + (1 << 30), A + (2 << 30), A + (3 << 30)
     mc = lib.qgemv_batch_mc32
-    assert qg.qgemv_mc32_workspace_bytes("q80", 2048, 8192, 9) == 32 * 9 * 2048 * 4
+    assert qg.qgemv_mc32_workspace_bytes("q80", 2048, 8192, 9) == 4 * 9 * 2048 * 4   # 16-vector kernel
+    assert qg.qgemv_mc32_workspace_bytes("q80", 2048, 4096, 9) == 16 * 9 * 2048 * 4  # 32 x 32 x 32
     assert qg.qgemv_mc32_workspace_bytes("q80", 2048, 8192, 8) == 4 * 8 * 2048 * 4
     assert qg.qgemv_mc32_workspace_bytes("q40", 2048, 2048, 8) == 0
     assert qg.qgemv_mc32_workspace_bytes("q40", 2048, 8224, 3) == 5 * 3 * 2048 * 4

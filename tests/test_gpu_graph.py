@@ -191,7 +191,7 @@ def test_graph_replays_match_direct_calls_and_oracle():
     graph.close()
 
 
-MC_CASES = [("q4k", 16384, 2048, 8, "i8mc"), ("q4k", 16384, 2048, 12, "i8mc"),
+MC_CASES = [("q4k", 16384, 2048, 8, "i8mc"), ("q4k", 16384, 2048, 14, "i8mc"),
             ("q4k", 4096, 1536, 40, "mc"), ("q80", 16384, 2048, 16, "mc32"),
             ("q6k", 16384, 2048, 32, "mc32"),
             # the few-vector kernel: Q4_0 with two column splits and the ordered reduce, Q4_K
@@ -201,7 +201,7 @@ MC_CASES = [("q4k", 16384, 2048, 8, "i8mc"), ("q4k", 16384, 2048, 12, "i8mc"),
 
 def test_graph_replays_the_matrix_core_routes():
     """The routes qgemv_batch takes for several vectors (the integer matrix cores for Q4_K with
-    8 and 12 vectors, the fp16 matrix cores with their staging pre-pass for 40, the 32-weight and
+    8 and 14 vectors, the fp16 matrix cores with their staging pre-pass for 40, the 32-weight and
     Q6_K integer kernels with their splits and ordered reduce, the few-vector kernel for Q4_0 and
     Q4_K) recorded with the activation
     quantization into one graph: every replay, with new inputs and direct work between, gives

@@ -56,7 +56,7 @@ def _check(wtype, wbuf, rows, cols, x, debug=True):
     # qgemv_batch: the same kernel (bit for bit) where it routes there, else the vector kernel
     # (on groups of 8 with more than 8 vectors), within the same bound
     route = qg.qgemv_route(wtype, rows, cols, nvec)
-    assert route in (("mc32", "vector", "i8mc") if nvec <= 8 else ("mc32", "grouped"))
+    assert route in (("mc32", "vector", "i8mc") if nvec <= 8 else ("mc32", "grouped", "i8mc"))
     yb = gu.gemv(wtype, wt, xq, xd, rows, cols, nvec)
     if route == "mc32":
         assert np.array_equal(yb.view(np.uint32), y.view(np.uint32))
@@ -140,7 +140,18 @@ SHAPES_FEW_Q6K = [
     (16384, 2048, 4),     # where qgemv_batch takes this kernel for Q4_K
 ]
 
+SHAPES_MID = [
+    # (rows, cols, nvec): 9..16 vectors on tensors of at least 16 Mi weights, where the
+    # few-vector kernel takes 3 or 4 halves of 4 vectors (Q4_K: 9..12)
+    (8192, 2048, 12),     # one split of four waves, three halves
+    (4096, 4096, 16),     # two splits, four halves
+    (2048, 8192, 10),     # four splits, three halves (two vectors idle)
+    (16384, 1280, 9),     # 40 blocks: three waves, the last with one super-block
+]
+
 CASES = ([(w, *s) for w in ("q80", "q40") for s in SHAPES] + [("q6k", *s) for s in SHAPES_Q6K] +
+         [(w, *s) for w in ("q80", "q40", "q6k", "q4k") for s in SHAPES_MID
+          if not (w == "q4k" and s[2] > 12)] +
          [(w, *s) for w in ("q80", "q40") for s in SHAPES_FEW] +
          [(w, *s) for w in ("q6k", "q4k") for s in SHAPES_FEW_Q6K])
 

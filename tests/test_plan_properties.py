@@ -59,6 +59,34 @@ def test_plan_invariants_and_workspace(shape):
     assert qg.qgemv_fused_launches(wtype, rows, cols, nvec, False) == 1
 
 
+def few_kernel_rule(wtype, rows, cols, nvec):
+    """Where qgemv_batch takes the few-vector integer matrix-core kernel (QGEMV_ROUTE_MC32 with
+    up to 16 vectors), as include/qgemv.h documents it: rows of up to 2048 columns (one split)
+    unless noted; with 1..8 vectors Q4_0 from 4 vectors on >= 32 Mi weights (3 from 256 Mi; 8
+    on wider rows), Q6_K from 4 vectors on 256 Mi weights and with 8 from 64 Mi, Q8_0 with 8
+    from 256 Mi, Q4_K with 4 on tensors of 16 to 96 MiB; with 9..16 vectors (any width) from
+    16 Mi weights, Q8_0 with 9..15 vectors not on 48 to 256 Mi, Q4_K only with 9..12 vectors
+    below 128 MiB."""
+    weights = rows * cols
+    wb = weight_bytes(wtype, rows, cols)
+    one = cols <= 2048
+    if nvec <= 8:
+        if wtype == "q40":
+            return weights >= 32 * MI and nvec >= (8 if not one else (3 if weights >= 256 * MI else 4))
+        if wtype == "q6k":
+            return one and ((weights >= 256 * MI and nvec >= 4) or (weights >= 64 * MI and nvec >= 8))
+        if wtype == "q80":
+            return one and weights >= 256 * MI and nvec >= 8
+        return one and nvec == 4 and 16 * MI <= wb < 96 * MI
+    if nvec > 16 or weights < 16 * MI:
+        return False
+    if wtype == "q80":
+        return nvec >= 16 or weights < 48 * MI or weights >= 256 * MI
+    if wtype == "q4k":
+        return nvec <= 12 and wb < 128 * MI
+    return True
+
+
 @settings(max_examples=400, deadline=None)
 @given(shapes(max_vec=256))
 def test_route_follows_the_documented_rule(shape):
@@ -66,15 +94,19 @@ def test_route_follows_the_documented_rule(shape):
     route = qg.qgemv_route(wtype, rows, cols, nvec)
     wb = weight_bytes(wtype, rows, cols)
     weights = rows * cols
+    few = few_kernel_rule(wtype, rows, cols, nvec)
     if wtype == "q4k":
         if nvec <= 8:
-            expect = "i8mc" if nvec >= 3 and wb >= I8_MIN_MIB[nvec] * MI else "vector"
+            i8 = nvec >= 3 and wb >= I8_MIN_MIB[nvec] * MI
+            expect = "i8mc" if i8 else ("mc32" if few else "vector")
+        elif nvec <= 16:
+            expect = "mc32" if few else "i8mc"
         else:
-            expect = "i8mc" if nvec <= 16 else "mc"
+            expect = "mc"
     elif nvec <= 8:
-        expect = "vector"
+        expect = "mc32" if few else "vector"
     else:
-        mc = nvec >= 32 or (nvec >= 16 and weights >= 24 * MI) or weights >= 48 * MI
+        mc = few or nvec >= 32 or (nvec >= 16 and weights >= 24 * MI) or weights >= 48 * MI
         expect = "mc32" if mc else "grouped"
     assert route == expect, (wtype, rows, cols, nvec, route)
 
