@@ -25,7 +25,8 @@ constexpr int mc32_step_blocks(int wtype, int vt) { return wtype == kTypeQ40 && 
 hipError_t launch_gemm_q32_mc(int wtype, const GemmArgs &a, int vt, bool debug,
                               hipStream_t stream);
 
-// Q8_0 and Q4_0 with 1..kQ32I8MaxVec vectors on the integer matrix cores (gemm_q32_i8.hip): a
+// Q8_0, Q4_0, Q6_K and Q4_K with 1..kQ32I8MaxVec vectors on the integer matrix cores
+// (gemm_q32_i8.hip; Q6_K and Q4_K rows of whole super-blocks): a
 // workgroup of up to kQ32I8MaxWaves waves takes 16 rows at a time over a column split of
 // kQ32I8BlocksPerWave blocks of 32 columns per wave (GemmArgs::sb_per_split ==
 // kQ32I8BlocksPerWave * waves, a.nb = cols / 32, row_tiles = ceil(rows / 16)); out is

@@ -1,4 +1,4 @@
-// Q8_0 and Q4_0 weights x 1..8 int8 activation vectors on the integer matrix cores
+// Q8_0, Q4_0, Q6_K and Q4_K weights x 1..16 int8 activation vectors on the integer matrix cores
 // (v_mfma_i32_16x16x64_i8).
 //
 // With a few vectors the vector kernel's int8 4-way dot products, eight per 32-weight block and
@@ -13,8 +13,8 @@
 //    0..15 and 16..31). The 16 output slots are 4 blocks x 4 vectors: the activation operand
 //    of slot (block g', vector v) holds the vector's codes at lane group g' and zeros in the
 //    other three, so every output is one (row, vector, block) partial. Two products (the two
-//    halves of the blocks) accumulate into one P; with 5..8 vectors a second pair takes
-//    vectors 4..7 with the same weight operands.
+//    halves of the blocks) accumulate into one P; each further half of 4 vectors (up to 4)
+//    takes another pair with the same weight operands.
 //  * Q4_0 stores codes 0..15 for weights q - 8: the products' accumulator input is -8 S (S the
 //    activation block's code sum), so P = sum (q - 8) xq comes out exact, as the vector kernel
 //    and the oracle define it.
