@@ -294,9 +294,14 @@ def summarize_traffic(args) -> None:
     wl = synth.WORKLOADS[args.workload]
     import block_quantized_weight_act_amd as qg
     wbytes = qg.qgemv_weight_bytes(wl.wtype, wl.rows, wl.cols)
-    launches = qg.qgemv_fused_launches(wl.wtype, wl.rows, wl.cols, wl.nvec, True)
-    kname = roofline_kernel(wl.wtype, qg.qgemv_plan_for(wl.wtype, wl.rows, wl.cols, wl.nvec),
-                            wl.nvec, launches, qg.qgemv_route(wl.wtype, wl.rows, wl.cols, wl.nvec))
+    if wl.nvec > 8:
+        # the product from codes (bench_many's roofline kernel): weights, codes and y
+        launches = 2
+        kname = many_kernel(qg, wl)
+    else:
+        launches = qg.qgemv_fused_launches(wl.wtype, wl.rows, wl.cols, wl.nvec, True)
+        kname = roofline_kernel(wl.wtype, qg.qgemv_plan_for(wl.wtype, wl.rows, wl.cols, wl.nvec),
+                                wl.nvec, launches, qg.qgemv_route(wl.wtype, wl.rows, wl.cols, wl.nvec))
     per = {}
     for path, counter in zip(args.summarize_traffic, ("FETCH_SIZE", "WRITE_SIZE")):
         rows = [r for r in _counter_rows(path) if r["Counter_Name"] == counter]
@@ -812,6 +817,34 @@ def cpu_baseline_decode_layer(products, seconds: float) -> dict:
             "gpu_y_check": {"max_err_over_bound": ratio, "ok": ratio <= 1.0}}
 
 
+def many_kernel(qg, wl) -> str:
+    """The product kernel of a workload with more than 8 vectors, as its template instance
+    appears in kernel traces (a prefix where an argument is chosen at launch)."""
+    rows, cols, nvec = wl.rows, wl.cols, wl.nvec
+    route = qg.qgemv_route(wl.wtype, rows, cols, nvec)
+    if route == "i8mc":
+        # the integer matrix cores (int8 products; 9..16 vectors)
+        return "gemm_q4k_i8_kernel<0, %d, " % ((nvec + 7) // 8)
+    if route == "mc32" and qg.qgemv_mc32_tile(wl.wtype, rows, cols, nvec) == 16:
+        # the 16 x 16 x 64 kernel (format, form from codes, halves of 4 vectors; the last
+        # argument follows the row width)
+        return "gemm_q32_i8_kernel<%d, 0, %d, " % ({"q4k": 1, "q6k": 2, "q40": 3, "q80": 4}[wl.wtype],
+                                                    (nvec + 3) // 4)
+    if route == "mc32":
+        # the workgroup shape by vector tiles (1, 2, 4): Q8_0 / Q4_0 rows, vector groups, tiles
+        # per wave; Q6_K row groups, vector tiles, row tiles per wave; then blocks per step
+        vtiles = (nvec + 31) // 32
+        vt = 4 if vtiles >= 3 else vtiles
+        if wl.wtype == "q6k":
+            return "gemm_q6k_mc_kernel<%d, %d, %d, 8, false>" % {1: (4, 1, 1), 2: (2, 2, 2),
+                                                                  4: (1, 4, 2)}[vt]
+        ks = 4 if wl.wtype == "q40" and vt == 2 else 8
+        return "gemm_q32_mc_kernel<%d, %d, %d, %d, %d, false>" % (
+            (4 if wl.wtype == "q80" else 3,) + {1: (4, 1, 1), 2: (4, 1, 2), 4: (2, 2, 2)}[vt] + (ks,))
+    # the library's tile rule: one group of ceil(nvec / 32) tiles up to 96 vectors, else 2
+    return "gemm_q4k_mfma_kernel<%d, false>" % ((nvec + 31) // 32 if nvec <= 96 else 2)
+
+
 def bench_many(args, wl) -> dict:
     """More than 8 vectors (the matrix-core kernel). Step = qgemv_quantize_act + qgemv_batch
     (plus the ordered reduce when the super-blocks are split), replayed as one graph over
@@ -910,24 +943,7 @@ def bench_many(args, wl) -> dict:
     # is set against the int8 matrix peak; the float route (fp16 products of exact integers)
     # is also given against its own fp16 peak.
     mfma_peak, mfma_unit = MFMA_I8_PEAK_TOPS, "TOP/s"
-    if route == "i8mc":
-        # the integer matrix cores (int8 products; 9..16 vectors)
-        kernel = "gemm_q4k_i8_kernel<0, %d, " % ((nvec + 7) // 8)
-    elif route == "mc32":
-        # the workgroup shape by vector tiles (1, 2, 4): Q8_0 / Q4_0 rows, vector groups, tiles
-        # per wave; Q6_K row groups, vector tiles, row tiles per wave; then blocks per step
-        vtiles = (nvec + 31) // 32
-        vt = 4 if vtiles >= 3 else vtiles
-        if wl.wtype == "q6k":
-            kernel = "gemm_q6k_mc_kernel<%d, %d, %d, 8, false>" % {1: (4, 1, 1), 2: (2, 2, 2),
-                                                                  4: (1, 4, 2)}[vt]
-        else:
-            ks = 4 if wl.wtype == "q40" and vt == 2 else 8
-            kernel = "gemm_q32_mc_kernel<%d, %d, %d, %d, %d, false>" % (
-                (4 if wl.wtype == "q80" else 3,) + {1: (4, 1, 1), 2: (4, 1, 2), 4: (2, 2, 2)}[vt] + (ks,))
-    else:
-        # the library's tile rule: one group of ceil(nvec / 32) tiles up to 96 vectors, else 2
-        kernel = "gemm_q4k_mfma_kernel<%d, false>" % ((nvec + 31) // 32 if nvec <= 96 else 2)
+    kernel = many_kernel(qg, wl)
     t_mfma = flops / (mfma_peak * 1e12)
     if t_hbm >= t_mfma:
         roof = {"bound": "hbm", "achieved": round(gemm_gbs, 1), "peak": HBM_PEAK_GBS,
@@ -977,6 +993,18 @@ def bench_many(args, wl) -> dict:
         "roofline": roof,
         "setup_s": round(setup_s, 1),
     }
+    if args.traffic_calibration:
+        # kernels of known size for the counters' scale (as in the main path): read probes
+        # over one weight copy, then plain 256 MiB device copies
+        sink = torch.zeros(1, dtype=torch.int32, device=dev)
+        for i in range(10):
+            qg.qgemv_read_probe(ws_list[i % copies], sink, blocks=4096, nbytes=wbytes)
+        src = torch.empty(CALIB_COPY_BYTES, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(10):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        out["traffic_calibration"] = {"read_probe_bytes": wbytes, "copy_bytes": CALIB_COPY_BYTES}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds, y.cpu().numpy(),
                                            max_rows=max(512, 32768 * 8 // nvec))

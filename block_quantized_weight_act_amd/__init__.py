@@ -27,6 +27,7 @@ __all__ = [
     "Graph", "qgemv_graph_begin", "qgemv_graph_end", "qgemv_graph_launch", "qgemv_graph_nodes",
     "qgemv_graph_destroy", "qgemv_graph_classify", "qgemv_i8mc_workspace_bytes", "qgemv_batch_i8mc",
     "qgemv_mc32_workspace_bytes", "qgemv_batch_mc32", "qgemv_debug_partials_mc32",
+    "qgemv_mc32_tile",
     "qgemv_debug_partials_i8mc", "qgemv_fused_i8mc", "qgemv_route", "ROUTES",
 ]
 
@@ -119,6 +120,7 @@ def _load():
         "qgemv_batch_mc32": (ctypes.c_int, [i32, vp, vp, vp, vp, i64, i64, i32, vp, sz, vp]),
         "qgemv_debug_partials_i8mc": (ctypes.c_int, [vp, vp, vp, vp, vp, i64, i64, i32, vp]),
         "qgemv_debug_partials_mc32": (ctypes.c_int, [i32, vp, vp, vp, vp, vp, i64, i64, i32, vp]),
+        "qgemv_mc32_tile": (ctypes.c_int, [i32, i64, i64, i32]),
         "qgemv_fused_i8mc": (ctypes.c_int, [vp, vp, vp, vp, vp, i64, i64, i32, vp, sz, vp]),
     }
     for name, (res, args) in sigs.items():
@@ -373,6 +375,11 @@ def qgemv_batch_mc32(wtype, w, xq, xd, y, rows: int, cols: int, nvec: int, works
         _wtype(wtype), _ptr(w, name="w"), _ptr(xq, torch.int8, "xq"),
         _ptr(xd, torch.float32, "xd"), _ptr(y, torch.float32, "y"), rows, cols, nvec, wsp, wsb,
         _stream(stream, y)))
+
+
+def qgemv_mc32_tile(wtype, rows: int, cols: int, nvec: int) -> int:
+    """16 or 32: the kernel qgemv_batch_mc32 runs for the shape (0: not taken)."""
+    return int(_load().qgemv_mc32_tile(_wtype(wtype), rows, cols, nvec))
 
 
 def qgemv_debug_partials_mc32(wtype, w, xq, xd, P, S, rows: int, cols: int, nvec: int,

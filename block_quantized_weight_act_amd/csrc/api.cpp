@@ -1311,6 +1311,11 @@ int qgemv_debug_partials_i8mc(const void *w, const int8_t *xq, const float *xd, 
     return run_i8(w, act, nullptr, P, S, rows, cols, nvec, nullptr, 0, stream);
 }
 
+int qgemv_mc32_tile(int wtype, int64_t rows, int64_t cols, int32_t nvec) {
+    if (!mc32_ok(wtype, rows, cols, nvec)) return 0;
+    return mc32_few_kernel(wtype, rows, cols, nvec) ? 16 : 32;
+}
+
 int qgemv_debug_partials_mc32(int wtype, const void *w, const int8_t *xq, const float *xd,
                               int32_t *P, int32_t *S, int64_t rows, int64_t cols, int32_t nvec,
                               hipStream_t stream) {

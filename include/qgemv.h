@@ -283,6 +283,10 @@ int qgemv_batch_mc32(int wtype, const void *w, const int8_t *xq, const float *xd
                      int64_t rows, int64_t cols, int32_t nvec, void *workspace,
                      size_t workspace_bytes, hipStream_t stream);
 
+/* Which kernel qgemv_batch_mc32 runs for a shape: 16 for the 16 x 16 x 64 one (1..16
+ * vectors), 32 for the 32 x 32 x 32 ones; 0 when it does not take the shape. Host only. */
+int qgemv_mc32_tile(int wtype, int64_t rows, int64_t cols, int32_t nvec);
+
 /* Tests only: the integer partials P [nvec][rows][cols/32] (Q6_K: [cols/16]) and
  * block sums S [nvec][cols/32] of qgemv_batch_mc32's kernels for any shape it
  * takes, as qgemv_debug_partials writes them; no y, no workspace. */

@@ -188,6 +188,9 @@ WORKLOADS = {
                                    outlier_frac=0.01, seed_rows=3005),
     "q6k_262144x1536_b8": Workload("q6k_262144x1536_b8", "q6k", 262144, 1536, 8, 1009, 3900,
                                    outlier_frac=0.01, seed_rows=3009),
+    # 16 vectors (tokens verified together) on a 65536-row Q4_0 matrix (weight seed 1008;
+    # vector v has activation seed 4000 + v)
+    "q40_65536x2048_b16": Workload("q40_65536x2048_b16", "q40", 65536, 2048, 16, 1008, 4000),
     # many vectors at once (tokens verified or prefilled together) on the matrices above:
     # vector v has activation seed 3100 + v (resp. 3400 + v)
     "q4k_262144x1536_b64": Workload("q4k_262144x1536_b64", "q4k", 262144, 1536, 64, 1003, 3100,

@@ -143,6 +143,21 @@ def test_routes():
     assert qg._load().qgemv_route(1, 8, 512, 300) == 0
 
 
+def test_mc32_tile_names_the_kernel():
+    """Which kernel qgemv_batch_mc32 runs: the 16 x 16 x 64 one for 1..8 vectors, for Q4_K, and
+    for 9..16 where the route rule gives it; the 32 x 32 x 32 ones above 16 vectors and on
+    small tensors; none where the entry point does not take the shape."""
+    assert qg.qgemv_mc32_tile("q40", 65536, 2048, 8) == 16
+    assert qg.qgemv_mc32_tile("q40", 65536, 2048, 16) == 16
+    assert qg.qgemv_mc32_tile("q40", 65536, 2048, 17) == 32
+    assert qg.qgemv_mc32_tile("q40", 1024, 1024, 12) == 32        # under 16 Mi weights
+    assert qg.qgemv_mc32_tile("q80", 65536, 2048, 12) == 32       # Q8_0 9..15 on 48..256 Mi
+    assert qg.qgemv_mc32_tile("q80", 65536, 2048, 16) == 16
+    assert qg.qgemv_mc32_tile("q4k", 65536, 2048, 12) == 16
+    assert qg.qgemv_mc32_tile("q4k", 65536, 2048, 17) == 0
+    assert qg.qgemv_mc32_tile("q6k", 1024, 1000, 4) == 0          # not whole super-blocks
+
+
 def test_grouped_workspace_covers_the_last_group():
     """Groups of 8 vectors share one workspace: it must hold the last, smaller group's partial
     sums too when that group's plan splits the columns and the full groups' does not."""
