@@ -8,9 +8,12 @@
 // vectors, so its int32 result is the block's exact integer partial P for every (row, vector):
 //
 //  * Q8_0: the weight operand is the stored int8 codes; P = sum q * xq.
-//  * Q4_0: the weight operand is the 4-bit codes 0..15 as int8 (one mask per 4 codes), and the
-//    offset of 8 is removed after the product in integer: P = sum q * xq - 8 S, S the block's
-//    activation code sum (as the vector kernel does), so a block of zero weights adds exactly 0.
+//  * Q4_0: the weight operand is 16 (q - 8) as int8: each code's nibble moved to the high half
+//    of its byte with the top bit flipped (one xor, one shift and one mask per 4 codes), so the
+//    product is 16 P exactly, P = sum (q - 8) xq, and a block of zero weights adds exactly 0.
+//    The factor 16 rides through the float sum and is taken out once per output at the end:
+//    scaling by a power of two commutes with float32 rounding, so y is the same as from P
+//    itself wherever the sums stay normal and finite (|y| below 2^123).
 //  * Float work per (row, vector, block): the conversion of P and one fma with d * xd (d the
 //    weight block's scale, xd the activation block's scale): y = sum over blocks of
 //    (d * xd) * P in float32.
@@ -19,7 +22,7 @@
 // wave 32 rows x TV tiles of 32 vectors, so the weight operand and the 16 row scales a lane
 // reads from LDS per block serve TV products: those scale reads are most of the LDS traffic)
 // over one column split, in steps of KS blocks. Each step's weights (codes and scales of the
-// workgroup's rows) and activation (codes, scales, block sums of its vectors) are loaded with
+// workgroup's rows) and activation (codes and scales of its vectors) are loaded with
 // coalesced 16-byte loads into LDS tiles padded against bank conflicts; the next step's loads
 // go out into registers before the current step's products, which read only LDS. KS = 8: 8
 // lanes per 128-byte line of each codes plane, one LDS buffer (two or three workgroups per CU);
@@ -50,12 +53,12 @@ template <int KS>
 __host__ __device__ constexpr int xpitch() { return 32 * KS + 16; }
 
 // LDS of one step's buffer: weight codes [32 RW rows][pitch], weight scales [KS blocks][32 RW]
-// float, activation codes [32 VW vectors][pitch], activation scales and block sums [KS][32 VW]
-// each (VW = VG TV vector tiles).
+// float, activation codes [32 VW vectors][pitch], activation scales [KS][32 VW] (VW = VG TV
+// vector tiles).
 template <int FMT, int RW, int VW, int KS>
 __host__ __device__ constexpr int q32_buf_bytes() {
     return 32 * RW * wpitch<FMT, KS>() + KS * 32 * RW * 4 + 32 * VW * xpitch<KS>() +
-           2 * KS * 32 * VW * 4;
+           KS * 32 * VW * 4;
 }
 
 template <int FMT, int RW, int VG, int TV, int KS, bool DBG>
@@ -152,7 +155,6 @@ __global__ void __launch_bounds__(256) gemm_q32_mc_kernel(GemmArgs a) {
         float *wd = reinterpret_cast<float *>(base + 32 * RW * WP);
         uint8_t *xq = base + 32 * RW * WP + kStep * 32 * RW * 4;
         float *xs = reinterpret_cast<float *>(xq + 32 * VW * kXPitch);
-        int *xsum = reinterpret_cast<int *>(xs + kStep * 32 * VW);
 #pragma unroll
         for (int j = 0; j < kWLoads; j++) {
             const int c = j * 256 + tid;
@@ -173,20 +175,16 @@ __global__ void __launch_bounds__(256) gemm_q32_mc_kernel(GemmArgs a) {
 #pragma unroll
         for (int j = 0; j < kXLoads; j++) {
             const int c = j * 256 + tid;
-            // the block's code sum over its two halves (lanes tid, tid ^ 1): exact
-            const uint4 q = xreg[j];
-            const int half = byte_sum(q.x, byte_sum(q.y, byte_sum(q.z, byte_sum(q.w, 0))));
-            const int s = half + __builtin_amdgcn_update_dpp(0, half, kDppXor1, 0xF, 0xF, false);
-            {
-                *reinterpret_cast<uint4 *>(xq + (c / (2 * kStep)) * kXPitch +
-                                           ((c % (2 * kStep)) / 2) * 32 + 16 * (c & 1)) = xreg[j];
-                if ((c & 1) == 0) {
-                    const int vl = c / (2 * kStep), blk = (c % (2 * kStep)) / 2;
-                    xsum[blk * 32 * VW + vl] = s;
-                    if (DBG && rt == 0) {
-                        const int v = v0 + vl, gb = b_lo + step * kStep + blk;
-                        if (v < nvec && gb < b_hi) a.S[static_cast<int64_t>(v) * nb + gb] = s;
-                    }
+            *reinterpret_cast<uint4 *>(xq + (c / (2 * kStep)) * kXPitch +
+                                       ((c % (2 * kStep)) / 2) * 32 + 16 * (c & 1)) = xreg[j];
+            if constexpr (DBG) {
+                // the block's code sum over its two halves (lanes tid, tid ^ 1): exact
+                const uint4 q = xreg[j];
+                const int half = byte_sum(q.x, byte_sum(q.y, byte_sum(q.z, byte_sum(q.w, 0))));
+                const int s = half + __builtin_amdgcn_update_dpp(0, half, kDppXor1, 0xF, 0xF, false);
+                if ((c & 1) == 0 && rt == 0) {
+                    const int v = v0 + c / (2 * kStep), gb = b_lo + step * kStep + (c % (2 * kStep)) / 2;
+                    if (v < nvec && gb < b_hi) a.S[static_cast<int64_t>(v) * nb + gb] = s;
                 }
             }
         }
@@ -220,7 +218,6 @@ __global__ void __launch_bounds__(256) gemm_q32_mc_kernel(GemmArgs a) {
         const float *wd = reinterpret_cast<const float *>(base + 32 * RW * WP);
         const uint8_t *xq = base + 32 * RW * WP + kStep * 32 * RW * 4;
         const float *xs = reinterpret_cast<const float *>(xq + 32 * VW * kXPitch);
-        const int *xsum = reinterpret_cast<const int *>(xs + kStep * 32 * VW);
         const int nblk = min(kStep, b_hi - (b_lo + step * kStep));
 #pragma unroll
         for (int k = 0; k < kStep; k++) {
@@ -229,12 +226,14 @@ __global__ void __launch_bounds__(256) gemm_q32_mc_kernel(GemmArgs a) {
                 if constexpr (FMT == kTypeQ80) {
                     A = *reinterpret_cast<const v4i_t *>(wq + k * 32 + 16 * h);
                 } else {
-                    // weights 16 h .. 16 h + 15 of the block: nibble h of its 16 code bytes
+                    // weights 16 h .. 16 h + 15 of the block: nibble h of its 16 code bytes,
+                    // as 16 (q - 8): bit 3 of the nibble flipped, the nibble in the high half
                     const uint4 raw = *reinterpret_cast<const uint4 *>(wq + k * 16);
-                    A = v4i_t{static_cast<int>((raw.x >> (4 * h)) & 0x0F0F0F0Fu),
-                              static_cast<int>((raw.y >> (4 * h)) & 0x0F0F0F0Fu),
-                              static_cast<int>((raw.z >> (4 * h)) & 0x0F0F0F0Fu),
-                              static_cast<int>((raw.w >> (4 * h)) & 0x0F0F0F0Fu)};
+                    const int sh = 4 - 4 * h;
+                    A = v4i_t{static_cast<int>(((raw.x ^ 0x88888888u) << sh) & 0xF0F0F0F0u),
+                              static_cast<int>(((raw.y ^ 0x88888888u) << sh) & 0xF0F0F0F0u),
+                              static_cast<int>(((raw.z ^ 0x88888888u) << sh) & 0xF0F0F0F0u),
+                              static_cast<int>(((raw.w ^ 0x88888888u) << sh) & 0xF0F0F0F0u)};
                 }
                 v16i_t P[TV];
 #pragma unroll
@@ -258,16 +257,16 @@ __global__ void __launch_bounds__(256) gemm_q32_mc_kernel(GemmArgs a) {
                 for (int t = 0; t < TV; t++) {
                     const int vl = (vg * TV + t) * 32 + l32;
                     const float xdv = xs[k * 32 * VW + vl];
-                    const int s8 = FMT == kTypeQ40 ? 8 * xsum[k * 32 * VW + vl] : 0;
 #pragma unroll
                     for (int i = 0; i < 16; i++) {
-                        const int p = FMT == kTypeQ40 ? P[t][i] - s8 : P[t][i];   // exact integer
+                        const int p = P[t][i];    // exact: P (Q8_0), 16 P (Q4_0)
                         if constexpr (DBG) {
                             const int row = row0 + rw * 32 + 8 * (i / 4) + 4 * h + i % 4;
                             const int gb = b_lo + step * kStep + k;
                             const int v = v0 + vl;
                             if (row < rows && v < nvec)
-                                a.P[(static_cast<int64_t>(v) * rows + row) * nb + gb] = p;
+                                a.P[(static_cast<int64_t>(v) * rows + row) * nb + gb] =
+                                    FMT == kTypeQ40 ? p >> 4 : p;
                         } else {
                             acc[t][i] = fmaf(dv[i] * xdv, static_cast<float>(p), acc[t][i]);
                         }
@@ -289,7 +288,9 @@ __global__ void __launch_bounds__(256) gemm_q32_mc_kernel(GemmArgs a) {
                     const int row = row0 + rw * 32 + 8 * qq + 4 * h;
 #pragma unroll
                     for (int i = 0; i < 4; i++)
-                        if (row + i < rows) yv[row + i] = acc[t][4 * qq + i];
+                        if (row + i < rows)
+                            yv[row + i] = FMT == kTypeQ40 ? acc[t][4 * qq + i] * 0.0625f
+                                                          : acc[t][4 * qq + i];
                 }
             }
         }
