@@ -15,9 +15,15 @@
 //    other three, so every output is one (row, vector, block) partial. Two products (the two
 //    halves of the blocks) accumulate into one P; each further half of 4 vectors (up to 4)
 //    takes another pair with the same weight operands.
-//  * Q4_0 stores codes 0..15 for weights q - 8: the products' accumulator input is -8 S (S the
-//    activation block's code sum), so P = sum (q - 8) xq comes out exact, as the vector kernel
-//    and the oracle define it.
+//  * Q4_0 stores codes 0..15 for weights q - 8, and P = sum (q - 8) xq comes out exact, as the
+//    vector kernel and the oracle define it, in one of two ways. With up to 8 vectors the
+//    weight operand is the codes and the first product's accumulator input is -8 S (S the
+//    activation block's code sum, kept in registers). With 9..16 the weight operand is
+//    16 (q - 8) as int8 (each nibble moved to the high half of its byte with its top bit
+//    flipped), so the products give 16 P with no accumulator input to read from LDS; the 16
+//    stays in the float sums and comes out once per output when y is stored (scaling by a
+//    power of two commutes with float32 rounding, so y is the one P itself gives wherever the
+//    sums stay normal and finite, |y| below 2^123).
 //  * Float work per output and block: (d * xd) and one fma with P converted, as in the vector
 //    kernel, so y stays within the same bound.
 //
@@ -50,8 +56,8 @@ constexpr int kBw = kQ32I8BlocksPerWave;
 
 // LDS of a workgroup of `waves` waves and NV vector slots: NV rows of codes (the split's blocks)
 // and a row of zeros, each of pitch bytes (the 16 spread the rows over the banks); the scales
-// and Q4_0's -8 S of the split's blocks [block][NV]; two slots of the waves' sums of a row
-// tile.
+// and Q4_0's -8 S or Q4_K's -xd S of the split's blocks [block][NV]; two slots of the waves'
+// sums of a row tile.
 __host__ __device__ constexpr int q32i8_pitch(int waves) { return waves * kBw * 32 + 16; }
 __host__ __device__ constexpr int q32i8_lds_bytes(int waves, int nv) {
     return (nv + 1) * q32i8_pitch(waves) + 2 * waves * kBw * nv * 4 + 2 * waves * 16 * nv * 4;
@@ -74,8 +80,11 @@ __global__ void __launch_bounds__(256) gemm_q32_i8_kernel(GemmArgs a) {
     // Q8_0 x 8: 84.2 against 91.3 us).
     constexpr bool SINGLE = (H == 2 && FMT != kTypeQ80) || H >= 3;
     // With up to 8 vectors the activation scales (and Q4_0's -8 S) of the lane's outputs stay in
-    // registers for the whole kernel; with more they are read from LDS per product.
+    // registers for the whole kernel; with more the scales are read from LDS per product, and
+    // Q4_0's weight operand is 16 (q - 8) (X16: measured on 65536 x 2048, 16 vectors 25.9 ->
+    // 23.3 us, 12 vectors 19.8 -> 19.2; with 8 on 262144 x 1536 it lost 2%).
     constexpr bool KEEP = H <= 2;
+    constexpr bool X16 = Q40 && !KEEP;
     extern __shared__ __attribute__((aligned(16))) uint8_t lds_q32i8[];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -86,7 +95,7 @@ __global__ void __launch_bounds__(256) gemm_q32_i8_kernel(GemmArgs a) {
     const int nblk = waves * kBw;              // staged blocks of the split
     uint8_t *const xq_s = lds_q32i8;           // [NV + 1][pitch]: codes, then zeros
     float *const xd_s = reinterpret_cast<float *>(lds_q32i8 + (NV + 1) * pitch);   // [nblk][NV]
-    int *const s8_s = reinterpret_cast<int *>(xd_s + nblk * NV);     // [nblk][NV]: Q4_0: -8 S
+    float *const s8_s = xd_s + nblk * NV;      // [nblk][NV]: Q4_K: -xd S; Q4_0 (not X16): -8 S
     float *const red_s = reinterpret_cast<float *>(s8_s + nblk * NV);  // [2][waves][16][NV]
     const int r = lane & 15;                   // tile row of this lane's weights and outputs
     const int g = lane >> 4;                   // lane group: block 4 i + g of the wave's 16
@@ -162,7 +171,7 @@ __global__ void __launch_bounds__(256) gemm_q32_i8_kernel(GemmArgs a) {
     WTile tA, tB;     // tB: the second tile of the first two (not with SINGLE)
 
     // ---- the split's activation into LDS: codes as stored (one (vector, block) item of 32
-    //      bytes per thread and pass), scales and -8 S; zeros for vectors past nvec and blocks
+    //      bytes per thread and pass), scales, -xd S (Q4_K) or -8 S (Q4_0); zeros for vectors past nvec and blocks
     //      past the split. The staging's loads go out first, then both tiles' weights, then the
     //      staging's stores ----
     for (int i = tid; i < pitch / 16; i += threads)
@@ -189,17 +198,17 @@ __global__ void __launch_bounds__(256) gemm_q32_i8_kernel(GemmArgs a) {
             const int it = p * threads + tid;
             const int v = it / nblk, b = it - v * nblk;
             const uint4 c0 = cv[p][0], c1 = cv[p][1];
-            const int s = byte_sum(c0.x, byte_sum(c0.y, byte_sum(c0.z, byte_sum(c0.w,
-                          byte_sum(c1.x, byte_sum(c1.y, byte_sum(c1.z, byte_sum(c1.w, 0))))))));
             *reinterpret_cast<uint4 *>(xq_s + v * pitch + 32 * b) = c0;
             *reinterpret_cast<uint4 *>(xq_s + v * pitch + 32 * b + 16) = c1;
             xd_s[b * NV + v] = sv[p];
-            if constexpr (QK)
-                reinterpret_cast<float *>(s8_s)[b * NV + v] = -(sv[p] * static_cast<float>(s));
-            else
-                s8_s[b * NV + v] = -8 * s;
-            if (DBG && blockIdx.x == 0 && v < nvec && b < nsb)
-                a.S[static_cast<int64_t>(v) * nb + b_lo + b] = s;
+            if constexpr (QK || (Q40 && !X16) || DBG) {
+                const int s = byte_sum(c0.x, byte_sum(c0.y, byte_sum(c0.z, byte_sum(c0.w,
+                              byte_sum(c1.x, byte_sum(c1.y, byte_sum(c1.z, byte_sum(c1.w, 0))))))));
+                if constexpr (QK) s8_s[b * NV + v] = -(sv[p] * static_cast<float>(s));
+                if constexpr (Q40 && !X16) reinterpret_cast<int *>(s8_s)[b * NV + v] = -8 * s;
+                if (DBG && blockIdx.x == 0 && v < nvec && b < nsb)
+                    a.S[static_cast<int64_t>(v) * nb + b_lo + b] = s;
+            }
         }
     }
     __syncthreads();
@@ -207,7 +216,7 @@ __global__ void __launch_bounds__(256) gemm_q32_i8_kernel(GemmArgs a) {
     // ---- this lane's operands from LDS, the same for every row tile: the activation rows it
     //      reads (slot r: block r / 4 of each group of 4, vector 4 h + r % 4; the zero row
     //      where r / 4 is not this lane group), and for its outputs (vectors 4 h .. 4 h + 3 of
-    //      block wb0 + 4 i + g) the scales and -8 S ----
+    //      block wb0 + 4 i + g) the scales and Q4_0's -8 S ----
     const bool live = (r >> 2) == g;
     const uint8_t *abase[H];
 #pragma unroll
@@ -226,9 +235,7 @@ __global__ void __launch_bounds__(256) gemm_q32_i8_kernel(GemmArgs a) {
                 xdk[i][h] = Q6 ? v4f_t{0.0f, 0.0f, 0.0f, 0.0f} : *reinterpret_cast<const v4f_t *>(xd_s + o);
                 c8k[i][h] = Q40 ? *reinterpret_cast<const v4i_t *>(s8_s + o) : v4i_t{0, 0, 0, 0};
             }
-            mink[i][h] = QK && r < 4
-                             ? reinterpret_cast<const float *>(s8_s)[(wb0 + 4 * i + g) * NV + 4 * h + r]
-                             : 0.0f;
+            mink[i][h] = QK && r < 4 ? s8_s[(wb0 + 4 * i + g) * NV + 4 * h + r] : 0.0f;
             // (Q6_K reads its activation scales per product instead: its weight operands take
             // more registers)
         }
@@ -237,9 +244,9 @@ __global__ void __launch_bounds__(256) gemm_q32_i8_kernel(GemmArgs a) {
         if constexpr (KEEP) return xdk[i][h];
         else return *reinterpret_cast<const v4f_t *>(xd_s + (wb0 + 4 * i + g) * NV + 4 * h);
     };
+    // Q4_0's -8 S as the first product's accumulator input (zeros for the other formats and X16)
     auto c8_of = [&](int i, int h) -> v4i_t {
         if constexpr (KEEP) return c8k[i][h];
-        else if constexpr (Q40) return *reinterpret_cast<const v4i_t *>(s8_s + (wb0 + 4 * i + g) * NV + 4 * h);
         else return v4i_t{0, 0, 0, 0};
     };
 
@@ -421,7 +428,7 @@ __global__ void __launch_bounds__(256) gemm_q32_i8_kernel(GemmArgs a) {
 #pragma unroll
             for (int i = 0; i < 4; i++) {
                 v4i_t B0, B1;
-                if constexpr (Q40) {
+                if constexpr (Q40 && !X16) {
                     const uint4 c = t.c[i][0];
                     B0 = v4i_t{static_cast<int>(c.x & 0x0F0F0F0Fu), static_cast<int>(c.y & 0x0F0F0F0Fu),
                                static_cast<int>(c.z & 0x0F0F0F0Fu), static_cast<int>(c.w & 0x0F0F0F0Fu)};
@@ -429,6 +436,15 @@ __global__ void __launch_bounds__(256) gemm_q32_i8_kernel(GemmArgs a) {
                                static_cast<int>((c.y >> 4) & 0x0F0F0F0Fu),
                                static_cast<int>((c.z >> 4) & 0x0F0F0F0Fu),
                                static_cast<int>((c.w >> 4) & 0x0F0F0F0Fu)};
+                } else if constexpr (X16) {
+                    // 16 (q - 8) as int8: bit 3 of each nibble flipped, the nibble in the high
+                    // half of its byte (low nibbles: weights 0..15, high: 16..31)
+                    const uint32_t x0 = t.c[i][0].x ^ 0x88888888u, x1 = t.c[i][0].y ^ 0x88888888u;
+                    const uint32_t x2 = t.c[i][0].z ^ 0x88888888u, x3 = t.c[i][0].w ^ 0x88888888u;
+                    B0 = v4i_t{static_cast<int>((x0 << 4) & 0xF0F0F0F0u), static_cast<int>((x1 << 4) & 0xF0F0F0F0u),
+                               static_cast<int>((x2 << 4) & 0xF0F0F0F0u), static_cast<int>((x3 << 4) & 0xF0F0F0F0u)};
+                    B1 = v4i_t{static_cast<int>(x0 & 0xF0F0F0F0u), static_cast<int>(x1 & 0xF0F0F0F0u),
+                               static_cast<int>(x2 & 0xF0F0F0F0u), static_cast<int>(x3 & 0xF0F0F0F0u)};
                 } else {
                     B0 = __builtin_bit_cast(v4i_t, t.c[i][0]);
                     B1 = __builtin_bit_cast(v4i_t, t.c[i][1]);
@@ -458,7 +474,7 @@ __global__ void __launch_bounds__(256) gemm_q32_i8_kernel(GemmArgs a) {
                         for (int e = 0; e < 4; e++) {
                             const int v = 4 * h + e;
                             if (v < nvec && row < rows && bv)
-                                a.P[(int64_t{v} * rows + row) * nb + blk] = P[h][e];
+                                a.P[(int64_t{v} * rows + row) * nb + blk] = X16 ? P[h][e] >> 4 : P[h][e];
                         }
                     }
                 }
@@ -508,7 +524,7 @@ __global__ void __launch_bounds__(256) gemm_q32_i8_kernel(GemmArgs a) {
 #pragma unroll
                     for (int w = 1; w < kQ32I8MaxWaves; w++)
                         if (w < waves) y += red_s[((slot * waves + w) * 16 + rr) * NV + v];
-                    out[static_cast<int64_t>(v) * rows + row] = y;
+                    out[static_cast<int64_t>(v) * rows + row] = X16 ? y * 0.0625f : y;
                 }
             }
             slot ^= 1;
