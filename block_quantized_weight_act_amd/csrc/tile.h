@@ -277,14 +277,14 @@ struct Q6kTile {
                 }
 #pragma unroll
                 for (int v = 0; v < V; v++) {
-                    int plo = 0, phi = 0;
+                    // the codes' offset as the dot products' starting values: -32 S of each
+                    // sub-block is the same for every row this lane reads
+                    int plo = -32 * at.lo[v][k], phi = -32 * at.hi[v][k];
 #pragma unroll
                     for (int s = 0; s < 4; s++) {
                         plo = dot4(lo[s], xw[v][k][s], plo);
                         phi = dot4(hi[s], xw[v][k][4 + s], phi);
                     }
-                    plo -= 32 * at.lo[v][k];
-                    phi -= 32 * at.hi[v][k];
                     const int scp = sc_lo * plo + sc_hi * phi;
                     acc[v] = fmaf(xs[v][k] * d, static_cast<float>(scp), acc[v]);
                     if (DBG && rv && L.cv[k]) {
@@ -360,13 +360,14 @@ struct Q40Tile {
                 }
 #pragma unroll
                 for (int v = 0; v < V; v++) {
-                    int p = 0;
+                    // the offset of the codes as the dot products' starting value: -8 S is the
+                    // same for every row this lane reads, so it costs nothing per row
+                    int p = -8 * at.sum[v][k];
 #pragma unroll
                     for (int i = 0; i < 4; i++) {
                         p = dot4(lo[i], xw[v][k][i], p);
                         p = dot4(hi[i], xw[v][k][4 + i], p);
                     }
-                    p -= 8 * at.sum[v][k];
                     acc[v] = fmaf(xs[v][k] * d, static_cast<float>(p), acc[v]);
                     if (DBG && rv && L.cv[k])
                         P[(static_cast<int64_t>(v) * rows + row) * nsub + L.g[k]] = p;
